@@ -1,0 +1,273 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for the generalized linear-attention
+ * recurrence.  TEST INFRASTRUCTURE ONLY: it is called from tests/, from the smoke
+ * check and from the CPU-baseline leg of the benchmark, never from the library.
+ * It shares no code, header or constant with the HIP path.
+ *
+ * What it computes (one layer, one head, token by token):
+ *
+ *   S_t = S_{t-1} A_t + beta_t v_t k_t^T ,   o_t = S_t q_t
+ *
+ *   [NoteBank] "History Replays Itself: Unleashing Long-Context Capability in Linear
+ *   Attention", Sec. 2 (Preliminary), Eq. (1).  q_t, k_t in R^{d_k}, v_t in R^{d_v},
+ *   S_t in R^{d_v x d_k}; A_t multiplies on the right.  Variants:
+ *     ADDITIVE     A_t = I, beta_t = 1                    (same passage)
+ *     GATED        A_t = alpha_t I                        (scalar-gated state)
+ *     GATED_DELTA  A_t = alpha_t (I - beta_t k_t k_t^T)   (gated delta rule)
+ *   The page names the gated and delta-rule families without printing them; the two
+ *   forms above are the plainest members of those families and are the ones this
+ *   library implements.  The write term beta_t v_t k_t^T is not scaled by alpha_t.
+ *
+ *   BASED          [BASED] "Simple linear attention language models balance the
+ *   recall-throughput tradeoff" (reading notes, Sec. 2.2, paper Eqs. (1)-(3), and
+ *   Sec. 2.3, paper Eq. (4)):
+ *     phi(x) = [1, x, vec(x x^T)/sqrt(2)]   (D = 1 + d' + d'^2, order-2 index 1+d'+i*d'+j)
+ *     s_t = s_{t-1} + phi(k_t) v_t^T  (D x d_v),   z_t = z_{t-1} + phi(k_t),  s_0 = z_0 = 0
+ *     o_t = s_t^T phi(q_t) / (z_t^T phi(q_t) + eps)
+ *   The notes say an implementation adds a small eps to the (positive) denominator;
+ *   eps is an argument here.  No input scaling is applied (the caller pre-scales).
+ *
+ * Because A_t acts on the right of S, every row i of S (a d_k-vector) evolves on its
+ * own:  s_i <- s_i A_t + beta_t v_t[i] k_t^T,  o_t[i] = s_i . q_t.  For the gated delta
+ * rule  s_i A_t = alpha_t (s_i - beta_t (s_i . k_t) k_t^T).  The routines below walk
+ * rows independently, which also lets a caller ask for a subset of rows (sampled
+ * parity at very long T).  oracle_literal() instead builds the d_k x d_k matrix A_t
+ * and multiplies it out, to pin the rank-1 form on tiny inputs.
+ *
+ * Layouts (row-major, last index fastest), identical to the library's:
+ *   q, k  [B][H][T][d_k]     v, o  [B][H][T][d_v]     alpha, beta  [B][H][T]
+ *   S     [B][H][d_v][d_k]   (ADDITIVE / GATED / GATED_DELTA)
+ *   s     [B][H][D][d_v],  z [B][H][D]                (BASED, d_k = d')
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_ADDITIVE = 0, OR_BASED = 1, OR_GATED = 2, OR_GATED_DELTA = 3 };
+
+int oracle_version(void) { return 1; }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+}
+
+/* ---------------------------------------------------------------------------------
+ * One row of S through T tokens (ADDITIVE, GATED, GATED_DELTA).
+ *   s      : d_k doubles, in = row of S0, out = row of S_T
+ *   o      : receives o_t[row] at o[t * o_stride]
+ * beta == NULL means beta_t = 1 (allowed for GATED; ADDITIVE ignores alpha, beta).
+ * ------------------------------------------------------------------------------- */
+static void row_recurrence(int variant, long T, int dk, int dv, int row, const double *q,
+                           const double *k, const double *v, const double *alpha,
+                           const double *beta, double *s, double *o, long o_stride) {
+  for (long t = 0; t < T; ++t) {
+    const double *kt = k + (size_t)t * dk;
+    const double *qt = q + (size_t)t * dk;
+    const double vt = v[(size_t)t * dv + row];
+    if (variant == OR_ADDITIVE) {
+      /* s <- s I + 1 * v_t[row] k_t */
+      for (int j = 0; j < dk; ++j) s[j] += vt * kt[j];
+    } else if (variant == OR_GATED) {
+      /* s <- s (alpha_t I) + beta_t v_t[row] k_t */
+      const double a = alpha[t];
+      const double b = beta ? beta[t] : 1.0;
+      for (int j = 0; j < dk; ++j) s[j] = a * s[j] + b * vt * kt[j];
+    } else { /* OR_GATED_DELTA */
+      /* s <- s alpha_t (I - beta_t k_t k_t^T) + beta_t v_t[row] k_t
+       *    = alpha_t (s - beta_t (s . k_t) k_t) + beta_t v_t[row] k_t           */
+      const double a = alpha[t];
+      const double b = beta[t];
+      double r = 0.0;
+      for (int j = 0; j < dk; ++j) r += s[j] * kt[j];
+      for (int j = 0; j < dk; ++j) s[j] = a * (s[j] - b * r * kt[j]) + b * vt * kt[j];
+    }
+    /* o_t[row] = s_t . q_t  (the read happens after the write: o_t = S_t q_t) */
+    double acc = 0.0;
+    for (int j = 0; j < dk; ++j) acc += s[j] * qt[j];
+    o[(size_t)t * o_stride] = acc;
+  }
+}
+
+/* BASED feature map phi(x) = [1, x, vec(x x^T)/sqrt(2)], D = 1 + d' + d'^2. */
+static void based_phi(const double *x, int dp, double *f) {
+  const double inv_sqrt2 = 1.0 / sqrt(2.0);
+  f[0] = 1.0;
+  for (int i = 0; i < dp; ++i) f[1 + i] = x[i];
+  for (int i = 0; i < dp; ++i)
+    for (int j = 0; j < dp; ++j) f[1 + dp + i * dp + j] = x[i] * x[j] * inv_sqrt2;
+}
+
+void oracle_based_phi(const double *x, int dp, double *f) { based_phi(x, dp, f); }
+
+/* One (b,h) slice of BASED through T tokens for a subset of value columns.
+ *   s : [D][ncols] (in = s0 restricted to cols, out = s_T), z : [D] (in/out)
+ *   o : [T][ncols]                                                              */
+static void based_slice(long T, int dp, int dv, const int *cols, int ncols, const double *q,
+                        const double *k, const double *v, double eps, double *s, double *z,
+                        double *o) {
+  const int D = 1 + dp + dp * dp;
+  double *fk = (double *)malloc(sizeof(double) * D);
+  double *fq = (double *)malloc(sizeof(double) * D);
+  for (long t = 0; t < T; ++t) {
+    based_phi(k + (size_t)t * dp, dp, fk);
+    based_phi(q + (size_t)t * dp, dp, fq);
+    /* s_t = s_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t) */
+    for (int f = 0; f < D; ++f) {
+      for (int c = 0; c < ncols; ++c) s[(size_t)f * ncols + c] += fk[f] * v[(size_t)t * dv + cols[c]];
+      z[f] += fk[f];
+    }
+    /* o_t = s_t^T phi(q_t) / (z_t^T phi(q_t) + eps) */
+    double den = 0.0;
+    for (int f = 0; f < D; ++f) den += z[f] * fq[f];
+    for (int c = 0; c < ncols; ++c) {
+      double num = 0.0;
+      for (int f = 0; f < D; ++f) num += s[(size_t)f * ncols + c] * fq[f];
+      o[(size_t)t * ncols + c] = num / (den + eps);
+    }
+  }
+  free(fk);
+  free(fq);
+}
+
+/* ---------------------------------------------------------------------------------
+ * oracle_prefill: the recurrence over T tokens for every (b, h).
+ *
+ *   rows / nrows : subset of value rows (GDN family) or value columns (BASED) to
+ *                  compute; rows == NULL means all d_v of them.  Outputs are then
+ *                  o [B][H][T][nrows], S_T [B][H][nrows][d_k] (GDN family) or
+ *                  s_T [B][H][D][nrows], z_T [B][H][D] (BASED).
+ *   S0 / z0      : NULL = zero start state (BASED: s_0 = 0, z_0 = 0).  S0 always has
+ *                  the full layout [B][H][d_v][d_k] (or [B][H][D][d_v]).
+ *   S_T / z_T    : may be NULL.
+ * Returns 0, or -1 on invalid arguments.
+ * ------------------------------------------------------------------------------- */
+int oracle_prefill(int variant, int B, int H, long T, int dk, int dv, const double *q,
+                   const double *k, const double *v, const double *alpha, const double *beta,
+                   const double *S0, const double *z0, double eps, const int *rows, int nrows,
+                   double *o, double *S_T, double *z_T, int nthreads) {
+  if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || !q || !k || !v || !o) return -1;
+  if ((variant == OR_GATED || variant == OR_GATED_DELTA) && !alpha) return -1;
+  if (variant == OR_GATED_DELTA && !beta) return -1;
+  if (variant < 0 || variant > 3) return -1;
+  const int nr = rows ? nrows : dv;
+  for (int i = 0; i < nr; ++i)
+    if (rows && (rows[i] < 0 || rows[i] >= dv)) return -1;
+  set_threads(nthreads);
+
+  if (variant == OR_BASED) {
+    const int dp = dk, D = 1 + dp + dp * dp;
+    int *cols = (int *)malloc(sizeof(int) * nr);
+    for (int c = 0; c < nr; ++c) cols[c] = rows ? rows[c] : c;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < H; ++h) {
+        const size_t bh = (size_t)b * H + h;
+        double *s = (double *)calloc((size_t)D * nr, sizeof(double));
+        double *z = (double *)calloc((size_t)D, sizeof(double));
+        if (S0)
+          for (int f = 0; f < D; ++f)
+            for (int c = 0; c < nr; ++c) s[(size_t)f * nr + c] = S0[(bh * D + f) * dv + cols[c]];
+        if (z0)
+          for (int f = 0; f < D; ++f) z[f] = z0[bh * D + f];
+        based_slice(T, dp, dv, cols, nr, q + bh * T * dp, k + bh * T * dp, v + bh * T * dv, eps,
+                    s, z, o + bh * T * nr);
+        if (S_T) memcpy(S_T + bh * D * nr, s, sizeof(double) * D * nr);
+        if (z_T) memcpy(z_T + bh * D, z, sizeof(double) * D);
+        free(s);
+        free(z);
+      }
+    free(cols);
+    return 0;
+  }
+
+#pragma omp parallel for collapse(3) schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int ri = 0; ri < nr; ++ri) {
+        const size_t bh = (size_t)b * H + h;
+        const int row = rows ? rows[ri] : ri;
+        double *s = (double *)malloc(sizeof(double) * dk);
+        if (S0)
+          memcpy(s, S0 + (bh * dv + row) * dk, sizeof(double) * dk);
+        else
+          memset(s, 0, sizeof(double) * dk);
+        row_recurrence(variant, T, dk, dv, row, q + bh * T * dk, k + bh * T * dk,
+                       v + bh * T * dv, alpha ? alpha + bh * T : NULL, beta ? beta + bh * T : NULL,
+                       s, o + bh * T * nr + ri, nr);
+        if (S_T) memcpy(S_T + (bh * nr + ri) * dk, s, sizeof(double) * dk);
+        free(s);
+      }
+  return 0;
+}
+
+/* oracle_decode_step: one token of the recurrence for N independent (sequence, head)
+ * states.  Layouts drop the T axis: q, k [N][d_k], v, o [N][d_v], alpha, beta [N],
+ * S [N][d_v][d_k] (BASED: s [N][D][d_v], z [N][D]).  S_in == NULL means zero state. */
+int oracle_decode_step(int variant, int N, int dk, int dv, const double *S_in, const double *z_in,
+                       const double *q, const double *k, const double *v, const double *alpha,
+                       const double *beta, double eps, double *S_out, double *z_out, double *o,
+                       int nthreads) {
+  /* One decode step is the recurrence with T = 1 on N slices (B = N, H = 1). */
+  return oracle_prefill(variant, N, 1, 1, dk, dv, q, k, v, alpha, beta, S_in, z_in, eps, NULL, 0, o,
+                        S_out, z_out, nthreads);
+}
+
+/* ---------------------------------------------------------------------------------
+ * oracle_literal: the same recurrence with A_t built as an explicit d_k x d_k matrix
+ * and S_t = S_{t-1} A_t + beta_t v_t k_t^T multiplied out in full (O(d_v d_k^2) per
+ * token).  Only for tiny inputs: it pins the row-wise rank-1 form used above.
+ * Variants: ADDITIVE, GATED, GATED_DELTA.  One (b,h) slice: q,k [T][dk], v,o [T][dv].
+ * ------------------------------------------------------------------------------- */
+int oracle_literal(int variant, long T, int dk, int dv, const double *q, const double *k,
+                   const double *v, const double *alpha, const double *beta, const double *S0,
+                   double *o, double *S_T) {
+  if (variant == OR_BASED || variant < 0 || variant > 3) return -1;
+  double *S = (double *)calloc((size_t)dv * dk, sizeof(double));
+  double *Sn = (double *)malloc(sizeof(double) * dv * dk);
+  double *A = (double *)malloc(sizeof(double) * dk * dk);
+  if (S0) memcpy(S, S0, sizeof(double) * dv * dk);
+  for (long t = 0; t < T; ++t) {
+    const double *kt = k + (size_t)t * dk;
+    const double a = (variant == OR_ADDITIVE) ? 1.0 : alpha[t];
+    const double b = (variant == OR_ADDITIVE) ? 1.0 : (beta ? beta[t] : 1.0);
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dk; ++j) {
+        double eye = (i == j) ? 1.0 : 0.0;
+        A[i * dk + j] = (variant == OR_GATED_DELTA) ? a * (eye - b * kt[i] * kt[j]) : a * eye;
+      }
+    for (int r = 0; r < dv; ++r)
+      for (int j = 0; j < dk; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += S[r * dk + i] * A[i * dk + j];
+        Sn[r * dk + j] = acc + b * v[(size_t)t * dv + r] * kt[j];
+      }
+    memcpy(S, Sn, sizeof(double) * dv * dk);
+    for (int r = 0; r < dv; ++r) {
+      double acc = 0.0;
+      for (int j = 0; j < dk; ++j) acc += S[r * dk + j] * q[(size_t)t * dk + j];
+      o[(size_t)t * dv + r] = acc;
+    }
+  }
+  if (S_T) memcpy(S_T, S, sizeof(double) * dv * dk);
+  free(S);
+  free(Sn);
+  free(A);
+  return 0;
+}

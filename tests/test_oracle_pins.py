@@ -1,0 +1,382 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test ties the oracle to something other than itself: a brute-force evaluation of
+a closed form, an invariant, a special case with a known answer, or a number printed
+on the pages (tests/golden/printed_values.json).  A plausible mistake in the oracle
+(dropped term, wrong sign, off-by-one in the causal mask, transposed operand, wrong
+feature layout, gate applied to the write term) fails at least one of them; see also
+test_oracle_mutants.py, which plants such mistakes and checks that they are caught.
+"""
+
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import models
+
+GOLDEN = json.loads((Path(__file__).parent / "golden" / "printed_values.json").read_text())
+
+
+def rel(x, y):
+    return float(np.max(np.abs(np.asarray(x) - np.asarray(y))) / max(np.max(np.abs(y)), 1e-300))
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def gdn_like(r, B, H, T, dk, dv, normalize=True):
+    q = r.standard_normal((B, H, T, dk))
+    k = r.standard_normal((B, H, T, dk))
+    if normalize:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, H, T, dv))
+    a = r.uniform(-2, 4, (B, H, T))
+    alpha = np.exp(-np.log1p(np.exp(a)))
+    beta = 1 / (1 + np.exp(-r.standard_normal((B, H, T))))
+    return q, k, v, alpha, beta
+
+
+# ----------------------------------------------------------------------------- additive
+def test_additive_matches_causal_bruteforce():
+    """Additive case: O = (Q K^T . M) V + Q S0^T, S_T = S0 + V^T K (M causal incl. diagonal)."""
+    r = rng(1)
+    B, H, T, dk, dv = 2, 3, 37, 5, 4
+    q, k, v = (r.standard_normal((B, H, T, d)) for d in (dk, dk, dv))
+    S0 = r.standard_normal((B, H, dv, dk))
+    o, S_T, _ = oracle.prefill("additive", q, k, v, S0=S0)
+    M = np.tril(np.ones((T, T)))
+    for b in range(B):
+        for h in range(H):
+            ref = ((q[b, h] @ k[b, h].T) * M) @ v[b, h] + q[b, h] @ S0[b, h].T
+            assert rel(o[b, h], ref) < 1e-12
+            assert rel(S_T[b, h], S0[b, h] + v[b, h].T @ k[b, h]) < 1e-12
+
+
+def test_additive_reads_after_write():
+    """o_t = S_t q_t reads the state *after* token t's write (diagonal included)."""
+    q = np.zeros((1, 1, 1, 3))
+    k = np.zeros((1, 1, 1, 3))
+    q[..., 0] = 1.0
+    k[..., 0] = 2.0
+    v = np.array([[[[5.0, -1.0]]]])
+    o, _, _ = oracle.prefill("additive", q, k, v)
+    assert np.array_equal(o[0, 0, 0], np.array([10.0, -2.0]))
+
+
+# ----------------------------------------------------------------------------- BASED
+def test_golden_feature_dims():
+    assert oracle.feature_dim(16) == GOLDEN["based_feature_dim_full_dprime16"]["value"]
+    assert 1 + 16 + 16 * 17 // 2 == GOLDEN["based_feature_dim_compact_dprime16"]["value"]
+    assert -(-273 // 64) * 64 == GOLDEN["based_feature_dim_padded_dprime16"]["value"]
+    assert oracle.based_phi(np.ones(16)).size == 273
+
+
+def test_taylor_feature_map_closed_form():
+    """phi(q).phi(k) = 1 + q.k + (q.k)^2/2 for 10^4 random pairs, d' = 16."""
+    r = rng(2)
+    worst = 0.0
+    for _ in range(10_000):
+        x, y = r.standard_normal(16), r.standard_normal(16)
+        t = float(x @ y)
+        kern = 1.0 + t + t * t / 2.0
+        worst = max(worst, abs(oracle.based_phi(x) @ oracle.based_phi(y) - kern) / abs(kern))
+    assert worst < 1e-13
+
+
+def test_taylor_scaled_closed_form():
+    """With xbar = x / d'^(1/4): phi(qbar).phi(kbar) = 1 + q.k/sqrt(d') + (q.k)^2/(2 d')."""
+    r = rng(3)
+    dp = 16
+    for _ in range(1000):
+        x, y = r.standard_normal(dp), r.standard_normal(dp)
+        t = float(x @ y)
+        s = dp ** 0.25
+        val = oracle.based_phi(x / s) @ oracle.based_phi(y / s)
+        assert abs(val - (1 + t / math.sqrt(dp) + t * t / (2 * dp))) < 1e-12 * (1 + t * t)
+
+
+def test_taylor_positivity():
+    """((t+1)^2+1)/2 >= 1/2: every kernel term is at least 1/2."""
+    t = np.linspace(-50, 50, 100001)
+    kern = 1 + t + t * t / 2
+    assert np.allclose(kern, ((t + 1) ** 2 + 1) / 2, rtol=1e-14, atol=0)
+    assert kern.min() >= 0.5 - 1e-15
+
+
+def _based_bruteforce(q, k, v, eps, prefix=None):
+    """y_i = sum_{j<=i} K(q_i,k_j) v_j / (sum_{j<=i} K(q_i,k_j) + eps), K(q,k)=1+q.k+(q.k)^2/2."""
+    if prefix is not None:
+        kq, vq = prefix
+        k = np.concatenate([kq, k])
+        v = np.concatenate([vq, v])
+    P = 0 if prefix is None else prefix[0].shape[0]
+    T = q.shape[0]
+    dots = q @ k.T
+    Kmat = 1 + dots + dots ** 2 / 2
+    mask = np.arange(P + T)[None, :] <= (P + np.arange(T))[:, None]
+    Kmat = Kmat * mask
+    den = Kmat.sum(1)
+    return (Kmat @ v) / (den + eps)[:, None], den
+
+
+def test_based_matches_bruteforce_and_denominator_bound():
+    r = rng(4)
+    B, H, T, dp, dv = 1, 2, 64, 4, 3
+    q = r.standard_normal((B, H, T, dp)) / 2
+    k = r.standard_normal((B, H, T, dp)) / 2
+    v = r.standard_normal((B, H, T, dv))
+    eps = 1e-6
+    o, s_T, z_T = oracle.prefill("based", q, k, v, eps=eps)
+    for h in range(H):
+        ref, den = _based_bruteforce(q[0, h], k[0, h], v[0, h], eps)
+        assert rel(o[0, h], ref) < 1e-12
+        assert np.all(den >= (np.arange(T) + 1) / 2 - 1e-12)
+        # the final state reproduces the sum over all keys for a fresh query
+        x = r.standard_normal(dp)
+        f = oracle.based_phi(x)
+        Kx = 1 + k[0, h] @ x + (k[0, h] @ x) ** 2 / 2
+        assert rel(s_T[0, h].T @ f, Kx @ v[0, h]) < 1e-12
+        assert abs(z_T[0, h] @ f - Kx.sum()) < 1e-10 * Kx.sum()
+
+
+def test_based_start_state_equals_prefix():
+    """Start (s0, z0) from a prefix == brute force over prefix + tokens."""
+    r = rng(5)
+    dp, dv, P, T = 3, 2, 20, 30
+    kp = r.standard_normal((1, 1, P, dp))
+    qp = r.standard_normal((1, 1, P, dp))
+    vp = r.standard_normal((1, 1, P, dv))
+    _, s0, z0 = oracle.prefill("based", qp, kp, vp)
+    q = r.standard_normal((1, 1, T, dp))
+    k = r.standard_normal((1, 1, T, dp))
+    v = r.standard_normal((1, 1, T, dv))
+    o, _, _ = oracle.prefill("based", q, k, v, S0=s0, z0=z0, eps=1e-6)
+    ref, _ = _based_bruteforce(q[0, 0], k[0, 0], v[0, 0], 1e-6, prefix=(kp[0, 0], vp[0, 0]))
+    assert rel(o[0, 0], ref) < 1e-12
+
+
+# ----------------------------------------------------------------------------- gated
+def test_gated_alpha_one_is_additive_bitwise():
+    r = rng(6)
+    B, H, T, dk, dv = 1, 2, 50, 6, 5
+    q, k, v = (r.standard_normal((B, H, T, d)) for d in (dk, dk, dv))
+    S0 = r.standard_normal((B, H, dv, dk))
+    ones = np.ones((B, H, T))
+    o1, S1, _ = oracle.prefill("gated", q, k, v, alpha=ones, beta=ones, S0=S0)
+    o2, S2, _ = oracle.prefill("additive", q, k, v, S0=S0)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+    o3, S3, _ = oracle.prefill("gated", q, k, v, alpha=ones, beta=None, S0=S0)
+    assert np.array_equal(o3, o2) and np.array_equal(S3, S2)
+
+
+def test_gated_closed_form():
+    """o_t = gamma_t S0 q_t + sum_{j<=t} (prod_{i=j+1..t} alpha_i) beta_j (k_j.q_t) v_j."""
+    r = rng(7)
+    T, dk, dv = 40, 5, 4
+    q, k, v, alpha, beta = gdn_like(r, 1, 1, T, dk, dv, normalize=False)
+    S0 = r.standard_normal((1, 1, dv, dk))
+    o, S_T, _ = oracle.prefill("gated", q, k, v, alpha=alpha, beta=beta, S0=S0)
+    a, b = alpha[0, 0], beta[0, 0]
+    ref = np.zeros((T, dv))
+    for t in range(T):
+        acc = np.prod(a[: t + 1]) * (S0[0, 0] @ q[0, 0, t])
+        for j in range(t + 1):
+            acc = acc + np.prod(a[j + 1: t + 1]) * b[j] * (k[0, 0, j] @ q[0, 0, t]) * v[0, 0, j]
+        ref[t] = acc
+    assert rel(o[0, 0], ref) < 1e-12
+    ST = np.prod(a) * S0[0, 0] + sum(np.prod(a[j + 1:]) * b[j] * np.outer(v[0, 0, j], k[0, 0, j])
+                                      for j in range(T))
+    assert rel(S_T[0, 0], ST) < 1e-12
+
+
+# ----------------------------------------------------------------------------- delta rule
+def test_delta_exact_overwrite():
+    """beta_t = 1 and k_t a standard basis vector e_i: S_t e_i = v_t exactly, for any
+    alpha and any previous state (read back with q_t = k_t)."""
+    r = rng(8)
+    T, dk, dv = 64, 8, 6
+    idx = r.integers(0, dk, T)
+    k = np.zeros((1, 1, T, dk))
+    k[0, 0, np.arange(T), idx] = 1.0
+    v = r.standard_normal((1, 1, T, dv))
+    alpha = r.uniform(0.05, 1.0, (1, 1, T))
+    beta = np.ones((1, 1, T))
+    S0 = r.standard_normal((1, 1, dv, dk)) * 3
+    o, _, _ = oracle.prefill("gated_delta", k, k, v, alpha=alpha, beta=beta, S0=S0)
+    assert np.array_equal(o, v)
+
+
+def test_delta_slot_memory():
+    """Keys from {e_i} with repeats, beta = 1: S_T e_i = (prod_{s > t_i} alpha_s) v_{t_i}
+    for the last write t_i to slot i, else (prod alpha) S0 e_i."""
+    r = rng(9)
+    T, dk, dv = 48, 10, 3
+    idx = r.integers(0, dk - 2, T)  # the last two slots are never written
+    k = np.zeros((1, 1, T, dk))
+    k[0, 0, np.arange(T), idx] = 1.0
+    q = r.standard_normal((1, 1, T, dk))
+    v = r.standard_normal((1, 1, T, dv))
+    alpha = r.uniform(0.5, 1.0, (1, 1, T))
+    S0 = r.standard_normal((1, 1, dv, dk))
+    _, S_T, _ = oracle.prefill("gated_delta", q, k, v, alpha=alpha, beta=np.ones((1, 1, T)), S0=S0)
+    a = alpha[0, 0]
+    for i in range(dk):
+        writes = np.nonzero(idx == i)[0]
+        if writes.size:
+            ti = writes[-1]
+            expect = np.prod(a[ti + 1:]) * v[0, 0, ti]
+        else:
+            expect = np.prod(a) * S0[0, 0, :, i]
+        assert np.allclose(S_T[0, 0, :, i], expect, rtol=1e-14, atol=1e-15)
+
+
+def test_delta_beta_zero_is_pure_decay():
+    r = rng(10)
+    T, dk, dv = 30, 6, 4
+    q, k, v, alpha, _ = gdn_like(r, 1, 1, T, dk, dv)
+    S0 = r.standard_normal((1, 1, dv, dk))
+    o, S_T, _ = oracle.prefill("gated_delta", q, k, v, alpha=alpha, beta=np.zeros((1, 1, T)), S0=S0)
+    g = np.cumprod(alpha[0, 0])
+    assert rel(S_T[0, 0], g[-1] * S0[0, 0]) < 1e-14
+    assert rel(o[0, 0], g[:, None] * (q[0, 0] @ S0[0, 0].T)) < 1e-13
+
+
+def test_delta_orthonormal_unrepeated_keys_equal_gated():
+    """alpha = 1, keys orthonormal and never repeated, S0 = 0: S_{t-1} k_t = 0, so the delta
+    rule reduces to the (beta-weighted) gated/additive write."""
+    r = rng(11)
+    dk = dv = 12
+    T = dk
+    Qm, _ = np.linalg.qr(r.standard_normal((dk, dk)))
+    k = Qm.T[None, None]  # rows orthonormal
+    q = r.standard_normal((1, 1, T, dk))
+    v = r.standard_normal((1, 1, T, dv))
+    beta = r.uniform(0.1, 1.0, (1, 1, T))
+    ones = np.ones((1, 1, T))
+    o1, S1, _ = oracle.prefill("gated_delta", q, k, v, alpha=ones, beta=beta)
+    o2, S2, _ = oracle.prefill("gated", q, k, v, alpha=ones, beta=beta)
+    assert rel(o1, o2) < 1e-13 and rel(S1, S2) < 1e-13
+
+
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta"])
+def test_rank1_form_matches_explicit_transition(variant):
+    """Row-wise rank-1 update == S_{t-1} A_t + beta_t v_t k_t^T with A_t built explicitly."""
+    r = rng(12)
+    T, dk, dv = 9, 4, 3
+    q, k, v, alpha, beta = gdn_like(r, 1, 1, T, dk, dv, normalize=False)
+    S0 = r.standard_normal((1, 1, dv, dk))
+    o, S_T, _ = oracle.prefill(variant, q, k, v, alpha=alpha, beta=beta, S0=S0)
+    ol, SL = oracle.literal(variant, q[0, 0], k[0, 0], v[0, 0], alpha[0, 0], beta[0, 0], S0[0, 0])
+    assert rel(o[0, 0], ol) < 1e-13 and rel(S_T[0, 0], SL) < 1e-13
+
+
+# ----------------------------------------------------------------------------- structure
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta"])
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+def test_chunked_derivation_matches_sequential(variant, C):
+    """The block algebra the kernels use (tests/models.py) equals the token recurrence."""
+    r = rng(13)
+    T, dk, dv = 203, 16, 12
+    q, k, v, alpha, beta = gdn_like(r, 1, 1, T, dk, dv)
+    S0 = r.standard_normal((1, 1, dv, dk)) * 0.5
+    o, S_T, _ = oracle.prefill(variant, q, k, v, alpha=alpha, beta=beta, S0=S0)
+    oc, Sc = models.chunked(variant, q[0, 0], k[0, 0], v[0, 0],
+                            None if variant == "additive" else alpha[0, 0],
+                            None if variant == "additive" else beta[0, 0], S0[0, 0], C)
+    assert rel(oc, o[0, 0]) < 1e-10 and rel(Sc, S_T[0, 0]) < 1e-10
+
+
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta"])
+def test_segment_scan_matches_sequential(variant):
+    """Per-segment affine maps + scan + rerun (the three-pass prefill) == recurrence."""
+    r = rng(14)
+    T, dk, dv, C = 64 * 7 + 13, 16, 8, 16
+    q, k, v, alpha, beta = gdn_like(r, 1, 1, T, dk, dv)
+    S0 = r.standard_normal((1, 1, dv, dk))
+    o, S_T, _ = oracle.prefill(variant, q, k, v, alpha=alpha, beta=beta, S0=S0)
+    os_, Ss = models.segmented(variant, q[0, 0], k[0, 0], v[0, 0],
+                               None if variant == "additive" else alpha[0, 0],
+                               None if variant == "additive" else beta[0, 0], S0[0, 0], C, 3)
+    assert rel(os_, o[0, 0]) < 1e-10 and rel(Ss, S_T[0, 0]) < 1e-10
+
+
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based"])
+def test_split_resume(variant):
+    """prefill(x[:a]) -> S_a; prefill(x[a:], S0=S_a) == prefill(x)."""
+    r = rng(15)
+    T, dk, dv, a = 90, 6, 5, 37
+    q, k, v, alpha, beta = gdn_like(r, 2, 2, T, dk, dv)
+    kw = dict(eps=1e-6)
+    o, S, z = oracle.prefill(variant, q, k, v, alpha, beta, **kw)
+    o1, S1, z1 = oracle.prefill(variant, q[:, :, :a], k[:, :, :a], v[:, :, :a], alpha[:, :, :a],
+                                beta[:, :, :a], **kw)
+    o2, S2, z2 = oracle.prefill(variant, q[:, :, a:], k[:, :, a:], v[:, :, a:], alpha[:, :, a:],
+                                beta[:, :, a:], S0=S1, z0=z1, **kw)
+    assert rel(np.concatenate([o1, o2], axis=2), o) < 1e-12
+    assert rel(S2, S) < 1e-12
+    if z is not None:
+        assert rel(z2, z) < 1e-12
+
+
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based"])
+def test_prefill_then_decode_equals_longer_prefill(variant):
+    r = rng(16)
+    T, n, dk, dv = 20, 5, 4, 3
+    q, k, v, alpha, beta = gdn_like(r, 1, 3, T + n, dk, dv)
+    o, S, z = oracle.prefill(variant, q, k, v, alpha, beta)
+    _, St, zt = oracle.prefill(variant, q[:, :, :T], k[:, :, :T], v[:, :, :T], alpha[:, :, :T],
+                               beta[:, :, :T])
+    St, zt = St[0], None if zt is None else zt[0]
+    for i in range(n):
+        t = T + i
+        od, St, zt = oracle.decode_step(variant, St, q[0, :, t], k[0, :, t], v[0, :, t],
+                                        alpha[0, :, t], beta[0, :, t], z=zt)
+        assert rel(od, o[0, :, t]) < 1e-12
+    assert rel(St, S[0]) < 1e-12
+
+
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta"])
+def test_linear_in_values_and_start_state(variant):
+    r = rng(17)
+    T, dk, dv = 33, 5, 4
+    q, k, v1, alpha, beta = gdn_like(r, 1, 1, T, dk, dv)
+    v2 = r.standard_normal(v1.shape)
+    S1, S2 = r.standard_normal((2, 1, 1, dv, dk))
+    c1, c2 = 0.7, -1.3
+    oa, Sa, _ = oracle.prefill(variant, q, k, v1, alpha, beta, S0=S1)
+    ob, Sb, _ = oracle.prefill(variant, q, k, v2, alpha, beta, S0=S2)
+    oc, Sc, _ = oracle.prefill(variant, q, k, c1 * v1 + c2 * v2, alpha, beta, S0=c1 * S1 + c2 * S2)
+    assert rel(oc, c1 * oa + c2 * ob) < 1e-12 and rel(Sc, c1 * Sa + c2 * Sb) < 1e-12
+
+
+@pytest.mark.parametrize("variant", ["gated_delta", "based"])
+def test_row_subset_matches_full(variant):
+    """The sampled-rows path (used for long-sequence parity) returns the same numbers."""
+    r = rng(18)
+    T, dk, dv = 25, 4, 6
+    q, k, v, alpha, beta = gdn_like(r, 2, 2, T, dk, dv)
+    rows = [5, 0, 3]
+    o, S, z = oracle.prefill(variant, q, k, v, alpha, beta)
+    os_, Ss, zs = oracle.prefill(variant, q, k, v, alpha, beta, rows=rows)
+    assert np.array_equal(os_, o[..., rows])
+    if variant == "based":
+        assert np.array_equal(Ss, S[..., rows]) and np.array_equal(zs, z)
+    else:
+        assert np.array_equal(Ss, S[:, :, rows, :])
+
+
+def test_state_bytes_match_printed_accounting():
+    J = GOLDEN["notebank_gdn_channels_J"]["value"]
+    d = GOLDEN["notebank_gdn_dk_dv"]["value"]
+    assert J == GOLDEN["notebank_gdn_layers"]["value"] * GOLDEN["notebank_gdn_heads_per_layer"]["value"]
+    assert 4 * J * d * d == GOLDEN["notebank_fp32_state_MiB"]["value"] * 2 ** 20
+    _, S, _ = oracle.prefill("gated_delta", *gdn_like(rng(19), 1, 1, 2, d, d))
+    assert S[0, 0].size * 4 * J == 48 * 2 ** 20
+    _, s, z = oracle.prefill("based", *gdn_like(rng(20), 1, 1, 2, 16, 64)[:3])
+    assert s[0, 0].size + z[0, 0].size == 273 * (64 + 1)
