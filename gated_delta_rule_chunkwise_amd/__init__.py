@@ -1,0 +1,152 @@
+"""Python binding of libla (MI355X / gfx950 linear-attention recurrence).
+
+Thin argument marshalling only: torch tensors provide device memory and the stream;
+every step of the computation runs in the HIP kernels behind the C ABI of
+``include/la.h``.  There is no CPU fallback -- if ``libla.so`` is missing or cannot be
+loaded, every call raises.
+
+    o, S_T, z_T = prefill("gated_delta", q, k, v, alpha, beta, S0=None)
+    o, S, z     = decode_step("gated_delta", S, q, k, v, alpha, beta, S_out=S)  # in place
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+ADDITIVE, BASED, GATED, GATED_DELTA = 0, 1, 2, 3
+VARIANTS = {"additive": ADDITIVE, "based": BASED, "gated": GATED, "gated_delta": GATED_DELTA}
+F32, BF16 = 0, 1
+STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_INVALID", -3: "LA_ERR_UNSUPPORTED",
+          -4: "LA_ERR_ALIGN", -5: "LA_ERR_WORKSPACE", -6: "LA_ERR_ALIAS", -7: "LA_ERR_HIP"}
+EXPORTS = ("la_abi_version", "la_status_string", "la_prefill_workspace_size", "la_prefill",
+           "la_decode_step")
+
+LIB_PATH = Path(__file__).resolve().parent / "libla.so"
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+def load(path: str | None = None):
+    """Load libla.so (raises OSError if it is missing or broken)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise OSError(f"{p} not found: build it with `python -m gated_delta_rule_chunkwise_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.la_abi_version.restype = i32
+    lib.la_status_string.argtypes = [i32]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i64, i32, i32,
+                                              ctypes.POINTER(ctypes.c_size_t)]
+    lib.la_prefill_workspace_size.restype = i32
+    lib.la_prefill.argtypes = [i32, i32, i32, i32, i64, i32, i32, f32] + [vp] * 11 + \
+        [ctypes.c_size_t, vp]
+    lib.la_prefill.restype = i32
+    lib.la_decode_step.argtypes = [i32, i32, i32, i32, i32, f32] + [vp] * 10 + [vp]
+    lib.la_decode_step.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _var(v) -> int:
+    return VARIANTS[v] if isinstance(v, str) else int(v)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def feature_dim(dp: int) -> int:
+    return 1 + dp + dp * dp
+
+
+def workspace_size(variant, dtype, B, H, T, d_k, d_v) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().la_prefill_workspace_size(_var(variant), dtype, B, H, T, d_k, d_v, ctypes.byref(n))
+    if st != 0:
+        raise LAError(st, "la_prefill_workspace_size")
+    return int(n.value)
+
+
+def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6, want_state=True,
+            o=None, S_T=None, z_T=None, workspace=None, stream=None):
+    """Run la_prefill.  q, k [B,H,T,d_k]; v [B,H,T,d_v]; alpha, beta [B,H,T] (same dtype as q);
+    S0 [B,H,d_v,d_k] fp32 (BASED: s0 [B,H,D,d_v], z0 [B,H,D]).  Returns (o, S_T, z_T)."""
+    var = _var(variant)
+    lib = load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype(q)
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    if want_state and S_T is None:
+        if var == BASED:
+            D = feature_dim(dk)
+            S_T = torch.empty((B, H, D, dv), dtype=torch.float32, device=dev)
+            z_T = torch.empty((B, H, D), dtype=torch.float32, device=dev) if z_T is None else z_T
+        else:
+            S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    ws_n = workspace_size(var, dt, B, H, T, dk, dv)
+    if ws_n and workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    st = lib.la_prefill(var, dt, B, H, T, dk, dv, float(eps), _p(q), _p(k), _p(v), _p(alpha),
+                        _p(beta), _p(S0), _p(z0), _p(o), _p(S_T), _p(z_T), _p(workspace),
+                        0 if workspace is None else workspace.numel() * workspace.element_size(),
+                        _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_prefill")
+    return o, S_T, z_T
+
+
+def decode_step(variant, S, q, k, v, alpha=None, beta=None, z=None, eps=1e-6, S_out=None,
+                z_out=None, o=None, stream=None):
+    """Run la_decode_step on N states.  S [N,d_v,d_k] (BASED: s [N,D,d_v], z [N,D]); q,k [N,d_k];
+    v [N,d_v]; alpha, beta [N].  S_out=S (and z_out=z) updates in place.  Returns (o, S_out, z_out)."""
+    var = _var(variant)
+    lib = load()
+    N, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype(q)
+    if o is None:
+        o = torch.empty((N, dv), dtype=q.dtype, device=q.device)
+    if S_out is None:
+        S_out = torch.empty_like(S)
+    if var == BASED and z_out is None:
+        z_out = torch.empty_like(z)
+    st = lib.la_decode_step(var, dt, N, dk, dv, float(eps), _p(S), _p(z), _p(S_out), _p(z_out),
+                            _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(o), _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_decode_step")
+    return o, S_out, z_out

@@ -1,0 +1,226 @@
+// la_abi.hip -- the C ABI declared in include/la.h: argument validation, aliasing and
+// alignment checks, workspace sizing and dispatch to the kernels.  Validation always
+// completes before anything is enqueued, so a rejected call touches no memory.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/la.h"
+#include "la_launch.h"
+
+namespace la {
+
+__global__ void copy_or_zero_kernel(const float *__restrict__ src, float *__restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t launch_copy_or_zero(const float *src, float *dst, size_t n, hipStream_t s) {
+  if (n == 0 || src == dst) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+namespace {
+
+struct Range {
+  const void *p;
+  size_t n;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+bool misaligned(const void *p, uintptr_t align = 16) { return p && ((uintptr_t)p & (align - 1)) != 0; }
+
+int based_D(int dp) { return 1 + dp + dp * dp; }
+
+// Shared shape checks for prefill; returns LA_OK or an error.
+int check_prefill_shape(int variant, int dtype, int B, int H, int64_t T, int dk, int dv) {
+  if (variant < LA_ADDITIVE || variant > LA_GATED_DELTA) return LA_ERR_INVALID;
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
+  if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0) return LA_ERR_INVALID;
+  if ((int64_t)B * H > (int64_t)INT32_MAX / 4) return LA_ERR_UNSUPPORTED;
+  if (variant == LA_BASED) {
+    if (dk != 16 || dv != 64) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+  }
+  if (dtype == LA_BF16) {
+    if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64))) return LA_ERR_UNSUPPORTED;
+  } else {
+    if (dk != 64 && dk != 128 && dk != 256) return LA_ERR_UNSUPPORTED;
+  }
+  return LA_OK;
+}
+
+size_t prefill_ws(int variant, int dtype, int B, int H, int64_t T, int dk, int dv) {
+  if (dtype != LA_BF16 || T == 0) return 0;
+  if (variant == LA_BASED) return based_chunk_workspace_bytes(B, H, T);
+  return chunk_workspace_bytes(variant, B, H, T, dk, dv);
+}
+
+}  // namespace
+}  // namespace la
+
+using namespace la;
+
+extern "C" {
+
+int la_abi_version(void) { return 1; }
+
+const char *la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL: return "LA_ERR_NULL: a required pointer is NULL";
+    case LA_ERR_INVALID: return "LA_ERR_INVALID: invalid argument";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: shape or dtype not supported";
+    case LA_ERR_ALIGN: return "LA_ERR_ALIGN: pointer not 16-byte aligned";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
+    case LA_ERR_ALIAS: return "LA_ERR_ALIAS: buffers overlap";
+    case LA_ERR_HIP: return "LA_ERR_HIP: a HIP launch failed";
+    default: return "unknown la_status";
+  }
+}
+
+int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int64_t seq_len,
+                              int d_k, int d_v, size_t *bytes) {
+  if (!bytes) return LA_ERR_NULL;
+  const int st = check_prefill_shape(variant, dtype, batch, heads, seq_len, d_k, d_v);
+  if (st != LA_OK) return st;
+  *bytes = prefill_ws(variant, dtype, batch, heads, seq_len, d_k, d_v);
+  return LA_OK;
+}
+
+int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k, int d_v,
+               float eps, const void *q, const void *k, const void *v, const void *alpha,
+               const void *beta, const float *S0, const float *z0, void *o, float *S_T,
+               float *z_T, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_prefill_shape(variant, dtype, batch, heads, seq_len, d_k, d_v);
+  if (st != LA_OK) return st;
+  const int B = batch, H = heads;
+  const int64_t T = seq_len;
+  const bool based = variant == LA_BASED;
+  // variant-specific pointer rules
+  if (variant == LA_ADDITIVE || based) {
+    if (alpha || beta) return LA_ERR_INVALID;
+  } else if (variant == LA_GATED) {
+    if (!alpha && T > 0) return LA_ERR_NULL;
+  } else {
+    if ((!alpha || !beta) && T > 0) return LA_ERR_NULL;
+  }
+  if (based) {
+    if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_INVALID;
+    if ((S_T == nullptr) != (z_T == nullptr)) return LA_ERR_INVALID;
+  } else if (z0 || z_T) {
+    return LA_ERR_INVALID;
+  }
+  if (T > 0 && (!q || !k || !v || !o)) return LA_ERR_NULL;
+  const size_t es = dtype == LA_F32 ? 4 : 2;
+  // q, k, v, o and the states are moved in 16-byte vectors; alpha and beta per element
+  const void *ptrs[] = {q, k, v, S0, z0, o, S_T, z_T, workspace};
+  for (const void *p : ptrs)
+    if (misaligned(p)) return LA_ERR_ALIGN;
+  if (misaligned(alpha, es) || misaligned(beta, es)) return LA_ERR_ALIGN;
+
+  const size_t BH = (size_t)B * H;
+  const size_t D = based ? (size_t)based_D(d_k) : 0;
+  const size_t state_n = based ? BH * D * d_v : BH * d_v * d_k;
+  const Range rq{q, BH * T * d_k * es}, rk{k, BH * T * d_k * es}, rv{v, BH * T * d_v * es};
+  const Range ra{alpha, BH * T * es}, rb{beta, BH * T * es};
+  const Range rS0{S0, state_n * 4}, rz0{z0, BH * D * 4};
+  const Range ro{o, BH * T * d_v * es}, rST{S_T, state_n * 4}, rzT{z_T, BH * D * 4};
+  const size_t need_ws = prefill_ws(variant, dtype, B, H, T, d_k, d_v);
+  if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return LA_ERR_WORKSPACE;
+  const Range rw{workspace, need_ws};
+  const Range outs[] = {ro, rST, rzT, rw};
+  const Range ins[] = {rq, rk, rv, ra, rb, rS0, rz0};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return LA_ERR_ALIAS;
+    for (int j = 0; j < 7; ++j) {
+      const bool same_state = (i == 1 && j == 5 && S_T == S0) || (i == 2 && j == 6 && z_T == z0);
+      if (!same_state && overlap(outs[i], ins[j])) return LA_ERR_ALIAS;
+    }
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T == 0) {  // empty sequence: the end state is the start state
+    if (S_T) e = launch_copy_or_zero(S0, S_T, state_n, s);
+    if (e == hipSuccess && z_T) e = launch_copy_or_zero(z0, z_T, BH * D, s);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+  }
+  if (based) {
+    if (dtype == LA_BF16)
+      e = launch_based_chunk_prefill(B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, workspace, s);
+    else
+      e = launch_recurrent_based(dtype, B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, s);
+  } else if (dtype == LA_BF16) {
+    e = launch_chunk_prefill(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, workspace, s);
+  } else {
+    e = launch_recurrent_rows(variant, dtype, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+  }
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, const float *S_in,
+                   const float *z_in, float *S_out, float *z_out, const void *q, const void *k,
+                   const void *v, const void *alpha, const void *beta, void *o, void *stream) {
+  if (variant < LA_ADDITIVE || variant > LA_GATED_DELTA) return LA_ERR_INVALID;
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
+  if (n <= 0 || d_k <= 0 || d_v <= 0) return LA_ERR_INVALID;
+  const bool based = variant == LA_BASED;
+  if (based) {
+    if (d_k != 16 || d_v != 64) return LA_ERR_UNSUPPORTED;
+  } else if (d_k != 64 && d_k != 128 && d_k != 256) {
+    return LA_ERR_UNSUPPORTED;
+  }
+  if (variant == LA_ADDITIVE || based) {
+    if (alpha || beta) return LA_ERR_INVALID;
+  } else if (variant == LA_GATED) {
+    if (!alpha) return LA_ERR_NULL;
+  } else if (!alpha || !beta) {
+    return LA_ERR_NULL;
+  }
+  if (!S_in || !S_out || !q || !k || !v || !o) return LA_ERR_NULL;
+  if (based && (!z_in || !z_out)) return LA_ERR_NULL;
+  if (!based && (z_in || z_out)) return LA_ERR_INVALID;
+  const size_t es = dtype == LA_F32 ? 4 : 2;
+  // states are moved in 16-byte vectors; the per-state token vectors element by element
+  const void *sp[] = {S_in, z_in, S_out, z_out};
+  for (const void *p : sp)
+    if (misaligned(p)) return LA_ERR_ALIGN;
+  const void *tp[] = {q, k, v, alpha, beta, o};
+  for (const void *p : tp)
+    if (misaligned(p, es)) return LA_ERR_ALIGN;
+  const size_t D = based ? (size_t)based_D(d_k) : 0;
+  const size_t state_n = based ? (size_t)n * D * d_v : (size_t)n * d_v * d_k;
+  const Range rSi{S_in, state_n * 4}, rzi{z_in, (size_t)n * D * 4};
+  const Range rSo{S_out, state_n * 4}, rzo{z_out, (size_t)n * D * 4};
+  const Range rq{q, (size_t)n * d_k * es}, rk{k, (size_t)n * d_k * es}, rv{v, (size_t)n * d_v * es};
+  const Range ra{alpha, (size_t)n * es}, rb{beta, (size_t)n * es}, ro{o, (size_t)n * d_v * es};
+  const Range outs[] = {rSo, rzo, ro};
+  const Range ins[] = {rSi, rzi, rq, rk, rv, ra, rb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return LA_ERR_ALIAS;
+    for (int j = 0; j < 7; ++j) {
+      const bool same_state = (i == 0 && j == 0 && S_out == S_in) || (i == 1 && j == 1 && z_out == z_in);
+      if (!same_state && overlap(outs[i], ins[j])) return LA_ERR_ALIAS;
+    }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (based)
+    e = launch_decode_based(dtype, n, eps, S_in, z_in, S_out, z_out, q, k, v, o, s);
+  else
+    e = launch_decode_rows(variant, dtype, n, d_k, d_v, S_in, S_out, q, k, v, alpha, beta, o, s);
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// la_launch.h -- private host-side launchers implemented by the kernel files.  All
+// arguments have been validated by the ABI layer (la_abi.hip) before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+enum { V_ADDITIVE = 0, V_BASED = 1, V_GATED = 2, V_GATED_DELTA = 3 };
+enum { T_F32 = 0, T_BF16 = 1 };
+
+// decode.hip
+hipError_t launch_decode_rows(int variant, int dtype, int n, int d_k, int d_v, const float *S_in,
+                              float *S_out, const void *q, const void *k, const void *v,
+                              const void *alpha, const void *beta, void *o, hipStream_t s);
+hipError_t launch_decode_based(int dtype, int n, float eps, const float *S_in, const float *z_in,
+                               float *S_out, float *z_out, const void *q, const void *k,
+                               const void *v, void *o, hipStream_t s);
+
+// recurrent.hip (token-recurrent prefill; fp32 path)
+hipError_t launch_recurrent_rows(int variant, int dtype, int B, int H, int64_t T, int d_k, int d_v,
+                                 const void *q, const void *k, const void *v, const void *alpha,
+                                 const void *beta, const float *S0, void *o, float *S_T,
+                                 hipStream_t s);
+hipError_t launch_recurrent_based(int dtype, int B, int H, int64_t T, float eps, const void *q,
+                                  const void *k, const void *v, const float *s0, const float *z0,
+                                  void *o, float *s_T, float *z_T, hipStream_t s);
+
+// chunk.hip (chunkwise bf16 prefill for ADDITIVE / GATED / GATED_DELTA)
+size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v);
+hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, int d_v,
+                                const void *q, const void *k, const void *v, const void *alpha,
+                                const void *beta, const float *S0, void *o, float *S_T,
+                                void *workspace, hipStream_t s);
+
+// based_chunk.hip (chunkwise bf16 BASED prefill)
+size_t based_chunk_workspace_bytes(int B, int H, int64_t T);
+hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const void *q,
+                                      const void *k, const void *v, const float *s0,
+                                      const float *z0, void *o, float *s_T, float *z_T,
+                                      void *workspace, hipStream_t s);
+
+// util (la_abi.hip): copy or zero-fill n floats with a kernel (capture-safe, no memset nodes)
+hipError_t launch_copy_or_zero(const float *src, float *dst, size_t n, hipStream_t s);
+
+}  // namespace la

@@ -1,0 +1,252 @@
+// recurrent.hip -- token-recurrent prefill in fp32 arithmetic.
+//
+// This is the path for fp32 inputs, whose 1e-4 accuracy target rules out bf16 matrix
+// operands.  It walks Eq. (1) of "History Replays Itself" (Sec. 2) token by token, one
+// state row per group of lanes: because A_t multiplies S from the right, every row s_r
+// of S evolves on its own, so rows are spread over waves and workgroups with no
+// communication.  Per token and row, with r = s_r.k_t, p = s_r.q_t (old row):
+//   GATED_DELTA  coef = beta_t (v_t[r] - alpha_t r),  GATED coef = beta_t v_t[r],
+//   ADDITIVE     coef = v_t[r] (alpha = 1);
+//   s_r <- alpha_t s_r + coef k_t,   o_t[r] = alpha_t p + coef (k_t.q_t)
+// One reduction round (three partial sums over the 8 lanes that hold a row) serves the
+// whole token.  Tokens are staged through LDS in tiles; outputs are gathered in LDS and
+// written back a tile at a time.
+//
+// BASED: columns c of s are independent given the shared normaliser, so one
+// workgroup per (b, h) keeps all of s in registers (value column per lane, features
+// spread over the four waves) and reduces numerator and denominator partials per tile.
+#include "la_device.h"
+#include "la_launch.h"
+
+namespace la {
+
+template <int DK, int VAR, typename T>
+__global__ __launch_bounds__(64) void recurrent_rows_kernel(int64_t T_len, int dv, int has_beta,
+                                                            const T *__restrict__ q,
+                                                            const T *__restrict__ k,
+                                                            const T *__restrict__ v,
+                                                            const T *__restrict__ alpha,
+                                                            const T *__restrict__ beta,
+                                                            const float *__restrict__ S0,
+                                                            T *__restrict__ o, float *S_T) {
+  constexpr int CPL = DK / 8;  // columns per lane
+  constexpr int NG = CPL / 4;  // float4 groups per lane
+  constexpr int TT = DK <= 128 ? 32 : 16;
+  __shared__ float4 ks[TT][DK / 4];
+  __shared__ float4 qs[TT][DK / 4];
+  __shared__ float vs[TT][8];
+  __shared__ float as_[TT], bs_[TT];
+  __shared__ float os_[TT][8];
+  const int lane = threadIdx.x;
+  const int rw = lane >> 3, cgp = lane & 7;
+  const int row0 = blockIdx.x * 8;
+  const int row = row0 + rw;
+  const int H = gridDim.y;
+  const size_t bh = (size_t)blockIdx.z * H + blockIdx.y;
+  const bool live = row < dv;
+
+  float s[CPL];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 4 * (cgp + 8 * g) + j;
+      s[4 * g + j] = (S0 && live) ? S0[(bh * dv + row) * DK + c] : 0.0f;
+    }
+
+  const T *qb = q + bh * (size_t)T_len * DK;
+  const T *kb = k + bh * (size_t)T_len * DK;
+  for (int64_t t0 = 0; t0 < T_len; t0 += TT) {
+    const int nt = (int)((T_len - t0) < TT ? (T_len - t0) : TT);
+    for (int i = lane; i < nt * (DK / 4); i += 64) {
+      const int tt = i / (DK / 4), c4 = i % (DK / 4);
+      const size_t off = (size_t)(t0 + tt) * DK + 4 * c4;
+      ks[tt][c4] = make_float4(io<T>::ld(kb, off), io<T>::ld(kb, off + 1), io<T>::ld(kb, off + 2),
+                               io<T>::ld(kb, off + 3));
+      qs[tt][c4] = make_float4(io<T>::ld(qb, off), io<T>::ld(qb, off + 1), io<T>::ld(qb, off + 2),
+                               io<T>::ld(qb, off + 3));
+    }
+    for (int i = lane; i < nt * 8; i += 64) {
+      const int tt = i >> 3, rr = i & 7;
+      vs[tt][rr] = (row0 + rr < dv) ? io<T>::ld(v, (bh * T_len + t0 + tt) * dv + row0 + rr) : 0.0f;
+    }
+    for (int i = lane; i < nt; i += 64) {
+      as_[i] = (VAR == V_ADDITIVE) ? 1.0f : io<T>::ld(alpha, bh * T_len + t0 + i);
+      bs_[i] = (VAR == V_GATED_DELTA || (VAR == V_GATED && has_beta))
+                   ? io<T>::ld(beta, bh * T_len + t0 + i) : 1.0f;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      float kv[CPL], qv[CPL];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float4 a4 = ks[tt][cgp + 8 * g], b4 = qs[tt][cgp + 8 * g];
+        kv[4 * g] = a4.x; kv[4 * g + 1] = a4.y; kv[4 * g + 2] = a4.z; kv[4 * g + 3] = a4.w;
+        qv[4 * g] = b4.x; qv[4 * g + 1] = b4.y; qv[4 * g + 2] = b4.z; qv[4 * g + 3] = b4.w;
+      }
+      float pr = 0.f, pp = 0.f, pkq = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        pr += s[j] * kv[j];
+        pp += s[j] * qv[j];
+        pkq += kv[j] * qv[j];
+      }
+      pr = group_sum<8>(pr);
+      pp = group_sum<8>(pp);
+      pkq = group_sum<8>(pkq);
+      const float a = as_[tt], b = bs_[tt], vt = vs[tt][rw];
+      const float coef = (VAR == V_GATED_DELTA) ? b * (vt - a * pr) : b * vt;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) s[j] = a * s[j] + coef * kv[j];
+      if (cgp == 0) os_[tt][rw] = a * pp + coef * pkq;
+    }
+    __syncthreads();
+    for (int i = lane; i < nt * 8; i += 64) {
+      const int tt = i >> 3, rr = i & 7;
+      if (row0 + rr < dv) io<T>::st(o, (bh * T_len + t0 + tt) * dv + row0 + rr, os_[tt][rr]);
+    }
+    __syncthreads();
+  }
+  if (S_T && live) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S_T[(bh * dv + row) * DK + 4 * (cgp + 8 * g) + j] = s[4 * g + j];
+  }
+}
+
+// BASED, d' = 16, d_v = 64, D = 273.  Thread t: value column c = t % 64, features
+// f = t/64 + 4 i (i < 69).  z is kept per feature by every lane of the owning wave.
+template <typename T>
+__global__ __launch_bounds__(256) void recurrent_based_kernel(int64_t T_len, float eps,
+                                                              const T *__restrict__ q,
+                                                              const T *__restrict__ k,
+                                                              const T *__restrict__ v,
+                                                              const float *__restrict__ s0,
+                                                              const float *__restrict__ z0,
+                                                              T *__restrict__ o, float *s_T,
+                                                              float *z_T) {
+  constexpr int DP = 16, DV = 64, D = 1 + DP + DP * DP, NF = (D + 3) / 4, TT = 16;
+  __shared__ float phk[TT][D + 3], phq[TT][D + 3];
+  __shared__ float vs[TT][DV];
+  __shared__ float part_num[4][TT][DV];
+  __shared__ float part_den[4][TT];
+  const int tid = threadIdx.x, c = tid & 63, fb = tid >> 6;
+  const size_t bh = (size_t)blockIdx.x;
+  float s[NF], z[NF];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int f = fb + 4 * i;
+    s[i] = (s0 && f < D) ? s0[(bh * D + f) * DV + c] : 0.0f;
+    z[i] = (z0 && f < D) ? z0[bh * D + f] : 0.0f;
+  }
+  const float rs2 = 0.70710678118654752f;
+  for (int64_t t0 = 0; t0 < T_len; t0 += TT) {
+    const int nt = (int)((T_len - t0) < TT ? (T_len - t0) : TT);
+    for (int i = tid; i < nt * D; i += 256) {
+      const int tt = i / D, f = i % D;
+      const size_t base = (bh * T_len + t0 + tt) * DP;
+      float fk, fq;
+      if (f == 0) { fk = 1.0f; fq = 1.0f; }
+      else if (f <= DP) { fk = io<T>::ld(k, base + f - 1); fq = io<T>::ld(q, base + f - 1); }
+      else {
+        const int a = (f - 1 - DP) >> 4, b = (f - 1 - DP) & 15;
+        fk = io<T>::ld(k, base + a) * io<T>::ld(k, base + b) * rs2;
+        fq = io<T>::ld(q, base + a) * io<T>::ld(q, base + b) * rs2;
+      }
+      phk[tt][f] = fk;
+      phq[tt][f] = fq;
+    }
+    for (int i = tid; i < nt * DV; i += 256)
+      vs[i / DV][i % DV] = io<T>::ld(v, (bh * T_len + t0) * DV + i);
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      const float vc = vs[tt][c];
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        const int f = fb + 4 * i;
+        if (f < D) {
+          const float pk = phk[tt][f], pq = phq[tt][f];
+          s[i] += pk * vc;
+          z[i] += pk;
+          num += pq * s[i];
+          den += pq * z[i];
+        }
+      }
+      part_num[fb][tt][c] = num;
+      if (c == 0) part_den[fb][tt] = den;
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * DV; i += 256) {
+      const int tt = i / DV, cc = i % DV;
+      const float num = (part_num[0][tt][cc] + part_num[1][tt][cc]) +
+                        (part_num[2][tt][cc] + part_num[3][tt][cc]);
+      const float den = (part_den[0][tt] + part_den[1][tt]) + (part_den[2][tt] + part_den[3][tt]);
+      io<T>::st(o, (bh * T_len + t0 + tt) * DV + cc, num / (den + eps));
+    }
+    __syncthreads();
+  }
+  if (s_T) {
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      const int f = fb + 4 * i;
+      if (f < D) {
+        s_T[(bh * D + f) * DV + c] = s[i];
+        if (c == 0) z_T[bh * D + f] = z[i];
+      }
+    }
+  }
+}
+
+template <int DK, typename T>
+static hipError_t go_rec(int variant, int B, int H, int64_t Tn, int dv, const void *q, const void *k,
+                         const void *v, const void *alpha, const void *beta, const float *S0, void *o,
+                         float *S_T, hipStream_t s) {
+  dim3 grid((dv + 7) / 8, H, B);
+  const int hb = beta != nullptr;
+#define LA_REC(VAR)                                                                              \
+  hipLaunchKernelGGL((recurrent_rows_kernel<DK, VAR, T>), grid, dim3(64), 0, s, Tn, dv, hb,      \
+                     (const T *)q, (const T *)k, (const T *)v, (const T *)alpha, (const T *)beta, \
+                     S0, (T *)o, S_T)
+  if (variant == V_ADDITIVE) LA_REC(V_ADDITIVE);
+  else if (variant == V_GATED) LA_REC(V_GATED);
+  else LA_REC(V_GATED_DELTA);
+#undef LA_REC
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t go_rec_dk(int variant, int B, int H, int64_t Tn, int dk, int dv, const void *q,
+                            const void *k, const void *v, const void *alpha, const void *beta,
+                            const float *S0, void *o, float *S_T, hipStream_t s) {
+  if (dk == 64) return go_rec<64, T>(variant, B, H, Tn, dv, q, k, v, alpha, beta, S0, o, S_T, s);
+  if (dk == 128) return go_rec<128, T>(variant, B, H, Tn, dv, q, k, v, alpha, beta, S0, o, S_T, s);
+  return go_rec<256, T>(variant, B, H, Tn, dv, q, k, v, alpha, beta, S0, o, S_T, s);
+}
+
+hipError_t launch_recurrent_rows(int variant, int dtype, int B, int H, int64_t T, int d_k, int d_v,
+                                 const void *q, const void *k, const void *v, const void *alpha,
+                                 const void *beta, const float *S0, void *o, float *S_T,
+                                 hipStream_t s) {
+  if (dtype == T_BF16)
+    return go_rec_dk<bf16_t>(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+  return go_rec_dk<float>(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+}
+
+hipError_t launch_recurrent_based(int dtype, int B, int H, int64_t T, float eps, const void *q,
+                                  const void *k, const void *v, const float *s0, const float *z0,
+                                  void *o, float *s_T, float *z_T, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)B * H));
+  if (dtype == T_BF16)
+    hipLaunchKernelGGL(recurrent_based_kernel<bf16_t>, grid, dim3(256), 0, s, T, eps,
+                       (const bf16_t *)q, (const bf16_t *)k, (const bf16_t *)v, s0, z0, (bf16_t *)o,
+                       s_T, z_T);
+  else
+    hipLaunchKernelGGL(recurrent_based_kernel<float>, grid, dim3(256), 0, s, T, eps,
+                       (const float *)q, (const float *)k, (const float *)v, s0, z0, (float *)o, s_T,
+                       z_T);
+  return hipGetLastError();
+}
+
+}  // namespace la

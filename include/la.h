@@ -1,0 +1,153 @@
+/*
+ * la.h -- C ABI of the MI355X (gfx950) linear-attention recurrence library (libla.so).
+ *
+ * The library computes, for every (batch b, head h) slice independently,
+ *
+ *     S_t = S_{t-1} A_t + beta_t v_t k_t^T ,        o_t = S_t q_t
+ *
+ * ("History Replays Itself: Unleashing Long-Context Capability in Linear Attention",
+ * Sec. 2 Preliminary, Eq. (1); one layer, one head; output gates and normalisation are
+ * outside the recurrence there and outside this library).  S_t is d_v x d_k, A_t acts
+ * on the right, and o_t reads the state after token t's write.  Variants:
+ *
+ *   LA_ADDITIVE      A_t = I, beta_t = 1                 (same passage, additive case)
+ *   LA_GATED         A_t = alpha_t I                      (scalar-gated state)
+ *   LA_GATED_DELTA   A_t = alpha_t (I - beta_t k_t k_t^T) (gated delta rule)
+ *   LA_BASED         second-order Taylor linear attention with normaliser
+ *                    ("Simple linear attention language models balance the
+ *                    recall-throughput tradeoff", reading notes Sec. 2.2 and 2.3, paper
+ *                    Eqs. (1)-(4)):  phi(x) = [1, x, vec(x x^T)/sqrt(2)],
+ *                    s_t = s_{t-1} + phi(k_t) v_t^T, z_t = z_{t-1} + phi(k_t),
+ *                    o_t = s_t^T phi(q_t) / (z_t^T phi(q_t) + eps).
+ *                    No input scaling is applied: callers that want the x/d'^(1/4)
+ *                    scaling of the paper's listing pre-scale q and k.
+ *
+ * Layouts (row-major, last index fastest; every pointer is DEVICE memory):
+ *   q, k      [B][H][T][d_k]        (BASED: d_k = d', the projected q/k width)
+ *   v, o      [B][H][T][d_v]
+ *   alpha,beta[B][H][T]             decay alpha_t in (0,1], write strength beta_t
+ *   S         [B][H][d_v][d_k] fp32 (ADDITIVE, GATED, GATED_DELTA)
+ *   s         [B][H][D][d_v]   fp32, z [B][H][D] fp32 (BASED, D = 1 + d' + d'^2,
+ *             feature order [1, x_0..x_{d'-1}, x_i x_j / sqrt 2 at 1 + d' + i d' + j])
+ *   Decode drops the T axis and replaces [B][H] by N independent states.
+ * q, k, v, alpha, beta and o share one element type (LA_F32 or LA_BF16); states are
+ * always fp32; all accumulation is fp32.  o is rounded to nearest-even on store.
+ *
+ * Inputs per variant (anything else returns LA_ERR_INVALID):
+ *   ADDITIVE      alpha and beta must be NULL.
+ *   GATED         alpha required; beta == NULL means beta_t = 1.
+ *   GATED_DELTA   alpha and beta required.
+ *   BASED         alpha and beta must be NULL; z pointers are required wherever the
+ *                 corresponding s pointer is given.
+ * Preconditions that are not checked: alpha_t in (0, 1] (outside it results are
+ * unspecified), finite inputs (NaN/Inf propagate).
+ *
+ * Ownership and threading: the caller owns every buffer, including the workspace.
+ * The library allocates no device memory, keeps no per-call global state, and only
+ * enqueues work on `stream` (a hipStream_t; NULL = the null stream).  Calls are
+ * asynchronous: buffers must stay alive until the stream has passed them.  Calls on
+ * distinct streams are independent.  Results are bitwise deterministic run to run.
+ *
+ * Alignment: states (S, s, z), the workspace, and -- for la_prefill -- q, k, v and o must
+ * be 16-byte aligned; every other pointer must be aligned to its element size.
+ *
+ * Errors: arguments are validated before anything is launched; a negative la_status
+ * is returned and no memory is touched.  LA_ERR_HIP means a launch failed.  Faults
+ * inside kernels surface, as HIP reports them, at the caller's next synchronisation.
+ * Nothing crosses the ABI as an exception and nothing is printed.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LA_ADDITIVE = 0, LA_BASED = 1, LA_GATED = 2, LA_GATED_DELTA = 3 };
+enum { LA_F32 = 0, LA_BF16 = 1 };
+
+enum {
+  LA_OK = 0,
+  LA_ERR_NULL = -1,        /* a required pointer is NULL                               */
+  LA_ERR_INVALID = -2,     /* bad variant/dtype, non-positive sizes, forbidden pointer */
+  LA_ERR_UNSUPPORTED = -3, /* valid but not implemented (d_k / d_v / dtype combination)*/
+  LA_ERR_ALIGN = -4,       /* a pointer is misaligned (see the alignment rules above)  */
+  LA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than la_prefill_workspace_size */
+  LA_ERR_ALIAS = -6,       /* two buffers overlap where that is not allowed            */
+  LA_ERR_HIP = -7          /* a HIP launch failed                                      */
+};
+
+/* Version of this ABI (bumped on any incompatible change). */
+int la_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *la_status_string(int status);
+
+/*
+ * Workspace that la_prefill needs for this problem, in bytes (0 is possible).  The
+ * workspace holds per-segment fp32 state maps of the chunked prefill (see la_prefill).
+ * Returns LA_OK and writes *bytes, or the same validation error la_prefill would give.
+ */
+int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int64_t seq_len,
+                              int d_k, int d_v, size_t *bytes);
+
+/*
+ * la_prefill -- run the recurrence over T = seq_len tokens for B x H slices.
+ *
+ *   S0 / z0  start state (NULL = zero state, the empty-prefix state s_0 = 0, z_0 = 0 of
+ *            the BASED notes, Sec. 2.2).  For BASED, S0/S_T are s and z0/z_T are z.
+ *   o        outputs o_t for every token.
+ *   S_T/z_T  end state (may be NULL when not wanted; BASED: both or neither).
+ *   eps      BASED denominator epsilon (ignored otherwise).  The BASED notes (Sec. 2.3)
+ *            say only that an implementation adds a small epsilon; 1e-6 is a sensible
+ *            choice.  o = num / (den + eps).
+ *   workspace, workspace_bytes
+ *            device scratch of at least la_prefill_workspace_size() bytes (may be NULL
+ *            when that size is 0).  Its contents on entry do not matter.
+ *
+ * Aliasing: o, S_T, z_T and the workspace must not overlap each other or any input.
+ * S_T may equal S0 exactly (in-place state update), and z_T may equal z0.
+ *
+ * Method: bf16 inputs take the chunkwise path -- chunks of 64 tokens, intra-chunk
+ * products on MFMA with fp32 accumulation, the gated delta rule's WY/UT transform
+ * solved in LDS, and an fp32 state carried across chunks and across segments of
+ * chunks (a three-pass segment scan: per-segment affine state maps, a scan of the
+ * segment start states, then every segment replayed from its start state).  fp32
+ * inputs take an fp32 token-recurrent path (fp32 FMA throughout).
+ *
+ * Supported: bf16 -- ADDITIVE/GATED/GATED_DELTA with d_k = d_v = 128 or 64;
+ *                    BASED with d' = 16, d_v = 64.
+ *            fp32 -- ADDITIVE/GATED/GATED_DELTA with d_k in {64, 128, 256} and any d_v;
+ *                    BASED with d' = 16 and d_v = 64.
+ *            Any T >= 1 (a partial last chunk is masked).
+ */
+int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k, int d_v,
+               float eps, const void *q, const void *k, const void *v, const void *alpha,
+               const void *beta, const float *S0, const float *z0, void *o, float *S_T,
+               float *z_T, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * la_decode_step -- one token for N independent states (e.g. N = sequences x heads):
+ *
+ *   S_out = S_in A + beta v k^T,  o = S_out q      (BASED: s, z updated, o normalised)
+ *
+ * Layouts: S_in/S_out [N][d_v][d_k] fp32 (BASED: s [N][D][d_v], z [N][D]),
+ * q, k [N][d_k], v, o [N][d_v], alpha, beta [N].  S_out may equal S_in (and z_out may
+ * equal z_in) for an in-place update; any other overlap returns LA_ERR_ALIAS.  Each
+ * state is read once and written once (this step is bound by HBM bandwidth).
+ *
+ * Supported: ADDITIVE/GATED/GATED_DELTA with d_k in {64, 128, 256} and any d_v >= 1;
+ *            BASED with d' = 16, d_v = 64; q/k/v/alpha/beta/o in fp32 or bf16.
+ */
+int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, const float *S_in,
+                   const float *z_in, float *S_out, float *z_out, const void *q, const void *k,
+                   const void *v, const void *alpha, const void *beta, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

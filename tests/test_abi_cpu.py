@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol declared in
+include/la.h, and rejects bad arguments before launching anything.  Every call here
+fails validation (fake device addresses are never dereferenced)."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import gated_delta_rule_chunkwise_amd as la
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = (ROOT / "include" / "la.h").read_text()
+
+A = 1 << 20  # a fake, 16-byte aligned "device" address: validation never dereferences it
+
+
+def declared_functions():
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s*(la_\w+)\s*\(", HEADER, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return la.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"la_prefill", "la_decode_step", "la_prefill_workspace_size",
+                          "la_status_string", "la_abi_version"}
+    raw = ctypes.CDLL(str(la.LIB_PATH))
+    for n in names:
+        assert hasattr(raw, n), f"libla.so does not export {n}"
+    assert set(la.EXPORTS) <= set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.la_abi_version() == 1
+    for code, name in la.STATUS.items():
+        assert lib.la_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.la_status_string(12345)
+
+
+def P(addr):
+    return ctypes.c_void_p(addr)
+
+
+def prefill(lib, variant=la.GATED_DELTA, dtype=la.BF16, B=1, H=2, T=100, dk=128, dv=128,
+            q=A, k=2 * A, v=3 * A, alpha=4 * A, beta=5 * A, S0=None, z0=None, o=6 * A, S_T=8 * A,
+            z_T=None, ws=None, ws_bytes=0):
+    if ws is None:
+        n = ctypes.c_size_t(0)
+        st = lib.la_prefill_workspace_size(variant, dtype, B, H, T, dk, dv, ctypes.byref(n))
+        if st == 0 and n.value:
+            ws, ws_bytes = 64 * A, n.value
+    return lib.la_prefill(variant, dtype, B, H, T, dk, dv, 1e-6, P(q), P(k), P(v),
+                          None if alpha is None else P(alpha), None if beta is None else P(beta),
+                          None if S0 is None else P(S0), None if z0 is None else P(z0), P(o),
+                          None if S_T is None else P(S_T), None if z_T is None else P(z_T),
+                          None if ws is None else P(ws), ws_bytes, None)
+
+
+def test_prefill_rejects_bad_variant_and_dtype(lib):
+    assert prefill(lib, variant=7) == -2
+    assert prefill(lib, variant=-1) == -2
+    assert prefill(lib, dtype=5) == -2
+
+
+def test_prefill_rejects_bad_sizes(lib):
+    assert prefill(lib, B=0) == -2
+    assert prefill(lib, H=-3) == -2
+    assert prefill(lib, T=-1) == -2
+    assert prefill(lib, dk=0) == -2
+
+
+def test_prefill_unsupported_shapes(lib):
+    assert prefill(lib, dk=96, dv=96) == -3
+    assert prefill(lib, dk=128, dv=64) == -3
+    assert prefill(lib, variant=la.BASED, alpha=None, beta=None, dk=8, dv=64) == -3
+
+
+def test_prefill_variant_pointer_rules(lib):
+    assert prefill(lib, variant=la.ADDITIVE) == -2             # alpha/beta must be NULL
+    assert prefill(lib, variant=la.GATED, alpha=None) == -1    # alpha required
+    assert prefill(lib, variant=la.GATED_DELTA, beta=None) == -1
+    assert prefill(lib, q=0) == -1
+    assert prefill(lib, variant=la.BASED, alpha=None, beta=None, dk=16, dv=64, S_T=8 * A,
+                   z_T=None) == -2                              # s without z
+    assert prefill(lib, z0=9 * A) == -2                         # z only for BASED
+
+
+def test_prefill_alignment(lib):
+    assert prefill(lib, q=A + 2) == -4
+    assert prefill(lib, S_T=8 * A + 4) == -4
+
+
+def test_prefill_aliasing(lib):
+    # o overlapping q
+    assert prefill(lib, o=A + 16) == -6
+    # S_T overlapping o
+    assert prefill(lib, S_T=6 * A + 64) == -6
+    # S_T overlapping S0 without being the same buffer
+    assert prefill(lib, S0=8 * A, S_T=8 * A + 256) == -6
+
+
+def test_prefill_workspace_rules(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 1, 16, 1 << 20, 128, 128,
+                                         ctypes.byref(n)) == 0
+    if n.value == 0:
+        pytest.skip("this configuration needs no workspace")
+    assert prefill(lib, T=1 << 20, H=16, ws=64 * A, ws_bytes=n.value - 1, q=A, k=A + (1 << 32),
+                   v=A + (2 << 32), alpha=A + (3 << 32), beta=A + (4 << 32), o=A + (5 << 32),
+                   S_T=A + (6 << 32)) == -5
+    assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 1, 16, 100, 128, 128, None) == -1
+
+
+def test_workspace_size_validates(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.la_prefill_workspace_size(9, la.BF16, 1, 1, 10, 128, 128, ctypes.byref(n)) == -2
+    assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 1, 1, 10, 96, 96,
+                                         ctypes.byref(n)) == -3
+    assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.F32, 1, 1, 10, 128, 128,
+                                         ctypes.byref(n)) == 0 and n.value == 0
+
+
+def decode(lib, variant=la.GATED_DELTA, dtype=la.BF16, n=16, dk=128, dv=128, S_in=A, z_in=None,
+           S_out=2 * A, z_out=None, q=4 * A, k=5 * A, v=6 * A, alpha=7 * A, beta=8 * A, o=9 * A):
+    f = lambda x: None if x is None else P(x)
+    return lib.la_decode_step(variant, dtype, n, dk, dv, 1e-6, f(S_in), f(z_in), f(S_out), f(z_out),
+                              f(q), f(k), f(v), f(alpha), f(beta), f(o), None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, variant=4) == -2
+    assert decode(lib, n=0) == -2
+    assert decode(lib, dk=100) == -3
+    assert decode(lib, variant=la.BASED, alpha=None, beta=None, dk=16, dv=32) == -3
+    assert decode(lib, S_in=None) == -1
+    assert decode(lib, beta=None) == -1
+    assert decode(lib, variant=la.ADDITIVE) == -2
+    assert decode(lib, variant=la.BASED, alpha=None, beta=None, dk=16, dv=64) == -1  # z missing
+    assert decode(lib, q=4 * A + 1) == -4             # q must be element aligned
+    assert decode(lib, S_in=A + 8) == -4              # states 16-byte aligned
+    assert decode(lib, o=6 * A + 32) == -6            # o overlaps v
+    assert decode(lib, S_out=A + 1024) == -6          # partial overlap of the states

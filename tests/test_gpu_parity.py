@@ -1,0 +1,197 @@
+"""GPU parity at sizes the oracle finishes in seconds: every call goes through the C ABI
+(libla.so) and is compared element by element with the fp64 oracle on the same seeded
+inputs.  Error metric and tolerances: tests/parity.py (2e-2 for bf16 inputs, 1e-4 for
+fp32 inputs, per (b, h) slice, max-norm relative)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.parity import TOL, assert_close, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+ROWS_VARIANTS = ["additive", "gated", "gated_delta"]
+
+
+def _inputs(variant, B, H, T, dk, dv, dtype, seed):
+    if variant == "based":
+        d = synth.based_inputs(B, H, T, dk, dv, dtype=dtype, seed=seed, device=DEV)
+        return d["q"], d["k"], d["v"], None, None
+    d = synth.gdn_inputs(B, H, T, dk, dv, dtype=dtype, seed=seed, device=DEV,
+                         normalize=(variant == "gated_delta"))
+    if variant == "additive":
+        return d["q"], d["k"], d["v"], None, None
+    return d["q"], d["k"], d["v"], d["alpha"], d["beta"]
+
+
+def _check_prefill(la, variant, B, H, T, dk, dv, dtype, seed, S0=None, z0=None):
+    q, k, v, a, b = _inputs(variant, B, H, T, dk, dv, dtype, seed)
+    print(f"[prefill] {variant} B={B} H={H} T={T} dk={dk} dv={dv} {dtype} seed={seed}", flush=True)
+    o, S_T, z_T = la.prefill(variant, q, k, v, a, b, S0=S0, z0=z0)
+    torch.cuda.synchronize()
+    oo, So, zo = oracle.prefill(variant, q, k, v, a, b, S0=S0, z0=z0)
+    tol = TOL[dtype]
+    assert_close(o, oo, tol, what="o")
+    assert_close(S_T, So, tol, what="S_T")
+    if variant == "based":
+        assert_close(z_T, zo, tol, what="z_T")
+    return o, S_T, z_T
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_small(la, variant, dtype):
+    if variant == "based":
+        _check_prefill(la, variant, 2, 3, 203, 16, 64, dtype, seed=11)
+    else:
+        for dk in (64, 128):
+            _check_prefill(la, variant, 2, 3, 203, dk, dk, dtype, seed=12 + dk)
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS)
+def test_prefill_fp32_other_widths(la, variant):
+    _check_prefill(la, variant, 1, 2, 77, 256, 40, torch.float32, seed=3)
+    _check_prefill(la, variant, 1, 2, 77, 64, 17, torch.float32, seed=4)
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_with_start_state(la, variant, dtype):
+    B, H, T = 1, 2, 130
+    if variant == "based":
+        dk, dv = 16, 64
+        w = synth.based_inputs(B, H, 40, dk, dv, dtype=dtype, seed=99, device=DEV)
+        _, s0, z0 = oracle.prefill("based", w["q"], w["k"], w["v"])
+        S0 = torch.tensor(s0, dtype=torch.float32, device=DEV)
+        z0 = torch.tensor(z0, dtype=torch.float32, device=DEV)
+    else:
+        dk = dv = 128
+        S0 = synth.gdn_state((B, H, dv, dk), seed=5, device=DEV) * 0.3
+        z0 = None
+    _check_prefill(la, variant, B, H, T, dk, dv, dtype, seed=21, S0=S0, z0=z0)
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+def test_prefill_empty_sequence_returns_start_state(la, variant):
+    dk, dv = (16, 64) if variant == "based" else (128, 128)
+    q, k, v, a, b = _inputs(variant, 1, 2, 0, dk, dv, torch.bfloat16, 1)
+    if variant == "based":
+        D = 1 + dk + dk * dk
+        S0 = torch.randn(1, 2, D, dv, device=DEV)
+        z0 = torch.rand(1, 2, D, device=DEV)
+    else:
+        S0, z0 = torch.randn(1, 2, dv, dk, device=DEV), None
+    o, S_T, z_T = la.prefill(variant, q, k, v, a, b, S0=S0, z0=z0)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(S_T, S0)
+    if z0 is not None:
+        assert torch.equal(z_T, z0)
+    _, S_T, _ = la.prefill(variant, q, k, v, a, b)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S_T) == 0
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 50), (256, 32)])
+def test_decode_steps(la, variant, dtype, dk, dv):
+    N, steps = 37, 6
+    print(f"[decode] {variant} N={N} dk={dk} dv={dv} {dtype}", flush=True)
+    d = synth.gdn_decode_inputs(steps, N, dk, dv, dtype=dtype, seed=7, device=DEV)
+    S = synth.gdn_state((N, dv, dk), seed=8, device=DEV)
+    S_ref = to64(S)
+    tol = TOL[dtype]
+    for t in range(steps):
+        a = None if variant == "additive" else d["alpha"][t]
+        b = None if variant == "additive" else d["beta"][t]
+        o, S, _ = la.decode_step(variant, S, d["q"][t], d["k"][t], d["v"][t], a, b, S_out=S)
+        torch.cuda.synchronize()
+        oo, S_ref, _ = oracle.decode_step(variant, S_ref, d["q"][t], d["k"][t], d["v"][t], a, b)
+        assert_close(o, oo, tol, lead=1, what=f"o step {t}")
+    assert_close(S, S_ref, tol, lead=1, what="S")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_based_steps(la, dtype):
+    N, steps, dp, dv = 29, 5, 16, 64
+    w = synth.based_warmup_inputs(N, 24, dp, dv, dtype=dtype, seed=3, device=DEV)
+    # both sides build the start state from the same warm-up tokens: the GPU through its
+    # own prefill, the oracle through its own recurrence
+    _, s, z = la.prefill("based", w["q"][None], w["k"][None], w["v"][None])
+    s, z = s[0].contiguous(), z[0].contiguous()
+    _, s_ref, z_ref = oracle.prefill("based", w["q"][None], w["k"][None], w["v"][None])
+    s_ref, z_ref = s_ref[0], z_ref[0]
+    d = synth.based_decode_inputs(steps, N, dp, dv, dtype=dtype, seed=4, device=DEV)
+    tol = TOL[dtype]
+    for t in range(steps):
+        o, s, z = la.decode_step("based", s, d["q"][t], d["k"][t], d["v"][t], z=z, S_out=s, z_out=z)
+        torch.cuda.synchronize()
+        oo, s_ref, z_ref = oracle.decode_step("based", s_ref, d["q"][t], d["k"][t], d["v"][t],
+                                              z=z_ref)
+        assert_close(o, oo, tol, lead=1, what=f"o step {t}")
+    assert_close(s, s_ref, tol, lead=1, what="s")
+    assert_close(z, z_ref, tol, lead=1, what="z")
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+def test_prefill_deterministic(la, variant):
+    dk, dv = (16, 64) if variant == "based" else (128, 128)
+    q, k, v, a, b = _inputs(variant, 1, 4, 333, dk, dv, torch.bfloat16, 5)
+    o1, S1, _ = la.prefill(variant, q, k, v, a, b)
+    o2, S2, _ = la.prefill(variant, q, k, v, a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def _check_prefill_sampled(la, variant, B, H, T, dk, dv, dtype, seed, rows, S0=None):
+    """Parity on a sample of value rows (rows evolve independently, so the oracle can
+    compute just those) for shapes where the full fp64 oracle would be slow."""
+    q, k, v, a, b = _inputs(variant, B, H, T, dk, dv, dtype, seed)
+    print(f"[prefill-sampled] {variant} B={B} H={H} T={T} rows={rows} {dtype}", flush=True)
+    o, S_T, _ = la.prefill(variant, q, k, v, a, b, S0=S0)
+    torch.cuda.synchronize()
+    oo, So, _ = oracle.prefill(variant, q, k, v, a, b, S0=S0, rows=rows)
+    tol = TOL[dtype]
+    assert_close(o[..., rows], oo, tol, what="o (sampled rows)")
+    assert_close(S_T[:, :, rows, :], So, tol, what="S_T (sampled rows)")
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS)
+def test_chunk_multi_chunk_segments(la, variant):
+    # 64 heads -> 16 segments of several chunks each, ragged tail
+    _check_prefill_sampled(la, variant, 4, 16, 64 * 37 + 29, 128, 128, torch.bfloat16, 31,
+                           rows=[0, 17, 63, 127])
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS)
+def test_chunk_single_segment_many_heads(la, variant):
+    # 128 heads fill the chip: one segment, no map/scan passes
+    S0 = synth.gdn_state((8, 16, 128, 128), seed=9, device=DEV) * 0.1
+    _check_prefill_sampled(la, variant, 8, 16, 64 * 3 + 10, 128, 128, torch.bfloat16, 32,
+                           rows=[1, 64, 126], S0=S0)
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS)
+@pytest.mark.parametrize("T", [1, 63, 64, 65])
+def test_chunk_short_sequences(la, variant, T):
+    _check_prefill(la, variant, 1, 2, T, 128, 128, torch.bfloat16, seed=40 + T)
+
+
+def test_chunk_split_resume_on_gpu(la):
+    """prefill(x[:a]) then prefill(x[a:], S0=S_a) matches one prefill(x) (within bf16 parity)."""
+    q, k, v, a, b = _inputs("gated_delta", 1, 4, 1000, 128, 128, torch.bfloat16, 50)
+    o, S, _ = la.prefill("gated_delta", q, k, v, a, b)
+    cut = 448
+    o1, S1, _ = la.prefill("gated_delta", q[:, :, :cut].contiguous(), k[:, :, :cut].contiguous(),
+                           v[:, :, :cut].contiguous(), a[:, :, :cut].contiguous(),
+                           b[:, :, :cut].contiguous())
+    o2, S2, _ = la.prefill("gated_delta", q[:, :, cut:].contiguous(), k[:, :, cut:].contiguous(),
+                           v[:, :, cut:].contiguous(), a[:, :, cut:].contiguous(),
+                           b[:, :, cut:].contiguous(), S0=S1)
+    torch.cuda.synchronize()
+    assert_close(torch.cat([o1, o2], dim=2), o, 2e-2, what="o split")
+    assert_close(S2, S, 2e-2, what="S split")
