@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X linear-attention recurrence library (one GPU).
+
+Headline workload: gated-delta chunkwise prefill of one layer, B = 1, H = 16,
+T = 1,048,576, d_k = d_v = 128, bf16 q/k/v/alpha/beta, fp32 state, seeded synthetic
+inputs with the gated-delta recipe (synth.gdn_inputs).  One step = one complete
+la_prefill over the whole sequence (its three passes: segment maps, scan, replay).
+value = tokens/s, a token being one position through all 16 heads.
+
+Also measured in the same run: the batched decode step (256 sequences x 16 heads,
+gated-delta state 128 x 128 and BASED state 273 x 64 per head, 1024 consecutive steps),
+and the fp64 oracle on a bounded sample of the prefill workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "prefill tokens/sec (GDN, T=1M) + decode steps/sec, 1×MI355X, % of roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+PROFILE_COUNTERS = ROOT / "profiles" / "gdn_prefill_1m_counters.txt"
+
+# algorithmic work per token-head of the gated-delta prefill at chunk 64, d = 128:
+# bytes: q, k, v (3 x 128 x 2) + alpha, beta (2 x 2) + o (128 x 2)
+BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 2 * 2 + 128 * 2          # 1028
+# FLOPs of the chunk form (multiply-add = 2): Grams K K^T and Q K^T, W, U~, A U
+# (5 x 2 C^2 d), W S^T, Q S^T, state update (3 x 2 C d^2), triangular solve (C^3 / 3)
+C_, D_ = 64, 128
+FLOPS_PER_TOKEN_HEAD = (5 * 2 * C_ * C_ * D_ + 3 * 2 * C_ * D_ * D_ + C_ ** 3 / 3) / C_
+
+
+def kernel_source_hash() -> str:
+    src = (ROOT / "gated_delta_rule_chunkwise_amd" / "csrc" / "chunk.hip").read_bytes()
+    return hashlib.sha256(src).hexdigest()[:16]
+
+
+def read_traffic(kernel_key: str):
+    """HBM bytes per launch of `kernel_key` from the committed counter summary, scaled by
+    the copy-kernel calibration recorded there; None if absent or taken on other code."""
+    if not PROFILE_COUNTERS.exists():
+        return None
+    txt = PROFILE_COUNTERS.read_text()
+    m = re.search(r"source_sha256_16:\s*(\w+)", txt)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"^{re.escape(kernel_key)}\s+traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    return float(m.group(1)) if m else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--seq-len", type=int, default=1 << 20)
+    ap.add_argument("--heads", type=int, default=16)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: this build has no multi-GPU path "
+                  "(every (batch, head) slice is independent; sharding is described in DESIGN.md)",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_chunkwise_amd as la
+    import synth
+
+    la.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    B, H, T, D = 1, args.heads, args.seq_len, 128
+
+    # ---------------------------------------------------------------- prefill
+    inp = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=3, device=dev)
+    q, k, v, a, b = inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"]
+    o = torch.empty((B, H, T, D), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws_n = la.workspace_size("gated_delta", la.BF16, B, H, T, D, D)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    nseg, seg_chunks = la.segments("gated_delta", la.BF16, B, H, T, D, D)
+    passes = [la.PASS_MAPS, la.PASS_SCAN, la.PASS_REPLAY] if nseg > 1 else [la.PASS_REPLAY]
+    names = {la.PASS_MAPS: "maps", la.PASS_SCAN: "scan", la.PASS_REPLAY: "replay"}
+
+    def step(evs=None):
+        for i, p in enumerate(passes):
+            la.prefill("gated_delta", q, k, v, a, b, o=o, S_T=S_T, workspace=ws, pass_=p,
+                       stream=stream)
+            if evs is not None:
+                evs[i + 1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per_pass = {names[p]: 0.0 for p in passes}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    all_evs = []
+    t_start.record(stream)
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(passes) + 1)]
+        evs[0].record(stream)
+        step(evs)
+        all_evs.append(evs)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    for evs in all_evs:
+        for i, p in enumerate(passes):
+            per_pass[names[p]] += evs[i].elapsed_time(evs[i + 1]) / args.steps
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = B * T / (ms_per_step * 1e-3)
+    token_heads = B * H * T
+    alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD
+    alg_flops = token_heads * FLOPS_PER_TOKEN_HEAD
+
+    # the dominant launch of the step and its algorithmic traffic per launch
+    dom = max(per_pass, key=per_pass.get)
+    dom_bytes = {"replay": token_heads * BYTES_PER_TOKEN_HEAD,
+                 "maps": token_heads * (2 * 128 * 2 + 2 * 2),
+                 "scan": B * H * nseg * (3 * D * D * 4)}[dom]
+    dom_gbs = dom_bytes / (per_pass[dom] * 1e-3) / 1e9
+    traffic = read_traffic(dom)
+    roofline = {
+        "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "kernel": f"chunk pass '{dom}' ({'chunk_kernel<MODE_OUT,true>' if dom == 'replay' else dom})",
+        "ms_per_launch": round(per_pass[dom], 4),
+    }
+    prefill_detail = {
+        "ms_per_pass": {kk: round(vv, 4) for kk, vv in per_pass.items()},
+        "segments": nseg, "chunks_per_segment": seg_chunks,
+        "alg_bytes": alg_bytes, "alg_flops": alg_flops,
+        "hbm_frac_whole_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bf16_mfma_frac_whole_step": round(alg_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "roofline_time_ms": round(max(alg_bytes / (HBM_PEAK_GBS * 1e9),
+                                      alg_flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e3, 4),
+    }
+    prefill_detail["roofline_frac_whole_step"] = round(prefill_detail["roofline_time_ms"] / ms_per_step, 4)
+
+    # host copy of a prefix of the same inputs for the CPU oracle sample
+    host = None
+    if not args.no_cpu_baseline:
+        Tmax = min(T, 1 << 17)
+        host = {n: t[:, :, :Tmax].cpu() for n, t in inp.items()}
+
+    # ---------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        del inp, q, k, v, a, b, o, ws
+        torch.cuda.empty_cache()
+        decode = bench_decode(torch, la, synth, dev, stream, args.decode_steps)
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = bench_cpu(host, H, D, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"gated-delta chunkwise prefill, B={B} H={H} T={T} d_k=d_v={D}, "
+                               "bf16 inputs, fp32 state, chunk 64", "batch": B, "heads": H,
+                   "seq_len": T, "d_k": D, "d_v": D, "chunk": 64, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "prefill": prefill_detail,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(torch, la, synth, dev, stream, steps):
+    """256 sequences x 16 heads; gated-delta and BASED decode, `steps` consecutive steps."""
+    N, D, dp, dv_b = 256 * 16, 128, 16, 64
+    Dphi = 1 + dp + dp * dp
+    res = {"states": N, "steps": steps}
+    # gated delta: seeded N(0,1) start state, per-step q/k/v/alpha/beta resident in HBM
+    S = synth.gdn_state((N, D, D), seed=4, device=dev)
+    g = synth.gdn_decode_inputs(steps, N, D, D, dtype=torch.bfloat16, seed=4, device=dev)
+    o = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    # BASED: start state = the end state of a 64-token warm-up prefill of the same batch
+    w = synth.based_warmup_inputs(N, 64, dp, dv_b, dtype=torch.bfloat16, seed=4, device=dev)
+    _, s, z = la.prefill("based", w["q"][None], w["k"][None], w["v"][None])
+    s, z = s[0].contiguous(), z[0].contiguous()
+    bd = synth.based_decode_inputs(steps, N, dp, dv_b, dtype=torch.bfloat16, seed=5, device=dev)
+    ob = torch.empty((N, dv_b), dtype=torch.bfloat16, device=dev)
+
+    def gdn_step(t):
+        la.decode_step("gated_delta", S, g["q"][t], g["k"][t], g["v"][t], g["alpha"][t],
+                       g["beta"][t], S_out=S, o=o, stream=stream)
+
+    def based_step(t):
+        la.decode_step("based", s, bd["q"][t], bd["k"][t], bd["v"][t], z=z, S_out=s, z_out=z,
+                       o=ob, stream=stream)
+
+    def timed(fn):
+        for t in range(8):
+            fn(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(steps):
+            fn(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_g = timed(gdn_step)
+    ms_b = timed(based_step)
+    bytes_g = 2 * N * D * D * 4 + N * (3 * D + 2 + D) * 2
+    bytes_b = 2 * N * (Dphi * dv_b + Dphi) * 4 + N * (2 * dp + 2 * dv_b) * 2
+    res["gated_delta"] = {"us_per_step": round(ms_g * 1e3, 2), "steps_per_s": round(1e3 / ms_g, 1),
+                          "alg_bytes_per_step": bytes_g,
+                          "hbm_frac": round(bytes_g / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    res["based"] = {"us_per_step": round(ms_b * 1e3, 2), "steps_per_s": round(1e3 / ms_b, 1),
+                    "alg_bytes_per_step": bytes_b,
+                    "hbm_frac": round(bytes_b / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    res["both_steps_per_s"] = round(1e3 / (ms_g + ms_b), 1)
+    return res
+
+
+def bench_cpu(host, H, D, target_s):
+    """The fp64 oracle, as it is, on the first T_s tokens of the same 16-head sequence (all
+    value rows, the same input values the GPU ran on), on this host's cores; T_s is grown
+    until the run takes about target_s."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    oracle._load()
+    Tmax = host["q"].shape[2]
+
+    def run(Ts):
+        d = {n: t[:, :, :Ts] for n, t in host.items()}
+        t0 = time.perf_counter()
+        oracle.prefill("gated_delta", d["q"], d["k"], d["v"], d["alpha"], d["beta"], nthreads=cores)
+        return time.perf_counter() - t0
+
+    Ts = min(2048, Tmax)
+    dt = run(Ts)
+    Ts2 = int(min(max(Ts * target_s / max(dt, 1e-3), Ts), Tmax)) // 64 * 64
+    dt2 = run(Ts2)
+    return {"value": round(Ts2 / dt2, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 oracle on the first {Ts2} tokens of the {H}-head gated-delta "
+                      f"sequence (all 128 value rows, d_k=d_v={D}), {dt2:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,8 @@ F32, BF16 = 0, 1
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_INVALID", -3: "LA_ERR_UNSUPPORTED",
           -4: "LA_ERR_ALIGN", -5: "LA_ERR_WORKSPACE", -6: "LA_ERR_ALIAS", -7: "LA_ERR_HIP"}
 EXPORTS = ("la_abi_version", "la_status_string", "la_prefill_workspace_size", "la_prefill",
-           "la_decode_step")
+           "la_prefill_pass", "la_prefill_segments", "la_decode_step")
+PASS_MAPS, PASS_SCAN, PASS_REPLAY = 1, 2, 3
 
 LIB_PATH = Path(__file__).resolve().parent / "libla.so"
 _lib = None
@@ -53,6 +54,11 @@ def load(path: str | None = None):
     lib.la_prefill.argtypes = [i32, i32, i32, i32, i64, i32, i32, f32] + [vp] * 11 + \
         [ctypes.c_size_t, vp]
     lib.la_prefill.restype = i32
+    lib.la_prefill_pass.argtypes = [i32] + lib.la_prefill.argtypes
+    lib.la_prefill_pass.restype = i32
+    lib.la_prefill_segments.argtypes = [i32, i32, i32, i32, i64, i32, i32,
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.la_prefill_segments.restype = i32
     lib.la_decode_step.argtypes = [i32, i32, i32, i32, i32, f32] + [vp] * 10 + [vp]
     lib.la_decode_step.restype = i32
     if path is None:
@@ -99,10 +105,21 @@ def workspace_size(variant, dtype, B, H, T, d_k, d_v) -> int:
     return int(n.value)
 
 
+def segments(variant, dtype, B, H, T, d_k, d_v):
+    """(n_segments, chunks_per_segment) that la_prefill uses for this problem."""
+    n, c = ctypes.c_int(0), ctypes.c_int(0)
+    st = load().la_prefill_segments(_var(variant), dtype, B, H, T, d_k, d_v, ctypes.byref(n),
+                                    ctypes.byref(c))
+    if st != 0:
+        raise LAError(st, "la_prefill_segments")
+    return n.value, c.value
+
+
 def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6, want_state=True,
-            o=None, S_T=None, z_T=None, workspace=None, stream=None):
-    """Run la_prefill.  q, k [B,H,T,d_k]; v [B,H,T,d_v]; alpha, beta [B,H,T] (same dtype as q);
-    S0 [B,H,d_v,d_k] fp32 (BASED: s0 [B,H,D,d_v], z0 [B,H,D]).  Returns (o, S_T, z_T)."""
+            o=None, S_T=None, z_T=None, workspace=None, stream=None, pass_=None):
+    """Run la_prefill (or one pass of it, ``pass_`` in PASS_MAPS/SCAN/REPLAY, see la.h).
+    q, k [B,H,T,d_k]; v [B,H,T,d_v]; alpha, beta [B,H,T] (same dtype as q); S0 [B,H,d_v,d_k]
+    fp32 (BASED: s0 [B,H,D,d_v], z0 [B,H,D]).  Returns (o, S_T, z_T)."""
     var = _var(variant)
     lib = load()
     B, H, T, dk = q.shape
@@ -121,12 +138,13 @@ def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6,
     ws_n = workspace_size(var, dt, B, H, T, dk, dv)
     if ws_n and workspace is None:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-    st = lib.la_prefill(var, dt, B, H, T, dk, dv, float(eps), _p(q), _p(k), _p(v), _p(alpha),
-                        _p(beta), _p(S0), _p(z0), _p(o), _p(S_T), _p(z_T), _p(workspace),
-                        0 if workspace is None else workspace.numel() * workspace.element_size(),
-                        _stream(stream))
+    args = (var, dt, B, H, T, dk, dv, float(eps), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(S0),
+            _p(z0), _p(o), _p(S_T), _p(z_T), _p(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    st = lib.la_prefill(*args) if pass_ is None else lib.la_prefill_pass(int(pass_), *args)
     if st != 0:
-        raise LAError(st, "la_prefill")
+        raise LAError(st, "la_prefill" if pass_ is None else "la_prefill_pass")
     return o, S_T, z_T
 
 

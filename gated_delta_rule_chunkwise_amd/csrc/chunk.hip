@@ -19,13 +19,23 @@
 // Every product with a 64- or 128-wide inner dimension runs on bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16) with fp32 accumulation; the state stays fp32.
 //
+// gfx950 layout choices.  All chunk tiles live in LDS row-major ([token][d]); operands
+// that contract over tokens (K^T, V^T) are read straight from those tiles with the
+// CDNA4 transpose read ds_read_b64_tr_b16, so no transposed copies are built.  L (fp32)
+// is kept transposed in the strict upper triangle of the same buffer whose lower
+// triangle receives T.  A workgroup (4 waves) uses at most ~80 KB of LDS, so two
+// workgroups share a CU and overlap their latency-bound phases (the triangular solve,
+// barriers) with each other's MFMA phases.  The next chunk's inputs are prefetched into
+// registers while the current chunk is processed.
+//
 // Sequence parallelism.  One workgroup owns the whole 128 x 128 state of one (b, h),
-// which fits its registers, so a workgroup streams chunks with no inter-workgroup
-// traffic.  A 1M-token sequence is split into segments so that B*H*segments fills the
-// chip, in three passes:
-//   pass 1 (MODE_MAP)  every segment from a zero start: its end state B_seg and, for the
-//                      delta rule, its d_k x d_k transition M_seg (the same chunk
-//                      recurrence run on the identity), or the scalar log decay
+// split over its 4 waves (32 state rows each, in registers), and streams chunks with
+// no inter-workgroup traffic.  A long sequence is split into segments so that
+// B*H*segments fills the chip, in three passes:
+//   pass 1 (MODE_MAP)  every segment from a zero start: its end state B_seg, and for the
+//                      delta rule its d_k x d_k transition M_seg (the same chunk
+//                      recurrence run on the identity, by a second workgroup per
+//                      segment), or the scalar log decay
 //   pass 2 (scan)      S_{i+1} = S_i M_i + B_i sequentially over segments, row-parallel
 //   pass 3 (MODE_OUT)  every segment replayed from its start state, writing o
 // With one segment (enough heads to fill the chip) only pass 3 runs.
@@ -38,28 +48,32 @@ namespace gdn {
 constexpr int C = 64;     // tokens per chunk
 constexpr int DK = 128;   // key width
 constexpr int DV = 128;   // value width
-constexpr int NW = 8;     // waves per workgroup
+constexpr int NW = 4;     // waves per workgroup
 constexpr int NTHR = NW * 64;
+constexpr int RPW = DV / NW;  // state rows per wave (two 16-row column tiles)
+#ifndef LA_CHUNK_WG_PER_CU
+#define LA_CHUNK_WG_PER_CU 2
+#endif
+#ifndef LA_CHUNK_PREFETCH
+#define LA_CHUNK_PREFETCH 0
+#endif
+// Two workgroups per CU hide each other's load latency and latency-bound phases; with
+// one, the next chunk is prefetched into registers instead.
+constexpr int WG_PER_CU = LA_CHUNK_WG_PER_CU;
+// Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
+// would raise register pressure past what two workgroups per CU allow).
+#define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
+constexpr bool PREFETCH = LA_CHUNK_PREFETCH != 0;
 
-constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, W, staging
-constexpr int LDT = C + 8;   // transposed bf16 tiles [D][C]: K^T, V^T
+constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V, W, O staging
 constexpr int LDA = C + 8;   // bf16 [C][C]: decay-masked Q K^T
-constexpr int LDL = C + 4;   // fp32 [C][C]: L, T
+constexpr int LDL = C + 4;   // fp32 [C][C]: L^T (strict upper) and T (lower)
 
 constexpr int SZ_ROW = C * LDK * 2;
-constexpr int SZ_TR = DK * LDT * 2;
-constexpr int SZ_L = C * LDL * 4;
+constexpr int SZ_LT = C * LDL * 4;
 constexpr int SZ_A = C * LDA * 2;
-constexpr int OFF_K = 0;
-constexpr int OFF_Q = OFF_K + SZ_ROW;
-constexpr int OFF_KT = OFF_Q + SZ_ROW;
-constexpr int OFF_VT = OFF_KT + SZ_TR;
-constexpr int OFF_LW = OFF_VT + SZ_TR;  // L (fp32) then -W (bf16); O staging without delta
-constexpr int OFF_T = OFF_LW + SZ_L;    // V staging then T (fp32)
-constexpr int OFF_A = OFF_T + SZ_L;
-constexpr int OFF_VEC = OFF_A + SZ_A;   // g, beta, gamma, decay-to-end, beta*gamma
-constexpr int SMEM = OFF_VEC + 5 * C * 4;
-static_assert(SZ_ROW <= SZ_L && SZ_ROW <= SZ_TR, "staging buffers fit their regions");
+constexpr int SZ_VEC = 5 * C * 4;
+static_assert(SZ_ROW <= SZ_LT, "O staging fits the L/T buffer");
 static_assert(DK == DV, "square state");
 
 enum { MODE_MAP = 0, MODE_OUT = 1 };
@@ -76,16 +90,30 @@ struct Args {
   int H, nseg, seg_chunks, variant, has_beta;
 };
 
-// Reads the MFMA operand for rows `row`, 32-wide k-step starting at col0 = 32 s: the
-// lane group g supplies columns col0+4g..+3 and col0+16+4g..+3, matching the column
-// order of two stacked 16x16 accumulator tiles (rows 4g..4g+3 of each).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// A operand with k along the columns of a row-major tile: row `row`, 32-wide k-step at
+// col0; lane group g supplies columns col0+4g..+3 and col0+16+4g..+3, the column order
+// of two stacked 16x16 accumulator tiles (their rows 4g..4g+3).
 __device__ __forceinline__ bf16x8 frag_pair(const bf16_t *base, int ld, int row, int col0, int g) {
   const uint2 lo = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 4 * g);
   const uint2 hi = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 16 + 4 * g);
-  u16x8 u;
-  u[0] = (uint16_t)lo.x; u[1] = (uint16_t)(lo.x >> 16); u[2] = (uint16_t)lo.y; u[3] = (uint16_t)(lo.y >> 16);
-  u[4] = (uint16_t)hi.x; u[5] = (uint16_t)(hi.x >> 16); u[6] = (uint16_t)hi.y; u[7] = (uint16_t)(hi.y >> 16);
-  return as_bf16x8(u);
+  const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Operand with k along the ROWS (tokens) of a row-major [token][d] tile: lane (g, i)
+// receives column 16 nt + i at tokens 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3 (the
+// same token order as frag_pair's columns).  ds_read_b64_tr_b16 hands lane i of each
+// 16-lane group element (i & 3) of the 8-byte chunks addressed by lanes 4 e + (i >> 2),
+// e = 0..3; lane j therefore addresses row tbase + (j >> 2), columns 16 nt + 4 (j & 3).
+__device__ __forceinline__ bf16x8 col_frag(const bf16_t *tile, int ld, int nt, int s, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const bf16_t *p0 = tile + (32 * s + 4 * g + (i >> 2)) * ld + 16 * nt + 4 * (i & 3);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + 16 * ld));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ bf16x8 pack_pair(f32x4 a, f32x4 b) {
@@ -99,22 +127,39 @@ __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
   tj = idx - ti * (ti + 1) / 2;
 }
 
+// Row t of T restricted to tokens perm(s, g), with the upper triangle (which holds L^T)
+// masked to zero, scaled per token by sc and packed as a bf16 A operand.
+__device__ __forceinline__ bf16x8 t_frag(const float *LT, const float *sc, int t, int s, int g) {
+  f32x4 a = ld4(LT + t * LDL + 32 * s + 4 * g);
+  f32x4 b = ld4(LT + t * LDL + 32 * s + 16 + 4 * g);
+  const f32x4 sa = ld4(sc + 32 * s + 4 * g), sb = ld4(sc + 32 * s + 16 + 4 * g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = (32 * s + 4 * g + e) > t ? 0.0f : a[e] * sa[e];
+    b[e] = (32 * s + 16 + 4 * g + e) > t ? 0.0f : b[e] * sb[e];
+  }
+  return pack_pair(a, b);
+}
+
 template <int MODE, bool DELTA>
-__global__ __launch_bounds__(NTHR) void chunk_kernel(const Args a) {
-  // column tiles (16 state rows each) owned by one wave
-  constexpr int NCT = (MODE == MODE_MAP && DELTA) ? 2 : 1;
+__global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
+  constexpr bool OUT = MODE == MODE_OUT;
   constexpr int MAPROWS = DELTA ? 2 * DV : DV;
+  constexpr int OFF_K = 0;
+  constexpr int OFF_Q = SZ_ROW;  // MODE_OUT only
+  constexpr int OFF_VW = OUT ? 2 * SZ_ROW : SZ_ROW;
+  constexpr int OFF_LT = OFF_VW + SZ_ROW;
+  constexpr int OFF_A = OFF_LT + SZ_LT;  // MODE_OUT only
+  constexpr int OFF_VEC = OUT ? OFF_A + SZ_A : OFF_LT + SZ_LT;
+  constexpr int SMEM = OFF_VEC + SZ_VEC;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   bf16_t *sK = reinterpret_cast<bf16_t *>(smem + OFF_K);
   bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + OFF_Q);
-  bf16_t *sKt = reinterpret_cast<bf16_t *>(smem + OFF_KT);
-  bf16_t *sVt = reinterpret_cast<bf16_t *>(smem + OFF_VT);
-  float *sL = reinterpret_cast<float *>(smem + OFF_LW);
-  bf16_t *sW = reinterpret_cast<bf16_t *>(smem + OFF_LW);
-  float *sT = reinterpret_cast<float *>(smem + OFF_T);
-  bf16_t *sVs = reinterpret_cast<bf16_t *>(smem + OFF_T);
+  bf16_t *sV = reinterpret_cast<bf16_t *>(smem + OFF_VW);   // V, then -W (delta rule)
+  bf16_t *sW = sV;
+  float *sLT = reinterpret_cast<float *>(smem + OFF_LT);
+  bf16_t *sO = reinterpret_cast<bf16_t *>(smem + OFF_LT);  // O staging after T is used
   bf16_t *sA = reinterpret_cast<bf16_t *>(smem + OFF_A);
-  bf16_t *sO = reinterpret_cast<bf16_t *>(smem + (DELTA ? OFF_VT : OFF_LW));
   float *sG = reinterpret_cast<float *>(smem + OFF_VEC);
   float *sBeta = sG + C;
   float *sGam = sG + 2 * C;
@@ -123,69 +168,99 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(const Args a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int seg = blockIdx.x;
+  // pass 1 with the delta rule runs two workgroups per segment: B rows and M rows
+  const bool m_kind = (MODE == MODE_MAP) && DELTA && (int)blockIdx.x >= a.nseg;
+  const int seg = m_kind ? (int)blockIdx.x - a.nseg : (int)blockIdx.x;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
-  const int row0 = wave * 16 * NCT;  // first state row owned by this wave
-  const bool m_rows = (MODE == MODE_MAP) && DELTA && wave >= NW / 2;
+  const int row0 = wave * RPW;  // first state row owned by this wave
 
   // ---- state: lane holds S^T[d = 16 m + 4 g + e][row0 + 16 c + l16] in st[m][c][e]
-  f32x4 st[DK / 16][NCT];
+  f32x4 st[DK / 16][2];
   {
     const float *src = nullptr;
-    if (MODE == MODE_OUT) src = a.nseg > 1 ? a.starts + (bh * a.nseg + seg) * DV * DK : (a.S0 ? a.S0 + bh * DV * DK : nullptr);
+    if (OUT) src = a.nseg > 1 ? a.starts + (bh * a.nseg + seg) * DV * DK : (a.S0 ? a.S0 + bh * DV * DK : nullptr);
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
+      for (int c = 0; c < 2; ++c) {
         const int r = row0 + 16 * c + l16;
         if (src) {
           st[m][c] = ld4(src + (size_t)r * DK + 16 * m + 4 * g);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)  // identity for the transition rows, zero otherwise
-            st[m][c][e] = (m_rows && (r - DV) == 16 * m + 4 * g + e) ? 1.0f : 0.0f;
+            st[m][c][e] = (m_kind && r == 16 * m + 4 * g + e) ? 1.0f : 0.0f;
         }
       }
   }
+
+  // ---- register prefetch of one chunk: 4 x 16 bytes of K (and Q, V) per thread
+  u32x4 pk[4], pq[4], pv[4];
+  float pal = 1.0f, pbe = 0.0f;
+  const bool load_v = !m_kind;
+#define LA_LD1(i)                                                                                \
+  do {                                                                                           \
+    const int id = tid + NTHR * (i), r = id >> 4, cv = id & 15;                                  \
+    const u32x4 z = {0u, 0u, 0u, 0u};                                                            \
+    pk[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.k + (prb + r) * DK + cv * 8) : z;       \
+    if (OUT) pq[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.q + (prb + r) * DK + cv * 8) : z; \
+    if (load_v) pv[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.v + (prb + r) * DV + cv * 8) : z; \
+  } while (0)
+#define LA_PREFETCH(T0)                                                                          \
+  do {                                                                                           \
+    const int64_t pt0 = (T0);                                                                    \
+    const int pn = (int)((T - pt0) < C ? (T - pt0) : C);                                         \
+    const size_t prb = bh * (size_t)T + pt0;                                                     \
+    LA_LD1(0); LA_LD1(1); LA_LD1(2); LA_LD1(3);                                                  \
+    if (wave == 0) {                                                                             \
+      pal = 1.0f;                                                                                \
+      pbe = 0.0f;                                                                                \
+      if (lane < pn) {                                                                           \
+        if (a.variant != V_ADDITIVE) pal = bf16_to_f32(a.alpha[prb + lane]);                     \
+        pbe = (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))               \
+                  ? bf16_to_f32(a.beta[prb + lane]) : 1.0f;                                      \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
 
   float gseg = 0.0f;  // log decay over the segment (scalar-gated map)
   int64_t prev_t0 = -1;
   int prev_n = 0;
   const int64_t first = (int64_t)seg * a.seg_chunks * C;
-  for (int ci = 0; ci < a.seg_chunks; ++ci) {
-    const int64_t t0 = first + (int64_t)ci * C;
-    if (t0 >= T) break;
-    const int n = (int)((T - t0) < C ? (T - t0) : C);
-    const size_t rb = bh * (size_t)T + t0;
+  int nchunks = a.seg_chunks;
+  if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
+  if (PREFETCH && nchunks > 0) LA_PREFETCH(first);
 
-    // ---- phase A: write out the previous chunk's O, load this chunk, gate prefix sums
-    if (MODE == MODE_OUT && prev_t0 >= 0) {
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const int n = (int)((T - t0) < C ? (T - t0) : C);
+    // An opaque copy of the lane index: LDS addresses derived from it are recomputed per
+    // chunk (a few integer ops) instead of being hoisted out of the loop, where dozens
+    // of them would occupy registers for the whole kernel.
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int l16 = lane_v & 15, g = lane_v >> 4;
+
+    // ---- phase A: write out the previous chunk's O, move the prefetched chunk to LDS,
+    // gate prefix sums
+    if (OUT && prev_t0 >= 0) {
       for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
         const int r = id / (DV / 8), cv = id % (DV / 8);
         *reinterpret_cast<uint4 *>(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8) =
             *reinterpret_cast<const uint4 *>(sO + r * LDK + cv * 8);
       }
     }
-    for (int id = tid; id < C * (DK / 8); id += NTHR) {
-      const int r = id / (DK / 8), cv = id % (DK / 8);
-      uint4 kv = make_uint4(0, 0, 0, 0), qv = kv, vv = kv;
-      if (r < n) {
-        kv = *reinterpret_cast<const uint4 *>(a.k + (rb + r) * DK + cv * 8);
-        vv = *reinterpret_cast<const uint4 *>(a.v + (rb + r) * DV + cv * 8);
-        if (MODE == MODE_OUT) qv = *reinterpret_cast<const uint4 *>(a.q + (rb + r) * DK + cv * 8);
-      }
-      *reinterpret_cast<uint4 *>(sK + r * LDK + cv * 8) = kv;
-      *reinterpret_cast<uint4 *>(sVs + r * LDK + cv * 8) = vv;
-      if (MODE == MODE_OUT) *reinterpret_cast<uint4 *>(sQ + r * LDK + cv * 8) = qv;
+    if (!PREFETCH) LA_PREFETCH(t0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = tid + NTHR * i, r = id >> 4, cv = id & 15;
+      *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * 8) = pk[i];
+      if (OUT) *reinterpret_cast<u32x4 *>(sQ + r * LDK + cv * 8) = pq[i];
+      if (load_v) *reinterpret_cast<u32x4 *>(sV + r * LDK + cv * 8) = pv[i];
     }
     if (wave == 0) {
-      float al = 1.0f, be = 0.0f;
-      if (lane < n) {
-        if (a.variant != V_ADDITIVE) al = bf16_to_f32(a.alpha[rb + lane]);
-        be = (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta)) ? bf16_to_f32(a.beta[rb + lane]) : 1.0f;
-      }
-      float x = (a.variant == V_ADDITIVE) ? 0.0f : logf(al);
+      float x = (a.variant == V_ADDITIVE) ? 0.0f : logf(pal);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -194,27 +269,17 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(const Args a) {
       const float gC = __shfl(x, 63, 64);
       const float gam = expf(x);
       sG[lane] = x;
-      sBeta[lane] = be;
+      sBeta[lane] = pbe;
       sGam[lane] = gam;
       sDec[lane] = expf(gC - x);
-      sBG[lane] = be * gam;
+      sBG[lane] = pbe * gam;
     }
     __syncthreads();
 
-    // ---- phase B: transposed copies of K and V; Gram tiles K K^T (-> L) and Q K^T (-> A)
-    for (int id = tid; id < DK * (C / 8); id += NTHR) {
-      const int d = id / (C / 8), tg = id % (C / 8);
-      u16x8 kk, vv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kk[e] = sK[(8 * tg + e) * LDK + d];
-        vv[e] = sVs[(8 * tg + e) * LDK + d];
-      }
-      *reinterpret_cast<u16x8 *>(sKt + d * LDT + 8 * tg) = kk;
-      *reinterpret_cast<u16x8 *>(sVt + d * LDT + 8 * tg) = vv;
-    }
+    // ---- phase B: start loading the next chunk; Gram tiles K K^T (-> L^T) and Q K^T (-> A)
+    if (PREFETCH && ci + 1 < nchunks) LA_PREFETCH(t0 + C);
     {
-      constexpr int NJ = (DELTA ? 10 : 0) + (MODE == MODE_OUT ? 10 : 0);
+      constexpr int NJ = (DELTA ? 10 : 0) + (OUT ? 10 : 0);
       for (int job = wave; job < NJ; job += NW) {
         const bool kk = DELTA && job < 10;
         int ti, tj;
@@ -229,14 +294,23 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(const Args a) {
         }
         const int j = 16 * tj + l16;
         const float gj = sG[j];
+        if (kk) {  // L_tj at the transposed position [j][t]
+          f32x4 lv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * ti + 4 * g + e;
-          if (kk) sL[t * LDL + j] = (t > j) ? sBeta[t] * expf(sG[t] - gj) * acc[e] : 0.0f;
-          else sA[t * LDA + j] = f32_to_bf16((t >= j) ? expf(sG[t] - gj) * acc[e] : 0.0f);
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * ti + 4 * g + e;
+            lv[e] = (t > j) ? sBeta[t] * expf(sG[t] - gj) * acc[e] : 0.0f;
+          }
+          *reinterpret_cast<f32x4 *>(sLT + j * LDL + 16 * ti + 4 * g) = lv;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * ti + 4 * g + e;
+            sA[t * LDA + j] = f32_to_bf16((t >= j) ? expf(sG[t] - gj) * acc[e] : 0.0f);
+          }
         }
       }
-      if (MODE == MODE_OUT) {  // the two above-diagonal tiles read by the A U products
+      if (OUT) {  // the two above-diagonal tiles read by the A U products
         for (int id = tid; id < 512; id += NTHR) {
           const int tile = id >> 8, e = id & 255;
           sA[(32 * tile + (e >> 4)) * LDA + 32 * tile + 16 + (e & 15)] = 0;
@@ -245,182 +319,194 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(const Args a) {
     }
     __syncthreads();
 
-    f32x4 Ut[4][NCT];  // U~ tiles of this wave's rows (delta rule)
+    f32x4 Ut[4][2];  // U~ tiles of this wave's rows (delta rule, B rows)
     if (DELTA) {
-      // ---- phase C: inverses of the four 16 x 16 diagonal blocks of (I + L)
+      // ---- phase C: inverses of the four 16 x 16 diagonal blocks of (I + L), written
+      // to the lower triangle of the diagonal blocks (column-by-column forward
+      // substitution, one lane per column)
       if (wave == 0) {
         const int bi = lane >> 4, c = lane & 15;
         float col[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          LA_FENCE();
           float acc = 0.0f;
 #pragma unroll
-          for (int kq = 0; kq < r; ++kq) acc += sL[(16 * bi + r) * LDL + 16 * bi + kq] * col[kq];
+          for (int kq = 0; kq < r; ++kq) acc += sLT[(16 * bi + kq) * LDL + 16 * bi + r] * col[kq];
           col[r] = (r == c) ? 1.0f : (r > c ? -acc : 0.0f);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(16 * bi + r) * LDL + 16 * bi + c] = col[r];
-      } else {
-        for (int id = tid - 64; id < 512; id += NTHR - 64) {  // blocks (0,1), (2,3) of T are zero
-          const int blk = id >> 8, e = id & 255;
-          sT[(32 * blk + (e >> 4)) * LDL + 32 * blk + 16 + (e & 15)] = 0.0f;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (r >= c) sLT[(16 * bi + r) * LDL + 16 * bi + c] = col[r];
       }
       __syncthreads();
       // ---- phase D: off-diagonal blocks T_ij = -T_ii sum_{k=j}^{i-1} L_ik T_kj, by
       // sub-diagonal level, on fp32 MFMA (16x16x4)
 #pragma unroll
       for (int level = 1; level <= 3; ++level) {
+        LA_FENCE();
         if (wave < 4 - level) {
           const int j = wave, i = wave + level;
           f32x4 x = {0.f, 0.f, 0.f, 0.f};
           for (int kb = j; kb < i; ++kb) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              const float fa = sL[(16 * i + l16) * LDL + 16 * kb + 4 * s + g];
-              const float fb = sT[(16 * kb + 4 * s + g) * LDL + 16 * j + l16];
+              const int kr = 4 * s + g;  // row of the k-block
+              const float fa = sLT[(16 * kb + kr) * LDL + 16 * i + l16];
+              float fb = sLT[(16 * kb + kr) * LDL + 16 * j + l16];
+              if (kb == j && l16 > kr) fb = 0.0f;  // upper part of a diagonal block
               x = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, x, 0, 0, 0);
             }
           }
           f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {  // inner index 4 g + s: x's own rows serve as B
-            const float fa = sT[(16 * i + l16) * LDL + 16 * i + 4 * g + s];
+            float fa = sLT[(16 * i + l16) * LDL + 16 * i + 4 * g + s];
+            if (4 * g + s > l16) fa = 0.0f;
             y = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, x[s], y, 0, 0, 0);
           }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * g + e) * LDL + 16 * j + l16] = -y[e];
+          for (int e = 0; e < 4; ++e) sLT[(16 * i + 4 * g + e) * LDL + 16 * j + l16] = -y[e];
         }
         __syncthreads();
       }
-      // ---- phase E: W = T diag(beta gamma) K (stored negated, bf16) and U~ = T diag(beta) V
-      // (kept in registers by the wave that owns those state rows)
+      // ---- phase E1: U~ = T diag(beta) V for this wave's own state rows (registers)
+      if (!m_kind) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          LA_FENCE();
+          Ut[mt][0] = {0.f, 0.f, 0.f, 0.f};
+          Ut[mt][1] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            if (s == 1 && mt < 2) continue;  // T is lower triangular
+            const bf16x8 fa = t_frag(sLT, sBeta, 16 * mt + l16, s, g);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              Ut[mt][c] = mfma_bf16(fa, col_frag(sV, LDK, 2 * wave + c, s, lane_v), Ut[mt][c]);
+          }
+        }
+      }
+      __syncthreads();
+      // ---- phase E2: W = T diag(beta gamma) K, stored negated (bf16) over V
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4 accw[NCT], accu[NCT];
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-          accw[c] = {0.f, 0.f, 0.f, 0.f};
-          accu[c] = {0.f, 0.f, 0.f, 0.f};
-        }
+        LA_FENCE();
+        f32x4 accw[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          if (s == 1 && mt < 2) continue;  // T is lower triangular
-          const f32x4 t0 = ld4(sT + (16 * mt + l16) * LDL + 32 * s + 4 * g);
-          const f32x4 t1 = ld4(sT + (16 * mt + l16) * LDL + 32 * s + 16 + 4 * g);
-          if (MODE == MODE_OUT || wave >= NW / 2) {
-            const f32x4 b0 = ld4(sBG + 32 * s + 4 * g), b1 = ld4(sBG + 32 * s + 16 + 4 * g);
-            const bf16x8 fa = pack_pair(t0 * b0, t1 * b1);
+          if (s == 1 && mt < 2) continue;
+          const bf16x8 fa = t_frag(sLT, sBG, 16 * mt + l16, s, g);
 #pragma unroll
-            for (int c = 0; c < NCT; ++c) {
-              const int nt = MODE == MODE_OUT ? wave : 2 * (wave - NW / 2) + c;
-              accw[c] = mfma_bf16(fa, frag_pair(sKt, LDT, 16 * nt + l16, 32 * s, g), accw[c]);
-            }
-          }
-          if (MODE == MODE_OUT || wave < NW / 2) {
-            const f32x4 b0 = ld4(sBeta + 32 * s + 4 * g), b1 = ld4(sBeta + 32 * s + 16 + 4 * g);
-            const bf16x8 fa = pack_pair(t0 * b0, t1 * b1);
-#pragma unroll
-            for (int c = 0; c < NCT; ++c) {
-              const int nt = MODE == MODE_OUT ? wave : 2 * wave + c;
-              accu[c] = mfma_bf16(fa, frag_pair(sVt, LDT, 16 * nt + l16, 32 * s, g), accu[c]);
-            }
-          }
-        }
-        if (MODE == MODE_OUT || wave >= NW / 2) {
-#pragma unroll
-          for (int c = 0; c < NCT; ++c) {
-            const int nt = MODE == MODE_OUT ? wave : 2 * (wave - NW / 2) + c;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sW[(16 * mt + 4 * g + e) * LDK + 16 * nt + l16] = f32_to_bf16(-accw[c][e]);
-          }
+          for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(fa, col_frag(sK, LDK, 2 * wave + c, s, lane_v), accw[c]);
         }
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) Ut[mt][c] = accu[c];
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sW[(16 * mt + 4 * g + e) * LDK + 16 * (2 * wave + c) + l16] = f32_to_bf16(-accw[c][e]);
       }
       __syncthreads();
     }
 
-    // ---- phase F: the state-dependent part, per wave on its own state rows
-    bf16x8 ufr[NCT][2], dufr[NCT][2];  // U and diag(decay) U as B operands (k = tokens)
-    bf16x8 sfr[NCT][DK / 32];          // S^T as B operand (k = d_k)
+    // ---- phase F: the state-dependent part, per wave on its own 32 state rows
+    f32x4 U[4][2], O[4][2];
 #pragma unroll
-    for (int c = 0; c < NCT; ++c)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int s = 0; s < DK / 32; ++s) sfr[c][s] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
-    if (DELTA) {
+      for (int c = 0; c < 2; ++c) {
+        U[mt][c] = (DELTA && !m_kind) ? Ut[mt][c] : f32x4{0.f, 0.f, 0.f, 0.f};
+        O[mt][c] = {0.f, 0.f, 0.f, 0.f};
+      }
+    if (DELTA || OUT) {  // U = U~ - W S^T and O = Q S^T, sharing the S^T operands
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        f32x4 U[4];
+      for (int s = 0; s < DK / 32; ++s) {
+        bf16x8 sfr[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          f32x4 acc = m_rows ? f32x4{0.f, 0.f, 0.f, 0.f} : Ut[mt][c];
+          LA_FENCE();
+          if (DELTA) {
+            const bf16x8 wf = frag_pair(sW, LDK, 16 * mt + l16, 32 * s, g);
 #pragma unroll
-          for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(frag_pair(sW, LDK, 16 * mt + l16, 32 * s, g), sfr[c][s], acc);
-          U[mt] = acc;
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const f32x4 d0 = ld4(sDec + 32 * s2 + 4 * g), d1 = ld4(sDec + 32 * s2 + 16 + 4 * g);
-          ufr[c][s2] = pack_pair(U[2 * s2], U[2 * s2 + 1]);
-          dufr[c][s2] = pack_pair(U[2 * s2] * d0, U[2 * s2 + 1] * d1);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        const int dvr = row0 + 16 * c + l16;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 vf = frag_pair(sVt, LDT, dvr, 32 * s2, g);
-          const f32x4 b0 = ld4(sBeta + 32 * s2 + 4 * g), b1 = ld4(sBeta + 32 * s2 + 16 + 4 * g);
-          const f32x4 d0 = ld4(sDec + 32 * s2 + 4 * g), d1 = ld4(sDec + 32 * s2 + 16 + 4 * g);
-          f32x4 v0, v1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v0[e] = (float)vf[e] * b0[e];
-            v1[e] = (float)vf[4 + e] * b1[e];
+            for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(wf, sfr[c], U[mt][c]);
           }
-          ufr[c][s2] = pack_pair(v0, v1);
-          dufr[c][s2] = pack_pair(v0 * d0, v1 * d1);
+          if (OUT) {
+            const bf16x8 qf = frag_pair(sQ, LDK, 16 * mt + l16, 32 * s, g);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(qf, sfr[c], O[mt][c]);
+          }
         }
       }
     }
-    if (MODE == MODE_OUT) {  // O = diag(gamma) Q S^T + A U  -> bf16 staging for coalesced stores
+    LA_FENCE();
+    bf16x8 ufr[2][2], dufr[2][2];  // U and diag(decay) U as operands with k = tokens
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const f32x4 d0 = ld4(sDec + 32 * s2 + 4 * g), d1 = ld4(sDec + 32 * s2 + 16 + 4 * g);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x4 u0, u1;
+        if (DELTA) {
+          u0 = U[2 * s2][c];
+          u1 = U[2 * s2 + 1][c];
+        } else {  // U = diag(beta) V, read along tokens from the V tile
+          const bf16x8 vf = col_frag(sV, LDK, 2 * wave + c, s2, lane_v);
+          const f32x4 b0 = ld4(sBeta + 32 * s2 + 4 * g), b1 = ld4(sBeta + 32 * s2 + 16 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            u0[e] = (float)vf[e] * b0[e];
+            u1[e] = (float)vf[4 + e] * b1[e];
+          }
+        }
+        ufr[c][s2] = pack_pair(u0, u1);
+        dufr[c][s2] = pack_pair(u0 * d0, u1 * d1);
+      }
+    }
+    if (OUT) {  // O = diag(gamma) Q S^T + A U  -> bf16 staging for coalesced stores
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        LA_FENCE();
+        const f32x4 gam = ld4(sGam + 16 * mt + 4 * g);
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(frag_pair(sQ, LDK, 16 * mt + l16, 32 * s, g), sfr[0][s], acc);
-        acc = acc * ld4(sGam + 16 * mt + 4 * g);
+        for (int c = 0; c < 2; ++c) O[mt][c] = O[mt][c] * gam;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (s2 == 1 && mt < 2) continue;  // A is causal
-          acc = mfma_bf16(frag_pair(sA, LDA, 16 * mt + l16, 32 * s2, g), ufr[0][s2], acc);
+          const bf16x8 af = frag_pair(sA, LDA, 16 * mt + l16, 32 * s2, g);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(af, ufr[c][s2], O[mt][c]);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sO[(16 * mt + 4 * g + e) * LDK + row0 + l16] = f32_to_bf16(acc[e]);
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sO[(16 * mt + 4 * g + e) * LDK + row0 + 16 * c + l16] = f32_to_bf16(O[mt][c][e]);
       }
     }
     {  // S^T <- gamma_C S^T + K^T diag(decay) U
       const float gC = sGam[C - 1];
       gseg += sG[C - 1];
 #pragma unroll
-      for (int m = 0; m < DK / 16; ++m)
+      for (int m = 0; m < DK / 16; ++m) {
+        LA_FENCE();
+        const bf16x8 k0 = col_frag(sK, LDK, m, 0, lane_v), k1 = col_frag(sK, LDK, m, 1, lane_v);
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
+        for (int c = 0; c < 2; ++c) {
           f32x4 acc = st[m][c] * gC;
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) acc = mfma_bf16(frag_pair(sKt, LDT, 16 * m + l16, 32 * s2, g), dufr[c][s2], acc);
+          acc = mfma_bf16(k0, dufr[c][0], acc);
+          acc = mfma_bf16(k1, dufr[c][1], acc);
           st[m][c] = acc;
         }
+      }
     }
     __syncthreads();
     prev_t0 = t0;
     prev_n = n;
   }
 
-  if (MODE == MODE_OUT) {
+  if (OUT) {
     if (prev_t0 >= 0) {
       for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
         const int r = id / (DV / 8), cv = id % (DV / 8);
@@ -430,22 +516,26 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(const Args a) {
     }
     if (a.nseg == 1 && a.S_T) {
 #pragma unroll
-      for (int m = 0; m < DK / 16; ++m) {
-        const int r = row0 + l16;
-        *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + 16 * m + 4 * g) = st[m][0];
-      }
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int r = row0 + 16 * c + l16;
+          *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + 16 * m + 4 * g) = st[m][c];
+        }
     }
   } else {
-    float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
+    float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK + (m_kind ? (size_t)DV * DK : 0);
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
+      for (int c = 0; c < 2; ++c) {
         const int r = row0 + 16 * c + l16;
         *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + 16 * m + 4 * g) = st[m][c];
       }
     if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
   }
+#undef LA_PREFETCH
+#undef LA_LD1
 }
 
 // Pass 2: S_{i+1} = S_i M_i + B_i (delta rule) or e^{gsum_i} S_i + B_i, row-parallel:
@@ -538,13 +628,21 @@ size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int 
   return gdn::ws_layout(variant == V_GATED_DELTA, B, H, T, &a, &b, &c);
 }
 
+void chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks) {
+  const gdn::Plan p = gdn::make_plan(B, H, T);
+  *nseg = p.nseg;
+  *seg_chunks = p.seg_chunks;
+}
+
 hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, int d_v,
                                 const void *q, const void *k, const void *v, const void *alpha,
                                 const void *beta, const float *S0, void *o, float *S_T,
-                                void *workspace, hipStream_t s) {
+                                void *workspace, int pass_mask, hipStream_t s) {
   using namespace gdn;
-  if (d_k != DK || d_v != DV)  // other widths: the token-recurrent kernel (fp32 arithmetic)
+  if (d_k != DK || d_v != DV) {  // other widths: the token-recurrent kernel (fp32 arithmetic)
+    if (!(pass_mask & PASS_REPLAY)) return hipSuccess;
     return launch_recurrent_rows(variant, T_BF16, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+  }
   const bool delta = variant == V_GATED_DELTA;
   const Plan p = make_plan(B, H, T);
   size_t om = 0, og = 0, os = 0;
@@ -568,14 +666,18 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   a.variant = variant;
   a.has_beta = beta != nullptr;
   const dim3 grid(p.nseg, H, B);
-  if (p.nseg > 1) {
-    if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_MAP, true>), grid, dim3(NTHR), 0, s, a);
+  if (p.nseg > 1 && (pass_mask & PASS_MAPS)) {  // delta rule: B-row and M-row workgroups
+    if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_MAP, true>), dim3(2 * p.nseg, H, B), dim3(NTHR), 0, s, a);
     else hipLaunchKernelGGL((chunk_kernel<MODE_MAP, false>), grid, dim3(NTHR), 0, s, a);
+  }
+  if (p.nseg > 1 && (pass_mask & PASS_SCAN)) {
     if (delta) hipLaunchKernelGGL((scan_kernel<true>), dim3(DV / 4, H, B), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((scan_kernel<false>), dim3(DV / 4, H, B), dim3(256), 0, s, a);
   }
-  if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_OUT, true>), grid, dim3(NTHR), 0, s, a);
-  else hipLaunchKernelGGL((chunk_kernel<MODE_OUT, false>), grid, dim3(NTHR), 0, s, a);
+  if (pass_mask & PASS_REPLAY) {
+    if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_OUT, true>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((chunk_kernel<MODE_OUT, false>), grid, dim3(NTHR), 0, s, a);
+  }
   return hipGetLastError();
 }
 

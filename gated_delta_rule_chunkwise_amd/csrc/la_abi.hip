@@ -96,10 +96,12 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
   return LA_OK;
 }
 
-int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k, int d_v,
-               float eps, const void *q, const void *k, const void *v, const void *alpha,
-               const void *beta, const float *S0, const float *z0, void *o, float *S_T,
-               float *z_T, void *workspace, size_t workspace_bytes, void *stream) {
+static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int heads,
+                        int64_t seq_len, int d_k, int d_v, float eps, const void *q,
+                        const void *k, const void *v, const void *alpha, const void *beta,
+                        const float *S0, const float *z0, void *o, float *S_T, float *z_T,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (pass_mask <= 0 || pass_mask > PASS_ALL) return LA_ERR_INVALID;
   int st = check_prefill_shape(variant, dtype, batch, heads, seq_len, d_k, d_v);
   if (st != LA_OK) return st;
   const int B = batch, H = heads;
@@ -151,22 +153,59 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (T == 0) {  // empty sequence: the end state is the start state
+    if (!(pass_mask & PASS_REPLAY)) return LA_OK;
     if (S_T) e = launch_copy_or_zero(S0, S_T, state_n, s);
     if (e == hipSuccess && z_T) e = launch_copy_or_zero(z0, z_T, BH * D, s);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
   }
   if (based) {
     if (dtype == LA_BF16)
-      e = launch_based_chunk_prefill(B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, workspace, s);
-    else
+      e = launch_based_chunk_prefill(B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, workspace, pass_mask, s);
+    else if (pass_mask & PASS_REPLAY)
       e = launch_recurrent_based(dtype, B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, s);
   } else if (dtype == LA_BF16) {
-    e = launch_chunk_prefill(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, workspace, s);
-  } else {
+    e = launch_chunk_prefill(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, workspace,
+                             pass_mask, s);
+  } else if (pass_mask & PASS_REPLAY) {
     e = launch_recurrent_rows(variant, dtype, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
   }
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
+
+int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k, int d_v,
+               float eps, const void *q, const void *k, const void *v, const void *alpha,
+               const void *beta, const float *S0, const float *z0, void *o, float *S_T,
+               float *z_T, void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_impl(PASS_ALL, variant, dtype, batch, heads, seq_len, d_k, d_v, eps, q, k, v,
+                      alpha, beta, S0, z0, o, S_T, z_T, workspace, workspace_bytes, stream);
+}
+
+int la_prefill_pass(int pass, int variant, int dtype, int batch, int heads, int64_t seq_len,
+                    int d_k, int d_v, float eps, const void *q, const void *k, const void *v,
+                    const void *alpha, const void *beta, const float *S0, const float *z0,
+                    void *o, float *S_T, float *z_T, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  if (pass != LA_PASS_MAPS && pass != LA_PASS_SCAN && pass != LA_PASS_REPLAY) return LA_ERR_INVALID;
+  const int mask = pass == LA_PASS_MAPS ? PASS_MAPS : (pass == LA_PASS_SCAN ? PASS_SCAN : PASS_REPLAY);
+  return prefill_impl(mask, variant, dtype, batch, heads, seq_len, d_k, d_v, eps, q, k, v, alpha,
+                      beta, S0, z0, o, S_T, z_T, workspace, workspace_bytes, stream);
+}
+
+int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k,
+                        int d_v, int *n_segments, int *chunks_per_segment) {
+  if (!n_segments || !chunks_per_segment) return LA_ERR_NULL;
+  const int st = check_prefill_shape(variant, dtype, batch, heads, seq_len, d_k, d_v);
+  if (st != LA_OK) return st;
+  *n_segments = 1;
+  *chunks_per_segment = 0;
+  if (dtype != LA_BF16 || seq_len == 0) return LA_OK;
+  if (variant == LA_BASED)
+    based_chunk_segments(batch, heads, seq_len, n_segments, chunks_per_segment);
+  else if (d_k == 128 && d_v == 128)
+    chunk_segments(batch, heads, seq_len, n_segments, chunks_per_segment);
+  return LA_OK;
+}
+
 
 int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, const float *S_in,
                    const float *z_in, float *S_out, float *z_out, const void *q, const void *k,

@@ -30,17 +30,21 @@ hipError_t launch_recurrent_based(int dtype, int B, int H, int64_t T, float eps,
 
 // chunk.hip (chunkwise bf16 prefill for ADDITIVE / GATED / GATED_DELTA)
 size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v);
+// pass_mask: PASS_MAPS | PASS_SCAN | PASS_REPLAY (see la_prefill_pass in la.h)
+enum { PASS_MAPS = 1, PASS_SCAN = 2, PASS_REPLAY = 4, PASS_ALL = 7 };
 hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, int d_v,
                                 const void *q, const void *k, const void *v, const void *alpha,
                                 const void *beta, const float *S0, void *o, float *S_T,
-                                void *workspace, hipStream_t s);
+                                void *workspace, int pass_mask, hipStream_t s);
+void chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks);
 
 // based_chunk.hip (chunkwise bf16 BASED prefill)
 size_t based_chunk_workspace_bytes(int B, int H, int64_t T);
 hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const void *q,
                                       const void *k, const void *v, const float *s0,
                                       const float *z0, void *o, float *s_T, float *z_T,
-                                      void *workspace, hipStream_t s);
+                                      void *workspace, int pass_mask, hipStream_t s);
+void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks);
 
 // util (la_abi.hip): copy or zero-fill n floats with a kernel (capture-safe, no memset nodes)
 hipError_t launch_copy_or_zero(const float *src, float *dst, size_t n, hipStream_t s);

@@ -130,6 +130,40 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
                float *z_T, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * la_prefill_pass -- run one of the three passes of la_prefill, for callers that
+ * schedule them separately (to time them, to overlap them with other work, or to
+ * shard one sequence across devices, where the scan becomes an exchange of per-slice
+ * maps).  With the same arguments and workspace on one stream,
+ *
+ *   la_prefill(...)  ==  la_prefill_pass(LA_PASS_MAPS, ...);
+ *                        la_prefill_pass(LA_PASS_SCAN, ...);
+ *                        la_prefill_pass(LA_PASS_REPLAY, ...);
+ *
+ *   LA_PASS_MAPS    per segment of chunks, the affine map of its end state on its start
+ *                   state (S_end = S_start M + B; M is d_k x d_k for the gated delta
+ *                   rule, a scalar decay otherwise), written to the workspace
+ *   LA_PASS_SCAN    segment start states S_{i+1} = S_i M_i + B_i from S0, and S_T
+ *   LA_PASS_REPLAY  every segment from its start state: o (and S_T for one segment)
+ *
+ * Passes that do not apply to a problem (one segment, fp32 inputs, other widths) do
+ * nothing; LA_PASS_REPLAY then performs the whole computation.  Arguments, validation
+ * and return values are those of la_prefill.
+ */
+enum { LA_PASS_MAPS = 1, LA_PASS_SCAN = 2, LA_PASS_REPLAY = 3 };
+int la_prefill_pass(int pass, int variant, int dtype, int batch, int heads, int64_t seq_len,
+                    int d_k, int d_v, float eps, const void *q, const void *k, const void *v,
+                    const void *alpha, const void *beta, const float *S0, const float *z0,
+                    void *o, float *S_T, float *z_T, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * How la_prefill splits each (b, h) sequence: *n_segments segments of
+ * *chunks_per_segment chunks of 64 tokens (1 and 0 when the chunked path is not used).
+ */
+int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k,
+                        int d_v, int *n_segments, int *chunks_per_segment);
+
+/*
  * la_decode_step -- one token for N independent states (e.g. N = sequences x heads):
  *
  *   S_out = S_in A + beta v k^T,  o = S_out q      (BASED: s, z updated, o normalised)
