@@ -141,9 +141,19 @@ __device__ __forceinline__ bf16x8 t_frag(const float *LT, const float *sc, int t
   return pack_pair(a, b);
 }
 
+// Waves per workgroup: 4 (32 state rows each), or 8 for the delta-rule map pass, whose
+// workgroup carries both the 128 B rows (waves 0-3) and the 128 M rows (waves 4-7) so
+// that the state-independent work of a chunk is done once for both.
+template <int MODE, bool DELTA> struct Waves {
+  static constexpr int value = (MODE == MODE_MAP && DELTA) ? 8 : NW;
+};
+
 template <int MODE, bool DELTA>
-__global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
+__global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW / 4)) void chunk_kernel(const Args a) {
   constexpr bool OUT = MODE == MODE_OUT;
+  constexpr int NWT = Waves<MODE, DELTA>::value;  // waves in this workgroup
+  constexpr int NT = NWT * 64;
+  constexpr int NLD = C * (DK / 8) / NT;           // 16-byte tile loads per thread
   constexpr int MAPROWS = DELTA ? 2 * DV : DV;
   constexpr int OFF_K = 0;
   constexpr int OFF_Q = SZ_ROW;  // MODE_OUT only
@@ -168,9 +178,9 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  // pass 1 with the delta rule runs two workgroups per segment: B rows and M rows
-  const bool m_kind = (MODE == MODE_MAP) && DELTA && (int)blockIdx.x >= a.nseg;
-  const int seg = m_kind ? (int)blockIdx.x - a.nseg : (int)blockIdx.x;
+  // in the delta-rule map pass, waves 4-7 carry the transition (M) rows
+  const bool m_kind = (MODE == MODE_MAP) && DELTA && wave >= NW;
+  const int seg = (int)blockIdx.x;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
   const int row0 = wave * RPW;  // first state row owned by this wave
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)  // identity for the transition rows, zero otherwise
-            st[m][c][e] = (m_kind && r == 16 * m + 4 * g + e) ? 1.0f : 0.0f;
+            st[m][c][e] = (m_kind && r - DV == 16 * m + 4 * g + e) ? 1.0f : 0.0f;
         }
       }
   }
@@ -198,10 +208,10 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
   // ---- register prefetch of one chunk: 4 x 16 bytes of K (and Q, V) per thread
   u32x4 pk[4], pq[4], pv[4];
   float pal = 1.0f, pbe = 0.0f;
-  const bool load_v = !m_kind;
+  const bool load_v = true;
 #define LA_LD1(i)                                                                                \
   do {                                                                                           \
-    const int id = tid + NTHR * (i), r = id >> 4, cv = id & 15;                                  \
+    const int id = tid + NT * (i), r = id >> 4, cv = id & 15;                                    \
     const u32x4 z = {0u, 0u, 0u, 0u};                                                            \
     pk[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.k + (prb + r) * DK + cv * 8) : z;       \
     if (OUT) pq[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.q + (prb + r) * DK + cv * 8) : z; \
@@ -212,7 +222,9 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
     const int64_t pt0 = (T0);                                                                    \
     const int pn = (int)((T - pt0) < C ? (T - pt0) : C);                                         \
     const size_t prb = bh * (size_t)T + pt0;                                                     \
-    LA_LD1(0); LA_LD1(1); LA_LD1(2); LA_LD1(3);                                                  \
+    LA_LD1(0);                                                                                   \
+    if (NLD > 1) LA_LD1(1);                                                                      \
+    if (NLD > 2) { LA_LD1(2); LA_LD1(3); }                                                       \
     if (wave == 0) {                                                                             \
       pal = 1.0f;                                                                                \
       pbe = 0.0f;                                                                                \
@@ -245,16 +257,16 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
     // ---- phase A: write out the previous chunk's O, move the prefetched chunk to LDS,
     // gate prefix sums
     if (OUT && prev_t0 >= 0) {
-      for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
+      for (int id = tid; id < prev_n * (DV / 8); id += NT) {
         const int r = id / (DV / 8), cv = id % (DV / 8);
-        *reinterpret_cast<uint4 *>(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8) =
-            *reinterpret_cast<const uint4 *>(sO + r * LDK + cv * 8);
+        gst16(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8,
+              *reinterpret_cast<const u32x4 *>(sO + r * LDK + cv * 8));
       }
     }
     if (!PREFETCH) LA_PREFETCH(t0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + NTHR * i, r = id >> 4, cv = id & 15;
+    for (int i = 0; i < NLD; ++i) {
+      const int id = tid + NT * i, r = id >> 4, cv = id & 15;
       *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * 8) = pk[i];
       if (OUT) *reinterpret_cast<u32x4 *>(sQ + r * LDK + cv * 8) = pq[i];
       if (load_v) *reinterpret_cast<u32x4 *>(sV + r * LDK + cv * 8) = pv[i];
@@ -278,40 +290,78 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
 
     // ---- phase B: start loading the next chunk; Gram tiles K K^T (-> L^T) and Q K^T (-> A)
     if (PREFETCH && ci + 1 < nchunks) LA_PREFETCH(t0 + C);
-    {
-      constexpr int NJ = (DELTA ? 10 : 0) + (OUT ? 10 : 0);
-      for (int job = wave; job < NJ; job += NW) {
-        const bool kk = DELTA && job < 10;
+    if (OUT) {
+      // Row-tile ownership: wave w computes the K K^T tiles of row tile w and the Q K^T
+      // tiles of row tile 3 - w (five tiles per wave); the A fragments of both row tiles
+      // are loaded once and each K row tile (the B fragments) once per wave.
+      const int tk = wave, tq = 3 - wave;
+      bf16x8 ak[DK / 32], aq[DK / 32];
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) {
+        if (DELTA) ak[s] = *reinterpret_cast<const bf16x8 *>(sK + (16 * tk + l16) * LDK + 32 * s + 8 * g);
+        aq[s] = *reinterpret_cast<const bf16x8 *>(sQ + (16 * tq + l16) * LDK + 32 * s + 8 * g);
+      }
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        LA_FENCE();
+        const bool do_kk = DELTA && tj <= tk;
+        const bool do_qk = tj <= tq;
+        if (!(do_kk || do_qk)) continue;
+        bf16x8 b[DK / 32];
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s)
+          b[s] = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
+        const int j = 16 * tj + l16;
+        const float gj = sG[j];
+        if (do_kk) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(ak[s], b[s], acc);
+          f32x4 lv;  // L_tj at the transposed position [j][t]
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * tk + 4 * g + e;
+            lv[e] = (t > j) ? sBeta[t] * expf(sG[t] - gj) * acc[e] : 0.0f;
+          }
+          *reinterpret_cast<f32x4 *>(sLT + j * LDL + 16 * tk + 4 * g) = lv;
+        }
+        if (do_qk) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(aq[s], b[s], acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * tq + 4 * g + e;
+            sA[t * LDA + j] = f32_to_bf16((t >= j) ? expf(sG[t] - gj) * acc[e] : 0.0f);
+          }
+        }
+      }
+    } else if (DELTA) {
+      // K K^T tiles only, (ti, tj) with tj <= ti, dealt round robin over the waves
+      for (int job = wave; job < 10; job += NWT) {
         int ti, tj;
-        tri_index(kk ? job : job - (DELTA ? 10 : 0), ti, tj);
-        const bf16_t *X = kk ? sK : sQ;
+        tri_index(job, ti, tj);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
-          const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(X + (16 * ti + l16) * LDK + 32 * s + 8 * g);
+          const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sK + (16 * ti + l16) * LDK + 32 * s + 8 * g);
           const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
           acc = mfma_bf16(fa, fb, acc);
         }
         const int j = 16 * tj + l16;
         const float gj = sG[j];
-        if (kk) {  // L_tj at the transposed position [j][t]
-          f32x4 lv;
+        f32x4 lv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 16 * ti + 4 * g + e;
-            lv[e] = (t > j) ? sBeta[t] * expf(sG[t] - gj) * acc[e] : 0.0f;
-          }
-          *reinterpret_cast<f32x4 *>(sLT + j * LDL + 16 * ti + 4 * g) = lv;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 16 * ti + 4 * g + e;
-            sA[t * LDA + j] = f32_to_bf16((t >= j) ? expf(sG[t] - gj) * acc[e] : 0.0f);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * ti + 4 * g + e;
+          lv[e] = (t > j) ? sBeta[t] * expf(sG[t] - gj) * acc[e] : 0.0f;
         }
+        *reinterpret_cast<f32x4 *>(sLT + j * LDL + 16 * ti + 4 * g) = lv;
       }
+    }
+    {
       if (OUT) {  // the two above-diagonal tiles read by the A U products
-        for (int id = tid; id < 512; id += NTHR) {
+        for (int id = tid; id < 512; id += NT) {
           const int tile = id >> 8, e = id & 255;
           sA[(32 * tile + (e >> 4)) * LDA + 32 * tile + 16 + (e & 15)] = 0;
         }
@@ -389,6 +439,7 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
       }
       __syncthreads();
       // ---- phase E2: W = T diag(beta gamma) K, stored negated (bf16) over V
+      constexpr int WPT = 8 / NWT;  // W column tiles per wave
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         LA_FENCE();
@@ -398,13 +449,13 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
           if (s == 1 && mt < 2) continue;
           const bf16x8 fa = t_frag(sLT, sBG, 16 * mt + l16, s, g);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(fa, col_frag(sK, LDK, 2 * wave + c, s, lane_v), accw[c]);
+          for (int c = 0; c < WPT; ++c) accw[c] = mfma_bf16(fa, col_frag(sK, LDK, WPT * wave + c, s, lane_v), accw[c]);
         }
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < WPT; ++c)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sW[(16 * mt + 4 * g + e) * LDK + 16 * (2 * wave + c) + l16] = f32_to_bf16(-accw[c][e]);
+            sW[(16 * mt + 4 * g + e) * LDK + 16 * (WPT * wave + c) + l16] = f32_to_bf16(-accw[c][e]);
       }
       __syncthreads();
     }
@@ -508,10 +559,10 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
 
   if (OUT) {
     if (prev_t0 >= 0) {
-      for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
+      for (int id = tid; id < prev_n * (DV / 8); id += NT) {
         const int r = id / (DV / 8), cv = id % (DV / 8);
-        *reinterpret_cast<uint4 *>(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8) =
-            *reinterpret_cast<const uint4 *>(sO + r * LDK + cv * 8);
+        gst16(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8,
+              *reinterpret_cast<const u32x4 *>(sO + r * LDK + cv * 8));
       }
     }
     if (a.nseg == 1 && a.S_T) {
@@ -524,7 +575,7 @@ __global__ __launch_bounds__(NTHR, WG_PER_CU) void chunk_kernel(const Args a) {
         }
     }
   } else {
-    float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK + (m_kind ? (size_t)DV * DK : 0);
+    float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
@@ -666,8 +717,8 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   a.variant = variant;
   a.has_beta = beta != nullptr;
   const dim3 grid(p.nseg, H, B);
-  if (p.nseg > 1 && (pass_mask & PASS_MAPS)) {  // delta rule: B-row and M-row workgroups
-    if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_MAP, true>), dim3(2 * p.nseg, H, B), dim3(NTHR), 0, s, a);
+  if (p.nseg > 1 && (pass_mask & PASS_MAPS)) {
+    if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_MAP, true>), grid, dim3(Waves<MODE_MAP, true>::value * 64), 0, s, a);
     else hipLaunchKernelGGL((chunk_kernel<MODE_MAP, false>), grid, dim3(NTHR), 0, s, a);
   }
   if (p.nseg > 1 && (pass_mask & PASS_SCAN)) {
