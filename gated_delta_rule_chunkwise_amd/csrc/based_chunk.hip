@@ -1,22 +1,484 @@
-// based_chunk.hip -- chunkwise bf16 BASED prefill (bring-up stub: token-recurrent path).
+// based_chunk.hip -- chunkwise bf16 prefill for BASED Taylor linear attention (d' = 16,
+// d_v = 64, D = 273 features).
+//
+// What is computed ("Simple linear attention language models balance the
+// recall-throughput tradeoff", reading notes Sec. 2.2-2.3, paper Eqs. (1)-(4)):
+//   phi(x) = [1, x, vec(x x^T)/sqrt 2],  s_t = s_{t-1} + phi(k_t) v_t^T,
+//   z_t = z_{t-1} + phi(k_t),  o_t = s_t^T phi(q_t) / (z_t^T phi(q_t) + eps).
+// Blockwise (the notes' Sec. 2.5 form U_b = (M_b . Phi_Q Phi_K^T) V_b + Phi_Q S_{<b}, and
+// its normaliser), for a chunk of C = 64 tokens entering with (s, z):
+//   A_tj = 1 + q_t.k_j + (q_t.k_j)^2 / 2 for j <= t, else 0   (= phi(q_t).phi(k_j))
+//   num  = Phi_Q s + A V,   den = Phi_Q z + A 1,   o = num / (den + eps)
+//   s   += Phi_K^T V,       z  += Phi_K^T 1
+// The in-chunk term uses the closed form of the kernel, so phi is never multiplied out
+// there; Phi_Q and Phi_K^T enter only the products with the state, and their entries are
+// generated in registers from q and k while the MFMA operands are built (the feature
+// expansion never touches LDS or HBM, which is the point the notes make about the
+// IO-aware kernel).
+//
+// gfx950 layout.  Internally the features are reordered so that the 256 order-2 features
+// come first (feature 16 i + j = x_i x_j / sqrt 2), then x_0..x_15, then the constant
+// (padded to 288 = 18 tiles of 16); the ABI layout [1, x, x (x) x] is restored when
+// states are read or written.  Four waves each own one 16-column tile of s (18 x 4 fp32
+// accumulator tiles, 72 registers); the normaliser z lives in LDS in fp32 and enters
+// the MFMAs as a one-column operand.  Every MFMA is v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation; token-contraction operands of k and v are read with ds_read_b64_tr_b16.
+//
+// Sequence parallelism: as for the gated recurrences, long sequences are split into
+// segments; since A_t = I here, a segment's map is a plain sum (delta s, delta z), so
+// pass 1 computes the sums from a zero state, pass 2 takes exclusive prefix sums over
+// segments, and pass 3 replays every segment from its start state.
 #include "la_device.h"
 #include "la_launch.h"
 
 namespace la {
+namespace based {
 
-size_t based_chunk_workspace_bytes(int, int, int64_t) { return 0; }
+constexpr int C = 64;    // tokens per chunk
+constexpr int DP = 16;   // q/k width d'
+constexpr int DV = 64;   // value width
+constexpr int D = 1 + DP + DP * DP;  // 273 features (ABI)
+constexpr int NF = 288;  // padded internal features (18 tiles)
+constexpr int NFT = NF / 16;
+constexpr int NW = 4;
+constexpr int NTHR = NW * 64;
 
-void based_chunk_segments(int, int, int64_t, int *nseg, int *seg_chunks) {
-  *nseg = 1;
-  *seg_chunks = 0;
+constexpr int LDQ = DP + 8;  // bf16 [C][DP] row-major q, k tiles (48-byte rows)
+constexpr int LDV = DV + 8;  // bf16 [C][DV] row-major v tile, o staging
+constexpr int LDKT = C + 8;  // bf16 [DP][C] k transposed
+constexpr int LDA = C + 8;   // bf16 [C][C] kernel matrix
+
+enum { MODE_MAP = 0, MODE_OUT = 1 };
+
+struct Args {
+  const bf16_t *q, *k, *v;
+  const float *s0, *z0;  // ABI layout; start state for a single segment (may be NULL)
+  bf16_t *o;
+  float *s_T, *z_T;      // ABI layout; written by pass 3 when there is a single segment
+  float *dsum;           // [BH][nseg][NF][DV + 1] per-segment sums (internal order; col DV = z)
+  float *starts;         // [BH][nseg][NF][DV + 1] segment start states (internal order)
+  int64_t T;
+  int H, nseg, seg_chunks;
+  float eps;
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ABI feature index of internal feature fi (-1 for padding)
+__device__ __forceinline__ int abi_feature(int fi) {
+  return fi < 256 ? 1 + DP + fi : (fi < 256 + DP ? 1 + (fi - 256) : (fi == 256 + DP ? 0 : -1));
+}
+
+__device__ __forceinline__ bf16x8 pack_pair(f32x4 a, f32x4 b) {
+  return pack8(a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
+}
+
+__device__ __forceinline__ f32x4 u16x4_to_f32(uint2 u) {
+  f32x4 r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xffff0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
+
+// Column 16 nt + (lane & 15) of a row-major [token][*] tile at tokens 32 s + 4 g + 0..3 and
+// 32 s + 16 + 4 g + 0..3 (g = lane >> 4), via the CDNA4 transpose read (see chunk.hip).
+__device__ __forceinline__ bf16x8 col_frag(const bf16_t *tile, int ld, int nt, int s, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const bf16_t *p0 = tile + (32 * s + 4 * g + (i >> 2)) * ld + 16 * nt + 4 * (i & 3);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + 16 * ld));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 frag_pair(const bf16_t *base, int ld, int row, int col0, int g) {
+  const uint2 lo = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 4 * g);
+  const uint2 hi = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 16 + 4 * g);
+  const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
+  ti = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
+  tj = idx - ti * (ti + 1) / 2;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
+  constexpr bool OUT = MODE == MODE_OUT;
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[C * LDQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[C * LDQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[DP * LDKT];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[C * LDV];
+  __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];
+  __shared__ __attribute__((aligned(16))) bf16_t sO[C * LDV];
+  __shared__ __attribute__((aligned(16))) float sZ[NF];     // z, internal order
+  __shared__ __attribute__((aligned(16))) float sZinc[NF];  // this chunk's Phi_K^T 1
+  __shared__ __attribute__((aligned(16))) float sDen[C];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int seg = blockIdx.x;
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int64_t T = a.T;
+  const int n_col = wave;  // value-column tile owned by this wave
+  const float rs2 = 0.70710678118654752f;
+
+  // ---- state: lane holds s[feature 16 m + 4 g + e][16 n_col + l16] in st[m][e]
+  f32x4 st[NFT];
+  {
+    const float *src_i = (OUT && a.nseg > 1) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
+    const float *src_a = (OUT && a.nseg == 1 && a.s0) ? a.s0 + bh * (size_t)D * DV : nullptr;
+#pragma unroll
+    for (int m = 0; m < NFT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int fi = 16 * m + 4 * g + e, col = 16 * n_col + l16;
+        float x = 0.0f;
+        if (src_i) x = src_i[(size_t)fi * (DV + 1) + col];
+        else if (src_a) {
+          const int af = abi_feature(fi);
+          x = af >= 0 ? src_a[(size_t)af * DV + col] : 0.0f;
+        }
+        st[m][e] = x;
+      }
+    for (int fi = tid; fi < NF; fi += NTHR) {
+      float x = 0.0f;
+      if (src_i) x = src_i[(size_t)fi * (DV + 1) + DV];
+      else if (OUT && a.nseg == 1 && a.z0) {
+        const int af = abi_feature(fi);
+        x = af >= 0 ? a.z0[bh * D + af] : 0.0f;
+      }
+      sZ[fi] = x;
+    }
+  }
+
+  int64_t prev_t0 = -1;
+  int prev_n = 0;
+  const int64_t first = (int64_t)seg * a.seg_chunks * C;
+  int nchunks = a.seg_chunks;
+  if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const int n = (int)((T - t0) < C ? (T - t0) : C);
+    const size_t rb = bh * (size_t)T + t0;
+    int lane_v = lane;  // opaque: keeps per-fragment LDS addresses inside the loop
+    asm volatile("" : "+v"(lane_v));
+
+    // ---- phase A: write out the previous chunk's o; load q, k, v (+ k transposed)
+    if (OUT && prev_t0 >= 0) {
+      for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
+        const int r = id / (DV / 8), cv = id % (DV / 8);
+        *reinterpret_cast<u32x4 *>(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8) =
+            *reinterpret_cast<const u32x4 *>(sO + r * LDV + cv * 8);
+      }
+    }
+    for (int id = tid; id < C * (DV / 8); id += NTHR) {  // v: 512 vectors of 8
+      const int r = id >> 3, cv = id & 7;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(sV + r * LDV + cv * 8) =
+          r < n ? *reinterpret_cast<const u32x4 *>(a.v + (rb + r) * DV + cv * 8) : z;
+    }
+    if (tid < 2 * C) {  // k rows (two vectors each), plus the transposed copy
+      const int r = tid >> 1, cv = tid & 1;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 kv = r < n ? *reinterpret_cast<const u32x4 *>(a.k + (rb + r) * DP + cv * 8) : z;
+      *reinterpret_cast<u32x4 *>(sK + r * LDQ + cv * 8) = kv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = kv[e >> 1];
+        sKt[(cv * 8 + e) * LDKT + r] = (bf16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    } else if (OUT) {
+      const int id = tid - 2 * C, r = id >> 1, cv = id & 1;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(sQ + r * LDQ + cv * 8) =
+          r < n ? *reinterpret_cast<const u32x4 *>(a.q + (rb + r) * DP + cv * 8) : z;
+    }
+    __syncthreads();
+
+    // ---- phase B: kernel matrix A = 1 + QK^T + (QK^T)^2/2, causal (bf16 in LDS)
+    if (OUT) {
+      for (int job = wave; job < 10; job += NW) {
+        int ti, tj;
+        tri_index(job, ti, tj);
+        bf16x8 fa, fb;  // q.k over d' = 16: the upper half of the 32-wide k-step is zero
+        if (g < 2) {
+          fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDQ + 8 * g);
+          fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDQ + 8 * g);
+        } else {
+          fa = pack8(0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f);
+          fb = fa;
+        }
+        const f32x4 acc = mfma_bf16(fa, fb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const int j = 16 * tj + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * ti + 4 * g + e;
+          const float x = acc[e];
+          sA[t * LDA + j] = f32_to_bf16(t >= j ? 1.0f + x + 0.5f * x * x : 0.0f);
+        }
+      }
+      for (int id = tid; id < 512; id += NTHR) {  // above-diagonal tiles (0,1), (2,3)
+        const int tile = id >> 8, e = id & 255;
+        sA[(32 * tile + (e >> 4)) * LDA + 32 * tile + 16 + (e & 15)] = 0;
+      }
+      __syncthreads();
+    }
+
+    // ---- phase C: numerator and denominator (old state), then the carry
+    f32x4 num[4];
+    const bf16x8 vf0 = col_frag(sV, LDV, n_col, 0, lane_v), vf1 = col_frag(sV, LDV, n_col, 1, lane_v);
+    // one-column operand (column 0): valid-token indicator, for A 1 and Phi_K^T 1
+    bf16x8 ones[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      f32x4 a0, a1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0[e] = (l16 == 0 && 32 * s2 + 4 * g + e < n) ? 1.0f : 0.0f;
+        a1[e] = (l16 == 0 && 32 * s2 + 16 + 4 * g + e < n) ? 1.0f : 0.0f;
+      }
+      ones[s2] = pack_pair(a0, a1);
+    }
+    if (OUT) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        __builtin_amdgcn_sched_barrier(0);
+        // q of token 16 mt + l16: all 16 values and this lane group's 4
+        const int t = 16 * mt + l16;
+        const u32x4 qa = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ);
+        const u32x4 qb = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ + 8);
+        float qv[16];
+        {
+          const uint32_t w[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            qv[2 * i] = __uint_as_float(w[i] << 16);
+            qv[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+          }
+        }
+        const f32x4 qg = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sQ + t * LDQ + 4 * g));
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
+        const bool den_tile = mt == wave;  // this wave also forms den for token tile mt
+#pragma unroll
+        for (int s = 0; s < NFT / 2; ++s) {
+          f32x4 a0, a1;  // Phi_Q entries of feature tiles 2 s and 2 s + 1
+          if (s < 8) {
+            a0 = qg * (qv[2 * s] * rs2);
+            a1 = qg * (qv[2 * s + 1] * rs2);
+          } else {
+            a0 = qg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a1[e] = (4 * g + e == 0) ? 1.0f : 0.0f;
+          }
+          const bf16x8 fa = pack_pair(a0, a1);
+          acc = mfma_bf16(fa, pack_pair(st[2 * s], st[2 * s + 1]), acc);
+          if (den_tile) {
+            f32x4 z0, z1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              z0[e] = l16 == 0 ? sZ[32 * s + 4 * g + e] : 0.0f;
+              z1[e] = l16 == 0 ? sZ[32 * s + 16 + 4 * g + e] : 0.0f;
+            }
+            dacc = mfma_bf16(fa, pack_pair(z0, z1), dacc);
+          }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (s2 == 1 && mt < 2) continue;  // A is causal
+          const bf16x8 af = frag_pair(sA, LDA, 16 * mt + l16, 32 * s2, g);
+          acc = mfma_bf16(af, s2 == 0 ? vf0 : vf1, acc);
+          if (den_tile) dacc = mfma_bf16(af, ones[s2], dacc);
+        }
+        num[mt] = acc;
+        if (den_tile && l16 == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sDen[16 * mt + 4 * g + e] = dacc[e];
+        }
+      }
+    }
+    {  // carry: s += Phi_K^T V, and Phi_K^T 1 for the feature tiles m = wave (mod 4)
+      const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
+#pragma unroll
+      for (int m = 0; m < NFT; ++m) {
+        if ((m & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc = st[m];
+        f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+        const bool zt = (m % NW) == wave;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          bf16x8 fa;  // Phi_K^T rows of feature tile m at this lane's 8 tokens
+          if (m < DP) {
+            const f32x4 k0 = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sKt + m * LDKT + 32 * s2 + 4 * g));
+            const f32x4 k1 = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sKt + m * LDKT + 32 * s2 + 16 + 4 * g));
+            f32x4 j0, j1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              j0[e] = (float)kj[s2][e];
+              j1[e] = (float)kj[s2][4 + e];
+            }
+            fa = pack_pair(k0 * j0 * rs2, k1 * j1 * rs2);
+          } else if (m == DP) {
+            fa = kj[s2];
+          } else {
+            f32x4 c0, c1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              c0[e] = (l16 == 0 && 32 * s2 + 4 * g + e < n) ? 1.0f : 0.0f;
+              c1[e] = (l16 == 0 && 32 * s2 + 16 + 4 * g + e < n) ? 1.0f : 0.0f;
+            }
+            fa = pack_pair(c0, c1);
+          }
+          acc = mfma_bf16(fa, s2 == 0 ? vf0 : vf1, acc);
+          if (zt) zacc = mfma_bf16(fa, ones[s2], zacc);
+        }
+        st[m] = acc;
+        if (zt && l16 == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sZinc[16 * m + 4 * g + e] = zacc[e];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- phase D: normalise into the o staging tile; z += this chunk's Phi_K^T 1
+    if (OUT) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * mt + 4 * g + e;
+          sO[t * LDV + 16 * n_col + l16] = f32_to_bf16(num[mt][e] / (sDen[t] + a.eps));
+        }
+    }
+    for (int fi = tid; fi < NF; fi += NTHR) sZ[fi] += sZinc[fi];
+    __syncthreads();
+    prev_t0 = t0;
+    prev_n = n;
+  }
+
+  if (OUT) {
+    if (prev_t0 >= 0) {
+      for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
+        const int r = id / (DV / 8), cv = id % (DV / 8);
+        *reinterpret_cast<u32x4 *>(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8) =
+            *reinterpret_cast<const u32x4 *>(sO + r * LDV + cv * 8);
+      }
+    }
+    if (a.nseg == 1 && a.s_T) {
+#pragma unroll
+      for (int m = 0; m < NFT; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int af = abi_feature(16 * m + 4 * g + e);
+          if (af >= 0) a.s_T[(bh * D + af) * DV + 16 * n_col + l16] = st[m][e];
+        }
+      for (int fi = tid; fi < NF; fi += NTHR) {
+        const int af = abi_feature(fi);
+        if (af >= 0) a.z_T[bh * D + af] = sZ[fi];
+      }
+    }
+  } else {
+    float *dst = a.dsum + (bh * a.nseg + seg) * (size_t)NF * (DV + 1);
+#pragma unroll
+    for (int m = 0; m < NFT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(size_t)(16 * m + 4 * g + e) * (DV + 1) + 16 * n_col + l16] = st[m][e];
+    for (int fi = tid; fi < NF; fi += NTHR) dst[(size_t)fi * (DV + 1) + DV] = sZ[fi];
+  }
+}
+
+// Pass 2: exclusive prefix sums of the per-segment sums, from the (ABI-layout) start
+// state; also the end state in the ABI layout.  One workgroup per (b, h).
+__global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  constexpr int NE = NF * (DV + 1);
+  for (int id = blockIdx.x * 256 + threadIdx.x; id < NE; id += gridDim.x * 256) {
+    const int fi = id / (DV + 1), col = id % (DV + 1);
+    const int af = abi_feature(fi);
+    float x = 0.0f;
+    if (af >= 0) {
+      if (col < DV && a.s0) x = a.s0[(bh * D + af) * DV + col];
+      if (col == DV && a.z0) x = a.z0[bh * D + af];
+    }
+    for (int i = 0; i < a.nseg; ++i) {
+      a.starts[(bh * a.nseg + i) * (size_t)NE + id] = x;
+      x += a.dsum[(bh * a.nseg + i) * (size_t)NE + id];
+    }
+    if (a.s_T && af >= 0) {
+      if (col < DV) a.s_T[(bh * D + af) * DV + col] = x;
+      else a.z_T[bh * D + af] = x;
+    }
+  }
+}
+
+struct Plan {
+  int nseg, seg_chunks;
+};
+
+// About two workgroups per CU in all, split only when the heads alone cannot fill it.
+Plan make_plan(int B, int H, int64_t T) {
+  const int64_t nch = (T + C - 1) / C;
+  const int64_t bhn = (int64_t)B * H;
+  int64_t nseg = 1;
+  if (bhn < 256) {
+    nseg = (512 + bhn - 1) / bhn;
+    if (nseg > nch) nseg = nch;
+    if (nseg < 1) nseg = 1;
+  }
+  const int64_t sc = (nch + nseg - 1) / nseg;
+  nseg = (nch + sc - 1) / sc;
+  return Plan{(int)nseg, (int)sc};
+}
+
+}  // namespace based
+
+size_t based_chunk_workspace_bytes(int B, int H, int64_t T) {
+  const based::Plan p = based::make_plan(B, H, T);
+  if (p.nseg <= 1) return 0;
+  return 2 * (size_t)B * H * p.nseg * based::NF * (based::DV + 1) * sizeof(float);
+}
+
+void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks) {
+  const based::Plan p = based::make_plan(B, H, T);
+  *nseg = p.nseg;
+  *seg_chunks = p.seg_chunks;
 }
 
 hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const void *q,
                                       const void *k, const void *v, const float *s0,
-                                      const float *z0, void *o, float *s_T, float *z_T, void *,
-                                      int pass_mask, hipStream_t s) {
-  if (!(pass_mask & PASS_REPLAY)) return hipSuccess;
-  return launch_recurrent_based(T_BF16, B, H, T, eps, q, k, v, s0, z0, o, s_T, z_T, s);
+                                      const float *z0, void *o, float *s_T, float *z_T,
+                                      void *workspace, int pass_mask, hipStream_t s) {
+  using namespace based;
+  const Plan p = make_plan(B, H, T);
+  Args a;
+  a.q = (const bf16_t *)q;
+  a.k = (const bf16_t *)k;
+  a.v = (const bf16_t *)v;
+  a.s0 = s0;
+  a.z0 = z0;
+  a.o = (bf16_t *)o;
+  a.s_T = s_T;
+  a.z_T = z_T;
+  const size_t half = (size_t)B * H * p.nseg * NF * (DV + 1);
+  a.dsum = p.nseg > 1 ? (float *)workspace : nullptr;
+  a.starts = p.nseg > 1 ? (float *)workspace + half : nullptr;
+  a.T = T;
+  a.H = H;
+  a.nseg = p.nseg;
+  a.seg_chunks = p.seg_chunks;
+  a.eps = eps;
+  const dim3 grid(p.nseg, H, B);
+  if (p.nseg > 1 && (pass_mask & PASS_MAPS))
+    hipLaunchKernelGGL(based_chunk_kernel<MODE_MAP>, grid, dim3(NTHR), 0, s, a);
+  if (p.nseg > 1 && (pass_mask & PASS_SCAN))
+    hipLaunchKernelGGL(based_scan_kernel, dim3(8, H, B), dim3(256), 0, s, a);
+  if (pass_mask & PASS_REPLAY)
+    hipLaunchKernelGGL(based_chunk_kernel<MODE_OUT>, grid, dim3(NTHR), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace la

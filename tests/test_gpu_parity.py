@@ -212,3 +212,25 @@ def test_prefill_passes_compose_to_prefill(la, variant):
         la.prefill(variant, q, k, v, a, b, o=o2, S_T=S2, workspace=ws, pass_=p)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_based_chunk_full_config_sampled_columns(la):
+    """BASED prefill at its full configuration (B=4, H=16, T=8192, d'=16, d_v=64, bf16):
+    every output element of a sample of value columns against the oracle; z_T in full."""
+    B, H, T, dp, dv = 4, 16, 8192, 16, 64
+    q, k, v, _, _ = _inputs("based", B, H, T, dp, dv, torch.bfloat16, seed=1)
+    nseg, _ = la.segments("based", la.BF16, B, H, T, dp, dv)
+    assert nseg > 1
+    print(f"[based full] segments={nseg}", flush=True)
+    o, s_T, z_T = la.prefill("based", q, k, v)
+    torch.cuda.synchronize()
+    cols = [0, 21, 42, 63]
+    oo, so, zo = oracle.prefill("based", q, k, v, rows=cols)
+    assert_close(o[..., cols], oo, 2e-2, what="o (sampled columns)")
+    assert_close(s_T[..., cols], so, 2e-2, what="s_T (sampled columns)")
+    assert_close(z_T, zo, 2e-2, what="z_T")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 1000])
+def test_based_chunk_short_and_ragged(la, T):
+    _check_prefill(la, "based", 1, 3, T, 16, 64, torch.bfloat16, seed=70 + T)
