@@ -31,5 +31,6 @@ def slice_rel(x, y, lead=2):
 
 def assert_close(x, y, tol, lead=2, what=""):
     worst, _ = slice_rel(x, y, lead)
+    print(f"    parity {what}: max slice rel err {worst:.3e} (bound {tol:.0e})", flush=True)
     assert worst <= tol, f"{what}: max slice rel err {worst:.3e} > {tol:.1e}"
     return worst
