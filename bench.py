@@ -71,6 +71,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-based", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 256 MiB copy (la_prefill with T = 0) so that HBM "
+                         "byte counters can be scaled against a known size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -90,6 +94,14 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     B, H, T, D = 1, args.heads, args.seq_len, 128
+
+    if args.calibrate_copy:  # copy_or_zero_kernel: reads and writes exactly 256 MiB
+        e = torch.empty((1, 4096, 0, 128), dtype=torch.bfloat16, device=dev)
+        ea = torch.empty((1, 4096, 0), dtype=torch.bfloat16, device=dev)
+        S0c = torch.randn((1, 4096, 128, 128), device=dev)
+        la.prefill("gated_delta", e, e, e, ea, ea, S0=S0c)
+        torch.cuda.synchronize()
+        del S0c
 
     # ---------------------------------------------------------------- prefill
     inp = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=3, device=dev)
@@ -134,18 +146,31 @@ def main():
     alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD
     alg_flops = token_heads * FLOPS_PER_TOKEN_HEAD
 
-    # the dominant launch of the step and its algorithmic traffic per launch
+    # the dominant launch of the step, with the algorithmic bytes and FLOPs of that pass:
+    #   replay: q, k, v, alpha, beta in, o out (1028 B) and the chunk-form FLOPs per token-head
+    #   maps:   k, v, alpha, beta in (516 B); K K^T, W, U~, the solve, and U and the state
+    #           update for 256 state rows (B_seg and M_seg): the same FLOP count per token-head
+    #   scan:   per segment, a 128 x 128 map and B_seg read, the start state written
     dom = max(per_pass, key=per_pass.get)
-    dom_bytes = {"replay": token_heads * BYTES_PER_TOKEN_HEAD,
-                 "maps": token_heads * (2 * 128 * 2 + 2 * 2),
-                 "scan": B * H * nseg * (3 * D * D * 4)}[dom]
-    dom_gbs = dom_bytes / (per_pass[dom] * 1e-3) / 1e9
-    traffic = read_traffic(dom)
+    pass_bytes = {"replay": token_heads * BYTES_PER_TOKEN_HEAD,
+                  "maps": token_heads * (2 * 128 * 2 + 2 * 2),
+                  "scan": B * H * nseg * (3 * D * D * 4)}
+    pass_flops = {"replay": alg_flops, "maps": alg_flops, "scan": B * H * nseg * 2 * D * D * D}
+    t_dom = per_pass[dom] * 1e-3
+    t_hbm = pass_bytes[dom] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = pass_flops[dom] / (BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        ach, peak, unit, bound = pass_bytes[dom] / t_dom / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    else:
+        ach, peak, unit, bound = pass_flops[dom] / t_dom / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    kname = {"replay": "chunk_kernel<MODE_OUT,true> (replay pass)",
+             "maps": "chunk_kernel<MODE_MAP,true> (segment-map pass)",
+             "scan": "scan_kernel<true> (segment scan)"}[dom]
     roofline = {
-        "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-        "kernel": f"chunk pass '{dom}' ({'chunk_kernel<MODE_OUT,true>' if dom == 'replay' else dom})",
+        "bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+        "frac": round(ach / peak, 4), "traffic": read_traffic(dom), "kernel": kname,
         "ms_per_launch": round(per_pass[dom], 4),
+        "alg_bytes_per_launch": pass_bytes[dom], "alg_flops_per_launch": pass_flops[dom],
     }
     prefill_detail = {
         "ms_per_pass": {kk: round(vv, 4) for kk, vv in per_pass.items()},
@@ -161,15 +186,20 @@ def main():
     # host copy of a prefix of the same inputs for the CPU oracle sample
     host = None
     if not args.no_cpu_baseline:
-        Tmax = min(T, 1 << 17)
+        Tmax = min(T, 1 << 19)
         host = {n: t[:, :, :Tmax].cpu() for n, t in inp.items()}
 
     # ---------------------------------------------------------------- decode
     decode = None
+    del inp, q, k, v, a, b, o, ws
+    torch.cuda.empty_cache()
     if not args.no_decode:
-        del inp, q, k, v, a, b, o, ws
-        torch.cuda.empty_cache()
         decode = bench_decode(torch, la, synth, dev, stream, args.decode_steps)
+
+    # ---------------------------------------------------------------- BASED prefill
+    based = None
+    if not args.no_based:
+        based = bench_based(torch, la, synth, dev, stream, args.steps)
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -187,6 +217,7 @@ def main():
         "roofline": roofline,
         "prefill": prefill_detail,
         "decode": decode,
+        "based_prefill": based,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -242,6 +273,41 @@ def bench_decode(torch, la, synth, dev, stream, steps):
     return res
 
 
+def bench_based(torch, la, synth, dev, stream, steps):
+    """BASED Taylor prefill, B=4, H=16, T=8192, d'=16, d_v=64, bf16 (all three passes)."""
+    B, H, T, dp, dv = 4, 16, 8192, 16, 64
+    d = synth.based_inputs(B, H, T, dp, dv, dtype=torch.bfloat16, seed=1, device=dev)
+    Dphi = 1 + dp + dp * dp
+    o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
+    s_T = torch.empty((B, H, Dphi, dv), dtype=torch.float32, device=dev)
+    z_T = torch.empty((B, H, Dphi), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(la.workspace_size("based", la.BF16, B, H, T, dp, dv), 16), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: la.prefill("based", d["q"], d["k"], d["v"], o=o, S_T=s_T, z_T=z_T, workspace=ws,
+                             stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(steps, 10)
+    e0.record(stream)
+    for _ in range(n):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    th = B * H * T
+    alg_bytes = th * (2 * dp * 2 + 2 * dv * 2) + 2 * B * H * Dphi * (dv + 1) * 4
+    C = 64  # chunk-form FLOPs per token-head: QK^T, A V, Phi_Q s, Phi_K^T V, normaliser
+    alg_flops = th * (2 * C * dp + 2 * C * dv + 4 * Dphi * dv + 2 * Dphi + C)
+    t_roof = max(alg_bytes / (HBM_PEAK_GBS * 1e9), alg_flops / (BF16_PEAK_TFLOPS * 1e12))
+    nseg, sc = la.segments("based", la.BF16, B, H, T, dp, dv)
+    return {"workload": "BASED Taylor prefill B=4 H=16 T=8192 d'=16 d_v=64 bf16",
+            "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "alg_bytes": alg_bytes, "alg_flops": alg_flops, "segments": nseg,
+            "roofline_time_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof * 1e3 / ms, 4)}
+
+
 def bench_cpu(host, H, D, target_s):
     """The fp64 oracle, as it is, on the first T_s tokens of the same 16-head sequence (all
     value rows, the same input values the GPU ran on), on this host's cores; T_s is grown
@@ -261,6 +327,10 @@ def bench_cpu(host, H, D, target_s):
     Ts = min(2048, Tmax)
     dt = run(Ts)
     Ts2 = int(min(max(Ts * target_s / max(dt, 1e-3), Ts), Tmax)) // 64 * 64
+    if Ts2 == Ts:
+        return {"value": round(Ts / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "sample": f"fp64 oracle on the first {Ts} tokens of the {H}-head gated-delta "
+                          f"sequence (all 128 value rows, d_k=d_v={D}), {dt:.1f} s wall"}
     dt2 = run(Ts2)
     return {"value": round(Ts2 / dt2, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 oracle on the first {Ts2} tokens of the {H}-head gated-delta "
