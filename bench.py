@@ -111,8 +111,10 @@ def main():
     ws_n = la.workspace_size("gated_delta", la.BF16, B, H, T, D, D)
     ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     nseg, seg_chunks = la.segments("gated_delta", la.BF16, B, H, T, D, D)
-    passes = [la.PASS_MAPS, la.PASS_SCAN, la.PASS_REPLAY] if nseg > 1 else [la.PASS_REPLAY]
-    names = {la.PASS_MAPS: "maps", la.PASS_SCAN: "scan", la.PASS_REPLAY: "replay"}
+    passes = [la.PASS_TRANSFORM, la.PASS_MAPS, la.PASS_SCAN, la.PASS_REPLAY] if nseg > 1 \
+        else [la.PASS_TRANSFORM, la.PASS_REPLAY]
+    names = {la.PASS_TRANSFORM: "transform", la.PASS_MAPS: "maps", la.PASS_SCAN: "scan",
+             la.PASS_REPLAY: "replay"}
 
     def step(evs=None):
         for i, p in enumerate(passes):
@@ -146,16 +148,23 @@ def main():
     alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD
     alg_flops = token_heads * FLOPS_PER_TOKEN_HEAD
 
-    # the dominant launch of the step, with the algorithmic bytes and FLOPs of that pass:
-    #   replay: q, k, v, alpha, beta in, o out (1028 B) and the chunk-form FLOPs per token-head
-    #   maps:   k, v, alpha, beta in (516 B); K K^T, W, U~, the solve, and U and the state
-    #           update for 256 state rows (B_seg and M_seg): the same FLOP count per token-head
-    #   scan:   per segment, a 128 x 128 map and B_seg read, the start state written
+    # the dominant launch of the step, with the algorithmic bytes and FLOPs of that pass
+    # (per token-head, C = 64, d = 128; the transform is 64 x 64 bf16 per chunk = 128 B):
+    #   transform: k, alpha, beta in, the transform out (388 B); K K^T and the solve
+    #              (2 C d + C^2 / 3 FLOP)
+    #   maps:      k, v, alpha, beta, transform in (644 B); W, U~ (2 x 2 C d) and W S^T and
+    #              the state update for 256 state rows, B_seg and M_seg (4 x 2 d^2)
+    #   scan:      per segment, a 128 x 128 map and B_seg read, the start state written
+    #   replay:    q, k, v, alpha, beta, transform in, o out (1156 B); Q K^T, W, U~, A U
+    #              (4 x 2 C d) and Q S^T, W S^T, the state update (3 x 2 d^2)
     dom = max(per_pass, key=per_pass.get)
-    pass_bytes = {"replay": token_heads * BYTES_PER_TOKEN_HEAD,
-                  "maps": token_heads * (2 * 128 * 2 + 2 * 2),
-                  "scan": B * H * nseg * (3 * D * D * 4)}
-    pass_flops = {"replay": alg_flops, "maps": alg_flops, "scan": B * H * nseg * 2 * D * D * D}
+    per_th = {"transform": (128 * 2 + 2 * 2 + 128, 2 * C_ * D_ + C_ * C_ / 3),
+              "maps": (2 * 128 * 2 + 2 * 2 + 128, 2 * 2 * C_ * D_ + 4 * 2 * D_ * D_),
+              "replay": (BYTES_PER_TOKEN_HEAD + 128, 4 * 2 * C_ * D_ + 3 * 2 * D_ * D_)}
+    pass_bytes = {kk: token_heads * vv[0] for kk, vv in per_th.items()}
+    pass_flops = {kk: token_heads * vv[1] for kk, vv in per_th.items()}
+    pass_bytes["scan"] = B * H * nseg * (3 * D * D * 4)
+    pass_flops["scan"] = B * H * nseg * 2 * D * D * D
     t_dom = per_pass[dom] * 1e-3
     t_hbm = pass_bytes[dom] / (HBM_PEAK_GBS * 1e9)
     t_mfma = pass_flops[dom] / (BF16_PEAK_TFLOPS * 1e12)
@@ -165,6 +174,7 @@ def main():
         ach, peak, unit, bound = pass_flops[dom] / t_dom / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     kname = {"replay": "chunk_kernel<MODE_OUT,true> (replay pass)",
              "maps": "chunk_kernel<MODE_MAP,true> (segment-map pass)",
+             "transform": "tprep_kernel (per-chunk UT transform pass)",
              "scan": "scan_kernel<true> (segment scan)"}[dom]
     roofline = {
         "bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,

@@ -23,7 +23,7 @@ STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_INVALID", -3: "LA_ERR_UNSUP
           -4: "LA_ERR_ALIGN", -5: "LA_ERR_WORKSPACE", -6: "LA_ERR_ALIAS", -7: "LA_ERR_HIP"}
 EXPORTS = ("la_abi_version", "la_status_string", "la_prefill_workspace_size", "la_prefill",
            "la_prefill_pass", "la_prefill_segments", "la_decode_step")
-PASS_MAPS, PASS_SCAN, PASS_REPLAY = 1, 2, 3
+PASS_MAPS, PASS_SCAN, PASS_REPLAY, PASS_TRANSFORM = 1, 2, 3, 4
 
 LIB_PATH = Path(__file__).resolve().parent / "libla.so"
 _lib = None
@@ -117,7 +117,7 @@ def segments(variant, dtype, B, H, T, d_k, d_v):
 
 def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6, want_state=True,
             o=None, S_T=None, z_T=None, workspace=None, stream=None, pass_=None):
-    """Run la_prefill (or one pass of it, ``pass_`` in PASS_MAPS/SCAN/REPLAY, see la.h).
+    """Run la_prefill (or one pass of it, ``pass_`` in PASS_TRANSFORM/MAPS/SCAN/REPLAY, see la.h).
     q, k [B,H,T,d_k]; v [B,H,T,d_v]; alpha, beta [B,H,T] (same dtype as q); S0 [B,H,d_v,d_k]
     fp32 (BASED: s0 [B,H,D,d_v], z0 [B,H,D]).  Returns (o, S_T, z_T)."""
     var = _var(variant)

@@ -14,19 +14,19 @@
 //   O  = diag(gamma) Q S^T + (P . Q K^T) U
 //   S' = gamma_C S + U^T diag(e^{g_C - g}) K  =  S M_c + B_c
 //
-// T is the UT/WY transform of the chunk; it is computed in fp32 in LDS by blocked
-// forward substitution (16 x 16 diagonal blocks, off-diagonal blocks on fp32 MFMA).
-// Every product with a 64- or 128-wide inner dimension runs on bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation; the state stays fp32.
+// T is the UT/WY transform of the chunk.  It depends on the keys and gates only, so it is
+// computed for every chunk at once, before any state is carried (pass 0 below): one wave
+// per chunk forms L from a K K^T Gram on bf16 MFMA, solves (I + L) T = I in fp32 by
+// blocked forward substitution (16 x 16 diagonal blocks on the VALU, the off-diagonal
+// blocks on fp32 MFMA), and stores T diag(beta) in bf16.  Every product with a 64- or 128-wide inner dimension runs on bf16
+// MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation; the state stays fp32.
 //
 // gfx950 layout choices.  All chunk tiles live in LDS row-major ([token][d]); operands
-// that contract over tokens (K^T, V^T) are read straight from those tiles with the
-// CDNA4 transpose read ds_read_b64_tr_b16, so no transposed copies are built.  L (fp32)
-// is kept transposed in the strict upper triangle of the same buffer whose lower
-// triangle receives T.  A workgroup (4 waves) uses at most ~80 KB of LDS, so two
-// workgroups share a CU and overlap their latency-bound phases (the triangular solve,
-// barriers) with each other's MFMA phases.  The next chunk's inputs are prefetched into
-// registers while the current chunk is processed.
+// that contract over tokens (K^T, V^T, and T, which is stored transposed) are read
+// straight from those tiles with the CDNA4 transpose read ds_read_b64_tr_b16, so no
+// transposed copies are built.  A state-carrying workgroup (4 waves) uses at most ~72 KB
+// of LDS, so two workgroups share a CU and overlap their latency-bound phases (loads,
+// barriers) with each other's MFMA phases.
 //
 // Sequence parallelism.  One workgroup owns the whole 128 x 128 state of one (b, h),
 // split over its 4 waves (32 state rows each, in registers), and streams chunks with
@@ -34,11 +34,12 @@
 // B*H*segments fills the chip, in three passes:
 //   pass 1 (MODE_MAP)  every segment from a zero start: its end state B_seg, and for the
 //                      delta rule its d_k x d_k transition M_seg (the same chunk
-//                      recurrence run on the identity, by a second workgroup per
-//                      segment), or the scalar log decay
+//                      recurrence run on the identity, by the second half of an 8-wave
+//                      workgroup), or the scalar log decay
 //   pass 2 (scan)      S_{i+1} = S_i M_i + B_i sequentially over segments, row-parallel
 //   pass 3 (MODE_OUT)  every segment replayed from its start state, writing o
-// With one segment (enough heads to fill the chip) only pass 3 runs.
+// With one segment (enough heads to fill the chip) only pass 3 runs.  For the delta rule
+// pass 0 precedes pass 1 (or pass 3 when there is one segment).
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -48,32 +49,22 @@ namespace gdn {
 constexpr int C = 64;     // tokens per chunk
 constexpr int DK = 128;   // key width
 constexpr int DV = 128;   // value width
-constexpr int NW = 4;     // waves per workgroup
+constexpr int NW = 4;     // waves per state-carrying workgroup
 constexpr int NTHR = NW * 64;
 constexpr int RPW = DV / NW;  // state rows per wave (two 16-row column tiles)
-#ifndef LA_CHUNK_WG_PER_CU
-#define LA_CHUNK_WG_PER_CU 2
-#endif
-#ifndef LA_CHUNK_PREFETCH
-#define LA_CHUNK_PREFETCH 0
-#endif
-// Two workgroups per CU hide each other's load latency and latency-bound phases; with
-// one, the next chunk is prefetched into registers instead.
-constexpr int WG_PER_CU = LA_CHUNK_WG_PER_CU;
 // Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
 // would raise register pressure past what two workgroups per CU allow).
 #define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
-constexpr bool PREFETCH = LA_CHUNK_PREFETCH != 0;
 
 constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V, W, O staging
 constexpr int LDA = C + 8;   // bf16 [C][C]: decay-masked Q K^T
-constexpr int LDL = C + 4;   // fp32 [C][C]: L^T (strict upper) and T (lower)
+constexpr int LDT = C + 8;   // bf16 [C][C]: (T diag(beta))^T
 
 constexpr int SZ_ROW = C * LDK * 2;
-constexpr int SZ_LT = C * LDL * 4;
 constexpr int SZ_A = C * LDA * 2;
+constexpr int SZ_T = C * LDT * 2;
 constexpr int SZ_VEC = 5 * C * 4;
-static_assert(SZ_ROW <= SZ_LT, "O staging fits the L/T buffer");
+constexpr size_t T_CHUNK = (size_t)C * C;  // bf16 elements of one stored transform
 static_assert(DK == DV, "square state");
 
 enum { MODE_MAP = 0, MODE_OUT = 1 };
@@ -86,8 +77,9 @@ struct Args {
   float *maps;       // [BH][nseg][maprows][DK] per-segment maps (rows: B_seg, then M_seg)
   float *gsum;       // [BH][nseg] per-segment log decay (no delta rule)
   float *starts;     // [BH][nseg][DV][DK] segment start states
-  int64_t T;
-  int H, nseg, seg_chunks, variant, has_beta;
+  bf16_t *tb;        // [BH][nch][C][C] per-chunk (T diag(beta))^T (delta rule)
+  int64_t T, nch;
+  int B, H, nseg, seg_chunks, variant, has_beta;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -122,23 +114,185 @@ __device__ __forceinline__ bf16x8 pack_pair(f32x4 a, f32x4 b) {
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
+// x scaled per token: elements 0..3 by a, 4..7 by b (the token order of col_frag).
+__device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 a, f32x4 b) {
+  return pack8((float)x[0] * a[0], (float)x[1] * a[1], (float)x[2] * a[2], (float)x[3] * a[3],
+               (float)x[4] * b[0], (float)x[5] * b[1], (float)x[6] * b[2], (float)x[7] * b[3]);
+}
+
 __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
   ti = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
   tj = idx - ti * (ti + 1) / 2;
 }
 
-// Row t of T restricted to tokens perm(s, g), with the upper triangle (which holds L^T)
-// masked to zero, scaled per token by sc and packed as a bf16 A operand.
-__device__ __forceinline__ bf16x8 t_frag(const float *LT, const float *sc, int t, int s, int g) {
-  f32x4 a = ld4(LT + t * LDL + 32 * s + 4 * g);
-  f32x4 b = ld4(LT + t * LDL + 32 * s + 16 + 4 * g);
-  const f32x4 sa = ld4(sc + 32 * s + 4 * g), sb = ld4(sc + 32 * s + 16 + 4 * g);
+// ---------------------------------------------------------------------------------------
+// Pass 0 (delta rule): for every chunk, TB = (I + L)^{-1} diag(beta), stored transposed
+// (row j of the stored tile is column j of TB) in bf16.  One wave per chunk, four
+// independent waves per workgroup (no barriers).  A partial last chunk has zero keys and
+// beta beyond its end, so its TB is zero there.
+//
+// Blocked solve on 16 x 16 blocks, in fp32: the four diagonal blocks D_b = (I + L_bb)^{-1}
+// by forward substitution (one lane per column of a block, the four blocks side by side,
+// in LDS), then the off-diagonal blocks by sub-diagonal level on fp32 MFMA (16x16x4),
+// T_ij = -D_i sum_{k=j}^{i-1} L_ik T_kj, in registers.  MFMA k-step s pairs lane group g
+// with inner index 4 g + s, so an accumulator tile (lane (g, c) holds rows 4 g + e of
+// column c) is directly a B operand, and the A operand L_ik[c][4 g + s] is the
+// accumulator tile of the Gram block (k, i): K K^T is symmetric.
+// ---------------------------------------------------------------------------------------
+constexpr int LDD = 20;  // fp32 16 x 16 diagonal blocks in pass 0
+struct TPrepLds {
+  float g[C], beta[C];
+  float d[4][16 * LDD];
+};
+
+__global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) TPrepLds sm[NW];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int64_t cid = (int64_t)blockIdx.x * NW + wave;
+  if (cid >= (int64_t)a.B * a.H * a.nch) return;
+  const int64_t bh = cid / a.nch, t0 = (cid % a.nch) * C;
+  const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
+  const size_t base = (size_t)bh * a.T + t0;
+  TPrepLds &L = sm[wave];
+
+  // K rows as MFMA operands, straight from global memory: kf[rt][s] holds row 16 rt + l16,
+  // columns 32 s + 8 grp .. +7 (the A and the B operand of K K^T have the same layout)
+  bf16x8 kf[4][DK / 32];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    a[e] = (32 * s + 4 * g + e) > t ? 0.0f : a[e] * sa[e];
-    b[e] = (32 * s + 16 + 4 * g + e) > t ? 0.0f : b[e] * sb[e];
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      const int r = 16 * rt + l16;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 w = r < n ? gld16(a.k + (base + r) * DK + 32 * s + 8 * grp) : z;
+      kf[rt][s] = __builtin_bit_cast(bf16x8, w);
+    }
+
+  // gates: g_t (inclusive prefix sum of log alpha) and beta_t, kept in LDS for broadcast
+  {
+    float gx = 0.0f, be = 0.0f;
+    if (lane < n) {
+      gx = logf(bf16_to_f32(a.alpha[base + lane]));
+      be = bf16_to_f32(a.beta[base + lane]);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(gx, off, 64);
+      if (lane >= off) gx += y;
+    }
+    L.g[lane] = gx;
+    L.beta[lane] = be;
   }
-  return pack_pair(a, b);
+  __asm__ volatile("" ::: "memory");  // one wave: LDS keeps its accesses in order
+
+  // Gram blocks.  Diagonal block b: L_bb^T (row k holds L_bb[.][k]) into LDS.  Block (k, i)
+  // above the diagonal: the A operand of L_ik, al[] below, in registers.
+  f32x4 al[6];  // (i, k) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * i + l16;  // row of L_ik held by this lane (A operand) / column (diag)
+    const float gr = L.g[r], br = L.beta[r];
+#pragma unroll
+    for (int k = 0; k <= i; ++k) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(kf[k][s], kf[i][s], acc);
+      // acc[e] = k_c . k_r with c = 16 k + 4 grp + e
+      const f32x4 gc = ld4(L.g + 16 * k + 4 * grp);
+      if (k < i) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = br * expf(gr - gc[e]) * acc[e];  // L_rc, r > c
+        al[i * (i - 1) / 2 + k] = v;
+      } else {  // diagonal: L_bb^T[c][r] = L_rc for r > c, from the block (b, b)
+        const f32x4 bc = ld4(L.beta + 16 * k + 4 * grp);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 16 * k + 4 * grp + e;
+          // the block is symmetric: acc[e] is also k_r . k_c with r = c, c = r swapped
+          v[e] = c > r ? bc[e] * expf(gc[e] - gr) * acc[e] : 0.0f;  // L_cr, c > r
+        }
+        // lane (grp, l16) holds L_bb[4 grp + e][l16] = L_bb^T[l16][4 grp + e]
+        *reinterpret_cast<f32x4 *>(L.d[i] + l16 * LDD + 4 * grp) = v;
+      }
+    }
+  }
+  __asm__ volatile("" ::: "memory");
+
+  {  // diagonal blocks: lane (b, c) solves column c of (I + L_bb) D_b = I, right-looking,
+     // then stores D_b row-major over L_bb^T
+    const int b = grp, c = l16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.0f : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+      const float xk = x[k];
+#pragma unroll
+      for (int q4 = (k + 1) / 4; q4 < 4; ++q4) {  // L_bb[r][k] for r > k: row k of L_bb^T
+        const f32x4 l = ld4(L.d[b] + k * LDD + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q4 + e > k) x[4 * q4 + e] -= l[e] * xk;
+      }
+    }
+    __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 16; ++r) L.d[b][r * LDD + c] = x[r];
+  }
+  __asm__ volatile("" ::: "memory");
+
+  // D_b as B operand (rows 4 grp + s of column l16) and as A operand (row l16, inner
+  // 4 grp + s): both from LDS
+#define LA_DB(b) f32x4{L.d[b][(4 * grp) * LDD + l16], L.d[b][(4 * grp + 1) * LDD + l16], \
+                       L.d[b][(4 * grp + 2) * LDD + l16], L.d[b][(4 * grp + 3) * LDD + l16]}
+#define LA_DA(b) ld4(L.d[b] + l16 * LDD + 4 * grp)
+  f32x4 db[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) db[b] = LA_DB(b);
+  // T_ij (i > j) as accumulator tiles: rows 4 grp + e of column l16
+  f32x4 tt[6];  // (i, j) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), same order as al
+#pragma unroll
+  for (int level = 1; level <= 3; ++level) {
+#pragma unroll
+    for (int j = 0; j + level < 4; ++j) {
+      const int i = j + level;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = j; kb < i; ++kb) {
+        const f32x4 A = al[i * (i - 1) / 2 + kb];
+        const f32x4 Bm = kb == j ? db[j] : tt[kb * (kb - 1) / 2 + j];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s], Bm[s], x, 0, 0, 0);
+      }
+      const f32x4 di = LA_DA(i);
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) y = __builtin_amdgcn_mfma_f32_16x16x4f32(di[s], x[s], y, 0, 0, 0);
+      tt[i * (i - 1) / 2 + j] = -y;
+    }
+  }
+#undef LA_DA
+#undef LA_DB
+
+  // stored tile row 16 j + l16 = column of T diag(beta): block (i, j) of T supplies its
+  // columns 16 i + 4 grp .. +3 (eight bytes per lane); blocks above the diagonal are zero
+  bf16_t *dst = a.tb + (size_t)cid * T_CHUNK;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float bj = L.beta[16 * j + l16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      if (i == j) t = db[j];
+      if (i > j) t = tt[i * (i - 1) / 2 + j];
+      t = t * bj;
+      const bf16x4 h = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+      gst8(dst + (16 * j + l16) * C + 16 * i + 4 * grp, __builtin_bit_cast(u32x2, h));
+    }
+  }
 }
 
 // Waves per workgroup: 4 (32 state rows each), or 8 for the delta-rule map pass, whose
@@ -148,42 +302,50 @@ template <int MODE, bool DELTA> struct Waves {
   static constexpr int value = (MODE == MODE_MAP && DELTA) ? 8 : NW;
 };
 
+// LDS carve-up (bytes) of the state-carrying kernels.
+template <int MODE, bool DELTA> struct Lds {
+  static constexpr bool OUT = MODE == MODE_OUT;
+  static constexpr int K = 0;
+  static constexpr int Q = SZ_ROW;                         // MODE_OUT: Q, then O staging
+  static constexpr int V = OUT ? 2 * SZ_ROW : SZ_ROW;      // V; MODE_OUT: then -W
+  static constexpr int W = OUT ? V : V + SZ_ROW;           // MODE_MAP keeps W apart
+  static constexpr int TB = (OUT || !DELTA) ? V + SZ_ROW : W + SZ_ROW;
+  static constexpr int A = DELTA ? TB + SZ_T : TB;         // MODE_OUT only
+  static constexpr int VEC = OUT ? A + SZ_A : (DELTA ? TB + SZ_T : TB);
+  static constexpr int SIZE = VEC + SZ_VEC;
+};
+
 template <int MODE, bool DELTA>
-__global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW / 4)) void chunk_kernel(const Args a) {
+__global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_kernel(const Args a) {
   constexpr bool OUT = MODE == MODE_OUT;
   constexpr int NWT = Waves<MODE, DELTA>::value;  // waves in this workgroup
   constexpr int NT = NWT * 64;
   constexpr int NLD = C * (DK / 8) / NT;           // 16-byte tile loads per thread
+  constexpr int NLT = C * (C / 8) / NT;            // 16-byte TB loads per thread
   constexpr int MAPROWS = DELTA ? 2 * DV : DV;
-  constexpr int OFF_K = 0;
-  constexpr int OFF_Q = SZ_ROW;  // MODE_OUT only
-  constexpr int OFF_VW = OUT ? 2 * SZ_ROW : SZ_ROW;
-  constexpr int OFF_LT = OFF_VW + SZ_ROW;
-  constexpr int OFF_A = OFF_LT + SZ_LT;  // MODE_OUT only
-  constexpr int OFF_VEC = OUT ? OFF_A + SZ_A : OFF_LT + SZ_LT;
-  constexpr int SMEM = OFF_VEC + SZ_VEC;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  bf16_t *sK = reinterpret_cast<bf16_t *>(smem + OFF_K);
-  bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + OFF_Q);
-  bf16_t *sV = reinterpret_cast<bf16_t *>(smem + OFF_VW);   // V, then -W (delta rule)
-  bf16_t *sW = sV;
-  float *sLT = reinterpret_cast<float *>(smem + OFF_LT);
-  bf16_t *sO = reinterpret_cast<bf16_t *>(smem + OFF_LT);  // O staging after T is used
-  bf16_t *sA = reinterpret_cast<bf16_t *>(smem + OFF_A);
-  float *sG = reinterpret_cast<float *>(smem + OFF_VEC);
+  typedef Lds<MODE, DELTA> LY;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LY::SIZE];
+  bf16_t *sK = reinterpret_cast<bf16_t *>(smem + LY::K);
+  bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + LY::Q);
+  bf16_t *sO = sQ;  // O staging once Q is consumed
+  bf16_t *sV = reinterpret_cast<bf16_t *>(smem + LY::V);
+  bf16_t *sW = reinterpret_cast<bf16_t *>(smem + LY::W);
+  bf16_t *sT = reinterpret_cast<bf16_t *>(smem + LY::TB);
+  bf16_t *sA = reinterpret_cast<bf16_t *>(smem + LY::A);
+  float *sG = reinterpret_cast<float *>(smem + LY::VEC);
   float *sBeta = sG + C;
   float *sGam = sG + 2 * C;
   float *sDec = sG + 3 * C;
-  float *sBG = sG + 4 * C;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
   // in the delta-rule map pass, waves 4-7 carry the transition (M) rows
   const bool m_kind = (MODE == MODE_MAP) && DELTA && wave >= NW;
+  const int wr = m_kind ? wave - NW : wave;  // wave index within its row set
   const int seg = (int)blockIdx.x;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
-  const int row0 = wave * RPW;  // first state row owned by this wave
+  const int row0 = wr * RPW;  // first state row owned by this wave
 
   // ---- state: lane holds S^T[d = 16 m + 4 g + e][row0 + 16 c + l16] in st[m][c][e]
   f32x4 st[DK / 16][2];
@@ -200,41 +362,10 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW /
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)  // identity for the transition rows, zero otherwise
-            st[m][c][e] = (m_kind && r - DV == 16 * m + 4 * g + e) ? 1.0f : 0.0f;
+            st[m][c][e] = (m_kind && r == 16 * m + 4 * g + e) ? 1.0f : 0.0f;
         }
       }
   }
-
-  // ---- register prefetch of one chunk: 4 x 16 bytes of K (and Q, V) per thread
-  u32x4 pk[4], pq[4], pv[4];
-  float pal = 1.0f, pbe = 0.0f;
-  const bool load_v = true;
-#define LA_LD1(i)                                                                                \
-  do {                                                                                           \
-    const int id = tid + NT * (i), r = id >> 4, cv = id & 15;                                    \
-    const u32x4 z = {0u, 0u, 0u, 0u};                                                            \
-    pk[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.k + (prb + r) * DK + cv * 8) : z;       \
-    if (OUT) pq[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.q + (prb + r) * DK + cv * 8) : z; \
-    if (load_v) pv[i] = r < pn ? *reinterpret_cast<const u32x4 *>(a.v + (prb + r) * DV + cv * 8) : z; \
-  } while (0)
-#define LA_PREFETCH(T0)                                                                          \
-  do {                                                                                           \
-    const int64_t pt0 = (T0);                                                                    \
-    const int pn = (int)((T - pt0) < C ? (T - pt0) : C);                                         \
-    const size_t prb = bh * (size_t)T + pt0;                                                     \
-    LA_LD1(0);                                                                                   \
-    if (NLD > 1) LA_LD1(1);                                                                      \
-    if (NLD > 2) { LA_LD1(2); LA_LD1(3); }                                                       \
-    if (wave == 0) {                                                                             \
-      pal = 1.0f;                                                                                \
-      pbe = 0.0f;                                                                                \
-      if (lane < pn) {                                                                           \
-        if (a.variant != V_ADDITIVE) pal = bf16_to_f32(a.alpha[prb + lane]);                     \
-        pbe = (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))               \
-                  ? bf16_to_f32(a.beta[prb + lane]) : 1.0f;                                      \
-      }                                                                                          \
-    }                                                                                            \
-  } while (0)
 
   float gseg = 0.0f;  // log decay over the segment (scalar-gated map)
   int64_t prev_t0 = -1;
@@ -242,7 +373,6 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW /
   const int64_t first = (int64_t)seg * a.seg_chunks * C;
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
-  if (PREFETCH && nchunks > 0) LA_PREFETCH(first);
 
   for (int ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = first + (int64_t)ci * C;
@@ -254,22 +384,54 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW /
     asm volatile("" : "+v"(lane_v));
     const int l16 = lane_v & 15, g = lane_v >> 4;
 
-    // ---- phase A: write out the previous chunk's O, move the prefetched chunk to LDS,
-    // gate prefix sums
+    // ---- phase A: issue this chunk's loads, write out the previous chunk's O, move the
+    // loaded tiles to LDS, gate prefix sums
+    u32x4 pk[NLD], pq[NLD], pv[NLD], pt[NLT > 0 ? NLT : 1];
+    float pal = 1.0f, pbe = 0.0f;
+    {
+      const size_t rb = bh * (size_t)T + t0;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int id = tid + NT * i, r = id >> 4, cv = id & 15;
+        pk[i] = r < n ? gld16(a.k + (rb + r) * DK + cv * 8) : z;
+        if (OUT) pq[i] = r < n ? gld16(a.q + (rb + r) * DK + cv * 8) : z;
+        pv[i] = r < n ? gld16(a.v + (rb + r) * DV + cv * 8) : z;
+      }
+      if (DELTA) {
+        const bf16_t *tsrc = a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK;
+#pragma unroll
+        for (int i = 0; i < NLT; ++i) {
+          const int id = tid + NT * i;
+          pt[i] = gld16(tsrc + id * 8);
+        }
+      }
+      if (wave == 0 && lane < n) {
+        if (a.variant != V_ADDITIVE) pal = bf16_to_f32(a.alpha[rb + lane]);
+        pbe = (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta)) ? bf16_to_f32(a.beta[rb + lane]) : 1.0f;
+      }
+    }
     if (OUT && prev_t0 >= 0) {
       for (int id = tid; id < prev_n * (DV / 8); id += NT) {
         const int r = id / (DV / 8), cv = id % (DV / 8);
         gst16(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8,
               *reinterpret_cast<const u32x4 *>(sO + r * LDK + cv * 8));
       }
+      __syncthreads();  // the staging area is about to receive Q
     }
-    if (!PREFETCH) LA_PREFETCH(t0);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int id = tid + NT * i, r = id >> 4, cv = id & 15;
       *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * 8) = pk[i];
       if (OUT) *reinterpret_cast<u32x4 *>(sQ + r * LDK + cv * 8) = pq[i];
-      if (load_v) *reinterpret_cast<u32x4 *>(sV + r * LDK + cv * 8) = pv[i];
+      *reinterpret_cast<u32x4 *>(sV + r * LDK + cv * 8) = pv[i];
+    }
+    if (DELTA) {
+#pragma unroll
+      for (int i = 0; i < NLT; ++i) {
+        const int id = tid + NT * i, r = id >> 3, cv = id & 7;
+        *reinterpret_cast<u32x4 *>(sT + r * LDT + cv * 8) = pt[i];
+      }
     }
     if (wave == 0) {
       float x = (a.variant == V_ADDITIVE) ? 0.0f : logf(pal);
@@ -279,149 +441,45 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW /
         if (lane >= off) x += y;
       }
       const float gC = __shfl(x, 63, 64);
-      const float gam = expf(x);
       sG[lane] = x;
       sBeta[lane] = pbe;
-      sGam[lane] = gam;
+      sGam[lane] = expf(x);
       sDec[lane] = expf(gC - x);
-      sBG[lane] = pbe * gam;
     }
     __syncthreads();
 
-    // ---- phase B: start loading the next chunk; Gram tiles K K^T (-> L^T) and Q K^T (-> A)
-    if (PREFETCH && ci + 1 < nchunks) LA_PREFETCH(t0 + C);
+    // ---- phase B: everything that does not need the state of this chunk's start (Q K^T,
+    // U~, W), then Q S^T
+    f32x4 Ut[4][2], O[4][2];
     if (OUT) {
-      // Row-tile ownership: wave w computes the K K^T tiles of row tile w and the Q K^T
-      // tiles of row tile 3 - w (five tiles per wave); the A fragments of both row tiles
-      // are loaded once and each K row tile (the B fragments) once per wave.
-      const int tk = wave, tq = 3 - wave;
-      bf16x8 ak[DK / 32], aq[DK / 32];
-#pragma unroll
-      for (int s = 0; s < DK / 32; ++s) {
-        if (DELTA) ak[s] = *reinterpret_cast<const bf16x8 *>(sK + (16 * tk + l16) * LDK + 32 * s + 8 * g);
-        aq[s] = *reinterpret_cast<const bf16x8 *>(sQ + (16 * tq + l16) * LDK + 32 * s + 8 * g);
-      }
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        LA_FENCE();
-        const bool do_kk = DELTA && tj <= tk;
-        const bool do_qk = tj <= tq;
-        if (!(do_kk || do_qk)) continue;
-        bf16x8 b[DK / 32];
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s)
-          b[s] = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
-        const int j = 16 * tj + l16;
-        const float gj = sG[j];
-        if (do_kk) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(ak[s], b[s], acc);
-          f32x4 lv;  // L_tj at the transposed position [j][t]
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 16 * tk + 4 * g + e;
-            lv[e] = (t > j) ? sBeta[t] * expf(sG[t] - gj) * acc[e] : 0.0f;
-          }
-          *reinterpret_cast<f32x4 *>(sLT + j * LDL + 16 * tk + 4 * g) = lv;
-        }
-        if (do_qk) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(aq[s], b[s], acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = 16 * tq + 4 * g + e;
-            sA[t * LDA + j] = f32_to_bf16((t >= j) ? expf(sG[t] - gj) * acc[e] : 0.0f);
-          }
-        }
-      }
-    } else if (DELTA) {
-      // K K^T tiles only, (ti, tj) with tj <= ti, dealt round robin over the waves
+      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves
       for (int job = wave; job < 10; job += NWT) {
         int ti, tj;
         tri_index(job, ti, tj);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
-          const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sK + (16 * ti + l16) * LDK + 32 * s + 8 * g);
+          const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
           const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
           acc = mfma_bf16(fa, fb, acc);
         }
         const int j = 16 * tj + l16;
         const float gj = sG[j];
-        f32x4 lv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * ti + 4 * g + e;
-          lv[e] = (t > j) ? sBeta[t] * expf(sG[t] - gj) * acc[e] : 0.0f;
-        }
-        *reinterpret_cast<f32x4 *>(sLT + j * LDL + 16 * ti + 4 * g) = lv;
-      }
-    }
-    {
-      if (OUT) {  // the two above-diagonal tiles read by the A U products
-        for (int id = tid; id < 512; id += NT) {
-          const int tile = id >> 8, e = id & 255;
-          sA[(32 * tile + (e >> 4)) * LDA + 32 * tile + 16 + (e & 15)] = 0;
+          sA[t * LDA + j] = f32_to_bf16((t >= j) ? expf(sG[t] - gj) * acc[e] : 0.0f);
         }
       }
+      // the two above-diagonal tiles read by the A U products
+      for (int id = tid; id < 512; id += NT) {
+        const int tile = id >> 8, e = id & 255;
+        sA[(32 * tile + (e >> 4)) * LDA + 32 * tile + 16 + (e & 15)] = 0;
+      }
     }
-    __syncthreads();
-
-    f32x4 Ut[4][2];  // U~ tiles of this wave's rows (delta rule, B rows)
     if (DELTA) {
-      // ---- phase C: inverses of the four 16 x 16 diagonal blocks of (I + L), written
-      // to the lower triangle of the diagonal blocks (column-by-column forward
-      // substitution, one lane per column)
-      if (wave == 0) {
-        const int bi = lane >> 4, c = lane & 15;
-        float col[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          LA_FENCE();
-          float acc = 0.0f;
-#pragma unroll
-          for (int kq = 0; kq < r; ++kq) acc += sLT[(16 * bi + kq) * LDL + 16 * bi + r] * col[kq];
-          col[r] = (r == c) ? 1.0f : (r > c ? -acc : 0.0f);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r >= c) sLT[(16 * bi + r) * LDL + 16 * bi + c] = col[r];
-      }
-      __syncthreads();
-      // ---- phase D: off-diagonal blocks T_ij = -T_ii sum_{k=j}^{i-1} L_ik T_kj, by
-      // sub-diagonal level, on fp32 MFMA (16x16x4)
-#pragma unroll
-      for (int level = 1; level <= 3; ++level) {
-        LA_FENCE();
-        if (wave < 4 - level) {
-          const int j = wave, i = wave + level;
-          f32x4 x = {0.f, 0.f, 0.f, 0.f};
-          for (int kb = j; kb < i; ++kb) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int kr = 4 * s + g;  // row of the k-block
-              const float fa = sLT[(16 * kb + kr) * LDL + 16 * i + l16];
-              float fb = sLT[(16 * kb + kr) * LDL + 16 * j + l16];
-              if (kb == j && l16 > kr) fb = 0.0f;  // upper part of a diagonal block
-              x = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, fb, x, 0, 0, 0);
-            }
-          }
-          f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {  // inner index 4 g + s: x's own rows serve as B
-            float fa = sLT[(16 * i + l16) * LDL + 16 * i + 4 * g + s];
-            if (4 * g + s > l16) fa = 0.0f;
-            y = __builtin_amdgcn_mfma_f32_16x16x4f32(fa, x[s], y, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sLT[(16 * i + 4 * g + e) * LDL + 16 * j + l16] = -y[e];
-        }
-        __syncthreads();
-      }
-      // ---- phase E1: U~ = T diag(beta) V for this wave's own state rows (registers)
       if (!m_kind) {
+        // U~ = TB V for this wave's own state rows (registers)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           LA_FENCE();
@@ -430,46 +488,41 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW /
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             if (s == 1 && mt < 2) continue;  // T is lower triangular
-            const bf16x8 fa = t_frag(sLT, sBeta, 16 * mt + l16, s, g);
+            const bf16x8 fa = col_frag(sT, LDT, mt, s, lane_v);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-              Ut[mt][c] = mfma_bf16(fa, col_frag(sV, LDK, 2 * wave + c, s, lane_v), Ut[mt][c]);
+              Ut[mt][c] = mfma_bf16(fa, col_frag(sV, LDK, 2 * wr + c, s, lane_v), Ut[mt][c]);
           }
         }
       }
-      __syncthreads();
-      // ---- phase E2: W = T diag(beta gamma) K, stored negated (bf16) over V
-      constexpr int WPT = 8 / NWT;  // W column tiles per wave
+      if (OUT || m_kind) {
+        // -W = -TB diag(gamma) K, column tiles 2 wr, 2 wr + 1 (bf16).  In MODE_OUT they
+        // overwrite the V columns that only this wave has read (for its U~ above).
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        LA_FENCE();
-        f32x4 accw[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int mt = 0; mt < 4; ++mt) {
+          LA_FENCE();
+          f32x4 accw[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (s == 1 && mt < 2) continue;
-          const bf16x8 fa = t_frag(sLT, sBG, 16 * mt + l16, s, g);
+          for (int s = 0; s < 2; ++s) {
+            if (s == 1 && mt < 2) continue;
+            const bf16x8 fa = scale8(col_frag(sT, LDT, mt, s, lane_v), ld4(sGam + 32 * s + 4 * g),
+                                     ld4(sGam + 32 * s + 16 + 4 * g));
 #pragma unroll
-          for (int c = 0; c < WPT; ++c) accw[c] = mfma_bf16(fa, col_frag(sK, LDK, WPT * wave + c, s, lane_v), accw[c]);
+            for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(fa, col_frag(sK, LDK, 2 * wr + c, s, lane_v), accw[c]);
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sW[(16 * mt + 4 * g + e) * LDK + 16 * (2 * wr + c) + l16] = f32_to_bf16(-accw[c][e]);
         }
-#pragma unroll
-        for (int c = 0; c < WPT; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sW[(16 * mt + 4 * g + e) * LDK + 16 * (WPT * wave + c) + l16] = f32_to_bf16(-accw[c][e]);
       }
-      __syncthreads();
     }
-
-    // ---- phase F: the state-dependent part, per wave on its own 32 state rows
-    f32x4 U[4][2], O[4][2];
+    if (OUT) {  // O = Q S^T (scaled by gamma in phase F)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        U[mt][c] = (DELTA && !m_kind) ? Ut[mt][c] : f32x4{0.f, 0.f, 0.f, 0.f};
-        O[mt][c] = {0.f, 0.f, 0.f, 0.f};
-      }
-    if (DELTA || OUT) {  // U = U~ - W S^T and O = Q S^T, sharing the S^T operands
+        for (int c = 0; c < 2; ++c) O[mt][c] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DK / 32; ++s) {
         bf16x8 sfr[2];
@@ -478,16 +531,32 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW /
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           LA_FENCE();
-          if (DELTA) {
-            const bf16x8 wf = frag_pair(sW, LDK, 16 * mt + l16, 32 * s, g);
+          const bf16x8 qf = frag_pair(sQ, LDK, 16 * mt + l16, 32 * s, g);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(wf, sfr[c], U[mt][c]);
-          }
-          if (OUT) {
-            const bf16x8 qf = frag_pair(sQ, LDK, 16 * mt + l16, 32 * s, g);
+          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(qf, sfr[c], O[mt][c]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- phase F: the state-dependent part, per wave on its own 32 state rows
+    f32x4 U[4][2];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(qf, sfr[c], O[mt][c]);
-          }
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) U[mt][c] = (DELTA && !m_kind) ? Ut[mt][c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (DELTA) {  // U = U~ - W S^T
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) {
+        bf16x8 sfr[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          LA_FENCE();
+          const bf16x8 wf = frag_pair(sW, LDK, 16 * mt + l16, 32 * s, g);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(wf, sfr[c], U[mt][c]);
         }
       }
     }
@@ -576,17 +645,16 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), (WG_PER_CU * NW /
     }
   } else {
     float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
+    const int rbase = m_kind ? DV : 0;
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int r = row0 + 16 * c + l16;
+        const int r = rbase + row0 + 16 * c + l16;
         *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + 16 * m + 4 * g) = st[m][c];
       }
     if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
   }
-#undef LA_PREFETCH
-#undef LA_LD1
 }
 
 // Pass 2: S_{i+1} = S_i M_i + B_i (delta rule) or e^{gsum_i} S_i + B_i, row-parallel:
@@ -655,28 +723,41 @@ Plan make_plan(int B, int H, int64_t T) {
   return Plan{(int)nseg, (int)sc};
 }
 
-size_t ws_layout(bool delta, int B, int H, int64_t T, size_t *off_maps, size_t *off_gsum,
-                 size_t *off_starts) {
+struct WsLayout {
+  size_t maps, gsum, starts, tb, total;
+};
+
+// Workspace: per-segment maps, log decays and start states (more than one segment), then
+// the per-chunk transforms (delta rule).  Every part starts on a 256-byte boundary.
+WsLayout ws_layout(bool delta, int B, int H, int64_t T) {
   const Plan p = make_plan(B, H, T);
-  if (p.nseg <= 1) return 0;
-  const size_t bhs = (size_t)B * H * p.nseg;
-  const size_t maprows = delta ? 2 * DV : DV;
+  const size_t bh = (size_t)B * H;
+  const size_t nch = (size_t)((T + C - 1) / C);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  WsLayout w{0, 0, 0, 0, 0};
   size_t off = 0;
-  *off_maps = off;
-  off += bhs * maprows * DK * 4;
-  *off_gsum = off;
-  off += ((bhs * 4 + 255) / 256) * 256;
-  *off_starts = off;
-  off += bhs * DV * DK * 4;
-  return off;
+  if (p.nseg > 1) {
+    const size_t bhs = bh * p.nseg;
+    w.maps = off;
+    off += up(bhs * (delta ? 2 * DV : DV) * DK * 4);
+    w.gsum = off;
+    off += up(bhs * 4);
+    w.starts = off;
+    off += up(bhs * DV * DK * 4);
+  }
+  if (delta) {
+    w.tb = off;
+    off += up(bh * nch * T_CHUNK * 2);
+  }
+  w.total = off;
+  return w;
 }
 
 }  // namespace gdn
 
 size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v) {
   if (d_k != gdn::DK || d_v != gdn::DV) return 0;
-  size_t a, b, c;
-  return gdn::ws_layout(variant == V_GATED_DELTA, B, H, T, &a, &b, &c);
+  return gdn::ws_layout(variant == V_GATED_DELTA, B, H, T).total;
 }
 
 void chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks) {
@@ -696,8 +777,8 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   }
   const bool delta = variant == V_GATED_DELTA;
   const Plan p = make_plan(B, H, T);
-  size_t om = 0, og = 0, os = 0;
-  ws_layout(delta, B, H, T, &om, &og, &os);
+  const WsLayout w = ws_layout(delta, B, H, T);
+  char *ws = (char *)workspace;
   Args a;
   a.q = (const bf16_t *)q;
   a.k = (const bf16_t *)k;
@@ -707,16 +788,23 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   a.S0 = S0;
   a.o = (bf16_t *)o;
   a.S_T = S_T;
-  a.maps = p.nseg > 1 ? (float *)((char *)workspace + om) : nullptr;
-  a.gsum = p.nseg > 1 ? (float *)((char *)workspace + og) : nullptr;
-  a.starts = p.nseg > 1 ? (float *)((char *)workspace + os) : nullptr;
+  a.maps = p.nseg > 1 ? (float *)(ws + w.maps) : nullptr;
+  a.gsum = p.nseg > 1 ? (float *)(ws + w.gsum) : nullptr;
+  a.starts = p.nseg > 1 ? (float *)(ws + w.starts) : nullptr;
+  a.tb = delta ? (bf16_t *)(ws + w.tb) : nullptr;
   a.T = T;
+  a.nch = (T + C - 1) / C;
+  a.B = B;
   a.H = H;
   a.nseg = p.nseg;
   a.seg_chunks = p.seg_chunks;
   a.variant = variant;
   a.has_beta = beta != nullptr;
   const dim3 grid(p.nseg, H, B);
+  if (delta && (pass_mask & PASS_TRANSFORM)) {
+    const int64_t chunks = (int64_t)B * H * a.nch;
+    hipLaunchKernelGGL(tprep_kernel, dim3((unsigned)((chunks + NW - 1) / NW)), dim3(NTHR), 0, s, a);
+  }
   if (p.nseg > 1 && (pass_mask & PASS_MAPS)) {
     if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_MAP, true>), grid, dim3(Waves<MODE_MAP, true>::value * 64), 0, s, a);
     else hipLaunchKernelGGL((chunk_kernel<MODE_MAP, false>), grid, dim3(NTHR), 0, s, a);

@@ -185,8 +185,14 @@ int la_prefill_pass(int pass, int variant, int dtype, int batch, int heads, int6
                     const void *alpha, const void *beta, const float *S0, const float *z0,
                     void *o, float *S_T, float *z_T, void *workspace, size_t workspace_bytes,
                     void *stream) {
-  if (pass != LA_PASS_MAPS && pass != LA_PASS_SCAN && pass != LA_PASS_REPLAY) return LA_ERR_INVALID;
-  const int mask = pass == LA_PASS_MAPS ? PASS_MAPS : (pass == LA_PASS_SCAN ? PASS_SCAN : PASS_REPLAY);
+  int mask;
+  switch (pass) {
+    case LA_PASS_TRANSFORM: mask = PASS_TRANSFORM; break;
+    case LA_PASS_MAPS: mask = PASS_MAPS; break;
+    case LA_PASS_SCAN: mask = PASS_SCAN; break;
+    case LA_PASS_REPLAY: mask = PASS_REPLAY; break;
+    default: return LA_ERR_INVALID;
+  }
   return prefill_impl(mask, variant, dtype, batch, heads, seq_len, d_k, d_v, eps, q, k, v, alpha,
                       beta, S0, z0, o, S_T, z_T, workspace, workspace_bytes, stream);
 }

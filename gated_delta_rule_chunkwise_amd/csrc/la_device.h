@@ -17,16 +17,20 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte global-memory load/store through an explicit global (address space 1)
+// 16-byte (and 8-byte) global-memory load/store through an explicit global (address space 1)
 // pointer, so the compiler emits global_load/global_store rather than flat accesses.
 __device__ __forceinline__ u32x4 gld16(const void *p) {
   return *(const __attribute__((address_space(1))) u32x4 *)(p);
 }
 __device__ __forceinline__ void gst16(void *p, u32x4 v) {
   *(__attribute__((address_space(1))) u32x4 *)(p) = v;
+}
+__device__ __forceinline__ void gst8(void *p, u32x2 v) {
+  *(__attribute__((address_space(1))) u32x2 *)(p) = v;
 }
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t u) { return __uint_as_float(((uint32_t)u) << 16); }

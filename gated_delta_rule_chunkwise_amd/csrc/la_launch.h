@@ -30,8 +30,8 @@ hipError_t launch_recurrent_based(int dtype, int B, int H, int64_t T, float eps,
 
 // chunk.hip (chunkwise bf16 prefill for ADDITIVE / GATED / GATED_DELTA)
 size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v);
-// pass_mask: PASS_MAPS | PASS_SCAN | PASS_REPLAY (see la_prefill_pass in la.h)
-enum { PASS_MAPS = 1, PASS_SCAN = 2, PASS_REPLAY = 4, PASS_ALL = 7 };
+// pass_mask: PASS_TRANSFORM | PASS_MAPS | PASS_SCAN | PASS_REPLAY (see la_prefill_pass in la.h)
+enum { PASS_MAPS = 1, PASS_SCAN = 2, PASS_REPLAY = 4, PASS_TRANSFORM = 8, PASS_ALL = 15 };
 hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, int d_v,
                                 const void *q, const void *k, const void *v, const void *alpha,
                                 const void *beta, const float *S0, void *o, float *S_T,

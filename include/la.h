@@ -88,7 +88,9 @@ const char *la_status_string(int status);
 
 /*
  * Workspace that la_prefill needs for this problem, in bytes (0 is possible).  The
- * workspace holds per-segment fp32 state maps of the chunked prefill (see la_prefill).
+ * workspace holds the chunked prefill's per-segment fp32 state maps and, for the gated
+ * delta rule, one bf16 64 x 64 transform per chunk of 64 tokens (8 KiB per chunk and
+ * head; see la_prefill_pass).
  * Returns LA_OK and writes *bytes, or the same validation error la_prefill would give.
  */
 int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int64_t seq_len,
@@ -113,9 +115,10 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  *
  * Method: bf16 inputs take the chunkwise path -- chunks of 64 tokens, intra-chunk
  * products on MFMA with fp32 accumulation, the gated delta rule's WY/UT transform
- * solved in LDS, and an fp32 state carried across chunks and across segments of
- * chunks (a three-pass segment scan: per-segment affine state maps, a scan of the
- * segment start states, then every segment replayed from its start state).  fp32
+ * solved per chunk in a pass of its own, and an fp32 state carried across chunks and
+ * across segments of chunks (a three-pass segment scan: per-segment affine state maps,
+ * a scan of the segment start states, then every segment replayed from its start
+ * state).  fp32
  * inputs take an fp32 token-recurrent path (fp32 FMA throughout).
  *
  * Supported: bf16 -- ADDITIVE/GATED/GATED_DELTA with d_k = d_v = 128 or 64;
@@ -130,26 +133,30 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
                float *z_T, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * la_prefill_pass -- run one of the three passes of la_prefill, for callers that
- * schedule them separately (to time them, to overlap them with other work, or to
- * shard one sequence across devices, where the scan becomes an exchange of per-slice
- * maps).  With the same arguments and workspace on one stream,
+ * la_prefill_pass -- run one of the passes of la_prefill, for callers that schedule
+ * them separately (to time them, to overlap them with other work, or to shard one
+ * sequence across devices, where the scan becomes an exchange of per-slice maps).  With
+ * the same arguments and workspace on one stream,
  *
- *   la_prefill(...)  ==  la_prefill_pass(LA_PASS_MAPS, ...);
+ *   la_prefill(...)  ==  la_prefill_pass(LA_PASS_TRANSFORM, ...);
+ *                        la_prefill_pass(LA_PASS_MAPS, ...);
  *                        la_prefill_pass(LA_PASS_SCAN, ...);
  *                        la_prefill_pass(LA_PASS_REPLAY, ...);
  *
- *   LA_PASS_MAPS    per segment of chunks, the affine map of its end state on its start
- *                   state (S_end = S_start M + B; M is d_k x d_k for the gated delta
- *                   rule, a scalar decay otherwise), written to the workspace
- *   LA_PASS_SCAN    segment start states S_{i+1} = S_i M_i + B_i from S0, and S_T
- *   LA_PASS_REPLAY  every segment from its start state: o (and S_T for one segment)
+ *   LA_PASS_TRANSFORM  gated delta rule on the chunked path: every chunk's UT transform
+ *                      (I + L)^{-1} diag(beta), which depends on keys and gates only,
+ *                      written to the workspace for the two passes that follow
+ *   LA_PASS_MAPS       per segment of chunks, the affine map of its end state on its
+ *                      start state (S_end = S_start M + B; M is d_k x d_k for the gated
+ *                      delta rule, a scalar decay otherwise), written to the workspace
+ *   LA_PASS_SCAN       segment start states S_{i+1} = S_i M_i + B_i from S0, and S_T
+ *   LA_PASS_REPLAY     every segment from its start state: o (and S_T for one segment)
  *
- * Passes that do not apply to a problem (one segment, fp32 inputs, other widths) do
- * nothing; LA_PASS_REPLAY then performs the whole computation.  Arguments, validation
- * and return values are those of la_prefill.
+ * Passes that do not apply to a problem (one segment, no delta rule, fp32 inputs, other
+ * widths) do nothing; LA_PASS_REPLAY then performs the rest of the computation.
+ * Arguments, validation and return values are those of la_prefill.
  */
-enum { LA_PASS_MAPS = 1, LA_PASS_SCAN = 2, LA_PASS_REPLAY = 3 };
+enum { LA_PASS_MAPS = 1, LA_PASS_SCAN = 2, LA_PASS_REPLAY = 3, LA_PASS_TRANSFORM = 4 };
 int la_prefill_pass(int pass, int variant, int dtype, int batch, int heads, int64_t seq_len,
                     int d_k, int d_v, float eps, const void *q, const void *k, const void *v,
                     const void *alpha, const void *beta, const float *S0, const float *z0,

@@ -125,6 +125,26 @@ def test_workspace_size_validates(lib):
                                          ctypes.byref(n)) == 0 and n.value == 0
 
 
+def test_workspace_holds_one_transform_per_chunk(lib):
+    """One segment per head (128 heads): the gated delta rule needs exactly one 64 x 64 bf16
+    transform per chunk and head; the gated variant needs nothing."""
+    n = ctypes.c_size_t(0)
+    T = 64 * 100 + 5  # 101 chunks, the last partial
+    assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 2, 64, T, 128, 128,
+                                         ctypes.byref(n)) == 0
+    assert n.value == 2 * 64 * 101 * 64 * 64 * 2
+    assert lib.la_prefill_workspace_size(la.GATED, la.BF16, 2, 64, T, 128, 128,
+                                         ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_prefill_pass_rejects_unknown_pass(lib):
+    for bad in (0, 5, -1):
+        assert lib.la_prefill_pass(bad, la.GATED_DELTA, la.BF16, 1, 2, 100, 128, 128, 1e-6,
+                                   P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), None, None,
+                                   P(6 * A), P(8 * A), None, None, 0, None) == -2
+
+
 def decode(lib, variant=la.GATED_DELTA, dtype=la.BF16, n=16, dk=128, dv=128, S_in=A, z_in=None,
            S_out=2 * A, z_out=None, q=4 * A, k=5 * A, v=6 * A, alpha=7 * A, beta=8 * A, o=9 * A):
     f = lambda x: None if x is None else P(x)

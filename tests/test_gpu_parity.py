@@ -199,7 +199,7 @@ def test_chunk_split_resume_on_gpu(la):
 
 @pytest.mark.parametrize("variant", ROWS_VARIANTS)
 def test_prefill_passes_compose_to_prefill(la, variant):
-    """la_prefill == la_prefill_pass(MAPS); (SCAN); (REPLAY), bit for bit."""
+    """la_prefill == la_prefill_pass(TRANSFORM); (MAPS); (SCAN); (REPLAY), bit for bit."""
     q, k, v, a, b = _inputs(variant, 1, 4, 64 * 20 + 7, 128, 128, torch.bfloat16, 60)
     nseg, _ = la.segments(variant, la.BF16, 1, 4, q.shape[2], 128, 128)
     assert nseg > 1
@@ -208,7 +208,7 @@ def test_prefill_passes_compose_to_prefill(la, variant):
                      dtype=torch.uint8, device=DEV)
     o2 = torch.empty_like(o1)
     S2 = torch.empty_like(S1)
-    for p in (la.PASS_MAPS, la.PASS_SCAN, la.PASS_REPLAY):
+    for p in (la.PASS_TRANSFORM, la.PASS_MAPS, la.PASS_SCAN, la.PASS_REPLAY):
         la.prefill(variant, q, k, v, a, b, o=o2, S_T=S2, workspace=ws, pass_=p)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
