@@ -55,9 +55,14 @@ constexpr int RPW = DV / NW;  // state rows per wave (two 16-row column tiles)
 // Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
 // would raise register pressure past what two workgroups per CU allow).
 #define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
+#ifndef LA_CHUNK_PREFETCH
+#define LA_CHUNK_PREFETCH 0
+#endif
+// Load the next chunk's tiles into registers while the current one is processed.
+constexpr bool PREFETCH = LA_CHUNK_PREFETCH != 0;
 
 constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V, W, O staging
-constexpr int LDA = C + 8;   // bf16 [C][C]: decay-masked Q K^T
+constexpr int LDA = C + 8;   // bf16 [C][C]: decay-masked Q K^T, transposed
 constexpr int LDT = C + 8;   // bf16 [C][C]: (T diag(beta))^T
 
 constexpr int SZ_ROW = C * LDK * 2;
@@ -75,7 +80,7 @@ struct Args {
   bf16_t *o;
   float *S_T;        // end state written by pass 3 when there is a single segment
   float *maps;       // [BH][nseg][maprows][DK] per-segment maps (rows: B_seg, then M_seg)
-  float *gsum;       // [BH][nseg] per-segment log decay (no delta rule)
+  float *gsum;       // [BH][nseg] per-segment log2 decay (no delta rule)
   float *starts;     // [BH][nseg][DV][DK] segment start states
   bf16_t *tb;        // [BH][nch][C][C] per-chunk (T diag(beta))^T (delta rule)
   int64_t T, nch;
@@ -169,11 +174,11 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
       kf[rt][s] = __builtin_bit_cast(bf16x8, w);
     }
 
-  // gates: g_t (inclusive prefix sum of log alpha) and beta_t, kept in LDS for broadcast
+  // gates: g_t (inclusive prefix sum of log2 alpha) and beta_t, kept in LDS for broadcast
   {
     float gx = 0.0f, be = 0.0f;
     if (lane < n) {
-      gx = logf(bf16_to_f32(a.alpha[base + lane]));
+      gx = log2f(bf16_to_f32(a.alpha[base + lane]));
       be = bf16_to_f32(a.beta[base + lane]);
     }
 #pragma unroll
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
       if (k < i) {
         f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = br * expf(gr - gc[e]) * acc[e];  // L_rc, r > c
+        for (int e = 0; e < 4; ++e) v[e] = br * exp2f(gr - gc[e]) * acc[e];  // L_rc, r > c
         al[i * (i - 1) / 2 + k] = v;
       } else {  // diagonal: L_bb^T[c][r] = L_rc for r > c, from the block (b, b)
         const f32x4 bc = ld4(L.beta + 16 * k + 4 * grp);
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
         for (int e = 0; e < 4; ++e) {
           const int c = 16 * k + 4 * grp + e;
           // the block is symmetric: acc[e] is also k_r . k_c with r = c, c = r swapped
-          v[e] = c > r ? bc[e] * expf(gc[e] - gr) * acc[e] : 0.0f;  // L_cr, c > r
+          v[e] = c > r ? bc[e] * exp2f(gc[e] - gr) * acc[e] : 0.0f;  // L_cr, c > r
         }
         // lane (grp, l16) holds L_bb[4 grp + e][l16] = L_bb^T[l16][4 grp + e]
         *reinterpret_cast<f32x4 *>(L.d[i] + l16 * LDD + 4 * grp) = v;
@@ -374,6 +379,36 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
 
+  // One chunk's tiles in registers (16-byte pieces of K, Q, V and TB per thread) and its
+  // gates (wave 0); with PREFETCH they are loaded one chunk ahead.
+  u32x4 pk[NLD], pq[NLD], pv[NLD], pt[NLT > 0 ? NLT : 1];
+  float pal = 1.0f, pbe = 0.0f;
+#define LA_LOAD(T0, N)                                                                             \
+  do {                                                                                             \
+    const int64_t lt0 = (T0);                                                                      \
+    const int ln = (N);                                                                            \
+    const size_t rb = bh * (size_t)T + lt0;                                                        \
+    const u32x4 z = {0u, 0u, 0u, 0u};                                                              \
+    _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                              \
+      const int id = tid + NT * i, r = id >> 4, cv = id & 15;                                      \
+      pk[i] = r < ln ? gld16(a.k + (rb + r) * DK + cv * 8) : z;                                    \
+      if (OUT) pq[i] = r < ln ? gld16(a.q + (rb + r) * DK + cv * 8) : z;                           \
+      pv[i] = r < ln ? gld16(a.v + (rb + r) * DV + cv * 8) : z;                                    \
+    }                                                                                              \
+    if (DELTA) {                                                                                   \
+      const bf16_t *tsrc = a.tb + (bh * a.nch + (size_t)(lt0 / C)) * T_CHUNK;                      \
+      _Pragma("unroll") for (int i = 0; i < NLT; ++i) pt[i] = gld16(tsrc + (tid + NT * i) * 8);    \
+    }                                                                                              \
+    pal = 1.0f;                                                                                    \
+    pbe = 0.0f;                                                                                    \
+    if (wave == 0 && lane < ln) {                                                                  \
+      if (a.variant != V_ADDITIVE) pal = bf16_to_f32(a.alpha[rb + lane]);                          \
+      pbe = (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))                   \
+                ? bf16_to_f32(a.beta[rb + lane]) : 1.0f;                                           \
+    }                                                                                              \
+  } while (0)
+  if (PREFETCH && nchunks > 0) LA_LOAD(first, (int)((T - first) < C ? (T - first) : C));
+
   for (int ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = first + (int64_t)ci * C;
     const int n = (int)((T - t0) < C ? (T - t0) : C);
@@ -384,33 +419,9 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     asm volatile("" : "+v"(lane_v));
     const int l16 = lane_v & 15, g = lane_v >> 4;
 
-    // ---- phase A: issue this chunk's loads, write out the previous chunk's O, move the
-    // loaded tiles to LDS, gate prefix sums
-    u32x4 pk[NLD], pq[NLD], pv[NLD], pt[NLT > 0 ? NLT : 1];
-    float pal = 1.0f, pbe = 0.0f;
-    {
-      const size_t rb = bh * (size_t)T + t0;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int id = tid + NT * i, r = id >> 4, cv = id & 15;
-        pk[i] = r < n ? gld16(a.k + (rb + r) * DK + cv * 8) : z;
-        if (OUT) pq[i] = r < n ? gld16(a.q + (rb + r) * DK + cv * 8) : z;
-        pv[i] = r < n ? gld16(a.v + (rb + r) * DV + cv * 8) : z;
-      }
-      if (DELTA) {
-        const bf16_t *tsrc = a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK;
-#pragma unroll
-        for (int i = 0; i < NLT; ++i) {
-          const int id = tid + NT * i;
-          pt[i] = gld16(tsrc + id * 8);
-        }
-      }
-      if (wave == 0 && lane < n) {
-        if (a.variant != V_ADDITIVE) pal = bf16_to_f32(a.alpha[rb + lane]);
-        pbe = (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta)) ? bf16_to_f32(a.beta[rb + lane]) : 1.0f;
-      }
-    }
+    // ---- phase A: write out the previous chunk's O, move this chunk's tiles (loaded
+    // into registers during the previous chunk) to LDS, gate prefix sums
+    if (!PREFETCH) LA_LOAD(t0, n);
     if (OUT && prev_t0 >= 0) {
       for (int id = tid; id < prev_n * (DV / 8); id += NT) {
         const int r = id / (DV / 8), cv = id % (DV / 8);
@@ -434,7 +445,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       }
     }
     if (wave == 0) {
-      float x = (a.variant == V_ADDITIVE) ? 0.0f : logf(pal);
+      float x = (a.variant == V_ADDITIVE) ? 0.0f : log2f(pal);  // gates in log2 units
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -443,38 +454,47 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       const float gC = __shfl(x, 63, 64);
       sG[lane] = x;
       sBeta[lane] = pbe;
-      sGam[lane] = expf(x);
-      sDec[lane] = expf(gC - x);
+      sGam[lane] = exp2f(x);
+      sDec[lane] = exp2f(gC - x);
     }
     __syncthreads();
 
     // ---- phase B: everything that does not need the state of this chunk's start (Q K^T,
     // U~, W), then Q S^T
+    if (PREFETCH && ci + 1 < nchunks) {
+      const int64_t nt0 = t0 + C;
+      LA_LOAD(nt0, (int)((T - nt0) < C ? (T - nt0) : C));
+    }
     f32x4 Ut[4][2], O[4][2];
     if (OUT) {
-      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves
-      for (int job = wave; job < 10; job += NWT) {
-        int ti, tj;
-        tri_index(job, ti, tj);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves, stored
+      // transposed (row j, column t): each lane writes its four rows t as 8 bytes
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-          const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
-          const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
-          acc = mfma_bf16(fa, fb, acc);
-        }
-        const int j = 16 * tj + l16;
-        const float gj = sG[j];
+      for (int m = 0; m < 3; ++m) {
+        const int job = wave + NWT * m;
+        if (job < 10) {
+          int ti, tj;
+          tri_index(job, ti, tj);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * ti + 4 * g + e;
-          sA[t * LDA + j] = f32_to_bf16((t >= j) ? expf(sG[t] - gj) * acc[e] : 0.0f);
+          for (int s = 0; s < DK / 32; ++s) {
+            const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
+            const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
+            acc = mfma_bf16(fa, fb, acc);
+          }
+          const int j = 16 * tj + l16;
+          const float gj = sG[j];
+          const f32x4 gt = ld4(sG + 16 * ti + 4 * g);
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (16 * ti + 4 * g + e >= j) ? exp2f(gt[e] - gj) * acc[e] : 0.0f;
+          *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         }
       }
-      // the two above-diagonal tiles read by the A U products
-      for (int id = tid; id < 512; id += NT) {
-        const int tile = id >> 8, e = id & 255;
-        sA[(32 * tile + (e >> 4)) * LDA + 32 * tile + 16 + (e & 15)] = 0;
+      // the two above-diagonal tiles read by the A U products: A (0,1) and (2,3)
+      if (tid < 128) {
+        const int tile = tid >> 6, e = tid & 63;
+        *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
       }
     }
     if (DELTA) {
@@ -496,29 +516,38 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         }
       }
       if (OUT || m_kind) {
-        // -W = -TB diag(gamma) K, column tiles 2 wr, 2 wr + 1 (bf16).  In MODE_OUT they
-        // overwrite the V columns that only this wave has read (for its U~ above).
+        // -W = -TB diag(gamma) K, column tiles 2 wr, 2 wr + 1 (bf16), computed as
+        // W^T = K^T diag(gamma) TB^T so that each lane holds four consecutive columns of a
+        // row of W (one 8-byte write).  In MODE_OUT they overwrite the V columns that only
+        // this wave has read (for its U~ above).
+        bf16x8 kt[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) kt[c][s] = col_frag(sK, LDK, 2 * wr + c, s, lane_v);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           LA_FENCE();
           f32x4 accw[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            if (s == 1 && mt < 2) continue;
-            const bf16x8 fa = scale8(col_frag(sT, LDT, mt, s, lane_v), ld4(sGam + 32 * s + 4 * g),
+            if (s == 1 && mt < 2) continue;  // T is lower triangular
+            const bf16x8 tf = scale8(col_frag(sT, LDT, mt, s, lane_v), ld4(sGam + 32 * s + 4 * g),
                                      ld4(sGam + 32 * s + 16 + 4 * g));
 #pragma unroll
-            for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(fa, col_frag(sK, LDK, 2 * wr + c, s, lane_v), accw[c]);
+            for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(kt[c][s], tf, accw[c]);
           }
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              sW[(16 * mt + 4 * g + e) * LDK + 16 * (2 * wr + c) + l16] = f32_to_bf16(-accw[c][e]);
+          for (int c = 0; c < 2; ++c) {  // lane: W[16 mt + l16][16 (2 wr + c) + 4 g + e]
+            const f32x4 w = -accw[c];
+            *reinterpret_cast<bf16x4 *>(sW + (16 * mt + l16) * LDK + 16 * (2 * wr + c) + 4 * g) =
+                bf16x4{(__bf16)w[0], (__bf16)w[1], (__bf16)w[2], (__bf16)w[3]};
+          }
         }
       }
     }
-    if (OUT) {  // O = Q S^T (scaled by gamma in phase F)
+    if (OUT) {  // O^T = S Q^T (scaled by gamma in phase F): lane (g, l16) of tile (mt, c)
+                // holds O[16 mt + l16][row0 + 16 c + 4 g + e]
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -533,7 +562,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
           LA_FENCE();
           const bf16x8 qf = frag_pair(sQ, LDK, 16 * mt + l16, 32 * s, g);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(qf, sfr[c], O[mt][c]);
+          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qf, O[mt][c]);
         }
       }
     }
@@ -584,25 +613,24 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         dufr[c][s2] = pack_pair(u0 * d0, u1 * d1);
       }
     }
-    if (OUT) {  // O = diag(gamma) Q S^T + A U  -> bf16 staging for coalesced stores
+    if (OUT) {  // O^T = S Q^T diag(gamma) + U^T A^T  -> bf16 staging (row-major O)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         LA_FENCE();
-        const f32x4 gam = ld4(sGam + 16 * mt + 4 * g);
+        const float gam = sGam[16 * mt + l16];
 #pragma unroll
         for (int c = 0; c < 2; ++c) O[mt][c] = O[mt][c] * gam;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (s2 == 1 && mt < 2) continue;  // A is causal
-          const bf16x8 af = frag_pair(sA, LDA, 16 * mt + l16, 32 * s2, g);
+          const bf16x8 af = col_frag(sA, LDA, mt, s2, lane_v);  // A[16 mt + l16][tokens]
 #pragma unroll
-          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(af, ufr[c][s2], O[mt][c]);
+          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], af, O[mt][c]);
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sO[(16 * mt + 4 * g + e) * LDK + row0 + 16 * c + l16] = f32_to_bf16(O[mt][c][e]);
+          *reinterpret_cast<bf16x4 *>(sO + (16 * mt + l16) * LDK + row0 + 16 * c + 4 * g) =
+              bf16x4{(__bf16)O[mt][c][0], (__bf16)O[mt][c][1], (__bf16)O[mt][c][2], (__bf16)O[mt][c][3]};
       }
     }
     {  // S^T <- gamma_C S^T + K^T diag(decay) U
@@ -655,6 +683,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       }
     if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
   }
+#undef LA_LOAD
 }
 
 // Pass 2: S_{i+1} = S_i M_i + B_i (delta rule) or e^{gsum_i} S_i + B_i, row-parallel:
@@ -690,7 +719,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const Args a) {
       acc.x += acc2.x;
       acc.y += acc2.y;
     } else {
-      const float dec = expf(a.gsum[bh * a.nseg + i]);
+      const float dec = exp2f(a.gsum[bh * a.nseg + i]);
       acc.x += dec * cur.x;
       acc.y += dec * cur.y;
     }
