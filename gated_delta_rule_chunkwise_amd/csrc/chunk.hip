@@ -55,13 +55,14 @@ constexpr int RPW = DV / NW;  // state rows per wave (two 16-row column tiles)
 // Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
 // would raise register pressure past what two workgroups per CU allow).
 #define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
-#ifndef LA_CHUNK_PREFETCH
-#define LA_CHUNK_PREFETCH 0
+#ifndef LA_CHUNK_PREFETCH_MAP
+#define LA_CHUNK_PREFETCH_MAP 1
 #endif
-// Load the next chunk's tiles into registers while the current one is processed.
-constexpr bool PREFETCH = LA_CHUNK_PREFETCH != 0;
+#ifndef LA_CHUNK_PREFETCH_OUT
+#define LA_CHUNK_PREFETCH_OUT 0
+#endif
 
-constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V, W, O staging
+constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V, W
 constexpr int LDA = C + 8;   // bf16 [C][C]: decay-masked Q K^T, transposed
 constexpr int LDT = C + 8;   // bf16 [C][C]: (T diag(beta))^T
 
@@ -164,23 +165,20 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
   // K rows as MFMA operands, straight from global memory: kf[rt][s] holds row 16 rt + l16,
   // columns 32 s + 8 grp .. +7 (the A and the B operand of K K^T have the same layout)
   bf16x8 kf[4][DK / 32];
+  {
+    const rsrc_t rk = make_rsrc(a.k + base * DK, (uint32_t)n * DK * 2);  // rows >= n read as 0
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-      const int r = 16 * rt + l16;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const u32x4 w = r < n ? gld16(a.k + (base + r) * DK + 32 * s + 8 * grp) : z;
-      kf[rt][s] = __builtin_bit_cast(bf16x8, w);
-    }
+      for (int s = 0; s < DK / 32; ++s)
+        kf[rt][s] = __builtin_bit_cast(bf16x8, bld16(rk, 2u * (uint32_t)((16 * rt + l16) * DK + 32 * s + 8 * grp)));
+  }
 
   // gates: g_t (inclusive prefix sum of log2 alpha) and beta_t, kept in LDS for broadcast
   {
-    float gx = 0.0f, be = 0.0f;
-    if (lane < n) {
-      gx = log2f(bf16_to_f32(a.alpha[base + lane]));
-      be = bf16_to_f32(a.beta[base + lane]);
-    }
+    const float al = bf16_to_f32(bld2(make_rsrc(a.alpha + base, (uint32_t)n * 2), 2u * lane));
+    float gx = lane < n ? log2f(al) : 0.0f;
+    const float be = bf16_to_f32(bld2(make_rsrc(a.beta + base, (uint32_t)n * 2), 2u * lane));
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(gx, off, 64);
@@ -311,7 +309,7 @@ template <int MODE, bool DELTA> struct Waves {
 template <int MODE, bool DELTA> struct Lds {
   static constexpr bool OUT = MODE == MODE_OUT;
   static constexpr int K = 0;
-  static constexpr int Q = SZ_ROW;                         // MODE_OUT: Q, then O staging
+  static constexpr int Q = SZ_ROW;                         // MODE_OUT only
   static constexpr int V = OUT ? 2 * SZ_ROW : SZ_ROW;      // V; MODE_OUT: then -W
   static constexpr int W = OUT ? V : V + SZ_ROW;           // MODE_MAP keeps W apart
   static constexpr int TB = (OUT || !DELTA) ? V + SZ_ROW : W + SZ_ROW;
@@ -328,11 +326,13 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   constexpr int NLD = C * (DK / 8) / NT;           // 16-byte tile loads per thread
   constexpr int NLT = C * (C / 8) / NT;            // 16-byte TB loads per thread
   constexpr int MAPROWS = DELTA ? 2 * DV : DV;
+  // Load the next chunk's tiles into registers while the current one is processed (where
+  // the registers allow it).
+  constexpr bool PREFETCH = OUT ? LA_CHUNK_PREFETCH_OUT != 0 : LA_CHUNK_PREFETCH_MAP != 0;
   typedef Lds<MODE, DELTA> LY;
   __shared__ __attribute__((aligned(16))) unsigned char smem[LY::SIZE];
   bf16_t *sK = reinterpret_cast<bf16_t *>(smem + LY::K);
   bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + LY::Q);
-  bf16_t *sO = sQ;  // O staging once Q is consumed
   bf16_t *sV = reinterpret_cast<bf16_t *>(smem + LY::V);
   bf16_t *sW = reinterpret_cast<bf16_t *>(smem + LY::W);
   bf16_t *sT = reinterpret_cast<bf16_t *>(smem + LY::TB);
@@ -386,25 +386,30 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 #define LA_LOAD(T0, N)                                                                             \
   do {                                                                                             \
     const int64_t lt0 = (T0);                                                                      \
-    const int ln = (N);                                                                            \
+    const uint32_t ln = (uint32_t)(N);                                                             \
     const size_t rb = bh * (size_t)T + lt0;                                                        \
-    const u32x4 z = {0u, 0u, 0u, 0u};                                                              \
+    const rsrc_t rk = make_rsrc(a.k + rb * DK, ln * DK * 2);                                       \
+    const rsrc_t rq = make_rsrc(OUT ? a.q + rb * DK : a.k, OUT ? ln * DK * 2 : 0);                 \
+    const rsrc_t rv = make_rsrc(a.v + rb * DV, ln * DV * 2);                                       \
     _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                              \
-      const int id = tid + NT * i, r = id >> 4, cv = id & 15;                                      \
-      pk[i] = r < ln ? gld16(a.k + (rb + r) * DK + cv * 8) : z;                                    \
-      if (OUT) pq[i] = r < ln ? gld16(a.q + (rb + r) * DK + cv * 8) : z;                           \
-      pv[i] = r < ln ? gld16(a.v + (rb + r) * DV + cv * 8) : z;                                    \
+      const uint32_t off = 16u * (uint32_t)(tid + NT * i);                                         \
+      pk[i] = bld16(rk, off);                                                                      \
+      if (OUT) pq[i] = bld16(rq, off);                                                             \
+      pv[i] = bld16(rv, off);                                                                      \
     }                                                                                              \
     if (DELTA) {                                                                                   \
-      const bf16_t *tsrc = a.tb + (bh * a.nch + (size_t)(lt0 / C)) * T_CHUNK;                      \
-      _Pragma("unroll") for (int i = 0; i < NLT; ++i) pt[i] = gld16(tsrc + (tid + NT * i) * 8);    \
+      const rsrc_t rt = make_rsrc(a.tb + (bh * a.nch + (size_t)(lt0 / C)) * T_CHUNK, T_CHUNK * 2); \
+      _Pragma("unroll") for (int i = 0; i < NLT; ++i) pt[i] = bld16(rt, 16u * (uint32_t)(tid + NT * i)); \
     }                                                                                              \
     pal = 1.0f;                                                                                    \
-    pbe = 0.0f;                                                                                    \
-    if (wave == 0 && lane < ln) {                                                                  \
-      if (a.variant != V_ADDITIVE) pal = bf16_to_f32(a.alpha[rb + lane]);                          \
-      pbe = (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))                   \
-                ? bf16_to_f32(a.beta[rb + lane]) : 1.0f;                                           \
+    pbe = (uint32_t)lane < ln ? 1.0f : 0.0f;                                                       \
+    if (wave == 0) {                                                                               \
+      if (a.variant != V_ADDITIVE) {                                                               \
+        const float x = bf16_to_f32(bld2(make_rsrc(a.alpha + rb, ln * 2), 2u * lane));             \
+        pal = (uint32_t)lane < ln ? x : 1.0f;                                                      \
+      }                                                                                            \
+      if (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))                      \
+        pbe = bf16_to_f32(bld2(make_rsrc(a.beta + rb, ln * 2), 2u * lane));                        \
     }                                                                                              \
   } while (0)
   if (PREFETCH && nchunks > 0) LA_LOAD(first, (int)((T - first) < C ? (T - first) : C));
@@ -419,17 +424,9 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     asm volatile("" : "+v"(lane_v));
     const int l16 = lane_v & 15, g = lane_v >> 4;
 
-    // ---- phase A: write out the previous chunk's O, move this chunk's tiles (loaded
-    // into registers during the previous chunk) to LDS, gate prefix sums
+    // ---- phase A: move this chunk's tiles (loaded into registers during the previous
+    // chunk when prefetching) to LDS, gate prefix sums
     if (!PREFETCH) LA_LOAD(t0, n);
-    if (OUT && prev_t0 >= 0) {
-      for (int id = tid; id < prev_n * (DV / 8); id += NT) {
-        const int r = id / (DV / 8), cv = id % (DV / 8);
-        gst16(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8,
-              *reinterpret_cast<const u32x4 *>(sO + r * LDK + cv * 8));
-      }
-      __syncthreads();  // the staging area is about to receive Q
-    }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int id = tid + NT * i, r = id >> 4, cv = id & 15;
@@ -459,37 +456,37 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     }
     __syncthreads();
 
-    // ---- phase B: everything that does not need the state of this chunk's start (Q K^T,
-    // U~, W), then Q S^T
+    // ---- phase B: everything that does not need the state of this chunk's start: Q K^T,
+    // U~, W
     if (PREFETCH && ci + 1 < nchunks) {
       const int64_t nt0 = t0 + C;
       LA_LOAD(nt0, (int)((T - nt0) < C ? (T - nt0) : C));
     }
-    f32x4 Ut[4][2], O[4][2];
+    f32x4 Ut[4][2];
     if (OUT) {
-      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves, stored
-      // transposed (row j, column t): each lane writes its four rows t as 8 bytes
+      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves (a wave
+      // without a third tile recomputes tile 9 and does not store it), stored transposed
+      // (row j, column t): each lane writes its four rows t as 8 bytes
 #pragma unroll
       for (int m = 0; m < 3; ++m) {
         const int job = wave + NWT * m;
-        if (job < 10) {
-          int ti, tj;
-          tri_index(job, ti, tj);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        int ti, tj;
+        tri_index(job < 10 ? job : 9, ti, tj);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < DK / 32; ++s) {
-            const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
-            const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
-            acc = mfma_bf16(fa, fb, acc);
-          }
-          const int j = 16 * tj + l16;
-          const float gj = sG[j];
-          const f32x4 gt = ld4(sG + 16 * ti + 4 * g);
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (16 * ti + 4 * g + e >= j) ? exp2f(gt[e] - gj) * acc[e] : 0.0f;
-          *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        for (int s = 0; s < DK / 32; ++s) {
+          const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
+          const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
+          acc = mfma_bf16(fa, fb, acc);
         }
+        const int j = 16 * tj + l16;
+        const float gj = sG[j];
+        const f32x4 gt = ld4(sG + 16 * ti + 4 * g);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (16 * ti + 4 * g + e >= j) ? exp2f(gt[e] - gj) * acc[e] : 0.0f;
+        if (job < 10)
+          *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
       }
       // the two above-diagonal tiles read by the A U products: A (0,1) and (2,3)
       if (tid < 128) {
@@ -498,71 +495,59 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       }
     }
     if (DELTA) {
-      if (!m_kind) {
-        // U~ = TB V for this wave's own state rows (registers)
+      // U~ = TB V for this wave's own state rows (B rows only; registers) and -W =
+      // -TB diag(gamma) K, column tiles 2 wr, 2 wr + 1 (MODE_OUT waves and the M-row waves),
+      // sharing each TB fragment.  W is formed as W^T = K^T diag(gamma) TB^T so that each
+      // lane holds four consecutive columns of a row of W (one 8-byte write); in MODE_OUT it
+      // overwrites the V columns that only this wave reads, after reading them.
+      const bool do_u = !m_kind, do_w = OUT || m_kind;
+      bf16x8 vf[2][2], kt[2][2];  // V columns and diag(gamma) K columns, k = tokens
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          LA_FENCE();
-          Ut[mt][0] = {0.f, 0.f, 0.f, 0.f};
-          Ut[mt][1] = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 ga = ld4(sGam + 32 * s + 4 * g), gb = ld4(sGam + 32 * s + 16 + 4 * g);
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            if (s == 1 && mt < 2) continue;  // T is lower triangular
-            const bf16x8 fa = col_frag(sT, LDT, mt, s, lane_v);
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              Ut[mt][c] = mfma_bf16(fa, col_frag(sV, LDK, 2 * wr + c, s, lane_v), Ut[mt][c]);
-          }
+        for (int c = 0; c < 2; ++c) {
+          if (do_u) vf[c][s] = col_frag(sV, LDK, 2 * wr + c, s, lane_v);
+          if (do_w) kt[c][s] = scale8(col_frag(sK, LDK, 2 * wr + c, s, lane_v), ga, gb);
         }
       }
-      if (OUT || m_kind) {
-        // -W = -TB diag(gamma) K, column tiles 2 wr, 2 wr + 1 (bf16), computed as
-        // W^T = K^T diag(gamma) TB^T so that each lane holds four consecutive columns of a
-        // row of W (one 8-byte write).  In MODE_OUT they overwrite the V columns that only
-        // this wave has read (for its U~ above).
-        bf16x8 kt[2][2];
+      // steps (mt, s), s = 1 only for mt >= 2 (T is lower triangular); the TB fragment of
+      // the next step is read before this step's MFMAs
+      bf16x8 tfb[2];
+      tfb[0] = col_frag(sT, LDT, 0, 0, lane_v);
+      f32x4 accw[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+      for (int it = 0; it < 6; ++it) {
+        const int mt = it < 2 ? it : 2 + (it - 2) / 2, s = it < 2 ? 0 : (it - 2) % 2;
+        if (it + 1 < 6) {
+          const int it1 = it + 1;
+          const int mt1 = it1 < 2 ? it1 : 2 + (it1 - 2) / 2, s1 = it1 < 2 ? 0 : (it1 - 2) % 2;
+          tfb[it1 & 1] = col_frag(sT, LDT, mt1, s1, lane_v);
+        }
+        LA_FENCE();
+        const bf16x8 tf = tfb[it & 1];
+        if (s == 0) {
 #pragma unroll
-          for (int s = 0; s < 2; ++s) kt[c][s] = col_frag(sK, LDK, 2 * wr + c, s, lane_v);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          LA_FENCE();
-          f32x4 accw[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            if (s == 1 && mt < 2) continue;  // T is lower triangular
-            const bf16x8 tf = scale8(col_frag(sT, LDT, mt, s, lane_v), ld4(sGam + 32 * s + 4 * g),
-                                     ld4(sGam + 32 * s + 16 + 4 * g));
-#pragma unroll
-            for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(kt[c][s], tf, accw[c]);
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {  // lane: W[16 mt + l16][16 (2 wr + c) + 4 g + e]
-            const f32x4 w = -accw[c];
-            *reinterpret_cast<bf16x4 *>(sW + (16 * mt + l16) * LDK + 16 * (2 * wr + c) + 4 * g) =
-                bf16x4{(__bf16)w[0], (__bf16)w[1], (__bf16)w[2], (__bf16)w[3]};
+          for (int c = 0; c < 2; ++c) {
+            Ut[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accw[c] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
         }
-      }
-    }
-    if (OUT) {  // O^T = S Q^T (scaled by gamma in phase F): lane (g, l16) of tile (mt, c)
-                // holds O[16 mt + l16][row0 + 16 c + 4 g + e]
+        if (do_u) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+          for (int c = 0; c < 2; ++c) Ut[mt][c] = mfma_bf16(tf, vf[c][s], Ut[mt][c]);
+        }
+        if (do_w) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) O[mt][c] = {0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(kt[c][s], tf, accw[c]);
+          if (mt < 2 || s == 1) {
 #pragma unroll
-      for (int s = 0; s < DK / 32; ++s) {
-        bf16x8 sfr[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          LA_FENCE();
-          const bf16x8 qf = frag_pair(sQ, LDK, 16 * mt + l16, 32 * s, g);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qf, O[mt][c]);
+            for (int c = 0; c < 2; ++c) {  // lane: W[16 mt + l16][16 (2 wr + c) + 4 g + e]
+              const f32x4 w = -accw[c];
+              *reinterpret_cast<bf16x4 *>(sW + (16 * mt + l16) * LDK + 16 * (2 * wr + c) + 4 * g) =
+                  bf16x4{(__bf16)w[0], (__bf16)w[1], (__bf16)w[2], (__bf16)w[3]};
+            }
+          }
         }
       }
     }
@@ -574,20 +559,24 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int c = 0; c < 2; ++c) U[mt][c] = (DELTA && !m_kind) ? Ut[mt][c] : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (DELTA) {  // U = U~ - W S^T
+    if (DELTA) {  // U = U~ - W S^T; W fragments read two steps ahead
+#define LA_WF(it) frag_pair(sW, LDK, 16 * ((it) % 4) + l16, 32 * ((it) / 4), g)
+      bf16x8 wb[3], sfr[2];
+      wb[0] = LA_WF(0);
+      wb[1] = LA_WF(1);
 #pragma unroll
-      for (int s = 0; s < DK / 32; ++s) {
-        bf16x8 sfr[2];
+      for (int it = 0; it < 16; ++it) {
+        const int s = it / 4, mt = it % 4;
+        if (it + 2 < 16) wb[(it + 2) % 3] = LA_WF(it + 2);
+        if (mt == 0) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          LA_FENCE();
-          const bf16x8 wf = frag_pair(sW, LDK, 16 * mt + l16, 32 * s, g);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(wf, sfr[c], U[mt][c]);
+          for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
         }
+        LA_FENCE();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(wb[it % 3], sfr[c], U[mt][c]);
       }
+#undef LA_WF
     }
     LA_FENCE();
     bf16x8 ufr[2][2], dufr[2][2];  // U and diag(decay) U as operands with k = tokens
@@ -613,38 +602,79 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         dufr[c][s2] = pack_pair(u0 * d0, u1 * d1);
       }
     }
-    if (OUT) {  // O^T = S Q^T diag(gamma) + U^T A^T  -> bf16 staging (row-major O)
+    if (OUT) {
+      // O^T = S Q^T diag(gamma) + U^T A^T on the chunk's entering state: lane (g, l16) of
+      // tile (mt, c) holds O[16 mt + l16][row0 + 16 c + 4 g + e], four consecutive outputs
+      // of one token, stored straight to HBM (8 bytes; rows past the chunk are dropped).
+      // Q and A fragments are read two steps / one step ahead.
+      f32x4 O[4][2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        LA_FENCE();
-        const float gam = sGam[16 * mt + l16];
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) O[mt][c] = O[mt][c] * gam;
+        for (int c = 0; c < 2; ++c) O[mt][c] = {0.f, 0.f, 0.f, 0.f};
+#define LA_QF(it) frag_pair(sQ, LDK, 16 * ((it) % 4) + l16, 32 * ((it) / 4), g)
+      {
+        bf16x8 qb[3], sfr[2];
+        qb[0] = LA_QF(0);
+        qb[1] = LA_QF(1);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          if (s2 == 1 && mt < 2) continue;  // A is causal
-          const bf16x8 af = col_frag(sA, LDA, mt, s2, lane_v);  // A[16 mt + l16][tokens]
+        for (int it = 0; it < 16; ++it) {
+          const int s = it / 4, mt = it % 4;
+          if (it + 2 < 16) qb[(it + 2) % 3] = LA_QF(it + 2);
+          if (mt == 0) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], af, O[mt][c]);
+            for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+          }
+          LA_FENCE();
+#pragma unroll
+          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qb[it % 3], O[mt][c]);
         }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          *reinterpret_cast<bf16x4 *>(sO + (16 * mt + l16) * LDK + row0 + 16 * c + 4 * g) =
-              bf16x4{(__bf16)O[mt][c][0], (__bf16)O[mt][c][1], (__bf16)O[mt][c][2], (__bf16)O[mt][c][3]};
       }
+#undef LA_QF
+      const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
+#define LA_AF(it) col_frag(sA, LDA, (it) < 2 ? (it) : 2 + ((it) - 2) / 2, (it) < 2 ? 0 : ((it) - 2) % 2, lane_v)
+      bf16x8 ab[2];
+      ab[0] = LA_AF(0);
+#pragma unroll
+      for (int it = 0; it < 6; ++it) {
+        const int mt = it < 2 ? it : 2 + (it - 2) / 2, s2 = it < 2 ? 0 : (it - 2) % 2;
+        if (it + 1 < 6) ab[(it + 1) & 1] = LA_AF(it + 1);
+        if (s2 == 0) {
+          const float gam = sGam[16 * mt + l16];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) O[mt][c] = O[mt][c] * gam;
+        }
+        LA_FENCE();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], ab[it & 1], O[mt][c]);
+        if (mt < 2 || s2 == 1) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const bf16x4 h = {(__bf16)O[mt][c][0], (__bf16)O[mt][c][1], (__bf16)O[mt][c][2], (__bf16)O[mt][c][3]};
+            bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 16 * c + 4 * g), __builtin_bit_cast(u32x2, h));
+          }
+        }
+      }
+#undef LA_AF
     }
-    {  // S^T <- gamma_C S^T + K^T diag(decay) U
+    {  // S^T <- gamma_C S^T + K^T diag(decay) U; K fragments read one step ahead
       const float gC = sGam[C - 1];
       gseg += sG[C - 1];
+      bf16x8 kb[2][2];
+      kb[0][0] = col_frag(sK, LDK, 0, 0, lane_v);
+      kb[0][1] = col_frag(sK, LDK, 0, 1, lane_v);
 #pragma unroll
       for (int m = 0; m < DK / 16; ++m) {
+        if (m + 1 < DK / 16) {
+          kb[(m + 1) & 1][0] = col_frag(sK, LDK, m + 1, 0, lane_v);
+          kb[(m + 1) & 1][1] = col_frag(sK, LDK, m + 1, 1, lane_v);
+        }
         LA_FENCE();
-        const bf16x8 k0 = col_frag(sK, LDK, m, 0, lane_v), k1 = col_frag(sK, LDK, m, 1, lane_v);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           f32x4 acc = st[m][c] * gC;
-          acc = mfma_bf16(k0, dufr[c][0], acc);
-          acc = mfma_bf16(k1, dufr[c][1], acc);
+          acc = mfma_bf16(kb[m & 1][0], dufr[c][0], acc);
+          acc = mfma_bf16(kb[m & 1][1], dufr[c][1], acc);
           st[m][c] = acc;
         }
       }
@@ -655,13 +685,6 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   }
 
   if (OUT) {
-    if (prev_t0 >= 0) {
-      for (int id = tid; id < prev_n * (DV / 8); id += NT) {
-        const int r = id / (DV / 8), cv = id % (DV / 8);
-        gst16(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8,
-              *reinterpret_cast<const u32x4 *>(sO + r * LDK + cv * 8));
-      }
-    }
     if (a.nseg == 1 && a.S_T) {
 #pragma unroll
       for (int m = 0; m < DK / 16; ++m)

@@ -33,6 +33,26 @@ __device__ __forceinline__ void gst8(void *p, u32x2 v) {
   *(__attribute__((address_space(1))) u32x2 *)(p) = v;
 }
 
+// Raw buffer access (CDNA "buffer" instructions): a descriptor holds a wave-uniform base
+// address and a size in bytes; lanes pass 32-bit byte offsets.  Loads beyond the size
+// return zero and stores beyond it are dropped, which is how partial tiles are handled.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bst16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bst8(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint16_t bld2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
 
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
