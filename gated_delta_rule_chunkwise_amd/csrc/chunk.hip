@@ -55,8 +55,10 @@ constexpr int RPW = DV / NW;  // state rows per wave (two 16-row column tiles)
 // Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
 // would raise register pressure past what two workgroups per CU allow).
 #define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
+// Parts of a chunk's inputs (bit masks for the register prefetch).
+enum { LD_K = 1, LD_Q = 2, LD_V = 4, LD_T = 8, LD_G = 16, LD_ALL = 31 };
 #ifndef LA_CHUNK_PREFETCH_MAP
-#define LA_CHUNK_PREFETCH_MAP 1
+#define LA_CHUNK_PREFETCH_MAP 31
 #endif
 #ifndef LA_CHUNK_PREFETCH_OUT
 #define LA_CHUNK_PREFETCH_OUT 0
@@ -90,24 +92,34 @@ struct Args {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// A operand with k along the columns of a row-major tile: row `row`, 32-wide k-step at
-// col0; lane group g supplies columns col0+4g..+3 and col0+16+4g..+3, the column order
-// of two stacked 16x16 accumulator tiles (their rows 4g..4g+3).
-__device__ __forceinline__ bf16x8 frag_pair(const bf16_t *base, int ld, int row, int col0, int g) {
-  const uint2 lo = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 4 * g);
-  const uint2 hi = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 16 + 4 * g);
-  const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
 // Operand with k along the ROWS (tokens) of a row-major [token][d] tile: lane (g, i)
-// receives column 16 nt + i at tokens 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3 (the
-// same token order as frag_pair's columns).  ds_read_b64_tr_b16 hands lane i of each
+// receives column 16 nt + i at tokens 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3, the
+// order of the rows of two stacked 16 x 16 accumulator tiles (their rows 4 g .. 4 g + 3), so
+// accumulators over tokens serve directly as the other operand.  ds_read_b64_tr_b16 hands lane i of each
 // 16-lane group element (i & 3) of the 8-byte chunks addressed by lanes 4 e + (i >> 2),
 // e = 0..3; lane j therefore addresses row tbase + (j >> 2), columns 16 nt + 4 (j & 3).
 __device__ __forceinline__ bf16x8 col_frag(const bf16_t *tile, int ld, int nt, int s, int lane) {
   const int g = lane >> 4, i = lane & 15;
   const bf16_t *p0 = tile + (32 * s + 4 * g + (i >> 2)) * ld + 16 * nt + 4 * (i & 3);
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + 16 * ld));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The state's register layout.  State tile m (16 rows of S^T) holds, in C-layout row
+// 4 g + e, the key index d = sd(m, g) + e with sd(m, g) = 32 (m / 2) + 8 g + 4 (m % 2): the
+// two tiles 2 s and 2 s + 1 of lane group g together cover the eight consecutive keys
+// 32 s + 8 g .. +7, so the state packed as an MFMA operand pairs with one contiguous
+// 16-byte read of a row of W or Q (no bank conflicts, unlike two 8-byte pieces).
+__device__ __forceinline__ int sd(int m, int g) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1); }
+
+// K^T rows in the state's key order as an A operand with k = tokens: lane (g, i) receives
+// K[tokens 32 s + 4 g + 0..3, 32 s + 16 + 4 g + 0..3][d = sd(m, i >> 2) + (i & 3)].  Same
+// transpose read as col_frag, with each lane quad addressing its own 4-key chunk.
+__device__ __forceinline__ bf16x8 kstate_frag(const bf16_t *tile, int ld, int m, int s, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const bf16_t *p0 = tile + (32 * s + 4 * g + (i >> 2)) * ld + sd(m, i & 3);
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + 16 * ld));
@@ -326,9 +338,9 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   constexpr int NLD = C * (DK / 8) / NT;           // 16-byte tile loads per thread
   constexpr int NLT = C * (C / 8) / NT;            // 16-byte TB loads per thread
   constexpr int MAPROWS = DELTA ? 2 * DV : DV;
-  // Load the next chunk's tiles into registers while the current one is processed (where
-  // the registers allow it).
-  constexpr bool PREFETCH = OUT ? LA_CHUNK_PREFETCH_OUT != 0 : LA_CHUNK_PREFETCH_MAP != 0;
+  // The parts of the next chunk loaded into registers while the current one is processed
+  // (as many as the registers allow).
+  constexpr int PF = OUT ? LA_CHUNK_PREFETCH_OUT : LA_CHUNK_PREFETCH_MAP;
   typedef Lds<MODE, DELTA> LY;
   __shared__ __attribute__((aligned(16))) unsigned char smem[LY::SIZE];
   bf16_t *sK = reinterpret_cast<bf16_t *>(smem + LY::K);
@@ -352,7 +364,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   const int64_t T = a.T;
   const int row0 = wr * RPW;  // first state row owned by this wave
 
-  // ---- state: lane holds S^T[d = 16 m + 4 g + e][row0 + 16 c + l16] in st[m][c][e]
+  // ---- state: lane holds S^T[d = sd(m, g) + e][row0 + 16 c + l16] in st[m][c][e]
   f32x4 st[DK / 16][2];
   {
     const float *src = nullptr;
@@ -363,11 +375,11 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       for (int c = 0; c < 2; ++c) {
         const int r = row0 + 16 * c + l16;
         if (src) {
-          st[m][c] = ld4(src + (size_t)r * DK + 16 * m + 4 * g);
+          st[m][c] = ld4(src + (size_t)r * DK + sd(m, g));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)  // identity for the transition rows, zero otherwise
-            st[m][c][e] = (m_kind && r == 16 * m + 4 * g + e) ? 1.0f : 0.0f;
+            st[m][c][e] = (m_kind && r == sd(m, g) + e) ? 1.0f : 0.0f;
         }
       }
   }
@@ -380,10 +392,11 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
 
   // One chunk's tiles in registers (16-byte pieces of K, Q, V and TB per thread) and its
-  // gates (wave 0); with PREFETCH they are loaded one chunk ahead.
+  // gates (wave 0).  The parts in PF are loaded one chunk ahead, the rest at the start of
+  // the chunk.
   u32x4 pk[NLD], pq[NLD], pv[NLD], pt[NLT > 0 ? NLT : 1];
   float pal = 1.0f, pbe = 0.0f;
-#define LA_LOAD(T0, N)                                                                             \
+#define LA_LOAD(T0, N, MASK)                                                                       \
   do {                                                                                             \
     const int64_t lt0 = (T0);                                                                      \
     const uint32_t ln = (uint32_t)(N);                                                             \
@@ -393,26 +406,28 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     const rsrc_t rv = make_rsrc(a.v + rb * DV, ln * DV * 2);                                       \
     _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                              \
       const uint32_t off = 16u * (uint32_t)(tid + NT * i);                                         \
-      pk[i] = bld16(rk, off);                                                                      \
-      if (OUT) pq[i] = bld16(rq, off);                                                             \
-      pv[i] = bld16(rv, off);                                                                      \
+      if ((MASK) & LD_K) pk[i] = bld16(rk, off);                                                   \
+      if (OUT && ((MASK) & LD_Q)) pq[i] = bld16(rq, off);                                          \
+      if ((MASK) & LD_V) pv[i] = bld16(rv, off);                                                   \
     }                                                                                              \
-    if (DELTA) {                                                                                   \
+    if (DELTA && ((MASK) & LD_T)) {                                                                \
       const rsrc_t rt = make_rsrc(a.tb + (bh * a.nch + (size_t)(lt0 / C)) * T_CHUNK, T_CHUNK * 2); \
       _Pragma("unroll") for (int i = 0; i < NLT; ++i) pt[i] = bld16(rt, 16u * (uint32_t)(tid + NT * i)); \
     }                                                                                              \
-    pal = 1.0f;                                                                                    \
-    pbe = (uint32_t)lane < ln ? 1.0f : 0.0f;                                                       \
-    if (wave == 0) {                                                                               \
-      if (a.variant != V_ADDITIVE) {                                                               \
-        const float x = bf16_to_f32(bld2(make_rsrc(a.alpha + rb, ln * 2), 2u * lane));             \
-        pal = (uint32_t)lane < ln ? x : 1.0f;                                                      \
+    if ((MASK) & LD_G) {                                                                           \
+      pal = 1.0f;                                                                                  \
+      pbe = (uint32_t)lane < ln ? 1.0f : 0.0f;                                                     \
+      if (wave == 0) {                                                                             \
+        if (a.variant != V_ADDITIVE) {                                                             \
+          const float x = bf16_to_f32(bld2(make_rsrc(a.alpha + rb, ln * 2), 2u * lane));           \
+          pal = (uint32_t)lane < ln ? x : 1.0f;                                                    \
+        }                                                                                          \
+        if (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))                    \
+          pbe = bf16_to_f32(bld2(make_rsrc(a.beta + rb, ln * 2), 2u * lane));                      \
       }                                                                                            \
-      if (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))                      \
-        pbe = bf16_to_f32(bld2(make_rsrc(a.beta + rb, ln * 2), 2u * lane));                        \
     }                                                                                              \
   } while (0)
-  if (PREFETCH && nchunks > 0) LA_LOAD(first, (int)((T - first) < C ? (T - first) : C));
+  if (PF && nchunks > 0) LA_LOAD(first, (int)((T - first) < C ? (T - first) : C), PF);
 
   for (int ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = first + (int64_t)ci * C;
@@ -426,7 +441,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 
     // ---- phase A: move this chunk's tiles (loaded into registers during the previous
     // chunk when prefetching) to LDS, gate prefix sums
-    if (!PREFETCH) LA_LOAD(t0, n);
+    if (PF != LD_ALL) LA_LOAD(t0, n, LD_ALL & ~PF);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int id = tid + NT * i, r = id >> 4, cv = id & 15;
@@ -458,9 +473,9 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 
     // ---- phase B: everything that does not need the state of this chunk's start: Q K^T,
     // U~, W
-    if (PREFETCH && ci + 1 < nchunks) {
+    if (PF && ci + 1 < nchunks) {
       const int64_t nt0 = t0 + C;
-      LA_LOAD(nt0, (int)((T - nt0) < C ? (T - nt0) : C));
+      LA_LOAD(nt0, (int)((T - nt0) < C ? (T - nt0) : C), PF);
     }
     f32x4 Ut[4][2];
     if (OUT) {
@@ -560,7 +575,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 #pragma unroll
       for (int c = 0; c < 2; ++c) U[mt][c] = (DELTA && !m_kind) ? Ut[mt][c] : f32x4{0.f, 0.f, 0.f, 0.f};
     if (DELTA) {  // U = U~ - W S^T; W fragments read two steps ahead
-#define LA_WF(it) frag_pair(sW, LDK, 16 * ((it) % 4) + l16, 32 * ((it) / 4), g)
+#define LA_WF(it) *reinterpret_cast<const bf16x8 *>(sW + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
       bf16x8 wb[3], sfr[2];
       wb[0] = LA_WF(0);
       wb[1] = LA_WF(1);
@@ -612,7 +627,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int c = 0; c < 2; ++c) O[mt][c] = {0.f, 0.f, 0.f, 0.f};
-#define LA_QF(it) frag_pair(sQ, LDK, 16 * ((it) % 4) + l16, 32 * ((it) / 4), g)
+#define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
       {
         bf16x8 qb[3], sfr[2];
         qb[0] = LA_QF(0);
@@ -661,13 +676,13 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       const float gC = sGam[C - 1];
       gseg += sG[C - 1];
       bf16x8 kb[2][2];
-      kb[0][0] = col_frag(sK, LDK, 0, 0, lane_v);
-      kb[0][1] = col_frag(sK, LDK, 0, 1, lane_v);
+      kb[0][0] = kstate_frag(sK, LDK, 0, 0, lane_v);
+      kb[0][1] = kstate_frag(sK, LDK, 0, 1, lane_v);
 #pragma unroll
       for (int m = 0; m < DK / 16; ++m) {
         if (m + 1 < DK / 16) {
-          kb[(m + 1) & 1][0] = col_frag(sK, LDK, m + 1, 0, lane_v);
-          kb[(m + 1) & 1][1] = col_frag(sK, LDK, m + 1, 1, lane_v);
+          kb[(m + 1) & 1][0] = kstate_frag(sK, LDK, m + 1, 0, lane_v);
+          kb[(m + 1) & 1][1] = kstate_frag(sK, LDK, m + 1, 1, lane_v);
         }
         LA_FENCE();
 #pragma unroll
@@ -691,7 +706,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int r = row0 + 16 * c + l16;
-          *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + 16 * m + 4 * g) = st[m][c];
+          *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + sd(m, g)) = st[m][c];
         }
     }
   } else {
@@ -702,7 +717,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int r = rbase + row0 + 16 * c + l16;
-        *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + 16 * m + 4 * g) = st[m][c];
+        *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + sd(m, g)) = st[m][c];
       }
     if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
   }
