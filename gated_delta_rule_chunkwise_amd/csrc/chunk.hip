@@ -157,15 +157,20 @@ __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
 // column c) is directly a B operand, and the A operand L_ik[c][4 g + s] is the
 // accumulator tile of the Gram block (k, i): K K^T is symmetric.
 // ---------------------------------------------------------------------------------------
-constexpr int LDD = 20;  // fp32 16 x 16 diagonal blocks in pass 0
+constexpr int LDD = 20;               // row stride of the fp32 16 x 16 diagonal blocks in pass 0
+constexpr int SZD = 16 * LDD + 16;    // block stride: the four blocks start 16 banks apart, so
+                                      // the four lane groups of a wave (one block each) never
+                                      // collide on a bank
 struct TPrepLds {
   float g[C], beta[C];
-  float d[4][16 * LDD];
+  float d[4][SZD];
 };
 
 __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) TPrepLds sm[NW];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform across the wave: saying so keeps every per-chunk address
+  // and buffer descriptor in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, grp = lane >> 4;
   const int64_t cid = (int64_t)blockIdx.x * NW + wave;
   if (cid >= (int64_t)a.B * a.H * a.nch) return;
@@ -354,7 +359,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   float *sGam = sG + 2 * C;
   float *sDec = sG + 3 * C;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
   // in the delta-rule map pass, waves 4-7 carry the transition (M) rows
   const bool m_kind = (MODE == MODE_MAP) && DELTA && wave >= NW;
