@@ -44,9 +44,9 @@ constexpr int NW = 4;
 constexpr int NTHR = NW * 64;
 
 constexpr int LDQ = DP + 8;  // bf16 [C][DP] row-major q, k tiles (48-byte rows)
-constexpr int LDV = DV + 8;  // bf16 [C][DV] row-major v tile, o staging
-constexpr int LDKT = C + 8;  // bf16 [DP][C] k transposed
-constexpr int LDA = C + 8;   // bf16 [C][C] kernel matrix
+constexpr int LDV = DV + 8;  // bf16 [C][DV] row-major v tile
+constexpr int LDKS = C + 4;  // fp32 [DP][C] k transposed, scaled by 1/sqrt 2
+constexpr int LDA = C + 8;   // bf16 [C][C] kernel matrix (transposed)
 
 enum { MODE_MAP = 0, MODE_OUT = 1 };
 
@@ -93,12 +93,7 @@ __device__ __forceinline__ bf16x8 col_frag(const bf16_t *tile, int ld, int nt, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__device__ __forceinline__ bf16x8 frag_pair(const bf16_t *base, int ld, int row, int col0, int g) {
-  const uint2 lo = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 4 * g);
-  const uint2 hi = *reinterpret_cast<const uint2 *>(base + row * ld + col0 + 16 + 4 * g);
-  const u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-  return __builtin_bit_cast(bf16x8, w);
-}
+__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
   ti = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
@@ -110,16 +105,14 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
   constexpr bool OUT = MODE == MODE_OUT;
   __shared__ __attribute__((aligned(16))) bf16_t sQ[C * LDQ];
   __shared__ __attribute__((aligned(16))) bf16_t sK[C * LDQ];
-  __shared__ __attribute__((aligned(16))) bf16_t sKt[DP * LDKT];
+  __shared__ __attribute__((aligned(16))) float sKs[DP * LDKS];
   __shared__ __attribute__((aligned(16))) bf16_t sV[C * LDV];
-  __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];
-  __shared__ __attribute__((aligned(16))) bf16_t sO[C * LDV];
-  __shared__ __attribute__((aligned(16))) float sZ[NF];     // z, internal order
-  __shared__ __attribute__((aligned(16))) float sZinc[NF];  // this chunk's Phi_K^T 1
+  __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];  // kernel matrix, transposed
+  __shared__ __attribute__((aligned(16))) float sZ[NF];        // z, internal order
+  __shared__ __attribute__((aligned(16))) float sZinc[NF];     // this chunk's Phi_K^T 1
   __shared__ __attribute__((aligned(16))) float sDen[C];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int seg = blockIdx.x;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
@@ -129,6 +122,7 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
   // ---- state: lane holds s[feature 16 m + 4 g + e][16 n_col + l16] in st[m][e]
   f32x4 st[NFT];
   {
+    const int l16 = lane & 15, g = lane >> 4;
     const float *src_i = (OUT && a.nseg > 1) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
     const float *src_a = (OUT && a.nseg == 1 && a.s0) ? a.s0 + bh * (size_t)D * DV : nullptr;
 #pragma unroll
@@ -155,83 +149,89 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
     }
   }
 
-  int64_t prev_t0 = -1;
-  int prev_n = 0;
   const int64_t first = (int64_t)seg * a.seg_chunks * C;
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
+
+  // one chunk's q, k, v in registers (loaded while the previous chunk is processed):
+  // two 16-byte pieces of v per thread, one of k (threads 0-127) or q (threads 128-255)
+  u32x4 pv[2], pkq;
+#define LA_BLOAD(T0)                                                                               \
+  do {                                                                                             \
+    const int64_t lt0 = (T0);                                                                      \
+    const uint32_t ln = (uint32_t)((T - lt0) < C ? (T - lt0) : C);                                 \
+    const size_t rb = bh * (size_t)T + lt0;                                                        \
+    const rsrc_t rv = make_rsrc(a.v + rb * DV, ln * DV * 2);                                       \
+    pv[0] = bld16(rv, 16u * (uint32_t)tid);                                                        \
+    pv[1] = bld16(rv, 16u * (uint32_t)(tid + NTHR));                                               \
+    if (tid < 2 * C) pkq = bld16(make_rsrc(a.k + rb * DP, ln * DP * 2), 16u * (uint32_t)tid);      \
+    else if (OUT) pkq = bld16(make_rsrc(a.q + rb * DP, ln * DP * 2), 16u * (uint32_t)(tid - 2 * C)); \
+  } while (0)
+  if (nchunks > 0) LA_BLOAD(first);
+
   for (int ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = first + (int64_t)ci * C;
     const int n = (int)((T - t0) < C ? (T - t0) : C);
-    const size_t rb = bh * (size_t)T + t0;
     int lane_v = lane;  // opaque: keeps per-fragment LDS addresses inside the loop
     asm volatile("" : "+v"(lane_v));
+    const int l16 = lane_v & 15, g = lane_v >> 4;
 
-    // ---- phase A: write out the previous chunk's o; load q, k, v (+ k transposed)
-    if (OUT && prev_t0 >= 0) {
-      for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
-        const int r = id / (DV / 8), cv = id % (DV / 8);
-        *reinterpret_cast<u32x4 *>(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8) =
-            *reinterpret_cast<const u32x4 *>(sO + r * LDV + cv * 8);
-      }
+    // ---- phase A: this chunk's q, k, v (+ k transposed) to LDS
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + NTHR * i, r = id >> 3, cv = id & 7;
+      *reinterpret_cast<u32x4 *>(sV + r * LDV + cv * 8) = pv[i];
     }
-    for (int id = tid; id < C * (DV / 8); id += NTHR) {  // v: 512 vectors of 8
-      const int r = id >> 3, cv = id & 7;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(sV + r * LDV + cv * 8) =
-          r < n ? *reinterpret_cast<const u32x4 *>(a.v + (rb + r) * DV + cv * 8) : z;
-    }
-    if (tid < 2 * C) {  // k rows (two vectors each), plus the transposed copy
+    if (tid < 2 * C) {
       const int r = tid >> 1, cv = tid & 1;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const u32x4 kv = r < n ? *reinterpret_cast<const u32x4 *>(a.k + (rb + r) * DP + cv * 8) : z;
-      *reinterpret_cast<u32x4 *>(sK + r * LDQ + cv * 8) = kv;
+      *reinterpret_cast<u32x4 *>(sK + r * LDQ + cv * 8) = pkq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = kv[e >> 1];
-        sKt[(cv * 8 + e) * LDKT + r] = (bf16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+        const uint32_t w = pkq[e >> 1];
+        sKs[(cv * 8 + e) * LDKS + r] = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)) * rs2;
       }
     } else if (OUT) {
       const int id = tid - 2 * C, r = id >> 1, cv = id & 1;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(sQ + r * LDQ + cv * 8) =
-          r < n ? *reinterpret_cast<const u32x4 *>(a.q + (rb + r) * DP + cv * 8) : z;
+      *reinterpret_cast<u32x4 *>(sQ + r * LDQ + cv * 8) = pkq;
     }
     __syncthreads();
+    if (ci + 1 < nchunks) LA_BLOAD(t0 + C);
 
-    // ---- phase B: kernel matrix A = 1 + QK^T + (QK^T)^2/2, causal (bf16 in LDS)
+    // ---- phase B: kernel matrix A = 1 + QK^T + (QK^T)^2/2, causal, stored transposed
+    // (row j, column t) in bf16; tiles dealt round robin (a wave without a third tile
+    // recomputes tile 9 and does not store it)
     if (OUT) {
-      for (int job = wave; job < 10; job += NW) {
+#pragma unroll
+      for (int mm = 0; mm < 3; ++mm) {
+        const int job = wave + NW * mm;
         int ti, tj;
-        tri_index(job, ti, tj);
+        tri_index(job < 10 ? job : 9, ti, tj);
         bf16x8 fa, fb;  // q.k over d' = 16: the upper half of the 32-wide k-step is zero
-        if (g < 2) {
-          fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDQ + 8 * g);
-          fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDQ + 8 * g);
-        } else {
-          fa = pack8(0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f);
-          fb = fa;
-        }
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        fa = __builtin_bit_cast(bf16x8, g < 2 ? *reinterpret_cast<const u32x4 *>(sQ + (16 * ti + l16) * LDQ + 8 * (g & 1)) : z4);
+        fb = __builtin_bit_cast(bf16x8, g < 2 ? *reinterpret_cast<const u32x4 *>(sK + (16 * tj + l16) * LDQ + 8 * (g & 1)) : z4);
         const f32x4 acc = mfma_bf16(fa, fb, f32x4{0.f, 0.f, 0.f, 0.f});
         const int j = 16 * tj + l16;
+        f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = 16 * ti + 4 * g + e;
           const float x = acc[e];
-          sA[t * LDA + j] = f32_to_bf16(t >= j ? 1.0f + x + 0.5f * x * x : 0.0f);
+          v[e] = (16 * ti + 4 * g + e >= j) ? 1.0f + x + 0.5f * x * x : 0.0f;
         }
+        if (job < 10)
+          *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
       }
-      for (int id = tid; id < 512; id += NTHR) {  // above-diagonal tiles (0,1), (2,3)
-        const int tile = id >> 8, e = id & 255;
-        sA[(32 * tile + (e >> 4)) * LDA + 32 * tile + 16 + (e & 15)] = 0;
+      if (tid < 128) {  // the above-diagonal tiles read by the A V products: A (0,1), (2,3)
+        const int tile = tid >> 6, e = tid & 63;
+        *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
       }
       __syncthreads();
     }
 
-    // ---- phase C: numerator and denominator (old state), then the carry
-    f32x4 num[4];
+    // ---- phase C: numerator and denominator on the entering state (transposed, so a
+    // lane holds four consecutive outputs of one token), then the carry
     const bf16x8 vf0 = col_frag(sV, LDV, n_col, 0, lane_v), vf1 = col_frag(sV, LDV, n_col, 1, lane_v);
-    // one-column operand (column 0): valid-token indicator, for A 1 and Phi_K^T 1
+    // one-row operand (row 0): valid-token indicator, for A 1 and Phi_K^T 1
     bf16x8 ones[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -243,65 +243,100 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       }
       ones[s2] = pack_pair(a0, a1);
     }
+    f32x4 num[4];
     if (OUT) {
+      // num^T[c][t] = sum_f s[f][c] phi_f(q_t) + sum_j v_j[c] A[t][j]: the state is the A
+      // operand (rows = value columns, k = features), phi(q_t) of this lane's token t the B
+      // operand, built in registers from q_t; the transposed product leaves four
+      // consecutive outputs of one token in each lane.
+      bf16x8 sfr[NFT / 2];
+#pragma unroll
+      for (int s = 0; s < NFT / 2; ++s) sfr[s] = pack_pair(st[2 * s], st[2 * s + 1]);
+#define LA_PHIQ(s, fb)                                                                             \
+  do {                                                                                             \
+    f32x4 b0, b1; /* phi(q_t) at features 32 s + 4 g + e and 32 s + 16 + 4 g + e */                \
+    if ((s) < 8) {                                                                                 \
+      b0 = qg * qs[2 * (s)];                                                                       \
+      b1 = qg * qs[2 * (s) + 1];                                                                   \
+    } else {                                                                                       \
+      b0 = qg;                                                                                     \
+      _Pragma("unroll") for (int e = 0; e < 4; ++e) b1[e] = (4 * g + e == 0) ? 1.0f : 0.0f;        \
+    }                                                                                              \
+    fb = pack_pair(b0, b1);                                                                        \
+  } while (0)
+#define LA_QROW(t)                                                                                 \
+  const u32x4 qa = *reinterpret_cast<const u32x4 *>(sQ + (t) * LDQ);                              \
+  const u32x4 qb = *reinterpret_cast<const u32x4 *>(sQ + (t) * LDQ + 8);                           \
+  float qs[16]; /* q_t[a] / sqrt 2 */                                                              \
+  {                                                                                                \
+    const uint32_t w[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};                \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                \
+      qs[2 * i] = __uint_as_float(w[i] << 16) * rs2;                                               \
+      qs[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * rs2;                                   \
+    }                                                                                              \
+  }                                                                                                \
+  const f32x4 qg = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sQ + (t) * LDQ + 4 * g))
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         __builtin_amdgcn_sched_barrier(0);
-        // q of token 16 mt + l16: all 16 values and this lane group's 4
-        const int t = 16 * mt + l16;
-        const u32x4 qa = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ);
-        const u32x4 qb = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ + 8);
-        float qv[16];
-        {
-          const uint32_t w[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            qv[2 * i] = __uint_as_float(w[i] << 16);
-            qv[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-          }
-        }
-        const f32x4 qg = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sQ + t * LDQ + 4 * g));
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, dacc = {0.f, 0.f, 0.f, 0.f};
-        const bool den_tile = mt == wave;  // this wave also forms den for token tile mt
+        LA_QROW(16 * mt + l16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NFT / 2; ++s) {
-          f32x4 a0, a1;  // Phi_Q entries of feature tiles 2 s and 2 s + 1
-          if (s < 8) {
-            a0 = qg * (qv[2 * s] * rs2);
-            a1 = qg * (qv[2 * s + 1] * rs2);
-          } else {
-            a0 = qg;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a1[e] = (4 * g + e == 0) ? 1.0f : 0.0f;
-          }
-          const bf16x8 fa = pack_pair(a0, a1);
-          acc = mfma_bf16(fa, pack_pair(st[2 * s], st[2 * s + 1]), acc);
-          if (den_tile) {
-            f32x4 z0, z1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              z0[e] = l16 == 0 ? sZ[32 * s + 4 * g + e] : 0.0f;
-              z1[e] = l16 == 0 ? sZ[32 * s + 16 + 4 * g + e] : 0.0f;
-            }
-            dacc = mfma_bf16(fa, pack_pair(z0, z1), dacc);
-          }
+          bf16x8 fb;
+          LA_PHIQ(s, fb);
+          acc = mfma_bf16(sfr[s], fb, acc);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (s2 == 1 && mt < 2) continue;  // A is causal
-          const bf16x8 af = frag_pair(sA, LDA, 16 * mt + l16, 32 * s2, g);
-          acc = mfma_bf16(af, s2 == 0 ? vf0 : vf1, acc);
-          if (den_tile) dacc = mfma_bf16(af, ones[s2], dacc);
+          acc = mfma_bf16(s2 == 0 ? vf0 : vf1, col_frag(sA, LDA, mt, s2, lane_v), acc);
         }
         num[mt] = acc;
-        if (den_tile && l16 == 0) {
+      }
+      {  // den for token tile mt = wave: the same products with z (one row) in place of s,
+         // and the row sums of A through the valid-token row
+        __builtin_amdgcn_sched_barrier(0);
+        const int mt = wave;
+        LA_QROW(16 * mt + l16);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sDen[16 * mt + 4 * g + e] = dacc[e];
+        for (int s = 0; s < NFT / 2; ++s) {
+          bf16x8 fb;
+          LA_PHIQ(s, fb);
+          const f32x4 z0 = l16 == 0 ? ld4f(sZ + 32 * s + 4 * g) : zero;
+          const f32x4 z1 = l16 == 0 ? ld4f(sZ + 32 * s + 16 + 4 * g) : zero;
+          dacc = mfma_bf16(pack_pair(z0, z1), fb, dacc);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (s2 == 1 && mt < 2) continue;
+          dacc = mfma_bf16(ones[s2], col_frag(sA, LDA, mt, s2, lane_v), dacc);
+        }
+        if (g == 0) sDen[16 * mt + l16] = dacc[0];
+      }
+#undef LA_QROW
+#undef LA_PHIQ
+    }
+    {
+      // carry.  Order-2 tile a (features x_a x_b / sqrt 2, b = 0..15): s += K^T diag(k_a / sqrt 2) V,
+      // i.e. the A operand is K^T itself (rows b, k = tokens, the same for every a) and the
+      // per-token factor k_t[a] / sqrt 2 scales the V operand.  Tile 16 (x_b): K^T V.  Tile 17
+      // (the constant): 1^T V.  z gets the same products with a ones column in place of V,
+      // on the waves whose turn it is (tile m = wave mod 4).
+      const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
+      f32x4 vlo[2], vhi[2];  // this lane's V column at its 8 tokens, fp32
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 vf = s2 == 0 ? vf0 : vf1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vlo[s2][e] = (float)vf[e];
+          vhi[s2][e] = (float)vf[4 + e];
         }
       }
-    }
-    {  // carry: s += Phi_K^T V, and Phi_K^T 1 for the feature tiles m = wave (mod 4)
-      const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
+      const f32x4 vmask0 = {(float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0)};
 #pragma unroll
       for (int m = 0; m < NFT; ++m) {
         if ((m & 1) == 0) __builtin_amdgcn_sched_barrier(0);
@@ -310,65 +345,43 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         const bool zt = (m % NW) == wave;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          bf16x8 fa;  // Phi_K^T rows of feature tile m at this lane's 8 tokens
           if (m < DP) {
-            const f32x4 k0 = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sKt + m * LDKT + 32 * s2 + 4 * g));
-            const f32x4 k1 = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sKt + m * LDKT + 32 * s2 + 16 + 4 * g));
-            f32x4 j0, j1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              j0[e] = (float)kj[s2][e];
-              j1[e] = (float)kj[s2][4 + e];
-            }
-            fa = pack_pair(k0 * j0 * rs2, k1 * j1 * rs2);
+            const f32x4 k0 = ld4f(sKs + m * LDKS + 32 * s2 + 4 * g), k1 = ld4f(sKs + m * LDKS + 32 * s2 + 16 + 4 * g);
+            acc = mfma_bf16(kj[s2], pack_pair(vlo[s2] * k0, vhi[s2] * k1), acc);
+            if (zt) zacc = mfma_bf16(kj[s2], pack_pair(vmask0 * k0, vmask0 * k1), zacc);
           } else if (m == DP) {
-            fa = kj[s2];
+            acc = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, acc);
+            if (zt) zacc = mfma_bf16(kj[s2], ones[s2], zacc);
           } else {
-            f32x4 c0, c1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              c0[e] = (l16 == 0 && 32 * s2 + 4 * g + e < n) ? 1.0f : 0.0f;
-              c1[e] = (l16 == 0 && 32 * s2 + 16 + 4 * g + e < n) ? 1.0f : 0.0f;
-            }
-            fa = pack_pair(c0, c1);
+            acc = mfma_bf16(ones[s2], s2 == 0 ? vf0 : vf1, acc);
+            if (zt) zacc = mfma_bf16(ones[s2], ones[s2], zacc);
           }
-          acc = mfma_bf16(fa, s2 == 0 ? vf0 : vf1, acc);
-          if (zt) zacc = mfma_bf16(fa, ones[s2], zacc);
         }
         st[m] = acc;
-        if (zt && l16 == 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sZinc[16 * m + 4 * g + e] = zacc[e];
-        }
+        if (zt && l16 == 0) *reinterpret_cast<f32x4 *>(sZinc + 16 * m + 4 * g) = zacc;
       }
     }
     __syncthreads();
 
-    // ---- phase D: normalise into the o staging tile; z += this chunk's Phi_K^T 1
+    // ---- phase D: o = num / (den + eps) straight to HBM; z += this chunk's Phi_K^T 1
     if (OUT) {
+      const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * mt + 4 * g + e;
-          sO[t * LDV + 16 * n_col + l16] = f32_to_bf16(num[mt][e] / (sDen[t] + a.eps));
-        }
+      for (int mt = 0; mt < 4; ++mt) {
+        const float r = 1.0f / (sDen[16 * mt + l16] + a.eps);
+        const f32x4 x = num[mt] * r;
+        const bf16x4 h = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+        bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + 16 * n_col + 4 * g), __builtin_bit_cast(u32x2, h));
+      }
     }
     for (int fi = tid; fi < NF; fi += NTHR) sZ[fi] += sZinc[fi];
-    __syncthreads();
-    prev_t0 = t0;
-    prev_n = n;
   }
+#undef LA_BLOAD
 
   if (OUT) {
-    if (prev_t0 >= 0) {
-      for (int id = tid; id < prev_n * (DV / 8); id += NTHR) {
-        const int r = id / (DV / 8), cv = id % (DV / 8);
-        *reinterpret_cast<u32x4 *>(a.o + (bh * (size_t)T + prev_t0 + r) * DV + cv * 8) =
-            *reinterpret_cast<const u32x4 *>(sO + r * LDV + cv * 8);
-      }
-    }
     if (a.nseg == 1 && a.s_T) {
+      __syncthreads();
+      const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
       for (int m = 0; m < NFT; ++m)
 #pragma unroll
@@ -382,6 +395,8 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       }
     }
   } else {
+    __syncthreads();
+    const int l16 = lane & 15, g = lane >> 4;
     float *dst = a.dsum + (bh * a.nseg + seg) * (size_t)NF * (DV + 1);
 #pragma unroll
     for (int m = 0; m < NFT; ++m)
