@@ -111,6 +111,12 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) float sZ[NF];        // z, internal order
   __shared__ __attribute__((aligned(16))) float sZinc[NF];     // this chunk's Phi_K^T 1
   __shared__ __attribute__((aligned(16))) float sDen[C];
+  // phi(q) as MFMA B-operand fragments, [token tile][feature step][lane] (16 bytes each):
+  // each wave builds its token tile's once per chunk, every wave reads all four
+  __shared__ __attribute__((aligned(16))) bf16x8 sPhi[MODE == MODE_OUT ? 4 * (NFT / 2) * 64 : 1];
+  // MODE_MAP: phi(k)^T of the 16 order-2 feature tiles as MFMA A-operand fragments,
+  // [tile][token step][lane], built once per chunk (four tiles per wave)
+  __shared__ __attribute__((aligned(16))) bf16x8 sPhiK[MODE == MODE_MAP ? DP * 2 * 64 : 1];
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int seg = blockIdx.x;
@@ -225,6 +231,35 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         const int tile = tid >> 6, e = tid & 63;
         *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
       }
+      {  // phi(q_t) for this wave's token tile mt = wave, t = 16 mt + l16: the B operand of
+         // feature step s holds features 32 s + 4 g + e and 32 s + 16 + 4 g + e
+        const int t = 16 * wave + l16;
+        const u32x4 qa = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ);
+        const u32x4 qb = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ + 8);
+        float qs[16];  // q_t[a] / sqrt 2
+        {
+          const uint32_t w[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            qs[2 * i] = __uint_as_float(w[i] << 16) * rs2;
+            qs[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * rs2;
+          }
+        }
+        const f32x4 qg = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sQ + t * LDQ + 4 * g));
+#pragma unroll
+        for (int s = 0; s < NFT / 2; ++s) {
+          f32x4 b0, b1;
+          if (s < 8) {
+            b0 = qg * qs[2 * s];
+            b1 = qg * qs[2 * s + 1];
+          } else {
+            b0 = qg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b1[e] = (4 * g + e == 0) ? 1.0f : 0.0f;
+          }
+          sPhi[(wave * (NFT / 2) + s) * 64 + lane] = pack_pair(b0, b1);
+        }
+      }
       __syncthreads();
     }
 
@@ -246,47 +281,17 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
     f32x4 num[4];
     if (OUT) {
       // num^T[c][t] = sum_f s[f][c] phi_f(q_t) + sum_j v_j[c] A[t][j]: the state is the A
-      // operand (rows = value columns, k = features), phi(q_t) of this lane's token t the B
-      // operand, built in registers from q_t; the transposed product leaves four
-      // consecutive outputs of one token in each lane.
+      // operand (rows = value columns, k = features), phi(q_t) (from LDS) the B operand;
+      // the transposed product leaves four consecutive outputs of one token in each lane.
       bf16x8 sfr[NFT / 2];
 #pragma unroll
       for (int s = 0; s < NFT / 2; ++s) sfr[s] = pack_pair(st[2 * s], st[2 * s + 1]);
-#define LA_PHIQ(s, fb)                                                                             \
-  do {                                                                                             \
-    f32x4 b0, b1; /* phi(q_t) at features 32 s + 4 g + e and 32 s + 16 + 4 g + e */                \
-    if ((s) < 8) {                                                                                 \
-      b0 = qg * qs[2 * (s)];                                                                       \
-      b1 = qg * qs[2 * (s) + 1];                                                                   \
-    } else {                                                                                       \
-      b0 = qg;                                                                                     \
-      _Pragma("unroll") for (int e = 0; e < 4; ++e) b1[e] = (4 * g + e == 0) ? 1.0f : 0.0f;        \
-    }                                                                                              \
-    fb = pack_pair(b0, b1);                                                                        \
-  } while (0)
-#define LA_QROW(t)                                                                                 \
-  const u32x4 qa = *reinterpret_cast<const u32x4 *>(sQ + (t) * LDQ);                              \
-  const u32x4 qb = *reinterpret_cast<const u32x4 *>(sQ + (t) * LDQ + 8);                           \
-  float qs[16]; /* q_t[a] / sqrt 2 */                                                              \
-  {                                                                                                \
-    const uint32_t w[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};                \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                \
-      qs[2 * i] = __uint_as_float(w[i] << 16) * rs2;                                               \
-      qs[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * rs2;                                   \
-    }                                                                                              \
-  }                                                                                                \
-  const f32x4 qg = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sQ + (t) * LDQ + 4 * g))
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         __builtin_amdgcn_sched_barrier(0);
-        LA_QROW(16 * mt + l16);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NFT / 2; ++s) {
-          bf16x8 fb;
-          LA_PHIQ(s, fb);
-          acc = mfma_bf16(sfr[s], fb, acc);
-        }
+        for (int s = 0; s < NFT / 2; ++s) acc = mfma_bf16(sfr[s], sPhi[(mt * (NFT / 2) + s) * 64 + lane_v], acc);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (s2 == 1 && mt < 2) continue;  // A is causal
@@ -298,16 +303,13 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
          // and the row sums of A through the valid-token row
         __builtin_amdgcn_sched_barrier(0);
         const int mt = wave;
-        LA_QROW(16 * mt + l16);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NFT / 2; ++s) {
-          bf16x8 fb;
-          LA_PHIQ(s, fb);
           const f32x4 z0 = l16 == 0 ? ld4f(sZ + 32 * s + 4 * g) : zero;
           const f32x4 z1 = l16 == 0 ? ld4f(sZ + 32 * s + 16 + 4 * g) : zero;
-          dacc = mfma_bf16(pack_pair(z0, z1), fb, dacc);
+          dacc = mfma_bf16(pack_pair(z0, z1), sPhi[(mt * (NFT / 2) + s) * 64 + lane_v], dacc);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -316,17 +318,36 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         }
         if (g == 0) sDen[16 * mt + l16] = dacc[0];
       }
-#undef LA_QROW
-#undef LA_PHIQ
+    }
+    if (!OUT) {
+      // MODE_MAP: phi(k)^T fragments of order-2 tile a (rows b: k_t[a] k_t[b] / sqrt 2 at this
+      // lane's 8 tokens), tiles a = wave, wave + 4, ..., then shared through LDS
+      const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        f32x4 klo, khi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          klo[e] = (float)kj[s2][e];
+          khi[e] = (float)kj[s2][4 + e];
+        }
+#pragma unroll
+        for (int i = 0; i < DP / NW; ++i) {
+          const int ta = wave + NW * i;
+          const f32x4 k0 = ld4f(sKs + ta * LDKS + 32 * s2 + 4 * g), k1 = ld4f(sKs + ta * LDKS + 32 * s2 + 16 + 4 * g);
+          sPhiK[(ta * 2 + s2) * 64 + lane] = pack_pair(klo * k0, khi * k1);
+        }
+      }
+      __syncthreads();
     }
     {
-      // carry.  Order-2 tile a (features x_a x_b / sqrt 2, b = 0..15): s += K^T diag(k_a / sqrt 2) V,
-      // i.e. the A operand is K^T itself (rows b, k = tokens, the same for every a) and the
-      // per-token factor k_t[a] / sqrt 2 scales the V operand.  Tile 16 (x_b): K^T V.  Tile 17
-      // (the constant): 1^T V.  z gets the same products with a ones column in place of V,
-      // on the waves whose turn it is (tile m = wave mod 4).
+      // carry.  Order-2 tile a (features x_a x_b / sqrt 2, b = 0..15): s += phi(K)_a^T V with
+      // phi(K)_a^T = K^T diag(k_a / sqrt 2) -- shared fragments from LDS in MODE_MAP; in
+      // MODE_OUT (no room for them) the factor scales this wave's V operand instead.  Tile
+      // 16 (x_b): K^T V.  Tile 17 (the constant): 1^T V.  Straight-line, the operands of
+      // the next tile read one step ahead; z's increment phi(K)^T 1 separately below.
       const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
-      f32x4 vlo[2], vhi[2];  // this lane's V column at its 8 tokens, fp32
+      f32x4 vlo[2], vhi[2];  // this lane's V column at its 8 tokens, fp32 (MODE_OUT)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const bf16x8 vf = s2 == 0 ? vf0 : vf1;
@@ -336,29 +357,54 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
           vhi[s2][e] = (float)vf[4 + e];
         }
       }
-      const f32x4 vmask0 = {(float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0)};
+      // per order-2 tile: MODE_MAP the two phi(K)^T fragments, MODE_OUT the four k_a vectors
+      bf16x8 pkb[2][2];
+      f32x4 kab[2][4];
+#define LA_CARRY_LOAD(m, slot)                                                                     \
+  do {                                                                                             \
+    if (!OUT) {                                                                                    \
+      pkb[slot][0] = sPhiK[((m) * 2 + 0) * 64 + lane_v];                                           \
+      pkb[slot][1] = sPhiK[((m) * 2 + 1) * 64 + lane_v];                                           \
+    } else {                                                                                       \
+      _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                                           \
+        kab[slot][2 * s2] = ld4f(sKs + (m) * LDKS + 32 * s2 + 4 * g);                              \
+        kab[slot][2 * s2 + 1] = ld4f(sKs + (m) * LDKS + 32 * s2 + 16 + 4 * g);                     \
+      }                                                                                            \
+    }                                                                                              \
+  } while (0)
+      LA_CARRY_LOAD(0, 0);
 #pragma unroll
-      for (int m = 0; m < NFT; ++m) {
-        if ((m & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < DP; ++m) {
+        if (m + 1 < DP) LA_CARRY_LOAD(m + 1, (m + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 acc = st[m];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (!OUT) acc = mfma_bf16(pkb[m & 1][s2], s2 == 0 ? vf0 : vf1, acc);
+          else acc = mfma_bf16(kj[s2], pack_pair(vlo[s2] * kab[m & 1][2 * s2], vhi[s2] * kab[m & 1][2 * s2 + 1]), acc);
+        }
+        st[m] = acc;
+      }
+#undef LA_CARRY_LOAD
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        st[DP] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[DP]);
+        st[DP + 1] = mfma_bf16(ones[s2], s2 == 0 ? vf0 : vf1, st[DP + 1]);
+      }
+      // z increment phi(K)^T 1 for this wave's tiles m = wave + 4 i
+      const f32x4 vmask0 = {(float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0)};
+      for (int m = wave; m < NFT; m += NW) {
         f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
-        const bool zt = (m % NW) == wave;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (m < DP) {
             const f32x4 k0 = ld4f(sKs + m * LDKS + 32 * s2 + 4 * g), k1 = ld4f(sKs + m * LDKS + 32 * s2 + 16 + 4 * g);
-            acc = mfma_bf16(kj[s2], pack_pair(vlo[s2] * k0, vhi[s2] * k1), acc);
-            if (zt) zacc = mfma_bf16(kj[s2], pack_pair(vmask0 * k0, vmask0 * k1), zacc);
-          } else if (m == DP) {
-            acc = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, acc);
-            if (zt) zacc = mfma_bf16(kj[s2], ones[s2], zacc);
+            zacc = mfma_bf16(kj[s2], pack_pair(vmask0 * k0, vmask0 * k1), zacc);
           } else {
-            acc = mfma_bf16(ones[s2], s2 == 0 ? vf0 : vf1, acc);
-            if (zt) zacc = mfma_bf16(ones[s2], ones[s2], zacc);
+            zacc = mfma_bf16(m == DP ? kj[s2] : ones[s2], ones[s2], zacc);
           }
         }
-        st[m] = acc;
-        if (zt && l16 == 0) *reinterpret_cast<f32x4 *>(sZinc + 16 * m + 4 * g) = zacc;
+        if (l16 == 0) *reinterpret_cast<f32x4 *>(sZinc + 16 * m + 4 * g) = zacc;
       }
     }
     __syncthreads();
@@ -411,6 +457,7 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
 __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   constexpr int NE = NF * (DV + 1);
+  constexpr int UNR = 8;  // segments whose sums are loaded together
   for (int id = blockIdx.x * 256 + threadIdx.x; id < NE; id += gridDim.x * 256) {
     const int fi = id / (DV + 1), col = id % (DV + 1);
     const int af = abi_feature(fi);
@@ -419,9 +466,16 @@ __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
       if (col < DV && a.s0) x = a.s0[(bh * D + af) * DV + col];
       if (col == DV && a.z0) x = a.z0[bh * D + af];
     }
-    for (int i = 0; i < a.nseg; ++i) {
-      a.starts[(bh * a.nseg + i) * (size_t)NE + id] = x;
-      x += a.dsum[(bh * a.nseg + i) * (size_t)NE + id];
+    for (int i0 = 0; i0 < a.nseg; i0 += UNR) {
+      float d[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        d[u] = i0 + u < a.nseg ? a.dsum[(bh * a.nseg + i0 + u) * (size_t)NE + id] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (i0 + u < a.nseg) a.starts[(bh * a.nseg + i0 + u) * (size_t)NE + id] = x;
+        x += d[u];
+      }
     }
     if (a.s_T && af >= 0) {
       if (col < DV) a.s_T[(bh * D + af) * DV + col] = x;
