@@ -93,6 +93,12 @@ __device__ __forceinline__ bf16x8 col_frag(const bf16_t *tile, int ld, int nt, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// feature fi (internal order) of z at its place in the denominator's A-operand fragments:
+// step s = fi / 32, lane 16 g (row 0) with g = (fi % 16) / 4, element 4 ((fi / 16) % 2) + fi % 4
+__device__ __forceinline__ int zf_index(int fi) {
+  return ((fi >> 5) * 64 + 16 * ((fi & 15) >> 2)) * 8 + 4 * ((fi >> 4) & 1) + (fi & 3);
+}
+
 __device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
@@ -111,6 +117,9 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) float sZ[NF];        // z, internal order
   __shared__ __attribute__((aligned(16))) float sZinc[NF];     // this chunk's Phi_K^T 1
   __shared__ __attribute__((aligned(16))) float sDen[C];
+  // MODE_OUT: z as the A operand of the denominator product (row 0 = z, other rows zero),
+  // [feature step][lane]; kept in step with sZ
+  __shared__ __attribute__((aligned(16))) bf16x8 sZf[MODE == MODE_OUT ? (NFT / 2) * 64 : 1];
   // phi(q) as MFMA B-operand fragments, [token tile][feature step][lane] (16 bytes each):
   // each wave builds its token tile's once per chunk, every wave reads all four
   __shared__ __attribute__((aligned(16))) bf16x8 sPhi[MODE == MODE_OUT ? 4 * (NFT / 2) * 64 : 1];
@@ -152,6 +161,12 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         x = af >= 0 ? a.z0[bh * D + af] : 0.0f;
       }
       sZ[fi] = x;
+    }
+    if (OUT) {
+      bf16_t *zf = reinterpret_cast<bf16_t *>(sZf);
+      for (int i = tid; i < (NFT / 2) * 64 * 8; i += NTHR) zf[i] = 0;
+      __syncthreads();
+      for (int fi = tid; fi < NF; fi += NTHR) zf[zf_index(fi)] = f32_to_bf16(sZ[fi]);
     }
   }
 
@@ -286,31 +301,37 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       bf16x8 sfr[NFT / 2];
 #pragma unroll
       for (int s = 0; s < NFT / 2; ++s) sfr[s] = pack_pair(st[2 * s], st[2 * s + 1]);
+      // feature steps outer, token tiles inner (four independent accumulators, and den for
+      // token tile mt = wave as a fifth: z as one operand row), the phi(q) fragments of the
+      // next step read one step ahead
+      bf16x8 ph[2][4];
+      f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NFT / 2; ++s) acc = mfma_bf16(sfr[s], sPhi[(mt * (NFT / 2) + s) * 64 + lane_v], acc);
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          if (s2 == 1 && mt < 2) continue;  // A is causal
-          acc = mfma_bf16(s2 == 0 ? vf0 : vf1, col_frag(sA, LDA, mt, s2, lane_v), acc);
-        }
-        num[mt] = acc;
+        num[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ph[0][mt] = sPhi[(mt * (NFT / 2)) * 64 + lane_v];
       }
-      {  // den for token tile mt = wave: the same products with z (one row) in place of s,
-         // and the row sums of A through the valid-token row
-        __builtin_amdgcn_sched_barrier(0);
-        const int mt = wave;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 zb[2];
+      zb[0] = sZf[lane_v];
 #pragma unroll
-        for (int s = 0; s < NFT / 2; ++s) {
-          const f32x4 z0 = l16 == 0 ? ld4f(sZ + 32 * s + 4 * g) : zero;
-          const f32x4 z1 = l16 == 0 ? ld4f(sZ + 32 * s + 16 + 4 * g) : zero;
-          dacc = mfma_bf16(pack_pair(z0, z1), sPhi[(mt * (NFT / 2) + s) * 64 + lane_v], dacc);
+      for (int s = 0; s < NFT / 2; ++s) {
+        if (s + 1 < NFT / 2) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) ph[(s + 1) & 1][mt] = sPhi[(mt * (NFT / 2) + s + 1) * 64 + lane_v];
+          zb[(s + 1) & 1] = sZf[(s + 1) * 64 + lane_v];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) num[mt] = mfma_bf16(sfr[s], ph[s & 1][mt], num[mt]);
+        dacc = mfma_bf16(zb[s & 1], sPhi[(wave * (NFT / 2) + s) * 64 + lane_v], dacc);
+      }
+#pragma unroll
+      for (int it = 0; it < 6; ++it) {  // A V: (mt, s2) with s2 = 1 only for mt >= 2 (causal)
+        const int mt = it < 2 ? it : 2 + (it - 2) / 2, s2 = it < 2 ? 0 : (it - 2) % 2;
+        num[mt] = mfma_bf16(s2 == 0 ? vf0 : vf1, col_frag(sA, LDA, mt, s2, lane_v), num[mt]);
+      }
+      {  // den: + the row sums of A (valid-token row), for token tile mt = wave
+        const int mt = wave;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (s2 == 1 && mt < 2) continue;
@@ -391,20 +412,25 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         st[DP] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[DP]);
         st[DP + 1] = mfma_bf16(ones[s2], s2 == 0 ? vf0 : vf1, st[DP + 1]);
       }
-      // z increment phi(K)^T 1 for this wave's tiles m = wave + 4 i
-      const f32x4 vmask0 = {(float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0), (float)(l16 == 0)};
-      for (int m = wave; m < NFT; m += NW) {
-        f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+      // z increment phi(K)^T 1: the order-2 part is the key Gram sum_t k_t k_t^T / sqrt 2
+      // (wave 0), the linear part sum_t k_t and the constant sum_t 1 (wave 1)
+      if (wave == 0) {
+        f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) gk = mfma_bf16(kj[s2], kj[s2], gk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sZinc[16 * (4 * g + e) + l16] = gk[e] * rs2;  // feature (4 g + e, l16)
+      } else if (wave == 1) {
+        f32x4 zl = {0.f, 0.f, 0.f, 0.f}, zc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          if (m < DP) {
-            const f32x4 k0 = ld4f(sKs + m * LDKS + 32 * s2 + 4 * g), k1 = ld4f(sKs + m * LDKS + 32 * s2 + 16 + 4 * g);
-            zacc = mfma_bf16(kj[s2], pack_pair(vmask0 * k0, vmask0 * k1), zacc);
-          } else {
-            zacc = mfma_bf16(m == DP ? kj[s2] : ones[s2], ones[s2], zacc);
-          }
+          zl = mfma_bf16(ones[s2], kj[s2], zl);      // row 0: sum_t k_t[l16]
+          zc = mfma_bf16(ones[s2], ones[s2], zc);    // [0][0]: number of valid tokens
         }
-        if (l16 == 0) *reinterpret_cast<f32x4 *>(sZinc + 16 * m + 4 * g) = zacc;
+        if (g == 0) {
+          sZinc[16 * DP + l16] = zl[0];
+          sZinc[16 * (DP + 1) + l16] = l16 == 0 ? zc[0] : 0.0f;
+        }
       }
     }
     __syncthreads();
@@ -420,7 +446,11 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + 16 * n_col + 4 * g), __builtin_bit_cast(u32x2, h));
       }
     }
-    for (int fi = tid; fi < NF; fi += NTHR) sZ[fi] += sZinc[fi];
+    for (int fi = tid; fi < NF; fi += NTHR) {
+      const float zn = sZ[fi] + sZinc[fi];
+      sZ[fi] = zn;
+      if (OUT) reinterpret_cast<bf16_t *>(sZf)[zf_index(fi)] = f32_to_bf16(zn);
+    }
   }
 #undef LA_BLOAD
 
