@@ -10,6 +10,7 @@
 //
 //   gated delta  L_tj = beta_t e^{g_t-g_j} k_t.k_j (j < t),  T = (I + L)^{-1}
 //                W = T diag(beta gamma) K,  U~ = T diag(beta) V,  U = U~ - W S^T
+//                (evaluated as U = T diag(beta) (V - diag(gamma) K S^T): W is never formed)
 //   gated/add.   U = diag(beta) V
 //   O  = diag(gamma) Q S^T + (P . Q K^T) U
 //   S' = gamma_C S + U^T diag(e^{g_C - g}) K  =  S M_c + B_c
@@ -64,7 +65,7 @@ enum { LD_K = 1, LD_Q = 2, LD_V = 4, LD_T = 8, LD_G = 16, LD_ALL = 31 };
 #define LA_CHUNK_PREFETCH_OUT 0
 #endif
 
-constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V, W
+constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V
 constexpr int LDA = C + 8;   // bf16 [C][C]: decay-masked Q K^T, transposed
 constexpr int LDT = C + 8;   // bf16 [C][C]: (T diag(beta))^T
 
@@ -111,7 +112,7 @@ __device__ __forceinline__ bf16x8 col_frag(const bf16_t *tile, int ld, int nt, i
 // 4 g + e, the key index d = sd(m, g) + e with sd(m, g) = 32 (m / 2) + 8 g + 4 (m % 2): the
 // two tiles 2 s and 2 s + 1 of lane group g together cover the eight consecutive keys
 // 32 s + 8 g .. +7, so the state packed as an MFMA operand pairs with one contiguous
-// 16-byte read of a row of W or Q (no bank conflicts, unlike two 8-byte pieces).
+// 16-byte read of a row of K or Q (no bank conflicts, unlike two 8-byte pieces).
 __device__ __forceinline__ int sd(int m, int g) { return 32 * (m >> 1) + 8 * g + 4 * (m & 1); }
 
 // K^T rows in the state's key order as an A operand with k = tokens: lane (g, i) receives
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
 
 // Waves per workgroup: 4 (32 state rows each), or 8 for the delta-rule map pass, whose
 // workgroup carries both the 128 B rows (waves 0-3) and the 128 M rows (waves 4-7) so
-// that the state-independent work of a chunk is done once for both.
+// that each chunk's tiles are loaded once for both.
 template <int MODE, bool DELTA> struct Waves {
   static constexpr int value = (MODE == MODE_MAP && DELTA) ? 8 : NW;
 };
@@ -327,9 +328,8 @@ template <int MODE, bool DELTA> struct Lds {
   static constexpr bool OUT = MODE == MODE_OUT;
   static constexpr int K = 0;
   static constexpr int Q = SZ_ROW;                         // MODE_OUT only
-  static constexpr int V = OUT ? 2 * SZ_ROW : SZ_ROW;      // V; MODE_OUT: then -W
-  static constexpr int W = OUT ? V : V + SZ_ROW;           // MODE_MAP keeps W apart
-  static constexpr int TB = (OUT || !DELTA) ? V + SZ_ROW : W + SZ_ROW;
+  static constexpr int V = OUT ? 2 * SZ_ROW : SZ_ROW;
+  static constexpr int TB = V + SZ_ROW;                    // delta rule only
   static constexpr int A = DELTA ? TB + SZ_T : TB;         // MODE_OUT only
   static constexpr int VEC = OUT ? A + SZ_A : (DELTA ? TB + SZ_T : TB);
   static constexpr int SIZE = VEC + SZ_VEC;
@@ -351,7 +351,6 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   bf16_t *sK = reinterpret_cast<bf16_t *>(smem + LY::K);
   bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + LY::Q);
   bf16_t *sV = reinterpret_cast<bf16_t *>(smem + LY::V);
-  bf16_t *sW = reinterpret_cast<bf16_t *>(smem + LY::W);
   bf16_t *sT = reinterpret_cast<bf16_t *>(smem + LY::TB);
   bf16_t *sA = reinterpret_cast<bf16_t *>(smem + LY::A);
   float *sG = reinterpret_cast<float *>(smem + LY::VEC);
@@ -476,13 +475,11 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     }
     __syncthreads();
 
-    // ---- phase B: everything that does not need the state of this chunk's start: Q K^T,
-    // U~, W
+    // ---- phase B (replay): the decay-masked Q K^T, which does not need the state
     if (PF && ci + 1 < nchunks) {
       const int64_t nt0 = t0 + C;
       LA_LOAD(nt0, (int)((T - nt0) < C ? (T - nt0) : C), PF);
     }
-    f32x4 Ut[4][2];
     if (OUT) {
       // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves (a wave
       // without a third tile recomputes tile 9 and does not store it), stored transposed
@@ -514,28 +511,61 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
       }
     }
+
+    // ---- phase F: the state-dependent part, per wave on its own 32 state rows
+    f32x4 U[4][2];
     if (DELTA) {
-      // U~ = TB V for this wave's own state rows (B rows only; registers) and -W =
-      // -TB diag(gamma) K, column tiles 2 wr, 2 wr + 1 (MODE_OUT waves and the M-row waves),
-      // sharing each TB fragment.  W is formed as W^T = K^T diag(gamma) TB^T so that each
-      // lane holds four consecutive columns of a row of W (one 8-byte write); in MODE_OUT it
-      // overwrites the V columns that only this wave reads, after reading them.
-      const bool do_u = !m_kind, do_w = OUT || m_kind;
-      bf16x8 vf[2][2], kt[2][2];  // V columns and diag(gamma) K columns, k = tokens
+      // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T on this wave's rows (K row
+      // fragments read two steps ahead), Y = V - gamma . K S^T in registers (V read along
+      // tokens; the transition rows of the map pass have no V), then the lower-triangular
+      // product with TB.  No W is formed.
+      f32x4 ks[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#define LA_KF(it) *reinterpret_cast<const bf16x8 *>(sK + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
+      {
+        bf16x8 kf[3], sfr[2];
+        kf[0] = LA_KF(0);
+        kf[1] = LA_KF(1);
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int s = it / 4, mt = it % 4;
+          if (it + 2 < 16) kf[(it + 2) % 3] = LA_KF(it + 2);
+          if (mt == 0) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+          }
+          LA_FENCE();
+#pragma unroll
+          for (int c = 0; c < 2; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
+        }
+      }
+#undef LA_KF
+      LA_FENCE();
+      bf16x8 yfr[2][2];  // Y as an operand with k = tokens, [c][s]
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const f32x4 ga = ld4(sGam + 32 * s + 4 * g), gb = ld4(sGam + 32 * s + 16 + 4 * g);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          if (do_u) vf[c][s] = col_frag(sV, LDK, 2 * wr + c, s, lane_v);
-          if (do_w) kt[c][s] = scale8(col_frag(sK, LDK, 2 * wr + c, s, lane_v), ga, gb);
+          f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
+          if (!m_kind) {
+            const bf16x8 vf = col_frag(sV, LDK, 2 * wr + c, s, lane_v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              y0[e] += (float)vf[e];
+              y1[e] += (float)vf[4 + e];
+            }
+          }
+          yfr[c][s] = pack_pair(y0, y1);
         }
       }
       // steps (mt, s), s = 1 only for mt >= 2 (T is lower triangular); the TB fragment of
       // the next step is read before this step's MFMAs
       bf16x8 tfb[2];
       tfb[0] = col_frag(sT, LDT, 0, 0, lane_v);
-      f32x4 accw[2];
 #pragma unroll
       for (int it = 0; it < 6; ++it) {
         const int mt = it < 2 ? it : 2 + (it - 2) / 2, s = it < 2 ? 0 : (it - 2) % 2;
@@ -545,58 +575,13 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
           tfb[it1 & 1] = col_frag(sT, LDT, mt1, s1, lane_v);
         }
         LA_FENCE();
-        const bf16x8 tf = tfb[it & 1];
         if (s == 0) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            Ut[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accw[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
+          for (int c = 0; c < 2; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (do_u) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) Ut[mt][c] = mfma_bf16(tf, vf[c][s], Ut[mt][c]);
-        }
-        if (do_w) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) accw[c] = mfma_bf16(kt[c][s], tf, accw[c]);
-          if (mt < 2 || s == 1) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {  // lane: W[16 mt + l16][16 (2 wr + c) + 4 g + e]
-              const f32x4 w = -accw[c];
-              *reinterpret_cast<bf16x4 *>(sW + (16 * mt + l16) * LDK + 16 * (2 * wr + c) + 4 * g) =
-                  bf16x4{(__bf16)w[0], (__bf16)w[1], (__bf16)w[2], (__bf16)w[3]};
-            }
-          }
-        }
+        for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
       }
-    }
-    __syncthreads();
-
-    // ---- phase F: the state-dependent part, per wave on its own 32 state rows
-    f32x4 U[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) U[mt][c] = (DELTA && !m_kind) ? Ut[mt][c] : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (DELTA) {  // U = U~ - W S^T; W fragments read two steps ahead
-#define LA_WF(it) *reinterpret_cast<const bf16x8 *>(sW + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
-      bf16x8 wb[3], sfr[2];
-      wb[0] = LA_WF(0);
-      wb[1] = LA_WF(1);
-#pragma unroll
-      for (int it = 0; it < 16; ++it) {
-        const int s = it / 4, mt = it % 4;
-        if (it + 2 < 16) wb[(it + 2) % 3] = LA_WF(it + 2);
-        if (mt == 0) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
-        }
-        LA_FENCE();
-#pragma unroll
-        for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(wb[it % 3], sfr[c], U[mt][c]);
-      }
-#undef LA_WF
     }
     LA_FENCE();
     bf16x8 ufr[2][2], dufr[2][2];  // U and diag(decay) U as operands with k = tokens
@@ -651,6 +636,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         }
       }
 #undef LA_QF
+      __syncthreads();  // every wave's A tiles are in LDS
       const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
 #define LA_AF(it) col_frag(sA, LDA, (it) < 2 ? (it) : 2 + ((it) - 2) / 2, (it) < 2 ? 0 : ((it) - 2) % 2, lane_v)
       bf16x8 ab[2];
