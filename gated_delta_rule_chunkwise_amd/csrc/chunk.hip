@@ -273,8 +273,10 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
   f32x4 db[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) db[b] = LA_DB(b);
-  // T_ij (i > j) as accumulator tiles: rows 4 grp + e of column l16
-  f32x4 tt[6];  // (i, j) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), same order as al
+  // T_ij (i > j) as accumulator tiles: rows 4 grp + e of column l16 (tt, the B operands
+  // of later levels), and transposed: row l16, columns 4 grp + e (ttT, for the store);
+  // the transpose is the same product with its operands swapped
+  f32x4 tt[6], ttT[6];  // (i, j) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), same order as al
 #pragma unroll
   for (int level = 1; level <= 3; ++level) {
 #pragma unroll
@@ -289,29 +291,36 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
         for (int s = 0; s < 4; ++s) x = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s], Bm[s], x, 0, 0, 0);
       }
       const f32x4 di = LA_DA(i);
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      f32x4 y = {0.f, 0.f, 0.f, 0.f}, yT = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) y = __builtin_amdgcn_mfma_f32_16x16x4f32(di[s], x[s], y, 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        if (i < 3) y = __builtin_amdgcn_mfma_f32_16x16x4f32(di[s], x[s], y, 0, 0, 0);
+        yT = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], di[s], yT, 0, 0, 0);
+      }
       tt[i * (i - 1) / 2 + j] = -y;
+      ttT[i * (i - 1) / 2 + j] = -yT;
     }
   }
 #undef LA_DA
 #undef LA_DB
 
-  // stored tile row 16 j + l16 = column of T diag(beta): block (i, j) of T supplies its
-  // columns 16 i + 4 grp .. +3 (eight bytes per lane); blocks above the diagonal are zero
+  // Stored tile: row t holds row t of T diag(beta) with its columns in the MFMA k order
+  // of the state passes: column j = 32 s + 16 h + 4 q + e at position 32 s + 8 q + 4 h + e,
+  // so that an operand fragment (columns 32 s + 4 q + 0..3 and 32 s + 16 + 4 q + 0..3 of
+  // one row) is one 16-byte read.  Lane (grp, l16) of block (i, jb) holds row 16 i + l16,
+  // columns 16 jb + 4 grp + 0..3 (eight bytes); blocks above the diagonal are zero.
   bf16_t *dst = a.tb + (size_t)cid * T_CHUNK;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float bj = L.beta[16 * j + l16];
+  for (int jb = 0; jb < 4; ++jb) {
+    const f32x4 bj = ld4(L.beta + 16 * jb + 4 * grp);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
-      if (i == j) t = db[j];
-      if (i > j) t = tt[i * (i - 1) / 2 + j];
+      if (i == jb) t = ld4(L.d[i] + l16 * LDD + 4 * grp);  // D_i row l16
+      if (i > jb) t = ttT[i * (i - 1) / 2 + jb];
       t = t * bj;
       const bf16x4 h = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-      gst8(dst + (16 * j + l16) * C + 16 * i + 4 * grp, __builtin_bit_cast(u32x2, h));
+      gst8(dst + (16 * i + l16) * C + 32 * (jb >> 1) + 8 * grp + 4 * (jb & 1), __builtin_bit_cast(u32x2, h));
     }
   }
 }
@@ -481,34 +490,37 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       LA_LOAD(nt0, (int)((T - nt0) < C ? (T - nt0) : C), PF);
     }
     if (OUT) {
-      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves (a wave
-      // without a third tile recomputes tile 9 and does not store it), stored transposed
-      // (row j, column t): each lane writes its four rows t as 8 bytes
+      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves, each
+      // computed as its transpose K Q^T: lane (g, l16) holds A[t][j] for token t = 16 ti + l16
+      // and keys j = 16 tj + 4 g + 0..3, stored in row t at the positions of the MFMA k
+      // order (j = 32 s + 16 h + 4 q + e at 32 s + 8 q + 4 h + e), one 8-byte write
 #pragma unroll
       for (int m = 0; m < 3; ++m) {
         const int job = wave + NWT * m;
-        int ti, tj;
-        tri_index(job < 10 ? job : 9, ti, tj);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (job < 10) {
+          int ti, tj;
+          tri_index(job, ti, tj);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-          const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
-          const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
-          acc = mfma_bf16(fa, fb, acc);
+          for (int s = 0; s < DK / 32; ++s) {
+            const bf16x8 fk = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
+            const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
+            acc = mfma_bf16(fk, fq, acc);
+          }
+          const int t = 16 * ti + l16;
+          const float gt = sG[t];
+          const f32x4 gj = ld4(sG + 16 * tj + 4 * g);
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (16 * tj + 4 * g + e <= t) ? exp2f(gt - gj[e]) * acc[e] : 0.0f;
+          *reinterpret_cast<bf16x4 *>(sA + t * LDA + 32 * (tj >> 1) + 8 * g + 4 * (tj & 1)) =
+              bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         }
-        const int j = 16 * tj + l16;
-        const float gj = sG[j];
-        const f32x4 gt = ld4(sG + 16 * ti + 4 * g);
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (16 * ti + 4 * g + e >= j) ? exp2f(gt[e] - gj) * acc[e] : 0.0f;
-        if (job < 10)
-          *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
       }
       // the two above-diagonal tiles read by the A U products: A (0,1) and (2,3)
       if (tid < 128) {
         const int tile = tid >> 6, e = tid & 63;
-        *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
+        *reinterpret_cast<uint2 *>(sA + (32 * tile + (e >> 2)) * LDA + 32 * tile + 8 * (e & 3) + 4) = make_uint2(0u, 0u);
       }
     }
 
@@ -565,14 +577,15 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       // steps (mt, s), s = 1 only for mt >= 2 (T is lower triangular); the TB fragment of
       // the next step is read before this step's MFMAs
       bf16x8 tfb[2];
-      tfb[0] = col_frag(sT, LDT, 0, 0, lane_v);
+#define LA_TF(mt, s) *reinterpret_cast<const bf16x8 *>(sT + (16 * (mt) + l16) * LDT + 32 * (s) + 8 * g)
+      tfb[0] = LA_TF(0, 0);
 #pragma unroll
       for (int it = 0; it < 6; ++it) {
         const int mt = it < 2 ? it : 2 + (it - 2) / 2, s = it < 2 ? 0 : (it - 2) % 2;
         if (it + 1 < 6) {
           const int it1 = it + 1;
           const int mt1 = it1 < 2 ? it1 : 2 + (it1 - 2) / 2, s1 = it1 < 2 ? 0 : (it1 - 2) % 2;
-          tfb[it1 & 1] = col_frag(sT, LDT, mt1, s1, lane_v);
+          tfb[it1 & 1] = LA_TF(mt1, s1);
         }
         LA_FENCE();
         if (s == 0) {
@@ -582,6 +595,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 #pragma unroll
         for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
       }
+#undef LA_TF
     }
     LA_FENCE();
     bf16x8 ufr[2][2], dufr[2][2];  // U and diag(decay) U as operands with k = tokens
@@ -638,7 +652,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 #undef LA_QF
       __syncthreads();  // every wave's A tiles are in LDS
       const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
-#define LA_AF(it) col_frag(sA, LDA, (it) < 2 ? (it) : 2 + ((it) - 2) / 2, (it) < 2 ? 0 : ((it) - 2) % 2, lane_v)
+#define LA_AF(it) *reinterpret_cast<const bf16x8 *>(sA + (16 * ((it) < 2 ? (it) : 2 + ((it) - 2) / 2) + l16) * LDA + 32 * ((it) < 2 ? 0 : ((it) - 2) % 2) + 8 * g)
       bf16x8 ab[2];
       ab[0] = LA_AF(0);
 #pragma unroll
