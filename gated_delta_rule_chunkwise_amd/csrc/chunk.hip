@@ -65,9 +65,9 @@ enum { LD_K = 1, LD_Q = 2, LD_V = 4, LD_T = 8, LD_G = 16, LD_ALL = 31 };
 #define LA_CHUNK_PREFETCH_OUT 0
 #endif
 
-constexpr int LDK = DK + 8;  // row-major bf16 tiles [C][DK]: K, Q, V
-constexpr int LDA = C + 8;   // bf16 [C][C]: decay-masked Q K^T, transposed
-constexpr int LDT = C + 8;   // bf16 [C][C]: (T diag(beta))^T
+constexpr int LDK = DK + 16;  // row-major bf16 tiles [C][DK]: K, Q, V (288-byte rows)
+constexpr int LDA = C + 16;   // bf16 [C][C]: decay-masked Q K^T, rows t, k-ordered columns
+constexpr int LDT = C + 16;   // bf16 [C][C]: T diag(beta), rows t, k-ordered columns
 
 constexpr int SZ_ROW = C * LDK * 2;
 constexpr int SZ_A = C * LDA * 2;
