@@ -224,7 +224,7 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
       if (k < i) {
         f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = br * exp2f(gr - gc[e]) * acc[e];  // L_rc, r > c
+        for (int e = 0; e < 4; ++e) v[e] = br * exp2_hw(gr - gc[e]) * acc[e];  // L_rc, r > c
         al[i * (i - 1) / 2 + k] = v;
       } else {  // diagonal: L_bb^T[c][r] = L_rc for r > c, from the block (b, b)
         const f32x4 bc = ld4(L.beta + 16 * k + 4 * grp);
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
         for (int e = 0; e < 4; ++e) {
           const int c = 16 * k + 4 * grp + e;
           // the block is symmetric: acc[e] is also k_r . k_c with r = c, c = r swapped
-          v[e] = c > r ? bc[e] * exp2f(gc[e] - gr) * acc[e] : 0.0f;  // L_cr, c > r
+          v[e] = c > r ? bc[e] * exp2_hw(gc[e] - gr) * acc[e] : 0.0f;  // L_cr, c > r
         }
         // lane (grp, l16) holds L_bb[4 grp + e][l16] = L_bb^T[l16][4 grp + e]
         *reinterpret_cast<f32x4 *>(L.d[i] + l16 * LDD + 4 * grp) = v;
@@ -479,8 +479,8 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       const float gC = __shfl(x, 63, 64);
       sG[lane] = x;
       sBeta[lane] = pbe;
-      sGam[lane] = exp2f(x);
-      sDec[lane] = exp2f(gC - x);
+      sGam[lane] = exp2_hw(x);
+      sDec[lane] = exp2_hw(gC - x);
     }
     __syncthreads();
 
@@ -512,7 +512,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
           const f32x4 gj = ld4(sG + 16 * tj + 4 * g);
           f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (16 * tj + 4 * g + e <= t) ? exp2f(gt - gj[e]) * acc[e] : 0.0f;
+          for (int e = 0; e < 4; ++e) v[e] = (16 * tj + 4 * g + e <= t) ? exp2_hw(gt - gj[e]) * acc[e] : 0.0f;
           *reinterpret_cast<bf16x4 *>(sA + t * LDA + 32 * (tj >> 1) + 8 * g + 4 * (tj & 1)) =
               bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         }
@@ -525,9 +525,18 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     }
 
     // ---- phase F: the state-dependent part, per wave on its own 32 state rows
-    f32x4 U[4][2];
+    // O^T = S Q^T diag(gamma) + U^T A^T (replay) on the chunk's entering state: lane
+    // (g, l16) of tile (mt, c) holds O[16 mt + l16][row0 + 16 c + 4 g + e], four consecutive
+    // outputs of one token, stored straight to HBM (8 bytes; rows past the chunk are dropped).
+    f32x4 U[4][2], O[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) O[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
     if (DELTA) {
-      // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T on this wave's rows (K row
+      // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T on this wave's rows, in the
+      // replay together with Q S^T (one packing of the state serves both; K and Q row
       // fragments read two steps ahead), Y = V - gamma . K S^T in registers (V read along
       // tokens; the transition rows of the map pass have no V), then the lower-triangular
       // product with TB.  No W is formed.
@@ -538,13 +547,20 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         for (int c = 0; c < 2; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #define LA_KF(it) *reinterpret_cast<const bf16x8 *>(sK + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
       {
-        bf16x8 kf[3], sfr[2];
+        bf16x8 kf[3], qf[3], sfr[2];
         kf[0] = LA_KF(0);
         kf[1] = LA_KF(1);
+        if (OUT) {
+          qf[0] = LA_QF(0);
+          qf[1] = LA_QF(1);
+        }
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
           const int s = it / 4, mt = it % 4;
-          if (it + 2 < 16) kf[(it + 2) % 3] = LA_KF(it + 2);
+          if (it + 2 < 16) {
+            kf[(it + 2) % 3] = LA_KF(it + 2);
+            if (OUT) qf[(it + 2) % 3] = LA_QF(it + 2);
+          }
           if (mt == 0) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
@@ -552,6 +568,10 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
           LA_FENCE();
 #pragma unroll
           for (int c = 0; c < 2; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
+          if (OUT) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qf[it % 3], O[mt][c]);
+          }
         }
       }
 #undef LA_KF
@@ -622,17 +642,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       }
     }
     if (OUT) {
-      // O^T = S Q^T diag(gamma) + U^T A^T on the chunk's entering state: lane (g, l16) of
-      // tile (mt, c) holds O[16 mt + l16][row0 + 16 c + 4 g + e], four consecutive outputs
-      // of one token, stored straight to HBM (8 bytes; rows past the chunk are dropped).
-      // Q and A fragments are read two steps / one step ahead.
-      f32x4 O[4][2];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) O[mt][c] = {0.f, 0.f, 0.f, 0.f};
-#define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
-      {
+      if (!DELTA) {  // Q S^T (the delta rule formed it with K S^T); Q fragments two steps ahead
         bf16x8 qb[3], sfr[2];
         qb[0] = LA_QF(0);
         qb[1] = LA_QF(1);
@@ -650,7 +660,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         }
       }
 #undef LA_QF
-      __syncthreads();  // every wave's A tiles are in LDS
+      __syncthreads();  // every wave's A tiles are in LDS; A fragments one step ahead
       const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
 #define LA_AF(it) *reinterpret_cast<const bf16x8 *>(sA + (16 * ((it) < 2 ? (it) : 2 + ((it) - 2) / 2) + l16) * LDA + 32 * ((it) < 2 ? 0 : ((it) - 2) % 2) + 8 * g)
       bf16x8 ab[2];

@@ -53,6 +53,11 @@ __device__ __forceinline__ uint16_t bld2(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 
+// 2^x with the hardware instruction alone (no denormal range reduction, so results below
+// 2^-126 may come out as zero).  Used for decay factors 2^(g_t - g_j) <= 1, where a
+// factor that small contributes nothing at the precision of the result.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
 
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
