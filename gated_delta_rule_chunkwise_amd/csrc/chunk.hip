@@ -127,6 +127,24 @@ __device__ __forceinline__ bf16x8 kstate_frag(const bf16_t *tile, int ld, int m,
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// State rows held by a wave: column l16 of its state tile c is state row
+// row0 + srow(c, l16), srow = 8 (l16 / 4) + 4 c + l16 % 4.  An accumulator tile over state
+// rows (lane (g, l16) holds its rows 4 g + e) then covers rows row0 + 8 g + 4 c + e, so the
+// two tiles c = 0, 1 of one token give eight consecutive outputs (one 16-byte store).
+__device__ __forceinline__ int srow(int c, int l16) { return 8 * (l16 >> 2) + 4 * c + (l16 & 3); }
+
+// V columns row0 + srow(c, i) as an operand with k = tokens (lane (g, i) receives tokens
+// 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3); the transpose read of col_frag with each
+// lane quad addressing its own 4-column chunk.
+__device__ __forceinline__ bf16x8 vrow_frag(const bf16_t *tile, int ld, int row0, int c, int s, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const bf16_t *p0 = tile + (32 * s + 4 * g + (i >> 2)) * ld + row0 + 8 * (i & 3) + 4 * c;
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + 16 * ld));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ bf16x8 pack_pair(f32x4 a, f32x4 b) {
   return pack8(a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
 }
@@ -377,7 +395,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   const int64_t T = a.T;
   const int row0 = wr * RPW;  // first state row owned by this wave
 
-  // ---- state: lane holds S^T[d = sd(m, g) + e][row0 + 16 c + l16] in st[m][c][e]
+  // ---- state: lane holds S^T[d = sd(m, g) + e][row0 + srow(c, l16)] in st[m][c][e]
   f32x4 st[DK / 16][2];
   {
     const float *src = nullptr;
@@ -386,7 +404,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int r = row0 + 16 * c + l16;
+        const int r = row0 + srow(c, l16);
         if (src) {
           st[m][c] = ld4(src + (size_t)r * DK + sd(m, g));
         } else {
@@ -526,8 +544,9 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
 
     // ---- phase F: the state-dependent part, per wave on its own 32 state rows
     // O^T = S Q^T diag(gamma) + U^T A^T (replay) on the chunk's entering state: lane
-    // (g, l16) of tile (mt, c) holds O[16 mt + l16][row0 + 16 c + 4 g + e], four consecutive
-    // outputs of one token, stored straight to HBM (8 bytes; rows past the chunk are dropped).
+    // (g, l16) of tile (mt, c) holds O[16 mt + l16][row0 + 8 g + 4 c + e]: with both tiles,
+    // eight consecutive outputs of one token, stored straight to HBM (16 bytes; rows past
+    // the chunk are dropped).
     f32x4 U[4][2], O[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -584,7 +603,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         for (int c = 0; c < 2; ++c) {
           f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
           if (!m_kind) {
-            const bf16x8 vf = col_frag(sV, LDK, 2 * wr + c, s, lane_v);
+            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s, lane_v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               y0[e] += (float)vf[e];
@@ -629,7 +648,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
           u0 = U[2 * s2][c];
           u1 = U[2 * s2 + 1][c];
         } else {  // U = diag(beta) V, read along tokens from the V tile
-          const bf16x8 vf = col_frag(sV, LDK, 2 * wave + c, s2, lane_v);
+          const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s2, lane_v);
           const f32x4 b0 = ld4(sBeta + 32 * s2 + 4 * g), b1 = ld4(sBeta + 32 * s2 + 16 + 4 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -677,13 +696,9 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
         LA_FENCE();
 #pragma unroll
         for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], ab[it & 1], O[mt][c]);
-        if (mt < 2 || s2 == 1) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const bf16x4 h = {(__bf16)O[mt][c][0], (__bf16)O[mt][c][1], (__bf16)O[mt][c][2], (__bf16)O[mt][c][3]};
-            bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 16 * c + 4 * g), __builtin_bit_cast(u32x2, h));
-          }
-        }
+        if (mt < 2 || s2 == 1)  // token 16 mt + l16, outputs row0 + 8 g .. +7
+          bst16(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 8 * g),
+                __builtin_bit_cast(u32x4, pack_pair(O[mt][0], O[mt][1])));
       }
 #undef LA_AF
     }
@@ -720,7 +735,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const int r = row0 + 16 * c + l16;
+          const int r = row0 + srow(c, l16);
           *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + sd(m, g)) = st[m][c];
         }
     }
@@ -731,7 +746,7 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int r = rbase + row0 + 16 * c + l16;
+        const int r = rbase + row0 + srow(c, l16);
         *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + sd(m, g)) = st[m][c];
       }
     if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
