@@ -416,8 +416,6 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
   }
 
   float gseg = 0.0f;  // log decay over the segment (scalar-gated map)
-  int64_t prev_t0 = -1;
-  int prev_n = 0;
   const int64_t first = (int64_t)seg * a.seg_chunks * C;
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
@@ -725,8 +723,6 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
       }
     }
     __syncthreads();
-    prev_t0 = t0;
-    prev_n = n;
   }
 
   if (OUT) {
@@ -752,6 +748,279 @@ __global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_ker
     if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
   }
 #undef LA_LOAD
+}
+
+// ---------------------------------------------------------------------------------------
+// Pass 1 (segment maps), streamed through LDS with direct global-to-LDS loads: one
+// workgroup per CU (8 waves for the delta rule: B rows and M rows), so LDS has room for two
+// copies of a chunk's tiles.  While chunk i is processed from one copy, chunk i + 1 lands in
+// the other (buffer_load ... lds: no registers, no LDS store instructions); every wave
+// forms the gate prefix sums itself, so one barrier per chunk suffices.
+// ---------------------------------------------------------------------------------------
+// Buffer descriptor as four words (base, size in bytes), for inline assembly.
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// One 16-byte-per-lane global-to-LDS load: lane L's 16 bytes at byte offset `off` of the
+// descriptor land at LDS address m0 + 16 L (m0 = lds_base, wave-uniform).  Issued from
+// inline assembly so that the compiler does not wait for it before every later LDS read
+// (it cannot tell the two copies of a tile apart); the kernel waits for it explicitly
+// (lds_dma_wait) before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
+}
+// vmcnt(0), the other counters left alone: every global load of this wave has landed.
+__device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Fill a row-padded LDS tile (ROWS rows of ROWB bytes at a stride of LDB bytes) from ROWS
+// contiguous global rows.  Wave-instruction j writes LDS bytes [1024 j, 1024 j + 1024), lane
+// L's 16 bytes at 1024 j + 16 L; lanes that fall in the padding, or past the descriptor's
+// size (rows beyond a partial chunk), write zeros.
+template <int ROWB, int LDB, int ROWS, int NWAVES>
+__device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, int lane) {
+  constexpr int TOTAL = ROWS * LDB;
+  static_assert(TOTAL % 1024 == 0, "whole wave-instructions");
+  constexpr int NI = TOTAL / 1024;
+  const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) void *)lds;
+#pragma unroll
+  for (int j0 = 0; j0 < NI; j0 += NWAVES) {
+    const int j = j0 + wave;
+    if (j < NI) {
+      const int p = 1024 * j + 16 * lane;
+      const int row = p / LDB, off = p - row * LDB;
+      const uint32_t src = off < ROWB ? (uint32_t)(row * ROWB + off) : 0xFFFFFFF0u;
+      lds_dma16(r, src, __builtin_amdgcn_readfirstlane(base + 1024u * (uint32_t)j));
+    }
+  }
+}
+
+// Gate prefix sums of one chunk, formed by each wave for itself: gw[0..63] = 2^{g_t},
+// gw[64..127] = 2^{g_C - g_t}, gw[128..191] = beta_t (g in log2 units, alpha = 1 and beta = 0
+// beyond the chunk).  Returns g_C.
+__device__ __forceinline__ float wave_gates(float al, float be, bool additive, float *gw, int lane) {
+  float x = additive ? 0.0f : log2f(al);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  const float gC = __shfl(x, 63, 64);
+  gw[lane] = exp2_hw(x);
+  gw[64 + lane] = exp2_hw(gC - x);
+  gw[128 + lane] = be;
+  return gC;
+}
+
+template <bool DELTA>
+__global__ __launch_bounds__((DELTA ? 8 : 4) * 64, 2) void map_kernel(const Args a) {
+  constexpr int NWT = DELTA ? 8 : 4;
+  constexpr int MAPROWS = DELTA ? 2 * DV : DV;
+  __shared__ __attribute__((aligned(16))) bf16_t sK0[C * LDK], sK1[C * LDK], sV0[C * LDK], sV1[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t sT0[DELTA ? C * LDT : 8], sT1[DELTA ? C * LDT : 8];
+  __shared__ __attribute__((aligned(16))) float sGw[NWT][3 * C];
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+  const bool m_kind = DELTA && wave >= NW;  // waves 4-7 carry the transition (M) rows
+  const int wr = m_kind ? wave - NW : wave;
+  const int row0 = wr * RPW;
+  const int seg = (int)blockIdx.x;
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int64_t T = a.T;
+  const bool additive = a.variant == V_ADDITIVE;
+  const bool use_beta = a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta);
+  float *gw = sGw[wave];
+
+  f32x4 st[DK / 16][2];  // zero start (B rows) or identity (M rows)
+#pragma unroll
+  for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[m][c][e] = (m_kind && row0 + srow(c, l16) == sd(m, g) + e) ? 1.0f : 0.0f;
+
+  const int64_t first = (int64_t)seg * a.seg_chunks * C;
+  int nchunks = a.seg_chunks;
+  if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
+  float gseg = 0.0f;
+
+  // chunk ci's tiles into one LDS copy (untracked DMA), its raw gate values into registers
+  auto issue = [&](int ci, bf16_t *dK, bf16_t *dV, bf16_t *dT, uint32_t &ral, uint32_t &rbe) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
+    const size_t rb = bh * (size_t)T + t0;
+    dma_tile<DK * 2, LDK * 2, C, NWT>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
+    dma_tile<DV * 2, LDK * 2, C, NWT>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)dV, wave, lane);
+    if (DELTA)
+      dma_tile<C * 2, LDT * 2, C, NWT>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
+                                       (unsigned char *)dT, wave, lane);
+    if (!additive) ral = bld2(make_rsrc(a.alpha + rb, n * 2), 2u * lane);
+    if (use_beta) rbe = bld2(make_rsrc(a.beta + rb, n * 2), 2u * lane);
+  };
+
+  // gates of chunk ci from its raw values (alpha = 1, beta = 0 past the sequence end)
+  auto gates = [&](int ci, uint32_t ral, uint32_t rbe) -> float {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const bool in = (int64_t)lane < T - t0;
+    const float al = (!additive && in) ? bf16_to_f32((bf16_t)ral) : 1.0f;
+    const float be = use_beta ? bf16_to_f32((bf16_t)rbe) : (in ? 1.0f : 0.0f);
+    return wave_gates(al, be, additive, gw, lane);
+  };
+
+  // one chunk from the LDS copy (sK, sV, sT), with its gate registers
+  auto step = [&](const bf16_t *sK, const bf16_t *sV, const bf16_t *sT, float gC) {
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int l16 = lane_v & 15, g = lane_v >> 4;
+    gseg += gC;
+    bf16x8 dufr[2][2];
+    if (DELTA) {
+      // U = TB (V - diag(gamma) K S^T) (no V for the M rows), as in the replay
+      f32x4 ks[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#define LA_KF(it) *reinterpret_cast<const bf16x8 *>(sK + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
+      {
+        bf16x8 kf[3], sfr[2];
+        kf[0] = LA_KF(0);
+        kf[1] = LA_KF(1);
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int s = it / 4, mt = it % 4;
+          if (it + 2 < 16) kf[(it + 2) % 3] = LA_KF(it + 2);
+          if (mt == 0) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+          }
+          LA_FENCE();
+#pragma unroll
+          for (int c = 0; c < 2; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
+        }
+      }
+#undef LA_KF
+      LA_FENCE();
+      bf16x8 yfr[2][2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const f32x4 ga = ld4(gw + 32 * s + 4 * g), gb = ld4(gw + 32 * s + 16 + 4 * g);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
+          if (!m_kind) {
+            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s, lane_v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              y0[e] += (float)vf[e];
+              y1[e] += (float)vf[4 + e];
+            }
+          }
+          yfr[c][s] = pack_pair(y0, y1);
+        }
+      }
+      f32x4 U[4][2];
+#define LA_TF(mt, s) *reinterpret_cast<const bf16x8 *>(sT + (16 * (mt) + l16) * LDT + 32 * (s) + 8 * g)
+      bf16x8 tfb[2];
+      tfb[0] = LA_TF(0, 0);
+#pragma unroll
+      for (int it = 0; it < 6; ++it) {
+        const int mt = it < 2 ? it : 2 + (it - 2) / 2, s = it < 2 ? 0 : (it - 2) % 2;
+        if (it + 1 < 6) {
+          const int it1 = it + 1;
+          tfb[it1 & 1] = LA_TF(it1 < 2 ? it1 : 2 + (it1 - 2) / 2, it1 < 2 ? 0 : (it1 - 2) % 2);
+        }
+        LA_FENCE();
+        if (s == 0) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
+      }
+#undef LA_TF
+      LA_FENCE();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f32x4 d0 = ld4(gw + 64 + 32 * s2 + 4 * g), d1 = ld4(gw + 64 + 32 * s2 + 16 + 4 * g);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) dufr[c][s2] = pack_pair(U[2 * s2][c] * d0, U[2 * s2 + 1][c] * d1);
+      }
+    } else {  // U = diag(beta) V
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f32x4 d0 = ld4(gw + 64 + 32 * s2 + 4 * g), d1 = ld4(gw + 64 + 32 * s2 + 16 + 4 * g);
+        const f32x4 b0 = ld4(gw + 128 + 32 * s2 + 4 * g), b1 = ld4(gw + 128 + 32 * s2 + 16 + 4 * g);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s2, lane_v);
+          f32x4 u0, u1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            u0[e] = (float)vf[e] * b0[e] * d0[e];
+            u1[e] = (float)vf[4 + e] * b1[e] * d1[e];
+          }
+          dufr[c][s2] = pack_pair(u0, u1);
+        }
+      }
+    }
+    {  // S^T <- gamma_C S^T + K^T diag(decay) U; K fragments read one step ahead
+      const float gam = exp2_hw(gC);
+      bf16x8 kb[2][2];
+      kb[0][0] = kstate_frag(sK, LDK, 0, 0, lane_v);
+      kb[0][1] = kstate_frag(sK, LDK, 0, 1, lane_v);
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m) {
+        if (m + 1 < DK / 16) {
+          kb[(m + 1) & 1][0] = kstate_frag(sK, LDK, m + 1, 0, lane_v);
+          kb[(m + 1) & 1][1] = kstate_frag(sK, LDK, m + 1, 1, lane_v);
+        }
+        LA_FENCE();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x4 acc = st[m][c] * gam;
+          acc = mfma_bf16(kb[m & 1][0], dufr[c][0], acc);
+          acc = mfma_bf16(kb[m & 1][1], dufr[c][1], acc);
+          st[m][c] = acc;
+        }
+      }
+    }
+  };
+
+  // Two LDS copies: chunk ci + 1 streams into one while chunk ci is processed from the
+  // other.  Each barrier is preceded by a wait for this wave's own loads, so after it every
+  // wave's part of the next tile has landed; the gates are taken from their raw values
+  // right after it (they have landed too) and before the next loads are issued.
+  uint32_t ral0 = 0, rbe0 = 0, ral1 = 0, rbe1 = 0;
+  if (nchunks > 0) issue(0, sK0, sV0, sT0, ral0, rbe0);
+  for (int ci = 0; ci < nchunks; ci += 2) {
+    lds_dma_wait();
+    __syncthreads();  // copy 0 holds chunk ci; every wave is done with copy 1
+    const float gC0 = gates(ci, ral0, rbe0);
+    if (ci + 1 < nchunks) issue(ci + 1, sK1, sV1, sT1, ral1, rbe1);
+    step(sK0, sV0, sT0, gC0);
+    if (ci + 1 < nchunks) {
+      lds_dma_wait();
+      __syncthreads();  // copy 1 holds chunk ci + 1; every wave is done with copy 0
+      const float gC1 = gates(ci + 1, ral1, rbe1);
+      if (ci + 2 < nchunks) issue(ci + 2, sK0, sV0, sT0, ral0, rbe0);
+      step(sK1, sV1, sT1, gC1);
+    }
+  }
+
+  float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
+  const int rbase = m_kind ? DV : 0;
+#pragma unroll
+  for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r = rbase + row0 + srow(c, l16);
+      *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + sd(m, g)) = st[m][c];
+    }
+  if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
 }
 
 // Pass 2: S_{i+1} = S_i M_i + B_i (delta rule) or e^{gsum_i} S_i + B_i, row-parallel:
@@ -903,8 +1172,8 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
     hipLaunchKernelGGL(tprep_kernel, dim3((unsigned)((chunks + NW - 1) / NW)), dim3(NTHR), 0, s, a);
   }
   if (p.nseg > 1 && (pass_mask & PASS_MAPS)) {
-    if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_MAP, true>), grid, dim3(Waves<MODE_MAP, true>::value * 64), 0, s, a);
-    else hipLaunchKernelGGL((chunk_kernel<MODE_MAP, false>), grid, dim3(NTHR), 0, s, a);
+    if (delta) hipLaunchKernelGGL((map_kernel<true>), grid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((map_kernel<false>), grid, dim3(NW * 64), 0, s, a);
   }
   if (p.nseg > 1 && (pass_mask & PASS_SCAN)) {
     if (delta) hipLaunchKernelGGL((scan_kernel<true>), dim3(DV / 4, H, B), dim3(256), 0, s, a);
