@@ -25,22 +25,23 @@
 // gfx950 layout choices.  All chunk tiles live in LDS row-major ([token][d]); operands
 // that contract over tokens (K^T, V^T, and T, which is stored transposed) are read
 // straight from those tiles with the CDNA4 transpose read ds_read_b64_tr_b16, so no
-// transposed copies are built.  A state-carrying workgroup (4 waves) uses at most ~72 KB
-// of LDS, so two workgroups share a CU and overlap their latency-bound phases (loads,
-// barriers) with each other's MFMA phases.
+// transposed copies are built.  Tiles stream from HBM into LDS with direct global-to-LDS
+// loads (buffer_load ... lds), issued one phase ahead of their use so that the loads of
+// the next chunk overlap the MFMA work of the current one.  A replay workgroup (4 waves)
+// uses 78 KB of LDS, so two share a CU.
 //
 // Sequence parallelism.  One workgroup owns the whole 128 x 128 state of one (b, h),
 // split over its 4 waves (32 state rows each, in registers), and streams chunks with
 // no inter-workgroup traffic.  A long sequence is split into segments so that
 // B*H*segments fills the chip, in three passes:
-//   pass 1 (MODE_MAP)  every segment from a zero start: its end state B_seg, and for the
-//                      delta rule its d_k x d_k transition M_seg (the same chunk
-//                      recurrence run on the identity, by the second half of an 8-wave
-//                      workgroup), or the scalar log decay
-//   pass 2 (scan)      S_{i+1} = S_i M_i + B_i sequentially over segments, row-parallel
-//   pass 3 (MODE_OUT)  every segment replayed from its start state, writing o
+//   pass 1 (map_kernel)    every segment from a zero start: its end state B_seg, and for
+//                          the delta rule its d_k x d_k transition M_seg (the same chunk
+//                          recurrence run on the identity, by the second half of an 8-wave
+//                          workgroup), or the scalar log decay
+//   pass 2 (scan_kernel)   S_{i+1} = S_i M_i + B_i sequentially over segments, row-parallel
+//   pass 3 (replay_kernel) every segment replayed from its start state, writing o
 // With one segment (enough heads to fill the chip) only pass 3 runs.  For the delta rule
-// pass 0 precedes pass 1 (or pass 3 when there is one segment).
+// pass 0 (tprep_kernel) precedes pass 1 (or pass 3 when there is one segment).
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -56,27 +57,12 @@ constexpr int RPW = DV / NW;  // state rows per wave (two 16-row column tiles)
 // Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
 // would raise register pressure past what two workgroups per CU allow).
 #define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
-// Parts of a chunk's inputs (bit masks for the register prefetch).
-enum { LD_K = 1, LD_Q = 2, LD_V = 4, LD_T = 8, LD_G = 16, LD_ALL = 31 };
-#ifndef LA_CHUNK_PREFETCH_MAP
-#define LA_CHUNK_PREFETCH_MAP 31
-#endif
-#ifndef LA_CHUNK_PREFETCH_OUT
-#define LA_CHUNK_PREFETCH_OUT 0
-#endif
-
 constexpr int LDK = DK + 16;  // row-major bf16 tiles [C][DK]: K, Q, V (288-byte rows)
 constexpr int LDA = C + 16;   // bf16 [C][C]: decay-masked Q K^T, rows t, k-ordered columns
 constexpr int LDT = C + 16;   // bf16 [C][C]: T diag(beta), rows t, k-ordered columns
 
-constexpr int SZ_ROW = C * LDK * 2;
-constexpr int SZ_A = C * LDA * 2;
-constexpr int SZ_T = C * LDT * 2;
-constexpr int SZ_VEC = 5 * C * 4;
 constexpr size_t T_CHUNK = (size_t)C * C;  // bf16 elements of one stored transform
 static_assert(DK == DV, "square state");
-
-enum { MODE_MAP = 0, MODE_OUT = 1 };
 
 struct Args {
   const bf16_t *q, *k, *v, *alpha, *beta;
@@ -343,413 +329,6 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
   }
 }
 
-// Waves per workgroup: 4 (32 state rows each), or 8 for the delta-rule map pass, whose
-// workgroup carries both the 128 B rows (waves 0-3) and the 128 M rows (waves 4-7) so
-// that each chunk's tiles are loaded once for both.
-template <int MODE, bool DELTA> struct Waves {
-  static constexpr int value = (MODE == MODE_MAP && DELTA) ? 8 : NW;
-};
-
-// LDS carve-up (bytes) of the state-carrying kernels.
-template <int MODE, bool DELTA> struct Lds {
-  static constexpr bool OUT = MODE == MODE_OUT;
-  static constexpr int K = 0;
-  static constexpr int Q = SZ_ROW;                         // MODE_OUT only
-  static constexpr int V = OUT ? 2 * SZ_ROW : SZ_ROW;
-  static constexpr int TB = V + SZ_ROW;                    // delta rule only
-  static constexpr int A = DELTA ? TB + SZ_T : TB;         // MODE_OUT only
-  static constexpr int VEC = OUT ? A + SZ_A : (DELTA ? TB + SZ_T : TB);
-  static constexpr int SIZE = VEC + SZ_VEC;
-};
-
-template <int MODE, bool DELTA>
-__global__ __launch_bounds__((Waves<MODE, DELTA>::value * 64), 2) void chunk_kernel(const Args a) {
-  constexpr bool OUT = MODE == MODE_OUT;
-  constexpr int NWT = Waves<MODE, DELTA>::value;  // waves in this workgroup
-  constexpr int NT = NWT * 64;
-  constexpr int NLD = C * (DK / 8) / NT;           // 16-byte tile loads per thread
-  constexpr int NLT = C * (C / 8) / NT;            // 16-byte TB loads per thread
-  constexpr int MAPROWS = DELTA ? 2 * DV : DV;
-  // The parts of the next chunk loaded into registers while the current one is processed
-  // (as many as the registers allow).
-  constexpr int PF = OUT ? LA_CHUNK_PREFETCH_OUT : LA_CHUNK_PREFETCH_MAP;
-  typedef Lds<MODE, DELTA> LY;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LY::SIZE];
-  bf16_t *sK = reinterpret_cast<bf16_t *>(smem + LY::K);
-  bf16_t *sQ = reinterpret_cast<bf16_t *>(smem + LY::Q);
-  bf16_t *sV = reinterpret_cast<bf16_t *>(smem + LY::V);
-  bf16_t *sT = reinterpret_cast<bf16_t *>(smem + LY::TB);
-  bf16_t *sA = reinterpret_cast<bf16_t *>(smem + LY::A);
-  float *sG = reinterpret_cast<float *>(smem + LY::VEC);
-  float *sBeta = sG + C;
-  float *sGam = sG + 2 * C;
-  float *sDec = sG + 3 * C;
-
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int l16 = lane & 15, g = lane >> 4;
-  // in the delta-rule map pass, waves 4-7 carry the transition (M) rows
-  const bool m_kind = (MODE == MODE_MAP) && DELTA && wave >= NW;
-  const int wr = m_kind ? wave - NW : wave;  // wave index within its row set
-  const int seg = (int)blockIdx.x;
-  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
-  const int64_t T = a.T;
-  const int row0 = wr * RPW;  // first state row owned by this wave
-
-  // ---- state: lane holds S^T[d = sd(m, g) + e][row0 + srow(c, l16)] in st[m][c][e]
-  f32x4 st[DK / 16][2];
-  {
-    const float *src = nullptr;
-    if (OUT) src = a.nseg > 1 ? a.starts + (bh * a.nseg + seg) * DV * DK : (a.S0 ? a.S0 + bh * DV * DK : nullptr);
-#pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r = row0 + srow(c, l16);
-        if (src) {
-          st[m][c] = ld4(src + (size_t)r * DK + sd(m, g));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)  // identity for the transition rows, zero otherwise
-            st[m][c][e] = (m_kind && r == sd(m, g) + e) ? 1.0f : 0.0f;
-        }
-      }
-  }
-
-  float gseg = 0.0f;  // log decay over the segment (scalar-gated map)
-  const int64_t first = (int64_t)seg * a.seg_chunks * C;
-  int nchunks = a.seg_chunks;
-  if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
-
-  // One chunk's tiles in registers (16-byte pieces of K, Q, V and TB per thread) and its
-  // gates (wave 0).  The parts in PF are loaded one chunk ahead, the rest at the start of
-  // the chunk.
-  u32x4 pk[NLD], pq[NLD], pv[NLD], pt[NLT > 0 ? NLT : 1];
-  float pal = 1.0f, pbe = 0.0f;
-#define LA_LOAD(T0, N, MASK)                                                                       \
-  do {                                                                                             \
-    const int64_t lt0 = (T0);                                                                      \
-    const uint32_t ln = (uint32_t)(N);                                                             \
-    const size_t rb = bh * (size_t)T + lt0;                                                        \
-    const rsrc_t rk = make_rsrc(a.k + rb * DK, ln * DK * 2);                                       \
-    const rsrc_t rq = make_rsrc(OUT ? a.q + rb * DK : a.k, OUT ? ln * DK * 2 : 0);                 \
-    const rsrc_t rv = make_rsrc(a.v + rb * DV, ln * DV * 2);                                       \
-    _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                              \
-      const uint32_t off = 16u * (uint32_t)(tid + NT * i);                                         \
-      if ((MASK) & LD_K) pk[i] = bld16(rk, off);                                                   \
-      if (OUT && ((MASK) & LD_Q)) pq[i] = bld16(rq, off);                                          \
-      if ((MASK) & LD_V) pv[i] = bld16(rv, off);                                                   \
-    }                                                                                              \
-    if (DELTA && ((MASK) & LD_T)) {                                                                \
-      const rsrc_t rt = make_rsrc(a.tb + (bh * a.nch + (size_t)(lt0 / C)) * T_CHUNK, T_CHUNK * 2); \
-      _Pragma("unroll") for (int i = 0; i < NLT; ++i) pt[i] = bld16(rt, 16u * (uint32_t)(tid + NT * i)); \
-    }                                                                                              \
-    if ((MASK) & LD_G) {                                                                           \
-      pal = 1.0f;                                                                                  \
-      pbe = (uint32_t)lane < ln ? 1.0f : 0.0f;                                                     \
-      if (wave == 0) {                                                                             \
-        if (a.variant != V_ADDITIVE) {                                                             \
-          const float x = bf16_to_f32(bld2(make_rsrc(a.alpha + rb, ln * 2), 2u * lane));           \
-          pal = (uint32_t)lane < ln ? x : 1.0f;                                                    \
-        }                                                                                          \
-        if (a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta))                    \
-          pbe = bf16_to_f32(bld2(make_rsrc(a.beta + rb, ln * 2), 2u * lane));                      \
-      }                                                                                            \
-    }                                                                                              \
-  } while (0)
-  if (PF && nchunks > 0) LA_LOAD(first, (int)((T - first) < C ? (T - first) : C), PF);
-
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int64_t t0 = first + (int64_t)ci * C;
-    const int n = (int)((T - t0) < C ? (T - t0) : C);
-    // An opaque copy of the lane index: LDS addresses derived from it are recomputed per
-    // chunk (a few integer ops) instead of being hoisted out of the loop, where dozens
-    // of them would occupy registers for the whole kernel.
-    int lane_v = lane;
-    asm volatile("" : "+v"(lane_v));
-    const int l16 = lane_v & 15, g = lane_v >> 4;
-
-    // ---- phase A: move this chunk's tiles (loaded into registers during the previous
-    // chunk when prefetching) to LDS, gate prefix sums
-    if (PF != LD_ALL) LA_LOAD(t0, n, LD_ALL & ~PF);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int id = tid + NT * i, r = id >> 4, cv = id & 15;
-      *reinterpret_cast<u32x4 *>(sK + r * LDK + cv * 8) = pk[i];
-      if (OUT) *reinterpret_cast<u32x4 *>(sQ + r * LDK + cv * 8) = pq[i];
-      *reinterpret_cast<u32x4 *>(sV + r * LDK + cv * 8) = pv[i];
-    }
-    if (DELTA) {
-#pragma unroll
-      for (int i = 0; i < NLT; ++i) {
-        const int id = tid + NT * i, r = id >> 3, cv = id & 7;
-        *reinterpret_cast<u32x4 *>(sT + r * LDT + cv * 8) = pt[i];
-      }
-    }
-    if (wave == 0) {
-      float x = (a.variant == V_ADDITIVE) ? 0.0f : log2f(pal);  // gates in log2 units
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-      }
-      const float gC = __shfl(x, 63, 64);
-      sG[lane] = x;
-      sBeta[lane] = pbe;
-      sGam[lane] = exp2_hw(x);
-      sDec[lane] = exp2_hw(gC - x);
-    }
-    __syncthreads();
-
-    // ---- phase B (replay): the decay-masked Q K^T, which does not need the state
-    if (PF && ci + 1 < nchunks) {
-      const int64_t nt0 = t0 + C;
-      LA_LOAD(nt0, (int)((T - nt0) < C ? (T - nt0) : C), PF);
-    }
-    if (OUT) {
-      // decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the waves, each
-      // computed as its transpose K Q^T: lane (g, l16) holds A[t][j] for token t = 16 ti + l16
-      // and keys j = 16 tj + 4 g + 0..3, stored in row t at the positions of the MFMA k
-      // order (j = 32 s + 16 h + 4 q + e at 32 s + 8 q + 4 h + e), one 8-byte write
-#pragma unroll
-      for (int m = 0; m < 3; ++m) {
-        const int job = wave + NWT * m;
-        if (job < 10) {
-          int ti, tj;
-          tri_index(job, ti, tj);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < DK / 32; ++s) {
-            const bf16x8 fk = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
-            const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
-            acc = mfma_bf16(fk, fq, acc);
-          }
-          const int t = 16 * ti + l16;
-          const float gt = sG[t];
-          const f32x4 gj = ld4(sG + 16 * tj + 4 * g);
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (16 * tj + 4 * g + e <= t) ? exp2_hw(gt - gj[e]) * acc[e] : 0.0f;
-          *reinterpret_cast<bf16x4 *>(sA + t * LDA + 32 * (tj >> 1) + 8 * g + 4 * (tj & 1)) =
-              bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-        }
-      }
-      // the two above-diagonal tiles read by the A U products: A (0,1) and (2,3)
-      if (tid < 128) {
-        const int tile = tid >> 6, e = tid & 63;
-        *reinterpret_cast<uint2 *>(sA + (32 * tile + (e >> 2)) * LDA + 32 * tile + 8 * (e & 3) + 4) = make_uint2(0u, 0u);
-      }
-    }
-
-    // ---- phase F: the state-dependent part, per wave on its own 32 state rows
-    // O^T = S Q^T diag(gamma) + U^T A^T (replay) on the chunk's entering state: lane
-    // (g, l16) of tile (mt, c) holds O[16 mt + l16][row0 + 8 g + 4 c + e]: with both tiles,
-    // eight consecutive outputs of one token, stored straight to HBM (16 bytes; rows past
-    // the chunk are dropped).
-    f32x4 U[4][2], O[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) O[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
-    if (DELTA) {
-      // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T on this wave's rows, in the
-      // replay together with Q S^T (one packing of the state serves both; K and Q row
-      // fragments read two steps ahead), Y = V - gamma . K S^T in registers (V read along
-      // tokens; the transition rows of the map pass have no V), then the lower-triangular
-      // product with TB.  No W is formed.
-      f32x4 ks[4][2];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#define LA_KF(it) *reinterpret_cast<const bf16x8 *>(sK + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
-      {
-        bf16x8 kf[3], qf[3], sfr[2];
-        kf[0] = LA_KF(0);
-        kf[1] = LA_KF(1);
-        if (OUT) {
-          qf[0] = LA_QF(0);
-          qf[1] = LA_QF(1);
-        }
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          const int s = it / 4, mt = it % 4;
-          if (it + 2 < 16) {
-            kf[(it + 2) % 3] = LA_KF(it + 2);
-            if (OUT) qf[(it + 2) % 3] = LA_QF(it + 2);
-          }
-          if (mt == 0) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
-          }
-          LA_FENCE();
-#pragma unroll
-          for (int c = 0; c < 2; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
-          if (OUT) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qf[it % 3], O[mt][c]);
-          }
-        }
-      }
-#undef LA_KF
-      LA_FENCE();
-      bf16x8 yfr[2][2];  // Y as an operand with k = tokens, [c][s]
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const f32x4 ga = ld4(sGam + 32 * s + 4 * g), gb = ld4(sGam + 32 * s + 16 + 4 * g);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
-          if (!m_kind) {
-            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s, lane_v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              y0[e] += (float)vf[e];
-              y1[e] += (float)vf[4 + e];
-            }
-          }
-          yfr[c][s] = pack_pair(y0, y1);
-        }
-      }
-      // steps (mt, s), s = 1 only for mt >= 2 (T is lower triangular); the TB fragment of
-      // the next step is read before this step's MFMAs
-      bf16x8 tfb[2];
-#define LA_TF(mt, s) *reinterpret_cast<const bf16x8 *>(sT + (16 * (mt) + l16) * LDT + 32 * (s) + 8 * g)
-      tfb[0] = LA_TF(0, 0);
-#pragma unroll
-      for (int it = 0; it < 6; ++it) {
-        const int mt = it < 2 ? it : 2 + (it - 2) / 2, s = it < 2 ? 0 : (it - 2) % 2;
-        if (it + 1 < 6) {
-          const int it1 = it + 1;
-          const int mt1 = it1 < 2 ? it1 : 2 + (it1 - 2) / 2, s1 = it1 < 2 ? 0 : (it1 - 2) % 2;
-          tfb[it1 & 1] = LA_TF(mt1, s1);
-        }
-        LA_FENCE();
-        if (s == 0) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
-      }
-#undef LA_TF
-    }
-    LA_FENCE();
-    bf16x8 ufr[2][2], dufr[2][2];  // U and diag(decay) U as operands with k = tokens
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const f32x4 d0 = ld4(sDec + 32 * s2 + 4 * g), d1 = ld4(sDec + 32 * s2 + 16 + 4 * g);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x4 u0, u1;
-        if (DELTA) {
-          u0 = U[2 * s2][c];
-          u1 = U[2 * s2 + 1][c];
-        } else {  // U = diag(beta) V, read along tokens from the V tile
-          const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s2, lane_v);
-          const f32x4 b0 = ld4(sBeta + 32 * s2 + 4 * g), b1 = ld4(sBeta + 32 * s2 + 16 + 4 * g);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            u0[e] = (float)vf[e] * b0[e];
-            u1[e] = (float)vf[4 + e] * b1[e];
-          }
-        }
-        ufr[c][s2] = pack_pair(u0, u1);
-        dufr[c][s2] = pack_pair(u0 * d0, u1 * d1);
-      }
-    }
-    if (OUT) {
-      if (!DELTA) {  // Q S^T (the delta rule formed it with K S^T); Q fragments two steps ahead
-        bf16x8 qb[3], sfr[2];
-        qb[0] = LA_QF(0);
-        qb[1] = LA_QF(1);
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-          const int s = it / 4, mt = it % 4;
-          if (it + 2 < 16) qb[(it + 2) % 3] = LA_QF(it + 2);
-          if (mt == 0) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
-          }
-          LA_FENCE();
-#pragma unroll
-          for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qb[it % 3], O[mt][c]);
-        }
-      }
-#undef LA_QF
-      __syncthreads();  // every wave's A tiles are in LDS; A fragments one step ahead
-      const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
-#define LA_AF(it) *reinterpret_cast<const bf16x8 *>(sA + (16 * ((it) < 2 ? (it) : 2 + ((it) - 2) / 2) + l16) * LDA + 32 * ((it) < 2 ? 0 : ((it) - 2) % 2) + 8 * g)
-      bf16x8 ab[2];
-      ab[0] = LA_AF(0);
-#pragma unroll
-      for (int it = 0; it < 6; ++it) {
-        const int mt = it < 2 ? it : 2 + (it - 2) / 2, s2 = it < 2 ? 0 : (it - 2) % 2;
-        if (it + 1 < 6) ab[(it + 1) & 1] = LA_AF(it + 1);
-        if (s2 == 0) {
-          const float gam = sGam[16 * mt + l16];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) O[mt][c] = O[mt][c] * gam;
-        }
-        LA_FENCE();
-#pragma unroll
-        for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], ab[it & 1], O[mt][c]);
-        if (mt < 2 || s2 == 1)  // token 16 mt + l16, outputs row0 + 8 g .. +7
-          bst16(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 8 * g),
-                __builtin_bit_cast(u32x4, pack_pair(O[mt][0], O[mt][1])));
-      }
-#undef LA_AF
-    }
-    {  // S^T <- gamma_C S^T + K^T diag(decay) U; K fragments read one step ahead
-      const float gC = sGam[C - 1];
-      gseg += sG[C - 1];
-      bf16x8 kb[2][2];
-      kb[0][0] = kstate_frag(sK, LDK, 0, 0, lane_v);
-      kb[0][1] = kstate_frag(sK, LDK, 0, 1, lane_v);
-#pragma unroll
-      for (int m = 0; m < DK / 16; ++m) {
-        if (m + 1 < DK / 16) {
-          kb[(m + 1) & 1][0] = kstate_frag(sK, LDK, m + 1, 0, lane_v);
-          kb[(m + 1) & 1][1] = kstate_frag(sK, LDK, m + 1, 1, lane_v);
-        }
-        LA_FENCE();
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          f32x4 acc = st[m][c] * gC;
-          acc = mfma_bf16(kb[m & 1][0], dufr[c][0], acc);
-          acc = mfma_bf16(kb[m & 1][1], dufr[c][1], acc);
-          st[m][c] = acc;
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  if (OUT) {
-    if (a.nseg == 1 && a.S_T) {
-#pragma unroll
-      for (int m = 0; m < DK / 16; ++m)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int r = row0 + srow(c, l16);
-          *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + sd(m, g)) = st[m][c];
-        }
-    }
-  } else {
-    float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
-    const int rbase = m_kind ? DV : 0;
-#pragma unroll
-    for (int m = 0; m < DK / 16; ++m)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r = rbase + row0 + srow(c, l16);
-        *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + sd(m, g)) = st[m][c];
-      }
-    if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
-  }
-#undef LA_LOAD
-}
-
 // ---------------------------------------------------------------------------------------
 // Pass 1 (segment maps), streamed through LDS with direct global-to-LDS loads: one
 // workgroup per CU (8 waves for the delta rule: B rows and M rows), so LDS has room for two
@@ -772,6 +351,15 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t off, uint32_t lds
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
                : "memory");
 }
+// 64 two-byte values (one per lane) into LDS: lane L's value lands zero-extended in the dword
+// at m0 + 4 L; lanes past the descriptor's size get zero (the range check is per element).
+__device__ __forceinline__ void lds_dma2(u32x4 rsrc, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tbuffer_load_ushort %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const void *)p);
+}
 // vmcnt(0), the other counters left alone: every global load of this wave has landed.
 __device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -784,7 +372,7 @@ __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, 
   constexpr int TOTAL = ROWS * LDB;
   static_assert(TOTAL % 1024 == 0, "whole wave-instructions");
   constexpr int NI = TOTAL / 1024;
-  const uint32_t base = (uint32_t)(size_t)(__attribute__((address_space(3))) void *)lds;
+  const uint32_t base = lds_addr(lds);
 #pragma unroll
   for (int j0 = 0; j0 < NI; j0 += NWAVES) {
     const int j = j0 + wave;
@@ -792,7 +380,7 @@ __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, 
       const int p = 1024 * j + 16 * lane;
       const int row = p / LDB, off = p - row * LDB;
       const uint32_t src = off < ROWB ? (uint32_t)(row * ROWB + off) : 0xFFFFFFF0u;
-      lds_dma16(r, src, __builtin_amdgcn_readfirstlane(base + 1024u * (uint32_t)j));
+      lds_dma16(r, src, base + 1024u * (uint32_t)j);
     }
   }
 }
@@ -821,6 +409,7 @@ __global__ __launch_bounds__((DELTA ? 8 : 4) * 64, 2) void map_kernel(const Args
   __shared__ __attribute__((aligned(16))) bf16_t sK0[C * LDK], sK1[C * LDK], sV0[C * LDK], sV1[C * LDK];
   __shared__ __attribute__((aligned(16))) bf16_t sT0[DELTA ? C * LDT : 8], sT1[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) float sGw[NWT][3 * C];
+  __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][2][C];  // per copy: raw alpha, beta
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -847,8 +436,8 @@ __global__ __launch_bounds__((DELTA ? 8 : 4) * 64, 2) void map_kernel(const Args
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
   float gseg = 0.0f;
 
-  // chunk ci's tiles into one LDS copy (untracked DMA), its raw gate values into registers
-  auto issue = [&](int ci, bf16_t *dK, bf16_t *dV, bf16_t *dT, uint32_t &ral, uint32_t &rbe) {
+  // chunk ci's tiles and raw gate values into one LDS copy
+  auto issue = [&](int ci, bf16_t *dK, bf16_t *dV, bf16_t *dT, uint32_t *dG) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
@@ -857,16 +446,16 @@ __global__ __launch_bounds__((DELTA ? 8 : 4) * 64, 2) void map_kernel(const Args
     if (DELTA)
       dma_tile<C * 2, LDT * 2, C, NWT>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
                                        (unsigned char *)dT, wave, lane);
-    if (!additive) ral = bld2(make_rsrc(a.alpha + rb, n * 2), 2u * lane);
-    if (use_beta) rbe = bld2(make_rsrc(a.beta + rb, n * 2), 2u * lane);
+    if (wave == 0 && !additive) lds_dma2(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(dG));
+    if (wave == 1 && use_beta) lds_dma2(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(dG + C));
   };
 
   // gates of chunk ci from its raw values (alpha = 1, beta = 0 past the sequence end)
-  auto gates = [&](int ci, uint32_t ral, uint32_t rbe) -> float {
+  auto gates = [&](int ci, const uint32_t *sG) -> float {
     const int64_t t0 = first + (int64_t)ci * C;
     const bool in = (int64_t)lane < T - t0;
-    const float al = (!additive && in) ? bf16_to_f32((bf16_t)ral) : 1.0f;
-    const float be = use_beta ? bf16_to_f32((bf16_t)rbe) : (in ? 1.0f : 0.0f);
+    const float al = (!additive && in) ? bf16_to_f32((bf16_t)sG[lane]) : 1.0f;
+    const float be = use_beta ? bf16_to_f32((bf16_t)sG[C + lane]) : (in ? 1.0f : 0.0f);
     return wave_gates(al, be, additive, gw, lane);
   };
 
@@ -992,21 +581,19 @@ __global__ __launch_bounds__((DELTA ? 8 : 4) * 64, 2) void map_kernel(const Args
 
   // Two LDS copies: chunk ci + 1 streams into one while chunk ci is processed from the
   // other.  Each barrier is preceded by a wait for this wave's own loads, so after it every
-  // wave's part of the next tile has landed; the gates are taken from their raw values
-  // right after it (they have landed too) and before the next loads are issued.
-  uint32_t ral0 = 0, rbe0 = 0, ral1 = 0, rbe1 = 0;
-  if (nchunks > 0) issue(0, sK0, sV0, sT0, ral0, rbe0);
+  // wave's part of the next chunk has landed.
+  if (nchunks > 0) issue(0, sK0, sV0, sT0, sGraw[0][0]);
   for (int ci = 0; ci < nchunks; ci += 2) {
     lds_dma_wait();
     __syncthreads();  // copy 0 holds chunk ci; every wave is done with copy 1
-    const float gC0 = gates(ci, ral0, rbe0);
-    if (ci + 1 < nchunks) issue(ci + 1, sK1, sV1, sT1, ral1, rbe1);
+    const float gC0 = gates(ci, sGraw[0][0]);
+    if (ci + 1 < nchunks) issue(ci + 1, sK1, sV1, sT1, sGraw[1][0]);
     step(sK0, sV0, sT0, gC0);
     if (ci + 1 < nchunks) {
       lds_dma_wait();
       __syncthreads();  // copy 1 holds chunk ci + 1; every wave is done with copy 0
-      const float gC1 = gates(ci + 1, ral1, rbe1);
-      if (ci + 2 < nchunks) issue(ci + 2, sK0, sV0, sT0, ral0, rbe0);
+      const float gC1 = gates(ci + 1, sGraw[1][0]);
+      if (ci + 2 < nchunks) issue(ci + 2, sK0, sV0, sT0, sGraw[0][0]);
       step(sK1, sV1, sT1, gC1);
     }
   }
@@ -1067,6 +654,333 @@ __global__ __launch_bounds__(256) void scan_kernel(const Args a) {
     __syncthreads();
   }
   if (a.S_T) *reinterpret_cast<float2 *>(a.S_T + (bh * DV + row) * DK + cp) = cur;
+}
+
+// ---------------------------------------------------------------------------------------
+// Pass 3 (replay): every segment from its start state (or the single segment from S0),
+// writing o and, with one segment, S_T.  Four waves own 32 state rows each.  Per chunk:
+//   phase 1  K S^T, Y = V - diag(gamma) K S^T and U = TB Y (delta rule), or U = diag(beta) V
+//   phase 2  the decay-masked Q K^T tiles (dealt over the waves, into LDS) and S Q^T
+//   phase 3  O = diag(gamma) Q S^T + (P . Q K^T) U, stored; S <- gamma_C S + K^T diag(dec) U
+// The tiles stream in with direct global-to-LDS loads while earlier work runs, in three
+// row buffers without extra copies: after phase 2 the Q, V and TB tiles are no longer
+// read, so the next chunk's K (into this chunk's Q buffer), V and TB are loaded during
+// phase 3; after phase 3 this chunk's K buffer is free and receives the next chunk's Q,
+// which phase 1 of that chunk covers.  Three barriers per chunk: start (K, V, TB landed;
+// previous chunk done), Q landed, A tiles written.
+// ---------------------------------------------------------------------------------------
+template <bool DELTA>
+__global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sR0[C * LDK], sR1[C * LDK], sV[C * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t sT[DELTA ? C * LDT : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];
+  __shared__ __attribute__((aligned(16))) float sGw[NW][4 * C];
+  __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][C];  // raw alpha, beta of a chunk
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int seg = (int)blockIdx.x;
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int64_t T = a.T;
+  const int row0 = wave * RPW;  // first state row owned by this wave
+  const bool additive = a.variant == V_ADDITIVE;
+  const bool use_beta = a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta);
+  // per wave: g_t (log2), gamma_t = 2^{g_t}, 2^{g_C - g_t}, beta_t
+  float *gw = sGw[wave];
+
+  // ---- state: lane holds S^T[d = sd(m, g) + e][row0 + srow(c, l16)] in st[m][c][e]
+  f32x4 st[DK / 16][2];
+  {
+    const int l16 = lane & 15, g = lane >> 4;
+    const float *src = a.nseg > 1 ? a.starts + (bh * a.nseg + seg) * DV * DK : (a.S0 ? a.S0 + bh * DV * DK : nullptr);
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        st[m][c] = src ? ld4(src + (size_t)(row0 + srow(c, l16)) * DK + sd(m, g)) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // the two above-diagonal A tiles that the A U products read, (0,1) and (2,3): zero for good
+  if (tid < 128) {
+    const int tile = tid >> 6, e = tid & 63;
+    *reinterpret_cast<uint2 *>(sA + (32 * tile + (e >> 2)) * LDA + 32 * tile + 8 * (e & 3) + 4) = make_uint2(0u, 0u);
+  }
+
+  const int64_t first = (int64_t)seg * a.seg_chunks * C;
+  int nchunks = a.seg_chunks;
+  if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
+
+  // chunk ci's K (into dK), V and TB tiles, and its raw gate values
+  auto issue_kv = [&](int ci, bf16_t *dK) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
+    const size_t rb = bh * (size_t)T + t0;
+    dma_tile<DK * 2, LDK * 2, C, NW>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
+    dma_tile<DV * 2, LDK * 2, C, NW>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)sV, wave, lane);
+    if (DELTA)
+      dma_tile<C * 2, LDT * 2, C, NW>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
+                                      (unsigned char *)sT, wave, lane);
+    if (wave == 0 && !additive) lds_dma2(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(sGraw[0]));
+    if (wave == 1 && use_beta) lds_dma2(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(sGraw[1]));
+  };
+  auto issue_q = [&](int ci, bf16_t *dQ) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
+    dma_tile<DK * 2, LDK * 2, C, NW>(rsrc_words(a.q + (bh * (size_t)T + t0) * DK, n * DK * 2), (unsigned char *)dQ,
+                                     wave, lane);
+  };
+  // gates of chunk ci from the raw values (alpha = 1, beta = 0 past the sequence end)
+  auto gates = [&](int ci) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const bool in = (int64_t)lane < T - t0;
+    const float al = (!additive && in) ? bf16_to_f32((bf16_t)sGraw[0][lane]) : 1.0f;
+    const float be = use_beta ? bf16_to_f32((bf16_t)sGraw[1][lane]) : (in ? 1.0f : 0.0f);
+    float x = additive ? 0.0f : log2f(al);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    const float gC = __shfl(x, 63, 64);
+    gw[lane] = x;
+    gw[64 + lane] = exp2_hw(x);
+    gw[128 + lane] = exp2_hw(gC - x);
+    gw[192 + lane] = be;
+  };
+
+  // one chunk: K in sK, Q in sQ; the next chunk's K goes to sQ, its Q to sK
+  auto step = [&](int ci, bf16_t *sK, bf16_t *sQ) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const int n = (int)((T - t0) < C ? (T - t0) : C);
+    const bool more = ci + 1 < nchunks;
+    lds_dma_wait();
+    __syncthreads();  // K, V, TB of chunk ci have landed; every wave is done with chunk ci - 1
+    gates(ci);
+    if (ci > 0) issue_q(ci, sQ);  // (chunk 0's Q was issued with its K)
+    // An opaque copy of the lane index: LDS addresses derived from it are recomputed per
+    // chunk (a few integer ops) instead of occupying registers for the whole kernel.
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int l16 = lane_v & 15, g = lane_v >> 4;
+
+    // ---- phase 1: U on this wave's rows, as operands with k = tokens (ufr), and with the
+    // decay to the chunk end applied (dufr)
+    bf16x8 ufr[2][2], dufr[2][2];
+    {
+      f32x4 U[4][2];
+      if (DELTA) {
+        // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T (K fragments two steps ahead),
+        // Y in registers (V read along tokens), then the lower-triangular product with TB
+        f32x4 ks[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#define LA_KF(it) *reinterpret_cast<const bf16x8 *>(sK + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
+        {
+          bf16x8 kf[3], sfr[2];
+          kf[0] = LA_KF(0);
+          kf[1] = LA_KF(1);
+#pragma unroll
+          for (int it = 0; it < 16; ++it) {
+            const int s = it / 4, mt = it % 4;
+            if (it + 2 < 16) kf[(it + 2) % 3] = LA_KF(it + 2);
+            if (mt == 0) {
+#pragma unroll
+              for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+            }
+            LA_FENCE();
+#pragma unroll
+            for (int c = 0; c < 2; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
+          }
+        }
+#undef LA_KF
+        LA_FENCE();
+        bf16x8 yfr[2][2];  // [c][s]
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const f32x4 ga = ld4(gw + 64 + 32 * s + 4 * g), gb = ld4(gw + 64 + 32 * s + 16 + 4 * g);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
+            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s, lane_v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              y0[e] += (float)vf[e];
+              y1[e] += (float)vf[4 + e];
+            }
+            yfr[c][s] = pack_pair(y0, y1);
+          }
+        }
+        // steps (mt, s), s = 1 only for mt >= 2 (T is lower triangular); the TB fragment of
+        // the next step is read before this step's MFMAs
+        bf16x8 tfb[2];
+#define LA_TF(it) *reinterpret_cast<const bf16x8 *>(sT + (16 * ((it) < 2 ? (it) : 2 + ((it) - 2) / 2) + l16) * LDT + 32 * ((it) < 2 ? 0 : ((it) - 2) % 2) + 8 * g)
+        tfb[0] = LA_TF(0);
+#pragma unroll
+        for (int it = 0; it < 6; ++it) {
+          const int mt = it < 2 ? it : 2 + (it - 2) / 2, s = it < 2 ? 0 : (it - 2) % 2;
+          if (it + 1 < 6) tfb[(it + 1) & 1] = LA_TF(it + 1);
+          LA_FENCE();
+          if (s == 0) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
+        }
+#undef LA_TF
+      } else {  // U = diag(beta) V, read along tokens from the V tile
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const f32x4 b0 = ld4(gw + 192 + 32 * s2 + 4 * g), b1 = ld4(gw + 192 + 32 * s2 + 16 + 4 * g);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s2, lane_v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              U[2 * s2][c][e] = (float)vf[e] * b0[e];
+              U[2 * s2 + 1][c][e] = (float)vf[4 + e] * b1[e];
+            }
+          }
+        }
+      }
+      LA_FENCE();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f32x4 d0 = ld4(gw + 128 + 32 * s2 + 4 * g), d1 = ld4(gw + 128 + 32 * s2 + 16 + 4 * g);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          ufr[c][s2] = pack_pair(U[2 * s2][c], U[2 * s2 + 1][c]);
+          dufr[c][s2] = pack_pair(U[2 * s2][c] * d0, U[2 * s2 + 1][c] * d1);
+        }
+      }
+    }
+    lds_dma_wait();
+    __syncthreads();  // Q of chunk ci has landed
+
+    // ---- phase 2: decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the
+    // waves, each computed as its transpose K Q^T: lane (g, l16) holds A[t][j] for token
+    // t = 16 ti + l16 and keys j = 16 tj + 4 g + 0..3, stored in row t at the positions of
+    // the MFMA k order (j = 32 s + 16 h + 4 q + e at 32 s + 8 q + 4 h + e), one 8-byte write
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const int job = wave + NW * m;
+      if (job < 10) {
+        int ti, tj;
+        tri_index(job, ti, tj);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+          const bf16x8 fk = *reinterpret_cast<const bf16x8 *>(sK + (16 * tj + l16) * LDK + 32 * s + 8 * g);
+          const bf16x8 fq = *reinterpret_cast<const bf16x8 *>(sQ + (16 * ti + l16) * LDK + 32 * s + 8 * g);
+          acc = mfma_bf16(fk, fq, acc);
+        }
+        const int t = 16 * ti + l16;
+        const float gt = gw[t];
+        const f32x4 gj = ld4(gw + 16 * tj + 4 * g);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (16 * tj + 4 * g + e <= t) ? exp2_hw(gt - gj[e]) * acc[e] : 0.0f;
+        *reinterpret_cast<bf16x4 *>(sA + t * LDA + 32 * (tj >> 1) + 8 * g + 4 * (tj & 1)) =
+            bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      }
+    }
+    // O^T = S Q^T on this wave's rows: lane (g, l16) of tile (mt, c) holds
+    // O[16 mt + l16][row0 + 8 g + 4 c + e] (Q fragments two steps ahead)
+    f32x4 O[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) O[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+#define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
+      bf16x8 qb[3], sfr[2];
+      qb[0] = LA_QF(0);
+      qb[1] = LA_QF(1);
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int s = it / 4, mt = it % 4;
+        if (it + 2 < 16) qb[(it + 2) % 3] = LA_QF(it + 2);
+        if (mt == 0) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+        }
+        LA_FENCE();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qb[it % 3], O[mt][c]);
+      }
+#undef LA_QF
+    }
+    __syncthreads();  // every wave's A tiles are written; Q, V and TB of chunk ci are no longer read
+    if (more) issue_kv(ci + 1, sQ);
+
+    // ---- phase 3: O = diag(gamma) S Q^T + U^T A^T, stored straight from the tiles: with
+    // both tiles, eight consecutive outputs of one token (16 bytes; rows past the chunk are
+    // dropped); A fragments one step ahead
+    {
+      const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
+#define LA_AF(it) *reinterpret_cast<const bf16x8 *>(sA + (16 * ((it) < 2 ? (it) : 2 + ((it) - 2) / 2) + l16) * LDA + 32 * ((it) < 2 ? 0 : ((it) - 2) % 2) + 8 * g)
+      bf16x8 ab[2];
+      ab[0] = LA_AF(0);
+#pragma unroll
+      for (int it = 0; it < 6; ++it) {
+        const int mt = it < 2 ? it : 2 + (it - 2) / 2, s2 = it < 2 ? 0 : (it - 2) % 2;
+        if (it + 1 < 6) ab[(it + 1) & 1] = LA_AF(it + 1);
+        if (s2 == 0) {
+          const float gam = gw[64 + 16 * mt + l16];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) O[mt][c] = O[mt][c] * gam;
+        }
+        LA_FENCE();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], ab[it & 1], O[mt][c]);
+        if (mt < 2 || s2 == 1)  // token 16 mt + l16, outputs row0 + 8 g .. +7
+          bst16(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 8 * g),
+                __builtin_bit_cast(u32x4, pack_pair(O[mt][0], O[mt][1])));
+      }
+#undef LA_AF
+    }
+    {  // S^T <- gamma_C S^T + K^T diag(decay) U; K fragments read one step ahead
+      const float gC = gw[64 + C - 1];
+      bf16x8 kb[2][2];
+      kb[0][0] = kstate_frag(sK, LDK, 0, 0, lane_v);
+      kb[0][1] = kstate_frag(sK, LDK, 0, 1, lane_v);
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m) {
+        if (m + 1 < DK / 16) {
+          kb[(m + 1) & 1][0] = kstate_frag(sK, LDK, m + 1, 0, lane_v);
+          kb[(m + 1) & 1][1] = kstate_frag(sK, LDK, m + 1, 1, lane_v);
+        }
+        LA_FENCE();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x4 acc = st[m][c] * gC;
+          acc = mfma_bf16(kb[m & 1][0], dufr[c][0], acc);
+          acc = mfma_bf16(kb[m & 1][1], dufr[c][1], acc);
+          st[m][c] = acc;
+        }
+      }
+    }
+  };
+
+  if (nchunks > 0) {
+    issue_kv(0, sR0);
+    issue_q(0, sR1);
+  }
+  for (int ci = 0; ci < nchunks; ci += 2) {
+    step(ci, sR0, sR1);
+    if (ci + 1 < nchunks) step(ci + 1, sR1, sR0);
+  }
+
+  if (a.nseg == 1 && a.S_T) {
+    const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int r = row0 + srow(c, l16);
+        *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + sd(m, g)) = st[m][c];
+      }
+  }
 }
 
 struct Plan {
@@ -1180,8 +1094,8 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
     else hipLaunchKernelGGL((scan_kernel<false>), dim3(DV / 4, H, B), dim3(256), 0, s, a);
   }
   if (pass_mask & PASS_REPLAY) {
-    if (delta) hipLaunchKernelGGL((chunk_kernel<MODE_OUT, true>), grid, dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((chunk_kernel<MODE_OUT, false>), grid, dim3(NTHR), 0, s, a);
+    if (delta) hipLaunchKernelGGL((replay_kernel<true>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((replay_kernel<false>), grid, dim3(NTHR), 0, s, a);
   }
   return hipGetLastError();
 }
