@@ -34,12 +34,13 @@
 // split over its 4 waves (32 state rows each, in registers), and streams chunks with
 // no inter-workgroup traffic.  A long sequence is split into segments so that
 // B*H*segments fills the chip, in three passes:
-//   pass 1 (map_kernel)    every segment from a zero start: its end state B_seg, and for
-//                          the delta rule its d_k x d_k transition M_seg (the same chunk
-//                          recurrence run on the identity, by the second half of an 8-wave
-//                          workgroup), or the scalar log decay
-//   pass 2 (scan_kernel)   S_{i+1} = S_i M_i + B_i sequentially over segments, row-parallel
-//   pass 3 (replay_kernel) every segment replayed from its start state, writing o
+//   pass 1 (map_kernel)    every segment but the last from a zero start: its end state
+//                          B_seg, and for the delta rule its d_k x d_k transition M_seg
+//                          (the same chunk recurrence run on the identity, by the second
+//                          half of an 8-wave workgroup), or the scalar log decay
+//   pass 2 (scan_*_kernel) S_{i+1} = S_i M_i + B_i sequentially over segments (fp32 MFMA)
+//   pass 3 (replay_kernel) every segment replayed from its start state, writing o; the
+//                          last segment also writes S_T
 // With one segment (enough heads to fill the chip) only pass 3 runs.  For the delta rule
 // pass 0 (tprep_kernel) precedes pass 1 (or pass 3 when there is one segment).
 #include "la_device.h"
@@ -610,50 +611,88 @@ __global__ __launch_bounds__((DELTA ? 8 : 4) * 64, 2) void map_kernel(const Args
   if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
 }
 
-// Pass 2: S_{i+1} = S_i M_i + B_i (delta rule) or e^{gsum_i} S_i + B_i, row-parallel:
-// each workgroup carries 4 rows of one head's state through all segments.
-template <bool DELTA>
-__global__ __launch_bounds__(256) void scan_kernel(const Args a) {
-  constexpr int MAPROWS = DELTA ? 2 * DV : DV;
-  __shared__ float sS[4][DK];
-  const int tid = threadIdx.x, rr = tid >> 6, cp = 2 * (tid & 63);
-  const int row = blockIdx.x * 4 + rr;
+// Pass 2 (delta rule): segment start states S_{i+1} = S_i M_i + B_i for i = 0 .. nseg - 2,
+// with S_0 = S0 (the last segment's map is never needed: its replay writes S_T).  One
+// workgroup per (b, h) and block of 16 state rows, 8 waves; wave w forms output columns
+// 16 w .. 16 w + 15 transposed, (S M + B)^T = M^T S^T + B^T, on fp32 MFMA (16x16x4: exact
+// fp32 products, so the scan adds no rounding beyond fp32 accumulation).  A k-step pairs
+// lane group g with key 16 c + 4 g + e (c = 0..7, e = 0..3): the A operand is then row
+// 16 c + 4 g + e of M read along 16 consecutive columns, and the B operand S[row][16 c +
+// 4 g + e] is what wave c's accumulator held (lane (g, i) of a tile holds rows i, columns
+// 16 w + 4 g + 0..3), exchanged through a double-buffered LDS copy of the 16 rows: one
+// barrier per segment.  Maps are loaded into registers two segments ahead.
+constexpr int SCAN_ROWS = 16;
+constexpr int LDSS = DK + 4;  // fp32 row stride of the LDS state block
+__global__ __launch_bounds__(512) void scan_delta_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) float sS[2][SCAN_ROWS * LDSS];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * SCAN_ROWS;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
-  float2 cur = make_float2(0.f, 0.f);
-  if (a.S0) cur = *reinterpret_cast<const float2 *>(a.S0 + (bh * DV + row) * DK + cp);
-  sS[rr][cp] = cur.x;
-  sS[rr][cp + 1] = cur.y;
-  __syncthreads();
-  for (int i = 0; i < a.nseg; ++i) {
-    *reinterpret_cast<float2 *>(a.starts + ((bh * a.nseg + i) * DV + row) * DK + cp) = cur;
-    const float *Mb = a.maps + (bh * a.nseg + i) * (size_t)MAPROWS * DK;
-    float2 acc = *reinterpret_cast<const float2 *>(Mb + (size_t)row * DK + cp);
-    if (DELTA) {
-      float2 acc2 = make_float2(0.f, 0.f);
-#pragma unroll 8
-      for (int kq = 0; kq < DK; kq += 2) {
-        const float2 m0 = *reinterpret_cast<const float2 *>(Mb + (size_t)(DV + kq) * DK + cp);
-        const float2 m1 = *reinterpret_cast<const float2 *>(Mb + (size_t)(DV + kq + 1) * DK + cp);
-        const float s0 = sS[rr][kq], s1 = sS[rr][kq + 1];
-        acc.x += s0 * m0.x;
-        acc.y += s0 * m0.y;
-        acc2.x += s1 * m1.x;
-        acc2.y += s1 * m1.y;
-      }
-      acc.x += acc2.x;
-      acc.y += acc2.y;
-    } else {
-      const float dec = exp2f(a.gsum[bh * a.nseg + i]);
-      acc.x += dec * cur.x;
-      acc.y += dec * cur.y;
-    }
-    __syncthreads();
-    sS[rr][cp] = acc.x;
-    sS[rr][cp + 1] = acc.y;
-    cur = acc;
-    __syncthreads();
+  const int nseg = a.nseg;
+  {  // S_0: 16 rows x 128 columns, 16 bytes per thread
+    const int r = tid >> 5, c4 = 4 * (tid & 31);
+    const f32x4 x = a.S0 ? ld4(a.S0 + (bh * DV + row0 + r) * DK + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4 *>(sS[0] + r * LDSS + c4) = x;
+    *reinterpret_cast<f32x4 *>(a.starts + ((bh * nseg) * DV + row0 + r) * DK + c4) = x;
   }
-  if (a.S_T) *reinterpret_cast<float2 *>(a.S_T + (bh * DV + row) * DK + cp) = cur;
+  const int col = 16 * wave + i16;  // output column of this lane's A-operand row
+  // segment i's map in registers, two segments ahead: M[16 c + 4 g + e][col] at 4 c + e,
+  // and B[row0 + i16][16 wave + 4 g + 0..3]
+  float mA[2][32];
+  f32x4 bC[2];
+  auto load = [&](int i, float *m, f32x4 &b) {
+    const float *Mb = a.maps + (bh * nseg + i) * (size_t)(2 * DV * DK);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[4 * c + e] = Mb[(size_t)(DV + 16 * c + 4 * g + e) * DK + col];
+    b = ld4(Mb + (size_t)(row0 + i16) * DK + 16 * wave + 4 * g);
+  };
+  auto step = [&](int i, float *m, f32x4 &b) {
+    const float *cur = sS[i & 1];
+    float *nxt = sS[(i + 1) & 1];
+    f32x4 acc0 = b, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const f32x4 sv = ld4(cur + i16 * LDSS + 16 * c + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[4 * c + e], sv[e], acc1, 0, 0, 0);
+        else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[4 * c + e], sv[e], acc0, 0, 0, 0);
+      }
+    }
+    load(i + 2 < nseg - 1 ? i + 2 : nseg - 2, m, b);  // unconditional, so the waits stay exact
+    const f32x4 nx = acc0 + acc1;
+    *reinterpret_cast<f32x4 *>(nxt + i16 * LDSS + 16 * wave + 4 * g) = nx;
+    *reinterpret_cast<f32x4 *>(a.starts + ((bh * nseg + i + 1) * DV + row0 + i16) * DK + 16 * wave + 4 * g) = nx;
+    __syncthreads();
+  };
+  __syncthreads();
+  if (nseg < 2) return;
+  load(0, mA[0], bC[0]);
+  load(nseg > 2 ? 1 : 0, mA[1], bC[1]);
+  int i = 0;
+  for (; i + 2 < nseg; i += 2) {  // segments i and i + 1 both have a successor
+    step(i, mA[0], bC[0]);
+    step(i + 1, mA[1], bC[1]);
+  }
+  if (i + 1 < nseg) step(i, mA[0], bC[0]);
+}
+
+// Pass 2 (scalar gates): S_{i+1} = 2^{gsum_i} S_i + B_i for i = 0 .. nseg - 2, elementwise;
+// each thread carries 4 consecutive elements of one state row.
+__global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
+  const int row = blockIdx.x * 8 + (threadIdx.x >> 5), c4 = 4 * (threadIdx.x & 31);
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int nseg = a.nseg;
+  f32x4 cur = a.S0 ? ld4(a.S0 + (bh * DV + row) * DK + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  *reinterpret_cast<f32x4 *>(a.starts + ((bh * nseg) * DV + row) * DK + c4) = cur;
+  for (int i = 0; i + 1 < nseg; ++i) {
+    const f32x4 b = ld4(a.maps + ((bh * nseg + i) * DV + row) * (size_t)DK + c4);
+    cur = exp2f(a.gsum[bh * nseg + i]) * cur + b;
+    *reinterpret_cast<f32x4 *>(a.starts + ((bh * nseg + i + 1) * DV + row) * DK + c4) = cur;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -971,7 +1010,7 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     if (ci + 1 < nchunks) step(ci + 1, sR1, sR0);
   }
 
-  if (a.nseg == 1 && a.S_T) {
+  if (seg == a.nseg - 1 && a.S_T) {  // the last segment ends the sequence
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
@@ -1086,12 +1125,14 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
     hipLaunchKernelGGL(tprep_kernel, dim3((unsigned)((chunks + NW - 1) / NW)), dim3(NTHR), 0, s, a);
   }
   if (p.nseg > 1 && (pass_mask & PASS_MAPS)) {
-    if (delta) hipLaunchKernelGGL((map_kernel<true>), grid, dim3(8 * 64), 0, s, a);
-    else hipLaunchKernelGGL((map_kernel<false>), grid, dim3(NW * 64), 0, s, a);
+    // every segment but the last (whose end state only the replay needs)
+    const dim3 mgrid(p.nseg - 1, H, B);
+    if (delta) hipLaunchKernelGGL((map_kernel<true>), mgrid, dim3(8 * 64), 0, s, a);
+    else hipLaunchKernelGGL((map_kernel<false>), mgrid, dim3(NW * 64), 0, s, a);
   }
   if (p.nseg > 1 && (pass_mask & PASS_SCAN)) {
-    if (delta) hipLaunchKernelGGL((scan_kernel<true>), dim3(DV / 4, H, B), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((scan_kernel<false>), dim3(DV / 4, H, B), dim3(256), 0, s, a);
+    if (delta) hipLaunchKernelGGL(scan_delta_kernel, dim3(DV / SCAN_ROWS, H, B), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL(scan_gated_kernel, dim3(DV / 8, H, B), dim3(256), 0, s, a);
   }
   if (pass_mask & PASS_REPLAY) {
     if (delta) hipLaunchKernelGGL((replay_kernel<true>), grid, dim3(NTHR), 0, s, a);

@@ -146,11 +146,12 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
  *   LA_PASS_TRANSFORM  gated delta rule on the chunked path: every chunk's UT transform
  *                      (I + L)^{-1} diag(beta), which depends on keys and gates only,
  *                      written to the workspace for the two passes that follow
- *   LA_PASS_MAPS       per segment of chunks, the affine map of its end state on its
- *                      start state (S_end = S_start M + B; M is d_k x d_k for the gated
- *                      delta rule, a scalar decay otherwise), written to the workspace
- *   LA_PASS_SCAN       segment start states S_{i+1} = S_i M_i + B_i from S0, and S_T
- *   LA_PASS_REPLAY     every segment from its start state: o (and S_T for one segment)
+ *   LA_PASS_MAPS       per segment of chunks except the last, the affine map of its end
+ *                      state on its start state (S_end = S_start M + B; M is d_k x d_k
+ *                      for the gated delta rule, a scalar decay otherwise), written to
+ *                      the workspace
+ *   LA_PASS_SCAN       segment start states S_{i+1} = S_i M_i + B_i from S0
+ *   LA_PASS_REPLAY     every segment from its start state: o, and S_T from the last one
  *
  * Passes that do not apply to a problem (one segment, no delta rule, fp32 inputs, other
  * widths) do nothing; LA_PASS_REPLAY then performs the rest of the computation.
