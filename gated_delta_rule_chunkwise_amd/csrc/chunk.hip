@@ -62,7 +62,11 @@ constexpr int LDK = DK + 16;  // row-major bf16 tiles [C][DK]: K, Q, V (288-byte
 constexpr int LDA = C + 16;   // bf16 [C][C]: decay-masked Q K^T, rows t, k-ordered columns
 constexpr int LDT = C + 16;   // bf16 [C][C]: T diag(beta), rows t, k-ordered columns
 
-constexpr size_t T_CHUNK = (size_t)C * C;  // bf16 elements of one stored transform
+// A stored transform, T diag(beta) in bf16, row-major in the MFMA k order: rows 0..31 keep
+// only their first 32 positions (the blocks right of the diagonal are zero), rows 32..63 all
+// 64: 6 KB per chunk.  tb_offset gives the element offset of row t.
+constexpr size_t T_CHUNK = 32 * 32 + 32 * 64;  // bf16 elements of one stored transform
+__host__ __device__ constexpr int tb_offset(int t) { return t < 32 ? 32 * t : 1024 + 64 * (t - 32); }
 static_assert(DK == DV, "square state");
 
 struct Args {
@@ -320,12 +324,13 @@ __global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
     const f32x4 bj = ld4(L.beta + 16 * jb + 4 * grp);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (i < 2 && jb >= 2) continue;  // not stored (zero)
       f32x4 t = {0.f, 0.f, 0.f, 0.f};
       if (i == jb) t = ld4(L.d[i] + l16 * LDD + 4 * grp);  // D_i row l16
       if (i > jb) t = ttT[i * (i - 1) / 2 + jb];
       t = t * bj;
       const bf16x4 h = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-      gst8(dst + (16 * i + l16) * C + 32 * (jb >> 1) + 8 * grp + 4 * (jb & 1), __builtin_bit_cast(u32x2, h));
+      gst8(dst + tb_offset(16 * i + l16) + 32 * (jb >> 1) + 8 * grp + 4 * (jb & 1), __builtin_bit_cast(u32x2, h));
     }
   }
 }
@@ -358,6 +363,7 @@ __device__ __forceinline__ void lds_dma2(u32x4 rsrc, uint32_t off, uint32_t lds_
   asm volatile("s_nop 0\n\tbuffer_load_ushort %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
                : "memory");
 }
+// LDS byte address of a pointer into a __shared__ array, as a wave-uniform value.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const void *)p);
 }
@@ -381,6 +387,27 @@ __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, 
       const int p = 1024 * j + 16 * lane;
       const int row = p / LDB, off = p - row * LDB;
       const uint32_t src = off < ROWB ? (uint32_t)(row * ROWB + off) : 0xFFFFFFF0u;
+      lds_dma16(r, src, base + 1024u * (uint32_t)j);
+    }
+  }
+}
+
+// A stored transform (6 KB, tb_offset layout) into a row-padded LDS tile of row stride LDT:
+// 10 wave-instructions of 1 KB; LDS bytes that the stored layout omits (right of the
+// diagonal in rows 0..31) and the row padding are zero-filled.
+template <int NWAVES>
+__device__ __forceinline__ void dma_tb(u32x4 r, unsigned char *lds, int wave, int lane) {
+  constexpr int LDB = LDT * 2, NI = C * LDB / 1024;
+  static_assert(C * LDB % 1024 == 0, "whole wave-instructions");
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int j0 = 0; j0 < NI; j0 += NWAVES) {
+    const int j = j0 + wave;
+    if (j < NI) {
+      const int p = 1024 * j + 16 * lane;
+      const int row = p / LDB, off = p - row * LDB;
+      const bool kept = off < (row < 32 ? 64 : 128);
+      const uint32_t src = kept ? (uint32_t)(2 * tb_offset(row) + off) : 0xFFFFFFF0u;
       lds_dma16(r, src, base + 1024u * (uint32_t)j);
     }
   }
@@ -445,7 +472,7 @@ __global__ __launch_bounds__((DELTA ? 8 : 4) * 64, 2) void map_kernel(const Args
     dma_tile<DK * 2, LDK * 2, C, NWT>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
     dma_tile<DV * 2, LDK * 2, C, NWT>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)dV, wave, lane);
     if (DELTA)
-      dma_tile<C * 2, LDT * 2, C, NWT>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
+      dma_tb<NWT>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
                                        (unsigned char *)dT, wave, lane);
     if (wave == 0 && !additive) lds_dma2(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(dG));
     if (wave == 1 && use_beta) lds_dma2(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(dG + C));
@@ -755,7 +782,7 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     dma_tile<DK * 2, LDK * 2, C, NW>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
     dma_tile<DV * 2, LDK * 2, C, NW>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)sV, wave, lane);
     if (DELTA)
-      dma_tile<C * 2, LDT * 2, C, NW>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
+      dma_tb<NW>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
                                       (unsigned char *)sT, wave, lane);
     if (wave == 0 && !additive) lds_dma2(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(sGraw[0]));
     if (wave == 1 && use_beta) lds_dma2(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(sGraw[1]));

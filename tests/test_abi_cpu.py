@@ -126,13 +126,15 @@ def test_workspace_size_validates(lib):
 
 
 def test_workspace_holds_one_transform_per_chunk(lib):
-    """One segment per head (128 heads): the gated delta rule needs exactly one 64 x 64 bf16
-    transform per chunk and head; the gated variant needs nothing."""
+    """One segment per head (128 heads): the gated delta rule needs exactly one stored
+    transform per chunk and head (the lower-triangular 64 x 64 bf16 T diag(beta) without the
+    blocks right of the diagonal in its first 32 rows: 32 x 32 + 32 x 64 values); the gated
+    variant needs nothing."""
     n = ctypes.c_size_t(0)
     T = 64 * 100 + 5  # 101 chunks, the last partial
     assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 2, 64, T, 128, 128,
                                          ctypes.byref(n)) == 0
-    assert n.value == 2 * 64 * 101 * 64 * 64 * 2
+    assert n.value == 2 * 64 * 101 * (32 * 32 + 32 * 64) * 2
     assert lib.la_prefill_workspace_size(la.GATED, la.BF16, 2, 64, T, 128, 128,
                                          ctypes.byref(n)) == 0
     assert n.value == 0
