@@ -364,8 +364,9 @@ __device__ __forceinline__ void lds_dma2(u32x4 rsrc, uint32_t off, uint32_t lds_
                : "memory");
 }
 // LDS byte address of a pointer into a __shared__ array, as a wave-uniform value.
+// (The low 32 bits of a generic address in the LDS aperture are the LDS address itself.)
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) const void *)p);
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)p);
 }
 // vmcnt(0), the other counters left alone: every global load of this wave has landed.
 __device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -413,17 +414,36 @@ __device__ __forceinline__ void dma_tb(u32x4 r, unsigned char *lds, int wave, in
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts by 1, 2, 4, 8 (lanes
+// past the start of their 16-lane row add zero), then the broadcasts of lane 15 into rows 1
+// and 3 and of lane 31 into rows 2 and 3; no LDS round trips, a fixed order.  Written in
+// assembly with the wait states DPP needs after a VALU write of its source.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:1 bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:2 bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:4 bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_shr:8 bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc\n\t"
+      "s_nop 1"
+      : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ float lane63(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)); }
+
 // Gate prefix sums of one chunk, formed by each wave for itself: gw[0..63] = 2^{g_t},
 // gw[64..127] = 2^{g_C - g_t}, gw[128..191] = beta_t (g in log2 units, alpha = 1 and beta = 0
 // beyond the chunk).  Returns g_C.
 __device__ __forceinline__ float wave_gates(float al, float be, bool additive, float *gw, int lane) {
-  float x = additive ? 0.0f : log2f(al);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  const float gC = __shfl(x, 63, 64);
+  const float x = wave_prefix_sum(additive ? 0.0f : log2f(al));
+  const float gC = lane63(x);
   gw[lane] = exp2_hw(x);
   gw[64 + lane] = exp2_hw(gC - x);
   gw[128 + lane] = be;
@@ -799,13 +819,8 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     const bool in = (int64_t)lane < T - t0;
     const float al = (!additive && in) ? bf16_to_f32((bf16_t)sGraw[0][lane]) : 1.0f;
     const float be = use_beta ? bf16_to_f32((bf16_t)sGraw[1][lane]) : (in ? 1.0f : 0.0f);
-    float x = additive ? 0.0f : log2f(al);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    const float gC = __shfl(x, 63, 64);
+    const float x = wave_prefix_sum(additive ? 0.0f : log2f(al));
+    const float gC = lane63(x);
     gw[lane] = x;
     gw[64 + lane] = exp2_hw(x);
     gw[128 + lane] = exp2_hw(gC - x);
