@@ -370,6 +370,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 // vmcnt(0), the other counters left alone: every global load of this wave has landed.
 __device__ __forceinline__ void lds_dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// At most N of this wave's vector-memory operations still outstanding (they complete in
+// issue order): everything issued before the last N has landed.
+template <int N> __device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier that orders LDS only: global stores still in flight are not waited for
+// (the direct loads a barrier publishes are waited for explicitly before it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Fill a row-padded LDS tile (ROWS rows of ROWB bytes at a stride of LDB bytes) from ROWS
 // contiguous global rows.  Wave-instruction j writes LDS bytes [1024 j, 1024 j + 1024), lane
@@ -749,11 +762,12 @@ __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
 //   phase 2  the decay-masked Q K^T tiles (dealt over the waves, into LDS) and S Q^T
 //   phase 3  O = diag(gamma) Q S^T + (P . Q K^T) U, stored; S <- gamma_C S + K^T diag(dec) U
 // The tiles stream in with direct global-to-LDS loads while earlier work runs, in three
-// row buffers without extra copies: after phase 2 the Q, V and TB tiles are no longer
-// read, so the next chunk's K (into this chunk's Q buffer), V and TB are loaded during
-// phase 3; after phase 3 this chunk's K buffer is free and receives the next chunk's Q,
-// which phase 1 of that chunk covers.  Three barriers per chunk: start (K, V, TB landed;
-// previous chunk done), Q landed, A tiles written.
+// row buffers without extra copies: after phase 1 the V and TB tiles are no longer read, so
+// the next chunk's V and TB load during phases 2 and 3; after phase 2 the Q tile is free
+// and receives the next chunk's K; after phase 3 this chunk's K buffer is free and
+// receives the next chunk's Q, which phase 1 of that chunk covers.  Three barriers per
+// chunk (start: K, V, TB landed, previous chunk done; Q landed; A tiles written); they
+// order LDS only, so the output stores of a chunk stay in flight across them.
 // ---------------------------------------------------------------------------------------
 template <bool DELTA>
 __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
@@ -794,16 +808,22 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
 
-  // chunk ci's K (into dK), V and TB tiles, and its raw gate values
-  auto issue_kv = [&](int ci, bf16_t *dK) {
+  // chunk ci's V and TB tiles
+  auto issue_vt = [&](int ci) {
+    const int64_t t0 = first + (int64_t)ci * C;
+    const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
+    const size_t rb = bh * (size_t)T + t0;
+    dma_tile<DV * 2, LDK * 2, C, NW>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)sV, wave, lane);
+    if (DELTA)
+      dma_tb<NW>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
+                 (unsigned char *)sT, wave, lane);
+  };
+  // chunk ci's K tile (into dK) and raw gate values
+  auto issue_kg = [&](int ci, bf16_t *dK) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
     dma_tile<DK * 2, LDK * 2, C, NW>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
-    dma_tile<DV * 2, LDK * 2, C, NW>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)sV, wave, lane);
-    if (DELTA)
-      dma_tb<NW>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
-                                      (unsigned char *)sT, wave, lane);
     if (wave == 0 && !additive) lds_dma2(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(sGraw[0]));
     if (wave == 1 && use_beta) lds_dma2(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(sGraw[1]));
   };
@@ -832,8 +852,10 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     const int64_t t0 = first + (int64_t)ci * C;
     const int n = (int)((T - t0) < C ? (T - t0) : C);
     const bool more = ci + 1 < nchunks;
-    lds_dma_wait();
-    __syncthreads();  // K, V, TB of chunk ci have landed; every wave is done with chunk ci - 1
+    // all but this wave's last four operations (the output stores of chunk ci - 1, or chunk
+    // 0's Q pieces, at least four) have completed: K, V, TB and the gates of chunk ci
+    vm_wait<4>();
+    lds_barrier();  // ... for every wave; every wave is done with chunk ci - 1
     gates(ci);
     if (ci > 0) issue_q(ci, sQ);  // (chunk 0's Q was issued with its K)
     // An opaque copy of the lane index: LDS addresses derived from it are recomputed per
@@ -936,7 +958,8 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
       }
     }
     lds_dma_wait();
-    __syncthreads();  // Q of chunk ci has landed
+    lds_barrier();  // Q of chunk ci has landed; V and TB of chunk ci are no longer read
+    if (more) issue_vt(ci + 1);
 
     // ---- phase 2: decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the
     // waves, each computed as its transpose K Q^T: lane (g, l16) holds A[t][j] for token
@@ -991,8 +1014,8 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
       }
 #undef LA_QF
     }
-    __syncthreads();  // every wave's A tiles are written; Q, V and TB of chunk ci are no longer read
-    if (more) issue_kv(ci + 1, sQ);
+    lds_barrier();  // every wave's A tiles are written; Q of chunk ci is no longer read
+    if (more) issue_kg(ci + 1, sQ);
 
     // ---- phase 3: O = diag(gamma) S Q^T + U^T A^T, stored straight from the tiles: with
     // both tiles, eight consecutive outputs of one token (16 bytes; rows past the chunk are
@@ -1044,7 +1067,8 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
   };
 
   if (nchunks > 0) {
-    issue_kv(0, sR0);
+    issue_vt(0);
+    issue_kg(0, sR0);
     issue_q(0, sR1);
   }
   for (int ci = 0; ci < nchunks; ci += 2) {
