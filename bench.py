@@ -4,7 +4,8 @@
 Headline workload: gated-delta chunkwise prefill of one layer, B = 1, H = 16,
 T = 1,048,576, d_k = d_v = 128, bf16 q/k/v/alpha/beta, fp32 state, seeded synthetic
 inputs with the gated-delta recipe (synth.gdn_inputs).  One step = one complete
-la_prefill over the whole sequence (its three passes: segment maps, scan, replay).
+la_prefill over the whole sequence (its four passes: per-chunk UT transforms, segment
+maps, segment scan, replay).
 value = tokens/s, a token being one position through all 16 heads.
 
 Also measured in the same run: the batched decode step (256 sequences x 16 heads,
@@ -149,22 +150,24 @@ def main():
     alg_flops = token_heads * FLOPS_PER_TOKEN_HEAD
 
     # the dominant launch of the step, with the algorithmic bytes and FLOPs of that pass
-    # (per token-head, C = 64, d = 128; the transform is 64 x 64 bf16 per chunk = 128 B):
-    #   transform: k, alpha, beta in, the transform out (388 B); K K^T and the solve
-    #              (2 C d + C^2 / 3 FLOP)
-    #   maps:      k, v, alpha, beta, transform in (644 B); W, U~ (2 x 2 C d) and W S^T and
-    #              the state update for 256 state rows, B_seg and M_seg (4 x 2 d^2)
-    #   scan:      per segment, a 128 x 128 map and B_seg read, the start state written
-    #   replay:    q, k, v, alpha, beta, transform in, o out (1156 B); Q K^T, W, U~, A U
-    #              (4 x 2 C d) and Q S^T, W S^T, the state update (3 x 2 d^2)
+    # (per token-head, C = 64, d = 128; a stored transform is 6 KB per chunk = 96 B per token):
+    #   transform: k, alpha, beta in, the transform out (356 B); K K^T and the solve
+    #              (2 C d + C^2 / 3 FLOP); every chunk
+    #   maps:      k, v, alpha, beta, transform in (612 B); K S^T, TB Y (2 C d + C^2) and the
+    #              state update for 256 state rows, B_seg and M_seg; every segment but the last
+    #   scan:      per segment but the last, its 256 x 128 map read; every start state written;
+    #              a 128 x 128 x 128 product per segment
+    #   replay:    q, k, v, alpha, beta, transform in, o out (1124 B); Q K^T, A U, TB Y
+    #              (4 x 2 C d) and K S^T, Q S^T, the state update (3 x 2 d^2); every chunk
     dom = max(per_pass, key=per_pass.get)
-    per_th = {"transform": (128 * 2 + 2 * 2 + 128, 2 * C_ * D_ + C_ * C_ / 3),
-              "maps": (2 * 128 * 2 + 2 * 2 + 128, 2 * 2 * C_ * D_ + 4 * 2 * D_ * D_),
-              "replay": (BYTES_PER_TOKEN_HEAD + 128, 4 * 2 * C_ * D_ + 3 * 2 * D_ * D_)}
-    pass_bytes = {kk: token_heads * vv[0] for kk, vv in per_th.items()}
-    pass_flops = {kk: token_heads * vv[1] for kk, vv in per_th.items()}
-    pass_bytes["scan"] = B * H * nseg * (3 * D * D * 4)
-    pass_flops["scan"] = B * H * nseg * 2 * D * D * D
+    map_frac = (nseg - 1) / nseg
+    per_th = {"transform": (128 * 2 + 2 * 2 + 96, 2 * C_ * D_ + C_ * C_ / 3, 1.0),
+              "maps": (2 * 128 * 2 + 2 * 2 + 96, 2 * 2 * C_ * D_ + 4 * 2 * D_ * D_, map_frac),
+              "replay": (BYTES_PER_TOKEN_HEAD + 96, 4 * 2 * C_ * D_ + 3 * 2 * D_ * D_, 1.0)}
+    pass_bytes = {kk: token_heads * vv[0] * vv[2] for kk, vv in per_th.items()}
+    pass_flops = {kk: token_heads * vv[1] * vv[2] for kk, vv in per_th.items()}
+    pass_bytes["scan"] = B * H * ((nseg - 1) * 2 * D * D * 4 + nseg * D * D * 4)
+    pass_flops["scan"] = B * H * (nseg - 1) * 2 * D * D * D
     t_dom = per_pass[dom] * 1e-3
     t_hbm = pass_bytes[dom] / (HBM_PEAK_GBS * 1e9)
     t_mfma = pass_flops[dom] / (BF16_PEAK_TFLOPS * 1e12)
@@ -172,10 +175,10 @@ def main():
         ach, peak, unit, bound = pass_bytes[dom] / t_dom / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
     else:
         ach, peak, unit, bound = pass_flops[dom] / t_dom / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
-    kname = {"replay": "chunk_kernel<MODE_OUT,true> (replay pass)",
-             "maps": "chunk_kernel<MODE_MAP,true> (segment-map pass)",
+    kname = {"replay": "replay_kernel<true> (replay pass)",
+             "maps": "map_kernel<true> (segment-map pass)",
              "transform": "tprep_kernel (per-chunk UT transform pass)",
-             "scan": "scan_kernel<true> (segment scan)"}[dom]
+             "scan": "scan_delta_kernel (segment scan)"}[dom]
     roofline = {
         "bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
         "frac": round(ach / peak, 4), "traffic": read_traffic(dom), "kernel": kname,
