@@ -350,20 +350,31 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
   return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
-// One 16-byte-per-lane global-to-LDS load: lane L's 16 bytes at byte offset `off` of the
+// One 16-byte-per-lane global-to-LDS load (NT: marked non-temporal, for streams that no
+// later pass of this call re-reads soon): lane L's 16 bytes at byte offset `off` of the
 // descriptor land at LDS address m0 + 16 L (m0 = lds_base, wave-uniform).  Issued from
 // inline assembly so that the compiler does not wait for it before every later LDS read
 // (it cannot tell the two copies of a tile apart); the kernel waits for it explicitly
 // (lds_dma_wait) before the barrier that publishes the tile.
+template <bool NT>
 __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
-               : "memory");
+  if (NT)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
 }
 // 64 two-byte values (one per lane) into LDS: lane L's value lands zero-extended in the dword
 // at m0 + 4 L; lanes past the descriptor's size get zero (the range check is per element).
+template <bool NT>
 __device__ __forceinline__ void lds_dma2(u32x4 rsrc, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tbuffer_load_ushort %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
-               : "memory");
+  if (NT)
+    asm volatile("s_nop 0\n\tbuffer_load_ushort %0, %1, 0 offen nt lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_ushort %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc), "{m0}"(lds_base)
+                 : "memory");
 }
 // LDS byte address of a pointer into a __shared__ array, as a wave-uniform value.
 // (The low 32 bits of a generic address in the LDS aperture are the LDS address itself.)
@@ -390,7 +401,7 @@ __device__ __forceinline__ void lds_barrier() {
 // contiguous global rows.  Wave-instruction j writes LDS bytes [1024 j, 1024 j + 1024), lane
 // L's 16 bytes at 1024 j + 16 L; lanes that fall in the padding, or past the descriptor's
 // size (rows beyond a partial chunk), write zeros.
-template <int ROWB, int LDB, int ROWS, int NWAVES>
+template <int ROWB, int LDB, int ROWS, int NWAVES, bool NT>
 __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, int lane) {
   constexpr int TOTAL = ROWS * LDB;
   static_assert(TOTAL % 1024 == 0, "whole wave-instructions");
@@ -403,7 +414,7 @@ __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, 
       const int p = 1024 * j + 16 * lane;
       const int row = p / LDB, off = p - row * LDB;
       const uint32_t src = off < ROWB ? (uint32_t)(row * ROWB + off) : 0xFFFFFFF0u;
-      lds_dma16(r, src, base + 1024u * (uint32_t)j);
+      lds_dma16<NT>(r, src, base + 1024u * (uint32_t)j);
     }
   }
 }
@@ -411,7 +422,7 @@ __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, 
 // A stored transform (6 KB, tb_offset layout) into a row-padded LDS tile of row stride LDT:
 // 10 wave-instructions of 1 KB; LDS bytes that the stored layout omits (right of the
 // diagonal in rows 0..31) and the row padding are zero-filled.
-template <int NWAVES>
+template <int NWAVES, bool NT>
 __device__ __forceinline__ void dma_tb(u32x4 r, unsigned char *lds, int wave, int lane) {
   constexpr int LDB = LDT * 2, NI = C * LDB / 1024;
   static_assert(C * LDB % 1024 == 0, "whole wave-instructions");
@@ -424,7 +435,7 @@ __device__ __forceinline__ void dma_tb(u32x4 r, unsigned char *lds, int wave, in
       const int row = p / LDB, off = p - row * LDB;
       const bool kept = off < (row < 32 ? 64 : 128);
       const uint32_t src = kept ? (uint32_t)(2 * tb_offset(row) + off) : 0xFFFFFFF0u;
-      lds_dma16(r, src, base + 1024u * (uint32_t)j);
+      lds_dma16<NT>(r, src, base + 1024u * (uint32_t)j);
     }
   }
 }
@@ -504,13 +515,13 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<DK * 2, LDK * 2, C, 1>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, 0, lane);
-    dma_tile<DV * 2, LDK * 2, C, 1>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)dV, 0, lane);
+    dma_tile<DK * 2, LDK * 2, C, 1, true>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, 0, lane);
+    dma_tile<DV * 2, LDK * 2, C, 1, true>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)dV, 0, lane);
     if (DELTA)
-      dma_tb<1>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2), (unsigned char *)dT, 0,
+      dma_tb<1, true>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2), (unsigned char *)dT, 0,
                 lane);
-    if (!additive) lds_dma2(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(dG));
-    if (use_beta) lds_dma2(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(dG + C));
+    if (!additive) lds_dma2<true>(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(dG));
+    if (use_beta) lds_dma2<true>(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(dG + C));
   };
 
   if (wave == NWT) {
@@ -827,9 +838,9 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<DV * 2, LDK * 2, C, NW>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)sV, wave, lane);
+    dma_tile<DV * 2, LDK * 2, C, NW, false>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)sV, wave, lane);
     if (DELTA)
-      dma_tb<NW>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
+      dma_tb<NW, false>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
                  (unsigned char *)sT, wave, lane);
   };
   // chunk ci's K tile (into dK) and raw gate values
@@ -837,14 +848,14 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<DK * 2, LDK * 2, C, NW>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
-    if (wave == 0 && !additive) lds_dma2(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(sGraw[0]));
-    if (wave == 1 && use_beta) lds_dma2(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(sGraw[1]));
+    dma_tile<DK * 2, LDK * 2, C, NW, false>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
+    if (wave == 0 && !additive) lds_dma2<false>(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(sGraw[0]));
+    if (wave == 1 && use_beta) lds_dma2<false>(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(sGraw[1]));
   };
   auto issue_q = [&](int ci, bf16_t *dQ) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
-    dma_tile<DK * 2, LDK * 2, C, NW>(rsrc_words(a.q + (bh * (size_t)T + t0) * DK, n * DK * 2), (unsigned char *)dQ,
+    dma_tile<DK * 2, LDK * 2, C, NW, false>(rsrc_words(a.q + (bh * (size_t)T + t0) * DK, n * DK * 2), (unsigned char *)dQ,
                                      wave, lane);
   };
   // gates of chunk ci from the raw values (alpha = 1, beta = 0 past the sequence end)
