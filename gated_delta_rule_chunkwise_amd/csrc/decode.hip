@@ -22,11 +22,16 @@
 
 namespace la {
 
-// One workgroup (256 threads) per state.  A row of DK floats is spread over LPR = DK/8
-// lanes, 8 columns each as two float4 at column groups lr and lr + LPR, so the LPR lanes
-// of a row read one contiguous run; 256/LPR rows are in flight per pass.
+// One workgroup of ROWS_NT threads per state.  A row of DK floats is spread over
+// LPR = DK/8 lanes, 8 columns each as two float4 at column groups lr and lr + LPR, so the
+// LPR lanes of a row read one contiguous run; ROWS_NT/LPR rows per pass, two passes
+// loaded before either is used.  Eight waves with few rows each keep more requests in
+// flight per CU than four waves with more rows each (which run at higher register use
+// and lower occupancy): about 10% more bandwidth for 128 x 128 states.
+constexpr int ROWS_NT = 512;
+
 template <int DK, int VAR, typename T>
-__global__ __launch_bounds__(256) void decode_rows_kernel(int dv, int has_beta,
+__global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_beta,
                                                           const float *__restrict__ S_in,
                                                           float *S_out, const T *__restrict__ q,
                                                           const T *__restrict__ k,
@@ -35,8 +40,8 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(int dv, int has_beta,
                                                           const T *__restrict__ beta,
                                                           T *__restrict__ o) {
   constexpr int LPR = DK / 8;
-  constexpr int RPP = 256 / LPR;
-  constexpr int UNROLL = 4;
+  constexpr int RPP = ROWS_NT / LPR;
+  constexpr int UNROLL = 2;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
@@ -103,11 +108,11 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(int dv, int has_beta,
   }
 }
 
-// BASED decode: one workgroup (256 threads) per state, d' = 16, d_v = 64, D = 273.
-// Thread t owns value columns 4(t%16)..+3 for the features f = t/16 + 16 i, so every
-// wave-wide access to s covers four whole 256-byte feature rows.
-template <typename T>
-__global__ __launch_bounds__(256) void decode_based_kernel(float eps, const float *__restrict__ S_in,
+// BASED decode: one workgroup (NT threads) per state, d' = 16, d_v = 64, D = 273.
+// Thread t owns value columns 4(t%16)..+3 for the features f = t/16 + (NT/16) i, so
+// every wave-wide access to s covers four whole 256-byte feature rows.
+template <int NT, typename T>
+__global__ __launch_bounds__(NT) void decode_based_kernel(float eps, const float *__restrict__ S_in,
                                                            const float *__restrict__ z_in,
                                                            float *S_out, float *z_out,
                                                            const T *__restrict__ q,
@@ -115,10 +120,11 @@ __global__ __launch_bounds__(256) void decode_based_kernel(float eps, const floa
                                                            const T *__restrict__ v,
                                                            T *__restrict__ o) {
   constexpr int DP = 16, DV = 64, D = 1 + DP + DP * DP;
+  constexpr int NW = NT / 64, FS = NT / 16;
   __shared__ float xk[DP], xq[DP];
   __shared__ float phk[D], phq[D];
-  __shared__ float4 red_num[4][16];
-  __shared__ float red_den[4];
+  __shared__ float4 red_num[NW][16];
+  __shared__ float red_den[NW];
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(256) void decode_based_kernel(float eps, const floa
   else if (tid < 2 * DP) xq[tid - DP] = io<T>::ld(q, (size_t)n * DP + tid - DP);
   __syncthreads();
   const float rs2 = 0.70710678118654752f;
-  for (int f = tid; f < D; f += 256) {
+  for (int f = tid; f < D; f += NT) {
     float fk, fq;
     if (f == 0) { fk = 1.0f; fq = 1.0f; }
     else if (f <= DP) { fk = xk[f - 1]; fq = xq[f - 1]; }
@@ -149,16 +155,16 @@ __global__ __launch_bounds__(256) void decode_based_kernel(float eps, const floa
   const float *Sn = S_in + (size_t)n * D * DV;
   float *So = S_out + (size_t)n * D * DV;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int NI = (D + 15) / 16;
+  constexpr int NI = (D + FS - 1) / FS;
   float4 sv[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int f = fo + 16 * i;
+    const int f = fo + FS * i;
     if (f < D) sv[i] = *reinterpret_cast<const float4 *>(Sn + (size_t)f * DV + 4 * cg);
   }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int f = fo + 16 * i;
+    const int f = fo + FS * i;
     if (f < D) {
       const float pk = phk[f], pq = phq[f];
       float4 s = sv[i];
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(256) void decode_based_kernel(float eps, const floa
   if (lane < 16) red_num[wave][lane] = num;
 
   float dpart = 0.0f;
-  for (int f = tid; f < D; f += 256) {
+  for (int f = tid; f < D; f += NT) {
     const float z = z_in[(size_t)n * D + f] + phk[f];
     z_out[(size_t)n * D + f] = z;
     dpart += phq[f] * z;
@@ -189,11 +195,14 @@ __global__ __launch_bounds__(256) void decode_based_kernel(float eps, const floa
   if (tid < 16) {
     float4 acc = red_num[0][tid];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 1; w < NW; ++w) {
       acc.x += red_num[w][tid].x; acc.y += red_num[w][tid].y;
       acc.z += red_num[w][tid].z; acc.w += red_num[w][tid].w;
     }
-    const float den = ((red_den[0] + red_den[1]) + (red_den[2] + red_den[3])) + eps;
+    float den = red_den[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) den += red_den[w];
+    den += eps;
     io<T>::st(o, (size_t)n * DV + 4 * tid + 0, acc.x / den);
     io<T>::st(o, (size_t)n * DV + 4 * tid + 1, acc.y / den);
     io<T>::st(o, (size_t)n * DV + 4 * tid + 2, acc.z / den);
@@ -205,7 +214,7 @@ template <int DK, int VAR, typename T>
 static hipError_t go_rows(int n, int dv, int has_beta, const float *S_in, float *S_out,
                           const void *q, const void *k, const void *v, const void *alpha,
                           const void *beta, void *o, hipStream_t s) {
-  hipLaunchKernelGGL((decode_rows_kernel<DK, VAR, T>), dim3(n), dim3(256), 0, s, dv, has_beta, S_in,
+  hipLaunchKernelGGL((decode_rows_kernel<DK, VAR, T>), dim3(n), dim3(ROWS_NT), 0, s, dv, has_beta, S_in,
                      S_out, (const T *)q, (const T *)k, (const T *)v, (const T *)alpha,
                      (const T *)beta, (T *)o);
   return hipGetLastError();
@@ -242,14 +251,17 @@ hipError_t launch_decode_rows(int variant, int dtype, int n, int d_k, int d_v, c
   return go_rows_dk<float>(variant, n, d_k, d_v, S_in, S_out, q, k, v, alpha, beta, o, s);
 }
 
+// Four waves per state: eight (512 threads, nine features per thread) measured no faster.
+constexpr int BASED_NT = 256;
+
 hipError_t launch_decode_based(int dtype, int n, float eps, const float *S_in, const float *z_in,
                                float *S_out, float *z_out, const void *q, const void *k,
                                const void *v, void *o, hipStream_t s) {
   if (dtype == T_BF16)
-    hipLaunchKernelGGL(decode_based_kernel<bf16_t>, dim3(n), dim3(256), 0, s, eps, S_in, z_in, S_out,
+    hipLaunchKernelGGL((decode_based_kernel<BASED_NT, bf16_t>), dim3(n), dim3(BASED_NT), 0, s, eps, S_in, z_in, S_out,
                        z_out, (const bf16_t *)q, (const bf16_t *)k, (const bf16_t *)v, (bf16_t *)o);
   else
-    hipLaunchKernelGGL(decode_based_kernel<float>, dim3(n), dim3(256), 0, s, eps, S_in, z_in, S_out,
+    hipLaunchKernelGGL((decode_based_kernel<BASED_NT, float>), dim3(n), dim3(BASED_NT), 0, s, eps, S_in, z_in, S_out,
                        z_out, (const float *)q, (const float *)k, (const float *)v, (float *)o);
   return hipGetLastError();
 }
