@@ -28,6 +28,8 @@
 // segments; since A_t = I here, a segment's map is a plain sum (delta s, delta z), so
 // pass 1 computes the sums from a zero state, pass 2 takes exclusive prefix sums over
 // segments, and pass 3 replays every segment from its start state.
+#include <utility>
+
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -45,7 +47,6 @@ constexpr int NTHR = NW * 64;
 
 constexpr int LDQ = DP + 8;  // bf16 [C][DP] row-major q, k tiles (48-byte rows)
 constexpr int LDV = DV + 8;  // bf16 [C][DV] row-major v tile
-constexpr int LDKS = C + 4;  // fp32 [DP][C] k transposed, scaled by 1/sqrt 2
 constexpr int LDA = C + 8;   // bf16 [C][C] kernel matrix (transposed)
 
 enum { MODE_MAP = 0, MODE_OUT = 1 };
@@ -99,7 +100,21 @@ __device__ __forceinline__ int zf_index(int fi) {
   return ((fi >> 5) * 64 + 16 * ((fi & 15) >> 2)) * 8 + 4 * ((fi >> 4) & 1) + (fi & 3);
 }
 
-__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// x as held by lane M of this lane's row of 16 (DPP row broadcast; folded into the VALU
+// instruction that consumes it)
+template <int M> __device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + M, 0xF, 0xF, true));
+}
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
   ti = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
@@ -111,7 +126,6 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
   constexpr bool OUT = MODE == MODE_OUT;
   __shared__ __attribute__((aligned(16))) bf16_t sQ[C * LDQ];
   __shared__ __attribute__((aligned(16))) bf16_t sK[C * LDQ];
-  __shared__ __attribute__((aligned(16))) float sKs[DP * LDKS];
   __shared__ __attribute__((aligned(16))) bf16_t sV[C * LDV];
   __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];  // kernel matrix, transposed
   __shared__ __attribute__((aligned(16))) float sZ[NF];        // z, internal order
@@ -123,9 +137,12 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
   // phi(q) as MFMA B-operand fragments, [token tile][feature step][lane] (16 bytes each):
   // each wave builds its token tile's once per chunk, every wave reads all four
   __shared__ __attribute__((aligned(16))) bf16x8 sPhi[MODE == MODE_OUT ? 4 * (NFT / 2) * 64 : 1];
-  // MODE_MAP: phi(k)^T of the 16 order-2 feature tiles as MFMA A-operand fragments,
-  // [tile][token step][lane], built once per chunk (four tiles per wave)
+  // phi(k)^T of the 16 order-2 feature tiles as MFMA A-operand fragments, [tile][token
+  // step][lane], built once per chunk (four tiles per wave).  MODE_OUT keeps them in sPhi's
+  // space once the numerator is done with phi(q).
   __shared__ __attribute__((aligned(16))) bf16x8 sPhiK[MODE == MODE_MAP ? DP * 2 * 64 : 1];
+  bf16x8 *const phik = OUT ? sPhi : sPhiK;
+  static_assert(!OUT || DP * 2 <= 4 * (NFT / 2), "phi(k) fragments must fit in sPhi");
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int seg = blockIdx.x;
@@ -197,7 +214,7 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
     asm volatile("" : "+v"(lane_v));
     const int l16 = lane_v & 15, g = lane_v >> 4;
 
-    // ---- phase A: this chunk's q, k, v (+ k transposed) to LDS
+    // ---- phase A: this chunk's q, k, v to LDS
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int id = tid + NTHR * i, r = id >> 3, cv = id & 7;
@@ -206,11 +223,6 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
     if (tid < 2 * C) {
       const int r = tid >> 1, cv = tid & 1;
       *reinterpret_cast<u32x4 *>(sK + r * LDQ + cv * 8) = pkq;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = pkq[e >> 1];
-        sKs[(cv * 8 + e) * LDKS + r] = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)) * rs2;
-      }
     } else if (OUT) {
       const int id = tid - 2 * C, r = id >> 1, cv = id & 1;
       *reinterpret_cast<u32x4 *>(sQ + r * LDQ + cv * 8) = pkq;
@@ -340,73 +352,63 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         if (g == 0) sDen[16 * mt + l16] = dacc[0];
       }
     }
-    if (!OUT) {
-      // MODE_MAP: phi(k)^T fragments of order-2 tile a (rows b: k_t[a] k_t[b] / sqrt 2 at this
-      // lane's 8 tokens), tiles a = wave, wave + 4, ..., then shared through LDS
+    if (OUT) __syncthreads();  // every wave is done with phi(q) before sPhi is overwritten
+    {
+      // phi(k)^T fragments of order-2 tile a (rows b: k_t[a] k_t[b] / sqrt 2 at this lane's
+      // 8 tokens), tiles a = wave, wave + 4, ..., shared through LDS.  The K^T fragment holds
+      // k_t[b] for b = lane % 16, so k_t[a] at the same tokens is lane a of the same 16-lane
+      // row: a DPP row broadcast inside the multiply (a must be a constant, hence the
+      // uniform branch on the wave index).
       const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
+      f32x4 klo[2], khi[2], kls[2], khs[2];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        f32x4 klo, khi;
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          klo[e] = (float)kj[s2][e];
-          khi[e] = (float)kj[s2][4 + e];
+          klo[s2][e] = (float)kj[s2][e];
+          khi[s2][e] = (float)kj[s2][4 + e];
+          kls[s2][e] = klo[s2][e] * rs2;
+          khs[s2][e] = khi[s2][e] * rs2;
         }
+      static_for<NW>([&](auto wc) {
+        if (wave == decltype(wc)::value) {
+          static_for<DP / NW>([&](auto ic) {
+            constexpr int ta = decltype(wc)::value + NW * decltype(ic)::value;
 #pragma unroll
-        for (int i = 0; i < DP / NW; ++i) {
-          const int ta = wave + NW * i;
-          const f32x4 k0 = ld4f(sKs + ta * LDKS + 32 * s2 + 4 * g), k1 = ld4f(sKs + ta * LDKS + 32 * s2 + 16 + 4 * g);
-          sPhiK[(ta * 2 + s2) * 64 + lane] = pack_pair(klo * k0, khi * k1);
+            for (int s2 = 0; s2 < 2; ++s2) {
+              f32x4 lo, hi;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                lo[e] = kls[s2][e] * row_bcast<ta>(klo[s2][e]);
+                hi[e] = khs[s2][e] * row_bcast<ta>(khi[s2][e]);
+              }
+              phik[(ta * 2 + s2) * 64 + lane] = pack_pair(lo, hi);
+            }
+          });
         }
-      }
+      });
       __syncthreads();
     }
     {
       // carry.  Order-2 tile a (features x_a x_b / sqrt 2, b = 0..15): s += phi(K)_a^T V with
-      // phi(K)_a^T = K^T diag(k_a / sqrt 2) -- shared fragments from LDS in MODE_MAP; in
-      // MODE_OUT (no room for them) the factor scales this wave's V operand instead.  Tile
-      // 16 (x_b): K^T V.  Tile 17 (the constant): 1^T V.  Straight-line, the operands of
-      // the next tile read one step ahead; z's increment phi(K)^T 1 separately below.
+      // the shared phi(K)_a^T fragments, read one tile ahead.  Tile 16 (x_b): K^T V.  Tile 17
+      // (the constant): 1^T V.  z's increment phi(K)^T 1 separately below.
       const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
-      f32x4 vlo[2], vhi[2];  // this lane's V column at its 8 tokens, fp32 (MODE_OUT)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 vf = s2 == 0 ? vf0 : vf1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vlo[s2][e] = (float)vf[e];
-          vhi[s2][e] = (float)vf[4 + e];
-        }
-      }
-      // per order-2 tile: MODE_MAP the two phi(K)^T fragments, MODE_OUT the four k_a vectors
       bf16x8 pkb[2][2];
-      f32x4 kab[2][4];
-#define LA_CARRY_LOAD(m, slot)                                                                     \
-  do {                                                                                             \
-    if (!OUT) {                                                                                    \
-      pkb[slot][0] = sPhiK[((m) * 2 + 0) * 64 + lane_v];                                           \
-      pkb[slot][1] = sPhiK[((m) * 2 + 1) * 64 + lane_v];                                           \
-    } else {                                                                                       \
-      _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                                           \
-        kab[slot][2 * s2] = ld4f(sKs + (m) * LDKS + 32 * s2 + 4 * g);                              \
-        kab[slot][2 * s2 + 1] = ld4f(sKs + (m) * LDKS + 32 * s2 + 16 + 4 * g);                     \
-      }                                                                                            \
-    }                                                                                              \
-  } while (0)
-      LA_CARRY_LOAD(0, 0);
+      pkb[0][0] = phik[0 * 64 + lane_v];
+      pkb[0][1] = phik[1 * 64 + lane_v];
 #pragma unroll
       for (int m = 0; m < DP; ++m) {
-        if (m + 1 < DP) LA_CARRY_LOAD(m + 1, (m + 1) & 1);
+        if (m + 1 < DP) {
+          pkb[(m + 1) & 1][0] = phik[((m + 1) * 2 + 0) * 64 + lane_v];
+          pkb[(m + 1) & 1][1] = phik[((m + 1) * 2 + 1) * 64 + lane_v];
+        }
         __builtin_amdgcn_sched_barrier(0);
         f32x4 acc = st[m];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          if (!OUT) acc = mfma_bf16(pkb[m & 1][s2], s2 == 0 ? vf0 : vf1, acc);
-          else acc = mfma_bf16(kj[s2], pack_pair(vlo[s2] * kab[m & 1][2 * s2], vhi[s2] * kab[m & 1][2 * s2 + 1]), acc);
-        }
+        for (int s2 = 0; s2 < 2; ++s2) acc = mfma_bf16(pkb[m & 1][s2], s2 == 0 ? vf0 : vf1, acc);
         st[m] = acc;
       }
-#undef LA_CARRY_LOAD
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         st[DP] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[DP]);
