@@ -16,13 +16,20 @@
 // expansion never touches LDS or HBM, which is the point the notes make about the
 // IO-aware kernel).
 //
-// gfx950 layout.  Internally the features are reordered so that the 256 order-2 features
-// come first (feature 16 i + j = x_i x_j / sqrt 2), then x_0..x_15, then the constant
-// (padded to 288 = 18 tiles of 16); the ABI layout [1, x, x (x) x] is restored when
-// states are read or written.  Four waves each own one 16-column tile of s (18 x 4 fp32
-// accumulator tiles, 72 registers); the normaliser z lives in LDS in fp32 and enters
-// the MFMAs as a one-column operand.  Every MFMA is v_mfma_f32_16x16x32_bf16 with fp32
-// accumulation; token-contraction operands of k and v are read with ds_read_b64_tr_b16.
+// gfx950 layout.  x x^T is symmetric, so phi(q).phi(k) only needs each unordered pair
+// {a, b} once: internally the order-2 block is kept as 9 "circulant diagonal" tiles.
+// Row r of tile d (d = 0..8) stands for the pair (r, (r + d) mod 16); for d = 1..7, and
+// rows r < 8 of d = 8, the state row is the sum of the two ABI rows (a, b) and (b, a),
+// and the key feature carries weight sqrt 2 instead of 1/sqrt 2 (both orders at once).
+// Row 8 of tile 8 is the constant feature, rows 9..15 are zero, tile 9 is x_0..x_15:
+// 160 internal features (10 tiles) instead of 273 (18 tiles with padding).  The ABI
+// layout [1, x, x (x) x] is restored when states are written: the antisymmetric part of
+// a start state never changes (every update is symmetric in (a, b)) and is added back.
+// Four waves each own one 16-column tile of s (10 x 4 fp32 accumulator tiles); the
+// normaliser z lives in LDS in fp32: its increment is a one-row MFMA operand, its product
+// with phi(q) is formed on the VALU from the fp32 features.  The state products are
+// v_mfma_f32_16x16x32_bf16 (q.k: 16x16x16) with fp32 accumulation; token-contraction
+// operands of k and v are read with ds_read_b64_tr_b16.
 //
 // Sequence parallelism: as for the gated recurrences, long sequences are split into
 // segments; since A_t = I here, a segment's map is a plain sum (delta s, delta z), so
@@ -40,12 +47,15 @@ constexpr int C = 64;    // tokens per chunk
 constexpr int DP = 16;   // q/k width d'
 constexpr int DV = 64;   // value width
 constexpr int D = 1 + DP + DP * DP;  // 273 features (ABI)
-constexpr int NF = 288;  // padded internal features (18 tiles)
+constexpr int ND = DP / 2 + 1;  // order-2 tiles: circulant diagonals d = 0..8
+constexpr int T_LIN = ND;       // tile of the linear features x_0..x_15
+constexpr int NF = 16 * (ND + 1);  // internal features (10 tiles)
 constexpr int NFT = NF / 16;
 constexpr int NW = 4;
 constexpr int NTHR = NW * 64;
 
-constexpr int LDQ = DP + 8;  // bf16 [C][DP] row-major q, k tiles (48-byte rows)
+constexpr int LDQ = DP + 8;  // bf16 [C][DP] row-major k tile (48-byte rows)
+constexpr int LDQ2 = 2 * DP + 8;  // bf16 [C][2 DP] q tile, each row holding q_t twice
 constexpr int LDV = DV + 8;  // bf16 [C][DV] row-major v tile
 constexpr int LDA = C + 8;   // bf16 [C][C] kernel matrix (transposed)
 
@@ -65,9 +75,47 @@ struct Args {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// ABI feature index of internal feature fi (-1 for padding)
-__device__ __forceinline__ int abi_feature(int fi) {
-  return fi < 256 ? 1 + DP + fi : (fi < 256 + DP ? 1 + (fi - 256) : (fi == 256 + DP ? 0 : -1));
+// The ABI features whose sum is internal feature fi: f1 and f2 (-1 = none).  f2 >= 0 only
+// for the symmetrised pairs, whose ABI rows (a, b) = f1 and (b, a) = f2 are both written
+// back from the one internal row.
+__device__ __forceinline__ void abi_pair(int fi, int &f1, int &f2) {
+  const int t = fi >> 4, r = fi & 15;
+  f1 = -1;
+  f2 = -1;
+  if (t == T_LIN) {
+    f1 = 1 + r;
+  } else if (t == ND - 1 && r >= DP / 2) {
+    if (r == DP / 2) f1 = 0;  // the constant
+  } else {
+    const int b = (r + t) & 15;
+    f1 = 1 + DP + DP * r + b;
+    if (t != 0) f2 = 1 + DP + DP * b + r;
+  }
+}
+
+// Internal feature fi of a state read in ABI layout (NULL = zero state).
+__device__ __forceinline__ float abi_load(const float *src, int fi, int stride, int col) {
+  if (!src) return 0.0f;
+  int f1, f2;
+  abi_pair(fi, f1, f2);
+  float x = f1 >= 0 ? src[(size_t)f1 * stride + col] : 0.0f;
+  if (f2 >= 0) x += src[(size_t)f2 * stride + col];
+  return x;
+}
+
+// Internal feature fi with value x written back in ABI layout; src is the start state
+// the symmetrised rows began from (NULL = zero), whose antisymmetric part is restored.
+__device__ __forceinline__ void abi_store(float *dst, const float *src, int fi, int stride, int col, float x) {
+  int f1, f2;
+  abi_pair(fi, f1, f2);
+  if (f1 < 0) return;
+  if (f2 < 0) {
+    dst[(size_t)f1 * stride + col] = x;
+    return;
+  }
+  const float asym = src ? src[(size_t)f1 * stride + col] - src[(size_t)f2 * stride + col] : 0.0f;
+  dst[(size_t)f1 * stride + col] = 0.5f * (x + asym);
+  dst[(size_t)f2 * stride + col] = 0.5f * (x - asym);
 }
 
 __device__ __forceinline__ bf16x8 pack_pair(f32x4 a, f32x4 b) {
@@ -94,17 +142,15 @@ __device__ __forceinline__ bf16x8 col_frag(const bf16_t *tile, int ld, int nt, i
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// feature fi (internal order) of z at its place in the denominator's A-operand fragments:
-// step s = fi / 32, lane 16 g (row 0) with g = (fi % 16) / 4, element 4 ((fi / 16) % 2) + fi % 4
-__device__ __forceinline__ int zf_index(int fi) {
-  return ((fi >> 5) * 64 + 16 * ((fi & 15) >> 2)) * 8 + 4 * ((fi >> 4) & 1) + (fi & 3);
-}
-
 
 // x as held by lane M of this lane's row of 16 (DPP row broadcast; folded into the VALU
 // instruction that consumes it)
 template <int M> __device__ __forceinline__ float row_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + M, 0xF, 0xF, true));
+}
+// x as held by lane (i - N) mod 16 of this lane's row of 16, i = lane % 16 (DPP row rotation)
+template <int N> __device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF, true));
 }
 
 // f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
@@ -124,25 +170,22 @@ __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
 template <int MODE>
 __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
   constexpr bool OUT = MODE == MODE_OUT;
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[C * LDQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[C * LDQ2];
   __shared__ __attribute__((aligned(16))) bf16_t sK[C * LDQ];
   __shared__ __attribute__((aligned(16))) bf16_t sV[C * LDV];
   __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];  // kernel matrix, transposed
   __shared__ __attribute__((aligned(16))) float sZ[NF];        // z, internal order
-  __shared__ __attribute__((aligned(16))) float sZinc[NF];     // this chunk's Phi_K^T 1
+  __shared__ __attribute__((aligned(16))) float sZinc[NF + 64];  // this chunk's Phi_K^T 1 (+ spare slots)
   __shared__ __attribute__((aligned(16))) float sDen[C];
-  // MODE_OUT: z as the A operand of the denominator product (row 0 = z, other rows zero),
-  // [feature step][lane]; kept in step with sZ
-  __shared__ __attribute__((aligned(16))) bf16x8 sZf[MODE == MODE_OUT ? (NFT / 2) * 64 : 1];
   // phi(q) as MFMA B-operand fragments, [token tile][feature step][lane] (16 bytes each):
   // each wave builds its token tile's once per chunk, every wave reads all four
   __shared__ __attribute__((aligned(16))) bf16x8 sPhi[MODE == MODE_OUT ? 4 * (NFT / 2) * 64 : 1];
-  // phi(k)^T of the 16 order-2 feature tiles as MFMA A-operand fragments, [tile][token
+  // phi(k)^T of the 9 order-2 feature tiles as MFMA A-operand fragments, [tile][token
   // step][lane], built once per chunk (four tiles per wave).  MODE_OUT keeps them in sPhi's
   // space once the numerator is done with phi(q).
-  __shared__ __attribute__((aligned(16))) bf16x8 sPhiK[MODE == MODE_MAP ? DP * 2 * 64 : 1];
+  __shared__ __attribute__((aligned(16))) bf16x8 sPhiK[MODE == MODE_MAP ? ND * 2 * 64 : 1];
   bf16x8 *const phik = OUT ? sPhi : sPhiK;
-  static_assert(!OUT || DP * 2 <= 4 * (NFT / 2), "phi(k) fragments must fit in sPhi");
+  static_assert(!OUT || ND * 2 <= 4 * (NFT / 2), "phi(k) fragments must fit in sPhi");
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int seg = blockIdx.x;
@@ -162,28 +205,11 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int fi = 16 * m + 4 * g + e, col = 16 * n_col + l16;
-        float x = 0.0f;
-        if (src_i) x = src_i[(size_t)fi * (DV + 1) + col];
-        else if (src_a) {
-          const int af = abi_feature(fi);
-          x = af >= 0 ? src_a[(size_t)af * DV + col] : 0.0f;
-        }
-        st[m][e] = x;
+        st[m][e] = src_i ? src_i[(size_t)fi * (DV + 1) + col] : abi_load(src_a, fi, DV, col);
       }
     for (int fi = tid; fi < NF; fi += NTHR) {
-      float x = 0.0f;
-      if (src_i) x = src_i[(size_t)fi * (DV + 1) + DV];
-      else if (OUT && a.nseg == 1 && a.z0) {
-        const int af = abi_feature(fi);
-        x = af >= 0 ? a.z0[bh * D + af] : 0.0f;
-      }
-      sZ[fi] = x;
-    }
-    if (OUT) {
-      bf16_t *zf = reinterpret_cast<bf16_t *>(sZf);
-      for (int i = tid; i < (NFT / 2) * 64 * 8; i += NTHR) zf[i] = 0;
-      __syncthreads();
-      for (int fi = tid; fi < NF; fi += NTHR) zf[zf_index(fi)] = f32_to_bf16(sZ[fi]);
+      sZ[fi] = src_i ? src_i[(size_t)fi * (DV + 1) + DV]
+                     : abi_load(OUT && a.nseg == 1 && a.z0 ? a.z0 + bh * D : nullptr, fi, 1, 0);
     }
   }
 
@@ -225,67 +251,85 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       *reinterpret_cast<u32x4 *>(sK + r * LDQ + cv * 8) = pkq;
     } else if (OUT) {
       const int id = tid - 2 * C, r = id >> 1, cv = id & 1;
-      *reinterpret_cast<u32x4 *>(sQ + r * LDQ + cv * 8) = pkq;
+      *reinterpret_cast<u32x4 *>(sQ + r * LDQ2 + cv * 8) = pkq;
+      *reinterpret_cast<u32x4 *>(sQ + r * LDQ2 + DP + cv * 8) = pkq;
     }
     __syncthreads();
     if (ci + 1 < nchunks) LA_BLOAD(t0 + C);
 
     // ---- phase B: kernel matrix A = 1 + QK^T + (QK^T)^2/2, causal, stored transposed
     // (row j, column t) in bf16; tiles dealt round robin (a wave without a third tile
-    // recomputes tile 9 and does not store it)
+    // recomputes tile 9 and stores the same values again).  q.k over d' = 16 is one
+    // v_mfma_f32_16x16x16_bf16 per tile: lane (g, i) supplies elements 4 g..4 g + 3 of row
+    // i; all six operand reads are issued before the first product.
+    float zq = 0.0f;  // MODE_OUT: z . phi(q_t) for token 16 wave + lane % 16
     if (OUT) {
+      v4i16 fa[3], fb[3];
+      int tis[3], tjs[3];
 #pragma unroll
       for (int mm = 0; mm < 3; ++mm) {
         const int job = wave + NW * mm;
-        int ti, tj;
-        tri_index(job < 10 ? job : 9, ti, tj);
-        bf16x8 fa, fb;  // q.k over d' = 16: the upper half of the 32-wide k-step is zero
-        const u32x4 z4 = {0u, 0u, 0u, 0u};
-        fa = __builtin_bit_cast(bf16x8, g < 2 ? *reinterpret_cast<const u32x4 *>(sQ + (16 * ti + l16) * LDQ + 8 * (g & 1)) : z4);
-        fb = __builtin_bit_cast(bf16x8, g < 2 ? *reinterpret_cast<const u32x4 *>(sK + (16 * tj + l16) * LDQ + 8 * (g & 1)) : z4);
-        const f32x4 acc = mfma_bf16(fa, fb, f32x4{0.f, 0.f, 0.f, 0.f});
-        const int j = 16 * tj + l16;
+        tri_index(job < 10 ? job : 9, tis[mm], tjs[mm]);
+        fa[mm] = *reinterpret_cast<const v4i16 *>(sQ + (16 * tis[mm] + l16) * LDQ2 + 4 * g);
+        fb[mm] = *reinterpret_cast<const v4i16 *>(sK + (16 * tjs[mm] + l16) * LDQ + 4 * g);
+      }
+#pragma unroll
+      for (int mm = 0; mm < 3; ++mm) {
+        const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa[mm], fb[mm], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const int ti = tis[mm], j = 16 * tjs[mm] + l16;
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = acc[e];
           v[e] = (16 * ti + 4 * g + e >= j) ? 1.0f + x + 0.5f * x * x : 0.0f;
         }
-        if (job < 10)
-          *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
       }
       if (tid < 128) {  // the above-diagonal tiles read by the A V products: A (0,1), (2,3)
         const int tile = tid >> 6, e = tid & 63;
         *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
       }
       {  // phi(q_t) for this wave's token tile mt = wave, t = 16 mt + l16: the B operand of
-         // feature step s holds features 32 s + 4 g + e and 32 s + 16 + 4 g + e
+         // feature step s holds rows 4 g + e of tiles 2 s and 2 s + 1.  With w[j] =
+         // q_t[(4 g + j) mod 16] (three 8-byte reads of the doubled row), row r = 4 g + e of
+         // diagonal tile d is w[e] w[e + d] / sqrt 2 -- every index a constant.  The same
+         // fp32 values give the normaliser's state term z . phi(q_t) (40 features per lane,
+         // then summed over the four lanes of the token).
         const int t = 16 * wave + l16;
-        const u32x4 qa = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ);
-        const u32x4 qb = *reinterpret_cast<const u32x4 *>(sQ + t * LDQ + 8);
-        float qs[16];  // q_t[a] / sqrt 2
-        {
-          const uint32_t w[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
+        float w[12];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            qs[2 * i] = __uint_as_float(w[i] << 16) * rs2;
-            qs[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * rs2;
-          }
+        for (int h = 0; h < 3; ++h) {
+          const f32x4 x = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sQ + t * LDQ2 + 4 * g + 4 * h));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[4 * h + e] = x[e];
         }
-        const f32x4 qg = u16x4_to_f32(*reinterpret_cast<const uint2 *>(sQ + t * LDQ + 4 * g));
+        float ws[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ws[e] = w[e] * rs2;
 #pragma unroll
         for (int s = 0; s < NFT / 2; ++s) {
-          f32x4 b0, b1;
-          if (s < 8) {
-            b0 = qg * qs[2 * s];
-            b1 = qg * qs[2 * s + 1];
-          } else {
-            b0 = qg;
+          f32x4 bt[2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b1[e] = (4 * g + e == 0) ? 1.0f : 0.0f;
+          for (int h = 0; h < 2; ++h) {
+            const int d = 2 * s + h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pr = ws[e] * w[e + (d < ND ? d : 0)];
+              if (d == T_LIN) bt[h][e] = w[e];
+              else if (d == ND - 1) bt[h][e] = g < 2 ? pr : (g == 2 && e == 0 ? 1.0f : 0.0f);
+              else bt[h][e] = pr;
+            }
           }
-          sPhi[(wave * (NFT / 2) + s) * 64 + lane] = pack_pair(b0, b1);
+          sPhi[(wave * (NFT / 2) + s) * 64 + lane] = pack_pair(bt[0], bt[1]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 zz = *reinterpret_cast<const f32x4 *>(sZ + 16 * (2 * s + h) + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zq += bt[h][e] * zz[e];
+          }
         }
+        zq += __shfl_xor(zq, 16, 64);
+        zq += __shfl_xor(zq, 32, 64);
       }
       __syncthreads();
     }
@@ -313,76 +357,79 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       bf16x8 sfr[NFT / 2];
 #pragma unroll
       for (int s = 0; s < NFT / 2; ++s) sfr[s] = pack_pair(st[2 * s], st[2 * s + 1]);
-      // feature steps outer, token tiles inner (four independent accumulators, and den for
-      // token tile mt = wave as a fifth: z as one operand row), the phi(q) fragments of the
-      // next step read one step ahead
+      // feature steps outer, token tiles inner (four independent accumulators), the phi(q)
+      // fragments of the next step read one step ahead
       bf16x8 ph[2][4];
-      f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         num[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         ph[0][mt] = sPhi[(mt * (NFT / 2)) * 64 + lane_v];
       }
-      bf16x8 zb[2];
-      zb[0] = sZf[lane_v];
 #pragma unroll
       for (int s = 0; s < NFT / 2; ++s) {
         if (s + 1 < NFT / 2) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) ph[(s + 1) & 1][mt] = sPhi[(mt * (NFT / 2) + s + 1) * 64 + lane_v];
-          zb[(s + 1) & 1] = sZf[(s + 1) * 64 + lane_v];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) num[mt] = mfma_bf16(sfr[s], ph[s & 1][mt], num[mt]);
-        dacc = mfma_bf16(zb[s & 1], sPhi[(wave * (NFT / 2) + s) * 64 + lane_v], dacc);
       }
 #pragma unroll
       for (int it = 0; it < 6; ++it) {  // A V: (mt, s2) with s2 = 1 only for mt >= 2 (causal)
         const int mt = it < 2 ? it : 2 + (it - 2) / 2, s2 = it < 2 ? 0 : (it - 2) % 2;
         num[mt] = mfma_bf16(s2 == 0 ? vf0 : vf1, col_frag(sA, LDA, mt, s2, lane_v), num[mt]);
       }
-      {  // den: + the row sums of A (valid-token row), for token tile mt = wave
+      {  // den = z . phi(q_t) + the row sums of A (valid-token row), for token tile mt = wave
         const int mt = wave;
+        f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (s2 == 1 && mt < 2) continue;
           dacc = mfma_bf16(ones[s2], col_frag(sA, LDA, mt, s2, lane_v), dacc);
         }
-        if (g == 0) sDen[16 * mt + l16] = dacc[0];
+        if (g == 0) sDen[16 * mt + l16] = dacc[0] + zq;
       }
     }
     if (OUT) __syncthreads();  // every wave is done with phi(q) before sPhi is overwritten
     {
-      // phi(k)^T fragments of order-2 tile a (rows b: k_t[a] k_t[b] / sqrt 2 at this lane's
-      // 8 tokens), tiles a = wave, wave + 4, ..., shared through LDS.  The K^T fragment holds
-      // k_t[b] for b = lane % 16, so k_t[a] at the same tokens is lane a of the same 16-lane
-      // row: a DPP row broadcast inside the multiply (a must be a constant, hence the
-      // uniform branch on the wave index).
+      // phi(k)^T fragments of the order-2 tiles (A operand: rows = features, k = tokens),
+      // tiles d = wave, wave + 4, ..., shared through LDS.  Row i of diagonal tile d is
+      // k_t[i] k_t[(i + d) mod 16] times 1/sqrt 2 (d = 0) or sqrt 2 (both orders of the
+      // pair); tile 8 keeps rows i < 8 and holds the constant 1 in row 8.  The K^T fragment
+      // holds k_t[i] for i = lane % 16 at the lane's 8 tokens, so k_t[(i + d) mod 16] at the
+      // same tokens is a DPP rotation of the 16-lane row, folded into the multiply (d must
+      // be a constant, hence the uniform branch on the wave index).
       const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
-      f32x4 klo[2], khi[2], kls[2], khs[2];
+      f32x4 kf[2][2], kw[2][2];  // [s2][lo/hi]: k_t[i] and sqrt 2 k_t[i], fp32
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          klo[s2][e] = (float)kj[s2][e];
-          khi[s2][e] = (float)kj[s2][4 + e];
-          kls[s2][e] = klo[s2][e] * rs2;
-          khs[s2][e] = khi[s2][e] * rs2;
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kf[s2][h][e] = (float)kj[s2][4 * h + e];
+            kw[s2][h][e] = kf[s2][h][e] * (2.0f * rs2);
+          }
       static_for<NW>([&](auto wc) {
         if (wave == decltype(wc)::value) {
-          static_for<DP / NW>([&](auto ic) {
-            constexpr int ta = decltype(wc)::value + NW * decltype(ic)::value;
+          static_for<(ND + NW - 1) / NW>([&](auto ic) {
+            constexpr int d = decltype(wc)::value + NW * decltype(ic)::value;
+            if constexpr (d < ND) {
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              f32x4 lo, hi;
+              for (int s2 = 0; s2 < 2; ++s2) {
+                f32x4 f[2];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                lo[e] = kls[s2][e] * row_bcast<ta>(klo[s2][e]);
-                hi[e] = khs[s2][e] * row_bcast<ta>(khi[s2][e]);
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    if constexpr (d == 0) f[h][e] = kf[s2][h][e] * kf[s2][h][e] * rs2;
+                    else f[h][e] = kw[s2][h][e] * row_ror<16 - d>(kf[s2][h][e]);
+                    if constexpr (d == ND - 1)
+                      if (l16 >= DP / 2) f[h][e] = l16 == DP / 2 ? 1.0f : 0.0f;
+                  }
+                phik[(d * 2 + s2) * 64 + lane] = pack_pair(f[0], f[1]);
               }
-              phik[(ta * 2 + s2) * 64 + lane] = pack_pair(lo, hi);
             }
           });
         }
@@ -390,16 +437,16 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       __syncthreads();
     }
     {
-      // carry.  Order-2 tile a (features x_a x_b / sqrt 2, b = 0..15): s += phi(K)_a^T V with
-      // the shared phi(K)_a^T fragments, read one tile ahead.  Tile 16 (x_b): K^T V.  Tile 17
-      // (the constant): 1^T V.  z's increment phi(K)^T 1 separately below.
+      // carry.  Order-2 tile d (with the constant in tile 8): s += phi(K)_d^T V with the shared
+      // phi(K)_d^T fragments, read one tile ahead.  Linear tile: K^T V.  z's increment
+      // phi(K)^T 1 separately below.
       const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
       bf16x8 pkb[2][2];
       pkb[0][0] = phik[0 * 64 + lane_v];
       pkb[0][1] = phik[1 * 64 + lane_v];
 #pragma unroll
-      for (int m = 0; m < DP; ++m) {
-        if (m + 1 < DP) {
+      for (int m = 0; m < ND; ++m) {
+        if (m + 1 < ND) {
           pkb[(m + 1) & 1][0] = phik[((m + 1) * 2 + 0) * 64 + lane_v];
           pkb[(m + 1) & 1][1] = phik[((m + 1) * 2 + 1) * 64 + lane_v];
         }
@@ -410,28 +457,29 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         st[m] = acc;
       }
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        st[DP] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[DP]);
-        st[DP + 1] = mfma_bf16(ones[s2], s2 == 0 ? vf0 : vf1, st[DP + 1]);
-      }
-      // z increment phi(K)^T 1: the order-2 part is the key Gram sum_t k_t k_t^T / sqrt 2
-      // (wave 0), the linear part sum_t k_t and the constant sum_t 1 (wave 1)
+      for (int s2 = 0; s2 < 2; ++s2) st[T_LIN] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[T_LIN]);
+      // z increment phi(K)^T 1: the order-2 part from the key Gram G = sum_t k_t k_t^T
+      // (wave 0; entry (a, b) lands in row a of diagonal tile (b - a) mod 16 when that is a
+      // kept row), the linear part sum_t k_t, the constant sum_t 1 and tile 8's zero rows
+      // (wave 1): every internal feature written once
       if (wave == 0) {
         f32x4 gk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) gk = mfma_bf16(kj[s2], kj[s2], gk);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sZinc[16 * (4 * g + e) + l16] = gk[e] * rs2;  // feature (4 g + e, l16)
-      } else if (wave == 1) {
-        f32x4 zl = {0.f, 0.f, 0.f, 0.f}, zc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          zl = mfma_bf16(ones[s2], kj[s2], zl);      // row 0: sum_t k_t[l16]
-          zc = mfma_bf16(ones[s2], ones[s2], zc);    // [0][0]: number of valid tokens
+        for (int e = 0; e < 4; ++e) {  // G[a][b], a = 4 g + e, b = l16; unkept entries to a spare slot
+          const int ra = 4 * g + e, d = (l16 - ra) & 15;
+          const bool keep = d < ND - 1 || (d == ND - 1 && ra < DP / 2);
+          sZinc[keep ? 16 * d + ra : NF + lane] = gk[e] * (d == 0 ? rs2 : 2.0f * rs2);
         }
+      } else if (wave == 1) {
+        f32x4 zl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) zl = mfma_bf16(ones[s2], kj[s2], zl);  // row 0: sum_t k_t[l16]
         if (g == 0) {
-          sZinc[16 * DP + l16] = zl[0];
-          sZinc[16 * (DP + 1) + l16] = l16 == 0 ? zc[0] : 0.0f;
+          sZinc[16 * T_LIN + l16] = zl[0];
+          // the constant feature counts the valid tokens
+          if (l16 >= DP / 2) sZinc[16 * (ND - 1) + l16] = l16 == DP / 2 ? (float)n : 0.0f;
         }
       }
     }
@@ -448,11 +496,7 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
         bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + 16 * n_col + 4 * g), __builtin_bit_cast(u32x2, h));
       }
     }
-    for (int fi = tid; fi < NF; fi += NTHR) {
-      const float zn = sZ[fi] + sZinc[fi];
-      sZ[fi] = zn;
-      if (OUT) reinterpret_cast<bf16_t *>(sZf)[zf_index(fi)] = f32_to_bf16(zn);
-    }
+    for (int fi = tid; fi < NF; fi += NTHR) sZ[fi] += sZinc[fi];
   }
 #undef LA_BLOAD
 
@@ -460,17 +504,14 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
     if (a.nseg == 1 && a.s_T) {
       __syncthreads();
       const int l16 = lane & 15, g = lane >> 4;
+      const float *s0 = a.s0 ? a.s0 + bh * (size_t)D * DV : nullptr;
+      const float *z0 = a.z0 ? a.z0 + bh * D : nullptr;
 #pragma unroll
       for (int m = 0; m < NFT; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int af = abi_feature(16 * m + 4 * g + e);
-          if (af >= 0) a.s_T[(bh * D + af) * DV + 16 * n_col + l16] = st[m][e];
-        }
-      for (int fi = tid; fi < NF; fi += NTHR) {
-        const int af = abi_feature(fi);
-        if (af >= 0) a.z_T[bh * D + af] = sZ[fi];
-      }
+        for (int e = 0; e < 4; ++e)
+          abi_store(a.s_T + bh * (size_t)D * DV, s0, 16 * m + 4 * g + e, DV, 16 * n_col + l16, st[m][e]);
+      for (int fi = tid; fi < NF; fi += NTHR) abi_store(a.z_T + bh * D, z0, fi, 1, 0, sZ[fi]);
     }
   } else {
     __syncthreads();
@@ -492,12 +533,10 @@ __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
   constexpr int UNR = 8;  // segments whose sums are loaded together
   for (int id = blockIdx.x * 256 + threadIdx.x; id < NE; id += gridDim.x * 256) {
     const int fi = id / (DV + 1), col = id % (DV + 1);
-    const int af = abi_feature(fi);
-    float x = 0.0f;
-    if (af >= 0) {
-      if (col < DV && a.s0) x = a.s0[(bh * D + af) * DV + col];
-      if (col == DV && a.z0) x = a.z0[bh * D + af];
-    }
+    // the start state and the end state's ABI place of this element: s[f][col] or z[f]
+    const float *src = col < DV ? (a.s0 ? a.s0 + bh * (size_t)D * DV : nullptr) : (a.z0 ? a.z0 + bh * D : nullptr);
+    const int stride = col < DV ? DV : 1, c = col < DV ? col : 0;
+    float x = abi_load(src, fi, stride, c);
     for (int i0 = 0; i0 < a.nseg; i0 += UNR) {
       float d[UNR];
 #pragma unroll
@@ -509,10 +548,7 @@ __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
         x += d[u];
       }
     }
-    if (a.s_T && af >= 0) {
-      if (col < DV) a.s_T[(bh * D + af) * DV + col] = x;
-      else a.z_T[bh * D + af] = x;
-    }
+    if (a.s_T) abi_store(col < DV ? a.s_T + bh * (size_t)D * DV : a.z_T + bh * D, src, fi, stride, c, x);
   }
 }
 
