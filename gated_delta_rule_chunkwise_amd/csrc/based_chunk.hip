@@ -167,8 +167,10 @@ __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
   tj = idx - ti * (ti + 1) / 2;
 }
 
+// Three replay workgroups per CU (49 KB of LDS, at most 168 registers each), four for the
+// maps pass (32 KB).
 template <int MODE>
-__global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
+__global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_kernel(const Args a) {
   constexpr bool OUT = MODE == MODE_OUT;
   __shared__ __attribute__((aligned(16))) bf16_t sQ[C * LDQ2];
   __shared__ __attribute__((aligned(16))) bf16_t sK[C * LDQ];
@@ -439,8 +441,20 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
     {
       // carry.  Order-2 tile d (with the constant in tile 8): s += phi(K)_d^T V with the shared
       // phi(K)_d^T fragments, read one tile ahead.  Linear tile: K^T V.  z's increment
-      // phi(K)^T 1 separately below.
+      // phi(K)^T 1: the order-2 part from the key Gram G = sum_t k_t k_t^T (wave 0; entry
+      // (a, b) lands in row a of diagonal tile (b - a) mod 16 when that is a kept row), the
+      // linear part sum_t k_t, the constant sum_t 1 and tile 8's zero rows (wave 1): every
+      // internal feature written once.  Its products go first so that their results are
+      // ready when the carry's are still in flight.
       const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
+      f32x4 zg = {0.f, 0.f, 0.f, 0.f};
+      if (wave == 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(kj[s2], kj[s2], zg);
+      } else if (wave == 1) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(ones[s2], kj[s2], zg);  // row 0: sum_t k_t[l16]
+      }
       bf16x8 pkb[2][2];
       pkb[0][0] = phik[0 * 64 + lane_v];
       pkb[0][1] = phik[1 * 64 + lane_v];
@@ -458,26 +472,16 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) st[T_LIN] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[T_LIN]);
-      // z increment phi(K)^T 1: the order-2 part from the key Gram G = sum_t k_t k_t^T
-      // (wave 0; entry (a, b) lands in row a of diagonal tile (b - a) mod 16 when that is a
-      // kept row), the linear part sum_t k_t, the constant sum_t 1 and tile 8's zero rows
-      // (wave 1): every internal feature written once
       if (wave == 0) {
-        f32x4 gk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) gk = mfma_bf16(kj[s2], kj[s2], gk);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // G[a][b], a = 4 g + e, b = l16; unkept entries to a spare slot
           const int ra = 4 * g + e, d = (l16 - ra) & 15;
           const bool keep = d < ND - 1 || (d == ND - 1 && ra < DP / 2);
-          sZinc[keep ? 16 * d + ra : NF + lane] = gk[e] * (d == 0 ? rs2 : 2.0f * rs2);
+          sZinc[keep ? 16 * d + ra : NF + lane] = zg[e] * (d == 0 ? rs2 : 2.0f * rs2);
         }
       } else if (wave == 1) {
-        f32x4 zl = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) zl = mfma_bf16(ones[s2], kj[s2], zl);  // row 0: sum_t k_t[l16]
         if (g == 0) {
-          sZinc[16 * T_LIN + l16] = zl[0];
+          sZinc[16 * T_LIN + l16] = zg[0];
           // the constant feature counts the valid tokens
           if (l16 >= DP / 2) sZinc[16 * (ND - 1) + l16] = l16 == DP / 2 ? (float)n : 0.0f;
         }
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
       const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const float r = 1.0f / (sDen[16 * mt + l16] + a.eps);
+        const float r = __builtin_amdgcn_rcpf(sDen[16 * mt + l16] + a.eps);
         const f32x4 x = num[mt] * r;
         const bf16x4 h = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
         bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + 16 * n_col + 4 * g), __builtin_bit_cast(u32x2, h));
@@ -526,11 +530,12 @@ __global__ __launch_bounds__(NTHR, 2) void based_chunk_kernel(const Args a) {
 }
 
 // Pass 2: exclusive prefix sums of the per-segment sums, from the (ABI-layout) start
-// state; also the end state in the ABI layout.  One workgroup per (b, h).
+// state; also the end state in the ABI layout.  One thread per state element and (b, h),
+// all segments' sums loaded at once (up to 16).
 __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   constexpr int NE = NF * (DV + 1);
-  constexpr int UNR = 8;  // segments whose sums are loaded together
+  constexpr int UNR = 16;  // segments whose sums are loaded together
   for (int id = blockIdx.x * 256 + threadIdx.x; id < NE; id += gridDim.x * 256) {
     const int fi = id / (DV + 1), col = id % (DV + 1);
     // the start state and the end state's ABI place of this element: s[f][col] or z[f]
@@ -556,13 +561,13 @@ struct Plan {
   int nseg, seg_chunks;
 };
 
-// About two workgroups per CU in all, split only when the heads alone cannot fill it.
+// About three workgroups per CU in all, split only when the heads alone cannot fill it.
 Plan make_plan(int B, int H, int64_t T) {
   const int64_t nch = (T + C - 1) / C;
   const int64_t bhn = (int64_t)B * H;
   int64_t nseg = 1;
-  if (bhn < 256) {
-    nseg = (512 + bhn - 1) / bhn;
+  if (bhn < 384) {
+    nseg = (768 + bhn - 1) / bhn;
     if (nseg > nch) nseg = nch;
     if (nseg < 1) nseg = 1;
   }
@@ -612,7 +617,7 @@ hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const 
   if (p.nseg > 1 && (pass_mask & PASS_MAPS))
     hipLaunchKernelGGL(based_chunk_kernel<MODE_MAP>, grid, dim3(NTHR), 0, s, a);
   if (p.nseg > 1 && (pass_mask & PASS_SCAN))
-    hipLaunchKernelGGL(based_scan_kernel, dim3(8, H, B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(based_scan_kernel, dim3((NF * (DV + 1) + 255) / 256, H, B), dim3(256), 0, s, a);
   if (pass_mask & PASS_REPLAY)
     hipLaunchKernelGGL(based_chunk_kernel<MODE_OUT>, grid, dim3(NTHR), 0, s, a);
   return hipGetLastError();
