@@ -63,9 +63,9 @@ enum { MODE_MAP = 0, MODE_OUT = 1 };
 
 struct Args {
   const bf16_t *q, *k, *v;
-  const float *s0, *z0;  // ABI layout; start state for a single segment (may be NULL)
+  const float *s0, *z0;  // ABI layout; start state of segment 0 (may be NULL = zero)
   bf16_t *o;
-  float *s_T, *z_T;      // ABI layout; written by pass 3 when there is a single segment
+  float *s_T, *z_T;      // ABI layout; written by the last segment's replay
   float *dsum;           // [BH][nseg][NF][DV + 1] per-segment sums (internal order; col DV = z)
   float *starts;         // [BH][nseg][NF][DV + 1] segment start states (internal order)
   int64_t T;
@@ -200,8 +200,10 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
   f32x4 st[NFT];
   {
     const int l16 = lane & 15, g = lane >> 4;
-    const float *src_i = (OUT && a.nseg > 1) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
-    const float *src_a = (OUT && a.nseg == 1 && a.s0) ? a.s0 + bh * (size_t)D * DV : nullptr;
+    // the replay starts segment 0 from S0 (ABI layout), later segments from the scan's
+    // start states; the map pass starts from zero
+    const float *src_i = (OUT && seg > 0) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
+    const float *src_a = (OUT && seg == 0 && a.s0) ? a.s0 + bh * (size_t)D * DV : nullptr;
 #pragma unroll
     for (int m = 0; m < NFT; ++m)
 #pragma unroll
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
       }
     for (int fi = tid; fi < NF; fi += NTHR) {
       sZ[fi] = src_i ? src_i[(size_t)fi * (DV + 1) + DV]
-                     : abi_load(OUT && a.nseg == 1 && a.z0 ? a.z0 + bh * D : nullptr, fi, 1, 0);
+                     : abi_load(OUT && seg == 0 && a.z0 ? a.z0 + bh * D : nullptr, fi, 1, 0);
     }
   }
 
@@ -505,7 +507,7 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
 #undef LA_BLOAD
 
   if (OUT) {
-    if (a.nseg == 1 && a.s_T) {
+    if (seg == a.nseg - 1 && a.s_T) {  // the last segment's end state is S_T
       __syncthreads();
       const int l16 = lane & 15, g = lane >> 4;
       const float *s0 = a.s0 ? a.s0 + bh * (size_t)D * DV : nullptr;
@@ -529,9 +531,10 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
   }
 }
 
-// Pass 2: exclusive prefix sums of the per-segment sums, from the (ABI-layout) start
-// state; also the end state in the ABI layout.  One thread per state element and (b, h),
-// all segments' sums loaded at once (up to 16).
+// Pass 2: the start states of segments 1..nseg-1, prefix sums of the per-segment sums of
+// segments 0..nseg-2 from the (ABI-layout) start state (segment 0 starts from it
+// directly, and the last segment's replay writes the end state).  One thread per state
+// element and (b, h), all segments' sums loaded at once (up to 16).
 __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   constexpr int NE = NF * (DV + 1);
@@ -542,18 +545,17 @@ __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
     const float *src = col < DV ? (a.s0 ? a.s0 + bh * (size_t)D * DV : nullptr) : (a.z0 ? a.z0 + bh * D : nullptr);
     const int stride = col < DV ? DV : 1, c = col < DV ? col : 0;
     float x = abi_load(src, fi, stride, c);
-    for (int i0 = 0; i0 < a.nseg; i0 += UNR) {
+    const int nmap = a.nseg - 1;  // segments with a map
+    for (int i0 = 0; i0 < nmap; i0 += UNR) {
       float d[UNR];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
-        d[u] = i0 + u < a.nseg ? a.dsum[(bh * a.nseg + i0 + u) * (size_t)NE + id] : 0.0f;
+      for (int u = 0; u < UNR; ++u) d[u] = i0 + u < nmap ? a.dsum[(bh * a.nseg + i0 + u) * (size_t)NE + id] : 0.0f;
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        if (i0 + u < a.nseg) a.starts[(bh * a.nseg + i0 + u) * (size_t)NE + id] = x;
         x += d[u];
+        if (i0 + u < nmap) a.starts[(bh * a.nseg + i0 + u + 1) * (size_t)NE + id] = x;
       }
     }
-    if (a.s_T) abi_store(col < DV ? a.s_T + bh * (size_t)D * DV : a.z_T + bh * D, src, fi, stride, c, x);
   }
 }
 
@@ -614,8 +616,8 @@ hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const 
   a.seg_chunks = p.seg_chunks;
   a.eps = eps;
   const dim3 grid(p.nseg, H, B);
-  if (p.nseg > 1 && (pass_mask & PASS_MAPS))
-    hipLaunchKernelGGL(based_chunk_kernel<MODE_MAP>, grid, dim3(NTHR), 0, s, a);
+  if (p.nseg > 1 && (pass_mask & PASS_MAPS))  // every segment but the last
+    hipLaunchKernelGGL(based_chunk_kernel<MODE_MAP>, dim3(p.nseg - 1, H, B), dim3(NTHR), 0, s, a);
   if (p.nseg > 1 && (pass_mask & PASS_SCAN))
     hipLaunchKernelGGL(based_scan_kernel, dim3((NF * (DV + 1) + 255) / 256, H, B), dim3(256), 0, s, a);
   if (pass_mask & PASS_REPLAY)
