@@ -16,6 +16,9 @@ promotes inputs exactly to float64.  What is computed, with citations:
   tradeoff", Sec. 2.2 (paper Eqs. (1)-(3)) and Sec. 2.3 (paper Eq. (4)): Taylor feature
   map phi(x) = [1, x, vec(x x^T)/sqrt 2], s_t = s_{t-1} + phi(k_t) v_t^T,
   z_t = z_{t-1} + phi(k_t), o_t = s_t^T phi(q_t) / (z_t^T phi(q_t) + eps).
+  ``based_compact``: the same recurrence with the compact map of the notes' feature-width
+  table (Sec. 2.3), [1, x, x_a^2/sqrt 2 (a = b), x_a x_b (a < b)], pairs in row-major
+  upper-triangle order (D = 1 + d' + d'(d'+1)/2 = 153 for d' = 16).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, brute force and invariants.  The eps convention and the absence of
@@ -32,8 +35,9 @@ from pathlib import Path
 
 import numpy as np
 
-ADDITIVE, BASED, GATED, GATED_DELTA = 0, 1, 2, 3
-VARIANTS = {"additive": ADDITIVE, "based": BASED, "gated": GATED, "gated_delta": GATED_DELTA}
+ADDITIVE, BASED, GATED, GATED_DELTA, BASED_COMPACT = 0, 1, 2, 3, 4
+VARIANTS = {"additive": ADDITIVE, "based": BASED, "gated": GATED, "gated_delta": GATED_DELTA,
+            "based_compact": BASED_COMPACT}
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "oracle.c"
@@ -79,6 +83,8 @@ def _load():
     lib.oracle_literal.restype = ctypes.c_int
     lib.oracle_based_phi.argtypes = [dp, ctypes.c_int, dp]
     lib.oracle_based_phi.restype = None
+    lib.oracle_based_phi_compact.argtypes = [dp, ctypes.c_int, dp]
+    lib.oracle_based_phi_compact.restype = None
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -103,8 +109,8 @@ def _variant(v) -> int:
     return VARIANTS[v] if isinstance(v, str) else int(v)
 
 
-def feature_dim(dp: int) -> int:
-    return 1 + dp + dp * dp
+def feature_dim(dp: int, compact: bool = False) -> int:
+    return 1 + dp + dp * (dp + 1) // 2 if compact else 1 + dp + dp * dp
 
 
 def max_threads() -> int:
@@ -133,8 +139,8 @@ def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6,
         rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
         nr = int(rows_arr.size)
     o = np.zeros((B, H, T, nr), dtype=np.float64)
-    if var == BASED:
-        D = feature_dim(dk)
+    if var in (BASED, BASED_COMPACT):
+        D = feature_dim(dk, var == BASED_COMPACT)
         S_T = np.zeros((B, H, D, nr)) if want_state else None
         z_T = np.zeros((B, H, D)) if want_state else None
     else:
@@ -162,8 +168,8 @@ def decode_step(variant, S, q, k, v, alpha=None, beta=None, z=None, eps=1e-6, nt
     alpha = _f64(alpha) if var in (GATED, GATED_DELTA) else None
     beta = _f64(beta) if var in (GATED, GATED_DELTA) else None
     o = np.zeros((N, dv))
-    if var == BASED:
-        D = feature_dim(dk)
+    if var in (BASED, BASED_COMPACT):
+        D = feature_dim(dk, var == BASED_COMPACT)
         S_out, z_out = np.zeros((N, D, dv)), np.zeros((N, D))
     else:
         S_out, z_out = np.zeros((N, dv, dk)), None
@@ -198,4 +204,12 @@ def based_phi(x):
     x = _f64(x)
     f = np.zeros(feature_dim(x.size))
     _load().oracle_based_phi(_ptr(x), int(x.size), _ptr(f))
+    return f
+
+
+def based_phi_compact(x):
+    """The compact map phi_c(x) for a 1-D vector x (fp64)."""
+    x = _f64(x)
+    f = np.zeros(feature_dim(x.size, compact=True))
+    _load().oracle_based_phi_compact(_ptr(x), int(x.size), _ptr(f))
     return f

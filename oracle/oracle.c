@@ -27,6 +27,13 @@
  *   The notes say an implementation adds a small eps to the (positive) denominator;
  *   eps is an argument here.  No input scaling is applied (the caller pre-scales).
  *
+ *   BASED_COMPACT  the same recurrence with the compact map of the same notes' feature-
+ *   width table (Sec. 2.3): every cross term once,
+ *     phi_c(x) = [1, x, (x_a^2/sqrt(2) if a == b else x_a x_b) for a <= b]
+ *   (D = 1 + d' + d'(d'+1)/2; the pairs in row-major upper-triangle order, a outer:
+ *   index 1 + d' + a d' - a(a-1)/2 + (b - a)).  phi_c(q).phi_c(k) equals
+ *   phi(q).phi(k), so the outputs are those of BASED; only the state layout differs.
+ *
  * Because A_t acts on the right of S, every row i of S (a d_k-vector) evolves on its
  * own:  s_i <- s_i A_t + beta_t v_t[i] k_t^T,  o_t[i] = s_i . q_t.  For the gated delta
  * rule  s_i A_t = alpha_t (s_i - beta_t (s_i . k_t) k_t^T).  The routines below walk
@@ -37,7 +44,7 @@
  * Layouts (row-major, last index fastest), identical to the library's:
  *   q, k  [B][H][T][d_k]     v, o  [B][H][T][d_v]     alpha, beta  [B][H][T]
  *   S     [B][H][d_v][d_k]   (ADDITIVE / GATED / GATED_DELTA)
- *   s     [B][H][D][d_v],  z [B][H][D]                (BASED, d_k = d')
+ *   s     [B][H][D][d_v],  z [B][H][D]                (BASED / BASED_COMPACT, d_k = d')
  */
 #include <math.h>
 #include <stddef.h>
@@ -48,7 +55,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_ADDITIVE = 0, OR_BASED = 1, OR_GATED = 2, OR_GATED_DELTA = 3 };
+enum { OR_ADDITIVE = 0, OR_BASED = 1, OR_GATED = 2, OR_GATED_DELTA = 3, OR_BASED_COMPACT = 4 };
 
 int oracle_version(void) { return 1; }
 
@@ -116,18 +123,33 @@ static void based_phi(const double *x, int dp, double *f) {
 
 void oracle_based_phi(const double *x, int dp, double *f) { based_phi(x, dp, f); }
 
+/* Compact BASED feature map: [1, x, then for a <= b: x_a^2/sqrt(2) (a == b) or x_a x_b],
+ * D = 1 + d' + d'(d'+1)/2. */
+static void based_phi_compact(const double *x, int dp, double *f) {
+  const double inv_sqrt2 = 1.0 / sqrt(2.0);
+  int n = 0;
+  f[n++] = 1.0;
+  for (int i = 0; i < dp; ++i) f[n++] = x[i];
+  for (int a = 0; a < dp; ++a)
+    for (int b = a; b < dp; ++b) f[n++] = (a == b) ? x[a] * x[a] * inv_sqrt2 : x[a] * x[b];
+}
+void oracle_based_phi_compact(const double *x, int dp, double *f) { based_phi_compact(x, dp, f); }
+
+static int based_dim(int dp, int compact) { return compact ? 1 + dp + dp * (dp + 1) / 2 : 1 + dp + dp * dp; }
+
 /* One (b,h) slice of BASED through T tokens for a subset of value columns.
  *   s : [D][ncols] (in = s0 restricted to cols, out = s_T), z : [D] (in/out)
  *   o : [T][ncols]                                                              */
-static void based_slice(long T, int dp, int dv, const int *cols, int ncols, const double *q,
-                        const double *k, const double *v, double eps, double *s, double *z,
-                        double *o) {
-  const int D = 1 + dp + dp * dp;
+static void based_slice(int compact, long T, int dp, int dv, const int *cols, int ncols,
+                        const double *q, const double *k, const double *v, double eps, double *s,
+                        double *z, double *o) {
+  const int D = based_dim(dp, compact);
+  void (*phi)(const double *, int, double *) = compact ? based_phi_compact : based_phi;
   double *fk = (double *)malloc(sizeof(double) * D);
   double *fq = (double *)malloc(sizeof(double) * D);
   for (long t = 0; t < T; ++t) {
-    based_phi(k + (size_t)t * dp, dp, fk);
-    based_phi(q + (size_t)t * dp, dp, fq);
+    phi(k + (size_t)t * dp, dp, fk);
+    phi(q + (size_t)t * dp, dp, fq);
     /* s_t = s_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t) */
     for (int f = 0; f < D; ++f) {
       for (int c = 0; c < ncols; ++c) s[(size_t)f * ncols + c] += fk[f] * v[(size_t)t * dv + cols[c]];
@@ -165,14 +187,15 @@ int oracle_prefill(int variant, int B, int H, long T, int dk, int dv, const doub
   if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || !q || !k || !v || !o) return -1;
   if ((variant == OR_GATED || variant == OR_GATED_DELTA) && !alpha) return -1;
   if (variant == OR_GATED_DELTA && !beta) return -1;
-  if (variant < 0 || variant > 3) return -1;
+  if (variant < 0 || variant > 4) return -1;
   const int nr = rows ? nrows : dv;
   for (int i = 0; i < nr; ++i)
     if (rows && (rows[i] < 0 || rows[i] >= dv)) return -1;
   set_threads(nthreads);
 
-  if (variant == OR_BASED) {
-    const int dp = dk, D = 1 + dp + dp * dp;
+  if (variant == OR_BASED || variant == OR_BASED_COMPACT) {
+    const int compact = variant == OR_BASED_COMPACT;
+    const int dp = dk, D = based_dim(dp, compact);
     int *cols = (int *)malloc(sizeof(int) * nr);
     for (int c = 0; c < nr; ++c) cols[c] = rows ? rows[c] : c;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -186,8 +209,8 @@ int oracle_prefill(int variant, int B, int H, long T, int dk, int dv, const doub
             for (int c = 0; c < nr; ++c) s[(size_t)f * nr + c] = S0[(bh * D + f) * dv + cols[c]];
         if (z0)
           for (int f = 0; f < D; ++f) z[f] = z0[bh * D + f];
-        based_slice(T, dp, dv, cols, nr, q + bh * T * dp, k + bh * T * dp, v + bh * T * dv, eps,
-                    s, z, o + bh * T * nr);
+        based_slice(compact, T, dp, dv, cols, nr, q + bh * T * dp, k + bh * T * dp, v + bh * T * dv,
+                    eps, s, z, o + bh * T * nr);
         if (S_T) memcpy(S_T + bh * D * nr, s, sizeof(double) * D * nr);
         if (z_T) memcpy(z_T + bh * D, z, sizeof(double) * D);
         free(s);
@@ -238,7 +261,7 @@ int oracle_decode_step(int variant, int N, int dk, int dv, const double *S_in, c
 int oracle_literal(int variant, long T, int dk, int dv, const double *q, const double *k,
                    const double *v, const double *alpha, const double *beta, const double *S0,
                    double *o, double *S_T) {
-  if (variant == OR_BASED || variant < 0 || variant > 3) return -1;
+  if (variant == OR_BASED || variant < 0 || variant > 3) return -1;  /* not the BASED maps */
   double *S = (double *)calloc((size_t)dv * dk, sizeof(double));
   double *Sn = (double *)malloc(sizeof(double) * dv * dk);
   double *A = (double *)malloc(sizeof(double) * dk * dk);

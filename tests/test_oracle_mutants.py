@@ -33,6 +33,11 @@ MUTANTS = [
     ("based_square_only", "f[1 + dp + i * dp + j] = x[i] * x[j] * inv_sqrt2;", "f[1 + dp + i * dp + j] = x[i] * x[i] * inv_sqrt2;"),
     ("based_den_uses_key", "for (int f = 0; f < D; ++f) den += z[f] * fq[f];", "for (int f = 0; f < D; ++f) den += z[f] * fk[f];"),
     ("based_read_before_write_z", "z[f] += fk[f];\n    }", "z[f] += 0.0 * fk[f];\n    }"),
+    ("compact_square_unscaled", "f[n++] = (a == b) ? x[a] * x[a] * inv_sqrt2 : x[a] * x[b];",
+     "f[n++] = (a == b) ? x[a] * x[a] : x[a] * x[b];"),
+    ("compact_cross_scaled", "f[n++] = (a == b) ? x[a] * x[a] * inv_sqrt2 : x[a] * x[b];",
+     "f[n++] = (a == b) ? x[a] * x[a] * inv_sqrt2 : x[a] * x[b] * inv_sqrt2;"),
+    ("compact_lower_triangle", "for (int b = a; b < dp; ++b) f[n++]", "for (int b = 0; b <= a; ++b) f[n++]"),
     ("start_state_ignored", "memcpy(s, S0 + (bh * dv + row) * dk, sizeof(double) * dk);",
      "memset(s, 0, sizeof(double) * dk);"),
 ]

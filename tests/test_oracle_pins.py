@@ -101,6 +101,44 @@ def test_taylor_scaled_closed_form():
         assert abs(val - (1 + t / math.sqrt(dp) + t * t / (2 * dp))) < 1e-12 * (1 + t * t)
 
 
+def _compact_pairs(dp):
+    """(a, b) of every compact order-2 feature, in its stored order: row-major upper triangle."""
+    return [(a, b) for a in range(dp) for b in range(a, dp)]
+
+
+def test_compact_feature_map_layout_and_kernel():
+    """The compact map keeps x_a^2/sqrt 2 and x_a x_b (a < b) once each, after [1, x], and has
+    the kernel value of the full map: phi_c(q).phi_c(k) = 1 + q.k + (q.k)^2/2."""
+    r = rng(21)
+    dp = 16
+    assert oracle.feature_dim(dp, compact=True) == GOLDEN["based_feature_dim_compact_dprime16"]["value"]
+    x = r.standard_normal(dp)
+    f = oracle.based_phi_compact(x)
+    assert f.size == 153 and f[0] == 1.0 and np.array_equal(f[1:1 + dp], x)
+    for i, (a, b) in enumerate(_compact_pairs(dp)):
+        want = x[a] * x[a] / math.sqrt(2) if a == b else x[a] * x[b]
+        assert abs(f[1 + dp + i] - want) <= 1e-15 * max(1.0, abs(want))
+    worst = 0.0
+    for _ in range(10_000):
+        x, y = r.standard_normal(dp), r.standard_normal(dp)
+        t = float(x @ y)
+        kern = 1.0 + t + t * t / 2.0
+        worst = max(worst, abs(oracle.based_phi_compact(x) @ oracle.based_phi_compact(y) - kern) / abs(kern))
+    assert worst < 1e-13
+
+
+def test_compact_scaled_closed_form():
+    """The scaled identity holds for the compact map too (inputs pre-scaled by d'^(-1/4))."""
+    r = rng(22)
+    dp = 16
+    for _ in range(1000):
+        x, y = r.standard_normal(dp), r.standard_normal(dp)
+        t = float(x @ y)
+        s = dp ** 0.25
+        val = oracle.based_phi_compact(x / s) @ oracle.based_phi_compact(y / s)
+        assert abs(val - (1 + t / math.sqrt(dp) + t * t / (2 * dp))) < 1e-12 * (1 + t * t)
+
+
 def test_taylor_positivity():
     """((t+1)^2+1)/2 >= 1/2: every kernel term is at least 1/2."""
     t = np.linspace(-50, 50, 100001)
@@ -157,6 +195,40 @@ def test_based_start_state_equals_prefix():
     k = r.standard_normal((1, 1, T, dp))
     v = r.standard_normal((1, 1, T, dv))
     o, _, _ = oracle.prefill("based", q, k, v, S0=s0, z0=z0, eps=1e-6)
+    ref, _ = _based_bruteforce(q[0, 0], k[0, 0], v[0, 0], 1e-6, prefix=(kp[0, 0], vp[0, 0]))
+    assert rel(o[0, 0], ref) < 1e-12
+
+
+def test_compact_matches_bruteforce_and_full_state():
+    """Compact BASED: outputs equal brute force; its end state is the full one with each
+    unordered pair folded, (s(a,b) + s(b,a)) / sqrt 2, and the squares kept."""
+    r = rng(23)
+    B, H, T, dp, dv = 1, 2, 48, 4, 3
+    q = r.standard_normal((B, H, T, dp)) / 2
+    k = r.standard_normal((B, H, T, dp)) / 2
+    v = r.standard_normal((B, H, T, dv))
+    eps = 1e-6
+    oc, sc, zc = oracle.prefill("based_compact", q, k, v, eps=eps)
+    of, sf, zf = oracle.prefill("based", q, k, v, eps=eps)
+    for h in range(H):
+        ref, _ = _based_bruteforce(q[0, h], k[0, h], v[0, h], eps)
+        assert rel(oc[0, h], ref) < 1e-12
+    assert rel(oc, of) < 1e-12
+    for i, (a, b) in enumerate(_compact_pairs(dp)):
+        fa, fb = 1 + dp + a * dp + b, 1 + dp + b * dp + a
+        want_s = sf[:, :, fa] if a == b else (sf[:, :, fa] + sf[:, :, fb]) / math.sqrt(2)
+        want_z = zf[:, :, fa] if a == b else (zf[:, :, fa] + zf[:, :, fb]) / math.sqrt(2)
+        assert rel(sc[:, :, 1 + dp + i], want_s) < 1e-12 and rel(zc[:, :, 1 + dp + i], want_z) < 1e-12
+    assert rel(sc[:, :, :1 + dp], sf[:, :, :1 + dp]) < 1e-12 and rel(zc[:, :, :1 + dp], zf[:, :, :1 + dp]) < 1e-12
+
+
+def test_compact_start_state_equals_prefix():
+    r = rng(24)
+    dp, dv, P, T = 3, 2, 20, 30
+    kp, qp, vp = r.standard_normal((1, 1, P, dp)), r.standard_normal((1, 1, P, dp)), r.standard_normal((1, 1, P, dv))
+    _, s0, z0 = oracle.prefill("based_compact", qp, kp, vp)
+    q, k, v = r.standard_normal((1, 1, T, dp)), r.standard_normal((1, 1, T, dp)), r.standard_normal((1, 1, T, dv))
+    o, _, _ = oracle.prefill("based_compact", q, k, v, S0=s0, z0=z0, eps=1e-6)
     ref, _ = _based_bruteforce(q[0, 0], k[0, 0], v[0, 0], 1e-6, prefix=(kp[0, 0], vp[0, 0]))
     assert rel(o[0, 0], ref) < 1e-12
 
@@ -306,7 +378,7 @@ def test_segment_scan_matches_sequential(variant):
     assert rel(os_, o[0, 0]) < 1e-10 and rel(Ss, S_T[0, 0]) < 1e-10
 
 
-@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based"])
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based", "based_compact"])
 def test_split_resume(variant):
     """prefill(x[:a]) -> S_a; prefill(x[a:], S0=S_a) == prefill(x)."""
     r = rng(15)
@@ -324,7 +396,7 @@ def test_split_resume(variant):
         assert rel(z2, z) < 1e-12
 
 
-@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based"])
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based", "based_compact"])
 def test_prefill_then_decode_equals_longer_prefill(variant):
     r = rng(16)
     T, n, dk, dv = 20, 5, 4, 3
@@ -355,7 +427,7 @@ def test_linear_in_values_and_start_state(variant):
     assert rel(oc, c1 * oa + c2 * ob) < 1e-12 and rel(Sc, c1 * Sa + c2 * Sb) < 1e-12
 
 
-@pytest.mark.parametrize("variant", ["gated_delta", "based"])
+@pytest.mark.parametrize("variant", ["gated_delta", "based", "based_compact"])
 def test_row_subset_matches_full(variant):
     """The sampled-rows path (used for long-sequence parity) returns the same numbers."""
     r = rng(18)
@@ -365,7 +437,7 @@ def test_row_subset_matches_full(variant):
     o, S, z = oracle.prefill(variant, q, k, v, alpha, beta)
     os_, Ss, zs = oracle.prefill(variant, q, k, v, alpha, beta, rows=rows)
     assert np.array_equal(os_, o[..., rows])
-    if variant == "based":
+    if variant.startswith("based"):
         assert np.array_equal(Ss, S[..., rows]) and np.array_equal(zs, z)
     else:
         assert np.array_equal(Ss, S[:, :, rows, :])
