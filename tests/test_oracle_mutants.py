@@ -28,7 +28,8 @@ MUTANTS = [
     ("read_previous_query", "const double *qt = q + (size_t)t * dk;\n    const double vt",
      "const double *qt = q + (size_t)(t > 0 ? t - 1 : 0) * dk;\n    const double vt"),
     ("value_row_index", "const double vt = v[(size_t)t * dv + row];", "const double vt = v[(size_t)t * dv + (dv - 1 - row)];"),
-    ("based_feature_scale", "const double inv_sqrt2 = 1.0 / sqrt(2.0);", "const double inv_sqrt2 = 0.5;"),
+    ("based_feature_scale", "const double inv_sqrt2 = 1.0 / sqrt(2.0);\n  f[0] = 1.0;",
+     "const double inv_sqrt2 = 0.5;\n  f[0] = 1.0;"),
     ("based_no_constant_feature", "f[0] = 1.0;", "f[0] = 0.0;"),
     ("based_square_only", "f[1 + dp + i * dp + j] = x[i] * x[j] * inv_sqrt2;", "f[1 + dp + i * dp + j] = x[i] * x[i] * inv_sqrt2;"),
     ("based_den_uses_key", "for (int f = 0; f < D; ++f) den += z[f] * fq[f];", "for (int f = 0; f < D; ++f) den += z[f] * fk[f];"),
