@@ -16,8 +16,9 @@ from pathlib import Path
 
 import torch
 
-ADDITIVE, BASED, GATED, GATED_DELTA = 0, 1, 2, 3
-VARIANTS = {"additive": ADDITIVE, "based": BASED, "gated": GATED, "gated_delta": GATED_DELTA}
+ADDITIVE, BASED, GATED, GATED_DELTA, BASED_COMPACT = 0, 1, 2, 3, 4
+VARIANTS = {"additive": ADDITIVE, "based": BASED, "gated": GATED, "gated_delta": GATED_DELTA,
+            "based_compact": BASED_COMPACT}
 F32, BF16 = 0, 1
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_INVALID", -3: "LA_ERR_UNSUPPORTED",
           -4: "LA_ERR_ALIGN", -5: "LA_ERR_WORKSPACE", -6: "LA_ERR_ALIAS", -7: "LA_ERR_HIP"}
@@ -93,8 +94,9 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def feature_dim(dp: int) -> int:
-    return 1 + dp + dp * dp
+def feature_dim(dp: int, compact: bool = False) -> int:
+    """State rows of the BASED variants: 1 + d' + d'^2, or 1 + d' + d'(d'+1)/2 (compact)."""
+    return 1 + dp + dp * (dp + 1) // 2 if compact else 1 + dp + dp * dp
 
 
 def workspace_size(variant, dtype, B, H, T, d_k, d_v) -> int:
@@ -129,8 +131,8 @@ def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6,
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
     if want_state and S_T is None:
-        if var == BASED:
-            D = feature_dim(dk)
+        if var in (BASED, BASED_COMPACT):
+            D = feature_dim(dk, var == BASED_COMPACT)
             S_T = torch.empty((B, H, D, dv), dtype=torch.float32, device=dev)
             z_T = torch.empty((B, H, D), dtype=torch.float32, device=dev) if z_T is None else z_T
         else:
@@ -161,7 +163,7 @@ def decode_step(variant, S, q, k, v, alpha=None, beta=None, z=None, eps=1e-6, S_
         o = torch.empty((N, dv), dtype=q.dtype, device=q.device)
     if S_out is None:
         S_out = torch.empty_like(S)
-    if var == BASED and z_out is None:
+    if var in (BASED, BASED_COMPACT) and z_out is None:
         z_out = torch.empty_like(z)
     st = lib.la_decode_step(var, dt, N, dk, dv, float(eps), _p(S), _p(z), _p(S_out), _p(z_out),
                             _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(o), _stream(stream))

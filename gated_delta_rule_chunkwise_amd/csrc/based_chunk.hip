@@ -1,5 +1,5 @@
 // based_chunk.hip -- chunkwise bf16 prefill for BASED Taylor linear attention (d' = 16,
-// d_v = 64, D = 273 features).
+// d_v = 64; states in the full D = 273 or the compact D = 153 feature layout).
 //
 // What is computed ("Simple linear attention language models balance the
 // recall-throughput tradeoff", reading notes Sec. 2.2-2.3, paper Eqs. (1)-(4)):
@@ -70,47 +70,64 @@ struct Args {
   float *starts;         // [BH][nseg][NF][DV + 1] segment start states (internal order)
   int64_t T;
   int H, nseg, seg_chunks;
+  int compact;           // ABI state layout: 0 = full (D = 273), 1 = compact (D = 153)
+  int Dabi;              // ABI feature count, 273 or 153
   float eps;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// The ABI features whose sum is internal feature fi: f1 and f2 (-1 = none).  f2 >= 0 only
-// for the symmetrised pairs, whose ABI rows (a, b) = f1 and (b, a) = f2 are both written
-// back from the one internal row.
-__device__ __forceinline__ void abi_pair(int fi, int &f1, int &f2) {
+// Compact ABI index of the pair a <= b (row-major upper triangle after [1, x]).
+__device__ __forceinline__ int compact_index(int a, int b) { return 1 + DP + a * DP - a * (a - 1) / 2 + (b - a); }
+
+// The ABI rows behind internal feature fi: internal = w (row f1 + row f2), f1, f2 = -1 for
+// none.  Full layout: f2 >= 0 only for the symmetrised pairs, whose ABI rows (a, b) = f1
+// and (b, a) = f2 are both written back from the one internal row (w = 1).  Compact
+// layout (LA_BASED_COMPACT): one ABI row per pair; for a < b the internal row holds
+// sqrt 2 times it (its key feature is sqrt 2 k_a k_b against the compact map's k_a k_b),
+// so w = sqrt 2; the squares, x and the constant map one to one.
+__device__ __forceinline__ void abi_pair(int fi, bool compact, int &f1, int &f2, float &w) {
   const int t = fi >> 4, r = fi & 15;
   f1 = -1;
   f2 = -1;
+  w = 1.0f;
   if (t == T_LIN) {
     f1 = 1 + r;
   } else if (t == ND - 1 && r >= DP / 2) {
     if (r == DP / 2) f1 = 0;  // the constant
   } else {
     const int b = (r + t) & 15;
-    f1 = 1 + DP + DP * r + b;
-    if (t != 0) f2 = 1 + DP + DP * b + r;
+    if (compact) {
+      f1 = compact_index(r < b ? r : b, r < b ? b : r);
+      if (t != 0) w = 1.41421356237309505f;
+    } else {
+      f1 = 1 + DP + DP * r + b;
+      if (t != 0) f2 = 1 + DP + DP * b + r;
+    }
   }
 }
 
 // Internal feature fi of a state read in ABI layout (NULL = zero state).
-__device__ __forceinline__ float abi_load(const float *src, int fi, int stride, int col) {
+__device__ __forceinline__ float abi_load(const float *src, bool compact, int fi, int stride, int col) {
   if (!src) return 0.0f;
   int f1, f2;
-  abi_pair(fi, f1, f2);
+  float w;
+  abi_pair(fi, compact, f1, f2, w);
   float x = f1 >= 0 ? src[(size_t)f1 * stride + col] : 0.0f;
   if (f2 >= 0) x += src[(size_t)f2 * stride + col];
-  return x;
+  return w * x;
 }
 
 // Internal feature fi with value x written back in ABI layout; src is the start state
 // the symmetrised rows began from (NULL = zero), whose antisymmetric part is restored.
-__device__ __forceinline__ void abi_store(float *dst, const float *src, int fi, int stride, int col, float x) {
+__device__ __forceinline__ void abi_store(float *dst, const float *src, bool compact, int fi, int stride,
+                                          int col, float x) {
   int f1, f2;
-  abi_pair(fi, f1, f2);
+  float w;
+  abi_pair(fi, compact, f1, f2, w);
   if (f1 < 0) return;
   if (f2 < 0) {
-    dst[(size_t)f1 * stride + col] = x;
+    dst[(size_t)f1 * stride + col] = w == 1.0f ? x : x * 0.70710678118654752f;
     return;
   }
   const float asym = src ? src[(size_t)f1 * stride + col] - src[(size_t)f2 * stride + col] : 0.0f;
@@ -203,17 +220,17 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     // the replay starts segment 0 from S0 (ABI layout), later segments from the scan's
     // start states; the map pass starts from zero
     const float *src_i = (OUT && seg > 0) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
-    const float *src_a = (OUT && seg == 0 && a.s0) ? a.s0 + bh * (size_t)D * DV : nullptr;
+    const float *src_a = (OUT && seg == 0 && a.s0) ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
 #pragma unroll
     for (int m = 0; m < NFT; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int fi = 16 * m + 4 * g + e, col = 16 * n_col + l16;
-        st[m][e] = src_i ? src_i[(size_t)fi * (DV + 1) + col] : abi_load(src_a, fi, DV, col);
+        st[m][e] = src_i ? src_i[(size_t)fi * (DV + 1) + col] : abi_load(src_a, a.compact, fi, DV, col);
       }
     for (int fi = tid; fi < NF; fi += NTHR) {
       sZ[fi] = src_i ? src_i[(size_t)fi * (DV + 1) + DV]
-                     : abi_load(OUT && seg == 0 && a.z0 ? a.z0 + bh * D : nullptr, fi, 1, 0);
+                     : abi_load(OUT && seg == 0 && a.z0 ? a.z0 + bh * a.Dabi : nullptr, a.compact, fi, 1, 0);
     }
   }
 
@@ -510,14 +527,15 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     if (seg == a.nseg - 1 && a.s_T) {  // the last segment's end state is S_T
       __syncthreads();
       const int l16 = lane & 15, g = lane >> 4;
-      const float *s0 = a.s0 ? a.s0 + bh * (size_t)D * DV : nullptr;
-      const float *z0 = a.z0 ? a.z0 + bh * D : nullptr;
+      const float *s0 = a.s0 ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
+      const float *z0 = a.z0 ? a.z0 + bh * a.Dabi : nullptr;
 #pragma unroll
       for (int m = 0; m < NFT; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          abi_store(a.s_T + bh * (size_t)D * DV, s0, 16 * m + 4 * g + e, DV, 16 * n_col + l16, st[m][e]);
-      for (int fi = tid; fi < NF; fi += NTHR) abi_store(a.z_T + bh * D, z0, fi, 1, 0, sZ[fi]);
+          abi_store(a.s_T + bh * (size_t)a.Dabi * DV, s0, a.compact, 16 * m + 4 * g + e, DV, 16 * n_col + l16,
+                    st[m][e]);
+      for (int fi = tid; fi < NF; fi += NTHR) abi_store(a.z_T + bh * a.Dabi, z0, a.compact, fi, 1, 0, sZ[fi]);
     }
   } else {
     __syncthreads();
@@ -542,9 +560,9 @@ __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
   for (int id = blockIdx.x * 256 + threadIdx.x; id < NE; id += gridDim.x * 256) {
     const int fi = id / (DV + 1), col = id % (DV + 1);
     // the start state and the end state's ABI place of this element: s[f][col] or z[f]
-    const float *src = col < DV ? (a.s0 ? a.s0 + bh * (size_t)D * DV : nullptr) : (a.z0 ? a.z0 + bh * D : nullptr);
+    const float *src = col < DV ? (a.s0 ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr) : (a.z0 ? a.z0 + bh * a.Dabi : nullptr);
     const int stride = col < DV ? DV : 1, c = col < DV ? col : 0;
-    float x = abi_load(src, fi, stride, c);
+    float x = abi_load(src, a.compact, fi, stride, c);
     const int nmap = a.nseg - 1;  // segments with a map
     for (int i0 = 0; i0 < nmap; i0 += UNR) {
       float d[UNR];
@@ -592,10 +610,10 @@ void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks) {
   *seg_chunks = p.seg_chunks;
 }
 
-hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const void *q,
-                                      const void *k, const void *v, const float *s0,
-                                      const float *z0, void *o, float *s_T, float *z_T,
-                                      void *workspace, int pass_mask, hipStream_t s) {
+hipError_t launch_based_chunk_prefill(bool compact, int B, int H, int64_t T, float eps,
+                                      const void *q, const void *k, const void *v,
+                                      const float *s0, const float *z0, void *o, float *s_T,
+                                      float *z_T, void *workspace, int pass_mask, hipStream_t s) {
   using namespace based;
   const Plan p = make_plan(B, H, T);
   Args a;
@@ -614,6 +632,8 @@ hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const 
   a.H = H;
   a.nseg = p.nseg;
   a.seg_chunks = p.seg_chunks;
+  a.compact = compact ? 1 : 0;
+  a.Dabi = compact ? 1 + DP + DP * (DP + 1) / 2 : D;
   a.eps = eps;
   const dim3 grid(p.nseg, H, B);
   if (p.nseg > 1 && (pass_mask & PASS_MAPS))  // every segment but the last

@@ -108,10 +108,21 @@ __global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_be
   }
 }
 
-// BASED decode: one workgroup (NT threads) per state, d' = 16, d_v = 64, D = 273.
-// Thread t owns value columns 4(t%16)..+3 for the features f = t/16 + (NT/16) i, so
-// every wave-wide access to s covers four whole 256-byte feature rows.
-template <int NT, typename T>
+// Pair (a, b), a <= b, of compact order-2 feature idx (row-major upper triangle of n x n).
+__device__ __forceinline__ void triangle_pair(int idx, int n, int &a, int &b) {
+  a = 0;
+  while (idx >= n - a) {
+    idx -= n - a;
+    ++a;
+  }
+  b = a + idx;
+}
+
+// BASED decode: one workgroup (NT threads) per state, d' = 16, d_v = 64, D = 273 (or the
+// compact D = 153: [1, x, x_a^2/sqrt 2 and x_a x_b for a < b]).  Thread t owns value
+// columns 4(t%16)..+3 for the features f = t/16 + (NT/16) i, so every wave-wide access
+// to s covers four whole 256-byte feature rows.
+template <int NT, bool COMPACT, typename T>
 __global__ __launch_bounds__(NT) void decode_based_kernel(float eps, const float *__restrict__ S_in,
                                                            const float *__restrict__ z_in,
                                                            float *S_out, float *z_out,
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(NT) void decode_based_kernel(float eps, const float
                                                            const T *__restrict__ k,
                                                            const T *__restrict__ v,
                                                            T *__restrict__ o) {
-  constexpr int DP = 16, DV = 64, D = 1 + DP + DP * DP;
+  constexpr int DP = 16, DV = 64, D = COMPACT ? 1 + DP + DP * (DP + 1) / 2 : 1 + DP + DP * DP;
   constexpr int NW = NT / 64, FS = NT / 16;
   __shared__ float xk[DP], xq[DP];
   __shared__ float phk[D], phq[D];
@@ -136,7 +147,13 @@ __global__ __launch_bounds__(NT) void decode_based_kernel(float eps, const float
     float fk, fq;
     if (f == 0) { fk = 1.0f; fq = 1.0f; }
     else if (f <= DP) { fk = xk[f - 1]; fq = xq[f - 1]; }
-    else {
+    else if (COMPACT) {
+      int i, j;
+      triangle_pair(f - 1 - DP, DP, i, j);
+      const float w = i == j ? rs2 : 1.0f;
+      fk = xk[i] * xk[j] * w;
+      fq = xq[i] * xq[j] * w;
+    } else {
       const int i = (f - 1 - DP) >> 4, j = (f - 1 - DP) & 15;
       fk = xk[i] * xk[j] * rs2;
       fq = xq[i] * xq[j] * rs2;
@@ -254,15 +271,22 @@ hipError_t launch_decode_rows(int variant, int dtype, int n, int d_k, int d_v, c
 // Four waves per state: eight (512 threads, nine features per thread) measured no faster.
 constexpr int BASED_NT = 256;
 
-hipError_t launch_decode_based(int dtype, int n, float eps, const float *S_in, const float *z_in,
-                               float *S_out, float *z_out, const void *q, const void *k,
-                               const void *v, void *o, hipStream_t s) {
+template <bool COMPACT>
+static void go_based(int dtype, int n, float eps, const float *S_in, const float *z_in, float *S_out,
+                     float *z_out, const void *q, const void *k, const void *v, void *o, hipStream_t s) {
   if (dtype == T_BF16)
-    hipLaunchKernelGGL((decode_based_kernel<BASED_NT, bf16_t>), dim3(n), dim3(BASED_NT), 0, s, eps, S_in, z_in, S_out,
-                       z_out, (const bf16_t *)q, (const bf16_t *)k, (const bf16_t *)v, (bf16_t *)o);
+    hipLaunchKernelGGL((decode_based_kernel<BASED_NT, COMPACT, bf16_t>), dim3(n), dim3(BASED_NT), 0, s, eps, S_in,
+                       z_in, S_out, z_out, (const bf16_t *)q, (const bf16_t *)k, (const bf16_t *)v, (bf16_t *)o);
   else
-    hipLaunchKernelGGL((decode_based_kernel<BASED_NT, float>), dim3(n), dim3(BASED_NT), 0, s, eps, S_in, z_in, S_out,
-                       z_out, (const float *)q, (const float *)k, (const float *)v, (float *)o);
+    hipLaunchKernelGGL((decode_based_kernel<BASED_NT, COMPACT, float>), dim3(n), dim3(BASED_NT), 0, s, eps, S_in,
+                       z_in, S_out, z_out, (const float *)q, (const float *)k, (const float *)v, (float *)o);
+}
+
+hipError_t launch_decode_based(int dtype, bool compact, int n, float eps, const float *S_in,
+                               const float *z_in, float *S_out, float *z_out, const void *q,
+                               const void *k, const void *v, void *o, hipStream_t s) {
+  if (compact) go_based<true>(dtype, n, eps, S_in, z_in, S_out, z_out, q, k, v, o, s);
+  else go_based<false>(dtype, n, eps, S_in, z_in, S_out, z_out, q, k, v, o, s);
   return hipGetLastError();
 }
 

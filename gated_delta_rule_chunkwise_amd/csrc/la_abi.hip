@@ -38,15 +38,16 @@ bool overlap(Range a, Range b) {
 
 bool misaligned(const void *p, uintptr_t align = 16) { return p && ((uintptr_t)p & (align - 1)) != 0; }
 
-int based_D(int dp) { return 1 + dp + dp * dp; }
+bool is_based(int variant) { return variant == LA_BASED || variant == LA_BASED_COMPACT; }
+int based_D(int dp, bool compact) { return compact ? 1 + dp + dp * (dp + 1) / 2 : 1 + dp + dp * dp; }
 
 // Shared shape checks for prefill; returns LA_OK or an error.
 int check_prefill_shape(int variant, int dtype, int B, int H, int64_t T, int dk, int dv) {
-  if (variant < LA_ADDITIVE || variant > LA_GATED_DELTA) return LA_ERR_INVALID;
+  if (variant < LA_ADDITIVE || variant > LA_BASED_COMPACT) return LA_ERR_INVALID;
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
   if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0) return LA_ERR_INVALID;
   if ((int64_t)B * H > (int64_t)INT32_MAX / 4) return LA_ERR_UNSUPPORTED;
-  if (variant == LA_BASED) {
+  if (is_based(variant)) {
     if (dk != 16 || dv != 64) return LA_ERR_UNSUPPORTED;
     return LA_OK;
   }
@@ -60,7 +61,7 @@ int check_prefill_shape(int variant, int dtype, int B, int H, int64_t T, int dk,
 
 size_t prefill_ws(int variant, int dtype, int B, int H, int64_t T, int dk, int dv) {
   if (dtype != LA_BF16 || T == 0) return 0;
-  if (variant == LA_BASED) return based_chunk_workspace_bytes(B, H, T);
+  if (is_based(variant)) return based_chunk_workspace_bytes(B, H, T);
   return chunk_workspace_bytes(variant, B, H, T, dk, dv);
 }
 
@@ -106,7 +107,7 @@ static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int he
   if (st != LA_OK) return st;
   const int B = batch, H = heads;
   const int64_t T = seq_len;
-  const bool based = variant == LA_BASED;
+  const bool based = is_based(variant), compact = variant == LA_BASED_COMPACT;
   // variant-specific pointer rules
   if (variant == LA_ADDITIVE || based) {
     if (alpha || beta) return LA_ERR_INVALID;
@@ -130,7 +131,7 @@ static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int he
   if (misaligned(alpha, es) || misaligned(beta, es)) return LA_ERR_ALIGN;
 
   const size_t BH = (size_t)B * H;
-  const size_t D = based ? (size_t)based_D(d_k) : 0;
+  const size_t D = based ? (size_t)based_D(d_k, compact) : 0;
   const size_t state_n = based ? BH * D * d_v : BH * d_v * d_k;
   const Range rq{q, BH * T * d_k * es}, rk{k, BH * T * d_k * es}, rv{v, BH * T * d_v * es};
   const Range ra{alpha, BH * T * es}, rb{beta, BH * T * es};
@@ -160,9 +161,10 @@ static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int he
   }
   if (based) {
     if (dtype == LA_BF16)
-      e = launch_based_chunk_prefill(B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, workspace, pass_mask, s);
+      e = launch_based_chunk_prefill(compact, B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, workspace,
+                                     pass_mask, s);
     else if (pass_mask & PASS_REPLAY)
-      e = launch_recurrent_based(dtype, B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, s);
+      e = launch_recurrent_based(dtype, compact, B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, s);
   } else if (dtype == LA_BF16) {
     e = launch_chunk_prefill(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, workspace,
                              pass_mask, s);
@@ -205,7 +207,7 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
   *n_segments = 1;
   *chunks_per_segment = 0;
   if (dtype != LA_BF16 || seq_len == 0) return LA_OK;
-  if (variant == LA_BASED)
+  if (is_based(variant))
     based_chunk_segments(batch, heads, seq_len, n_segments, chunks_per_segment);
   else if (d_k == 128 && d_v == 128)
     chunk_segments(batch, heads, seq_len, n_segments, chunks_per_segment);
@@ -216,10 +218,10 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
 int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, const float *S_in,
                    const float *z_in, float *S_out, float *z_out, const void *q, const void *k,
                    const void *v, const void *alpha, const void *beta, void *o, void *stream) {
-  if (variant < LA_ADDITIVE || variant > LA_GATED_DELTA) return LA_ERR_INVALID;
+  if (variant < LA_ADDITIVE || variant > LA_BASED_COMPACT) return LA_ERR_INVALID;
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
   if (n <= 0 || d_k <= 0 || d_v <= 0) return LA_ERR_INVALID;
-  const bool based = variant == LA_BASED;
+  const bool based = is_based(variant), compact = variant == LA_BASED_COMPACT;
   if (based) {
     if (d_k != 16 || d_v != 64) return LA_ERR_UNSUPPORTED;
   } else if (d_k != 64 && d_k != 128 && d_k != 256) {
@@ -243,7 +245,7 @@ int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, c
   const void *tp[] = {q, k, v, alpha, beta, o};
   for (const void *p : tp)
     if (misaligned(p, es)) return LA_ERR_ALIGN;
-  const size_t D = based ? (size_t)based_D(d_k) : 0;
+  const size_t D = based ? (size_t)based_D(d_k, compact) : 0;
   const size_t state_n = based ? (size_t)n * D * d_v : (size_t)n * d_v * d_k;
   const Range rSi{S_in, state_n * 4}, rzi{z_in, (size_t)n * D * 4};
   const Range rSo{S_out, state_n * 4}, rzo{z_out, (size_t)n * D * 4};
@@ -262,7 +264,7 @@ int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, c
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (based)
-    e = launch_decode_based(dtype, n, eps, S_in, z_in, S_out, z_out, q, k, v, o, s);
+    e = launch_decode_based(dtype, compact, n, eps, S_in, z_in, S_out, z_out, q, k, v, o, s);
   else
     e = launch_decode_rows(variant, dtype, n, d_k, d_v, S_in, S_out, q, k, v, alpha, beta, o, s);
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;

@@ -15,18 +15,19 @@ enum { T_F32 = 0, T_BF16 = 1 };
 hipError_t launch_decode_rows(int variant, int dtype, int n, int d_k, int d_v, const float *S_in,
                               float *S_out, const void *q, const void *k, const void *v,
                               const void *alpha, const void *beta, void *o, hipStream_t s);
-hipError_t launch_decode_based(int dtype, int n, float eps, const float *S_in, const float *z_in,
-                               float *S_out, float *z_out, const void *q, const void *k,
-                               const void *v, void *o, hipStream_t s);
+// compact: the 153-feature map of LA_BASED_COMPACT instead of the 273-feature one
+hipError_t launch_decode_based(int dtype, bool compact, int n, float eps, const float *S_in,
+                               const float *z_in, float *S_out, float *z_out, const void *q,
+                               const void *k, const void *v, void *o, hipStream_t s);
 
 // recurrent.hip (token-recurrent prefill; fp32 path)
 hipError_t launch_recurrent_rows(int variant, int dtype, int B, int H, int64_t T, int d_k, int d_v,
                                  const void *q, const void *k, const void *v, const void *alpha,
                                  const void *beta, const float *S0, void *o, float *S_T,
                                  hipStream_t s);
-hipError_t launch_recurrent_based(int dtype, int B, int H, int64_t T, float eps, const void *q,
-                                  const void *k, const void *v, const float *s0, const float *z0,
-                                  void *o, float *s_T, float *z_T, hipStream_t s);
+hipError_t launch_recurrent_based(int dtype, bool compact, int B, int H, int64_t T, float eps,
+                                  const void *q, const void *k, const void *v, const float *s0,
+                                  const float *z0, void *o, float *s_T, float *z_T, hipStream_t s);
 
 // chunk.hip (chunkwise bf16 prefill for ADDITIVE / GATED / GATED_DELTA)
 size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v);
@@ -40,10 +41,10 @@ void chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks);
 
 // based_chunk.hip (chunkwise bf16 BASED prefill)
 size_t based_chunk_workspace_bytes(int B, int H, int64_t T);
-hipError_t launch_based_chunk_prefill(int B, int H, int64_t T, float eps, const void *q,
-                                      const void *k, const void *v, const float *s0,
-                                      const float *z0, void *o, float *s_T, float *z_T,
-                                      void *workspace, int pass_mask, hipStream_t s);
+hipError_t launch_based_chunk_prefill(bool compact, int B, int H, int64_t T, float eps,
+                                      const void *q, const void *k, const void *v,
+                                      const float *s0, const float *z0, void *o, float *s_T,
+                                      float *z_T, void *workspace, int pass_mask, hipStream_t s);
 void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks);
 
 // util (la_abi.hip): copy or zero-fill n floats with a kernel (capture-safe, no memset nodes)

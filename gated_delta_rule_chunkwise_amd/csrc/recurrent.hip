@@ -115,9 +115,10 @@ __global__ __launch_bounds__(64) void recurrent_rows_kernel(int64_t T_len, int d
   }
 }
 
-// BASED, d' = 16, d_v = 64, D = 273.  Thread t: value column c = t % 64, features
-// f = t/64 + 4 i (i < 69).  z is kept per feature by every lane of the owning wave.
-template <typename T>
+// BASED, d' = 16, d_v = 64, D = 273 (COMPACT: D = 153, [1, x, x_a^2/sqrt 2 and x_a x_b
+// for a < b in row-major upper-triangle order]).  Thread t: value column c = t % 64,
+// features f = t/64 + 4 i.  z is kept per feature by every lane of the owning wave.
+template <bool COMPACT, typename T>
 __global__ __launch_bounds__(256) void recurrent_based_kernel(int64_t T_len, float eps,
                                                               const T *__restrict__ q,
                                                               const T *__restrict__ k,
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(256) void recurrent_based_kernel(int64_t T_len, flo
                                                               const float *__restrict__ z0,
                                                               T *__restrict__ o, float *s_T,
                                                               float *z_T) {
-  constexpr int DP = 16, DV = 64, D = 1 + DP + DP * DP, NF = (D + 3) / 4, TT = 16;
+  constexpr int DP = 16, DV = 64, D = COMPACT ? 1 + DP + DP * (DP + 1) / 2 : 1 + DP + DP * DP;
+  constexpr int NF = (D + 3) / 4, TT = 16;
   __shared__ float phk[TT][D + 3], phq[TT][D + 3];
   __shared__ float vs[TT][DV];
   __shared__ float part_num[4][TT][DV];
@@ -150,9 +152,22 @@ __global__ __launch_bounds__(256) void recurrent_based_kernel(int64_t T_len, flo
       if (f == 0) { fk = 1.0f; fq = 1.0f; }
       else if (f <= DP) { fk = io<T>::ld(k, base + f - 1); fq = io<T>::ld(q, base + f - 1); }
       else {
-        const int a = (f - 1 - DP) >> 4, b = (f - 1 - DP) & 15;
-        fk = io<T>::ld(k, base + a) * io<T>::ld(k, base + b) * rs2;
-        fq = io<T>::ld(q, base + a) * io<T>::ld(q, base + b) * rs2;
+        int a, b = f - 1 - DP;  // order-2 feature: pair (a, b)
+        float w = rs2;
+        if (COMPACT) {
+          a = 0;
+          while (b >= DP - a) {
+            b -= DP - a;
+            ++a;
+          }
+          b += a;
+          if (a != b) w = 1.0f;
+        } else {
+          a = b >> 4;
+          b &= 15;
+        }
+        fk = io<T>::ld(k, base + a) * io<T>::ld(k, base + b) * w;
+        fq = io<T>::ld(q, base + a) * io<T>::ld(q, base + b) * w;
       }
       phk[tt][f] = fk;
       phq[tt][f] = fq;
@@ -234,18 +249,26 @@ hipError_t launch_recurrent_rows(int variant, int dtype, int B, int H, int64_t T
   return go_rec_dk<float>(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
 }
 
-hipError_t launch_recurrent_based(int dtype, int B, int H, int64_t T, float eps, const void *q,
-                                  const void *k, const void *v, const float *s0, const float *z0,
-                                  void *o, float *s_T, float *z_T, hipStream_t s) {
+template <bool COMPACT>
+static void go_rec_based(int dtype, int B, int H, int64_t T, float eps, const void *q, const void *k,
+                         const void *v, const float *s0, const float *z0, void *o, float *s_T,
+                         float *z_T, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)B * H));
   if (dtype == T_BF16)
-    hipLaunchKernelGGL(recurrent_based_kernel<bf16_t>, grid, dim3(256), 0, s, T, eps,
+    hipLaunchKernelGGL((recurrent_based_kernel<COMPACT, bf16_t>), grid, dim3(256), 0, s, T, eps,
                        (const bf16_t *)q, (const bf16_t *)k, (const bf16_t *)v, s0, z0, (bf16_t *)o,
                        s_T, z_T);
   else
-    hipLaunchKernelGGL(recurrent_based_kernel<float>, grid, dim3(256), 0, s, T, eps,
+    hipLaunchKernelGGL((recurrent_based_kernel<COMPACT, float>), grid, dim3(256), 0, s, T, eps,
                        (const float *)q, (const float *)k, (const float *)v, s0, z0, (float *)o, s_T,
                        z_T);
+}
+
+hipError_t launch_recurrent_based(int dtype, bool compact, int B, int H, int64_t T, float eps,
+                                  const void *q, const void *k, const void *v, const float *s0,
+                                  const float *z0, void *o, float *s_T, float *z_T, hipStream_t s) {
+  if (compact) go_rec_based<true>(dtype, B, H, T, eps, q, k, v, s0, z0, o, s_T, z_T, s);
+  else go_rec_based<false>(dtype, B, H, T, eps, q, k, v, s0, z0, o, s_T, z_T, s);
   return hipGetLastError();
 }
 

@@ -21,6 +21,11 @@
  *                    o_t = s_t^T phi(q_t) / (z_t^T phi(q_t) + eps).
  *                    No input scaling is applied: callers that want the x/d'^(1/4)
  *                    scaling of the paper's listing pre-scale q and k.
+ *   LA_BASED_COMPACT the same recurrence and outputs with the compact feature map of the
+ *                    same notes' feature-width table (Sec. 2.3), which keeps every cross
+ *                    term once: phi_c(x) = [1, x, x_a^2/sqrt(2) (a = b), x_a x_b (a < b)],
+ *                    so phi_c(q).phi_c(k) = phi(q).phi(k) with 1 + d' + d'(d'+1)/2 features
+ *                    (153 for d' = 16: 44% less state than 273).
  *
  * Layouts (row-major, last index fastest; every pointer is DEVICE memory):
  *   q, k      [B][H][T][d_k]        (BASED: d_k = d', the projected q/k width)
@@ -28,7 +33,10 @@
  *   alpha,beta[B][H][T]             decay alpha_t in (0,1], write strength beta_t
  *   S         [B][H][d_v][d_k] fp32 (ADDITIVE, GATED, GATED_DELTA)
  *   s         [B][H][D][d_v]   fp32, z [B][H][D] fp32 (BASED, D = 1 + d' + d'^2,
- *             feature order [1, x_0..x_{d'-1}, x_i x_j / sqrt 2 at 1 + d' + i d' + j])
+ *             feature order [1, x_0..x_{d'-1}, x_i x_j / sqrt 2 at 1 + d' + i d' + j];
+ *             BASED_COMPACT, D = 1 + d' + d'(d'+1)/2, order [1, x_0..x_{d'-1}, then the
+ *             pairs a <= b in row-major upper-triangle order: pair (a, b) at
+ *             1 + d' + a d' - a(a-1)/2 + (b - a)])
  *   Decode drops the T axis and replaces [B][H] by N independent states.
  * q, k, v, alpha, beta and o share one element type (LA_F32 or LA_BF16); states are
  * always fp32; all accumulation is fp32.  o is rounded to nearest-even on store.
@@ -37,7 +45,8 @@
  *   ADDITIVE      alpha and beta must be NULL.
  *   GATED         alpha required; beta == NULL means beta_t = 1.
  *   GATED_DELTA   alpha and beta required.
- *   BASED         alpha and beta must be NULL; z pointers are required wherever the
+ *   BASED, BASED_COMPACT
+ *                 alpha and beta must be NULL; z pointers are required wherever the
  *                 corresponding s pointer is given.
  * Preconditions that are not checked: alpha_t in (0, 1] (outside it results are
  * unspecified), finite inputs (NaN/Inf propagate).
@@ -66,7 +75,7 @@
 extern "C" {
 #endif
 
-enum { LA_ADDITIVE = 0, LA_BASED = 1, LA_GATED = 2, LA_GATED_DELTA = 3 };
+enum { LA_ADDITIVE = 0, LA_BASED = 1, LA_GATED = 2, LA_GATED_DELTA = 3, LA_BASED_COMPACT = 4 };
 enum { LA_F32 = 0, LA_BF16 = 1 };
 
 enum {
@@ -122,9 +131,9 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  * inputs take an fp32 token-recurrent path (fp32 FMA throughout).
  *
  * Supported: bf16 -- ADDITIVE/GATED/GATED_DELTA with d_k = d_v = 128 or 64;
- *                    BASED with d' = 16, d_v = 64.
+ *                    BASED and BASED_COMPACT with d' = 16, d_v = 64.
  *            fp32 -- ADDITIVE/GATED/GATED_DELTA with d_k in {64, 128, 256} and any d_v;
- *                    BASED with d' = 16 and d_v = 64.
+ *                    BASED and BASED_COMPACT with d' = 16 and d_v = 64.
  *            Any T >= 1 (a partial last chunk is masked).
  */
 int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k, int d_v,
@@ -182,7 +191,8 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
  * state is read once and written once (this step is bound by HBM bandwidth).
  *
  * Supported: ADDITIVE/GATED/GATED_DELTA with d_k in {64, 128, 256} and any d_v >= 1;
- *            BASED with d' = 16, d_v = 64; q/k/v/alpha/beta/o in fp32 or bf16.
+ *            BASED and BASED_COMPACT with d' = 16, d_v = 64; q/k/v/alpha/beta/o in fp32
+ *            or bf16.
  */
 int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, const float *S_in,
                    const float *z_in, float *S_out, float *z_out, const void *q, const void *k,

@@ -63,6 +63,7 @@ def prefill(lib, variant=la.GATED_DELTA, dtype=la.BF16, B=1, H=2, T=100, dk=128,
 
 def test_prefill_rejects_bad_variant_and_dtype(lib):
     assert prefill(lib, variant=7) == -2
+    assert prefill(lib, variant=5) == -2
     assert prefill(lib, variant=-1) == -2
     assert prefill(lib, dtype=5) == -2
 
@@ -155,7 +156,9 @@ def decode(lib, variant=la.GATED_DELTA, dtype=la.BF16, n=16, dk=128, dv=128, S_i
 
 
 def test_decode_validation(lib):
-    assert decode(lib, variant=4) == -2
+    assert decode(lib, variant=5) == -2
+    assert decode(lib, variant=la.BASED_COMPACT, alpha=None, beta=None, dk=16, dv=64) == -1  # z missing
+    assert decode(lib, variant=la.BASED_COMPACT, alpha=None, beta=None, dk=16, dv=32) == -3
     assert decode(lib, n=0) == -2
     assert decode(lib, dk=100) == -3
     assert decode(lib, variant=la.BASED, alpha=None, beta=None, dk=16, dv=32) == -3

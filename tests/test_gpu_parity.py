@@ -15,10 +15,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 ROWS_VARIANTS = ["additive", "gated", "gated_delta"]
+BASED_VARIANTS = ["based", "based_compact"]
 
 
 def _inputs(variant, B, H, T, dk, dv, dtype, seed):
-    if variant == "based":
+    if variant in BASED_VARIANTS:
         d = synth.based_inputs(B, H, T, dk, dv, dtype=dtype, seed=seed, device=DEV)
         return d["q"], d["k"], d["v"], None, None
     d = synth.gdn_inputs(B, H, T, dk, dv, dtype=dtype, seed=seed, device=DEV,
@@ -37,15 +38,15 @@ def _check_prefill(la, variant, B, H, T, dk, dv, dtype, seed, S0=None, z0=None):
     tol = TOL[dtype]
     assert_close(o, oo, tol, what="o")
     assert_close(S_T, So, tol, what="S_T")
-    if variant == "based":
+    if variant in BASED_VARIANTS:
         assert_close(z_T, zo, tol, what="z_T")
     return o, S_T, z_T
 
 
-@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + BASED_VARIANTS)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_prefill_small(la, variant, dtype):
-    if variant == "based":
+    if variant in BASED_VARIANTS:
         _check_prefill(la, variant, 2, 3, 203, 16, 64, dtype, seed=11)
     else:
         for dk in (64, 128):
@@ -58,14 +59,14 @@ def test_prefill_fp32_other_widths(la, variant):
     _check_prefill(la, variant, 1, 2, 77, 64, 17, torch.float32, seed=4)
 
 
-@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + BASED_VARIANTS)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_prefill_with_start_state(la, variant, dtype):
     B, H, T = 1, 2, 130
-    if variant == "based":
+    if variant in BASED_VARIANTS:
         dk, dv = 16, 64
         w = synth.based_inputs(B, H, 40, dk, dv, dtype=dtype, seed=99, device=DEV)
-        _, s0, z0 = oracle.prefill("based", w["q"], w["k"], w["v"])
+        _, s0, z0 = oracle.prefill(variant, w["q"], w["k"], w["v"])
         S0 = torch.tensor(s0, dtype=torch.float32, device=DEV)
         z0 = torch.tensor(z0, dtype=torch.float32, device=DEV)
     else:
@@ -75,12 +76,12 @@ def test_prefill_with_start_state(la, variant, dtype):
     _check_prefill(la, variant, B, H, T, dk, dv, dtype, seed=21, S0=S0, z0=z0)
 
 
-@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + BASED_VARIANTS)
 def test_prefill_empty_sequence_returns_start_state(la, variant):
-    dk, dv = (16, 64) if variant == "based" else (128, 128)
+    dk, dv = (16, 64) if variant in BASED_VARIANTS else (128, 128)
     q, k, v, a, b = _inputs(variant, 1, 2, 0, dk, dv, torch.bfloat16, 1)
-    if variant == "based":
-        D = 1 + dk + dk * dk
+    if variant in BASED_VARIANTS:
+        D = oracle.feature_dim(dk, compact=(variant == "based_compact"))
         S0 = torch.randn(1, 2, D, dv, device=DEV)
         z0 = torch.rand(1, 2, D, device=DEV)
     else:
@@ -115,31 +116,32 @@ def test_decode_steps(la, variant, dtype, dk, dv):
     assert_close(S, S_ref, tol, lead=1, what="S")
 
 
+@pytest.mark.parametrize("variant", BASED_VARIANTS)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_decode_based_steps(la, dtype):
+def test_decode_based_steps(la, variant, dtype):
     N, steps, dp, dv = 29, 5, 16, 64
     w = synth.based_warmup_inputs(N, 24, dp, dv, dtype=dtype, seed=3, device=DEV)
     # both sides build the start state from the same warm-up tokens: the GPU through its
     # own prefill, the oracle through its own recurrence
-    _, s, z = la.prefill("based", w["q"][None], w["k"][None], w["v"][None])
+    _, s, z = la.prefill(variant, w["q"][None], w["k"][None], w["v"][None])
     s, z = s[0].contiguous(), z[0].contiguous()
-    _, s_ref, z_ref = oracle.prefill("based", w["q"][None], w["k"][None], w["v"][None])
+    _, s_ref, z_ref = oracle.prefill(variant, w["q"][None], w["k"][None], w["v"][None])
     s_ref, z_ref = s_ref[0], z_ref[0]
     d = synth.based_decode_inputs(steps, N, dp, dv, dtype=dtype, seed=4, device=DEV)
     tol = TOL[dtype]
     for t in range(steps):
-        o, s, z = la.decode_step("based", s, d["q"][t], d["k"][t], d["v"][t], z=z, S_out=s, z_out=z)
+        o, s, z = la.decode_step(variant, s, d["q"][t], d["k"][t], d["v"][t], z=z, S_out=s, z_out=z)
         torch.cuda.synchronize()
-        oo, s_ref, z_ref = oracle.decode_step("based", s_ref, d["q"][t], d["k"][t], d["v"][t],
+        oo, s_ref, z_ref = oracle.decode_step(variant, s_ref, d["q"][t], d["k"][t], d["v"][t],
                                               z=z_ref)
         assert_close(o, oo, tol, lead=1, what=f"o step {t}")
     assert_close(s, s_ref, tol, lead=1, what="s")
     assert_close(z, z_ref, tol, lead=1, what="z")
 
 
-@pytest.mark.parametrize("variant", ROWS_VARIANTS + ["based"])
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + BASED_VARIANTS)
 def test_prefill_deterministic(la, variant):
-    dk, dv = (16, 64) if variant == "based" else (128, 128)
+    dk, dv = (16, 64) if variant in BASED_VARIANTS else (128, 128)
     q, k, v, a, b = _inputs(variant, 1, 4, 333, dk, dv, torch.bfloat16, 5)
     o1, S1, _ = la.prefill(variant, q, k, v, a, b)
     o2, S2, _ = la.prefill(variant, q, k, v, a, b)
@@ -231,6 +233,46 @@ def test_based_chunk_full_config_sampled_columns(la):
     assert_close(z_T, zo, 2e-2, what="z_T")
 
 
+@pytest.mark.parametrize("variant", BASED_VARIANTS)
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 1000])
-def test_based_chunk_short_and_ragged(la, T):
-    _check_prefill(la, "based", 1, 3, T, 16, 64, torch.bfloat16, seed=70 + T)
+def test_based_chunk_short_and_ragged(la, variant, T):
+    _check_prefill(la, variant, 1, 3, T, 16, 64, torch.bfloat16, seed=70 + T)
+
+
+@pytest.mark.parametrize("variant", BASED_VARIANTS)
+def test_based_passes_compose_to_prefill(la, variant):
+    """BASED: la_prefill == la_prefill_pass(MAPS); (SCAN); (REPLAY), bit for bit, with a
+    start state (segment 0 starts from it, the last segment writes the end state)."""
+    B, H, T, dp, dv = 1, 4, 64 * 20 + 7, 16, 64
+    q, k, v, _, _ = _inputs(variant, B, H, T, dp, dv, torch.bfloat16, 61)
+    nseg, _ = la.segments(variant, la.BF16, B, H, T, dp, dv)
+    assert nseg > 1
+    w = synth.based_inputs(B, H, 50, dp, dv, dtype=torch.bfloat16, seed=62, device=DEV)
+    _, s0, z0 = la.prefill(variant, w["q"], w["k"], w["v"])
+    o1, s1, z1 = la.prefill(variant, q, k, v, S0=s0, z0=z0)
+    ws = torch.empty(la.workspace_size(variant, la.BF16, B, H, T, dp, dv), dtype=torch.uint8, device=DEV)
+    o2, s2, z2 = torch.empty_like(o1), torch.empty_like(s1), torch.empty_like(z1)
+    for p in (la.PASS_TRANSFORM, la.PASS_MAPS, la.PASS_SCAN, la.PASS_REPLAY):
+        la.prefill(variant, q, k, v, S0=s0, z0=z0, o=o2, S_T=s2, z_T=z2, workspace=ws, pass_=p)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(z1, z2)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_based_compact_matches_full(la, dtype):
+    """Both feature layouts give the same outputs (the kernel value is the same), and the
+    compact end state is the full one with each unordered pair folded."""
+    B, H, T, dp, dv = 2, 2, 300, 16, 64
+    q, k, v, _, _ = _inputs("based", B, H, T, dp, dv, dtype, 63)
+    of, sf, zf = la.prefill("based", q, k, v)
+    oc, sc, zc = la.prefill("based_compact", q, k, v)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert_close(oc, to64(of), tol, what="o compact vs full")
+    sf, zf = to64(sf), to64(zf)
+    idx = [(a, b) for a in range(dp) for b in range(a, dp)]
+    fold_s = np.stack([sf[:, :, 1 + dp + a * dp + a] if a == b else
+                       (sf[:, :, 1 + dp + a * dp + b] + sf[:, :, 1 + dp + b * dp + a]) / np.sqrt(2)
+                       for a, b in idx], axis=2)
+    assert_close(sc[:, :, 1 + dp:], fold_s, tol, what="s compact vs folded full")
+    assert_close(sc[:, :, :1 + dp], sf[:, :, :1 + dp], tol, what="s [1, x] rows")
