@@ -213,6 +213,7 @@ def main():
     based = None
     if not args.no_based:
         based = bench_based(torch, la, synth, dev, stream, args.steps)
+        based["compact"] = bench_based(torch, la, synth, dev, stream, args.steps, "based_compact")
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -237,9 +238,11 @@ def main():
 
 
 def bench_decode(torch, la, synth, dev, stream, steps):
-    """256 sequences x 16 heads; gated-delta and BASED decode, `steps` consecutive steps."""
+    """256 sequences x 16 heads; gated-delta and BASED decode (and BASED with the compact
+    153-feature state), `steps` consecutive steps."""
     N, D, dp, dv_b = 256 * 16, 128, 16, 64
     Dphi = 1 + dp + dp * dp
+    Dc = 1 + dp + dp * (dp + 1) // 2
     res = {"states": N, "steps": steps}
     # gated delta: seeded N(0,1) start state, per-step q/k/v/alpha/beta resident in HBM
     S = synth.gdn_state((N, D, D), seed=4, device=dev)
@@ -251,6 +254,8 @@ def bench_decode(torch, la, synth, dev, stream, steps):
     s, z = s[0].contiguous(), z[0].contiguous()
     bd = synth.based_decode_inputs(steps, N, dp, dv_b, dtype=torch.bfloat16, seed=5, device=dev)
     ob = torch.empty((N, dv_b), dtype=torch.bfloat16, device=dev)
+    _, sc, zc = la.prefill("based_compact", w["q"][None], w["k"][None], w["v"][None])
+    sc, zc = sc[0].contiguous(), zc[0].contiguous()
 
     def gdn_step(t):
         la.decode_step("gated_delta", S, g["q"][t], g["k"][t], g["v"][t], g["alpha"][t],
@@ -259,6 +264,10 @@ def bench_decode(torch, la, synth, dev, stream, steps):
     def based_step(t):
         la.decode_step("based", s, bd["q"][t], bd["k"][t], bd["v"][t], z=z, S_out=s, z_out=z,
                        o=ob, stream=stream)
+
+    def compact_step(t):
+        la.decode_step("based_compact", sc, bd["q"][t], bd["k"][t], bd["v"][t], z=zc, S_out=sc,
+                       z_out=zc, o=ob, stream=stream)
 
     def timed(fn):
         for t in range(8):
@@ -274,6 +283,7 @@ def bench_decode(torch, la, synth, dev, stream, steps):
 
     ms_g = timed(gdn_step)
     ms_b = timed(based_step)
+    ms_c = timed(compact_step)
     bytes_g = 2 * N * D * D * 4 + N * (3 * D + 2 + D) * 2
     bytes_b = 2 * N * (Dphi * dv_b + Dphi) * 4 + N * (2 * dp + 2 * dv_b) * 2
     res["gated_delta"] = {"us_per_step": round(ms_g * 1e3, 2), "steps_per_s": round(1e3 / ms_g, 1),
@@ -282,21 +292,26 @@ def bench_decode(torch, la, synth, dev, stream, steps):
     res["based"] = {"us_per_step": round(ms_b * 1e3, 2), "steps_per_s": round(1e3 / ms_b, 1),
                     "alg_bytes_per_step": bytes_b,
                     "hbm_frac": round(bytes_b / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    bytes_c = 2 * N * (Dc * dv_b + Dc) * 4 + N * (2 * dp + 2 * dv_b) * 2
+    res["based_compact"] = {"us_per_step": round(ms_c * 1e3, 2), "steps_per_s": round(1e3 / ms_c, 1),
+                            "alg_bytes_per_step": bytes_c, "state_features": Dc,
+                            "hbm_frac": round(bytes_c / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     res["both_steps_per_s"] = round(1e3 / (ms_g + ms_b), 1)
     return res
 
 
-def bench_based(torch, la, synth, dev, stream, steps):
-    """BASED Taylor prefill, B=4, H=16, T=8192, d'=16, d_v=64, bf16 (all three passes)."""
+def bench_based(torch, la, synth, dev, stream, steps, variant="based"):
+    """BASED Taylor prefill, B=4, H=16, T=8192, d'=16, d_v=64, bf16 (all three passes); the
+    compact variant keeps a 153-feature state."""
     B, H, T, dp, dv = 4, 16, 8192, 16, 64
     d = synth.based_inputs(B, H, T, dp, dv, dtype=torch.bfloat16, seed=1, device=dev)
-    Dphi = 1 + dp + dp * dp
+    Dphi = 1 + dp + dp * (dp + 1) // 2 if variant == "based_compact" else 1 + dp + dp * dp
     o = torch.empty((B, H, T, dv), dtype=torch.bfloat16, device=dev)
     s_T = torch.empty((B, H, Dphi, dv), dtype=torch.float32, device=dev)
     z_T = torch.empty((B, H, Dphi), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(la.workspace_size("based", la.BF16, B, H, T, dp, dv), 16), dtype=torch.uint8,
+    ws = torch.empty(max(la.workspace_size(variant, la.BF16, B, H, T, dp, dv), 16), dtype=torch.uint8,
                      device=dev)
-    run = lambda: la.prefill("based", d["q"], d["k"], d["v"], o=o, S_T=s_T, z_T=z_T, workspace=ws,
+    run = lambda: la.prefill(variant, d["q"], d["k"], d["v"], o=o, S_T=s_T, z_T=z_T, workspace=ws,
                              stream=stream)
     for _ in range(3):
         run()
@@ -314,8 +329,8 @@ def bench_based(torch, la, synth, dev, stream, steps):
     C = 64  # chunk-form FLOPs per token-head: QK^T, A V, Phi_Q s, Phi_K^T V, normaliser
     alg_flops = th * (2 * C * dp + 2 * C * dv + 4 * Dphi * dv + 2 * Dphi + C)
     t_roof = max(alg_bytes / (HBM_PEAK_GBS * 1e9), alg_flops / (BF16_PEAK_TFLOPS * 1e12))
-    nseg, sc = la.segments("based", la.BF16, B, H, T, dp, dv)
-    return {"workload": "BASED Taylor prefill B=4 H=16 T=8192 d'=16 d_v=64 bf16",
+    nseg, sc = la.segments(variant, la.BF16, B, H, T, dp, dv)
+    return {"workload": f"BASED Taylor prefill B=4 H=16 T=8192 d'=16 d_v=64 bf16, {Dphi}-feature state",
             "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "alg_bytes": alg_bytes, "alg_flops": alg_flops, "segments": nseg,
             "roofline_time_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof * 1e3 / ms, 4)}
