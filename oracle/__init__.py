@@ -20,6 +20,11 @@ promotes inputs exactly to float64.  What is computed, with citations:
   table (Sec. 2.3), [1, x, x_a^2/sqrt 2 (a = b), x_a x_b (a < b)], pairs in row-major
   upper-triangle order (D = 1 + d' + d'(d'+1)/2 = 153 for d' = 16).
 
+* [NoteBank] Sec. 3 Eqs. (3)-(5), App. B.2 Eq. (8), App. B.3 Eq. (9): the write step's key
+  distinctiveness per write chunk (``write_scores``), the best scoring window of each
+  complete chunk (``write_windows``), the per-channel note addresses (``note_addresses``)
+  and the addressing votes (``address_votes``).  Argmax ties go to the earliest index.
+
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, brute force and invariants.  The eps convention and the absence of
 input scaling for BASED are chosen conventions that no page value fixes
@@ -86,6 +91,19 @@ def _load():
     lib.oracle_based_phi_compact.argtypes = [dp, ctypes.c_int, dp]
     lib.oracle_based_phi_compact.restype = None
     lib.oracle_max_threads.restype = ctypes.c_int
+    lp = ctypes.POINTER(ctypes.c_long)
+    lib.oracle_write_scores.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_int,
+                                        ctypes.c_long, dp, dp, dp]
+    lib.oracle_write_scores.restype = ctypes.c_int
+    lib.oracle_write_windows.argtypes = [ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                         ctypes.c_long, dp, lp, dp]
+    lib.oracle_write_windows.restype = ctypes.c_int
+    lib.oracle_note_addresses.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, dp, dp, lp, ip, lp, dp]
+    lib.oracle_note_addresses.restype = ctypes.c_int
+    lib.oracle_address_votes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp,
+                                         ctypes.c_int, lp, dp, ip, ip, ip]
+    lib.oracle_address_votes.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -213,3 +231,65 @@ def based_phi_compact(x):
     f = np.zeros(feature_dim(x.size, compact=True))
     _load().oracle_based_phi_compact(_ptr(x), int(x.size), _ptr(f))
     return f
+
+
+def _lptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_long))
+
+
+def _iptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+
+
+def write_scores(k, chunk=512):
+    """Key distinctiveness d_t = 1 - <khat_t, mubar> per write chunk and head (Eqs. (3), (8)).
+    k [B, H, T, d_k].  Returns (d_head [B, H, T], d_mean [B, T]) in float64."""
+    k = _f64(k)
+    B, H, T, dk = k.shape
+    d_head, d_mean = np.zeros((B, H, T)), np.zeros((B, T))
+    if _load().oracle_write_scores(B, H, T, dk, int(chunk), _ptr(k), _ptr(d_head), _ptr(d_mean)) != 0:
+        raise ValueError("oracle_write_scores rejected its arguments")
+    return d_head, d_mean
+
+
+def write_windows(d_mean, chunk=512, window=48, tail=32):
+    """Best window (start, sum) per complete write chunk of d_mean [B, T] (App. B.2)."""
+    d = _f64(d_mean)
+    B, T = d.shape
+    nc = T // chunk
+    start, val = np.zeros((B, nc), dtype=np.int64), np.zeros((B, nc))
+    if _load().oracle_write_windows(B, T, int(chunk), int(window), int(tail), _ptr(d), _lptr(start),
+                                    _ptr(val)) != 0:
+        raise ValueError("oracle_write_windows rejected its arguments")
+    return start, val
+
+
+def note_addresses(d_head, q, spans, coords):
+    """Eqs. (4), (9): t* [B, N, H] = argmax of d_head over each note's span, rho [B, N, H, d_rho]
+    = q at t* on the head's coordinates.  spans [B, N, 2] (start, length); coords [H, d_rho]."""
+    d, q = _f64(d_head), _f64(q)
+    B, H, T, dk = q.shape
+    spans = np.ascontiguousarray(np.asarray(spans, dtype=np.int64))
+    coords = np.ascontiguousarray(np.asarray(coords, dtype=np.int32))
+    N, drho = spans.shape[1], coords.shape[1]
+    t_star, rho = np.zeros((B, N, H), dtype=np.int64), np.zeros((B, N, H, drho))
+    if _load().oracle_note_addresses(B, H, T, dk, N, drho, _ptr(d), _ptr(q), _lptr(spans), _iptr(coords),
+                                     _lptr(t_star), _ptr(rho)) != 0:
+        raise ValueError("oracle_note_addresses rejected its arguments")
+    return t_star, rho
+
+
+def address_votes(rho, u, R, positions):
+    """Eq. (5): rho [N, J, d_rho] note addresses, u [n_Q, J, d_rho] question features.
+    Returns (score [J, N], choice [J], votes [N], selected [R], -1 padded, in document order)."""
+    rho, u = _f64(rho), _f64(u)
+    N, J, drho = rho.shape
+    nQ = u.shape[0]
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64))
+    score = np.zeros((J, N))
+    choice, votes = np.zeros(J, dtype=np.int32), np.zeros(N, dtype=np.int32)
+    sel = np.zeros(R, dtype=np.int32)
+    if _load().oracle_address_votes(N, J, nQ, drho, _ptr(rho), _ptr(u), int(R), _lptr(pos), _ptr(score),
+                                    _iptr(choice), _iptr(votes), _iptr(sel)) != 0:
+        raise ValueError("oracle_address_votes rejected its arguments")
+    return score, choice, votes, sel

@@ -294,3 +294,187 @@ int oracle_literal(int variant, long T, int dk, int dv, const double *q, const d
   free(A);
   return 0;
 }
+
+/* =================================================================================
+ * NoteBank write and address steps on the recurrence's keys and queries
+ * ([NoteBank] "History Replays Itself: Unleashing Long-Context Capability in Linear
+ * Attention", Sec. 3 Eqs. (3)-(5), App. B.2 Eq. (8), App. B.3 Eq. (9)).  One layer's
+ * heads are the channels (l, h).  Argmax ties go to the earliest index (the pages fix
+ * the tie rule only for the vote ranking, where earlier-inserted notes win).
+ * ================================================================================= */
+
+/* Key distinctiveness per write chunk of C tokens (the last, possibly partial, chunk over
+ * its own tokens): khat_t = k_t/|k_t|, mu = mean of khat over the chunk, mubar = mu/|mu|,
+ * d_t = 1 - <khat_t, mubar> per head; d_mean_t = mean of d_t over the H heads.
+ * A zero vector normalises to zero.  k [B][H][T][dk]; d_head [B][H][T]; d_mean [B][T]. */
+int oracle_write_scores(int B, int H, long T, int dk, long C, const double *k, double *d_head,
+                        double *d_mean) {
+  if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || C <= 0 || !k || !d_head) return -1;
+  double *mu = (double *)malloc(sizeof(double) * dk);
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const double *kb = k + ((size_t)b * H + h) * T * dk;
+      double *db = d_head + ((size_t)b * H + h) * T;
+      for (long c0 = 0; c0 < T; c0 += C) {
+        const long c1 = c0 + C < T ? c0 + C : T;
+        for (int j = 0; j < dk; ++j) mu[j] = 0.0;
+        for (long t = c0; t < c1; ++t) {
+          double n = 0.0;
+          for (int j = 0; j < dk; ++j) n += kb[t * dk + j] * kb[t * dk + j];
+          n = sqrt(n);
+          if (n > 0.0)
+            for (int j = 0; j < dk; ++j) mu[j] += kb[t * dk + j] / n;
+        }
+        double mn = 0.0;
+        for (int j = 0; j < dk; ++j) {
+          mu[j] /= (double)(c1 - c0);
+          mn += mu[j] * mu[j];
+        }
+        mn = sqrt(mn);
+        for (long t = c0; t < c1; ++t) {
+          double n = 0.0, dot = 0.0;
+          for (int j = 0; j < dk; ++j) n += kb[t * dk + j] * kb[t * dk + j];
+          n = sqrt(n);
+          if (n > 0.0 && mn > 0.0)
+            for (int j = 0; j < dk; ++j) dot += (kb[t * dk + j] / n) * (mu[j] / mn);
+          db[t] = 1.0 - dot;
+        }
+      }
+    }
+  free(mu);
+  if (d_mean)
+    for (int b = 0; b < B; ++b)
+      for (long t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int h = 0; h < H; ++h) s += d_head[((size_t)b * H + h) * T + t];
+        d_mean[(size_t)b * T + t] = s / H;
+      }
+  return 0;
+}
+
+/* Best scoring window per complete write chunk (App. B.2): the candidate region of chunk
+ * c is [max(0, cC - tail), (c+1)C), the chunk plus the previous chunk's last `tail`
+ * tokens with their own scores; every window of W consecutive tokens inside it (the
+ * whole region if it is shorter) is scored by the sum of d_mean; the highest wins.
+ * A final incomplete chunk produces no note.  best_start / best_sum [B][T / C]. */
+int oracle_write_windows(int B, long T, long C, long W, long tail, const double *d_mean,
+                         long *best_start, double *best_sum) {
+  if (B <= 0 || T < 0 || C <= 0 || W <= 0 || tail < 0 || !d_mean || !best_start) return -1;
+  const long nc = T / C;
+  for (int b = 0; b < B; ++b)
+    for (long c = 0; c < nc; ++c) {
+      const double *d = d_mean + (size_t)b * T;
+      const long lo = c * C - tail > 0 ? c * C - tail : 0, hi = (c + 1) * C;
+      const long w = hi - lo < W ? hi - lo : W;
+      long bs = lo;
+      double bv = -INFINITY;
+      for (long s = lo; s + w <= hi; ++s) {
+        double v = 0.0;
+        for (long t = s; t < s + w; ++t) v += d[t];
+        if (v > bv) {
+          bv = v;
+          bs = s;
+        }
+      }
+      best_start[(size_t)b * nc + c] = bs;
+      if (best_sum) best_sum[(size_t)b * nc + c] = bv;
+    }
+  return 0;
+}
+
+/* Note addresses (Eqs. (4), (9)): for note i with span [start, start + len) and head h,
+ * t* = argmax over the span of d_head, and rho = the query at t* restricted to the head's
+ * d_rho fixed coordinates.  spans [B][N][2]; coords [H][d_rho]; q [B][H][T][dk];
+ * t_star [B][N][H]; rho [B][N][H][d_rho]. */
+int oracle_note_addresses(int B, int H, long T, int dk, int N, int drho, const double *d_head,
+                          const double *q, const long *spans, const int *coords, long *t_star,
+                          double *rho) {
+  if (B <= 0 || H <= 0 || T <= 0 || dk <= 0 || N < 0 || drho <= 0) return -1;
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < N; ++i) {
+      const long s0 = spans[((size_t)b * N + i) * 2], len = spans[((size_t)b * N + i) * 2 + 1];
+      if (s0 < 0 || len < 1 || s0 + len > T) return -1;
+      for (int h = 0; h < H; ++h) {
+        const double *d = d_head + ((size_t)b * H + h) * T;
+        long ts = s0;
+        for (long t = s0 + 1; t < s0 + len; ++t)
+          if (d[t] > d[ts]) ts = t;
+        t_star[((size_t)b * N + i) * H + h] = ts;
+        for (int r = 0; r < drho; ++r) {
+          const int cidx = coords[h * drho + r];
+          if (cidx < 0 || cidx >= dk) return -1;
+          rho[(((size_t)b * N + i) * H + h) * drho + r] = q[(((size_t)b * H + h) * T + ts) * dk + cidx];
+        }
+      }
+    }
+  return 0;
+}
+
+/* Addressing and voting (Eq. (5)): s[j][i] = max over question positions tau of the
+ * cosine of u_tau and rho_i in channel j (a zero vector has cosine 0); each channel votes
+ * for its argmax note; V_i = number of channels voting for i.  Up to R notes with the
+ * most votes (and at least one) are retrieved, earlier-inserted (lower index) first on
+ * equal votes, then put in document order (by position, index on equal positions).
+ * rho [N][J][drho]; u [nQ][J][drho]; score [J][N]; choice [J]; votes [N]; selected [R]
+ * (-1 padded). */
+int oracle_address_votes(int N, int J, int nQ, int drho, const double *rho, const double *u,
+                         int R, const long *positions, double *score, int *choice, int *votes,
+                         int *selected) {
+  if (N <= 0 || J <= 0 || nQ <= 0 || drho <= 0 || R <= 0) return -1;
+  for (int i = 0; i < N; ++i) votes[i] = 0;
+  for (int j = 0; j < J; ++j) {
+    int best = 0;
+    double bestv = -INFINITY;
+    for (int i = 0; i < N; ++i) {
+      const double *r = rho + ((size_t)i * J + j) * drho;
+      double rn = 0.0;
+      for (int e = 0; e < drho; ++e) rn += r[e] * r[e];
+      rn = sqrt(rn);
+      double m = -INFINITY;
+      for (int tau = 0; tau < nQ; ++tau) {
+        const double *x = u + ((size_t)tau * J + j) * drho;
+        double un = 0.0, dot = 0.0;
+        for (int e = 0; e < drho; ++e) {
+          un += x[e] * x[e];
+          dot += x[e] * r[e];
+        }
+        un = sqrt(un);
+        const double c = (un > 0.0 && rn > 0.0) ? dot / (un * rn) : 0.0;
+        if (c > m) m = c;
+      }
+      if (score) score[(size_t)j * N + i] = m;
+      if (m > bestv) {
+        bestv = m;
+        best = i;
+      }
+    }
+    choice[j] = best;
+    votes[best] += 1;
+  }
+  /* ranking: votes descending, index ascending */
+  int nsel = 0;
+  for (int r = 0; r < R; ++r) {
+    int pick = -1;
+    for (int i = 0; i < N; ++i) {
+      if (votes[i] == 0) continue;
+      int taken = 0;
+      for (int s = 0; s < nsel; ++s)
+        if (selected[s] == i) taken = 1;
+      if (taken) continue;
+      if (pick < 0 || votes[i] > votes[pick]) pick = i;
+    }
+    if (pick < 0) break;
+    selected[nsel++] = pick;
+  }
+  /* document order */
+  for (int a = 1; a < nsel; ++a)
+    for (int c = a; c > 0; --c) {
+      const int x = selected[c - 1], y = selected[c];
+      if (positions[y] < positions[x] || (positions[y] == positions[x] && y < x)) {
+        selected[c - 1] = y;
+        selected[c] = x;
+      }
+    }
+  for (int r = nsel; r < R; ++r) selected[r] = -1;
+  return 0;
+}

@@ -39,6 +39,18 @@ MUTANTS = [
     ("compact_cross_scaled", "f[n++] = (a == b) ? x[a] * x[a] * inv_sqrt2 : x[a] * x[b];",
      "f[n++] = (a == b) ? x[a] * x[a] * inv_sqrt2 : x[a] * x[b] * inv_sqrt2;"),
     ("compact_lower_triangle", "for (int b = a; b < dp; ++b) f[n++]", "for (int b = 0; b <= a; ++b) f[n++]"),
+    ("write_mean_not_renormalised", "dot += (kb[t * dk + j] / n) * (mu[j] / mn);", "dot += (kb[t * dk + j] / n) * mu[j];"),
+    ("write_keys_not_normalised", "if (n > 0.0)\n            for (int j = 0; j < dk; ++j) mu[j] += kb[t * dk + j] / n;",
+     "if (n > 0.0)\n            for (int j = 0; j < dk; ++j) mu[j] += kb[t * dk + j];"),
+    ("window_ignores_tail", "const long lo = c * C - tail > 0 ? c * C - tail : 0, hi = (c + 1) * C;",
+     "const long lo = c * C, hi = (c + 1) * C;"),
+    ("window_ties_to_latest", "if (v > bv) {", "if (v >= bv) {"),
+    ("address_ties_to_latest", "if (d[t] > d[ts]) ts = t;", "if (d[t] >= d[ts]) ts = t;"),
+    ("vote_uses_last_question_token", "if (c > m) m = c;", "m = c;"),
+    ("vote_ranking_prefers_later_note", "if (pick < 0 || votes[i] > votes[pick]) pick = i;",
+     "if (pick < 0 || votes[i] >= votes[pick]) pick = i;"),
+    ("selection_not_in_document_order", "if (positions[y] < positions[x] || (positions[y] == positions[x] && y < x)) {",
+     "if (0) {"),
     ("start_state_ignored", "memcpy(s, S0 + (bh * dv + row) * dk, sizeof(double) * dk);",
      "memset(s, 0, sizeof(double) * dk);"),
 ]
@@ -54,6 +66,7 @@ def test_pins_reject_planted_mistake(tmp_path, name, old, new):
                     str(tmp_path / "oracle.c"), "-o", str(lib), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        str(ROOT / "tests" / "test_oracle_pins.py")],
+                        str(ROOT / "tests" / "test_oracle_pins.py"),
+                        str(ROOT / "tests" / "test_oracle_notebank_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the pin suite:\n{r.stdout[-2000:]}"
