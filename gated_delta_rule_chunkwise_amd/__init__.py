@@ -23,7 +23,8 @@ F32, BF16 = 0, 1
 STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_INVALID", -3: "LA_ERR_UNSUPPORTED",
           -4: "LA_ERR_ALIGN", -5: "LA_ERR_WORKSPACE", -6: "LA_ERR_ALIAS", -7: "LA_ERR_HIP"}
 EXPORTS = ("la_abi_version", "la_status_string", "la_prefill_workspace_size", "la_prefill",
-           "la_prefill_pass", "la_prefill_segments", "la_decode_step")
+           "la_prefill_pass", "la_prefill_segments", "la_decode_step",
+           "la_write_scores", "la_write_windows", "la_note_addresses", "la_address_votes")
 PASS_MAPS, PASS_SCAN, PASS_REPLAY, PASS_TRANSFORM = 1, 2, 3, 4
 
 LIB_PATH = Path(__file__).resolve().parent / "libla.so"
@@ -62,6 +63,14 @@ def load(path: str | None = None):
     lib.la_prefill_segments.restype = i32
     lib.la_decode_step.argtypes = [i32, i32, i32, i32, i32, f32] + [vp] * 10 + [vp]
     lib.la_decode_step.restype = i32
+    lib.la_write_scores.argtypes = [i32, i32, i32, i64, i32, i32, vp, vp, vp, vp]
+    lib.la_write_scores.restype = i32
+    lib.la_write_windows.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.la_write_windows.restype = i32
+    lib.la_note_addresses.argtypes = [i32, i32, i32, i64, i32, i32, i32] + [vp] * 7
+    lib.la_note_addresses.restype = i32
+    lib.la_address_votes.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32] + [vp] * 6
+    lib.la_address_votes.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -170,3 +179,65 @@ def decode_step(variant, S, q, k, v, alpha=None, beta=None, z=None, eps=1e-6, S_
     if st != 0:
         raise LAError(st, "la_decode_step")
     return o, S_out, z_out
+
+
+# ------------------------------------------------------------------ NoteBank write / address steps
+
+
+def write_scores(k, chunk=512, d_head=None, d_mean=None, stream=None):
+    """la_write_scores: key distinctiveness per write chunk.  k [B,H,T,d_k] (fp32 or bf16).
+    Returns (d_head [B,H,T], d_mean [B,T]) fp32."""
+    B, H, T, dk = k.shape
+    if d_head is None:
+        d_head = torch.empty((B, H, T), dtype=torch.float32, device=k.device)
+    if d_mean is None:
+        d_mean = torch.empty((B, T), dtype=torch.float32, device=k.device)
+    st = load().la_write_scores(_dtype(k), B, H, T, dk, int(chunk), _p(k), _p(d_head), _p(d_mean),
+                                _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_write_scores")
+    return d_head, d_mean
+
+
+def write_windows(d_mean, chunk=512, window=48, tail=32, stream=None):
+    """la_write_windows: (best_start [B, T//chunk] int64, best_sum fp32) per complete chunk."""
+    B, T = d_mean.shape
+    nc = T // chunk
+    start = torch.empty((B, nc), dtype=torch.int64, device=d_mean.device)
+    val = torch.empty((B, nc), dtype=torch.float32, device=d_mean.device)
+    st = load().la_write_windows(B, T, int(chunk), int(window), int(tail), _p(d_mean), _p(start), _p(val),
+                                 _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_write_windows")
+    return start, val
+
+
+def note_addresses(d_head, q, spans, coords, stream=None):
+    """la_note_addresses: (t_star [B,N,H] int64, rho [B,N,H,d_rho] in q's dtype) for spans
+    [B,N,2] int64 (start, length) and coords [H,d_rho] int32."""
+    B, H, T, dk = q.shape
+    N, drho = spans.shape[1], coords.shape[1]
+    t_star = torch.empty((B, N, H), dtype=torch.int64, device=q.device)
+    rho = torch.empty((B, N, H, drho), dtype=q.dtype, device=q.device)
+    st = load().la_note_addresses(_dtype(q), B, H, T, dk, N, drho, _p(d_head), _p(q), _p(spans), _p(coords),
+                                  _p(t_star), _p(rho), _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_note_addresses")
+    return t_star, rho
+
+
+def address_votes(rho, u, R, positions, want_score=True, stream=None):
+    """la_address_votes: rho [N,J,d_rho], u [n_Q,J,d_rho] (same dtype), positions [N] int64.
+    Returns (score [J,N] fp32 or None, choice [J], votes [N], selected [R]) int32."""
+    N, J, drho = rho.shape
+    nQ = u.shape[0]
+    dev = rho.device
+    score = torch.empty((J, N), dtype=torch.float32, device=dev) if want_score else None
+    choice = torch.empty(J, dtype=torch.int32, device=dev)
+    votes = torch.empty(N, dtype=torch.int32, device=dev)
+    sel = torch.empty(R, dtype=torch.int32, device=dev)
+    st = load().la_address_votes(_dtype(rho), N, J, nQ, drho, _p(rho), _p(u), int(R), _p(positions), _p(score),
+                                 _p(choice), _p(votes), _p(sel), _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_address_votes")
+    return score, choice, votes, sel

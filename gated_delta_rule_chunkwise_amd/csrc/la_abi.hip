@@ -270,4 +270,87 @@ int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, c
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+int la_write_scores(int dtype, int batch, int heads, int64_t seq_len, int d_k, int chunk,
+                    const void *k, float *d_head, float *d_mean, void *stream) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
+  if (batch <= 0 || heads <= 0 || seq_len < 0 || d_k <= 0 || chunk <= 0) return LA_ERR_INVALID;
+  if (d_k != 64 && d_k != 128 && d_k != 256) return LA_ERR_UNSUPPORTED;
+  if (batch > 65535 || heads > 65535 || (seq_len + chunk - 1) / chunk > INT32_MAX) return LA_ERR_UNSUPPORTED;
+  if (seq_len == 0) return LA_OK;
+  if (!k || !d_head) return LA_ERR_NULL;
+  if (misaligned(k) || misaligned(d_head, 4) || misaligned(d_mean, 4)) return LA_ERR_ALIGN;
+  const size_t es = dtype == LA_F32 ? 4 : 2, BHT = (size_t)batch * heads * seq_len;
+  const Range rk{k, BHT * d_k * es}, rd{d_head, BHT * 4}, rm{d_mean, (size_t)batch * seq_len * 4};
+  if (overlap(rk, rd) || overlap(rk, rm) || overlap(rd, rm)) return LA_ERR_ALIAS;
+  const hipError_t e = launch_write_scores(dtype, batch, heads, seq_len, d_k, chunk, k, d_head, d_mean,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+int la_write_windows(int batch, int64_t seq_len, int chunk, int window, int tail,
+                     const float *d_mean, int64_t *best_start, float *best_sum, void *stream) {
+  if (batch <= 0 || seq_len < 0 || chunk <= 0 || window <= 0 || tail < 0 || tail > chunk)
+    return LA_ERR_INVALID;
+  if (batch > 65535 || seq_len / chunk > INT32_MAX) return LA_ERR_UNSUPPORTED;
+  const int64_t nc = seq_len / chunk;
+  if (nc == 0) return LA_OK;
+  if (!d_mean || !best_start) return LA_ERR_NULL;
+  if (misaligned(d_mean, 4) || misaligned(best_start, 8) || misaligned(best_sum, 4)) return LA_ERR_ALIGN;
+  const Range rm{d_mean, (size_t)batch * seq_len * 4}, rs{best_start, (size_t)batch * nc * 8},
+      rv{best_sum, (size_t)batch * nc * 4};
+  if (overlap(rm, rs) || overlap(rm, rv) || overlap(rs, rv)) return LA_ERR_ALIAS;
+  const hipError_t e = launch_write_windows(batch, seq_len, chunk, window, tail, d_mean, best_start, best_sum,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+int la_note_addresses(int dtype, int batch, int heads, int64_t seq_len, int d_k, int n_notes,
+                      int d_rho, const float *d_head, const void *q, const int64_t *spans,
+                      const int32_t *coords, int64_t *t_star, void *rho, void *stream) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
+  if (batch <= 0 || heads <= 0 || seq_len <= 0 || d_k <= 0 || n_notes < 0 || d_rho <= 0) return LA_ERR_INVALID;
+  if (heads > 16 || d_rho > d_k || batch > 65535) return LA_ERR_UNSUPPORTED;
+  if (n_notes == 0) return LA_OK;
+  if (!d_head || !q || !spans || !coords || !t_star || !rho) return LA_ERR_NULL;
+  const size_t es = dtype == LA_F32 ? 4 : 2;
+  if (misaligned(d_head, 4) || misaligned(q, es) || misaligned(spans, 8) || misaligned(coords, 4) ||
+      misaligned(t_star, 8) || misaligned(rho, es))
+    return LA_ERR_ALIGN;
+  const size_t BN = (size_t)batch * n_notes, BHT = (size_t)batch * heads * seq_len;
+  const Range rt{t_star, BN * heads * 8}, rr{rho, BN * heads * d_rho * es};
+  const Range ins[] = {{d_head, BHT * 4}, {q, BHT * d_k * es}, {spans, BN * 16}, {coords, (size_t)heads * d_rho * 4}};
+  if (overlap(rt, rr)) return LA_ERR_ALIAS;
+  for (const Range &r : ins)
+    if (overlap(rt, r) || overlap(rr, r)) return LA_ERR_ALIAS;
+  const hipError_t e = launch_note_addresses(dtype, batch, heads, seq_len, d_k, n_notes, d_rho, d_head, q, spans,
+                                             coords, t_star, rho, (hipStream_t)stream);
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+int la_address_votes(int dtype, int n_notes, int channels, int n_query, int d_rho,
+                     const void *rho, const void *u, int R, const int64_t *positions, float *score,
+                     int32_t *choice, int32_t *votes, int32_t *selected, void *stream) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
+  if (n_notes <= 0 || channels <= 0 || n_query <= 0 || d_rho <= 0 || R <= 0) return LA_ERR_INVALID;
+  if ((d_rho != 8 && d_rho != 16 && d_rho != 32) || n_query > 1024 || R > 64 || channels > 65535)
+    return LA_ERR_UNSUPPORTED;
+  if (!rho || !u || !positions || !choice || !votes || !selected) return LA_ERR_NULL;
+  const size_t es = dtype == LA_F32 ? 4 : 2;
+  if (misaligned(rho, es) || misaligned(u, es) || misaligned(positions, 8) || misaligned(score, 4) ||
+      misaligned(choice, 4) || misaligned(votes, 4) || misaligned(selected, 4))
+    return LA_ERR_ALIGN;
+  const size_t N = n_notes, J = channels;
+  const Range outs[] = {{score, J * N * 4}, {choice, J * 4}, {votes, N * 4}, {selected, (size_t)R * 4}};
+  const Range ins[] = {{rho, N * J * d_rho * es}, {u, (size_t)n_query * J * d_rho * es}, {positions, N * 8}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return LA_ERR_ALIAS;
+    for (const Range &r : ins)
+      if (overlap(outs[i], r)) return LA_ERR_ALIAS;
+  }
+  const hipError_t e = launch_address_votes(dtype, n_notes, channels, n_query, d_rho, rho, u, R, positions, score,
+                                            choice, votes, selected, (hipStream_t)stream);
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 }  // extern "C"

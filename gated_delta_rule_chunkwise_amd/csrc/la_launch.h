@@ -47,6 +47,18 @@ hipError_t launch_based_chunk_prefill(bool compact, int B, int H, int64_t T, flo
                                       float *z_T, void *workspace, int pass_mask, hipStream_t s);
 void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks);
 
+// notebank.hip (NoteBank write and address steps)
+hipError_t launch_write_scores(int dtype, int B, int H, int64_t T, int d_k, int chunk, const void *k,
+                               float *d_head, float *d_mean, hipStream_t s);
+hipError_t launch_write_windows(int B, int64_t T, int chunk, int window, int tail, const float *d_mean,
+                                int64_t *best_start, float *best_sum, hipStream_t s);
+hipError_t launch_note_addresses(int dtype, int B, int H, int64_t T, int d_k, int N, int d_rho,
+                                 const float *d_head, const void *q, const int64_t *spans, const int *coords,
+                                 int64_t *t_star, void *rho, hipStream_t s);
+hipError_t launch_address_votes(int dtype, int N, int J, int nQ, int d_rho, const void *rho, const void *u,
+                                int R, const int64_t *positions, float *score, int *choice, int *votes,
+                                int *selected, hipStream_t s);
+
 // util (la_abi.hip): copy or zero-fill n floats with a kernel (capture-safe, no memset nodes)
 hipError_t launch_copy_or_zero(const float *src, float *dst, size_t n, hipStream_t s);
 

@@ -198,6 +198,73 @@ int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, c
                    const float *z_in, float *S_out, float *z_out, const void *q, const void *k,
                    const void *v, const void *alpha, const void *beta, void *o, void *stream);
 
+/*
+ * ---------------------------------------------------------------------------------
+ * NoteBank write and address steps on the recurrence's keys and queries
+ * ("History Replays Itself: Unleashing Long-Context Capability in Linear Attention",
+ * Sec. 3 Eqs. (3)-(5), App. B.2 Eq. (8), App. B.3 Eq. (9)).  The channels (l, h) are the
+ * heads of one layer (a caller with several layers stacks them as heads).  Argmax ties go
+ * to the earliest index; the pages fix a tie rule only for the vote ranking (earlier-
+ * inserted notes first), and the same rule is used throughout.  Choosing the note spans
+ * from sentence boundaries needs the text and is the caller's: the library scores windows
+ * and builds addresses for given spans.  All pointers are DEVICE memory; the calls are
+ * asynchronous on `stream`; nothing is allocated.
+ * ---------------------------------------------------------------------------------
+ */
+
+/*
+ * la_write_scores -- key distinctiveness (Eqs. (3), (8)).  Per write chunk of `chunk`
+ * tokens (the last, possibly partial, chunk over its own tokens) and head:
+ *   khat_t = k_t / |k_t|,  mubar = normalised mean of khat over the chunk,
+ *   d_head[b][h][t] = 1 - <khat_t, mubar>       (a zero key or mean normalises to zero)
+ *   d_mean[b][t]    = (1/H) sum_h d_head[b][h][t]   (the channel average; may be NULL)
+ * k [B][H][T][d_k] in `dtype` (LA_F32 / LA_BF16), 16-byte aligned; d_head [B][H][T] and
+ * d_mean [B][T] fp32.  Computed in fp32 (one read of k from HBM).
+ * Supported: d_k in {64, 128, 256}, chunk >= 1.
+ */
+int la_write_scores(int dtype, int batch, int heads, int64_t seq_len, int d_k, int chunk,
+                    const void *k, float *d_head, float *d_mean, void *stream);
+
+/*
+ * la_write_windows -- the write step's best window (App. B.2): for every COMPLETE write
+ * chunk c (a final incomplete chunk makes no note), the candidate region is
+ * [max(0, c chunk - tail), (c + 1) chunk) -- the chunk plus the previous chunk's last
+ * `tail` tokens with their own scores -- and every `window` consecutive tokens in it (the
+ * whole region if it is shorter) are scored by the sum of d_mean.  best_start [B][T/chunk]
+ * (int64) receives the highest-scoring window's first token, best_sum (fp32, may be NULL)
+ * its score.  Sums in fp32.  Requires chunk >= 1, window >= 1, 0 <= tail <= chunk.
+ */
+int la_write_windows(int batch, int64_t seq_len, int chunk, int window, int tail,
+                     const float *d_mean, int64_t *best_start, float *best_sum, void *stream);
+
+/*
+ * la_note_addresses -- native addresses (Eqs. (4), (9)).  For note i with span
+ * spans[b][i] = (start, length) and head h: t_star[b][i][h] = argmax over the span of
+ * d_head[b][h][t], and rho[b][i][h][r] = q[b][h][t*][coords[h][r]] (the query, in q's
+ * dtype, at the head's fixed coordinates; not normalised).  q [B][H][T][d_k];
+ * spans [B][N][2] int64; coords [H][d_rho] int32 (distinct values in [0, d_k) per head).
+ * A span outside [0, T) (or empty) yields t_star = -1 and a zero address; a coordinate
+ * outside [0, d_k) yields a zero entry (device data is not inspected on the host).
+ * Supported: heads <= 16, 1 <= d_rho <= d_k.
+ */
+int la_note_addresses(int dtype, int batch, int heads, int64_t seq_len, int d_k, int n_notes,
+                      int d_rho, const float *d_head, const void *q, const int64_t *spans,
+                      const int32_t *coords, int64_t *t_star, void *rho, void *stream);
+
+/*
+ * la_address_votes -- addressing and voting (Eq. (5)).  rho [N][J][d_rho] note addresses,
+ * u [n_query][J][d_rho] question features, both in `dtype`; in fp32 (App. B.3: both cast
+ * to fp32 and l2-normalised):  score[j][i] = max_tau <uhat_tau, rhohat_i> (a zero vector
+ * has cosine 0; score may be NULL), choice[j] = argmax_i score[j][i], votes[i] = number of
+ * channels choosing i.  selected [R] receives up to R notes with the most votes (and at
+ * least one; equal votes: the lower index, i.e. the earlier-inserted note) in document
+ * order (by positions[i], int64, then index), padded with -1.
+ * Supported: d_rho in {8, 16, 32}, n_query <= 1024, 1 <= R <= 64.
+ */
+int la_address_votes(int dtype, int n_notes, int channels, int n_query, int d_rho,
+                     const void *rho, const void *u, int R, const int64_t *positions, float *score,
+                     int32_t *choice, int32_t *votes, int32_t *selected, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -170,3 +170,32 @@ def test_decode_validation(lib):
     assert decode(lib, S_in=A + 8) == -4              # states 16-byte aligned
     assert decode(lib, o=6 * A + 32) == -6            # o overlaps v
     assert decode(lib, S_out=A + 1024) == -6          # partial overlap of the states
+
+
+def test_notebank_validation(lib):
+    """The NoteBank entry points validate before launching (no device memory is touched)."""
+    f = lambda x: None if x is None else P(x)
+    ws = lambda dtype=la.BF16, B=1, H=4, T=1000, dk=128, C=512, k=A, dh=2 * A, dm=3 * A: \
+        lib.la_write_scores(dtype, B, H, T, dk, C, f(k), f(dh), f(dm), None)
+    assert ws(dtype=3) == -2 and ws(C=0) == -2 and ws(B=0) == -2
+    assert ws(dk=96) == -3
+    assert ws(k=None) == -1 and ws(dh=None) == -1
+    assert ws(k=A + 8) == -4
+    assert ws(dh=A) == -6  # output overlaps the keys
+    assert ws(T=0, k=None) == 0
+    ww = lambda B=1, T=1024, C=512, W=48, tail=32, dm=A, bs=2 * A, bv=3 * A: \
+        lib.la_write_windows(B, T, C, W, tail, f(dm), f(bs), f(bv), None)
+    assert ww(tail=600) == -2 and ww(W=0) == -2 and ww(tail=-1) == -2
+    assert ww(bs=None) == -1 and ww(bs=A + 4) == -4
+    assert ww(T=100, dm=None, bs=None) == 0  # no complete chunk: nothing to do
+    na = lambda dtype=la.BF16, B=1, H=8, T=1000, dk=128, N=4, dr=16, dh=A, q=2 * A, sp=3 * A, co=4 * A, \
+        ts=5 * A, rho=6 * A: lib.la_note_addresses(dtype, B, H, T, dk, N, dr, f(dh), f(q), f(sp), f(co),
+                                                   f(ts), f(rho), None)
+    assert na(H=17) == -3 and na(dr=200) == -3 and na(N=-1) == -2
+    assert na(sp=None) == -1 and na(ts=A) == -6
+    assert na(N=0, dh=None) == 0
+    av = lambda dtype=la.BF16, N=100, J=8, nQ=20, dr=16, R=4, rho=A, u=2 * A, pos=3 * A, sc=4 * A, ch=5 * A, \
+        vo=6 * A, se=7 * A: lib.la_address_votes(dtype, N, J, nQ, dr, f(rho), f(u), R, f(pos), f(sc), f(ch),
+                                                 f(vo), f(se), None)
+    assert av(dr=12) == -3 and av(nQ=2000) == -3 and av(R=65) == -3 and av(R=0) == -2
+    assert av(ch=None) == -1 and av(se=A) == -6
