@@ -73,6 +73,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-based", action="store_true")
+    ap.add_argument("--no-notebank", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB copy (la_prefill with T = 0) so that HBM "
                          "byte counters can be scaled against a known size")
@@ -215,6 +216,11 @@ def main():
         based = bench_based(torch, la, synth, dev, stream, args.steps)
         based["compact"] = bench_based(torch, la, synth, dev, stream, args.steps, "based_compact")
 
+    # ---------------------------------------------------------------- NoteBank steps
+    notebank = None
+    if not args.no_notebank:
+        notebank = bench_notebank(torch, la, synth, dev, stream)
+
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -232,6 +238,7 @@ def main():
         "prefill": prefill_detail,
         "decode": decode,
         "based_prefill": based,
+        "notebank": notebank,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -334,6 +341,46 @@ def bench_based(torch, la, synth, dev, stream, steps, variant="based"):
             "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
             "alg_bytes": alg_bytes, "alg_flops": alg_flops, "segments": nseg,
             "roofline_time_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof * 1e3 / ms, 4)}
+
+
+def bench_notebank(torch, la, synth, dev, stream):
+    """NoteBank write scoring over the 1M-token, 16-head keys (512-token write chunks, 48-token
+    windows, 32-token tails) and addressing at the pages' archive size (4092 notes, 192 channels,
+    d_rho = 16, a 128-token question, R = 8)."""
+    B, H, T, D = 1, 16, 1 << 20, 128
+    k = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=3, device=dev)["k"]
+    d_head = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    d_mean = torch.empty((B, T), dtype=torch.float32, device=dev)
+
+    def timed(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_s = timed(lambda: la.write_scores(k, 512, d_head=d_head, d_mean=d_mean, stream=stream))
+    ms_w = timed(lambda: la.write_windows(d_mean, 512, 48, 32, stream=stream))
+    bytes_s = B * H * T * (D * 2 + 4) + B * T * 4 + B * H * T * 4  # keys, d_head out, d_mean (read H rows, write 1)
+    del k
+    N, J, nQ, dr, R = 4092, 192, 128, 16, 8
+    g = torch.Generator(device=dev).manual_seed(11)
+    rho = torch.randn((N, J, dr), generator=g, device=dev).to(torch.bfloat16)
+    u = torch.randn((nQ, J, dr), generator=g, device=dev).to(torch.bfloat16)
+    pos = torch.arange(N, dtype=torch.int64, device=dev) * 256
+    ms_v = timed(lambda: la.address_votes(rho, u, R, pos, want_score=False, stream=stream))
+    flops_v = 2 * nQ * N * J * dr
+    return {"write_scores": {"workload": "keys B=1 H=16 T=1048576 d_k=128 bf16, 512-token write chunks",
+                             "ms": round(ms_s, 4), "alg_bytes": bytes_s,
+                             "hbm_frac": round(bytes_s / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "write_windows": {"ms": round(ms_w, 4), "chunks": T // 512},
+            "address_votes": {"workload": f"{N} notes x {J} channels, d_rho={dr}, {nQ}-token question, R={R}",
+                              "ms": round(ms_v, 4), "alg_flops": flops_v,
+                              "fp32_vector_frac": round(flops_v / (ms_v * 1e-3) / 157.3e12, 4)}}
 
 
 def bench_cpu(host, H, D, target_s):

@@ -59,18 +59,30 @@ __global__ __launch_bounds__(WS_THREADS) void write_scores_kernel(int64_t T_len,
   const int n = (int)((T_len - c0) < C ? (T_len - c0) : C);
   const T *kc = k + (bh * T_len + c0) * DK;
 
-  // pass 1: sum of the unit keys (the 1/|chunk| of the mean cancels in the normalisation)
+  // pass 1: sum of the unit keys (the 1/|chunk| of the mean cancels in the normalisation);
+  // UNR token steps loaded before any is used
+  constexpr int UNR = 4;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t = wave * TPW + tok; t < n; t += TPS) {
-    float x[8];
-    load8<T>(kc + (size_t)t * DK + 8 * sub, x);
-    float ss = 0.0f;
+  for (int t0 = wave * TPW + tok; t0 < n; t0 += UNR * TPS) {
+    float x[UNR][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-    ss = group_sum<LPT>(ss);
-    const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
+    for (int u = 0; u < UNR; ++u) {
+      const int t = t0 + u * TPS;
+      if (t < n) load8<T>(kc + (size_t)t * DK + 8 * sub, x[u]);
+      else
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += x[j] * inv;
+        for (int j = 0; j < 8; ++j) x[u][j] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += x[u][j] * x[u][j];
+      ss = group_sum<LPT>(ss);
+      const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += x[u][j] * inv;
+    }
   }
   // lanes with the same `sub` hold the same 8 coordinates: fold the token groups
 #pragma unroll
@@ -102,18 +114,29 @@ __global__ __launch_bounds__(WS_THREADS) void write_scores_kernel(int64_t T_len,
 #pragma unroll
   for (int j = 0; j < 8; ++j) mb[j] = s_mubar[8 * sub + j];
   float *dh = d_head + bh * T_len + c0;
-  for (int t = wave * TPW + tok; t < n; t += TPS) {
-    float x[8];
-    load8<T>(kc + (size_t)t * DK + 8 * sub, x);
-    float ss = 0.0f, dot = 0.0f;
+  for (int t0 = wave * TPW + tok; t0 < n; t0 += UNR * TPS) {
+    float x[UNR][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ss += x[j] * x[j];
-      dot += x[j] * mb[j];
+    for (int u = 0; u < UNR; ++u) {
+      const int t = t0 + u * TPS;
+      if (t < n) load8<T>(kc + (size_t)t * DK + 8 * sub, x[u]);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[u][j] = 0.0f;
     }
-    ss = group_sum<LPT>(ss);
-    dot = group_sum<LPT>(dot);
-    if (sub == 0) dh[t] = 1.0f - (ss > 0.0f ? dot / sqrtf(ss) : 0.0f);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      float ss = 0.0f, dot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ss += x[u][j] * x[u][j];
+        dot += x[u][j] * mb[j];
+      }
+      ss = group_sum<LPT>(ss);
+      dot = group_sum<LPT>(dot);
+      const int t = t0 + u * TPS;
+      if (sub == 0 && t < n) dh[t] = 1.0f - (ss > 0.0f ? dot / sqrtf(ss) : 0.0f);
+    }
   }
 }
 
