@@ -191,3 +191,32 @@ def test_address_votes_pages_example(la):
     torch.cuda.synchronize()
     assert ch.tolist() == [0, 1, 0] and vo.tolist() == [2, 1]
     assert sel.tolist() == [1, 0] and sel1.tolist() == [0] and sel4.tolist() == [1, 0, -1, -1]
+
+
+def test_write_scores_full_size_sampled_chunks(la):
+    """The 1M-token, 16-head keys of the gated-delta prefill: every score of a sample of write
+    chunks (chunks are independent, so the oracle scores just those) and the windows of the
+    sampled chunks from the GPU's own d_mean."""
+    B, H, T, D, C = 1, 16, 1 << 20, 128, 512
+    k = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=3, device=DEV)["k"]
+    dh, dm = la.write_scores(k, chunk=C)
+    torch.cuda.synchronize()
+    for c in (0, 1, 777, T // C - 1):
+        kc = k[:, :, c * C:(c + 1) * C]
+        odh, odm = oracle.write_scores(kc, chunk=C)
+        assert_abs(dh[:, :, c * C:(c + 1) * C], odh, 1e-5, f"d_head chunk {c}")
+        assert_abs(dm[:, c * C:(c + 1) * C], odm, 1e-5, f"d_mean chunk {c}")
+
+
+def test_address_votes_pages_archive_size(la):
+    """Addressing at the pages' archive size: 4092 notes, 192 channels (24 layers x 8 heads),
+    d_rho = 16, a 128-token question, R = 8."""
+    r = np.random.default_rng(12)
+    N, J, nQ, R = 4092, 192, 128, 8
+    rho = torch.tensor(r.standard_normal((N, J, 16)), dtype=torch.bfloat16, device=DEV)
+    u = torch.tensor(r.standard_normal((nQ, J, 16)), dtype=torch.bfloat16, device=DEV)
+    pos = torch.tensor(np.arange(N) * 256, dtype=torch.int64, device=DEV)
+    sc, ch, vo, sel = la.address_votes(rho, u, R, pos)
+    torch.cuda.synchronize()
+    _check_votes(sc.cpu().numpy(), ch.cpu().numpy(), vo.cpu().numpy(), sel.cpu().numpy(),
+                 to64(rho), to64(u), R, pos.cpu().numpy())
