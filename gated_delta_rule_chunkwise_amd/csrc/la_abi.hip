@@ -332,7 +332,8 @@ int la_address_votes(int dtype, int n_notes, int channels, int n_query, int d_rh
                      int32_t *choice, int32_t *votes, int32_t *selected, void *stream) {
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
   if (n_notes <= 0 || channels <= 0 || n_query <= 0 || d_rho <= 0 || R <= 0) return LA_ERR_INVALID;
-  if ((d_rho != 8 && d_rho != 16 && d_rho != 32) || n_query > 1024 || R > 64 || channels > 65535)
+  if ((d_rho != 8 && d_rho != 16 && d_rho != 32) || n_query > 1024 || R > 64 || channels > 65535 ||
+      n_notes > 16384)
     return LA_ERR_UNSUPPORTED;
   if (!rho || !u || !positions || !choice || !votes || !selected) return LA_ERR_NULL;
   const size_t es = dtype == LA_F32 ? 4 : 2;

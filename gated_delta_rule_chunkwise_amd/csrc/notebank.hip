@@ -248,52 +248,71 @@ __global__ void note_address_kernel(int H, int64_t T_len, int DK, int N, int DR,
   }
 }
 
-// One workgroup (256 threads) per channel j.  The question vectors are normalised once into
-// LDS; each thread takes notes i = tid, tid + 256, ... and keeps its address in registers.
+// One workgroup (1024 threads) per channel j.  The question vectors are normalised once into
+// LDS; each thread takes notes i = tid, tid + 1024, ... two at a time (every LDS read of a
+// question vector serves both) and keeps their addresses in registers.
+constexpr int VT = 1024;
 template <int DR, typename T>
-__global__ __launch_bounds__(256) void channel_vote_kernel(int N, int J, int nQ, const T *__restrict__ rho,
-                                                           const T *__restrict__ u, float *__restrict__ score,
-                                                           int *__restrict__ choice) {
+__device__ __forceinline__ float unit_address(const T *r, float (&x)[DR]) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < DR; ++e) {
+    x[e] = io<T>::ld(r, e);
+    ss += x[e] * x[e];
+  }
+  return ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
+}
+template <int DR, typename T>
+__global__ __launch_bounds__(VT) void channel_vote_kernel(int N, int J, int nQ, const T *__restrict__ rho,
+                                                          const T *__restrict__ u, float *__restrict__ score,
+                                                          int *__restrict__ choice) {
   extern __shared__ float s_u[];  // [nQ][DR], normalised
-  __shared__ float sv[4];
-  __shared__ long long si[4];
+  __shared__ float sv[VT / 64];
+  __shared__ long long si[VT / 64];
   const int j = blockIdx.x, tid = threadIdx.x;
-  for (int tau = tid; tau < nQ; tau += 256) {
-    const T *x = u + ((size_t)tau * J + j) * DR;
-    float ss = 0.0f;
-    for (int e = 0; e < DR; ++e) {
-      const float v = io<T>::ld(x, e);
-      ss += v * v;
-    }
-    const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
-    for (int e = 0; e < DR; ++e) s_u[tau * DR + e] = io<T>::ld(x, e) * inv;
+  for (int tau = tid; tau < nQ; tau += VT) {
+    float x[DR];
+    const float inv = unit_address<DR, T>(u + ((size_t)tau * J + j) * DR, x);
+#pragma unroll
+    for (int e = 0; e < DR; ++e) s_u[tau * DR + e] = x[e] * inv;
   }
   __syncthreads();
   float bv = -INFINITY;
   long long bi = 0;
-  for (int i = tid; i < N; i += 256) {
-    const T *r = rho + ((size_t)i * J + j) * DR;
-    float rr[DR];
-    float ss = 0.0f;
+  for (int i0 = tid; i0 < N; i0 += 2 * VT) {
+    const int i1 = i0 + VT;
+    const bool has1 = i1 < N;
+    float r0[DR], r1[DR];
+    const float n0 = unit_address<DR, T>(rho + ((size_t)i0 * J + j) * DR, r0);
+    const float n1 = has1 ? unit_address<DR, T>(rho + ((size_t)i1 * J + j) * DR, r1) : 0.0f;
 #pragma unroll
     for (int e = 0; e < DR; ++e) {
-      rr[e] = io<T>::ld(r, e);
-      ss += rr[e] * rr[e];
+      r0[e] *= n0;
+      r1[e] = has1 ? r1[e] * n1 : 0.0f;
     }
-    const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
-#pragma unroll
-    for (int e = 0; e < DR; ++e) rr[e] *= inv;
-    float m = -INFINITY;
+    float m0 = -INFINITY, m1 = -INFINITY;
     for (int tau = 0; tau < nQ; ++tau) {
-      float dot = 0.0f;
+      float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
-      for (int e = 0; e < DR; ++e) dot += s_u[tau * DR + e] * rr[e];
-      m = fmaxf(m, dot);
+      for (int e = 0; e < DR; ++e) {
+        const float x = s_u[tau * DR + e];
+        d0 += x * r0[e];
+        d1 += x * r1[e];
+      }
+      m0 = fmaxf(m0, d0);
+      m1 = fmaxf(m1, d1);
     }
-    if (score) score[(size_t)j * N + i] = m;
-    if (better(m, i, bv, bi)) {
-      bv = m;
-      bi = i;
+    if (score) score[(size_t)j * N + i0] = m0;
+    if (better(m0, i0, bv, bi)) {
+      bv = m0;
+      bi = i0;
+    }
+    if (has1) {
+      if (score) score[(size_t)j * N + i1] = m1;
+      if (better(m1, i1, bv, bi)) {
+        bv = m1;
+        bi = i1;
+      }
     }
   }
   block_argmax(bv, bi, sv, si);
@@ -302,26 +321,27 @@ __global__ __launch_bounds__(256) void channel_vote_kernel(int N, int J, int nQ,
 
 // One workgroup of 1024 threads: votes, the R best notes by (votes, earlier index), then
 // document order by (position, index).
+constexpr int MAX_NOTES = 16384;  // votes counted in LDS
 __global__ __launch_bounds__(1024) void select_notes_kernel(int N, int J, int R, const int *__restrict__ choice,
                                                             const int64_t *__restrict__ positions,
                                                             int *__restrict__ votes, int *__restrict__ selected) {
   __shared__ int s_sel[64];
   __shared__ int s_v[16];
   __shared__ int s_i[16];
+  __shared__ int s_votes[MAX_NOTES];
   const int tid = threadIdx.x;
-  for (int i = tid; i < N; i += 1024) {
-    int v = 0;
-    for (int j = 0; j < J; ++j) v += choice[j] == i;
-    votes[i] = v;
-  }
+  for (int i = tid; i < N; i += 1024) s_votes[i] = 0;
   __syncthreads();
+  for (int j = tid; j < J; j += 1024) atomicAdd(&s_votes[choice[j]], 1);  // integer counts: order-free
+  __syncthreads();
+  for (int i = tid; i < N; i += 1024) votes[i] = s_votes[i];
   int nsel = 0;
   for (int r = 0; r < R; ++r) {
     int bv = 0, bi = -1;  // only notes with at least one vote
     for (int i = tid; i < N; i += 1024) {
       int taken = 0;
       for (int s = 0; s < nsel; ++s) taken |= s_sel[s] == i;
-      const int v = votes[i];
+      const int v = s_votes[i];
       if (!taken && v > 0 && (v > bv || (v == bv && (bi < 0 || i < bi)))) {
         bv = v;
         bi = i;
@@ -422,10 +442,10 @@ hipError_t launch_address_votes(int dtype, int N, int J, int nQ, int d_rho, cons
 #define LA_VOTE(DR)                                                                                  \
   do {                                                                                               \
     if (dtype == T_BF16)                                                                             \
-      hipLaunchKernelGGL((nb::channel_vote_kernel<DR, bf16_t>), dim3(J), dim3(256), lds, s, N, J, nQ, \
+      hipLaunchKernelGGL((nb::channel_vote_kernel<DR, bf16_t>), dim3(J), dim3(nb::VT), lds, s, N, J, nQ, \
                          (const bf16_t *)rho, (const bf16_t *)u, score, choice);                     \
     else                                                                                             \
-      hipLaunchKernelGGL((nb::channel_vote_kernel<DR, float>), dim3(J), dim3(256), lds, s, N, J, nQ,  \
+      hipLaunchKernelGGL((nb::channel_vote_kernel<DR, float>), dim3(J), dim3(nb::VT), lds, s, N, J, nQ,  \
                          (const float *)rho, (const float *)u, score, choice);                       \
   } while (0)
   switch (d_rho) {

@@ -259,7 +259,7 @@ int la_note_addresses(int dtype, int batch, int heads, int64_t seq_len, int d_k,
  * channels choosing i.  selected [R] receives up to R notes with the most votes (and at
  * least one; equal votes: the lower index, i.e. the earlier-inserted note) in document
  * order (by positions[i], int64, then index), padded with -1.
- * Supported: d_rho in {8, 16, 32}, n_query <= 1024, 1 <= R <= 64.
+ * Supported: d_rho in {8, 16, 32}, n_query <= 1024, n_notes <= 16384, 1 <= R <= 64.
  */
 int la_address_votes(int dtype, int n_notes, int channels, int n_query, int d_rho,
                      const void *rho, const void *u, int R, const int64_t *positions, float *score,

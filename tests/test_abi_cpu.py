@@ -197,5 +197,5 @@ def test_notebank_validation(lib):
     av = lambda dtype=la.BF16, N=100, J=8, nQ=20, dr=16, R=4, rho=A, u=2 * A, pos=3 * A, sc=4 * A, ch=5 * A, \
         vo=6 * A, se=7 * A: lib.la_address_votes(dtype, N, J, nQ, dr, f(rho), f(u), R, f(pos), f(sc), f(ch),
                                                  f(vo), f(se), None)
-    assert av(dr=12) == -3 and av(nQ=2000) == -3 and av(R=65) == -3 and av(R=0) == -2
+    assert av(dr=12) == -3 and av(nQ=2000) == -3 and av(R=65) == -3 and av(R=0) == -2 and av(N=20000) == -3
     assert av(ch=None) == -1 and av(se=A) == -6
