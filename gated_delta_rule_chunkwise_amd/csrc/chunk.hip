@@ -49,25 +49,32 @@
 namespace la {
 namespace gdn {
 
-constexpr int C = 64;     // tokens per chunk
-constexpr int DK = 128;   // key width
-constexpr int DV = 128;   // value width
-constexpr int NW = 4;     // waves per state-carrying workgroup
-constexpr int NTHR = NW * 64;
-constexpr int RPW = DV / NW;  // state rows per wave (two 16-row column tiles)
+constexpr int C = 64;       // tokens per chunk
+constexpr int WROWS = 128;  // value rows (rows of S) carried by one state workgroup
 // Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
 // would raise register pressure past what two workgroups per CU allow).
 #define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
-constexpr int LDK = DK + 16;  // row-major bf16 tiles [C][DK]: K, Q, V (288-byte rows)
-constexpr int LDA = C + 16;   // bf16 [C][C]: decay-masked Q K^T, rows t, k-ordered columns
-constexpr int LDT = C + 16;   // bf16 [C][C]: T diag(beta), rows t, k-ordered columns
+constexpr int LDV = WROWS + 16;  // bf16 V tile [C][WROWS]: a workgroup's value columns (288-byte rows)
+constexpr int LDA = C + 16;      // bf16 [C][C]: decay-masked Q K^T, rows t, k-ordered columns
+constexpr int LDT = C + 16;      // bf16 [C][C]: T diag(beta), rows t, k-ordered columns
+
+// Geometry per key width (d_k = d_v).  A state workgroup carries WROWS rows of S over all
+// d_k keys, in registers: NW waves of 16 NCT rows each (NCT 16-row column tiles per wave).
+//   d = 128: 4 waves x 32 rows, one workgroup per (b, h, segment), two workgroups per CU
+//   d = 256: 8 waves x 16 rows (the same 64 state registers per lane), two row blocks per
+//            (b, h, segment); K and Q tiles of 34 KB each leave room for one workgroup per CU
+// K, Q tiles are [C][DK + 16] (the 16-element padding gives 2-row bank offsets as at 128).
+template <int DK_> struct Geo;
+template <> struct Geo<128> { static constexpr int DK = 128, DV = 128, NW = 4, NCT = 2; };
+template <> struct Geo<256> { static constexpr int DK = 256, DV = 256, NW = 8, NCT = 1; };
+// state-carrying waves of a map workgroup (one more wave issues the loads)
+template <bool DELTA, int DK> constexpr int map_waves() { return (DELTA || Geo<DK>::NCT == 1) ? 8 : 4; }
 
 // A stored transform, T diag(beta) in bf16, row-major in the MFMA k order: rows 0..31 keep
 // only their first 32 positions (the blocks right of the diagonal are zero), rows 32..63 all
 // 64: 6 KB per chunk.  tb_offset gives the element offset of row t.
 constexpr size_t T_CHUNK = 32 * 32 + 32 * 64;  // bf16 elements of one stored transform
 __host__ __device__ constexpr int tb_offset(int t) { return t < 32 ? 32 * t : 1024 + 64 * (t - 32); }
-static_assert(DK == DV, "square state");
 
 struct Args {
   const bf16_t *q, *k, *v, *alpha, *beta;
@@ -118,22 +125,42 @@ __device__ __forceinline__ bf16x8 kstate_frag(const bf16_t *tile, int ld, int m,
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// State rows held by a wave: column l16 of its state tile c is state row
+// State rows held by a wave.  Two column tiles (NCT = 2): column l16 of tile c is state row
 // row0 + srow(c, l16), srow = 8 (l16 / 4) + 4 c + l16 % 4.  An accumulator tile over state
 // rows (lane (g, l16) holds its rows 4 g + e) then covers rows row0 + 8 g + 4 c + e, so the
-// two tiles c = 0, 1 of one token give eight consecutive outputs (one 16-byte store).
-__device__ __forceinline__ int srow(int c, int l16) { return 8 * (l16 >> 2) + 4 * c + (l16 & 3); }
+// two tiles c = 0, 1 of one token give eight consecutive outputs (one 16-byte store).  One
+// column tile (NCT = 1): column l16 is row row0 + l16, and a lane's four outputs of one
+// token are consecutive (one 8-byte store).
+template <int NCT> __device__ __forceinline__ int srow(int c, int l16) {
+  return NCT == 2 ? 8 * (l16 >> 2) + 4 * c + (l16 & 3) : l16;
+}
 
-// V columns row0 + srow(c, i) as an operand with k = tokens (lane (g, i) receives tokens
+// V columns col0 + srow(c, i) as an operand with k = tokens (lane (g, i) receives tokens
 // 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3); the transpose read of col_frag with each
 // lane quad addressing its own 4-column chunk.
-__device__ __forceinline__ bf16x8 vrow_frag(const bf16_t *tile, int ld, int row0, int c, int s, int lane) {
+template <int NCT>
+__device__ __forceinline__ bf16x8 vrow_frag(const bf16_t *tile, int ld, int col0, int c, int s, int lane) {
   const int g = lane >> 4, i = lane & 15;
-  const bf16_t *p0 = tile + (32 * s + 4 * g + (i >> 2)) * ld + row0 + 8 * (i & 3) + 4 * c;
+  const bf16_t *p0 = tile + (32 * s + 4 * g + (i >> 2)) * ld + col0 + (NCT == 2 ? 8 * (i & 3) + 4 * c : 4 * (i & 3));
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0 + 16 * ld));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Block index -> (segment, row block) when NB workgroups share a segment: the NB blocks of
+// one segment are 8 indices apart, so they land on the same XCD (workgroups are dealt to
+// the 8 XCDs in turn) at about the same time and read the segment's K and Q through one
+// L2.  The grid covers 8 NB ceil(segments / 8) blocks; those past the last segment exit.
+template <int NB> __device__ __forceinline__ void split_block(int x, int &seg, int &rb) {
+  if (NB == 1) {
+    seg = x;
+    rb = 0;
+  } else {
+    const int q = x >> 3;
+    rb = q % NB;
+    seg = 8 * (q / NB) + (x & 7);
+  }
 }
 
 __device__ __forceinline__ bf16x8 pack_pair(f32x4 a, f32x4 b) {
@@ -176,13 +203,16 @@ struct TPrepLds {
   float d[4][SZD];
 };
 
-__global__ __launch_bounds__(NTHR, 4) void tprep_kernel(const Args a) {
-  __shared__ __attribute__((aligned(16))) TPrepLds sm[NW];
+constexpr int TPW = 4;  // independent waves (chunks) per transform workgroup
+// d = 256 holds twice the key fragments (128 registers), so two waves per SIMD
+template <int DK>
+__global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) TPrepLds sm[TPW];
   // the wave index is uniform across the wave: saying so keeps every per-chunk address
   // and buffer descriptor in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int64_t cid = (int64_t)blockIdx.x * NW + wave;
+  const int64_t cid = (int64_t)blockIdx.x * TPW + wave;
   if (cid >= (int64_t)a.B * a.H * a.nch) return;
   const int64_t bh = cid / a.nch, t0 = (cid % a.nch) * C;
   const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
@@ -398,10 +428,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Fill a row-padded LDS tile (ROWS rows of ROWB bytes at a stride of LDB bytes) from ROWS
-// contiguous global rows.  Wave-instruction j writes LDS bytes [1024 j, 1024 j + 1024), lane
+// global rows SRCB bytes apart (the first ROWB bytes of each).  Wave-instruction j writes LDS bytes [1024 j, 1024 j + 1024), lane
 // L's 16 bytes at 1024 j + 16 L; lanes that fall in the padding, or past the descriptor's
 // size (rows beyond a partial chunk), write zeros.
-template <int ROWB, int LDB, int ROWS, int NWAVES, bool NT>
+template <int ROWB, int LDB, int ROWS, int NWAVES, bool NT, int SRCB = ROWB>
 __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, int lane) {
   constexpr int TOTAL = ROWS * LDB;
   static_assert(TOTAL % 1024 == 0, "whole wave-instructions");
@@ -413,7 +443,7 @@ __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, 
     if (j < NI) {
       const int p = 1024 * j + 16 * lane;
       const int row = p / LDB, off = p - row * LDB;
-      const uint32_t src = off < ROWB ? (uint32_t)(row * ROWB + off) : 0xFFFFFFF0u;
+      const uint32_t src = off < ROWB ? (uint32_t)(row * SRCB + off) : 0xFFFFFFF0u;
       lds_dma16<NT>(r, src, base + 1024u * (uint32_t)j);
     }
   }
@@ -476,34 +506,46 @@ __device__ __forceinline__ float wave_gates(float al, float be, bool additive, f
   return gC;
 }
 
-template <bool DELTA>
-__global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(const Args a) {
-  constexpr int NWT = DELTA ? 8 : 4;  // state-carrying waves; wave NWT issues every load
-  constexpr int MAPROWS = DELTA ? 2 * DV : DV;
-  __shared__ __attribute__((aligned(16))) bf16_t sK0[C * LDK], sK1[C * LDK], sV0[C * LDK], sV1[C * LDK];
+// Map rows are [B_seg rows 0 .. d_v - 1; M_seg rows d_v .. d_v + d_k - 1] (delta rule) or
+// B_seg rows only; a workgroup carries NWT * RPW of them (d = 128: all 256 / all 128; d = 256:
+// 128 of 512 / 128 of 256) and loads the V columns of its B rows only.
+template <bool DELTA, int DK>
+__global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kernel(const Args a) {
+  constexpr int DV = Geo<DK>::DV, NCT = Geo<DK>::NCT, RPW = 16 * NCT, LDK = DK + 16;
+  constexpr int NWT = map_waves<DELTA, DK>();  // state-carrying waves; wave NWT issues every load
+  constexpr int MAPROWS = DELTA ? DV + DK : DV;
+  constexpr int MWR = NWT * RPW;        // map rows per workgroup
+  constexpr int NMB = MAPROWS / MWR;    // workgroups per segment
+  constexpr int NIT = 4 * (DK / 32);    // (token tile, key step) pairs of a K S^T product
+  static_assert(MAPROWS % MWR == 0 && (DV % MWR == 0 || MWR > DV), "map blocks of one kind");
+  __shared__ __attribute__((aligned(16))) bf16_t sK0[C * LDK], sK1[C * LDK], sV0[C * LDV], sV1[C * LDV];
   __shared__ __attribute__((aligned(16))) bf16_t sT0[DELTA ? C * LDT : 8], sT1[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) float sGw[NWT][3 * C];
   __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][2][C];  // per copy: raw alpha, beta
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const bool m_kind = DELTA && wave >= NW;  // waves 4-7 carry the transition (M) rows
-  const int wr = m_kind ? wave - NW : wave;
-  const int row0 = wr * RPW;
-  const int seg = (int)blockIdx.x;
+  int seg, mb;
+  split_block<NMB>((int)blockIdx.x, seg, mb);
+  if (NMB > 1 && seg >= a.nseg - 1) return;  // (whole workgroup) past the last mapped segment
+  const int grow0 = mb * MWR + wave * RPW;  // first map row of this wave (unused by the loader)
+  const bool m_kind = DELTA && grow0 >= DV;  // transition (M) rows, started from the identity
+  const int row0 = m_kind ? grow0 - DV : grow0;
+  const int vcol0 = mb * MWR;                // first V column of the workgroup's tile
+  const bool has_v = vcol0 < DV;             // (workgroup-uniform) any B rows here
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
   const bool additive = a.variant == V_ADDITIVE;
   const bool use_beta = a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta);
   float *gw = sGw[wave];
 
-  f32x4 st[DK / 16][2];  // zero start (B rows) or identity (M rows)
+  f32x4 st[DK / 16][NCT];  // zero start (B rows) or identity (M rows)
 #pragma unroll
   for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < NCT; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st[m][c][e] = (m_kind && row0 + srow(c, l16) == sd(m, g) + e) ? 1.0f : 0.0f;
+      for (int e = 0; e < 4; ++e) st[m][c][e] = (m_kind && row0 + srow<NCT>(c, l16) == sd(m, g) + e) ? 1.0f : 0.0f;
 
   const int64_t first = (int64_t)seg * a.seg_chunks * C;
   int nchunks = a.seg_chunks;
@@ -516,7 +558,9 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
     dma_tile<DK * 2, LDK * 2, C, 1, true>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, 0, lane);
-    dma_tile<DV * 2, LDK * 2, C, 1, true>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)dV, 0, lane);
+    if (has_v)
+      dma_tile<WROWS * 2, LDV * 2, C, 1, true, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
+                                                       (unsigned char *)dV, 0, lane);
     if (DELTA)
       dma_tb<1, true>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2), (unsigned char *)dT, 0,
                 lane);
@@ -557,43 +601,43 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
     asm volatile("" : "+v"(lane_v));
     const int l16 = lane_v & 15, g = lane_v >> 4;
     gseg += gC;
-    bf16x8 dufr[2][2];
+    bf16x8 dufr[NCT][2];
     if (DELTA) {
       // U = TB (V - diag(gamma) K S^T) (no V for the M rows), as in the replay
-      f32x4 ks[4][2];
+      f32x4 ks[4][NCT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < NCT; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #define LA_KF(it) *reinterpret_cast<const bf16x8 *>(sK + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
       {
-        bf16x8 kf[3], sfr[2];
+        bf16x8 kf[3], sfr[NCT];
         kf[0] = LA_KF(0);
         kf[1] = LA_KF(1);
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < NIT; ++it) {
           const int s = it / 4, mt = it % 4;
-          if (it + 2 < 16) kf[(it + 2) % 3] = LA_KF(it + 2);
+          if (it + 2 < NIT) kf[(it + 2) % 3] = LA_KF(it + 2);
           if (mt == 0) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+            for (int c = 0; c < NCT; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
           }
           LA_FENCE();
 #pragma unroll
-          for (int c = 0; c < 2; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
+          for (int c = 0; c < NCT; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
         }
       }
 #undef LA_KF
       LA_FENCE();
-      bf16x8 yfr[2][2];
+      bf16x8 yfr[NCT][2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const f32x4 ga = ld4(gw + 32 * s + 4 * g), gb = ld4(gw + 32 * s + 16 + 4 * g);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NCT; ++c) {
           f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
           if (!m_kind) {
-            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s, lane_v);
+            const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s, lane_v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               y0[e] += (float)vf[e];
@@ -603,7 +647,7 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
           yfr[c][s] = pack_pair(y0, y1);
         }
       }
-      f32x4 U[4][2];
+      f32x4 U[4][NCT];
 #define LA_TF(mt, s) *reinterpret_cast<const bf16x8 *>(sT + (16 * (mt) + l16) * LDT + 32 * (s) + 8 * g)
       bf16x8 tfb[2];
       tfb[0] = LA_TF(0, 0);
@@ -617,10 +661,10 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
         LA_FENCE();
         if (s == 0) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < NCT; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
+        for (int c = 0; c < NCT; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
       }
 #undef LA_TF
       LA_FENCE();
@@ -628,7 +672,7 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
       for (int s2 = 0; s2 < 2; ++s2) {
         const f32x4 d0 = ld4(gw + 64 + 32 * s2 + 4 * g), d1 = ld4(gw + 64 + 32 * s2 + 16 + 4 * g);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) dufr[c][s2] = pack_pair(U[2 * s2][c] * d0, U[2 * s2 + 1][c] * d1);
+        for (int c = 0; c < NCT; ++c) dufr[c][s2] = pack_pair(U[2 * s2][c] * d0, U[2 * s2 + 1][c] * d1);
       }
     } else {  // U = diag(beta) V
 #pragma unroll
@@ -636,8 +680,8 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
         const f32x4 d0 = ld4(gw + 64 + 32 * s2 + 4 * g), d1 = ld4(gw + 64 + 32 * s2 + 16 + 4 * g);
         const f32x4 b0 = ld4(gw + 128 + 32 * s2 + 4 * g), b1 = ld4(gw + 128 + 32 * s2 + 16 + 4 * g);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s2, lane_v);
+        for (int c = 0; c < NCT; ++c) {
+          const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s2, lane_v);
           f32x4 u0, u1;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -661,7 +705,7 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
         }
         LA_FENCE();
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NCT; ++c) {
           f32x4 acc = st[m][c] * gam;
           acc = mfma_bf16(kb[m & 1][0], dufr[c][0], acc);
           acc = mfma_bf16(kb[m & 1][1], dufr[c][1], acc);
@@ -689,49 +733,63 @@ __global__ __launch_bounds__(((DELTA ? 8 : 4) + 1) * 64, 3) void map_kernel(cons
 #pragma unroll
   for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int r = rbase + row0 + srow(c, l16);
+    for (int c = 0; c < NCT; ++c) {
+      const int r = rbase + row0 + srow<NCT>(c, l16);
       *reinterpret_cast<f32x4 *>(dst + (size_t)r * DK + sd(m, g)) = st[m][c];
     }
-  if (!DELTA && tid == 0) a.gsum[bh * a.nseg + seg] = gseg;
+  if (!DELTA && tid == 0 && mb == 0) a.gsum[bh * a.nseg + seg] = gseg;
 }
 
 // Pass 2 (delta rule): segment start states S_{i+1} = S_i M_i + B_i for i = 0 .. nseg - 2,
 // with S_0 = S0 (the last segment's map is never needed: its replay writes S_T).  One
-// workgroup per (b, h) and block of 16 state rows, 8 waves; wave w forms output columns
-// 16 w .. 16 w + 15 transposed, (S M + B)^T = M^T S^T + B^T, on fp32 MFMA (16x16x4: exact
-// fp32 products, so the scan adds no rounding beyond fp32 accumulation).  A k-step pairs
-// lane group g with key 16 c + 4 g + e (c = 0..7, e = 0..3): the A operand is then row
-// 16 c + 4 g + e of M read along 16 consecutive columns, and the B operand S[row][16 c +
-// 4 g + e] is what wave c's accumulator held (lane (g, i) of a tile holds rows i, columns
-// 16 w + 4 g + 0..3), exchanged through a double-buffered LDS copy of the 16 rows: one
-// barrier per segment.  Maps are loaded into registers two segments ahead.
+// workgroup per (b, h) and block of 16 state rows, DK / 16 waves; wave w forms output
+// columns 16 w .. 16 w + 15 transposed, (S M + B)^T = M^T S^T + B^T, on fp32 MFMA (16x16x4:
+// exact fp32 products, so the scan adds no rounding beyond fp32 accumulation).  A k-step
+// pairs lane group g with key 16 c + 4 g + e (c = 0 .. DK/16 - 1, e = 0..3): the A operand is
+// then row 16 c + 4 g + e of M read along 16 consecutive columns, and the B operand
+// S[row][16 c + 4 g + e] is what wave c's accumulator held (lane (g, i) of a tile holds rows
+// i, columns 16 w + 4 g + 0..3), exchanged through a double-buffered LDS copy of the 16 rows:
+// one barrier per segment.  Maps are loaded into registers ahead of use: two segments ahead
+// at d = 128; one at d = 256, whose 16 waves leave 128 registers per lane.
 constexpr int SCAN_ROWS = 16;
-constexpr int LDSS = DK + 4;  // fp32 row stride of the LDS state block
-__global__ __launch_bounds__(512) void scan_delta_kernel(const Args a) {
+template <int DK>
+__global__ __launch_bounds__(DK * 4) void scan_delta_kernel(const Args a) {
+  constexpr int DV = Geo<DK>::DV, LDSS = DK + 4;  // fp32 row stride of the LDS state block
+  constexpr int DEPTH = DK == 128 ? 2 : 1;         // segments of maps held in registers
+  constexpr int TPR = DK / 4;                      // threads per row of the start state
   __shared__ __attribute__((aligned(16))) float sS[2][SCAN_ROWS * LDSS];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int i16 = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * SCAN_ROWS;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int nseg = a.nseg;
-  {  // S_0: 16 rows x 128 columns, 16 bytes per thread
-    const int r = tid >> 5, c4 = 4 * (tid & 31);
+  {  // S_0: 16 rows x DK columns, 16 bytes per thread
+    const int r = tid / TPR, c4 = 4 * (tid % TPR);
     const f32x4 x = a.S0 ? ld4(a.S0 + (bh * DV + row0 + r) * DK + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4 *>(sS[0] + r * LDSS + c4) = x;
     *reinterpret_cast<f32x4 *>(a.starts + ((bh * nseg) * DV + row0 + r) * DK + c4) = x;
   }
   const int col = 16 * wave + i16;  // output column of this lane's A-operand row
-  // segment i's map in registers, two segments ahead: M[16 c + 4 g + e][col] at 4 c + e,
-  // and B[row0 + i16][16 wave + 4 g + 0..3]
-  float mA[2][32];
-  f32x4 bC[2];
+  // segment i's map in registers: M[16 c + 4 g + e][col] at 4 c + e, and
+  // B[row0 + i16][16 wave + 4 g + 0..3]
+  float mA[DEPTH][DK / 4];
+  f32x4 bC[DEPTH];
   auto load = [&](int i, float *m, f32x4 &b) {
-    const float *Mb = a.maps + (bh * nseg + i) * (size_t)(2 * DV * DK);
+    const float *Mb = a.maps + (bh * nseg + i) * (size_t)((DV + DK) * DK);
+    if constexpr (DK == 128) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < DK / 16; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m[4 * c + e] = Mb[(size_t)(DV + 16 * c + 4 * g + e) * DK + col];
+        for (int e = 0; e < 4; ++e) m[4 * c + e] = Mb[(size_t)(DV + 16 * c + 4 * g + e) * DK + col];
+    } else {  // buffer loads: one lane offset plus constant offsets (no per-load addresses)
+      const rsrc_t r = make_rsrc(Mb, (uint32_t)((DV + DK) * DK * 4));
+      const uint32_t lo = 4u * (uint32_t)((DV + 4 * g) * DK + col);
+#pragma unroll
+      for (int c = 0; c < DK / 16; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          m[4 * c + e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)lo, 4 * (16 * c + e) * DK, 0));
+    }
     b = ld4(Mb + (size_t)(row0 + i16) * DK + 16 * wave + 4 * g);
   };
   auto step = [&](int i, float *m, f32x4 &b) {
@@ -739,7 +797,7 @@ __global__ __launch_bounds__(512) void scan_delta_kernel(const Args a) {
     float *nxt = sS[(i + 1) & 1];
     f32x4 acc0 = b, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < DK / 16; ++c) {
       const f32x4 sv = ld4(cur + i16 * LDSS + 16 * c + 4 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -747,7 +805,10 @@ __global__ __launch_bounds__(512) void scan_delta_kernel(const Args a) {
         else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[4 * c + e], sv[e], acc0, 0, 0, 0);
       }
     }
-    load(i + 2 < nseg - 1 ? i + 2 : nseg - 2, m, b);  // unconditional, so the waits stay exact
+    // unconditional, so the waits stay exact; at depth 1 only after this step's products
+    // (one set of map registers)
+    if constexpr (DEPTH == 1) LA_FENCE();
+    load(i + DEPTH < nseg - 1 ? i + DEPTH : nseg - 2, m, b);
     const f32x4 nx = acc0 + acc1;
     *reinterpret_cast<f32x4 *>(nxt + i16 * LDSS + 16 * wave + 4 * g) = nx;
     *reinterpret_cast<f32x4 *>(a.starts + ((bh * nseg + i + 1) * DV + row0 + i16) * DK + 16 * wave + 4 * g) = nx;
@@ -755,20 +816,28 @@ __global__ __launch_bounds__(512) void scan_delta_kernel(const Args a) {
   };
   __syncthreads();
   if (nseg < 2) return;
-  load(0, mA[0], bC[0]);
-  load(nseg > 2 ? 1 : 0, mA[1], bC[1]);
-  int i = 0;
-  for (; i + 2 < nseg; i += 2) {  // segments i and i + 1 both have a successor
-    step(i, mA[0], bC[0]);
-    step(i + 1, mA[1], bC[1]);
+  if constexpr (DEPTH == 2) {
+    load(0, mA[0], bC[0]);
+    load(nseg > 2 ? 1 : 0, mA[1], bC[1]);
+    int i = 0;
+    for (; i + 2 < nseg; i += 2) {  // segments i and i + 1 both have a successor
+      step(i, mA[0], bC[0]);
+      step(i + 1, mA[1], bC[1]);
+    }
+    if (i + 1 < nseg) step(i, mA[0], bC[0]);
+  } else {
+    load(0, mA[0], bC[0]);
+    for (int i = 0; i + 1 < nseg; ++i) step(i, mA[0], bC[0]);
   }
-  if (i + 1 < nseg) step(i, mA[0], bC[0]);
 }
 
 // Pass 2 (scalar gates): S_{i+1} = 2^{gsum_i} S_i + B_i for i = 0 .. nseg - 2, elementwise;
-// each thread carries 4 consecutive elements of one state row.
+// each thread carries 4 consecutive elements of one state row (256 threads: 256 / (DK / 4)
+// rows per workgroup).
+template <int DK>
 __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
-  const int row = blockIdx.x * 8 + (threadIdx.x >> 5), c4 = 4 * (threadIdx.x & 31);
+  constexpr int DV = Geo<DK>::DV, TPR = DK / 4;
+  const int row = blockIdx.x * (256 / TPR) + (int)threadIdx.x / TPR, c4 = 4 * ((int)threadIdx.x % TPR);
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int nseg = a.nseg;
   f32x4 cur = a.S0 ? ld4(a.S0 + (bh * DV + row) * DK + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -794,34 +863,40 @@ __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
 // chunk (start: K, V, TB landed, previous chunk done; Q landed; A tiles written); they
 // order LDS only, so the output stores of a chunk stay in flight across them.
 // ---------------------------------------------------------------------------------------
-template <bool DELTA>
-__global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
-  __shared__ __attribute__((aligned(16))) bf16_t sR0[C * LDK], sR1[C * LDK], sV[C * LDK];
+template <bool DELTA, int DK>
+__global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args a) {
+  constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NCT = Geo<DK>::NCT, RPW = 16 * NCT, LDK = DK + 16;
+  constexpr int NRB = DV / WROWS;      // row blocks (workgroups) per segment
+  constexpr int NIT = 4 * (DK / 32);   // (token tile, key step) pairs of a K S^T / Q S^T product
+  __shared__ __attribute__((aligned(16))) bf16_t sR0[C * LDK], sR1[C * LDK], sV[C * LDV];
   __shared__ __attribute__((aligned(16))) bf16_t sT[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];
   __shared__ __attribute__((aligned(16))) float sGw[NW][4 * C];
   __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][C];  // raw alpha, beta of a chunk
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int seg = (int)blockIdx.x;
+  int seg, rblk;
+  split_block<NRB>((int)blockIdx.x, seg, rblk);
+  if (NRB > 1 && seg >= a.nseg) return;  // (whole workgroup) past the last segment
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
-  const int row0 = wave * RPW;  // first state row owned by this wave
+  const int vcol0 = rblk * WROWS;       // first value row (V / O column) of this workgroup
+  const int row0 = vcol0 + wave * RPW;  // first state row owned by this wave
   const bool additive = a.variant == V_ADDITIVE;
   const bool use_beta = a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta);
   // per wave: g_t (log2), gamma_t = 2^{g_t}, 2^{g_C - g_t}, beta_t
   float *gw = sGw[wave];
 
   // ---- state: lane holds S^T[d = sd(m, g) + e][row0 + srow(c, l16)] in st[m][c][e]
-  f32x4 st[DK / 16][2];
+  f32x4 st[DK / 16][NCT];
   {
     const int l16 = lane & 15, g = lane >> 4;
     const float *src = a.nseg > 1 ? a.starts + (bh * a.nseg + seg) * DV * DK : (a.S0 ? a.S0 + bh * DV * DK : nullptr);
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        st[m][c] = src ? ld4(src + (size_t)(row0 + srow(c, l16)) * DK + sd(m, g)) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NCT; ++c)
+        st[m][c] = src ? ld4(src + (size_t)(row0 + srow<NCT>(c, l16)) * DK + sd(m, g)) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // the two above-diagonal A tiles that the A U products read, (0,1) and (2,3): zero for good
   if (tid < 128) {
@@ -838,7 +913,8 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<DV * 2, LDK * 2, C, NW, false>(rsrc_words(a.v + rb * DV, n * DV * 2), (unsigned char *)sV, wave, lane);
+    dma_tile<WROWS * 2, LDV * 2, C, NW, false, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
+                                                       (unsigned char *)sV, wave, lane);
     if (DELTA)
       dma_tb<NW, false>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
                  (unsigned char *)sT, wave, lane);
@@ -891,45 +967,45 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
 
     // ---- phase 1: U on this wave's rows, as operands with k = tokens (ufr), and with the
     // decay to the chunk end applied (dufr)
-    bf16x8 ufr[2][2], dufr[2][2];
+    bf16x8 ufr[NCT][2], dufr[NCT][2];
     {
-      f32x4 U[4][2];
+      f32x4 U[4][NCT];
       if (DELTA) {
         // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T (K fragments two steps ahead),
         // Y in registers (V read along tokens), then the lower-triangular product with TB
-        f32x4 ks[4][2];
+        f32x4 ks[4][NCT];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < NCT; ++c) ks[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #define LA_KF(it) *reinterpret_cast<const bf16x8 *>(sK + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
         {
-          bf16x8 kf[3], sfr[2];
+          bf16x8 kf[3], sfr[NCT];
           kf[0] = LA_KF(0);
           kf[1] = LA_KF(1);
 #pragma unroll
-          for (int it = 0; it < 16; ++it) {
+          for (int it = 0; it < NIT; ++it) {
             const int s = it / 4, mt = it % 4;
-            if (it + 2 < 16) kf[(it + 2) % 3] = LA_KF(it + 2);
+            if (it + 2 < NIT) kf[(it + 2) % 3] = LA_KF(it + 2);
             if (mt == 0) {
 #pragma unroll
-              for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+              for (int c = 0; c < NCT; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
             }
             LA_FENCE();
 #pragma unroll
-            for (int c = 0; c < 2; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
+            for (int c = 0; c < NCT; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
           }
         }
 #undef LA_KF
         LA_FENCE();
-        bf16x8 yfr[2][2];  // [c][s]
+        bf16x8 yfr[NCT][2];  // [c][s]
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const f32x4 ga = ld4(gw + 64 + 32 * s + 4 * g), gb = ld4(gw + 64 + 32 * s + 16 + 4 * g);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
+          for (int c = 0; c < NCT; ++c) {
             f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
-            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s, lane_v);
+            const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s, lane_v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               y0[e] += (float)vf[e];
@@ -950,10 +1026,10 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
           LA_FENCE();
           if (s == 0) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < NCT; ++c) U[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
 #pragma unroll
-          for (int c = 0; c < 2; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
+          for (int c = 0; c < NCT; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
         }
 #undef LA_TF
       } else {  // U = diag(beta) V, read along tokens from the V tile
@@ -961,8 +1037,8 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
         for (int s2 = 0; s2 < 2; ++s2) {
           const f32x4 b0 = ld4(gw + 192 + 32 * s2 + 4 * g), b1 = ld4(gw + 192 + 32 * s2 + 16 + 4 * g);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const bf16x8 vf = vrow_frag(sV, LDK, row0, c, s2, lane_v);
+          for (int c = 0; c < NCT; ++c) {
+            const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s2, lane_v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               U[2 * s2][c][e] = (float)vf[e] * b0[e];
@@ -976,7 +1052,7 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
       for (int s2 = 0; s2 < 2; ++s2) {
         const f32x4 d0 = ld4(gw + 128 + 32 * s2 + 4 * g), d1 = ld4(gw + 128 + 32 * s2 + 16 + 4 * g);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NCT; ++c) {
           ufr[c][s2] = pack_pair(U[2 * s2][c], U[2 * s2 + 1][c]);
           dufr[c][s2] = pack_pair(U[2 * s2][c] * d0, U[2 * s2 + 1][c] * d1);
         }
@@ -991,7 +1067,7 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     // t = 16 ti + l16 and keys j = 16 tj + 4 g + 0..3, stored in row t at the positions of
     // the MFMA k order (j = 32 s + 16 h + 4 q + e at 32 s + 8 q + 4 h + e), one 8-byte write
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
+    for (int m = 0; m < (10 + NW - 1) / NW; ++m) {
       const int job = wave + NW * m;
       if (job < 10) {
         int ti, tj;
@@ -1015,27 +1091,27 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
     }
     // O^T = S Q^T on this wave's rows: lane (g, l16) of tile (mt, c) holds
     // O[16 mt + l16][row0 + 8 g + 4 c + e] (Q fragments two steps ahead)
-    f32x4 O[4][2];
+    f32x4 O[4][NCT];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) O[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < NCT; ++c) O[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
 #define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
-      bf16x8 qb[3], sfr[2];
+      bf16x8 qb[3], sfr[NCT];
       qb[0] = LA_QF(0);
       qb[1] = LA_QF(1);
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {
+      for (int it = 0; it < NIT; ++it) {
         const int s = it / 4, mt = it % 4;
-        if (it + 2 < 16) qb[(it + 2) % 3] = LA_QF(it + 2);
+        if (it + 2 < NIT) qb[(it + 2) % 3] = LA_QF(it + 2);
         if (mt == 0) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
+          for (int c = 0; c < NCT; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
         }
         LA_FENCE();
 #pragma unroll
-        for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(sfr[c], qb[it % 3], O[mt][c]);
+        for (int c = 0; c < NCT; ++c) O[mt][c] = mfma_bf16(sfr[c], qb[it % 3], O[mt][c]);
       }
 #undef LA_QF
     }
@@ -1057,14 +1133,20 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
         if (s2 == 0) {
           const float gam = gw[64 + 16 * mt + l16];
 #pragma unroll
-          for (int c = 0; c < 2; ++c) O[mt][c] = O[mt][c] * gam;
+          for (int c = 0; c < NCT; ++c) O[mt][c] = O[mt][c] * gam;
         }
         LA_FENCE();
 #pragma unroll
-        for (int c = 0; c < 2; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], ab[it & 1], O[mt][c]);
-        if (mt < 2 || s2 == 1)  // token 16 mt + l16, outputs row0 + 8 g .. +7
-          bst16(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 8 * g),
-                __builtin_bit_cast(u32x4, pack_pair(O[mt][0], O[mt][1])));
+        for (int c = 0; c < NCT; ++c) O[mt][c] = mfma_bf16(ufr[c][s2], ab[it & 1], O[mt][c]);
+        if (mt < 2 || s2 == 1) {  // token 16 mt + l16
+          if constexpr (NCT == 2)  // outputs row0 + 8 g .. +7
+            bst16(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 8 * g),
+                  __builtin_bit_cast(u32x4, pack_pair(O[mt][0], O[mt][1])));
+          else  // outputs row0 + 4 g .. +3
+            bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 4 * g),
+                 __builtin_bit_cast(u32x2, bf16x4{(__bf16)O[mt][0][0], (__bf16)O[mt][0][1], (__bf16)O[mt][0][2],
+                                                  (__bf16)O[mt][0][3]}));
+        }
       }
 #undef LA_AF
     }
@@ -1081,7 +1163,7 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
         }
         LA_FENCE();
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NCT; ++c) {
           f32x4 acc = st[m][c] * gC;
           acc = mfma_bf16(kb[m & 1][0], dufr[c][0], acc);
           acc = mfma_bf16(kb[m & 1][1], dufr[c][1], acc);
@@ -1106,8 +1188,8 @@ __global__ __launch_bounds__(NTHR, 2) void replay_kernel(const Args a) {
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int r = row0 + srow(c, l16);
+      for (int c = 0; c < NCT; ++c) {
+        const int r = row0 + srow<NCT>(c, l16);
         *reinterpret_cast<f32x4 *>(a.S_T + (bh * DV + r) * DK + sd(m, g)) = st[m][c];
       }
   }
@@ -1117,14 +1199,15 @@ struct Plan {
   int nseg, seg_chunks;
 };
 
-// Segments per (b, h): enough workgroups to give every CU about four, but only when the
+// Segments per (b, h): enough workgroups to give every CU about four (state workgroups are
+// row blocks of WROWS rows, so a (b, h) at d = 256 is two of them), but only when the
 // heads alone cannot fill the chip (a split costs one extra pass over the keys/values).
-Plan make_plan(int B, int H, int64_t T) {
+Plan make_plan(int B, int H, int64_t T, int dv) {
   const int64_t nch = (T + C - 1) / C;
-  const int64_t bhn = (int64_t)B * H;
+  const int64_t units = (int64_t)B * H * (dv / WROWS);
   int64_t nseg = 1;
-  if (bhn < 128) {
-    nseg = (1024 + bhn - 1) / bhn;
+  if (units < 128) {
+    nseg = (1024 + units - 1) / units;
     if (nseg > nch) nseg = nch;
     if (nseg < 1) nseg = 1;
   }
@@ -1139,8 +1222,8 @@ struct WsLayout {
 
 // Workspace: per-segment maps, log decays and start states (more than one segment), then
 // the per-chunk transforms (delta rule).  Every part starts on a 256-byte boundary.
-WsLayout ws_layout(bool delta, int B, int H, int64_t T) {
-  const Plan p = make_plan(B, H, T);
+WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d) {
+  const Plan p = make_plan(B, H, T, d);
   const size_t bh = (size_t)B * H;
   const size_t nch = (size_t)((T + C - 1) / C);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1149,11 +1232,11 @@ WsLayout ws_layout(bool delta, int B, int H, int64_t T) {
   if (p.nseg > 1) {
     const size_t bhs = bh * p.nseg;
     w.maps = off;
-    off += up(bhs * (delta ? 2 * DV : DV) * DK * 4);
+    off += up(bhs * (size_t)(delta ? 2 * d : d) * d * 4);
     w.gsum = off;
     off += up(bhs * 4);
     w.starts = off;
-    off += up(bhs * DV * DK * 4);
+    off += up(bhs * (size_t)d * d * 4);
   }
   if (delta) {
     w.tb = off;
@@ -1163,15 +1246,49 @@ WsLayout ws_layout(bool delta, int B, int H, int64_t T) {
   return w;
 }
 
+bool chunk_width(int d_k, int d_v) { return d_k == d_v && (d_k == 128 || d_k == 256); }
+
+// Grid width for NB workgroups per segment (split_block's layout).
+unsigned seg_grid(int nsegs, int NB) { return NB == 1 ? (unsigned)nsegs : (unsigned)(8 * NB * ((nsegs + 7) / 8)); }
+
+template <int DK>
+void launch_passes(const Args &a, bool delta, int pass_mask, hipStream_t s) {
+  constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NRB = DV / WROWS;
+  const int B = a.B, H = a.H;
+  if (delta && (pass_mask & PASS_TRANSFORM)) {
+    const int64_t chunks = (int64_t)B * H * a.nch;
+    hipLaunchKernelGGL((tprep_kernel<DK>), dim3((unsigned)((chunks + TPW - 1) / TPW)), dim3(TPW * 64), 0, s, a);
+  }
+  if (a.nseg > 1 && (pass_mask & PASS_MAPS)) {
+    // every segment but the last (whose end state only the replay needs)
+    if (delta) {
+      constexpr int NWT = map_waves<true, DK>(), NMB = (DV + DK) / (NWT * 16 * Geo<DK>::NCT);
+      hipLaunchKernelGGL((map_kernel<true, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3((NWT + 1) * 64), 0, s, a);
+    } else {
+      constexpr int NWT = map_waves<false, DK>(), NMB = DV / (NWT * 16 * Geo<DK>::NCT);
+      hipLaunchKernelGGL((map_kernel<false, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3((NWT + 1) * 64), 0, s, a);
+    }
+  }
+  if (a.nseg > 1 && (pass_mask & PASS_SCAN)) {
+    if (delta) hipLaunchKernelGGL((scan_delta_kernel<DK>), dim3(DV / SCAN_ROWS, H, B), dim3(DK * 4), 0, s, a);
+    else hipLaunchKernelGGL((scan_gated_kernel<DK>), dim3(DV / (256 / (DK / 4)), H, B), dim3(256), 0, s, a);
+  }
+  if (pass_mask & PASS_REPLAY) {
+    const dim3 grid(seg_grid(a.nseg, NRB), H, B);
+    if (delta) hipLaunchKernelGGL((replay_kernel<true, DK>), grid, dim3(NW * 64), 0, s, a);
+    else hipLaunchKernelGGL((replay_kernel<false, DK>), grid, dim3(NW * 64), 0, s, a);
+  }
+}
+
 }  // namespace gdn
 
 size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v) {
-  if (d_k != gdn::DK || d_v != gdn::DV) return 0;
-  return gdn::ws_layout(variant == V_GATED_DELTA, B, H, T).total;
+  if (!gdn::chunk_width(d_k, d_v)) return 0;
+  return gdn::ws_layout(variant == V_GATED_DELTA, B, H, T, d_k).total;
 }
 
-void chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks) {
-  const gdn::Plan p = gdn::make_plan(B, H, T);
+void chunk_segments(int B, int H, int64_t T, int d, int *nseg, int *seg_chunks) {
+  const gdn::Plan p = gdn::make_plan(B, H, T, d);
   *nseg = p.nseg;
   *seg_chunks = p.seg_chunks;
 }
@@ -1181,13 +1298,13 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
                                 const void *beta, const float *S0, void *o, float *S_T,
                                 void *workspace, int pass_mask, hipStream_t s) {
   using namespace gdn;
-  if (d_k != DK || d_v != DV) {  // other widths: the token-recurrent kernel (fp32 arithmetic)
+  if (!chunk_width(d_k, d_v)) {  // other widths: the token-recurrent kernel (fp32 arithmetic)
     if (!(pass_mask & PASS_REPLAY)) return hipSuccess;
     return launch_recurrent_rows(variant, T_BF16, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
   }
   const bool delta = variant == V_GATED_DELTA;
-  const Plan p = make_plan(B, H, T);
-  const WsLayout w = ws_layout(delta, B, H, T);
+  const Plan p = make_plan(B, H, T, d_k);
+  const WsLayout w = ws_layout(delta, B, H, T, d_k);
   char *ws = (char *)workspace;
   Args a;
   a.q = (const bf16_t *)q;
@@ -1210,25 +1327,8 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   a.seg_chunks = p.seg_chunks;
   a.variant = variant;
   a.has_beta = beta != nullptr;
-  const dim3 grid(p.nseg, H, B);
-  if (delta && (pass_mask & PASS_TRANSFORM)) {
-    const int64_t chunks = (int64_t)B * H * a.nch;
-    hipLaunchKernelGGL(tprep_kernel, dim3((unsigned)((chunks + NW - 1) / NW)), dim3(NTHR), 0, s, a);
-  }
-  if (p.nseg > 1 && (pass_mask & PASS_MAPS)) {
-    // every segment but the last (whose end state only the replay needs)
-    const dim3 mgrid(p.nseg - 1, H, B);
-    if (delta) hipLaunchKernelGGL((map_kernel<true>), mgrid, dim3((8 + 1) * 64), 0, s, a);
-    else hipLaunchKernelGGL((map_kernel<false>), mgrid, dim3((NW + 1) * 64), 0, s, a);
-  }
-  if (p.nseg > 1 && (pass_mask & PASS_SCAN)) {
-    if (delta) hipLaunchKernelGGL(scan_delta_kernel, dim3(DV / SCAN_ROWS, H, B), dim3(512), 0, s, a);
-    else hipLaunchKernelGGL(scan_gated_kernel, dim3(DV / 8, H, B), dim3(256), 0, s, a);
-  }
-  if (pass_mask & PASS_REPLAY) {
-    if (delta) hipLaunchKernelGGL((replay_kernel<true>), grid, dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((replay_kernel<false>), grid, dim3(NTHR), 0, s, a);
-  }
+  if (d_k == 128) launch_passes<128>(a, delta, pass_mask, s);
+  else launch_passes<256>(a, delta, pass_mask, s);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ int check_prefill_shape(int variant, int dtype, int B, int H, int64_t T, int dk,
     return LA_OK;
   }
   if (dtype == LA_BF16) {
-    if (!((dk == 128 && dv == 128) || (dk == 64 && dv == 64))) return LA_ERR_UNSUPPORTED;
+    if (!(dk == dv && (dk == 64 || dk == 128 || dk == 256))) return LA_ERR_UNSUPPORTED;
   } else {
     if (dk != 64 && dk != 128 && dk != 256) return LA_ERR_UNSUPPORTED;
   }
@@ -209,8 +209,8 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
   if (dtype != LA_BF16 || seq_len == 0) return LA_OK;
   if (is_based(variant))
     based_chunk_segments(batch, heads, seq_len, n_segments, chunks_per_segment);
-  else if (d_k == 128 && d_v == 128)
-    chunk_segments(batch, heads, seq_len, n_segments, chunks_per_segment);
+  else if (d_k == d_v && (d_k == 128 || d_k == 256))
+    chunk_segments(batch, heads, seq_len, d_k, n_segments, chunks_per_segment);
   return LA_OK;
 }
 

@@ -37,7 +37,7 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
                                 const void *q, const void *k, const void *v, const void *alpha,
                                 const void *beta, const float *S0, void *o, float *S_T,
                                 void *workspace, int pass_mask, hipStream_t s);
-void chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks);
+void chunk_segments(int B, int H, int64_t T, int d, int *nseg, int *seg_chunks);
 
 // based_chunk.hip (chunkwise bf16 BASED prefill)
 size_t based_chunk_workspace_bytes(int B, int H, int64_t T);
