@@ -74,6 +74,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-based", action="store_true")
     ap.add_argument("--no-notebank", action="store_true")
+    ap.add_argument("--no-d256", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB copy (la_prefill with T = 0) so that HBM "
                          "byte counters can be scaled against a known size")
@@ -210,6 +211,11 @@ def main():
     if not args.no_decode:
         decode = bench_decode(torch, la, synth, dev, stream, args.decode_steps)
 
+    # ---------------------------------------------------------------- d = 256 gated delta
+    gdn256 = None
+    if not args.no_d256:
+        gdn256 = bench_gdn256(torch, la, synth, dev, stream, args.steps, args.warmup, args.seq_len)
+
     # ---------------------------------------------------------------- BASED prefill
     based = None
     if not args.no_based:
@@ -237,11 +243,91 @@ def main():
         "roofline": roofline,
         "prefill": prefill_detail,
         "decode": decode,
+        "gdn_d256": gdn256,
         "based_prefill": based,
         "notebank": notebank,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_gdn256(torch, la, synth, dev, stream, steps, warmup, T):
+    """The gated-delta shape of the NoteBank paper's own backbone: 8 heads of width 256
+    (d_k = d_v = 256, fp32 state 256 x 256 per head), bf16 inputs with the gated-delta
+    recipe, T tokens (1M by default): the four passes timed with HIP events on the launch
+    stream; then the decode step on 256 sequences x 8 heads of that width."""
+    B, H, D = 1, 8, 256
+    inp = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=6, device=dev)
+    q, k, v, a, b = inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"]
+    o = torch.empty((B, H, T, D), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(la.workspace_size("gated_delta", la.BF16, B, H, T, D, D), 16), dtype=torch.uint8,
+                     device=dev)
+    nseg, sc = la.segments("gated_delta", la.BF16, B, H, T, D, D)
+    passes = [la.PASS_TRANSFORM, la.PASS_MAPS, la.PASS_SCAN, la.PASS_REPLAY] if nseg > 1 \
+        else [la.PASS_TRANSFORM, la.PASS_REPLAY]
+    names = {la.PASS_TRANSFORM: "transform", la.PASS_MAPS: "maps", la.PASS_SCAN: "scan",
+             la.PASS_REPLAY: "replay"}
+
+    def run(evs=None):
+        for i, p in enumerate(passes):
+            la.prefill("gated_delta", q, k, v, a, b, o=o, S_T=S_T, workspace=ws, pass_=p, stream=stream)
+            if evs is not None:
+                evs[i + 1].record(stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    per_pass = {names[p]: 0.0 for p in passes}
+    total = 0.0
+    for _ in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(passes) + 1)]
+        evs[0].record(stream)
+        run(evs)
+        torch.cuda.synchronize()
+        total += evs[0].elapsed_time(evs[-1]) / steps
+        for i, p in enumerate(passes):
+            per_pass[names[p]] += evs[i].elapsed_time(evs[i + 1]) / steps
+    # algorithmic work per token-head at d = 256, chunk 64 (as for d = 128): q, k, v, o and
+    # the two gates; chunk-form FLOPs 5 x 2 C^2 d + 3 x 2 C d^2 + C^3 / 3 per chunk
+    th = B * H * T
+    byt = th * (4 * D * 2 + 2 * 2)
+    flo = th * (5 * 2 * C_ * C_ * D + 3 * 2 * C_ * D * D + C_ ** 3 / 3) / C_
+    t_roof = max(byt / (HBM_PEAK_GBS * 1e9), flo / (BF16_PEAK_TFLOPS * 1e12))
+    # the replay reads q, k, v, the gates and the stored transform (96 B per token) and writes o
+    rep_b = th * (4 * D * 2 + 2 * 2 + 96)
+    res = {"workload": f"gated-delta chunkwise prefill, B={B} H={H} T={T} d_k=d_v={D}, bf16 inputs, "
+                       "fp32 state, chunk 64",
+           "ms": round(total, 4), "tokens_per_s": round(B * T / (total * 1e-3), 1),
+           "ms_per_pass": {kk: round(vv, 4) for kk, vv in per_pass.items()},
+           "segments": nseg, "chunks_per_segment": sc, "alg_bytes": byt, "alg_flops": flo,
+           "roofline_time_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof * 1e3 / total, 4),
+           "bf16_mfma_frac": round(flo / (total * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "replay_hbm_frac": round(rep_b / (per_pass["replay"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del inp, q, k, v, a, b, o, ws
+    torch.cuda.empty_cache()
+
+    N, nsteps = 256 * 8, 256
+    S = synth.gdn_state((N, D, D), seed=7, device=dev)
+    g = synth.gdn_decode_inputs(nsteps, N, D, D, dtype=torch.bfloat16, seed=7, device=dev)
+    od = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    step = lambda t: la.decode_step("gated_delta", S, g["q"][t], g["k"][t], g["v"][t], g["alpha"][t],
+                                    g["beta"][t], S_out=S, o=od, stream=stream)
+    for t in range(8):
+        step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(nsteps):
+        step(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / nsteps
+    bd = 2 * N * D * D * 4 + N * (3 * D + 2 + D) * 2
+    res["decode"] = {"states": N, "steps": nsteps, "us_per_step": round(ms * 1e3, 2),
+                     "steps_per_s": round(1e3 / ms, 1), "alg_bytes_per_step": bd,
+                     "hbm_frac": round(bd / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def bench_decode(torch, la, synth, dev, stream, steps):

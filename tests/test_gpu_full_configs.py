@@ -9,6 +9,8 @@ it computes sampled outputs exactly: value rows (gated family) and value columns
   cfg3  gated delta, B=1 H=16 T=1048576 d=128, bf16      -- 2 heads x 3 rows, whole T
   cfg4  decode, 256 x 16 states, 1024 steps, GDN + BASED -- o at every step and the
         final state, for 24 sampled states of each kind
+  gated delta at the NoteBank paper's own head shape, B=1 H=8 T=1048576 d=256, bf16
+        -- 2 heads x 4 rows (both row blocks), whole T
 """
 
 import numpy as np
@@ -32,11 +34,11 @@ def test_cfg0_additive_fp32(la):
     assert_close(S, So, 1e-4, what="cfg0 S_T")
 
 
-def _gdn_sampled(la, T, heads, rows, seed):
-    B, H, D = 1, 16, 128
+def _gdn_sampled(la, T, heads, rows, seed, H=16, D=128):
+    B = 1
     d = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=seed, device=DEV)
     nseg, sc = la.segments("gated_delta", la.BF16, B, H, T, D, D)
-    print(f"[gdn T={T}] segments={nseg} x {sc} chunks", flush=True)
+    print(f"[gdn T={T} H={H} d={D}] segments={nseg} x {sc} chunks", flush=True)
     o, S, _ = la.prefill("gated_delta", d["q"], d["k"], d["v"], d["alpha"], d["beta"])
     torch.cuda.synchronize()
     hs = list(heads)
@@ -53,6 +55,13 @@ def test_cfg2_gdn_64k_all_heads_sampled_rows(la):
 
 def test_cfg3_gdn_1m_sampled(la):
     _gdn_sampled(la, 1 << 20, [0, 15], [3, 64, 126], seed=3)
+
+
+def test_gdn_8x256_1m_sampled(la):
+    # the NoteBank paper's own GDN head shape (8 heads of width 256) at 1M tokens, in the
+    # launch configuration bench.py times (64 segments x 2 row blocks per head); sampled
+    # rows of both row blocks, whole sequence
+    _gdn_sampled(la, 1 << 20, [0, 7], [5, 127, 128, 250], seed=6, H=8, D=256)
 
 
 def test_cfg4_decode_1024_steps_sampled_states(la):
