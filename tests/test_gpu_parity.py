@@ -98,7 +98,7 @@ def test_prefill_empty_sequence_returns_start_state(la, variant):
 
 @pytest.mark.parametrize("variant", ROWS_VARIANTS)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 50), (256, 32)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 50), (256, 32), (256, 256), (256, 200)])
 def test_decode_steps(la, variant, dtype, dk, dv):
     N, steps = 37, 6
     print(f"[decode] {variant} N={N} dk={dk} dv={dv} {dtype}", flush=True)
