@@ -304,6 +304,16 @@ def bench_gdn256(torch, la, synth, dev, stream, steps, warmup, T):
            "roofline_time_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof * 1e3 / total, 4),
            "bf16_mfma_frac": round(flo / (total * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
            "replay_hbm_frac": round(rep_b / (per_pass["replay"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # the recurrence's share of the pages' 24-layer GDN at this length: 24 whole-layer
+    # prefills back to back (each layer reuses these inputs; projections, convolutions and
+    # the other layer parts are outside the recurrence)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(24):
+        la.prefill("gated_delta", q, k, v, a, b, o=o, S_T=S_T, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["stack_24_layers_ms"] = round(e0.elapsed_time(e1), 3)
     del inp, q, k, v, a, b, o, ws
     torch.cuda.empty_cache()
 

@@ -71,6 +71,8 @@ def load(path: str | None = None):
     lib.la_note_addresses.restype = i32
     lib.la_address_votes.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32] + [vp] * 6
     lib.la_address_votes.restype = i32
+    lib.la_state_scale.argtypes = [i64, f32, vp, vp, vp]
+    lib.la_state_scale.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -241,3 +243,18 @@ def address_votes(rho, u, R, positions, want_score=True, stream=None):
     if st != 0:
         raise LAError(st, "la_address_votes")
     return score, choice, votes, sel
+
+
+def state_scale(S, lam, out=None, stream=None):
+    """la_state_scale: out = lam * S for an fp32 state of any shape (lam in [0, 1]; lam = 0
+    writes zeros).  out=S rescales in place; out=None returns a new tensor (with lam = 1,
+    the copy a replay branch starts from)."""
+    if S.dtype != torch.float32:
+        raise TypeError("states are float32")
+    if out is None:
+        out = torch.empty_like(S)
+    st = load().la_state_scale(S.numel(), float(lam), _p(S), _p(out), _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_state_scale")
+    return out
+

@@ -98,8 +98,9 @@ const char *la_status_string(int status);
 /*
  * Workspace that la_prefill needs for this problem, in bytes (0 is possible).  The
  * workspace holds the chunked prefill's per-segment fp32 state maps and, for the gated
- * delta rule, one bf16 64 x 64 transform per chunk of 64 tokens (8 KiB per chunk and
- * head; see la_prefill_pass).
+ * delta rule, one bf16 lower-triangular 64 x 64 transform per chunk of 64 tokens (6 KiB
+ * per chunk and head: the zero blocks right of the diagonal in its first 32 rows are not
+ * stored; see la_prefill_pass).
  * Returns LA_OK and writes *bytes, or the same validation error la_prefill would give.
  */
 int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int64_t seq_len,
@@ -130,7 +131,8 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  * state).  fp32
  * inputs take an fp32 token-recurrent path (fp32 FMA throughout).
  *
- * Supported: bf16 -- ADDITIVE/GATED/GATED_DELTA with d_k = d_v = 128 or 64;
+ * Supported: bf16 -- ADDITIVE/GATED/GATED_DELTA with d_k = d_v in {64, 128, 256}
+ *                    (128 and 256 chunkwise; 64 token-recurrent in fp32);
  *                    BASED and BASED_COMPACT with d' = 16, d_v = 64.
  *            fp32 -- ADDITIVE/GATED/GATED_DELTA with d_k in {64, 128, 256} and any d_v;
  *                    BASED and BASED_COMPACT with d' = 16 and d_v = 64.
@@ -197,6 +199,21 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
 int la_decode_step(int variant, int dtype, int n, int d_k, int d_v, float eps, const float *S_in,
                    const float *z_in, float *S_out, float *z_out, const void *q, const void *k,
                    const void *v, const void *alpha, const void *beta, void *o, void *stream);
+
+/*
+ * la_state_scale -- S_out = lambda * S_in over n fp32 elements (any state: S, s or z).
+ * The state handling around a NoteBank replay ("History Replays Itself", App. B
+ * Algorithm 1 and App. C.3): the retrieval and read branches each work on their own copy
+ * of the retained state, and at the readout boundary the state is rescaled, S <- lambda S
+ * with lambda in [0, 1] (1 leaves it unchanged, 0 resets it; NoteBank uses 0 right before
+ * replay).  lambda = 1 with distinct buffers is the copy.  lambda = 0 writes zeros
+ * without reading S_in (which may then be NULL), so a reset also clears non-finite
+ * values.  Products are single fp32 multiplications (correctly rounded).
+ * S_out may equal S_in (in place); any other overlap returns LA_ERR_ALIAS.  Both must be
+ * 16-byte aligned.  n = 0 is a no-op; n < 0 or lambda outside [0, 1] returns
+ * LA_ERR_INVALID.  One read and one write of the state (bound by HBM bandwidth).
+ */
+int la_state_scale(int64_t n, float lambda, const float *S_in, float *S_out, void *stream);
 
 /*
  * ---------------------------------------------------------------------------------

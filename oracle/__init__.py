@@ -20,6 +20,9 @@ promotes inputs exactly to float64.  What is computed, with citations:
   table (Sec. 2.3), [1, x, x_a^2/sqrt 2 (a = b), x_a x_b (a < b)], pairs in row-major
   upper-triangle order (D = 1 + d' + d'(d'+1)/2 = 153 for d' = 16).
 
+* [NoteBank] App. B Algorithm 1 and App. C.3: the retained state is copied for each
+  branch and rescaled at the readout boundary, S <- lambda S, lambda in [0, 1]
+  (``state_scale``; lambda = 0 is read as the reset to the zero state).
 * [NoteBank] Sec. 3 Eqs. (3)-(5), App. B.2 Eq. (8), App. B.3 Eq. (9): the write step's key
   distinctiveness per write chunk (``write_scores``), the best scoring window of each
   complete chunk (``write_windows``), the per-channel note addresses (``note_addresses``)
@@ -293,3 +296,14 @@ def address_votes(rho, u, R, positions):
                                     _iptr(choice), _iptr(votes), _iptr(sel)) != 0:
         raise ValueError("oracle_address_votes rejected its arguments")
     return score, choice, votes, sel
+
+
+def state_scale(S, lam):
+    """S <- lambda S ([NoteBank] App. C.3: lambda in [0, 1], 1 leaves the state unchanged,
+    0 resets it).  fp64; lambda = 0 gives the zero state whatever S holds (the reset)."""
+    lam = float(lam)
+    if not 0.0 <= lam <= 1.0:
+        raise ValueError("lambda must lie in [0, 1]")
+    x = _f64(S)
+    return np.zeros_like(x) if lam == 0.0 else lam * x
+

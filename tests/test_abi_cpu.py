@@ -196,6 +196,19 @@ def test_decode_validation(lib):
     assert decode(lib, S_out=A + 1024) == -6          # partial overlap of the states
 
 
+def test_state_scale_validation(lib):
+    """la_state_scale validates before launching; n = 0 is a no-op (no device needed)."""
+    f = lambda n=1024, lam=0.5, src=A, dst=2 * A: lib.la_state_scale(
+        n, ctypes.c_float(lam), None if src is None else P(src), None if dst is None else P(dst), None)
+    assert f(n=-1) == -2
+    assert f(lam=1.5) == -2 and f(lam=-0.25) == -2 and f(lam=float("nan")) == -2
+    assert f(n=0) == 0
+    assert f(dst=None) == -1
+    assert f(src=None) == -1           # lambda != 0 reads S_in
+    assert f(src=A + 4) == -4 and f(dst=2 * A + 8) == -4
+    assert f(dst=A + 16) == -6         # partial overlap (n = 1024 floats = 4 KiB)
+
+
 def test_notebank_validation(lib):
     """The NoteBank entry points validate before launching (no device memory is touched)."""
     f = lambda x: None if x is None else P(x)

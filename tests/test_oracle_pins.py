@@ -452,3 +452,30 @@ def test_state_bytes_match_printed_accounting():
     assert S[0, 0].size * 4 * J == 48 * 2 ** 20
     _, s, z = oracle.prefill("based", *gdn_like(rng(20), 1, 1, 2, 16, 64)[:3])
     assert s[0, 0].size + z[0, 0].size == 273 * (64 + 1)
+
+
+def test_state_scale_pins():
+    """S <- lambda S at the readout boundary ([NoteBank] App. C.3): lambda = 1 leaves the state
+    unchanged and lambda = 0 resets it (the two values the pages fix), and rescaling the start
+    state of a recurrence with zero values rescales its end state by the same factor (the
+    decays act linearly on S, Eq. (1))."""
+    rng = np.random.default_rng(5)
+    S = rng.standard_normal((3, 4, 5))
+    assert np.array_equal(oracle.state_scale(S, 1.0), S)
+    Sbad = S.copy()
+    Sbad[0, 0, 0] = np.inf
+    assert np.array_equal(oracle.state_scale(Sbad, 0.0), np.zeros_like(S))
+    B, H, T, d = 1, 2, 37, 8
+    q, k = rng.standard_normal((B, H, T, d)), rng.standard_normal((B, H, T, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = np.zeros((B, H, T, d))
+    al = rng.uniform(0.5, 1.0, (B, H, T))
+    be = rng.uniform(0.0, 1.0, (B, H, T))
+    S0 = rng.standard_normal((B, H, d, d))
+    lam = 0.375
+    _, S1, _ = oracle.prefill("gated_delta", q, k, v, al, be, S0=oracle.state_scale(S0, lam))
+    _, S2, _ = oracle.prefill("gated_delta", q, k, v, al, be, S0=S0)
+    assert np.allclose(S1, lam * S2, rtol=1e-13, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.state_scale(S, 1.25)
+
