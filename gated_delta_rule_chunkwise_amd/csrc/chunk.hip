@@ -507,8 +507,11 @@ __device__ __forceinline__ float wave_gates(float al, float be, bool additive, f
 }
 
 // Map rows are [B_seg rows 0 .. d_v - 1; M_seg rows d_v .. d_v + d_k - 1] (delta rule) or
-// B_seg rows only; a workgroup carries NWT * RPW of them (d = 128: all 256 / all 128; d = 256:
-// 128 of 512 / 128 of 256) and loads the V columns of its B rows only.
+// B_seg rows only; a workgroup carries NWT * RPW of them and loads the V columns of its B
+// rows.  Delta rule: the first half of the state waves carry B rows vcol0 .., the second
+// half the M rows with the same indices (d = 128: all 128 of each in one workgroup; d = 256:
+// 64 of each in each of four), so the workgroups of a segment do equal work, keep pace and
+// share each K tile through L2.
 template <bool DELTA, int DK>
 __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kernel(const Args a) {
   constexpr int DV = Geo<DK>::DV, NCT = Geo<DK>::NCT, RPW = 16 * NCT, LDK = DK + 16;
@@ -516,9 +519,12 @@ __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kern
   constexpr int MAPROWS = DELTA ? DV + DK : DV;
   constexpr int MWR = NWT * RPW;        // map rows per workgroup
   constexpr int NMB = MAPROWS / MWR;    // workgroups per segment
+  constexpr int HALF = DELTA ? NWT / 2 : NWT;  // waves per row kind (B, then M)
+  constexpr int VW = HALF * RPW;        // value columns (B rows) of a workgroup
+  constexpr int LDVM = VW + 16;         // row stride of its V tile
   constexpr int NIT = 4 * (DK / 32);    // (token tile, key step) pairs of a K S^T product
-  static_assert(MAPROWS % MWR == 0 && (DV % MWR == 0 || MWR > DV), "map blocks of one kind");
-  __shared__ __attribute__((aligned(16))) bf16_t sK0[C * LDK], sK1[C * LDK], sV0[C * LDV], sV1[C * LDV];
+  static_assert(MAPROWS % MWR == 0 && NMB * VW == DV, "every B (and M) row in one workgroup");
+  __shared__ __attribute__((aligned(16))) bf16_t sK0[C * LDK], sK1[C * LDK], sV0[C * LDVM], sV1[C * LDVM];
   __shared__ __attribute__((aligned(16))) bf16_t sT0[DELTA ? C * LDT : 8], sT1[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) float sGw[NWT][3 * C];
   __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][2][C];  // per copy: raw alpha, beta
@@ -528,11 +534,9 @@ __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kern
   int seg, mb;
   split_block<NMB>((int)blockIdx.x, seg, mb);
   if (NMB > 1 && seg >= a.nseg - 1) return;  // (whole workgroup) past the last mapped segment
-  const int grow0 = mb * MWR + wave * RPW;  // first map row of this wave (unused by the loader)
-  const bool m_kind = DELTA && grow0 >= DV;  // transition (M) rows, started from the identity
-  const int row0 = m_kind ? grow0 - DV : grow0;
-  const int vcol0 = mb * MWR;                // first V column of the workgroup's tile
-  const bool has_v = vcol0 < DV;             // (workgroup-uniform) any B rows here
+  const bool m_kind = DELTA && wave >= HALF;  // transition (M) rows, started from the identity
+  const int vcol0 = mb * VW;                  // first B row / V column of the workgroup
+  const int row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;  // (unused by the loader)
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
   const bool additive = a.variant == V_ADDITIVE;
@@ -558,9 +562,8 @@ __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kern
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
     dma_tile<DK * 2, LDK * 2, C, 1, true>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, 0, lane);
-    if (has_v)
-      dma_tile<WROWS * 2, LDV * 2, C, 1, true, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
-                                                       (unsigned char *)dV, 0, lane);
+    dma_tile<VW * 2, LDVM * 2, C, 1, true, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
+                                                   (unsigned char *)dV, 0, lane);
     if (DELTA)
       dma_tb<1, true>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2), (unsigned char *)dT, 0,
                 lane);
@@ -637,7 +640,7 @@ __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kern
         for (int c = 0; c < NCT; ++c) {
           f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
           if (!m_kind) {
-            const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s, lane_v);
+            const bf16x8 vf = vrow_frag<NCT>(sV, LDVM, row0 - vcol0, c, s, lane_v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               y0[e] += (float)vf[e];
@@ -681,7 +684,7 @@ __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kern
         const f32x4 b0 = ld4(gw + 128 + 32 * s2 + 4 * g), b1 = ld4(gw + 128 + 32 * s2 + 16 + 4 * g);
 #pragma unroll
         for (int c = 0; c < NCT; ++c) {
-          const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s2, lane_v);
+          const bf16x8 vf = vrow_frag<NCT>(sV, LDVM, row0 - vcol0, c, s2, lane_v);
           f32x4 u0, u1;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
