@@ -303,7 +303,8 @@ def bench_gdn256(torch, la, synth, dev, stream, steps, warmup, T):
            "segments": nseg, "chunks_per_segment": sc, "alg_bytes": byt, "alg_flops": flo,
            "roofline_time_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof * 1e3 / total, 4),
            "bf16_mfma_frac": round(flo / (total * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-           "replay_hbm_frac": round(rep_b / (per_pass["replay"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+           "replay_hbm_frac": round(rep_b / (per_pass["replay"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "replay_traffic": read_traffic("d256_replay")}
     # the recurrence's share of the pages' 24-layer GDN at this length: 24 whole-layer
     # prefills back to back (each layer reuses these inputs; projections, convolutions and
     # the other layer parts are outside the recurrence)
