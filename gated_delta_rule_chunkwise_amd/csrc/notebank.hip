@@ -19,8 +19,8 @@
 //                         notes first on equal votes) and their document order.
 //
 // All of it is bandwidth- or latency-light next to the recurrence: the write scores read
-// each key once from HBM (the second pass over a chunk hits in L2), the rest touch
-// kilobytes.  Every reduction has a fixed order, so results are bitwise reproducible.
+// each bf16 key once from HBM (a chunk of up to 512 tokens is held in registers), the rest
+// touch kilobytes.  Every reduction has a fixed order, so results are bitwise reproducible.
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -137,6 +137,100 @@ __global__ __launch_bounds__(WS_THREADS) void write_scores_kernel(int64_t T_len,
       const int t = t0 + u * TPS;
       if (sub == 0 && t < n) dh[t] = 1.0f - (ss > 0.0f ? dot / sqrtf(ss) : 0.0f);
     }
+  }
+}
+
+// bf16 keys and write chunks of at most 512 tokens: one 1024-thread workgroup holds the whole
+// chunk in registers (a lane keeps 16 bytes of a key per token step: 32 registers at d_k = 128,
+// 64 at 256), so each key is read from HBM once and both the unit-key sum and the scores are
+// formed from the registers.  (The two-pass kernel above re-reads the chunk, and with many
+// chunks in flight per XCD that second read mostly misses L2.)  Same arithmetic, same
+// fixed reduction order within a workgroup.
+constexpr int WR_THREADS = 1024, WR_MAXC = 512;
+// (d_k <= 128: two workgroups per CU, so one streams its chunk in while the other reduces)
+template <int DK>
+__global__ __launch_bounds__(WR_THREADS, DK <= 128 ? 8 : 4) void write_scores_reg_kernel(int64_t T_len, int C,
+                                                                      const bf16_t *__restrict__ k,
+                                                                      float *__restrict__ d_head) {
+  constexpr int LPT = DK / 8, TPS = WR_THREADS / LPT, NS = WR_MAXC / TPS, NW = WR_THREADS / 64;
+  __shared__ float s_mu[NW][DK];
+  __shared__ float s_mubar[DK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % LPT, tok = tid / LPT;  // token of this lane within a step
+  const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * C;
+  const int n = (int)((T_len - c0) < C ? (T_len - c0) : C);
+  // buffer loads: tokens past the chunk's end read zeros
+  const rsrc_t rk = make_rsrc(k + (bh * T_len + c0) * DK, (uint32_t)n * DK * 2);
+
+  u32x4 raw[NS];  // every load issued before any is used
+#pragma unroll
+  for (int s = 0; s < NS; ++s) raw[s] = bld16(rk, 2u * (uint32_t)((s * TPS + tok) * DK + 8 * sub));
+  auto unpack = [](u32x4 w, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  };
+  // sum of the unit keys (the 1/|chunk| of the mean cancels in the normalisation)
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float x[8];
+    unpack(raw[s], x);
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+    ss = group_sum<LPT>(ss);
+    const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += x[j] * inv;
+  }
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += __shfl_xor(acc[j], off, 64);
+  if (lane < LPT)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_mu[wave][8 * sub + j] = acc[j];
+  __syncthreads();
+  if (tid < DK) {
+    float m = s_mu[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m += s_mu[w][tid];
+    s_mubar[tid] = m;
+  }
+  __syncthreads();
+  if (wave == 0) {  // |mu|, then mubar = mu / |mu| (zero stays zero)
+    float ss = 0.0f;
+    for (int i = lane; i < DK; i += 64) ss += s_mubar[i] * s_mubar[i];
+    ss = group_sum<64>(ss);
+    const float inv = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;
+    for (int i = lane; i < DK; i += 64) s_mubar[i] *= inv;
+  }
+  __syncthreads();
+  float mb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mb[j] = s_mubar[8 * sub + j];
+  // keep the packed words (not both passes' unpacked floats) live across the reduction
+#pragma unroll
+  for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(raw[s]));
+  float *dh = d_head + bh * T_len + c0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float x[8];
+    unpack(raw[s], x);
+    float ss = 0.0f, dot = 0.0f;  // the norm again, from the registers
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ss += x[j] * x[j];
+      dot += x[j] * mb[j];
+    }
+    ss = group_sum<LPT>(ss);
+    dot = group_sum<LPT>(dot);
+    const int t = s * TPS + tok;
+    if (sub == 0 && t < n) dh[t] = 1.0f - (ss > 0.0f ? dot / sqrtf(ss) : 0.0f);
   }
 }
 
@@ -390,7 +484,10 @@ __global__ __launch_bounds__(1024) void select_notes_kernel(int N, int J, int R,
 template <int DK, typename T>
 static void go_scores(int B, int H, int64_t T_len, int C, const void *k, float *d_head, hipStream_t s) {
   const dim3 grid((unsigned)((T_len + C - 1) / C), H, B);
-  hipLaunchKernelGGL((write_scores_kernel<DK, T>), grid, dim3(WS_THREADS), 0, s, T_len, C, (const T *)k, d_head);
+  if (sizeof(T) == 2 && C <= WR_MAXC)
+    hipLaunchKernelGGL((write_scores_reg_kernel<DK>), grid, dim3(WR_THREADS), 0, s, T_len, C, (const bf16_t *)k, d_head);
+  else
+    hipLaunchKernelGGL((write_scores_kernel<DK, T>), grid, dim3(WS_THREADS), 0, s, T_len, C, (const T *)k, d_head);
 }
 
 }  // namespace nb
