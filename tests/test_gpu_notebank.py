@@ -45,6 +45,18 @@ def test_write_scores(la, dtype, dk):
     assert_abs(dm, odm, 1e-5, "d_mean")
 
 
+@pytest.mark.parametrize("C", [511, 777])
+def test_write_scores_bf16_chunk_lengths(la, C):
+    # bf16 keys: chunks of at most 512 tokens are scored from registers, longer ones by the
+    # two-pass kernel; both against the oracle, with a partial last chunk
+    k, _ = _keys(1, 2, 3 * C + 100, 128, torch.bfloat16, seed=C)
+    dh, dm = la.write_scores(k, chunk=C)
+    torch.cuda.synchronize()
+    odh, odm = oracle.write_scores(k, chunk=C)
+    assert_abs(dh, odh, 1e-5, f"d_head, chunk {C}")
+    assert_abs(dm, odm, 1e-5, f"d_mean, chunk {C}")
+
+
 def test_write_scores_edge_cases(la):
     # one partial chunk; a zero key (scores 1); identical keys (score 0); chunk of 1 token
     k = torch.zeros((1, 2, 37, 128), dtype=torch.bfloat16, device=DEV)
