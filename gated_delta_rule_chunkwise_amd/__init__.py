@@ -253,6 +253,8 @@ def state_scale(S, lam, out=None, stream=None):
         raise TypeError("states are float32")
     if out is None:
         out = torch.empty_like(S)
+    elif out.dtype != torch.float32 or out.numel() != S.numel():
+        raise ValueError("out must be a float32 tensor with as many elements as S")
     st = load().la_state_scale(S.numel(), float(lam), _p(S), _p(out), _stream(stream))
     if st != 0:
         raise LAError(st, "la_state_scale")
