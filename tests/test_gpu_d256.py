@@ -64,6 +64,14 @@ def test_d256_with_start_state(la, variant):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
+def test_d256_batched_segments(la, variant):
+    # B = 3 x H = 2: several segments per (b, h), start states, a ragged tail
+    S0 = synth.gdn_state((3, 2, D, D), seed=93, device=DEV) * 0.2
+    nseg, _ = _check(la, variant, 3, 2, 64 * 11 + 33, seed=94, S0=S0, rows=[0, 64, 127, 128, 191, 255])
+    assert nseg > 1
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("T", [1, 63, 64, 65])
 def test_d256_short_sequences(la, variant, T):
     _check(la, variant, 1, 2, T, seed=90 + T)

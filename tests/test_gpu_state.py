@@ -55,3 +55,14 @@ def test_branch_copy_leaves_retained_state(la):
     torch.cuda.synchronize()
     assert torch.equal(S, keep)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_state_scale_reset_without_input_through_abi(la):
+    """lambda = 0 with a NULL S_in through the C ABI: the reset reads nothing and writes zeros."""
+    import ctypes
+    S = torch.full((1000,), 7.0, device=DEV)
+    st = la.load().la_state_scale(S.numel(), ctypes.c_float(0.0), None, ctypes.c_void_p(S.data_ptr()),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0 and torch.count_nonzero(S) == 0
+
