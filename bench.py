@@ -75,6 +75,7 @@ def main():
     ap.add_argument("--no-based", action="store_true")
     ap.add_argument("--no-notebank", action="store_true")
     ap.add_argument("--no-d256", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB copy (la_prefill with T = 0) so that HBM "
                          "byte counters can be scaled against a known size")
@@ -216,6 +217,11 @@ def main():
     if not args.no_d256:
         gdn256 = bench_gdn256(torch, la, synth, dev, stream, args.steps, args.warmup, args.seq_len)
 
+    # ---------------------------------------------------------------- the two smaller configs
+    small = None
+    if not args.no_small:
+        small = bench_small_configs(torch, la, synth, dev, stream)
+
     # ---------------------------------------------------------------- BASED prefill
     based = None
     if not args.no_based:
@@ -244,11 +250,52 @@ def main():
         "prefill": prefill_detail,
         "decode": decode,
         "gdn_d256": gdn256,
+        "small_configs": small,
         "based_prefill": based,
         "notebank": notebank,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_small_configs(torch, la, synth, dev, stream):
+    """The two smaller configurations: additive linear attention in fp32 (B=1, H=1, T=1024,
+    d=64: one head, so launch latency bounds it) and the gated-delta prefill at 64K tokens
+    (B=1, H=16, T=65536, d=128, bf16), each as la_prefill calls timed with HIP events."""
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    res = {}
+    d0 = synth.additive_inputs(1, 1, 1024, 64, dtype=torch.float32, seed=0, device=dev)
+    o0 = torch.empty_like(d0["v"])
+    S0 = torch.empty((1, 1, 64, 64), dtype=torch.float32, device=dev)
+    ms0 = timed(lambda: la.prefill("additive", d0["q"], d0["k"], d0["v"], o=o0, S_T=S0, stream=stream), 200)
+    res["additive_fp32"] = {"workload": "additive linear attention, B=1 H=1 T=1024 d=64, fp32",
+                            "us_per_call": round(ms0 * 1e3, 2), "tokens_per_s": round(1024 / (ms0 * 1e-3), 1)}
+    B, H, T, D = 1, 16, 65536, 128
+    g = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=2, device=dev)
+    o2 = torch.empty_like(g["v"])
+    S2 = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(la.workspace_size("gated_delta", la.BF16, B, H, T, D, D), 16), dtype=torch.uint8, device=dev)
+    ms2 = timed(lambda: la.prefill("gated_delta", g["q"], g["k"], g["v"], g["alpha"], g["beta"], o=o2, S_T=S2,
+                                   workspace=ws, stream=stream), 20)
+    byt = B * H * T * BYTES_PER_TOKEN_HEAD
+    flo = B * H * T * FLOPS_PER_TOKEN_HEAD
+    t_roof = max(byt / (HBM_PEAK_GBS * 1e9), flo / (BF16_PEAK_TFLOPS * 1e12))
+    nseg, sc = la.segments("gated_delta", la.BF16, B, H, T, D, D)
+    res["gdn_64k"] = {"workload": "gated-delta chunkwise prefill, B=1 H=16 T=65536 d_k=d_v=128, bf16, chunk 64",
+                      "ms": round(ms2, 4), "tokens_per_s": round(T / (ms2 * 1e-3), 1), "segments": nseg,
+                      "chunks_per_segment": sc, "alg_bytes": byt, "alg_flops": flo,
+                      "roofline_time_ms": round(t_roof * 1e3, 4), "roofline_frac": round(t_roof * 1e3 / ms2, 4)}
+    return res
 
 
 def bench_gdn256(torch, la, synth, dev, stream, steps, warmup, T):
