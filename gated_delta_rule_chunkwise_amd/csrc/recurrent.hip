@@ -240,12 +240,182 @@ static hipError_t go_rec_dk(int variant, int B, int H, int64_t Tn, int dk, int d
   return go_rec<256, T>(variant, B, H, Tn, dv, q, k, v, alpha, beta, S0, o, S_T, s);
 }
 
+// ---------------------------------------------------------------------------------------
+// Short fp32 sequences, ADDITIVE and GATED (no delta term).  Unrolling Eq. (1) with
+// g_t = sum_{i<=t} log alpha_i and gamma_t = e^{g_t}:
+//   S_t = gamma_t S_0 + sum_{j<=t} beta_j e^{g_t - g_j} v_j k_j^T,
+//   o_t = gamma_t S_0 q_t + sum_{j<=t} beta_j e^{g_t - g_j} (q_t . k_j) v_j,
+// which is parallel over tokens (the masked attention form).  Up to QMAX_T tokens it
+// replaces the token-by-token walk, whose per-token chain of reductions bounds a single
+// head.  The gate prefix sums are fp64, so that g_t - g_j keeps its accuracy over thousands
+// of tokens; everything else is fp32 with fixed summation orders.
+constexpr int QMAX_T = 2048, QTOK = 16, QKEY = 64, QNT = 256, QDV = 128;
+
+// g[0..n) = prefix sums of log alpha (fp64) for one (b, h), in LDS.
+__device__ void gate_prefix(int n, const float *alpha, double *g, double *part) {
+  const int tid = threadIdx.x, per = (n + QNT - 1) / QNT;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  double run = 0.0;
+  for (int i = lo; i < hi; ++i) run += log((double)alpha[i]);
+  part[tid] = run;
+  __syncthreads();
+  if (tid == 0) {  // exclusive scan of the 256 partial sums, in order
+    double acc = 0.0;
+    for (int w = 0; w < QNT; ++w) {
+      const double x = part[w];
+      part[w] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  run = part[tid];
+  for (int i = lo; i < hi; ++i) {
+    run += log((double)alpha[i]);
+    g[i] = run;
+  }
+  __syncthreads();
+}
+
+// Outputs of QTOK tokens (all d_v columns) per workgroup: scores against key tiles of QKEY
+// tokens in LDS, weighted and causally masked, then accumulated against the value tile.
+template <int DK, int VAR>
+__global__ __launch_bounds__(QNT) void quad_out_kernel(int64_t T_len, int dv, int has_beta,
+                                                       const float *__restrict__ q, const float *__restrict__ k,
+                                                       const float *__restrict__ v, const float *__restrict__ alpha,
+                                                       const float *__restrict__ beta,
+                                                       const float *__restrict__ S0, float *__restrict__ o) {
+  __shared__ double g[QMAX_T];
+  __shared__ double part[QNT];
+  __shared__ float sq[QTOK][DK + 1], sk[QKEY][DK + 1], sv[QKEY][QDV], sp[QTOK][QKEY];
+  const int tid = threadIdx.x;
+  const size_t bh = blockIdx.y;
+  const int T = (int)T_len;
+  const int t0 = blockIdx.x * QTOK, nt = min(QTOK, T - t0), tend = t0 + nt;
+  if (VAR == V_GATED) gate_prefix(tend, alpha + bh * T_len, g, part);
+  for (int i = tid; i < nt * DK; i += QNT) sq[i / DK][i % DK] = q[(bh * T_len + t0 + i / DK) * DK + i % DK];
+  __syncthreads();
+  constexpr int NO = QTOK * QDV / QNT;  // outputs per thread (at most)
+  float acc[NO];
+#pragma unroll
+  for (int m = 0; m < NO; ++m) {
+    acc[m] = 0.0f;
+    const int e = tid + QNT * m, tt = e / dv, c = e % dv;
+    if (S0 && e < nt * dv) {  // gamma_t S_0 q_t
+      const float *srow = S0 + (bh * dv + c) * DK;
+      float x = 0.0f;
+      for (int d = 0; d < DK; ++d) x += srow[d] * sq[tt][d];
+      acc[m] = (VAR == V_GATED ? (float)exp(g[t0 + tt]) : 1.0f) * x;
+    }
+  }
+  for (int j0 = 0; j0 < tend; j0 += QKEY) {
+    const int nk = min(QKEY, tend - j0);
+    __syncthreads();  // the previous tile is no longer read
+    for (int i = tid; i < nk * DK; i += QNT) sk[i / DK][i % DK] = k[(bh * T_len + j0 + i / DK) * DK + i % DK];
+    for (int i = tid; i < nk * dv; i += QNT) sv[i / dv][i % dv] = v[(bh * T_len + j0 + i / dv) * dv + i % dv];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < QTOK * QKEY / QNT; ++m) {
+      const int e = tid + QNT * m, tt = e / QKEY, jj = e % QKEY, t = t0 + tt, j = j0 + jj;
+      float sc = 0.0f;
+      if (tt < nt && jj < nk && j <= t) {
+        for (int d = 0; d < DK; ++d) sc += sq[tt][d] * sk[jj][d];
+        if (VAR == V_GATED)
+          sc *= (has_beta ? beta[bh * T_len + j] : 1.0f) * (float)exp(g[t] - g[j]);
+      }
+      sp[tt][jj] = sc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NO; ++m) {
+      const int e = tid + QNT * m, tt = e / dv, c = e % dv;
+      if (e < nt * dv)
+        for (int jj = 0; jj < nk; ++jj) acc[m] += sp[tt][jj] * sv[jj][c];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NO; ++m) {
+    const int e = tid + QNT * m;
+    if (e < nt * dv) o[(bh * T_len + t0 + e / dv) * dv + e % dv] = acc[m];
+  }
+}
+
+// End state row c of one (b, h): S_T[c][d] = gamma_T S_0[c][d] + sum_j w_j v_j[c] k_j[d],
+// w_j = beta_j e^{g_T - g_j}; the tokens are split over QNT / DK groups of threads, whose
+// partial sums are added in a fixed order.
+template <int DK, int VAR>
+__global__ __launch_bounds__(QNT) void quad_state_kernel(int64_t T_len, int dv, int has_beta,
+                                                         const float *__restrict__ k, const float *__restrict__ v,
+                                                         const float *__restrict__ alpha,
+                                                         const float *__restrict__ beta,
+                                                         const float *__restrict__ S0, float *__restrict__ S_T) {
+  __shared__ double g[QMAX_T];
+  __shared__ double part[QNT];
+  __shared__ float wv[QMAX_T];
+  __shared__ float red[QNT];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const int T = (int)T_len;
+  if (VAR == V_GATED) gate_prefix(T, alpha + bh * T_len, g, part);
+  for (int j = tid; j < T; j += QNT) {
+    float w = 1.0f;
+    if (VAR == V_GATED) w = (has_beta ? beta[bh * T_len + j] : 1.0f) * (float)exp(g[T - 1] - g[j]);
+    wv[j] = w * v[(bh * T_len + j) * dv + c];
+  }
+  __syncthreads();
+  constexpr int NG = QNT / DK;
+  const int d = tid % DK, tg = tid / DK;
+  float x = 0.0f;
+  for (int j = tg; j < T; j += NG) x += wv[j] * k[(bh * T_len + j) * DK + d];
+  red[tid] = x;
+  __syncthreads();
+  if (tg == 0) {
+    float sum = red[d];
+    for (int r = 1; r < NG; ++r) sum += red[r * DK + d];
+    const size_t idx = (bh * dv + c) * DK + d;
+    const float s0 = S0 ? S0[idx] : 0.0f;
+    S_T[idx] = (VAR == V_GATED ? (float)exp(g[T - 1]) : 1.0f) * s0 + sum;
+  }
+}
+
+// Whether the attention form takes this problem (fp32 inputs only): its work grows as
+// B H T^2 while the token walk's time grows as T (given enough parallel rows), so only
+// small problems: T <= QMAX_T and B H ceil(T / 64)^2 <= 4096 (one head of 4096 tokens' worth).
+static bool quad_ok(int variant, int64_t BH, int64_t T, int dk, int dv) {
+  const int64_t tiles = (T + QKEY - 1) / QKEY;
+  return (variant == V_ADDITIVE || variant == V_GATED) && T >= 1 && T <= QMAX_T && BH * tiles * tiles <= 4096 &&
+         (dk == 64 || dk == 128) && dv >= 1 && dv <= QDV;
+}
+
+template <int DK, int VAR>
+static void go_quad(int B, int H, int64_t T, int dv, int has_beta, const float *q, const float *k, const float *v,
+                    const float *alpha, const float *beta, const float *S0, float *o, float *S_T, hipStream_t s) {
+  const unsigned bh = (unsigned)((int64_t)B * H);
+  hipLaunchKernelGGL((quad_out_kernel<DK, VAR>), dim3((unsigned)((T + QTOK - 1) / QTOK), bh), dim3(QNT), 0, s, T,
+                     dv, has_beta, q, k, v, alpha, beta, S0, o);
+  if (S_T)
+    hipLaunchKernelGGL((quad_state_kernel<DK, VAR>), dim3((unsigned)dv, bh), dim3(QNT), 0, s, T, dv, has_beta, k, v,
+                       alpha, beta, S0, S_T);
+}
+
 hipError_t launch_recurrent_rows(int variant, int dtype, int B, int H, int64_t T, int d_k, int d_v,
                                  const void *q, const void *k, const void *v, const void *alpha,
                                  const void *beta, const float *S0, void *o, float *S_T,
                                  hipStream_t s) {
   if (dtype == T_BF16)
     return go_rec_dk<bf16_t>(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+  if (quad_ok(variant, (int64_t)B * H, T, d_k, d_v)) {  // short fp32 sequences without the delta term
+    const float *fq = (const float *)q, *fk = (const float *)k, *fv = (const float *)v;
+    const float *fa = (const float *)alpha, *fb = (const float *)beta;
+    const int hb = beta != nullptr;
+    if (variant == V_ADDITIVE) {
+      if (d_k == 64) go_quad<64, V_ADDITIVE>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, (float *)o, S_T, s);
+      else go_quad<128, V_ADDITIVE>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, (float *)o, S_T, s);
+    } else {
+      if (d_k == 64) go_quad<64, V_GATED>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, (float *)o, S_T, s);
+      else go_quad<128, V_GATED>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, (float *)o, S_T, s);
+    }
+    return hipGetLastError();
+  }
   return go_rec_dk<float>(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
 }
 

@@ -129,7 +129,10 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  * across segments of chunks (a three-pass segment scan: per-segment affine state maps,
  * a scan of the segment start states, then every segment replayed from its start
  * state).  fp32
- * inputs take an fp32 token-recurrent path (fp32 FMA throughout).
+ * inputs take an fp32 path (fp32 FMA throughout): ADDITIVE and GATED problems of at most 2048
+ * tokens and small size (B H ceil(T/64)^2 <= 4096, d_k in {64, 128}, d_v <= 128) in the
+ * masked attention form that Eq. (1) unrolls to (parallel over tokens, gate prefix sums in
+ * fp64), everything else token by token.
  *
  * Supported: bf16 -- ADDITIVE/GATED/GATED_DELTA with d_k = d_v in {64, 128, 256}
  *                    (128 and 256 chunkwise; 64 token-recurrent in fp32);

@@ -59,6 +59,16 @@ def test_prefill_fp32_other_widths(la, variant):
     _check_prefill(la, variant, 1, 2, 77, 64, 17, torch.float32, seed=4)
 
 
+@pytest.mark.parametrize("variant", ["additive", "gated"])
+@pytest.mark.parametrize("T", [2048, 2049])
+def test_prefill_fp32_attention_form_limit(la, variant, T):
+    # fp32 additive/gated prefills of at most 2048 tokens use the masked attention form
+    # (parallel over tokens), longer ones the token-recurrent walk: both sides of the limit,
+    # with a start state and beta given
+    S0 = synth.gdn_state((1, 2, 64, 64), seed=17, device=DEV) * 0.3
+    _check_prefill(la, variant, 1, 2, T, 64, 64, torch.float32, seed=18, S0=S0)
+
+
 @pytest.mark.parametrize("variant", ROWS_VARIANTS + BASED_VARIANTS)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_prefill_with_start_state(la, variant, dtype):
