@@ -24,7 +24,8 @@ STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_INVALID", -3: "LA_ERR_UNSUP
           -4: "LA_ERR_ALIGN", -5: "LA_ERR_WORKSPACE", -6: "LA_ERR_ALIAS", -7: "LA_ERR_HIP"}
 EXPORTS = ("la_abi_version", "la_status_string", "la_prefill_workspace_size", "la_prefill",
            "la_prefill_pass", "la_prefill_segments", "la_decode_step",
-           "la_write_scores", "la_write_windows", "la_note_addresses", "la_address_votes")
+           "la_write_scores", "la_write_windows", "la_note_addresses", "la_address_votes",
+           "la_state_scale")
 PASS_MAPS, PASS_SCAN, PASS_REPLAY, PASS_TRANSFORM = 1, 2, 3, 4
 
 LIB_PATH = Path(__file__).resolve().parent / "libla.so"

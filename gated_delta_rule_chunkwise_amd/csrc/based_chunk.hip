@@ -217,10 +217,12 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
   f32x4 st[NFT];
   {
     const int l16 = lane & 15, g = lane >> 4;
-    // the replay starts segment 0 from S0 (ABI layout), later segments from the scan's
-    // start states; the map pass starts from zero
-    const float *src_i = (OUT && seg > 0) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
-    const float *src_a = (OUT && seg == 0 && a.s0) ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
+    // with several segments the replay starts every segment from the scan's start states
+    // (segment 0's is S0 in internal order, so no replay workgroup reads S0 while the last
+    // one writes S_T, which may be the same buffer); with one segment it starts from S0
+    // (ABI layout); the map pass starts from zero
+    const float *src_i = (OUT && a.nseg > 1) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
+    const float *src_a = (OUT && a.nseg == 1 && a.s0) ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
 #pragma unroll
     for (int m = 0; m < NFT; ++m)
 #pragma unroll
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
       }
     for (int fi = tid; fi < NF; fi += NTHR) {
       sZ[fi] = src_i ? src_i[(size_t)fi * (DV + 1) + DV]
-                     : abi_load(OUT && seg == 0 && a.z0 ? a.z0 + bh * a.Dabi : nullptr, a.compact, fi, 1, 0);
+                     : abi_load(OUT && a.nseg == 1 && a.z0 ? a.z0 + bh * a.Dabi : nullptr, a.compact, fi, 1, 0);
     }
   }
 
@@ -549,10 +551,10 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
   }
 }
 
-// Pass 2: the start states of segments 1..nseg-1, prefix sums of the per-segment sums of
-// segments 0..nseg-2 from the (ABI-layout) start state (segment 0 starts from it
-// directly, and the last segment's replay writes the end state).  One thread per state
-// element and (b, h), all segments' sums loaded at once (up to 16).
+// Pass 2: the start states of all segments in internal order: segment 0's is the
+// (ABI-layout) start state, the others prefix sums of the per-segment sums of segments
+// 0..nseg-2 from it (the last segment's replay writes the end state).  One thread per
+// state element and (b, h), up to 16 segments' sums loaded at once.
 __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   constexpr int NE = NF * (DV + 1);
@@ -563,6 +565,7 @@ __global__ __launch_bounds__(256) void based_scan_kernel(const Args a) {
     const float *src = col < DV ? (a.s0 ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr) : (a.z0 ? a.z0 + bh * a.Dabi : nullptr);
     const int stride = col < DV ? DV : 1, c = col < DV ? col : 0;
     float x = abi_load(src, a.compact, fi, stride, c);
+    a.starts[(bh * a.nseg) * (size_t)NE + id] = x;
     const int nmap = a.nseg - 1;  // segments with a map
     for (int i0 = 0; i0 < nmap; i0 += UNR) {
       float d[UNR];

@@ -32,7 +32,7 @@ constexpr int ROWS_NT = 512;
 
 template <int DK, int VAR, typename T>
 __global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_beta,
-                                                          const float *__restrict__ S_in,
+                                                          const float *S_in,
                                                           float *S_out, const T *__restrict__ q,
                                                           const T *__restrict__ k,
                                                           const T *__restrict__ v,
@@ -123,8 +123,8 @@ __device__ __forceinline__ void triangle_pair(int idx, int n, int &a, int &b) {
 // columns 4(t%16)..+3 for the features f = t/16 + (NT/16) i, so every wave-wide access
 // to s covers four whole 256-byte feature rows.
 template <int NT, bool COMPACT, typename T>
-__global__ __launch_bounds__(NT) void decode_based_kernel(float eps, const float *__restrict__ S_in,
-                                                           const float *__restrict__ z_in,
+__global__ __launch_bounds__(NT) void decode_based_kernel(float eps, const float *S_in,
+                                                           const float *z_in,
                                                            float *S_out, float *z_out,
                                                            const T *__restrict__ q,
                                                            const T *__restrict__ k,

@@ -286,3 +286,29 @@ def test_based_compact_matches_full(la, dtype):
                        for a, b in idx], axis=2)
     assert_close(sc[:, :, 1 + dp:], fold_s, tol, what="s compact vs folded full")
     assert_close(sc[:, :, :1 + dp], sf[:, :, :1 + dp], tol, what="s [1, x] rows")
+
+
+@pytest.mark.parametrize("variant", ROWS_VARIANTS + BASED_VARIANTS)
+def test_prefill_in_place_state_across_segments(la, variant):
+    """S_T may be S0's own buffer (include/la.h) also when the sequence is split into
+    segments, whose replays run concurrently: the in-place result equals the out-of-place
+    one bit for bit."""
+    B, H, T = 1, 4, 64 * 20 + 7
+    dk, dv = (16, 64) if variant in BASED_VARIANTS else (128, 128)
+    q, k, v, a, b = _inputs(variant, B, H, T, dk, dv, torch.bfloat16, 64)
+    nseg, _ = la.segments(variant, la.BF16, B, H, T, dk, dv)
+    assert nseg > 1
+    if variant in BASED_VARIANTS:
+        w = synth.based_inputs(B, H, 50, dk, dv, dtype=torch.bfloat16, seed=65, device=DEV)
+        _, S0, z0 = la.prefill(variant, w["q"], w["k"], w["v"])
+    else:
+        S0, z0 = synth.gdn_state((B, H, dv, dk), seed=65, device=DEV) * 0.3, None
+    o1, S1, z1 = la.prefill(variant, q, k, v, a, b, S0=S0, z0=z0)
+    S_io = S0.clone()
+    z_io = None if z0 is None else z0.clone()
+    o2, S2, z2 = la.prefill(variant, q, k, v, a, b, S0=S_io, z0=z_io, S_T=S_io, z_T=z_io)
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == S_io.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(S1, S_io)
+    if z0 is not None:
+        assert torch.equal(z1, z_io)

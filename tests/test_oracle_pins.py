@@ -29,14 +29,14 @@ def rng(seed):
     return np.random.default_rng(seed)
 
 
-def gdn_like(r, B, H, T, dk, dv, normalize=True):
+def gdn_like(r, B, H, T, dk, dv, normalize=True, a_range=(-2, 4)):
     q = r.standard_normal((B, H, T, dk))
     k = r.standard_normal((B, H, T, dk))
     if normalize:
         q /= np.linalg.norm(q, axis=-1, keepdims=True)
         k /= np.linalg.norm(k, axis=-1, keepdims=True)
     v = r.standard_normal((B, H, T, dv))
-    a = r.uniform(-2, 4, (B, H, T))
+    a = r.uniform(a_range[0], a_range[1], (B, H, T))
     alpha = np.exp(-np.log1p(np.exp(a)))
     beta = 1 / (1 + np.exp(-r.standard_normal((B, H, T))))
     return q, k, v, alpha, beta
@@ -364,18 +364,50 @@ def test_chunked_derivation_matches_sequential(variant, C):
     assert rel(oc, o[0, 0]) < 1e-10 and rel(Sc, S_T[0, 0]) < 1e-10
 
 
-@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta"])
-def test_segment_scan_matches_sequential(variant):
-    """Per-segment affine maps + scan + rerun (the three-pass prefill) == recurrence."""
+def _segment_case(variant):
+    # slow gates (a ~ U(-8, -4), alpha in [0.98, 0.9997]): the state carried across a
+    # 48-token segment keeps most of its size, so the segment transitions matter
     r = rng(14)
     T, dk, dv, C = 64 * 7 + 13, 16, 8, 16
-    q, k, v, alpha, beta = gdn_like(r, 1, 1, T, dk, dv)
+    q, k, v, alpha, beta = gdn_like(r, 1, 1, T, dk, dv, a_range=(-8, -4))
     S0 = r.standard_normal((1, 1, dv, dk))
     o, S_T, _ = oracle.prefill(variant, q, k, v, alpha=alpha, beta=beta, S0=S0)
     os_, Ss = models.segmented(variant, q[0, 0], k[0, 0], v[0, 0],
                                None if variant == "additive" else alpha[0, 0],
                                None if variant == "additive" else beta[0, 0], S0[0, 0], C, 3)
-    assert rel(os_, o[0, 0]) < 1e-10 and rel(Ss, S_T[0, 0]) < 1e-10
+    return max(rel(os_, o[0, 0]), rel(Ss, S_T[0, 0]))
+
+
+@pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta"])
+def test_segment_scan_matches_sequential(variant):
+    """Per-segment affine maps + scan + rerun (the three-pass prefill) == recurrence."""
+    assert _segment_case(variant) < 1e-10
+
+
+@pytest.mark.parametrize("mistake", ["zero_transition", "transposed_transition", "dropped_decay"])
+@pytest.mark.parametrize("variant", ["gated", "gated_delta"])
+def test_segment_pin_catches_planted_transition_mistakes(monkeypatch, variant, mistake):
+    """The segment pin above is sensitive to the transition M_c that the map pass composes:
+    a zeroed, transposed or undecayed transition, planted in a copy of the chunk-map model,
+    moves the result far past the pin's bound."""
+    good = models.chunk_map
+
+    def planted(variant_, K, V, a, b):
+        M, Bc = good(variant_, K, V, a, b)
+        if mistake == "zero_transition":
+            M = np.zeros_like(M)
+        elif mistake == "transposed_transition":
+            M = M.T.copy()
+        else:  # the chunk's decay left out of the transition
+            M = M / np.exp(np.sum(np.log(a)))
+        return M, Bc
+
+    monkeypatch.setattr(models, "chunk_map", planted)
+    err = _segment_case(variant)
+    if variant == "gated" and mistake == "transposed_transition":
+        assert err < 1e-10  # gamma I is symmetric: nothing to catch
+    else:
+        assert err > 1e-2, f"planted {mistake} gives only {err:.2e}"
 
 
 @pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based", "based_compact"])
