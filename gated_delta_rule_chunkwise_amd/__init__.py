@@ -129,6 +129,17 @@ def segments(variant, dtype, B, H, T, d_k, d_v):
     return n.value, c.value
 
 
+def prefill_passes(variant, dtype, B, H, T, d_k, d_v):
+    """The passes la_prefill runs for this problem, in order: calling la_prefill_pass with
+    each in turn (same buffers, one workspace) is la_prefill."""
+    nseg, _ = segments(variant, dtype, B, H, T, d_k, d_v)
+    ps = [PASS_TRANSFORM] if (_var(variant) == GATED_DELTA and dtype == BF16 and d_k == d_v
+                              and d_k in (128, 256)) else []
+    if nseg > 1:
+        ps += [PASS_MAPS, PASS_SCAN]
+    return ps + [PASS_REPLAY]
+
+
 def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6, want_state=True,
             o=None, S_T=None, z_T=None, workspace=None, stream=None, pass_=None):
     """Run la_prefill (or one pass of it, ``pass_`` in PASS_TRANSFORM/MAPS/SCAN/REPLAY, see la.h).
