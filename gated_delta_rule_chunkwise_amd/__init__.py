@@ -25,7 +25,8 @@ STATUS = {0: "LA_OK", -1: "LA_ERR_NULL", -2: "LA_ERR_INVALID", -3: "LA_ERR_UNSUP
 EXPORTS = ("la_abi_version", "la_status_string", "la_prefill_workspace_size", "la_prefill",
            "la_prefill_pass", "la_prefill_segments", "la_decode_step",
            "la_write_scores", "la_write_windows", "la_note_addresses", "la_address_votes",
-           "la_state_scale")
+           "la_state_scale", "la_prefill_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 << 20  # LA_NOALLOC_SCRATCH_BYTES
 PASS_MAPS, PASS_SCAN, PASS_REPLAY, PASS_TRANSFORM = 1, 2, 3, 4
 
 LIB_PATH = Path(__file__).resolve().parent / "libla.so"
@@ -59,6 +60,8 @@ def load(path: str | None = None):
     lib.la_prefill.restype = i32
     lib.la_prefill_pass.argtypes = [i32] + lib.la_prefill.argtypes
     lib.la_prefill_pass.restype = i32
+    lib.la_prefill_noalloc.argtypes = [i32, i32, i32, i32, i64, i32, i32, f32] + [vp] * 11
+    lib.la_prefill_noalloc.restype = i32
     lib.la_prefill_segments.argtypes = [i32, i32, i32, i32, i64, i32, i32,
                                         ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.la_prefill_segments.restype = i32
@@ -170,6 +173,31 @@ def prefill(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6,
     st = lib.la_prefill(*args) if pass_ is None else lib.la_prefill_pass(int(pass_), *args)
     if st != 0:
         raise LAError(st, "la_prefill" if pass_ is None else "la_prefill_pass")
+    return o, S_T, z_T
+
+
+def prefill_noalloc(variant, q, k, v, alpha=None, beta=None, S0=None, z0=None, eps=1e-6, o=None,
+                    S_T=None, z_T=None, stream=None):
+    """Run la_prefill_noalloc: la_prefill with its workspace in the library's static device
+    scratch (the call itself allocates nothing; pass o and S_T (z_T) to allocate nothing
+    here either).  Same layouts as prefill().  Returns (o, S_T, z_T)."""
+    var = _var(variant)
+    lib = load()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if S_T is None:
+        if var in (BASED, BASED_COMPACT):
+            D = feature_dim(dk, var == BASED_COMPACT)
+            S_T = torch.empty((B, H, D, dv), dtype=torch.float32, device=q.device)
+            z_T = torch.empty((B, H, D), dtype=torch.float32, device=q.device) if z_T is None else z_T
+        else:
+            S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    st = lib.la_prefill_noalloc(var, _dtype(q), B, H, T, dk, dv, float(eps), _p(q), _p(k), _p(v), _p(alpha),
+                                _p(beta), _p(S0), _p(z0), _p(o), _p(S_T), _p(z_T), _stream(stream))
+    if st != 0:
+        raise LAError(st, "la_prefill_noalloc")
     return o, S_T, z_T
 
 

@@ -584,31 +584,36 @@ struct Plan {
   int nseg, seg_chunks;
 };
 
-// About three workgroups per CU in all, split only when the heads alone cannot fill it.
-Plan make_plan(int B, int H, int64_t T) {
+// At most `nseg` segments of equal whole-chunk length over nch chunks.
+Plan plan_of(int64_t nch, int64_t nseg) {
+  if (nseg > nch) nseg = nch;
+  if (nseg < 1) nseg = 1;
+  const int64_t sc = (nch + nseg - 1) / nseg;
+  return Plan{(int)((nch + sc - 1) / sc), (int)sc};
+}
+
+size_t ws_bytes(int B, int H, const Plan &p) {
+  return p.nseg > 1 ? 2 * (size_t)B * H * p.nseg * NF * (DV + 1) * sizeof(float) : 0;
+}
+
+// About three workgroups per CU in all, split only when the heads alone cannot fill it;
+// fewer segments when the workspace must stay within `cap` bytes (one segment needs none).
+Plan make_plan(int B, int H, int64_t T, size_t cap) {
   const int64_t nch = (T + C - 1) / C;
   const int64_t bhn = (int64_t)B * H;
-  int64_t nseg = 1;
-  if (bhn < 384) {
-    nseg = (768 + bhn - 1) / bhn;
-    if (nseg > nch) nseg = nch;
-    if (nseg < 1) nseg = 1;
-  }
-  const int64_t sc = (nch + nseg - 1) / nseg;
-  nseg = (nch + sc - 1) / sc;
-  return Plan{(int)nseg, (int)sc};
+  Plan p = plan_of(nch, bhn < 384 ? (768 + bhn - 1) / bhn : 1);
+  while (p.nseg > 1 && ws_bytes(B, H, p) > cap) p = plan_of(nch, p.nseg / 2);
+  return p;
 }
 
 }  // namespace based
 
-size_t based_chunk_workspace_bytes(int B, int H, int64_t T) {
-  const based::Plan p = based::make_plan(B, H, T);
-  if (p.nseg <= 1) return 0;
-  return 2 * (size_t)B * H * p.nseg * based::NF * (based::DV + 1) * sizeof(float);
+size_t based_chunk_workspace_bytes(int B, int H, int64_t T, size_t cap) {
+  return based::ws_bytes(B, H, based::make_plan(B, H, T, cap));
 }
 
 void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks) {
-  const based::Plan p = based::make_plan(B, H, T);
+  const based::Plan p = based::make_plan(B, H, T, SIZE_MAX);
   *nseg = p.nseg;
   *seg_chunks = p.seg_chunks;
 }
@@ -616,9 +621,10 @@ void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks) {
 hipError_t launch_based_chunk_prefill(bool compact, int B, int H, int64_t T, float eps,
                                       const void *q, const void *k, const void *v,
                                       const float *s0, const float *z0, void *o, float *s_T,
-                                      float *z_T, void *workspace, int pass_mask, hipStream_t s) {
+                                      float *z_T, void *workspace, size_t ws_cap, int pass_mask,
+                                      hipStream_t s) {
   using namespace based;
-  const Plan p = make_plan(B, H, T);
+  const Plan p = make_plan(B, H, T, ws_cap);
   Args a;
   a.q = (const bf16_t *)q;
   a.k = (const bf16_t *)k;

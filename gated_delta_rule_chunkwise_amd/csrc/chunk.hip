@@ -1216,21 +1216,12 @@ struct Plan {
   int nseg, seg_chunks;
 };
 
-// Segments per (b, h): enough workgroups to give every CU about four (state workgroups are
-// row blocks of WROWS rows, so a (b, h) at d = 256 is two of them), but only when the
-// heads alone cannot fill the chip (a split costs one extra pass over the keys/values).
-Plan make_plan(int B, int H, int64_t T, int dv) {
-  const int64_t nch = (T + C - 1) / C;
-  const int64_t units = (int64_t)B * H * (dv / WROWS);
-  int64_t nseg = 1;
-  if (units < 128) {
-    nseg = (1024 + units - 1) / units;
-    if (nseg > nch) nseg = nch;
-    if (nseg < 1) nseg = 1;
-  }
+// At most `nseg` segments of equal whole-chunk length over nch chunks.
+Plan plan_of(int64_t nch, int64_t nseg) {
+  if (nseg > nch) nseg = nch;
+  if (nseg < 1) nseg = 1;
   const int64_t sc = (nch + nseg - 1) / nseg;
-  nseg = (nch + sc - 1) / sc;
-  return Plan{(int)nseg, (int)sc};
+  return Plan{(int)((nch + sc - 1) / sc), (int)sc};
 }
 
 struct WsLayout {
@@ -1239,8 +1230,7 @@ struct WsLayout {
 
 // Workspace: per-segment maps, log decays and start states (more than one segment), then
 // the per-chunk transforms (delta rule).  Every part starts on a 256-byte boundary.
-WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d) {
-  const Plan p = make_plan(B, H, T, d);
+WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d, const Plan &p) {
   const size_t bh = (size_t)B * H;
   const size_t nch = (size_t)((T + C - 1) / C);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1261,6 +1251,18 @@ WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d) {
   }
   w.total = off;
   return w;
+}
+
+// Segments per (b, h): enough workgroups to give every CU about four (state workgroups are
+// row blocks of WROWS rows, so a (b, h) at d = 256 is two of them), but only when the
+// heads alone cannot fill the chip (a split costs one extra pass over the keys/values);
+// fewer when the workspace must stay within `cap` bytes.
+Plan make_plan(bool delta, int B, int H, int64_t T, int dv, size_t cap) {
+  const int64_t nch = (T + C - 1) / C;
+  const int64_t units = (int64_t)B * H * (dv / WROWS);
+  Plan p = plan_of(nch, units < 128 ? (1024 + units - 1) / units : 1);
+  while (p.nseg > 1 && ws_layout(delta, B, H, T, dv, p).total > cap) p = plan_of(nch, p.nseg / 2);
+  return p;
 }
 
 bool chunk_width(int d_k, int d_v) { return d_k == d_v && (d_k == 128 || d_k == 256); }
@@ -1299,13 +1301,14 @@ void launch_passes(const Args &a, bool delta, int pass_mask, hipStream_t s) {
 
 }  // namespace gdn
 
-size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v) {
+size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v, size_t cap) {
   if (!gdn::chunk_width(d_k, d_v)) return 0;
-  return gdn::ws_layout(variant == V_GATED_DELTA, B, H, T, d_k).total;
+  const bool delta = variant == V_GATED_DELTA;
+  return gdn::ws_layout(delta, B, H, T, d_k, gdn::make_plan(delta, B, H, T, d_k, cap)).total;
 }
 
-void chunk_segments(int B, int H, int64_t T, int d, int *nseg, int *seg_chunks) {
-  const gdn::Plan p = gdn::make_plan(B, H, T, d);
+void chunk_segments(int variant, int B, int H, int64_t T, int d, int *nseg, int *seg_chunks) {
+  const gdn::Plan p = gdn::make_plan(variant == V_GATED_DELTA, B, H, T, d, SIZE_MAX);
   *nseg = p.nseg;
   *seg_chunks = p.seg_chunks;
 }
@@ -1313,15 +1316,15 @@ void chunk_segments(int B, int H, int64_t T, int d, int *nseg, int *seg_chunks) 
 hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, int d_v,
                                 const void *q, const void *k, const void *v, const void *alpha,
                                 const void *beta, const float *S0, void *o, float *S_T,
-                                void *workspace, int pass_mask, hipStream_t s) {
+                                void *workspace, size_t ws_cap, int pass_mask, hipStream_t s) {
   using namespace gdn;
   if (!chunk_width(d_k, d_v)) {  // other widths: the token-recurrent kernel (fp32 arithmetic)
     if (!(pass_mask & PASS_REPLAY)) return hipSuccess;
     return launch_recurrent_rows(variant, T_BF16, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
   }
   const bool delta = variant == V_GATED_DELTA;
-  const Plan p = make_plan(B, H, T, d_k);
-  const WsLayout w = ws_layout(delta, B, H, T, d_k);
+  const Plan p = make_plan(delta, B, H, T, d_k, ws_cap);
+  const WsLayout w = ws_layout(delta, B, H, T, d_k, p);
   char *ws = (char *)workspace;
   Args a;
   a.q = (const bf16_t *)q;

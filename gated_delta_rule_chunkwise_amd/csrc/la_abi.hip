@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/la.h"
 #include "la_launch.h"
 
@@ -76,10 +78,42 @@ int check_prefill_shape(int variant, int dtype, int B, int H, int64_t T, int dk,
   return LA_OK;
 }
 
-size_t prefill_ws(int variant, int dtype, int B, int H, int64_t T, int dk, int dv) {
+// Workspace bytes of a prefill whose segment plan keeps them within `cap` (SIZE_MAX: the
+// plan depends on the shape alone); more than `cap` when even one segment needs more.
+size_t prefill_ws(int variant, int dtype, int B, int H, int64_t T, int dk, int dv, size_t cap = SIZE_MAX) {
   if (dtype != LA_BF16 || T == 0) return 0;
-  if (is_based(variant)) return based_chunk_workspace_bytes(B, H, T);
-  return chunk_workspace_bytes(variant, B, H, T, dk, dv);
+  if (is_based(variant)) return based_chunk_workspace_bytes(B, H, T, cap);
+  return chunk_workspace_bytes(variant, B, H, T, dk, dv, cap);
+}
+
+}  // namespace
+
+// Scratch of la_prefill_noalloc: the prefill workspace for callers that cannot allocate.
+// One copy per device (a code-object global), held until the process ends.  Host code uses
+// it only through the device address hipGetSymbolAddress returns (the array's name is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+
+// The scratch's device address on the current device, looked up once per device with that
+// device current.
+int scratch_for_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LA_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return LA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LA_OK;
 }
 
 }  // namespace
@@ -118,7 +152,8 @@ static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int he
                         int64_t seq_len, int d_k, int d_v, float eps, const void *q,
                         const void *k, const void *v, const void *alpha, const void *beta,
                         const float *S0, const float *z0, void *o, float *S_T, float *z_T,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+                        void *workspace, size_t workspace_bytes, void *stream,
+                        size_t ws_cap = SIZE_MAX) {
   if (pass_mask <= 0 || pass_mask > PASS_ALL) return LA_ERR_INVALID;
   int st = check_prefill_shape(variant, dtype, batch, heads, seq_len, d_k, d_v);
   if (st != LA_OK) return st;
@@ -154,7 +189,7 @@ static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int he
   const Range ra{alpha, BH * T * es}, rb{beta, BH * T * es};
   const Range rS0{S0, state_n * 4}, rz0{z0, BH * D * 4};
   const Range ro{o, BH * T * d_v * es}, rST{S_T, state_n * 4}, rzT{z_T, BH * D * 4};
-  const size_t need_ws = prefill_ws(variant, dtype, B, H, T, d_k, d_v);
+  const size_t need_ws = prefill_ws(variant, dtype, B, H, T, d_k, d_v, ws_cap);
   if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return LA_ERR_WORKSPACE;
   const Range rw{workspace, need_ws};
   const Range outs[] = {ro, rST, rzT, rw};
@@ -179,12 +214,12 @@ static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int he
   if (based) {
     if (dtype == LA_BF16)
       e = launch_based_chunk_prefill(compact, B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, workspace,
-                                     pass_mask, s);
+                                     ws_cap, pass_mask, s);
     else if (pass_mask & PASS_REPLAY)
       e = launch_recurrent_based(dtype, compact, B, H, T, eps, q, k, v, S0, z0, o, S_T, z_T, s);
   } else if (dtype == LA_BF16) {
     e = launch_chunk_prefill(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, workspace,
-                             pass_mask, s);
+                             ws_cap, pass_mask, s);
   } else if (pass_mask & PASS_REPLAY) {
     e = launch_recurrent_rows(variant, dtype, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
   }
@@ -197,6 +232,25 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
                float *z_T, void *workspace, size_t workspace_bytes, void *stream) {
   return prefill_impl(PASS_ALL, variant, dtype, batch, heads, seq_len, d_k, d_v, eps, q, k, v,
                       alpha, beta, S0, z0, o, S_T, z_T, workspace, workspace_bytes, stream);
+}
+
+int la_prefill_noalloc(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k,
+                       int d_v, float eps, const void *q, const void *k, const void *v,
+                       const void *alpha, const void *beta, const float *S0, const float *z0,
+                       void *o, float *S_T, float *z_T, void *stream) {
+  // shape first: a problem whose workspace exceeds the scratch even with one segment is
+  // rejected before any HIP call
+  const int st = check_prefill_shape(variant, dtype, batch, heads, seq_len, d_k, d_v);
+  if (st != LA_OK) return st;
+  if (prefill_ws(variant, dtype, batch, heads, seq_len, d_k, d_v, LA_NOALLOC_SCRATCH_BYTES) >
+      LA_NOALLOC_SCRATCH_BYTES)
+    return LA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const int sst = scratch_for_current_device(&ws);
+  if (sst != LA_OK) return sst;
+  return prefill_impl(PASS_ALL, variant, dtype, batch, heads, seq_len, d_k, d_v, eps, q, k, v, alpha,
+                      beta, S0, z0, o, S_T, z_T, ws, LA_NOALLOC_SCRATCH_BYTES, stream,
+                      LA_NOALLOC_SCRATCH_BYTES);
 }
 
 int la_prefill_pass(int pass, int variant, int dtype, int batch, int heads, int64_t seq_len,
@@ -227,7 +281,7 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
   if (is_based(variant))
     based_chunk_segments(batch, heads, seq_len, n_segments, chunks_per_segment);
   else if (d_k == d_v && (d_k == 128 || d_k == 256))
-    chunk_segments(batch, heads, seq_len, d_k, n_segments, chunks_per_segment);
+    chunk_segments(variant, batch, heads, seq_len, d_k, n_segments, chunks_per_segment);
   return LA_OK;
 }
 

@@ -30,21 +30,24 @@ hipError_t launch_recurrent_based(int dtype, bool compact, int B, int H, int64_t
                                   const float *z0, void *o, float *s_T, float *z_T, hipStream_t s);
 
 // chunk.hip (chunkwise bf16 prefill for ADDITIVE / GATED / GATED_DELTA)
-size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v);
+// ws_cap: the segment plan keeps the workspace within this many bytes (SIZE_MAX: no limit;
+// the plan then depends on the shape alone, as la_prefill_segments reports it)
+size_t chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v, size_t ws_cap);
 // pass_mask: PASS_TRANSFORM | PASS_MAPS | PASS_SCAN | PASS_REPLAY (see la_prefill_pass in la.h)
 enum { PASS_MAPS = 1, PASS_SCAN = 2, PASS_REPLAY = 4, PASS_TRANSFORM = 8, PASS_ALL = 15 };
 hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, int d_v,
                                 const void *q, const void *k, const void *v, const void *alpha,
                                 const void *beta, const float *S0, void *o, float *S_T,
-                                void *workspace, int pass_mask, hipStream_t s);
-void chunk_segments(int B, int H, int64_t T, int d, int *nseg, int *seg_chunks);
+                                void *workspace, size_t ws_cap, int pass_mask, hipStream_t s);
+void chunk_segments(int variant, int B, int H, int64_t T, int d, int *nseg, int *seg_chunks);
 
 // based_chunk.hip (chunkwise bf16 BASED prefill)
-size_t based_chunk_workspace_bytes(int B, int H, int64_t T);
+size_t based_chunk_workspace_bytes(int B, int H, int64_t T, size_t ws_cap);
 hipError_t launch_based_chunk_prefill(bool compact, int B, int H, int64_t T, float eps,
                                       const void *q, const void *k, const void *v,
                                       const float *s0, const float *z0, void *o, float *s_T,
-                                      float *z_T, void *workspace, int pass_mask, hipStream_t s);
+                                      float *z_T, void *workspace, size_t ws_cap, int pass_mask,
+                                      hipStream_t s);
 void based_chunk_segments(int B, int H, int64_t T, int *nseg, int *seg_chunks);
 
 // notebank.hip (NoteBank write and address steps)

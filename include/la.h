@@ -52,8 +52,9 @@
  * unspecified), finite inputs (NaN/Inf propagate).
  *
  * Ownership and threading: the caller owns every buffer, including the workspace.
- * The library allocates no device memory, keeps no per-call global state, and only
- * enqueues work on `stream` (a hipStream_t; NULL = the null stream).  Calls are
+ * The library allocates no device memory (its one static device array, the scratch of
+ * la_prefill_noalloc, comes with the code object), keeps no per-call global state, and
+ * only enqueues work on `stream` (a hipStream_t; NULL = the null stream).  Calls are
  * asynchronous: buffers must stay alive until the stream has passed them.  Calls on
  * distinct streams are independent.  Results are bitwise deterministic run to run.
  *
@@ -139,7 +140,9 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  *                    BASED and BASED_COMPACT with d' = 16, d_v = 64.
  *            fp32 -- ADDITIVE/GATED/GATED_DELTA with d_k in {64, 128, 256} and any d_v;
  *                    BASED and BASED_COMPACT with d' = 16 and d_v = 64.
- *            Any T >= 1 (a partial last chunk is masked).
+ *            Any T >= 1 (a partial last chunk is masked).  T = 0 is the empty prefix:
+ *            nothing is read from q, k, v, alpha, beta (they may be NULL), o is empty,
+ *            and S_T/z_T receive the start state (zeros when S0 is NULL).
  */
 int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k, int d_v,
                float eps, const void *q, const void *k, const void *v, const void *alpha,
@@ -186,7 +189,29 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
                         int d_v, int *n_segments, int *chunks_per_segment);
 
 /*
- * la_decode_step -- one token for N independent states (e.g. N = sequences x heads):
+ * la_prefill_noalloc -- la_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, which comes from a static device array of
+ * LA_NOALLOC_SCRATCH_BYTES bytes that the library holds, one per device, until the
+ * process ends.  The segment plan is chosen so that the workspace fits in it (fewer
+ * segments than la_prefill may use, so results can differ from la_prefill's within the
+ * rounding of the chunked path); a problem whose workspace exceeds it even with a single
+ * segment returns LA_ERR_WORKSPACE before anything is launched (for the gated delta rule
+ * with bf16 inputs, about B H T <= 1.4 million token-heads).  The stream must belong to
+ * the current device.  Every call on a device shares that device's array and leaves its
+ * contents behind: calls that overlap on one device (two streams, or two threads) race.
+ * It calls no hipMalloc, hipFree or other allocating routine.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int la_prefill_noalloc(int variant, int dtype, int batch, int heads, int64_t seq_len, int d_k,
+                       int d_v, float eps, const void *q, const void *k, const void *v,
+                       const void *alpha, const void *beta, const float *S0, const float *z0,
+                       void *o, float *S_T, float *z_T, void *stream);
+
+/*
+ * la_decode_step -- one token for N independent states (e.g. N = sequences x heads): one
+ * step of Eq. (1) of "History Replays Itself" (Sec. 2 Preliminary), or of the BASED
+ * recurrence (reading notes Sec. 2.2-2.3), from the given state:
  *
  *   S_out = S_in A + beta v k^T,  o = S_out q      (BASED: s, z updated, o normalised)
  *

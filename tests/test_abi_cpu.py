@@ -236,3 +236,13 @@ def test_notebank_validation(lib):
                                                  f(vo), f(se), None)
     assert av(dr=12) == -3 and av(nQ=2000) == -3 and av(R=65) == -3 and av(R=0) == -2 and av(N=20000) == -3
     assert av(ch=None) == -1 and av(se=A) == -6
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """la_prefill_noalloc validates the shape and checks that the workspace fits its static
+    scratch (even with one segment) before it touches the device."""
+    args = [P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), None, None, P(6 * A), P(8 * A), None, None]
+    # 16 heads x 1M tokens of gated delta rule: the per-chunk transforms alone exceed it
+    assert lib.la_prefill_noalloc(la.GATED_DELTA, la.BF16, 1, 16, 1 << 20, 128, 128, 1e-6, *args) == -5
+    assert lib.la_prefill_noalloc(9, la.BF16, 1, 2, 100, 128, 128, 1e-6, *args) == -2
+    assert lib.la_prefill_noalloc(la.GATED_DELTA, la.BF16, 1, 2, 100, 96, 96, 1e-6, *args) == -3
