@@ -66,6 +66,9 @@ int check_prefill_shape(int variant, int dtype, int B, int H, int64_t T, int dk,
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID;
   if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0) return LA_ERR_INVALID;
   if ((int64_t)B * H > (int64_t)INT32_MAX / 4) return LA_ERR_UNSUPPORTED;
+  // at most 2^37 token-heads (2^31 chunks of 64: chunk and segment counts stay in 32 bits);
+  // the inputs of a larger problem would not fit in any device's memory
+  if (T > 0 && (int64_t)B * H > ((int64_t)1 << 37) / T) return LA_ERR_UNSUPPORTED;
   if (is_based(variant)) {
     if (dk != 16 || dv != 64) return LA_ERR_UNSUPPORTED;
     return LA_OK;

@@ -140,7 +140,8 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  *                    BASED and BASED_COMPACT with d' = 16, d_v = 64.
  *            fp32 -- ADDITIVE/GATED/GATED_DELTA with d_k in {64, 128, 256} and any d_v;
  *                    BASED and BASED_COMPACT with d' = 16 and d_v = 64.
- *            Any T >= 1 (a partial last chunk is masked).  T = 0 is the empty prefix:
+ *            Any T >= 1 up to B H T <= 2^37 token-heads (a partial last chunk is
+ *            masked; larger problems return LA_ERR_UNSUPPORTED).  T = 0 is the empty prefix:
  *            nothing is read from q, k, v, alpha, beta (they may be NULL), o is empty,
  *            and S_T/z_T receive the start state (zeros when S0 is NULL).
  */
