@@ -1253,14 +1253,18 @@ WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d, const Plan &p) {
   return w;
 }
 
-// Segments per (b, h): enough workgroups to give every CU about four (state workgroups are
-// row blocks of WROWS rows, so a (b, h) at d = 256 is two of them), but only when the
-// heads alone cannot fill the chip (a split costs one extra pass over the keys/values);
-// fewer when the workspace must stay within `cap` bytes.
+// Segments per (b, h): one full round of replay workgroups, i.e. as many as the chip holds
+// at once (two per CU at d = 128, one at d = 256, whose workgroups are twice as wide; state
+// workgroups are row blocks of WROWS rows, so a (b, h) at d = 256 is two of them), but only
+// when the heads alone cannot fill the chip (a split costs one extra pass over the keys
+// and values).  More segments leave the replay's time unchanged and lengthen the scan, a
+// chain of one dependent step per segment.  Fewer when the workspace must stay within
+// `cap` bytes.
 Plan make_plan(bool delta, int B, int H, int64_t T, int dv, size_t cap) {
   const int64_t nch = (T + C - 1) / C;
   const int64_t units = (int64_t)B * H * (dv / WROWS);
-  Plan p = plan_of(nch, units < 128 ? (1024 + units - 1) / units : 1);
+  const int64_t slots = dv == 128 ? 512 : 256;
+  Plan p = plan_of(nch, units < 128 ? (slots + units - 1) / units : 1);
   while (p.nseg > 1 && ws_layout(delta, B, H, T, dv, p).total > cap) p = plan_of(nch, p.nseg / 2);
   return p;
 }

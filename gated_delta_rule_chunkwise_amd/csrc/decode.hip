@@ -24,13 +24,34 @@ namespace la {
 
 // One workgroup of ROWS_NT threads per state.  A row of DK floats is spread over
 // LPR = DK/8 lanes, 8 columns each as two float4 at column groups lr and lr + LPR, so the
-// LPR lanes of a row read one contiguous run; ROWS_NT/LPR rows per pass, two passes
-// loaded before either is used.  Eight waves with few rows each keep more requests in
+// LPR lanes of a row read one contiguous run; ROWS_NT/LPR rows per pass, UNROLL passes
+// loaded before any is used.  Eight waves with few rows each keep more requests in
 // flight per CU than four waves with more rows each (which run at higher register use
 // and lower occupancy): about 10% more bandwidth for 128 x 128 states.
+//
+// STREAM: the state set is larger than the 256 MB Infinity Cache can keep between steps,
+// so every step streams it from HBM: eight passes in flight and non-temporal loads and
+// stores (which do not displace other data from the caches).  Measured on 128 x 128 states:
+// 5.8 TB/s against 5.2 TB/s for the cached form once the set exceeds ~384 MiB; below that
+// the cached form is faster (6.2-6.4 TB/s at 256 MiB, where part of the set stays cached).
 constexpr int ROWS_NT = 512;
+constexpr size_t STREAM_BYTES = (size_t)320 << 20;  // state sets above this stream
 
-template <int DK, int VAR, typename T>
+template <bool NT>
+__device__ __forceinline__ float4 ld_state(const float *p) {
+  if (NT) {
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(t[0], t[1], t[2], t[3]);
+  }
+  return *reinterpret_cast<const float4 *>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_state(float *p, float a, float b, float c, float d) {
+  if (NT) __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4 *>(p));
+  else *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+}
+
+template <int DK, int VAR, typename T, bool STREAM>
 __global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_beta,
                                                           const float *S_in,
                                                           float *S_out, const T *__restrict__ q,
@@ -41,7 +62,7 @@ __global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_be
                                                           T *__restrict__ o) {
   constexpr int LPR = DK / 8;
   constexpr int RPP = ROWS_NT / LPR;
-  constexpr int UNROLL = 2;
+  constexpr int UNROLL = STREAM ? 8 : 2;  // streaming: up to 8 passes (all 128 rows at d = 128) in flight
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
@@ -74,8 +95,8 @@ __global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_be
     for (int u = 0; u < UNROLL; ++u) {
       const int r = r0 + u * RPP + rp;
       if (r < dv) {
-        s0[u] = *reinterpret_cast<const float4 *>(Sn + (size_t)r * DK + c0);
-        s1[u] = *reinterpret_cast<const float4 *>(Sn + (size_t)r * DK + c1);
+        s0[u] = ld_state<STREAM>(Sn + (size_t)r * DK + c0);
+        s1[u] = ld_state<STREAM>(Sn + (size_t)r * DK + c1);
         vr[u] = io<T>::ld(v, (size_t)n * dv + r);
       }
     }
@@ -100,8 +121,8 @@ __global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_be
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = a * x[j] + coef * kk[j];
-        *reinterpret_cast<float4 *>(So + (size_t)r * DK + c0) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4 *>(So + (size_t)r * DK + c1) = make_float4(x[4], x[5], x[6], x[7]);
+        st_state<STREAM>(So + (size_t)r * DK + c0, x[0], x[1], x[2], x[3]);
+        st_state<STREAM>(So + (size_t)r * DK + c1, x[4], x[5], x[6], x[7]);
         if (lr == 0) io<T>::st(o, (size_t)n * dv + r, a * pp + coef * kq);
       }
     }
@@ -231,9 +252,14 @@ template <int DK, int VAR, typename T>
 static hipError_t go_rows(int n, int dv, int has_beta, const float *S_in, float *S_out,
                           const void *q, const void *k, const void *v, const void *alpha,
                           const void *beta, void *o, hipStream_t s) {
-  hipLaunchKernelGGL((decode_rows_kernel<DK, VAR, T>), dim3(n), dim3(ROWS_NT), 0, s, dv, has_beta, S_in,
-                     S_out, (const T *)q, (const T *)k, (const T *)v, (const T *)alpha,
-                     (const T *)beta, (T *)o);
+  if ((size_t)n * dv * DK * sizeof(float) > STREAM_BYTES)
+    hipLaunchKernelGGL((decode_rows_kernel<DK, VAR, T, true>), dim3(n), dim3(ROWS_NT), 0, s, dv, has_beta, S_in,
+                       S_out, (const T *)q, (const T *)k, (const T *)v, (const T *)alpha, (const T *)beta,
+                       (T *)o);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<DK, VAR, T, false>), dim3(n), dim3(ROWS_NT), 0, s, dv, has_beta, S_in,
+                       S_out, (const T *)q, (const T *)k, (const T *)v, (const T *)alpha, (const T *)beta,
+                       (T *)o);
   return hipGetLastError();
 }
 

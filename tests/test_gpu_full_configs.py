@@ -102,3 +102,28 @@ def test_cfg4_decode_1024_steps_sampled_states(la):
     assert_close(outs_b.transpose(0, 1)[None], oo_b[:, :, 64:], 2e-2, what="cfg4 BASED o, every step")
     assert_close(s[idx][None], so_b, 2e-2, what="cfg4 BASED final s")
     assert_close(z[idx][None], zo_b, 2e-2, what="cfg4 BASED final z")
+
+
+@pytest.mark.parametrize("D,N", [(128, 6144), (256, 2048)])
+def test_decode_streaming_state_sets(la, D, N):
+    """State sets larger than the Infinity Cache (384 and 512 MiB) take the streaming decode
+    kernel (non-temporal accesses, four passes in flight): o at every one of 16 steps and
+    the final state, for 16 sampled states, against the oracle run over the same tokens."""
+    steps = 16
+    idx = torch.linspace(0, N - 1, 16).long().tolist()
+    S = synth.gdn_state((N, D, D), seed=15, device=DEV)
+    S_ref0 = S[idx].clone()
+    g = synth.gdn_decode_inputs(steps, N, D, D, dtype=torch.bfloat16, seed=15, device=DEV)
+    outs = torch.empty((steps, len(idx), D), dtype=torch.bfloat16, device=DEV)
+    o = torch.empty((N, D), dtype=torch.bfloat16, device=DEV)
+    print(f"[decode streaming] d={D} N={N} ({N * D * D * 4 >> 20} MiB)", flush=True)
+    for t in range(steps):
+        la.decode_step("gated_delta", S, g["q"][t], g["k"][t], g["v"][t], g["alpha"][t],
+                       g["beta"][t], S_out=S, o=o)
+        outs[t] = o[idx]
+    torch.cuda.synchronize()
+    tq = lambda n: g[n][:, idx].transpose(0, 1).contiguous()[None]
+    oo, So, _ = oracle.prefill("gated_delta", tq("q"), tq("k"), tq("v"), tq("alpha"), tq("beta"),
+                               S0=S_ref0[None])
+    assert_close(outs.transpose(0, 1)[None], oo, 2e-2, what="streaming decode o, every step")
+    assert_close(S[idx][None], So, 2e-2, what="streaming decode final state")
