@@ -1324,7 +1324,8 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   using namespace gdn;
   if (!chunk_width(d_k, d_v)) {  // other widths: the token-recurrent kernel (fp32 arithmetic)
     if (!(pass_mask & PASS_REPLAY)) return hipSuccess;
-    return launch_recurrent_rows(variant, T_BF16, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+    return launch_recurrent_rows(variant, T_BF16, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, nullptr, 0,
+                                 s);
   }
   const bool delta = variant == V_GATED_DELTA;
   const Plan p = make_plan(delta, B, H, T, d_k, ws_cap);

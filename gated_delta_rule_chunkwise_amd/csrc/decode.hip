@@ -30,7 +30,7 @@ namespace la {
 // and lower occupancy): about 10% more bandwidth for 128 x 128 states.
 //
 // STREAM: the state set is larger than the 256 MB Infinity Cache can keep between steps,
-// so every step streams it from HBM: eight passes in flight and non-temporal loads and
+// so every step streams it from HBM: 128 rows in flight and non-temporal loads and
 // stores (which do not displace other data from the caches).  Measured on 128 x 128 states:
 // 5.8 TB/s against 5.2 TB/s for the cached form once the set exceeds ~384 MiB; below that
 // the cached form is faster (6.2-6.4 TB/s at 256 MiB, where part of the set stays cached).
@@ -51,8 +51,12 @@ __device__ __forceinline__ void st_state(float *p, float a, float b, float c, fl
   else *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
 }
 
+// Threads per state: the streaming form at d = 256 keeps a whole 256 KB state in flight with
+// 1024 threads (four passes of 64 rows): 5.8 TB/s on 512 MiB of states against 5.6 with 512.
+template <int DK, bool STREAM> constexpr int rows_threads() { return (STREAM && DK == 256) ? 1024 : ROWS_NT; }
+
 template <int DK, int VAR, typename T, bool STREAM>
-__global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_beta,
+__global__ __launch_bounds__((rows_threads<DK, STREAM>())) void decode_rows_kernel(int dv, int has_beta,
                                                           const float *S_in,
                                                           float *S_out, const T *__restrict__ q,
                                                           const T *__restrict__ k,
@@ -61,8 +65,9 @@ __global__ __launch_bounds__(ROWS_NT) void decode_rows_kernel(int dv, int has_be
                                                           const T *__restrict__ beta,
                                                           T *__restrict__ o) {
   constexpr int LPR = DK / 8;
-  constexpr int RPP = ROWS_NT / LPR;
-  constexpr int UNROLL = STREAM ? 8 : 2;  // streaming: up to 8 passes (all 128 rows at d = 128) in flight
+  constexpr int RPP = rows_threads<DK, STREAM>() / LPR;
+  // streaming: 128 rows in flight (all of a 128 x 128 state; half of a 256 x 256 one)
+  constexpr int UNROLL = STREAM ? (DK == 256 ? 4 : 8) : 2;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
@@ -253,7 +258,8 @@ static hipError_t go_rows(int n, int dv, int has_beta, const float *S_in, float 
                           const void *q, const void *k, const void *v, const void *alpha,
                           const void *beta, void *o, hipStream_t s) {
   if ((size_t)n * dv * DK * sizeof(float) > STREAM_BYTES)
-    hipLaunchKernelGGL((decode_rows_kernel<DK, VAR, T, true>), dim3(n), dim3(ROWS_NT), 0, s, dv, has_beta, S_in,
+    hipLaunchKernelGGL((decode_rows_kernel<DK, VAR, T, true>), dim3(n), dim3(rows_threads<DK, true>()), 0, s, dv,
+                       has_beta, S_in,
                        S_out, (const T *)q, (const T *)k, (const T *)v, (const T *)alpha, (const T *)beta,
                        (T *)o);
   else

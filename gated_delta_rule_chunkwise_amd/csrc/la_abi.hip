@@ -84,7 +84,11 @@ int check_prefill_shape(int variant, int dtype, int B, int H, int64_t T, int dk,
 // Workspace bytes of a prefill whose segment plan keeps them within `cap` (SIZE_MAX: the
 // plan depends on the shape alone); more than `cap` when even one segment needs more.
 size_t prefill_ws(int variant, int dtype, int B, int H, int64_t T, int dk, int dv, size_t cap = SIZE_MAX) {
-  if (dtype != LA_BF16 || T == 0) return 0;
+  if (T == 0) return 0;
+  if (dtype != LA_BF16) {  // fp32: only the short chunk form uses one (without it, another fp32 path runs)
+    const size_t need = is_based(variant) ? 0 : fp32_chunk_workspace_bytes(variant, B, H, T, dk, dv);
+    return need <= cap ? need : 0;
+  }
   if (is_based(variant)) return based_chunk_workspace_bytes(B, H, T, cap);
   return chunk_workspace_bytes(variant, B, H, T, dk, dv, cap);
 }
@@ -224,7 +228,8 @@ static int prefill_impl(int pass_mask, int variant, int dtype, int batch, int he
     e = launch_chunk_prefill(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, workspace,
                              ws_cap, pass_mask, s);
   } else if (pass_mask & PASS_REPLAY) {
-    e = launch_recurrent_rows(variant, dtype, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+    e = launch_recurrent_rows(variant, dtype, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T,
+                              need_ws ? workspace : nullptr, need_ws, s);
   }
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

@@ -21,10 +21,14 @@ hipError_t launch_decode_based(int dtype, bool compact, int n, float eps, const 
                                const void *k, const void *v, void *o, hipStream_t s);
 
 // recurrent.hip (token-recurrent prefill; fp32 path)
+// fp32 ADDITIVE / GATED problems of at most 2048 tokens (and small B H) take a chunk form
+// whose per-chunk state sums live in the workspace: it runs when the workspace holds
+// fp32_chunk_workspace_bytes() (non-zero), else the token walk or the attention form runs.
+size_t fp32_chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v);
 hipError_t launch_recurrent_rows(int variant, int dtype, int B, int H, int64_t T, int d_k, int d_v,
                                  const void *q, const void *k, const void *v, const void *alpha,
                                  const void *beta, const float *S0, void *o, float *S_T,
-                                 hipStream_t s);
+                                 void *workspace, size_t ws_bytes, hipStream_t s);
 hipError_t launch_recurrent_based(int dtype, bool compact, int B, int H, int64_t T, float eps,
                                   const void *q, const void *k, const void *v, const float *s0,
                                   const float *z0, void *o, float *s_T, float *z_T, hipStream_t s);

@@ -377,6 +377,249 @@ __global__ __launch_bounds__(QNT) void quad_state_kernel(int64_t T_len, int dv, 
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// fp32 chunk form for short ADDITIVE / GATED prefills (fp32 inputs): Eq. (1) unrolled over
+// chunks of 64 tokens (the BASED notes' Sec. 2.5 block form U_b = (M_b . Q K^T) V_b + Q S_{<b}
+// with the scalar gate, derived from Eq. (1) of "History Replays Itself", Sec. 2):
+//   g_t = in-chunk prefix of log alpha, G_c = g at the chunk's end, w_j = beta_j e^{G_c - g_j}
+//   B_c = V^T diag(w) K                      (the chunk's contribution to the next state)
+//   S_{c+1} = e^{G_c} S_c + B_c,  S_0 = S0
+//   O_c = diag(e^{g}) Q S_c^T + (P . Q K^T . beta) V,  P_tj = e^{g_t - g_j} (j <= t)
+// Every product runs on fp32 MFMA (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulate),
+// so the path keeps fp32 accuracy.  Two launches: every chunk's B_c and G_c in parallel
+// (fchunk_sum_kernel), then every chunk's start state as an elementwise prefix of the
+// earlier B_j, held in registers in the operand layout of the Q S^T product, and the
+// chunk's outputs (fchunk_out_kernel); the last chunk also writes S_T.  The first kernel
+// also copies S0 into the workspace, so that S_T may be S0's own buffer.  The prefix re-reads
+// up to nch - 1 sums per chunk, so the form serves short sequences (T <= FC_MAX_T).
+//
+// fp32 MFMA 16x16x4 layout: lane l supplies A[i][k] and B[k][j] with i = j = l % 16,
+// k = l / 16; the accumulator lane l holds C[4 (l / 16) + e][l % 16], e = 0..3.
+// B_c is stored so that lane (kk, j) of the wave owning value rows 16 ci .. 16 ci + 15 reads
+// S[16 ci + j][4 s + kk] at ((ci (DK / 4) + s) 4 + kk) 16 + j: one coalesced 256-byte load
+// per s.
+constexpr int FC = 64, FC_MAX_T = 2048, FC_NT = 256, FC_MAXDV = 128;
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (fixed order).
+__device__ __forceinline__ float fc_wave_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Rows [0, n) of a [FC][ld] fp32 LDS tile from rows of `w` floats `stride` apart (rows past
+// n zero); w a multiple of 4.
+__device__ __forceinline__ void fc_tile(float *dst, int ld, const float *src, size_t stride, int w, int n, int tid) {
+  const int w4 = w / 4;
+  for (int i = tid; i < FC * w4; i += FC_NT) {
+    const int r = i / w4, c4 = 4 * (i % w4);
+    const float4 x = r < n ? *reinterpret_cast<const float4 *>(src + (size_t)r * stride + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4 *>(dst + r * ld + c4) = x;
+  }
+}
+
+template <int DK, int VAR>
+__global__ __launch_bounds__(FC_NT) void fchunk_sum_kernel(int64_t T_len, int dv, int has_beta,
+                                                           const float *__restrict__ k, const float *__restrict__ v,
+                                                           const float *__restrict__ alpha,
+                                                           const float *__restrict__ beta, const float *S0,
+                                                           float *__restrict__ bsum, float *__restrict__ gsum) {
+  constexpr int LK = DK + 4, LV = FC_MAXDV + 4;
+  __shared__ __attribute__((aligned(16))) float sK[FC * LK];
+  __shared__ __attribute__((aligned(16))) float sV[FC * LV];
+  __shared__ float sW[FC];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i16 = lane & 15, g4 = lane >> 4;
+  const int c = blockIdx.x, nch = gridDim.x;
+  const size_t bh = blockIdx.y;
+  const int64_t t0 = (int64_t)c * FC;
+  const int n = (int)((T_len - t0) < FC ? (T_len - t0) : FC);
+  fc_tile(sK, LK, k + (bh * T_len + t0) * DK, DK, DK, n, tid);
+  fc_tile(sV, LV, v + (bh * T_len + t0) * dv, dv, dv, n, tid);
+  if (wave == 0) {
+    const size_t at = bh * T_len + t0 + lane;
+    const float la = (VAR == V_GATED && lane < n) ? __logf(alpha[at]) : 0.0f;
+    const float gt = fc_wave_scan(la, lane);
+    const float G = __shfl(gt, 63, 64);
+    const float b = lane < n ? ((VAR == V_GATED && has_beta) ? beta[at] : 1.0f) : 0.0f;
+    sW[lane] = VAR == V_GATED ? b * __expf(G - gt) : b;
+    if (lane == 0) gsum[bh * nch + c] = G;
+  }
+  __syncthreads();
+  // slab 0 of (b, h): the start state in the same layout, so that the output kernel never
+  // reads S0 (S_T, which its last chunk writes, may be S0's buffer)
+  const int ndi = DK / 16, nci = dv / 16;
+  if (c == 0) {
+    float *d0 = bsum + bh * (nch + 1) * (size_t)dv * DK;
+    for (int ci = wave; ci < nci; ci += 4)
+      for (int s = 0; s < DK / 4; ++s)
+        d0[(ci * (DK / 4) + s) * 64 + lane] = S0 ? S0[(bh * dv + 16 * ci + i16) * DK + 4 * s + g4] : 0.0f;
+  }
+  // tiles of B_c^T: (di, ci), k = tokens; lane (g4, i16) ends with B_c[16 ci + i16][16 di + 4 g4 + e]
+  float *dst = bsum + (bh * (nch + 1) + c + 1) * (size_t)dv * DK;
+  for (int tile = wave; tile < ndi * nci; tile += 4) {
+    const int di = tile % ndi, ci = tile / ndi;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < FC / 4; ++s) {
+      const int j = 4 * s + g4;
+      acc = mfma_f32(sK[j * LK + 16 * di + i16], sW[j] * sV[j * LV + 16 * ci + i16], acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[((ci * (DK / 4) + 4 * di + g4) * 4 + e) * 16 + i16] = acc[e];
+  }
+}
+
+template <int DK, int VAR>
+__global__ __launch_bounds__(FC_NT) void fchunk_out_kernel(int64_t T_len, int dv, int has_beta,
+                                                           const float *__restrict__ q, const float *__restrict__ k,
+                                                           const float *__restrict__ v, const float *__restrict__ alpha,
+                                                           const float *__restrict__ beta,
+                                                           const float *__restrict__ bsum,
+                                                           const float *__restrict__ gsum, float *__restrict__ o,
+                                                           float *S_T) {
+  constexpr int LK = DK + 4, LV = FC_MAXDV + 4, LA = FC + 4, NS = DK / 4;
+  constexpr int NCI = FC_MAXDV / 16 / 4;  // value-row tiles per wave, at most
+  __shared__ __attribute__((aligned(16))) float sQ[FC * LK];
+  __shared__ __attribute__((aligned(16))) float sK[FC * LK];
+  __shared__ __attribute__((aligned(16))) float sV[FC * LV];
+  __shared__ __attribute__((aligned(16))) float sA[FC * LA];
+  __shared__ float sg[FC], sb[FC];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, i16 = lane & 15, g4 = lane >> 4;
+  const int c = blockIdx.x, nch = gridDim.x;
+  const size_t bh = blockIdx.y;
+  const int64_t t0 = (int64_t)c * FC;
+  const int n = (int)((T_len - t0) < FC ? (T_len - t0) : FC);
+  const int nci = dv / 16;
+  fc_tile(sQ, LK, q + (bh * T_len + t0) * DK, DK, DK, n, tid);
+  fc_tile(sK, LK, k + (bh * T_len + t0) * DK, DK, DK, n, tid);
+  fc_tile(sV, LV, v + (bh * T_len + t0) * dv, dv, dv, n, tid);
+  if (wave == 0) {
+    const size_t at = bh * T_len + t0 + lane;
+    const float la = (VAR == V_GATED && lane < n) ? __logf(alpha[at]) : 0.0f;
+    sg[lane] = fc_wave_scan(la, lane);
+    sb[lane] = lane < n ? ((VAR == V_GATED && has_beta) ? beta[at] : 1.0f) : 0.0f;
+  }
+
+  // start state of this chunk: lane (g4, i16) of wave w keeps S[16 ci + i16][4 s + g4] for its
+  // tiles ci = w + 4 m, every s; slab 0 holds S0, slab j + 1 the sum B_j of chunk j
+  const float *slabs = bsum + bh * (nch + 1) * (size_t)dv * DK;
+  float S[NCI][NS];
+#pragma unroll
+  for (int m = 0; m < NCI; ++m) {
+    const int ci = wave + 4 * m;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) S[m][s] = ci < nci ? slabs[(ci * NS + s) * 64 + lane] : 0.0f;
+  }
+  auto accumulate = [&](int j) {  // S <- e^{G_j} S + B_j
+    const float dec = VAR == V_GATED ? __expf(gsum[bh * nch + j]) : 1.0f;
+    const float *src = slabs + (size_t)(j + 1) * dv * DK;
+#pragma unroll
+    for (int m = 0; m < NCI; ++m) {
+      const int ci = wave + 4 * m;
+      if (ci < nci) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) S[m][s] = dec * S[m][s] + src[(ci * NS + s) * 64 + lane];
+      }
+    }
+  };
+  for (int j = 0; j < c; ++j) accumulate(j);
+  __syncthreads();
+
+  // decay-masked Q K^T into LDS (tiles above the diagonal are zero)
+  for (int tile = wave; tile < 16; tile += 4) {
+    const int ti = tile / 4, tj = tile % 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        acc = mfma_f32(sQ[(16 * ti + i16) * LK + 4 * s + g4], sK[(16 * tj + i16) * LK + 4 * s + g4], acc);
+    }
+    const int jj = 16 * tj + i16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * ti + 4 * g4 + e;
+      float x = 0.0f;
+      if (tj <= ti && jj <= t) x = VAR == V_GATED ? acc[e] * sb[jj] * __expf(sg[t] - sg[jj]) : acc[e];
+      sA[t * LA + jj] = x;
+    }
+  }
+  __syncthreads();
+
+  // outputs: for each value-row tile of this wave and each token tile,
+  // O = diag(e^{g}) Q S^T + A V
+#pragma unroll
+  for (int m = 0; m < NCI; ++m) {
+    const int ci = wave + 4 * m;
+    if (ci >= nci) break;
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc = mfma_f32(sQ[(16 * ti + i16) * LK + 4 * s + g4], S[m][s], acc);
+      if (VAR == V_GATED) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= __expf(sg[16 * ti + 4 * g4 + e]);
+      }
+#pragma unroll
+      for (int s = 0; s < FC / 4; ++s)
+        acc = mfma_f32(sA[(16 * ti + i16) * LA + 4 * s + g4], sV[(4 * s + g4) * LV + 16 * ci + i16], acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ti + 4 * g4 + e;
+        if (t < n) o[(bh * T_len + t0 + t) * dv + 16 * ci + i16] = acc[e];
+      }
+    }
+  }
+
+  if (c == nch - 1 && S_T) {  // the end state: S_T = e^{G_c} S_c + B_c
+    accumulate(c);
+#pragma unroll
+    for (int m = 0; m < NCI; ++m) {
+      const int ci = wave + 4 * m;
+      if (ci < nci) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) S_T[(bh * dv + 16 * ci + i16) * DK + 4 * s + g4] = S[m][s];
+      }
+    }
+  }
+}
+
+// Whether the fp32 chunk form takes this problem: ADDITIVE or GATED, fp32, at least two
+// chunks and at most FC_MAX_T tokens, d_k in {64, 128}, d_v a multiple of 16 up to 128, and
+// small (B H nch^2 <= 4096: its chunk sums are re-read by every later chunk).
+static bool fchunk_ok(int variant, int64_t BH, int64_t T, int dk, int dv) {
+  const int64_t nch = (T + FC - 1) / FC;
+  return (variant == V_ADDITIVE || variant == V_GATED) && nch >= 2 && T <= FC_MAX_T && BH * nch * nch <= 4096 &&
+         (dk == 64 || dk == 128) && dv % 16 == 0 && dv >= 16 && dv <= FC_MAXDV;
+}
+
+size_t fp32_chunk_workspace_bytes(int variant, int B, int H, int64_t T, int d_k, int d_v) {
+  const int64_t BH = (int64_t)B * H;
+  if (!fchunk_ok(variant, BH, T, d_k, d_v)) return 0;
+  const size_t nch = (size_t)((T + FC - 1) / FC);
+  return ((size_t)BH * (nch + 1) * d_v * d_k * sizeof(float) + 255) / 256 * 256 + (size_t)BH * nch * sizeof(float);
+}
+
+template <int DK, int VAR>
+static void go_fchunk(int B, int H, int64_t T, int dv, int has_beta, const float *q, const float *k, const float *v,
+                      const float *alpha, const float *beta, const float *S0, float *o, float *S_T, void *ws,
+                      hipStream_t s) {
+  const unsigned bh = (unsigned)((int64_t)B * H), nch = (unsigned)((T + FC - 1) / FC);
+  float *bsum = (float *)ws;  // [B H][nch + 1][d_v d_k]: the start state, then every chunk's sum
+  float *gsum = (float *)((char *)ws + ((size_t)bh * (nch + 1) * dv * DK * sizeof(float) + 255) / 256 * 256);
+  hipLaunchKernelGGL((fchunk_sum_kernel<DK, VAR>), dim3(nch, bh), dim3(FC_NT), 0, s, T, dv, has_beta, k, v, alpha,
+                     beta, S0, bsum, gsum);
+  hipLaunchKernelGGL((fchunk_out_kernel<DK, VAR>), dim3(nch, bh), dim3(FC_NT), 0, s, T, dv, has_beta, q, k, v, alpha,
+                     beta, bsum, gsum, o, S_T);
+}
+
 // Whether the attention form takes this problem (fp32 inputs only): its work grows as
 // B H T^2 while the token walk's time grows as T (given enough parallel rows), so only
 // small problems: T <= QMAX_T and B H ceil(T / 64)^2 <= 4096 (one head of 4096 tokens' worth).
@@ -399,10 +642,25 @@ static void go_quad(int B, int H, int64_t T, int dv, int has_beta, const float *
 
 hipError_t launch_recurrent_rows(int variant, int dtype, int B, int H, int64_t T, int d_k, int d_v,
                                  const void *q, const void *k, const void *v, const void *alpha,
-                                 const void *beta, const float *S0, void *o, float *S_T,
-                                 hipStream_t s) {
+                                 const void *beta, const float *S0, void *o, float *S_T, void *workspace,
+                                 size_t ws_bytes, hipStream_t s) {
   if (dtype == T_BF16)
     return go_rec_dk<bf16_t>(variant, B, H, T, d_k, d_v, q, k, v, alpha, beta, S0, o, S_T, s);
+  const size_t fws = fp32_chunk_workspace_bytes(variant, B, H, T, d_k, d_v);
+  if (fws > 0 && workspace && fws <= ws_bytes) {  // short fp32 sequences: the chunk form
+    const float *fq = (const float *)q, *fk = (const float *)k, *fv = (const float *)v;
+    const float *fa = (const float *)alpha, *fb = (const float *)beta;
+    const int hb = beta != nullptr;
+    float *fo = (float *)o;
+    if (variant == V_ADDITIVE) {
+      if (d_k == 64) go_fchunk<64, V_ADDITIVE>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, fo, S_T, workspace, s);
+      else go_fchunk<128, V_ADDITIVE>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, fo, S_T, workspace, s);
+    } else {
+      if (d_k == 64) go_fchunk<64, V_GATED>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, fo, S_T, workspace, s);
+      else go_fchunk<128, V_GATED>(B, H, T, d_v, hb, fq, fk, fv, fa, fb, S0, fo, S_T, workspace, s);
+    }
+    return hipGetLastError();
+  }
   if (quad_ok(variant, (int64_t)B * H, T, d_k, d_v)) {  // short fp32 sequences without the delta term
     const float *fq = (const float *)q, *fk = (const float *)k, *fv = (const float *)v;
     const float *fa = (const float *)alpha, *fb = (const float *)beta;

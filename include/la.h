@@ -101,7 +101,8 @@ const char *la_status_string(int status);
  * workspace holds the chunked prefill's per-segment fp32 state maps and, for the gated
  * delta rule, one bf16 lower-triangular 64 x 64 transform per chunk of 64 tokens (6 KiB
  * per chunk and head: the zero blocks right of the diagonal in its first 32 rows are not
- * stored; see la_prefill_pass).
+ * stored; see la_prefill_pass); for short fp32 ADDITIVE and GATED problems, the start state
+ * and one fp32 d_v x d_k state sum per chunk.
  * Returns LA_OK and writes *bytes, or the same validation error la_prefill would give.
  */
 int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int64_t seq_len,
@@ -130,10 +131,12 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  * across segments of chunks (a three-pass segment scan: per-segment affine state maps,
  * a scan of the segment start states, then every segment replayed from its start
  * state).  fp32
- * inputs take an fp32 path (fp32 FMA throughout): ADDITIVE and GATED problems of at most 2048
- * tokens and small size (B H ceil(T/64)^2 <= 4096, d_k in {64, 128}, d_v <= 128) in the
- * masked attention form that Eq. (1) unrolls to (parallel over tokens, gate prefix sums in
- * fp64), everything else token by token.
+ * inputs take an fp32 path (fp32 products and accumulation throughout): ADDITIVE and GATED
+ * problems of 2 to 32 chunks (at most 2048 tokens, B H nch^2 <= 4096, d_k in {64, 128},
+ * d_v a multiple of 16 up to 128) in a chunk form on fp32 MFMA whose per-chunk state sums
+ * live in the workspace; other small ADDITIVE and GATED problems (T <= 2048,
+ * B H ceil(T/64)^2 <= 4096, d_v <= 128) in the masked attention form that Eq. (1) unrolls
+ * to (parallel over tokens, gate prefix sums in fp64); everything else token by token.
  *
  * Supported: bf16 -- ADDITIVE/GATED/GATED_DELTA with d_k = d_v in {64, 128, 256}
  *                    (128 and 256 chunkwise; 64 token-recurrent in fp32);

@@ -312,3 +312,22 @@ def test_prefill_in_place_state_across_segments(la, variant):
     assert torch.equal(o1, o2) and torch.equal(S1, S_io)
     if z0 is not None:
         assert torch.equal(z1, z_io)
+
+
+@pytest.mark.parametrize("variant", ["additive", "gated"])
+@pytest.mark.parametrize("T", [130, 1024])
+def test_prefill_fp32_chunk_form_in_place(la, variant, T):
+    """fp32 additive/gated prefills of 2..32 chunks run in the fp32 chunk form, whose chunks'
+    workgroups all start from S0 while the last writes S_T: in place (S_T is S0's buffer)
+    equals out of place bit for bit, and both match the oracle at the fp32 bound."""
+    B, H, dk = 1, 2, 64
+    q, k, v, a, b = _inputs(variant, B, H, T, dk, dk, torch.float32, 66)
+    S0 = synth.gdn_state((B, H, dk, dk), seed=67, device=DEV) * 0.3
+    o1, S1, _ = la.prefill(variant, q, k, v, a, b, S0=S0)
+    S_io = S0.clone()
+    o2, _, _ = la.prefill(variant, q, k, v, a, b, S0=S_io, S_T=S_io)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S_io)
+    oo, So, _ = oracle.prefill(variant, q, k, v, a, b, S0=S0)
+    assert_close(o1, oo, 1e-4, what="o")
+    assert_close(S1, So, 1e-4, what="S_T")
