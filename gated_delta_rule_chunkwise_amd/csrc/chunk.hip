@@ -50,25 +50,31 @@ namespace la {
 namespace gdn {
 
 constexpr int C = 64;       // tokens per chunk
-constexpr int WROWS = 128;  // value rows (rows of S) carried by one state workgroup
 // Keeps the scheduler from hoisting every operand load of a fully unrolled loop (which
 // would raise register pressure past what two workgroups per CU allow).
 #define LA_FENCE() __builtin_amdgcn_sched_barrier(0)
-constexpr int LDV = WROWS + 16;  // bf16 V tile [C][WROWS]: a workgroup's value columns (288-byte rows)
 constexpr int LDA = C + 16;      // bf16 [C][C]: decay-masked Q K^T, rows t, k-ordered columns
 constexpr int LDT = C + 16;      // bf16 [C][C]: T diag(beta), rows t, k-ordered columns
 
-// Geometry per key width (d_k = d_v).  A state workgroup carries WROWS rows of S over all
-// d_k keys, in registers: NW waves of 16 NCT rows each (NCT 16-row column tiles per wave).
-//   d = 128: 4 waves x 32 rows, one workgroup per (b, h, segment), two workgroups per CU
-//   d = 256: 8 waves x 16 rows (the same 64 state registers per lane), two row blocks per
-//            (b, h, segment); K and Q tiles of 34 KB each leave room for one workgroup per CU
+// Geometry per key width (d_k = d_v).  A replay workgroup carries all d_v rows of S over
+// all d_k keys, in registers: NW waves of 16 NCT rows each (NCT 16-row column tiles per
+// wave, so that every K or Q operand read from LDS feeds NCT products).
+//   d = 128: 4 waves x 32 rows (64 state registers per lane), two workgroups per CU
+//   d = 256: 8 waves x 32 rows (128 state registers per lane, two waves per SIMD), one
+//            workgroup per CU (K, Q and V tiles of 34 KB each).  Against 16-row waves in two
+//            row-block workgroups, each state row reads half the LDS operand bytes.
 // K, Q tiles are [C][DK + 16] (the 16-element padding gives 2-row bank offsets as at 128).
 template <int DK_> struct Geo;
 template <> struct Geo<128> { static constexpr int DK = 128, DV = 128, NW = 4, NCT = 2; };
-template <> struct Geo<256> { static constexpr int DK = 256, DV = 256, NW = 8, NCT = 1; };
-// state-carrying waves of a map workgroup (one more wave issues the loads)
-template <bool DELTA, int DK> constexpr int map_waves() { return (DELTA || Geo<DK>::NCT == 1) ? 8 : 4; }
+template <> struct Geo<256> { static constexpr int DK = 256, DV = 256, NW = 8, NCT = 2; };
+// Map workgroups: NCT as in the replay; 8 state waves (4 for the scalar-decay maps at
+// d = 128).  At d = 128 one more wave issues every load (three waves per SIMD, 170
+// registers each); at d = 256 the 128 state registers per lane need two waves per SIMD
+// (256 registers), so the state waves issue the loads themselves.
+template <int DK_> struct MapGeo { static constexpr int NCT = Geo<DK_>::NCT; };
+template <bool DELTA, int DK> constexpr int map_waves() { return (DELTA || DK == 256) ? 8 : 4; }
+template <int DK> constexpr bool map_loader() { return DK != 256; }
+template <bool DELTA, int DK> constexpr int map_threads() { return (map_waves<DELTA, DK>() + (map_loader<DK>() ? 1 : 0)) * 64; }
 
 // A stored transform, T diag(beta) in bf16, row-major in the MFMA k order: rows 0..31 keep
 // only their first 32 positions (the blocks right of the diagonal are zero), rows 32..63 all
@@ -510,12 +516,14 @@ __device__ __forceinline__ float wave_gates(float al, float be, bool additive, f
 // B_seg rows only; a workgroup carries NWT * RPW of them and loads the V columns of its B
 // rows.  Delta rule: the first half of the state waves carry B rows vcol0 .., the second
 // half the M rows with the same indices (d = 128: all 128 of each in one workgroup; d = 256:
-// 64 of each in each of four), so the workgroups of a segment do equal work, keep pace and
+// 128 of each in each of two), so the workgroups of a segment do equal work, keep pace and
 // share each K tile through L2.
 template <bool DELTA, int DK>
-__global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kernel(const Args a) {
-  constexpr int DV = Geo<DK>::DV, NCT = Geo<DK>::NCT, RPW = 16 * NCT, LDK = DK + 16;
-  constexpr int NWT = map_waves<DELTA, DK>();  // state-carrying waves; wave NWT issues every load
+__global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 : 2)) void map_kernel(const Args a) {
+  constexpr int DV = Geo<DK>::DV, NCT = MapGeo<DK>::NCT, RPW = 16 * NCT, LDK = DK + 16;
+  constexpr int NWT = map_waves<DELTA, DK>();  // state-carrying waves; wave NWT (if any) issues every load
+  constexpr bool LOADER = map_loader<DK>();
+  constexpr int NIW = LOADER ? 1 : NWT;        // waves that share the issue of a chunk's loads
   constexpr int MAPROWS = DELTA ? DV + DK : DV;
   constexpr int MWR = NWT * RPW;        // map rows per workgroup
   constexpr int NMB = MAPROWS / MWR;    // workgroups per segment
@@ -556,34 +564,36 @@ __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kern
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
   float gseg = 0.0f;
 
-  // chunk ci's tiles and raw gate values into one LDS copy, all issued by the loader wave
-  auto issue = [&](int ci, bf16_t *dK, bf16_t *dV, bf16_t *dT, uint32_t *dG) {
+  // chunk ci's tiles and raw gate values into one LDS copy, issued by the loader wave or
+  // shared by the state waves (ln: the lane index, an opaque copy inside the chunk loop)
+  auto issue = [&](int ci, bf16_t *dK, bf16_t *dV, bf16_t *dT, uint32_t *dG, int ln) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<DK * 2, LDK * 2, C, 1, true>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, 0, lane);
-    dma_tile<VW * 2, LDVM * 2, C, 1, true, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
-                                                   (unsigned char *)dV, 0, lane);
+    const int iw = LOADER ? 0 : wave;
+    dma_tile<DK * 2, LDK * 2, C, NIW, true>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, iw, ln);
+    dma_tile<VW * 2, LDVM * 2, C, NIW, true, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
+                                                     (unsigned char *)dV, iw, ln);
     if (DELTA)
-      dma_tb<1, true>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2), (unsigned char *)dT, 0,
-                lane);
-    if (!additive) lds_dma2<true>(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(dG));
-    if (use_beta) lds_dma2<true>(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(dG + C));
+      dma_tb<NIW, true>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2), (unsigned char *)dT,
+                        iw, ln);
+    if (!additive && (LOADER || wave == 0)) lds_dma2<true>(rsrc_words(a.alpha + rb, n * 2), 2u * ln, lds_addr(dG));
+    if (use_beta && (LOADER || wave == NIW - 1)) lds_dma2<true>(rsrc_words(a.beta + rb, n * 2), 2u * ln, lds_addr(dG + C));
   };
 
-  if (wave == NWT) {
+  if (LOADER && wave == NWT) {
     // The loader wave: chunk ci + 1 streams into one LDS copy while the state waves work
     // on chunk ci in the other; it waits for its loads before each barrier, so after the
     // barrier the chunk has landed for every wave.
-    if (nchunks > 0) issue(0, sK0, sV0, sT0, sGraw[0][0]);
+    if (nchunks > 0) issue(0, sK0, sV0, sT0, sGraw[0][0], lane);
     for (int ci = 0; ci < nchunks; ci += 2) {
       lds_dma_wait();
       __syncthreads();
-      if (ci + 1 < nchunks) issue(ci + 1, sK1, sV1, sT1, sGraw[1][0]);
+      if (ci + 1 < nchunks) issue(ci + 1, sK1, sV1, sT1, sGraw[1][0], lane);
       if (ci + 1 < nchunks) {
         lds_dma_wait();
         __syncthreads();
-        if (ci + 2 < nchunks) issue(ci + 2, sK0, sV0, sT0, sGraw[0][0]);
+        if (ci + 2 < nchunks) issue(ci + 2, sK0, sV0, sT0, sGraw[0][0], lane);
       }
     }
     return;
@@ -718,14 +728,27 @@ __global__ __launch_bounds__((map_waves<DELTA, DK>() + 1) * 64, 3) void map_kern
     }
   };
 
-  // Two LDS copies: chunk ci + 1 streams into one (issued by the loader wave) while chunk
-  // ci is processed from the other; one barrier per chunk.
+  // Two LDS copies: chunk ci + 1 streams into one (issued by the loader wave, or by the
+  // state waves right after the barrier) while chunk ci is processed from the other; one
+  // barrier per chunk.
+  auto issue_next = [&](int ci, bf16_t *dK, bf16_t *dV, bf16_t *dT, uint32_t *dG) {
+    if (!LOADER && ci < nchunks) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      issue(ci, dK, dV, dT, dG, ln);
+    }
+  };
+  if (!LOADER && nchunks > 0) issue(0, sK0, sV0, sT0, sGraw[0][0], lane);
   for (int ci = 0; ci < nchunks; ci += 2) {
+    if (!LOADER) lds_dma_wait();
     __syncthreads();  // copy 0 holds chunk ci; every wave is done with copy 1
+    issue_next(ci + 1, sK1, sV1, sT1, sGraw[1][0]);
     const float gC0 = gates(ci, sGraw[0][0]);
     step(sK0, sV0, sT0, gC0);
     if (ci + 1 < nchunks) {
+      if (!LOADER) lds_dma_wait();
       __syncthreads();  // copy 1 holds chunk ci + 1; every wave is done with copy 0
+      issue_next(ci + 2, sK0, sV0, sT0, sGraw[0][0]);
       const float gC1 = gates(ci + 1, sGraw[1][0]);
       step(sK1, sV1, sT1, gC1);
     }
@@ -883,9 +906,10 @@ __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
 template <bool DELTA, int DK>
 __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args a) {
   constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NCT = Geo<DK>::NCT, RPW = 16 * NCT, LDK = DK + 16;
-  constexpr int NRB = DV / WROWS;      // row blocks (workgroups) per segment
+  constexpr int ROWS = NW * RPW, LDVR = ROWS + 16;  // state rows of a workgroup; its V tile's row stride
+  constexpr int NRB = DV / ROWS;       // row blocks (workgroups) per segment
   constexpr int NIT = 4 * (DK / 32);   // (token tile, key step) pairs of a K S^T / Q S^T product
-  __shared__ __attribute__((aligned(16))) bf16_t sR0[C * LDK], sR1[C * LDK], sV[C * LDV];
+  __shared__ __attribute__((aligned(16))) bf16_t sR0[C * LDK], sR1[C * LDK], sV[C * LDVR];
   __shared__ __attribute__((aligned(16))) bf16_t sT[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];
   __shared__ __attribute__((aligned(16))) float sGw[NW][4 * C];
@@ -897,7 +921,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   if (NRB > 1 && seg >= a.nseg) return;  // (whole workgroup) past the last segment
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
-  const int vcol0 = rblk * WROWS;       // first value row (V / O column) of this workgroup
+  const int vcol0 = rblk * ROWS;        // first value row (V / O column) of this workgroup
   const int row0 = vcol0 + wave * RPW;  // first state row owned by this wave
   const bool additive = a.variant == V_ADDITIVE;
   const bool use_beta = a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta);
@@ -925,31 +949,31 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
 
-  // chunk ci's V and TB tiles
-  auto issue_vt = [&](int ci) {
+  // chunk ci's V and TB tiles (ln: the lane index, an opaque per-chunk copy in the loop)
+  auto issue_vt = [&](int ci, int ln) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<WROWS * 2, LDV * 2, C, NW, false, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
-                                                       (unsigned char *)sV, wave, lane);
+    dma_tile<ROWS * 2, LDVR * 2, C, NW, false, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
+                                                       (unsigned char *)sV, wave, ln);
     if (DELTA)
       dma_tb<NW, false>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
-                 (unsigned char *)sT, wave, lane);
+                 (unsigned char *)sT, wave, ln);
   };
   // chunk ci's K tile (into dK) and raw gate values
-  auto issue_kg = [&](int ci, bf16_t *dK) {
+  auto issue_kg = [&](int ci, bf16_t *dK, int ln) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<DK * 2, LDK * 2, C, NW, false>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, lane);
-    if (wave == 0 && !additive) lds_dma2<false>(rsrc_words(a.alpha + rb, n * 2), 2u * lane, lds_addr(sGraw[0]));
-    if (wave == 1 && use_beta) lds_dma2<false>(rsrc_words(a.beta + rb, n * 2), 2u * lane, lds_addr(sGraw[1]));
+    dma_tile<DK * 2, LDK * 2, C, NW, false>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, ln);
+    if (wave == 0 && !additive) lds_dma2<false>(rsrc_words(a.alpha + rb, n * 2), 2u * ln, lds_addr(sGraw[0]));
+    if (wave == 1 && use_beta) lds_dma2<false>(rsrc_words(a.beta + rb, n * 2), 2u * ln, lds_addr(sGraw[1]));
   };
-  auto issue_q = [&](int ci, bf16_t *dQ) {
+  auto issue_q = [&](int ci, bf16_t *dQ, int ln) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     dma_tile<DK * 2, LDK * 2, C, NW, false>(rsrc_words(a.q + (bh * (size_t)T + t0) * DK, n * DK * 2), (unsigned char *)dQ,
-                                     wave, lane);
+                                     wave, ln);
   };
   // gates of chunk ci from the raw values (alpha = 1, beta = 0 past the sequence end)
   auto gates = [&](int ci) {
@@ -975,11 +999,12 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     vm_wait<4>();
     lds_barrier();  // ... for every wave; every wave is done with chunk ci - 1
     gates(ci);
-    if (ci > 0) issue_q(ci, sQ);  // (chunk 0's Q was issued with its K)
-    // An opaque copy of the lane index: LDS addresses derived from it are recomputed per
-    // chunk (a few integer ops) instead of occupying registers for the whole kernel.
+    // An opaque copy of the lane index: LDS addresses and load offsets derived from it are
+    // recomputed per chunk (a few integer ops) instead of occupying registers for the whole
+    // kernel.
     int lane_v = lane;
     asm volatile("" : "+v"(lane_v));
+    if (ci > 0) issue_q(ci, sQ, lane_v);  // (chunk 0's Q was issued with its K)
     const int l16 = lane_v & 15, g = lane_v >> 4;
 
     // ---- phase 1: U on this wave's rows, as operands with k = tokens (ufr), and with the
@@ -1022,7 +1047,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
 #pragma unroll
           for (int c = 0; c < NCT; ++c) {
             f32x4 y0 = -(ga * ks[2 * s][c]), y1 = -(gb * ks[2 * s + 1][c]);
-            const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s, lane_v);
+            const bf16x8 vf = vrow_frag<NCT>(sV, LDVR, row0 - vcol0, c, s, lane_v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               y0[e] += (float)vf[e];
@@ -1055,7 +1080,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
           const f32x4 b0 = ld4(gw + 192 + 32 * s2 + 4 * g), b1 = ld4(gw + 192 + 32 * s2 + 16 + 4 * g);
 #pragma unroll
           for (int c = 0; c < NCT; ++c) {
-            const bf16x8 vf = vrow_frag<NCT>(sV, LDV, row0 - vcol0, c, s2, lane_v);
+            const bf16x8 vf = vrow_frag<NCT>(sV, LDVR, row0 - vcol0, c, s2, lane_v);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               U[2 * s2][c][e] = (float)vf[e] * b0[e];
@@ -1077,7 +1102,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     }
     lds_dma_wait();
     lds_barrier();  // Q of chunk ci has landed; V and TB of chunk ci are no longer read
-    if (more) issue_vt(ci + 1);
+    if (more) issue_vt(ci + 1, lane_v);
 
     // ---- phase 2: decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the
     // waves, each computed as its transpose K Q^T: lane (g, l16) holds A[t][j] for token
@@ -1113,6 +1138,13 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int c = 0; c < NCT; ++c) O[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (DK == 256) {
+      // the state packed for phase 1 is packed again here rather than kept (64 registers)
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) asm volatile("" : "+v"(st[m][c]));
+    }
     {
 #define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
       bf16x8 qb[3], sfr[NCT];
@@ -1133,7 +1165,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
 #undef LA_QF
     }
     lds_barrier();  // every wave's A tiles are written; Q of chunk ci is no longer read
-    if (more) issue_kg(ci + 1, sQ);
+    if (more) issue_kg(ci + 1, sQ, lane_v);
 
     // ---- phase 3: O = diag(gamma) S Q^T + U^T A^T, stored straight from the tiles: with
     // both tiles, eight consecutive outputs of one token (16 bytes; rows past the chunk are
@@ -1191,9 +1223,9 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   };
 
   if (nchunks > 0) {
-    issue_vt(0);
-    issue_kg(0, sR0);
-    issue_q(0, sR1);
+    issue_vt(0, lane);
+    issue_kg(0, sR0, lane);
+    issue_q(0, sR1, lane);
   }
   for (int ci = 0; ci < nchunks; ci += 2) {
     step(ci, sR0, sR1);
@@ -1254,15 +1286,14 @@ WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d, const Plan &p) {
 }
 
 // Segments per (b, h): one full round of replay workgroups, i.e. as many as the chip holds
-// at once (two per CU at d = 128, one at d = 256, whose workgroups are twice as wide; state
-// workgroups are row blocks of WROWS rows, so a (b, h) at d = 256 is two of them), but only
-// when the heads alone cannot fill the chip (a split costs one extra pass over the keys
-// and values).  More segments leave the replay's time unchanged and lengthen the scan, a
+// at once (two per CU at d = 128, one at d = 256, whose workgroups are twice as wide), but
+// only when the heads alone cannot fill half of it (a split costs one extra pass over the
+// keys and values).  More segments leave the replay's time unchanged and lengthen the scan, a
 // chain of one dependent step per segment.  Fewer when the workspace must stay within
 // `cap` bytes.
 Plan make_plan(bool delta, int B, int H, int64_t T, int dv, size_t cap) {
   const int64_t nch = (T + C - 1) / C;
-  const int64_t units = (int64_t)B * H * (dv / WROWS);
+  const int64_t units = (int64_t)B * H;  // a replay workgroup carries a whole state
   const int64_t slots = dv == 128 ? 512 : 256;
   Plan p = plan_of(nch, units < 128 ? (slots + units - 1) / units : 1);
   while (p.nseg > 1 && ws_layout(delta, B, H, T, dv, p).total > cap) p = plan_of(nch, p.nseg / 2);
@@ -1276,7 +1307,7 @@ unsigned seg_grid(int nsegs, int NB) { return NB == 1 ? (unsigned)nsegs : (unsig
 
 template <int DK>
 void launch_passes(const Args &a, bool delta, int pass_mask, hipStream_t s) {
-  constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NRB = DV / WROWS;
+  constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NRB = DV / (NW * 16 * Geo<DK>::NCT);
   const int B = a.B, H = a.H;
   if (delta && (pass_mask & PASS_TRANSFORM)) {
     const int64_t chunks = (int64_t)B * H * a.nch;
@@ -1285,11 +1316,13 @@ void launch_passes(const Args &a, bool delta, int pass_mask, hipStream_t s) {
   if (a.nseg > 1 && (pass_mask & PASS_MAPS)) {
     // every segment but the last (whose end state only the replay needs)
     if (delta) {
-      constexpr int NWT = map_waves<true, DK>(), NMB = (DV + DK) / (NWT * 16 * Geo<DK>::NCT);
-      hipLaunchKernelGGL((map_kernel<true, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3((NWT + 1) * 64), 0, s, a);
+      constexpr int NWT = map_waves<true, DK>(), NMB = (DV + DK) / (NWT * 16 * MapGeo<DK>::NCT);
+      hipLaunchKernelGGL((map_kernel<true, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3(map_threads<true, DK>()), 0,
+                         s, a);
     } else {
-      constexpr int NWT = map_waves<false, DK>(), NMB = DV / (NWT * 16 * Geo<DK>::NCT);
-      hipLaunchKernelGGL((map_kernel<false, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3((NWT + 1) * 64), 0, s, a);
+      constexpr int NWT = map_waves<false, DK>(), NMB = DV / (NWT * 16 * MapGeo<DK>::NCT);
+      hipLaunchKernelGGL((map_kernel<false, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3(map_threads<false, DK>()),
+                         0, s, a);
     }
   }
   if (a.nseg > 1 && (pass_mask & PASS_SCAN)) {

@@ -142,15 +142,14 @@ def test_workspace_holds_one_transform_per_chunk(lib):
 
 
 def test_width_256_plan_and_workspace(lib):
-    """d_k = d_v = 256 (bf16) takes the chunk path: a state workgroup carries 128 of a head's
-    256 value rows, so one (b, h) counts as two workgroups when the sequence is split into
-    segments, of which one round fills the chip (256 at d = 256, one per CU; 512 at d = 128,
-    two per CU): 1M tokens over 8 heads of 256 make 16 segments of 1024 chunks, over 16
-    heads of 128 32 segments of 512; the workspace holds per segment a 512 x 256 fp32 map
-    (B rows, then transition rows) and a 256 x 256 start state, and one stored transform per
-    chunk."""
+    """d_k = d_v = 256 (bf16) takes the chunk path: a replay workgroup carries a whole state
+    (eight waves of 32 value rows), and when the sequence is split into segments one round of
+    workgroups fills the chip (256 at d = 256, one per CU; 512 at d = 128, two per CU): 1M
+    tokens over 8 heads of 256 make 32 segments of 512 chunks, over 16 heads of 128 32
+    segments of 512; the workspace holds per segment a 512 x 256 fp32 map (B rows, then
+    transition rows) and a 256 x 256 start state, and one stored transform per chunk."""
     n, c = ctypes.c_int(0), ctypes.c_int(0)
-    for (H, d, plan) in ((8, 256, (16, 1024)), (16, 128, (32, 512))):
+    for (H, d, plan) in ((8, 256, (32, 512)), (16, 128, (32, 512))):
         assert lib.la_prefill_segments(la.GATED_DELTA, la.BF16, 1, H, 1 << 20, d, d, ctypes.byref(n),
                                        ctypes.byref(c)) == 0
         assert (n.value, c.value) == plan
@@ -158,12 +157,14 @@ def test_width_256_plan_and_workspace(lib):
     ws = ctypes.c_size_t(0)
     assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 1, 8, 1 << 20, 256, 256,
                                          ctypes.byref(ws)) == 0
-    bhs = 8 * 16
+    bhs = 8 * 32
     assert ws.value == up(bhs * 512 * 256 * 4) + up(bhs * 4) + up(bhs * 256 * 256 * 4) + \
         8 * 16384 * (32 * 32 + 32 * 64) * 2
-    # one segment once the row blocks fill the chip (64 heads x 2 row blocks)
-    assert lib.la_prefill_segments(la.GATED, la.BF16, 4, 16, 1000, 256, 256, ctypes.byref(n),
+    # one segment once the heads alone reach half a round (128 workgroups)
+    assert lib.la_prefill_segments(la.GATED, la.BF16, 8, 16, 1000, 256, 256, ctypes.byref(n),
                                    ctypes.byref(c)) == 0 and n.value == 1
+    assert lib.la_prefill_segments(la.GATED, la.BF16, 4, 16, 1000, 256, 256, ctypes.byref(n),
+                                   ctypes.byref(c)) == 0 and n.value == 4
     assert prefill(lib, dk=256, dv=128) == -3
 
 

@@ -79,9 +79,9 @@ def test_d256_short_sequences(la, variant, T):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_d256_single_segment_many_heads(la, variant):
-    # 64 heads x 2 row blocks fill the chip: one segment, the replay alone from S0
-    S0 = synth.gdn_state((4, 16, D, D), seed=85, device=DEV) * 0.1
-    nseg, _ = _check(la, variant, 4, 16, 64 * 2 + 7, seed=86, S0=S0, rows=[2, 127, 128, 254])
+    # 128 heads (one workgroup of all 256 state rows each): one segment, the replay alone from S0
+    S0 = synth.gdn_state((8, 16, D, D), seed=85, device=DEV) * 0.1
+    nseg, _ = _check(la, variant, 8, 16, 64 * 2 + 7, seed=86, S0=S0, rows=[2, 127, 128, 254])
     assert nseg == 1
 
 

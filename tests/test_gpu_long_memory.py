@@ -44,7 +44,7 @@ REGIMES = {
     "beta0": dict(a_range=(-8.0, -4.0), beta="zero"),
 }
 # (B, H, T) per key width: several multi-chunk segments per (b, h), ragged last chunk
-SHAPES = {128: (1, 8, 64 * 100 + 37), 256: (1, 4, 64 * 60 + 5)}
+SHAPES = {128: (1, 8, 64 * 100 + 37), 256: (1, 8, 64 * 40 + 5)}
 
 
 def _inputs(variant, B, H, T, D, seed, **regime):
