@@ -1,10 +1,11 @@
 """GPU parity of the chunkwise bf16 prefill at the gated-delta shape of the NoteBank paper's
 own backbone (8 heads of width 256 per layer, "History Replays Itself", App. C on the GDN
-configuration): d_k = d_v = 256, fp32 state 256 x 256 per head.  At this width a state
-workgroup carries 128 of a head's 256 value rows, so every (b, h, segment) is two
-workgroups, and the segment maps are 512 rows (256 B rows, 256 transition rows) split over
-four map workgroups.  Every call goes through the C ABI and is compared with the fp64
-oracle on the same seeded inputs (bound 2e-2, per (b, h) slice, max-norm relative)."""
+configuration): d_k = d_v = 256, fp32 state 256 x 256 per head.  At this width a replay
+workgroup carries a whole state (eight waves of 32 value rows), and the segment maps are
+512 rows (256 B rows, 256 transition rows) split over two map workgroups, each with half
+of the B rows and the transition rows of the same indices.  Every call goes through the C
+ABI and is compared with the fp64 oracle on the same seeded inputs (bound 2e-2, per (b, h)
+slice, max-norm relative)."""
 
 import pytest
 import torch
@@ -45,14 +46,14 @@ def _check(la, variant, B, H, T, seed, S0=None, rows=None):
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_d256_small_ragged(la, variant):
-    # 2 heads x 2 row blocks: four one-chunk segments, the last one partial
+    # 2 heads: four one-chunk segments (one per chunk), the last one partial
     nseg, _ = _check(la, variant, 1, 2, 203, seed=81)
     assert nseg == 4
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_d256_multi_chunk_segments(la, variant):
-    # 4 heads: 100 segments of 3 chunks, every value row of both row blocks sampled
+    # 4 heads: 60 segments of 5 chunks; value rows sampled from both map workgroups' halves
     nseg, sc = _check(la, variant, 1, 4, 64 * 300 - 17, seed=82, rows=[0, 101, 127, 128, 200, 255])
     assert nseg > 8 and sc > 1
 
