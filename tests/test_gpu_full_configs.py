@@ -10,7 +10,7 @@ it computes sampled outputs exactly: value rows (gated family) and value columns
   cfg4  decode, 256 x 16 states, 1024 steps, GDN + BASED -- o at every step and the
         final state, for 24 sampled states of each kind
   gated delta at the NoteBank paper's own head shape, B=1 H=8 T=1048576 d=256, bf16
-        -- 2 heads x 4 rows (both row blocks), whole T
+        -- 2 heads x 4 rows (both halves of the state), whole T
 """
 
 import numpy as np
@@ -59,8 +59,8 @@ def test_cfg3_gdn_1m_sampled(la):
 
 def test_gdn_8x256_1m_sampled(la):
     # the NoteBank paper's own GDN head shape (8 heads of width 256) at 1M tokens, in the
-    # launch configuration bench.py times (64 segments x 2 row blocks per head); sampled
-    # rows of both row blocks, whole sequence
+    # launch configuration bench.py times (32 segments per head, one replay workgroup and two
+    # map workgroups each); sampled rows from both map workgroups' halves, whole sequence
     _gdn_sampled(la, 1 << 20, [0, 7], [5, 127, 128, 250], seed=6, H=8, D=256)
 
 

@@ -44,7 +44,7 @@ REGIMES = {
     "beta0": dict(a_range=(-8.0, -4.0), beta="zero"),
 }
 # (B, H, T) per key width: several multi-chunk segments per (b, h), ragged last chunk
-SHAPES = {128: (1, 8, 64 * 100 + 37), 256: (1, 8, 64 * 40 + 5)}
+SHAPES = {128: (1, 8, 64 * 63 + 37), 256: (1, 8, 64 * 40 + 5)}
 
 
 def _inputs(variant, B, H, T, D, seed, **regime):
@@ -195,7 +195,7 @@ def _million(la, variant, D, H, heads, rows, seed, sensitive, **regime):
 
 def test_1m_delta_alpha1_pool_keys_sampled(la):
     """1M tokens x 16 heads, alpha = 1 and pooled keys: the part of S outside the keys' span
-    is carried unchanged through all 64 segments, so every transition matters."""
+    is carried unchanged through all 32 segments, so every transition matters."""
     _million(la, "gated_delta", 128, 16, [0, 9], [3, 64, 126], seed=21, sensitive=True,
              alpha_one=True, keys="pool")
 

@@ -22,8 +22,8 @@ def _gdn(B, H, T, seed):
 
 
 def test_noalloc_matches_prefill_two_calls_second_smaller(la):
-    # call 1: 16 heads x 65536 tokens.  la_prefill's workspace (64 segments) exceeds the
-    # scratch, so the no-alloc call runs fewer, longer segments
+    # call 1: 16 heads x 65536 tokens.  la_prefill's workspace (16 segments per head) exceeds
+    # the scratch, so the no-alloc call runs fewer, longer segments
     B, H, T = 1, 16, 65536
     x = _gdn(B, H, T, 31)
     S0 = synth.gdn_state((B, H, 128, 128), seed=31, device=DEV) * 0.3
