@@ -21,6 +21,12 @@ head, 1024 consecutive steps; plus the gated-delta step on a 1 GiB state set tha
 256 MB Infinity Cache cannot hold), the 8-head x 256 gated-delta shape, the NoteBank
 write/address steps, and the fp64 oracle on each configuration on the host cores.
 
+The published peaks (HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s) are the roofline
+denominators.  Beside them the run measures what the same device reaches on two plain
+library operations, a 2 GiB device-to-device copy and an 8192^3 bf16 matrix product
+(torch, i.e. the ROCm libraries), and reports the replay's rate against that copy rate
+too; the device's properties as the runtime reports them are listed with them.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
 
@@ -126,6 +132,7 @@ def main():
     ap.add_argument("--no-notebank", action="store_true")
     ap.add_argument("--no-d256", action="store_true")
     ap.add_argument("--no-small", action="store_true")
+    ap.add_argument("--no-reference-rates", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB copy (la_prefill with T = 0) so that HBM "
                          "byte counters can be scaled against a known size")
@@ -195,6 +202,10 @@ def main():
     gdn256 = None if args.no_d256 else bench_gdn256(torch, la, synth, dev, stream, timer, args.steps,
                                                     args.warmup, args.seq_len)
     notebank = None if args.no_notebank else bench_notebank(torch, la, synth, dev, stream, timer)
+    rates = None if args.no_reference_rates else bench_reference_rates(torch, dev, timer)
+    if rates is not None:
+        roofline["measured_copy_gbs"] = rates["copy"]["gbs"]
+        roofline["frac_of_measured_copy"] = round(ach / rates["copy"]["gbs"], 4) if hbm_bound else None
     cpu = None if args.no_cpu_baseline else bench_cpu(args.cpu_seconds)
 
     out = {
@@ -217,6 +228,7 @@ def main():
                     "cfg4_decode": decode},
         "gdn_d256": gdn256,
         "notebank": notebank,
+        "reference_rates": rates,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -502,6 +514,37 @@ def bench_notebank(torch, la, synth, dev, stream, timer):
             "address_votes": {"workload": f"{N} notes x {J} channels, d_rho={dr}, {nQ}-token question, R={R}",
                               "ms": stats(ms_v), "alg_flops": flops_v,
                               "fp32_vector_frac": round(flops_v / (mv * 1e-3) / (FP32_VEC_PEAK_TFLOPS * 1e12), 4)}}
+
+
+def bench_reference_rates(torch, dev, timer):
+    """What the device reaches on two plain library operations, as a check on the
+    published peaks: a 2 GiB device-to-device copy (eight times the Infinity Cache; bytes
+    read plus bytes written per second) and an 8192 x 8192 x 8192 bf16 matrix product
+    (2 * 8192^3 FLOP, contiguous operands).  Also the device's properties as the runtime
+    reports them."""
+    props = torch.cuda.get_device_properties(dev)
+    keep = ("name", "gcnArchName", "multi_processor_count", "total_memory", "L2_cache_size",
+            "max_threads_per_multi_processor", "warp_size", "clock_rate", "memory_clock_rate",
+            "memory_bus_width")
+    device = {kk: getattr(props, kk) for kk in keep if isinstance(getattr(props, kk, None), (int, str))}
+    n = 1 << 30  # bf16 elements: 2 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = timer.reps(lambda: dst.copy_(src), reps=10, warmup=2)
+    med = statistics.median(ms)
+    copy = {"bytes": 4 * n, "ms": stats(ms), "gbs": round(4 * n / (med * 1e-3) / 1e9, 1),
+            "frac_of_published_peak": round(4 * n / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    b = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    ms = timer.reps(lambda: torch.mm(a, b), reps=10, warmup=3)
+    med = statistics.median(ms)
+    gemm = {"flops": 2 * m ** 3, "ms": stats(ms), "tflops": round(2 * m ** 3 / (med * 1e-3) / 1e12, 1),
+            "frac_of_published_peak": round(2 * m ** 3 / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del a, b
+    torch.cuda.empty_cache()
+    return {"device": device, "copy": copy, "bf16_gemm": gemm}
 
 
 def bench_cpu(target_s):
