@@ -14,6 +14,11 @@ K-step bracket divided by K, and the median, minimum and maximum of the per-step
 are reported beside it.  The other configurations are timed the same way (at least five
 repetitions each).  Inputs are generated on the device before any timed region.
 
+The headline prefill is timed a second time with slow decay (gate logits U(-8, -4)
+instead of the recipe's U(-2, 4)): with the recipe's gates every segment transition decays
+to exactly zero within a chunk or two and the map pass stops carrying it, with slow decay
+it carries every transition row to the end of its segment (`prefill_slow_decay`).
+
 Also measured in the same run: the fp32 additive configuration (1 head x 1024 tokens),
 BASED prefill (B=4, H=16, T=8192), the 64K-token gated-delta prefill, the batched decode
 step (256 sequences x 16 heads, gated-delta state 128 x 128 and BASED state 273 x 64 per
@@ -133,6 +138,7 @@ def main():
     ap.add_argument("--no-d256", action="store_true")
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--no-reference-rates", action="store_true")
+    ap.add_argument("--no-slow-decay", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 256 MiB copy (la_prefill with T = 0) so that HBM "
                          "byte counters can be scaled against a known size")
@@ -192,6 +198,18 @@ def main():
         "alg_flops_per_launch": alg_f, "longest_pass": dominant,
     }
 
+    # the same prefill with slow decay, a ~ U(-8, -4) (alpha in [0.982, 0.9997]): the segment
+    # transitions stay nonzero, so the map pass carries every transition row to the end
+    slow = None
+    if not args.no_slow_decay:
+        slow = bench_gdn_prefill(torch, la, synth, dev, stream, B, H, T, D, max(3, args.steps // 2),
+                                 args.warmup, seed=3, a_range=(-8.0, -4.0))
+        ms_slow = slow.pop("_ms_per_step")
+        slow.pop("_dominant")
+        slow["ms_per_step"] = round(ms_slow, 4)
+        slow["tokens_per_s"] = round(B * T / (ms_slow * 1e-3), 1)
+        slow["gates"] = "alpha = exp(-softplus(a)), a ~ U(-8, -4)"
+
     # ---------------------------------------------------------------- other configurations
     small = None if args.no_small else bench_small_configs(torch, la, synth, dev, stream, timer)
     based = None
@@ -221,6 +239,7 @@ def main():
                    "and per pass on the launch stream"},
         "roofline": roofline,
         "prefill": pre,
+        "prefill_slow_decay": slow,
         "configs": {"cfg0_additive_fp32": None if small is None else small["additive_fp32"],
                     "cfg1_based_prefill": based,
                     "cfg2_gdn_64k": None if small is None else small["gdn_64k"],
@@ -234,10 +253,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def bench_gdn_prefill(torch, la, synth, dev, stream, B, H, T, D, steps, warmup, seed):
+def bench_gdn_prefill(torch, la, synth, dev, stream, B, H, T, D, steps, warmup, seed, a_range=None):
     """The gated-delta prefill as its separate passes, each bracketed by HIP events on the
-    launch stream; returns per-pass and per-step statistics."""
-    inp = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=seed, device=dev)
+    launch stream; returns per-pass and per-step statistics.  a_range: the gate logits'
+    range (the recipe's U(-2, 4) by default)."""
+    inp = synth.gdn_inputs(B, H, T, D, D, dtype=torch.bfloat16, seed=seed, device=dev,
+                           **({} if a_range is None else {"a_range": a_range}))
     q, k, v, a, b = inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"]
     o = torch.empty((B, H, T, D), dtype=torch.bfloat16, device=dev)
     S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)

@@ -738,19 +738,41 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
       issue(ci, dK, dV, dT, dG, ln);
     }
   };
+  // A wave of transition rows whose every entry has become exactly zero (the decay since
+  // the segment start has fallen below the smallest fp32 value) keeps them zero: with finite
+  // inputs, K S^T, U and the update of such rows are exact zeros, so skipping its chunk work
+  // leaves every result bit for bit as it was (the barriers and loads go on).  The wave
+  // checks every eight chunks, right after a barrier, when its last update has long
+  // completed.  Rows that merely become small (a decay per chunk above one half can hold the
+  // smallest subnormal) are never skipped.
+  bool m_dead = false;
   if (!LOADER && nchunks > 0) issue(0, sK0, sV0, sT0, sGraw[0][0], lane);
   for (int ci = 0; ci < nchunks; ci += 2) {
     if (!LOADER) lds_dma_wait();
     __syncthreads();  // copy 0 holds chunk ci; every wave is done with copy 1
     issue_next(ci + 1, sK1, sV1, sT1, sGraw[1][0]);
-    const float gC0 = gates(ci, sGraw[0][0]);
-    step(sK0, sV0, sT0, gC0);
+    if (m_kind && !m_dead && (ci & 7) == 0 && ci > 0) {
+      bool nz = false;
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nz |= st[m][c][e] != 0.0f;
+      m_dead = __builtin_amdgcn_ballot_w64(nz) == 0;
+    }
+    if (!m_dead) {
+      const float gC0 = gates(ci, sGraw[0][0]);
+      step(sK0, sV0, sT0, gC0);
+    }
     if (ci + 1 < nchunks) {
       if (!LOADER) lds_dma_wait();
       __syncthreads();  // copy 1 holds chunk ci + 1; every wave is done with copy 0
       issue_next(ci + 2, sK0, sV0, sT0, sGraw[0][0]);
-      const float gC1 = gates(ci + 1, sGraw[1][0]);
-      step(sK1, sV1, sT1, gC1);
+      if (!m_dead) {
+        const float gC1 = gates(ci + 1, sGraw[1][0]);
+        step(sK1, sV1, sT1, gC1);
+      }
     }
   }
 
