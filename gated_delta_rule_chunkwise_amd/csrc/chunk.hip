@@ -210,6 +210,7 @@ struct TPrepLds {
 };
 
 constexpr int TPW = 4;  // independent waves (chunks) per transform workgroup
+constexpr int MAP_WINDOW = 8;  // chunks the map pass tries first at the end of a segment
 // d = 256 holds twice the key fragments (128 registers), so two waves per SIMD
 template <int DK>
 __global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(const Args a) {
@@ -536,6 +537,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   __shared__ __attribute__((aligned(16))) bf16_t sT0[DELTA ? C * LDT : 8], sT1[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) float sGw[NWT][3 * C];
   __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][2][C];  // per copy: raw alpha, beta
+  __shared__ int sZero[4];  // the window's verdict (see below)
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -552,17 +554,35 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   float *gw = sGw[wave];
 
   f32x4 st[DK / 16][NCT];  // zero start (B rows) or identity (M rows)
+  auto init_state = [&]() {  // (formed again from an opaque lane index, rather than kept)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int i16 = ln & 15, gi = ln >> 4;
 #pragma unroll
-  for (int m = 0; m < DK / 16; ++m)
+    for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-    for (int c = 0; c < NCT; ++c)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st[m][c][e] = (m_kind && row0 + srow<NCT>(c, l16) == sd(m, g) + e) ? 1.0f : 0.0f;
+        for (int e = 0; e < 4; ++e) st[m][c][e] = (m_kind && row0 + srow<NCT>(c, i16) == sd(m, gi) + e) ? 1.0f : 0.0f;
+  };
+  init_state();
 
   const int64_t first = (int64_t)seg * a.seg_chunks * C;
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
   float gseg = 0.0f;
+
+  // The window.  The map of a segment (S_end = S_start M + B) composes the maps of its first
+  // chunks and of its last MAP_WINDOW chunks: M = M_first M_last, B = B_first M_last + B_last.
+  // When the transition of the last chunks is exactly zero in fp32 (every transition row
+  // decayed below the smallest fp32 value; for scalar gates, their log2 product below -150),
+  // the segment's map is (0, B_last) to within that underflow, and the first chunks need not
+  // be carried at all.  So the map pass runs the last MAP_WINDOW chunks first (B rows from
+  // zero, transition rows from the identity) and carries the whole segment only when their
+  // transition is not zero.  (With the transition split over two workgroups, as at d = 256,
+  // neither sees the whole of it: the whole segment is carried.)
+  constexpr bool WINDOW = NMB == 1;
+  const int cw = (WINDOW && nchunks > 2 * MAP_WINDOW) ? nchunks - MAP_WINDOW : 0;
 
   // chunk ci's tiles and raw gate values into one LDS copy, issued by the loader wave or
   // shared by the state waves (ln: the lane index, an opaque copy inside the chunk loop)
@@ -585,16 +605,23 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
     // The loader wave: chunk ci + 1 streams into one LDS copy while the state waves work
     // on chunk ci in the other; it waits for its loads before each barrier, so after the
     // barrier the chunk has landed for every wave.
-    if (nchunks > 0) issue(0, sK0, sV0, sT0, sGraw[0][0], lane);
-    for (int ci = 0; ci < nchunks; ci += 2) {
-      lds_dma_wait();
-      __syncthreads();
-      if (ci + 1 < nchunks) issue(ci + 1, sK1, sV1, sT1, sGraw[1][0], lane);
-      if (ci + 1 < nchunks) {
+    // the window's chunks, then (unless its transition is zero) the whole segment
+    for (int cb = cw; nchunks > 0;) {
+      issue(cb, sK0, sV0, sT0, sGraw[0][0], lane);
+      for (int ci = cb; ci < nchunks; ci += 2) {
         lds_dma_wait();
         __syncthreads();
-        if (ci + 2 < nchunks) issue(ci + 2, sK0, sV0, sT0, sGraw[0][0], lane);
+        if (ci + 1 < nchunks) issue(ci + 1, sK1, sV1, sT1, sGraw[1][0], lane);
+        if (ci + 1 < nchunks) {
+          lds_dma_wait();
+          __syncthreads();
+          if (ci + 2 < nchunks) issue(ci + 2, sK0, sV0, sT0, sGraw[0][0], lane);
+        }
       }
+      if (cb == 0) break;
+      __syncthreads();  // the window's verdict
+      if (sZero[0] & sZero[1] & sZero[2] & sZero[3]) break;
+      cb = 0;
     }
     return;
   }
@@ -745,35 +772,54 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   // checks every eight chunks, right after a barrier, when its last update has long
   // completed.  Rows that merely become small (a decay per chunk above one half can hold the
   // smallest subnormal) are never skipped.
-  bool m_dead = false;
-  if (!LOADER && nchunks > 0) issue(0, sK0, sV0, sT0, sGraw[0][0], lane);
-  for (int ci = 0; ci < nchunks; ci += 2) {
-    if (!LOADER) lds_dma_wait();
-    __syncthreads();  // copy 0 holds chunk ci; every wave is done with copy 1
-    issue_next(ci + 1, sK1, sV1, sT1, sGraw[1][0]);
-    if (m_kind && !m_dead && (ci & 7) == 0 && ci > 0) {
-      bool nz = false;
+  auto rows_zero = [&]() -> bool {  // (whole wave) every state entry of the wave is 0
+    bool nz = false;
 #pragma unroll
-      for (int m = 0; m < DK / 16; ++m)
+    for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
-        for (int c = 0; c < NCT; ++c)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nz |= st[m][c][e] != 0.0f;
-      m_dead = __builtin_amdgcn_ballot_w64(nz) == 0;
-    }
-    if (!m_dead) {
-      const float gC0 = gates(ci, sGraw[0][0]);
-      step(sK0, sV0, sT0, gC0);
-    }
-    if (ci + 1 < nchunks) {
+        for (int e = 0; e < 4; ++e) nz |= st[m][c][e] != 0.0f;
+    return __builtin_amdgcn_ballot_w64(nz) == 0;
+  };
+  // the window's chunks cw .. nchunks - 1, then (unless its transition is zero) the whole
+  // segment from its first chunk; copy 0 first each time
+  for (int cb = cw; nchunks > 0;) {
+    bool m_dead = false;
+    if (!LOADER) issue(cb, sK0, sV0, sT0, sGraw[0][0], lane);
+    for (int ci = cb; ci < nchunks; ci += 2) {
       if (!LOADER) lds_dma_wait();
-      __syncthreads();  // copy 1 holds chunk ci + 1; every wave is done with copy 0
-      issue_next(ci + 2, sK0, sV0, sT0, sGraw[0][0]);
+      __syncthreads();  // copy 0 holds chunk ci; every wave is done with copy 1
+      issue_next(ci + 1, sK1, sV1, sT1, sGraw[1][0]);
+      if (m_kind && !m_dead && ((ci - cb) & 7) == 0 && ci > cb) m_dead = rows_zero();
       if (!m_dead) {
-        const float gC1 = gates(ci + 1, sGraw[1][0]);
-        step(sK1, sV1, sT1, gC1);
+        const float gC0 = gates(ci, sGraw[0][0]);
+        step(sK0, sV0, sT0, gC0);
+      }
+      if (ci + 1 < nchunks) {
+        if (!LOADER) lds_dma_wait();
+        __syncthreads();  // copy 1 holds chunk ci + 1; every wave is done with copy 0
+        issue_next(ci + 2, sK0, sV0, sT0, sGraw[0][0]);
+        if (!m_dead) {
+          const float gC1 = gates(ci + 1, sGraw[1][0]);
+          step(sK1, sV1, sT1, gC1);
+        }
       }
     }
+    if (cb == 0) break;
+    if (DELTA) {
+      if (m_kind) {
+        const bool z = rows_zero();
+        if (lane == 0) sZero[wave - HALF] = z ? 1 : 0;
+      }
+    } else if (wave < 4 && lane == 0) {
+      sZero[wave] = gseg < -150.0f ? 1 : 0;  // 2^gseg rounds to zero
+    }
+    __syncthreads();  // the window's verdict
+    if (sZero[0] & sZero[1] & sZero[2] & sZero[3]) break;
+    init_state();
+    gseg = 0.0f;
+    cb = 0;
   }
 
   float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
