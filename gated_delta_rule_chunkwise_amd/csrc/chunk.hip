@@ -537,16 +537,16 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   __shared__ __attribute__((aligned(16))) bf16_t sT0[DELTA ? C * LDT : 8], sT1[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) float sGw[NWT][3 * C];
   __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][2][C];  // per copy: raw alpha, beta
-  __shared__ int sZero[4];  // the window's verdict (see below)
+  __shared__ int sZero[8];  // the window's verdict (see below)
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
   int seg, mb;
   split_block<NMB>((int)blockIdx.x, seg, mb);
   if (NMB > 1 && seg >= a.nseg - 1) return;  // (whole workgroup) past the last mapped segment
-  const bool m_kind = DELTA && wave >= HALF;  // transition (M) rows, started from the identity
-  const int vcol0 = mb * VW;                  // first B row / V column of the workgroup
-  const int row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;  // (unused by the loader)
+  bool m_kind = DELTA && wave >= HALF;  // transition (M) rows, started from the identity
+  const int vcol0 = mb * VW;            // first B row / V column of the workgroup
+  int row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;  // (unused by the loader)
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
   const bool additive = a.variant == V_ADDITIVE;
@@ -579,10 +579,13 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   // the segment's map is (0, B_last) to within that underflow, and the first chunks need not
   // be carried at all.  So the map pass runs the last MAP_WINDOW chunks first (B rows from
   // zero, transition rows from the identity) and carries the whole segment only when their
-  // transition is not zero.  (With the transition split over two workgroups, as at d = 256,
-  // neither sees the whole of it: the whole segment is carried.)
-  constexpr bool WINDOW = NMB == 1;
-  const int cw = (WINDOW && nchunks > 2 * MAP_WINDOW) ? nchunks - MAP_WINDOW : 0;
+  // transition is not zero.  With the transition rows split over two workgroups (d = 256),
+  // neither would see all of them: there every wave of both first carries transition rows
+  // over the window (the workgroup's own half and the other's, so that both reach the same
+  // verdict), and a zero transition is followed by the window's B rows alone.
+  const int cw = nchunks > 2 * MAP_WINDOW ? nchunks - MAP_WINDOW : 0;
+  constexpr bool SPLIT = DELTA && NMB == 2;
+  constexpr int NZF = SPLIT ? 8 : 4;  // verdict flags
 
   // chunk ci's tiles and raw gate values into one LDS copy, issued by the loader wave or
   // shared by the state waves (ln: the lane index, an opaque copy inside the chunk loop)
@@ -782,10 +785,24 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
         for (int e = 0; e < 4; ++e) nz |= st[m][c][e] != 0.0f;
     return __builtin_amdgcn_ballot_w64(nz) == 0;
   };
-  // the window's chunks cw .. nchunks - 1, then (unless its transition is zero) the whole
-  // segment from its first chunk; copy 0 first each time
-  for (int cb = cw; nchunks > 0;) {
-    bool m_dead = false;
+  // Phases: 0 (SPLIT only) the window's transition rows on every wave; 1 the window (B rows,
+  // and the transition rows unless SPLIT, where they are known to be zero); 2 the whole
+  // segment.  Copy 0 first each time.
+  int phase = cw == 0 ? 2 : (SPLIT ? 0 : 1);
+  if (SPLIT && phase == 0) {
+    m_kind = true;
+    row0 = (wave < HALF ? VW * (1 - mb) + wave * RPW : vcol0 + (wave - HALF) * RPW);
+    init_state();
+  }
+  for (; nchunks > 0;) {
+    const int cb = phase == 2 ? 0 : cw;
+    bool m_dead = SPLIT && phase == 1 && m_kind;
+    if (m_dead) {
+#pragma unroll
+      for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) st[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if (!LOADER) issue(cb, sK0, sV0, sT0, sGraw[0][0], lane);
     for (int ci = cb; ci < nchunks; ci += 2) {
       if (!LOADER) lds_dma_wait();
@@ -806,20 +823,27 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
         }
       }
     }
-    if (cb == 0) break;
+    if (phase == 2 || (SPLIT && phase == 1)) break;
     if (DELTA) {
       if (m_kind) {
         const bool z = rows_zero();
-        if (lane == 0) sZero[wave - HALF] = z ? 1 : 0;
+        if (lane == 0) sZero[SPLIT ? wave : wave - HALF] = z ? 1 : 0;
       }
     } else if (wave < 4 && lane == 0) {
       sZero[wave] = gseg < -150.0f ? 1 : 0;  // 2^gseg rounds to zero
     }
     __syncthreads();  // the window's verdict
-    if (sZero[0] & sZero[1] & sZero[2] & sZero[3]) break;
+    bool zero = true;
+#pragma unroll
+    for (int i = 0; i < NZF; ++i) zero = zero && sZero[i] != 0;
+    if (zero && !SPLIT) break;
+    if (SPLIT) {  // back to the workgroup's own rows
+      m_kind = wave >= HALF;
+      row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;
+    }
+    phase = zero ? 1 : 2;
     init_state();
     gseg = 0.0f;
-    cb = 0;
   }
 
   float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
