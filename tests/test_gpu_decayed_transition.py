@@ -1,16 +1,19 @@
 """GPU parity of the gated-delta prefill when the segment transitions decay to exactly zero
 (GPU, through the C ABI).
 
-The map pass stops updating a wave of transition rows once every entry is exactly zero:
-the product of the decays since the segment start has fallen below the smallest fp32
-value, and zero rows stay zero under every later chunk (Eq. (1) of "History Replays
-Itself", Sec. 2, with A_t = alpha_t (I - beta_t k_t k_t^T): a zero row times A_t is zero).
-One call here holds heads with fast decay (alpha = exp(-softplus(a)), a ~ U(-2, 4): the
-transition is zero after a chunk or two, so those waves skip most chunks) beside heads with
-slow decay (a ~ U(-8, -4): the transition survives every segment), with a start state and a
-ragged tail.  The test first checks, on the maps the map pass leaves in the workspace, that
-both regimes occur; then it compares o and S_T with the fp64 oracle on sampled value rows
-(bound 2e-2 per (b, h) slice, max-norm relative)."""
+The map pass first carries the last 8 chunks of a segment; when the transition over them
+is exactly zero in fp32 (every product of decays below the smallest fp32 value), the
+segment's map is theirs and its earlier chunks are not carried (Eq. (1) of "History
+Replays Itself", Sec. 2, with A_t = alpha_t (I - beta_t k_t k_t^T): a map composes as
+M = M_first M_last, B = B_first M_last + B_last).  Otherwise it carries the whole segment,
+and stops updating a wave of transition rows once every entry is exactly zero.  One call in
+the first test holds heads with fast decay (alpha = exp(-softplus(a)), a ~ U(-2, 4): the
+transition is zero after a chunk or two) beside heads with slow decay (a ~ U(-8, -4): it
+survives every segment), with a start state and a ragged tail; the test checks on the maps
+the map pass leaves in the workspace that both regimes occur.  The second alternates fast
+and slow decay in blocks of 8 chunks inside every head, so that some segments end in a
+zero window and others carry everything.  Both compare o and S_T with the fp64 oracle on
+sampled value rows (bound 2e-2 per (b, h) slice, max-norm relative)."""
 
 import pytest
 import torch
@@ -55,5 +58,24 @@ def test_decayed_transitions_skip_exactly(la, D, H, T):
     o, S_T, _ = la.prefill("gated_delta", q, k, v, a, b, S0=S0)
     torch.cuda.synchronize()
     oo, So, _ = oracle.prefill("gated_delta", q, k, v, a, b, S0=S0, rows=rows)
+    assert_close(o[..., rows], oo, 2e-2, what="o (sampled rows)")
+    assert_close(S_T[:, :, rows, :], So, 2e-2, what="S_T (sampled rows)")
+
+
+@pytest.mark.parametrize("D,H,T", [(128, 32, 64 * 200 + 21), (256, 16, 64 * 16 * 12 + 5)])
+def test_decay_changing_inside_segments(la, D, H, T):
+    fast = synth.gdn_inputs(1, H, T, D, D, dtype=torch.bfloat16, seed=520 + D, device=DEV)
+    slow = synth.gdn_inputs(1, H, T, D, D, dtype=torch.bfloat16, seed=530 + D, device=DEV,
+                            a_range=(-8.0, -4.0))
+    block = (torch.arange(T, device=DEV) // 512) % 2 == 0  # fast decay in even 8-chunk blocks
+    alpha = torch.where(block, fast["alpha"], slow["alpha"]).contiguous()
+    q, k, v, b = fast["q"], fast["k"], fast["v"], fast["beta"]
+    S0 = synth.gdn_state((1, H, D, D), seed=540 + D, device=DEV) * 0.2
+    nseg, sc = la.segments("gated_delta", la.BF16, 1, H, T, D, D)
+    print(f"[decay blocks] d={D} H={H} T={T} segments={nseg}x{sc}", flush=True)
+    rows = [1, 64, D - 2]
+    o, S_T, _ = la.prefill("gated_delta", q, k, v, alpha, b, S0=S0)
+    torch.cuda.synchronize()
+    oo, So, _ = oracle.prefill("gated_delta", q, k, v, alpha, b, S0=S0, rows=rows)
     assert_close(o[..., rows], oo, 2e-2, what="o (sampled rows)")
     assert_close(S_T[:, :, rows, :], So, 2e-2, what="S_T (sampled rows)")
