@@ -170,7 +170,9 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
  *   LA_PASS_MAPS       per segment of chunks except the last, the affine map of its end
  *                      state on its start state (S_end = S_start M + B; M is d_k x d_k
  *                      for the gated delta rule, a scalar decay otherwise), written to
- *                      the workspace
+ *                      the workspace (when the decay over a segment's last 8 chunks takes
+ *                      M to exactly zero in fp32, the map is formed from those chunks
+ *                      alone: M = 0, B theirs)
  *   LA_PASS_SCAN       segment start states S_{i+1} = S_i M_i + B_i from S0
  *   LA_PASS_REPLAY     every segment from its start state: o, and S_T from the last one
  *
