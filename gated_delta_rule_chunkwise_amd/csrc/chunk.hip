@@ -89,6 +89,8 @@ struct Args {
   float *S_T;        // end state written by pass 3 when there is a single segment
   float *maps;       // [BH][nseg][maprows][DK] per-segment maps (rows: B_seg, then M_seg)
   float *gsum;       // [BH][nseg] per-segment log2 decay (no delta rule)
+  uint8_t *mzero;    // [BH][nseg] (delta rule, same memory as gsum) 1: the segment's map is
+                     // its window's, with a zero transition (S_{i+1} = B_i)
   float *starts;     // [BH][nseg][DV][DK] segment start states
   bf16_t *tb;        // [BH][nch][C][C] per-chunk (T diag(beta))^T (delta rule)
   int64_t T, nch;
@@ -789,6 +791,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   // and the transition rows unless SPLIT, where they are known to be zero); 2 the whole
   // segment.  Copy 0 first each time.
   int phase = cw == 0 ? 2 : (SPLIT ? 0 : 1);
+  bool windowed = false;
   if (SPLIT && phase == 0) {
     m_kind = true;
     row0 = (wave < HALF ? VW * (1 - mb) + wave * RPW : vcol0 + (wave - HALF) * RPW);
@@ -823,7 +826,11 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
         }
       }
     }
-    if (phase == 2 || (SPLIT && phase == 1)) break;
+    if (phase == 2) break;
+    if (SPLIT && phase == 1) {
+      windowed = true;
+      break;
+    }
     if (DELTA) {
       if (m_kind) {
         const bool z = rows_zero();
@@ -836,7 +843,10 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
     bool zero = true;
 #pragma unroll
     for (int i = 0; i < NZF; ++i) zero = zero && sZero[i] != 0;
-    if (zero && !SPLIT) break;
+    if (zero && !SPLIT) {
+      windowed = true;
+      break;
+    }
     if (SPLIT) {  // back to the workgroup's own rows
       m_kind = wave >= HALF;
       row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;
@@ -846,6 +856,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
     gseg = 0.0f;
   }
 
+  if (DELTA && mb == 0 && tid == 0) a.mzero[bh * a.nseg + seg] = windowed ? 1 : 0;
   float *dst = a.maps + (bh * a.nseg + seg) * (size_t)MAPROWS * DK;
   const int rbase = m_kind ? DV : 0;
 #pragma unroll
@@ -887,6 +898,9 @@ __global__ __launch_bounds__(DK * 4) void scan_delta_kernel(const Args a) {
     *reinterpret_cast<f32x4 *>(sS[0] + r * LDSS + c4) = x;
     *reinterpret_cast<f32x4 *>(a.starts + ((bh * nseg) * DV + row0 + r) * DK + c4) = x;
   }
+  // every map of the (b, h) formed from a window with a zero transition: each start state is
+  // the previous segment's B rows, which the replay reads from the maps themselves
+  if (__syncthreads_and(nseg - 1 <= DK * 4 && (tid >= nseg - 1 || a.mzero[bh * nseg + tid] != 0))) return;
   const int col = 16 * wave + i16;  // output column of this lane's A-operand row
   // segment i's map in registers: M[16 c + 4 g + e][col] at 4 c + e, and
   // B[row0 + i16][16 wave + 4 g + 0..3]
@@ -1024,7 +1038,11 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   f32x4 st[DK / 16][NCT];
   {
     const int l16 = lane & 15, g = lane >> 4;
-    const float *src = a.nseg > 1 ? a.starts + (bh * a.nseg + seg) * DV * DK : (a.S0 ? a.S0 + bh * DV * DK : nullptr);
+    // a segment after one whose map has a zero transition starts from that map's B rows
+    const float *src = a.nseg == 1 ? (a.S0 ? a.S0 + bh * DV * DK : nullptr)
+                       : (DELTA && seg > 0 && a.mzero[bh * a.nseg + seg - 1])
+                           ? a.maps + (bh * a.nseg + seg - 1) * (size_t)(DV + DK) * DK
+                           : a.starts + (bh * a.nseg + seg) * DV * DK;
 #pragma unroll
     for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
@@ -1470,6 +1488,7 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   a.S_T = S_T;
   a.maps = p.nseg > 1 ? (float *)(ws + w.maps) : nullptr;
   a.gsum = p.nseg > 1 ? (float *)(ws + w.gsum) : nullptr;
+  a.mzero = p.nseg > 1 ? (uint8_t *)(ws + w.gsum) : nullptr;
   a.starts = p.nseg > 1 ? (float *)(ws + w.starts) : nullptr;
   a.tb = delta ? (bf16_t *)(ws + w.tb) : nullptr;
   a.T = T;
