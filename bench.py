@@ -15,9 +15,10 @@ are reported beside it.  The other configurations are timed the same way (at lea
 repetitions each).  Inputs are generated on the device before any timed region.
 
 The headline prefill is timed a second time with slow decay (gate logits U(-8, -4)
-instead of the recipe's U(-2, 4)): with the recipe's gates every segment transition decays
-to exactly zero within a chunk or two and the map pass stops carrying it, with slow decay
-it carries every transition row to the end of its segment (`prefill_slow_decay`).
+instead of the recipe's U(-2, 4)): with the recipe's gates the transition over each
+segment's last 8 chunks is exactly zero in fp32, so the map pass carries only those chunks
+and the scan has nothing to chain; with slow decay the map pass carries whole segments and
+the scan chains them (`prefill_slow_decay`).
 
 Also measured in the same run: the fp32 additive configuration (1 head x 1024 tokens),
 BASED prefill (B=4, H=16, T=8192), the 64K-token gated-delta prefill, the batched decode
@@ -199,7 +200,7 @@ def main():
     }
 
     # the same prefill with slow decay, a ~ U(-8, -4) (alpha in [0.982, 0.9997]): the segment
-    # transitions stay nonzero, so the map pass carries every transition row to the end
+    # transitions stay nonzero, so the map pass carries whole segments
     slow = None
     if not args.no_slow_decay:
         slow = bench_gdn_prefill(torch, la, synth, dev, stream, B, H, T, D, max(3, args.steps // 2),
