@@ -49,7 +49,9 @@
  *                 alpha and beta must be NULL; z pointers are required wherever the
  *                 corresponding s pointer is given.
  * Preconditions that are not checked: alpha_t in (0, 1] (outside it results are
- * unspecified), finite inputs (NaN/Inf propagate).
+ * unspecified), finite inputs (NaN/Inf propagate through the recurrence, except across a
+ * point where the decay has taken the state's dependence on earlier tokens to exactly zero
+ * in fp32: the chunked prefill stops carrying those tokens there, as it may).
  *
  * Ownership and threading: the caller owns every buffer, including the workspace.
  * The library allocates no device memory (its one static device array, the scratch of
