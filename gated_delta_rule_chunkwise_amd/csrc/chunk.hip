@@ -585,7 +585,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   // neither would see all of them: there every wave of both first carries transition rows
   // over the window (the workgroup's own half and the other's, so that both reach the same
   // verdict), and a zero transition is followed by the window's B rows alone.
-  const int cw = nchunks > 2 * MAP_WINDOW ? nchunks - MAP_WINDOW : 0;
+  const int cw = (!additive && nchunks > 2 * MAP_WINDOW) ? nchunks - MAP_WINDOW : 0;  // (no decay, no window)
   constexpr bool SPLIT = DELTA && NMB == 2;
   constexpr int NZF = SPLIT ? 8 : 4;  // verdict flags
 
@@ -609,8 +609,8 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   if (LOADER && wave == NWT) {
     // The loader wave: chunk ci + 1 streams into one LDS copy while the state waves work
     // on chunk ci in the other; it waits for its loads before each barrier, so after the
-    // barrier the chunk has landed for every wave.
-    // the window's chunks, then (unless its transition is zero) the whole segment
+    // barrier the chunk has landed for every wave.  The window's chunks first, then (unless
+    // their transition is zero) the whole segment.
     for (int cb = cw; nchunks > 0;) {
       issue(cb, sK0, sV0, sT0, sGraw[0][0], lane);
       for (int ci = cb; ci < nchunks; ci += 2) {
