@@ -380,8 +380,11 @@ __global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(cons
 // for two copies of a chunk's tiles.  While chunk i is processed from one copy, chunk i + 1
 // lands in the other (buffer_load ... lds: no registers, no LDS store instructions).  One
 // extra wave issues every load, so the state waves never stall on issuing them (8.5%
-// faster than spreading the loads over the state waves); every state wave forms the gate
-// prefix sums itself, so one barrier per chunk suffices.
+// faster than spreading the loads over the state waves; at d = 256, where a ninth wave
+// would cap the registers, the state waves share the loads); every state wave forms the
+// gate prefix sums itself, so one barrier per chunk suffices.  A segment is first tried on
+// its last 8 chunks, which suffice when their transition is exactly zero (the window, in
+// map_kernel).
 // ---------------------------------------------------------------------------------------
 // Buffer descriptor as four words (base, size in bytes), for inline assembly.
 __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
