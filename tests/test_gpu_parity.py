@@ -314,6 +314,28 @@ def test_prefill_in_place_state_across_segments(la, variant):
         assert torch.equal(z1, z_io)
 
 
+@pytest.mark.parametrize("variant", ["gated", "gated_delta"])
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_in_place_state_windowed_segments(la, variant, D):
+    """The same with segments long enough (20 chunks) for the map pass to form each map from
+    its last 8 chunks, whose transition the recipe's gates take to exactly zero: the scan
+    then only copies S0 for the first segment and the replay starts every other segment
+    from the previous map's B rows, while the last segment writes S_T over S0."""
+    B, H = 1, 8
+    T = 64 * 32 * 20 - 5
+    q, k, v, a, b = _inputs(variant, B, H, T, D, D, torch.bfloat16, 68)
+    nseg, sc = la.segments(variant, la.BF16, B, H, T, D, D)
+    print(f"[in-place windowed] {variant} d={D} segments={nseg}x{sc}", flush=True)
+    assert nseg > 1 and sc > 16
+    S0 = synth.gdn_state((B, H, D, D), seed=69, device=DEV) * 0.3
+    o1, S1, _ = la.prefill(variant, q, k, v, a, b, S0=S0)
+    S_io = S0.clone()
+    o2, S2, _ = la.prefill(variant, q, k, v, a, b, S0=S_io, S_T=S_io)
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == S_io.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(S1, S_io)
+
+
 @pytest.mark.parametrize("variant", ["additive", "gated"])
 @pytest.mark.parametrize("T", [130, 1024])
 def test_prefill_fp32_chunk_form_in_place(la, variant, T):
