@@ -118,3 +118,51 @@ def segmented(variant, q, k, v, alpha, beta, S0, C, seg_chunks):
         bb = None if beta is None else beta[sl]
         o[sl], _ = chunked(variant, q[sl], k[sl], v[sl], a, bb, Sst, C)
     return o, S
+
+
+def windowed_segmented(variant, q, k, v, alpha, beta, S0, C, seg_chunks, window, force=False):
+    """segmented(), with each segment's map formed as the map pass forms it: first from its
+    last `window` chunks alone; when their composed transition is exactly zero the
+    segment's map is (0, B_last), since the whole map composes as M = M_first M_last,
+    B = B_first M_last + B_last; otherwise from all its chunks.  force=True takes the
+    window's map even when its transition is not zero (a planted mistake)."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    seg = C * seg_chunks
+    starts = list(range(0, T, seg))
+
+    def compose(c_from, c_to):
+        M = np.eye(dk)
+        Bm = np.zeros((dv, dk))
+        for c0 in range(c_from, c_to, C):
+            sl = slice(c0, min(c0 + C, T))
+            a = None if alpha is None else alpha[sl]
+            bb = None if beta is None else beta[sl]
+            Mc, Bc = chunk_map(variant, k[sl], v[sl], a, bb)
+            M, Bm = M @ Mc, Bm @ Mc + Bc
+        return M, Bm
+
+    maps, used_window = [], []
+    for s0 in starts:
+        s1 = min(s0 + seg, T)
+        nch = (s1 - s0 + C - 1) // C
+        if nch > 2 * window:
+            Mw, Bw = compose(s1 - window * C, s1)
+            if force or not np.any(Mw):
+                maps.append((np.zeros((dk, dk)) if not force else Mw, Bw))
+                used_window.append(True)
+                continue
+        maps.append(compose(s0, s1))
+        used_window.append(False)
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, dtype=np.float64)
+    seg_start = []
+    for M, Bm in maps:
+        seg_start.append(S)
+        S = S @ M + Bm
+    o = np.zeros((T, dv))
+    for s0, Sst in zip(starts, seg_start):
+        sl = slice(s0, min(s0 + seg, T))
+        a = None if alpha is None else alpha[sl]
+        bb = None if beta is None else beta[sl]
+        o[sl], _ = chunked(variant, q[sl], k[sl], v[sl], a, bb, Sst, C)
+    return o, S, used_window

@@ -410,6 +410,46 @@ def test_segment_pin_catches_planted_transition_mistakes(monkeypatch, variant, m
         assert err > 1e-2, f"planted {mistake} gives only {err:.2e}"
 
 
+def _window_case(variant, kill, force=False):
+    # segments of 8 chunks of 8 tokens, windows of 3 chunks; kill=True sets alpha = 1e-200 on
+    # two tokens inside every segment's window, whose decay product (1e-400) is exactly zero
+    # in fp64, so the window's transition is zero; otherwise slow gates keep it alive
+    r = rng(16)
+    C, seg_chunks, window = 8, 8, 3
+    T, dk, dv = C * seg_chunks * 4 - 3, 6, 5
+    q, k, v, alpha, beta = gdn_like(r, 1, 1, T, dk, dv, a_range=(-8, -4))
+    if kill:
+        for s0 in range(0, T, C * seg_chunks):
+            for t in (s0 + C * (seg_chunks - window) + 2, s0 + C * (seg_chunks - window) + 5):
+                if t < T:
+                    alpha[0, 0, t] = 1e-200
+    S0 = r.standard_normal((1, 1, dv, dk))
+    o, S_T, _ = oracle.prefill(variant, q, k, v, alpha=alpha, beta=beta, S0=S0)
+    ow, Sw, used = models.windowed_segmented(variant, q[0, 0], k[0, 0], v[0, 0], alpha[0, 0],
+                                             beta[0, 0], S0[0, 0], C, seg_chunks, window, force)
+    return max(rel(ow, o[0, 0]), rel(Sw, S_T[0, 0])), used
+
+
+@pytest.mark.parametrize("variant", ["gated", "gated_delta"])
+def test_window_maps_match_sequential(variant):
+    """The map pass's window: a segment whose last chunks compose to an exactly zero
+    transition is mapped from those chunks alone, (0, B_last); with the window's
+    transition zero (decay underflowing fp64) every full segment takes the window and the
+    result still equals the token recurrence; with slow decay no segment takes it."""
+    err, used = _window_case(variant, kill=True)
+    assert err < 1e-10 and used[:-1] == [True] * (len(used) - 1)
+    err, used = _window_case(variant, kill=False)
+    assert err < 1e-10 and not any(used)
+
+
+@pytest.mark.parametrize("variant", ["gated", "gated_delta"])
+def test_window_pin_catches_a_window_taken_without_a_zero_transition(variant):
+    """Taking the window's map while its transition is not zero drops the earlier chunks'
+    contribution B_first M_last and the start state's S M_first M_last: far past the bound."""
+    err, used = _window_case(variant, kill=False, force=True)
+    assert any(used) and err > 1e-2, f"forced window gives only {err:.2e}"
+
+
 @pytest.mark.parametrize("variant", ["additive", "gated", "gated_delta", "based", "based_compact"])
 def test_split_resume(variant):
     """prefill(x[:a]) -> S_a; prefill(x[a:], S0=S_a) == prefill(x)."""
