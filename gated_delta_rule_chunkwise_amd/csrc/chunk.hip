@@ -1,4 +1,5 @@
-// chunk.hip -- chunkwise bf16 prefill for ADDITIVE / GATED / GATED_DELTA (d_k = d_v = 128).
+// chunk.hip -- chunkwise bf16 prefill for ADDITIVE / GATED / GATED_DELTA (d_k = d_v = 128
+// or 256).
 //
 // Method.  Eq. (1) of "History Replays Itself" (Sec. 2) is evaluated on chunks of C = 64
 // tokens with the state carried across chunk boundaries, as the NoteBank paper's
@@ -30,15 +31,18 @@
 // the next chunk overlap the MFMA work of the current one.  A replay workgroup (4 waves)
 // uses 78 KB of LDS, so two share a CU.
 //
-// Sequence parallelism.  One workgroup owns the whole 128 x 128 state of one (b, h),
-// split over its 4 waves (32 state rows each, in registers), and streams chunks with
-// no inter-workgroup traffic.  A long sequence is split into segments so that
+// Sequence parallelism.  One workgroup owns the whole state of one (b, h), split over its
+// waves (32 state rows each, in registers; 4 waves at d = 128, 8 at 256), and streams chunks
+// with no inter-workgroup traffic.  A long sequence is split into segments so that
 // B*H*segments fills the chip, in three passes:
 //   pass 1 (map_kernel)    every segment but the last from a zero start: its end state
 //                          B_seg, and for the delta rule its d_k x d_k transition M_seg
 //                          (the same chunk recurrence run on the identity, by the second
-//                          half of an 8-wave workgroup), or the scalar log decay
-//   pass 2 (scan_*_kernel) S_{i+1} = S_i M_i + B_i sequentially over segments (fp32 MFMA)
+//                          half of an 8-wave workgroup), or the scalar log decay; first
+//                          over the segment's last 8 chunks alone, which give the map when
+//                          their transition is exactly zero in fp32
+//   pass 2 (scan_*_kernel) S_{i+1} = S_i M_i + B_i sequentially over segments (fp32 MFMA;
+//                          nothing to chain when every transition is zero)
 //   pass 3 (replay_kernel) every segment replayed from its start state, writing o; the
 //                          last segment also writes S_T
 // With one segment (enough heads to fill the chip) only pass 3 runs.  For the delta rule
