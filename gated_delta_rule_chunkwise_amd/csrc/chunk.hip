@@ -1003,8 +1003,10 @@ __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Pass 3 (replay): every segment from its start state (or the single segment from S0),
-// writing o and, with one segment, S_T.  Four waves own 32 state rows each.  Per chunk:
+// Pass 3 (replay): every segment from its start state (or the single segment from S0; a
+// segment after one whose map has a zero transition from that map's B rows), writing o,
+// and S_T from the last segment.  Each wave owns 32 state rows (4 waves at d = 128, 8 at
+// 256).  Per chunk:
 //   phase 1  K S^T, Y = V - diag(gamma) K S^T and U = TB Y (delta rule), or U = diag(beta) V
 //   phase 2  the decay-masked Q K^T tiles (dealt over the waves, into LDS) and S Q^T
 //   phase 3  O = diag(gamma) Q S^T + (P . Q K^T) U, stored; S <- gamma_C S + K^T diag(dec) U
