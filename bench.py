@@ -300,10 +300,17 @@ def bench_gdn_prefill(torch, la, synth, dev, stream, B, H, T, D, steps, warmup, 
     pass_stats = {kk: stats(vv) for kk, vv in per_pass.items()}
     dom = max(pass_stats, key=lambda kk: pass_stats[kk]["mean"])
     wide = "" if D == 128 else f", {D}"
-    kernels = {"replay": f"replay_kernel<true{wide}> (replay pass)",
-               "maps": f"map_kernel<true{wide}> (segment-map pass)",
-               "transform": f"tprep_kernel{'<%d>' % D if D != 128 else ''} (per-chunk UT transform pass)",
-               "scan": f"scan_delta_kernel{'<%d>' % D if D != 128 else ''} (segment scan)"}
+    if D == 128:  # the replay forms each chunk's solve; stored transforms serve the map pass
+        kernels = {"replay": "replay_kernel<true> (replay pass, forming each chunk's solve from its keys)",
+                   "maps": "map_kernel<true> (the segments' last 8 chunks), tprep_kernel and map_kernel<true> "
+                           "(the other chunks of segments whose transition over those 8 is not zero)",
+                   "transform": "tprep_kernel (UT transforms of the segments' last 8 chunks)",
+                   "scan": "scan_delta_kernel (segment scan)"}
+    else:
+        kernels = {"replay": f"replay_kernel<true{wide}> (replay pass)",
+                   "maps": f"map_kernel<true{wide}> (segment-map pass)",
+                   "transform": f"tprep_kernel<{D}> (per-chunk UT transform pass)",
+                   "scan": f"scan_delta_kernel<{D}> (segment scan)"}
     res = {"workload": f"gated-delta chunkwise prefill, B={B} H={H} T={T} d_k=d_v={D}, bf16 inputs, "
                        "fp32 state, chunk 64",
            "ms_per_step_stats": stats(per_step), "ms_per_pass": pass_stats,

@@ -16,12 +16,17 @@
 //   O  = diag(gamma) Q S^T + (P . Q K^T) U
 //   S' = gamma_C S + U^T diag(e^{g_C - g}) K  =  S M_c + B_c
 //
-// T is the UT/WY transform of the chunk.  It depends on the keys and gates only, so it is
-// computed for every chunk at once, before any state is carried (pass 0 below): one wave
-// per chunk forms L from a K K^T Gram on bf16 MFMA, solves (I + L) T = I in fp32 by
-// blocked forward substitution (16 x 16 diagonal blocks on the VALU, the off-diagonal
-// blocks on fp32 MFMA), and stores T diag(beta) in bf16.  Every product with a 64- or 128-wide inner dimension runs on bf16
-// MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation; the state stays fp32.
+// T is the UT/WY transform of the chunk.  It depends on the keys and gates only.  At
+// d = 128 the replay forms what it needs of it per chunk from the K tile already in LDS (the
+// diagonal blocks (I + L_bb)^{-1} by doubling products, then U by forward substitution over
+// the chunk's 16-token blocks; ChunkSolve below), so no transform crosses HBM on the way to
+// the outputs.  The map pass reads stored transforms (pass 0 below: one wave per chunk forms
+// L from a K K^T Gram on bf16 MFMA, solves (I + L) T = I in fp32 by blocked forward
+// substitution (16 x 16 diagonal blocks on the VALU, the off-diagonal blocks on fp32 MFMA),
+// and stores T diag(beta) in bf16); at d = 128 only for the chunks it carries.  At d = 256
+// pass 0 covers every chunk and the replay reads the stored transforms too.  Every product
+// with a 64- or 128-wide inner dimension runs on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with
+// fp32 accumulation; the state stays fp32.
 //
 // gfx950 layout choices.  All chunk tiles live in LDS row-major ([token][d]); operands
 // that contract over tokens (K^T, V^T, and T, which is stored transposed) are read
@@ -46,7 +51,11 @@
 //   pass 3 (replay_kernel) every segment replayed from its start state, writing o; the
 //                          last segment also writes S_T
 // With one segment (enough heads to fill the chip) only pass 3 runs.  For the delta rule
-// pass 0 (tprep_kernel) precedes pass 1 (or pass 3 when there is one segment).
+// pass 0 (tprep_kernel) precedes pass 1 (at d = 256 also pass 3 when there is one
+// segment).  At d = 128 pass 0 transforms the segments' last 8 chunks only, and pass 1 is
+// three launches: the maps of those 8 chunks (flagging each segment whose transition over
+// them is exactly zero, for which that map is the segment's), the transforms of the other
+// chunks of the segments not flagged, and the maps of those segments over all their chunks.
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -98,10 +107,24 @@ struct Args {
   float *starts;     // [BH][nseg][DV][DK] segment start states
   bf16_t *tb;        // [BH][nch][C][C] per-chunk (T diag(beta))^T (delta rule)
   int64_t T, nch;
+  int64_t tp_nch;    // (tp_mode 0) chunks per (b, h), from the first, that pass 0 transforms
+  int tp_mode;       // pass 0: 0 the first tp_nch chunks; 1 the windows of the mapped segments;
+                     // 2 the chunks before the window of mapped segments not flagged in mzero
+  int map_mode;      // delta-rule map pass: 0 window, then the whole segment unless the window
+                     // suffices; 1 the window only (flags mzero, maps only where it suffices);
+                     // 2 whole segments where mzero is not set
+  int map_cw;        // first window chunk of a mapped segment (0: no window)
   int B, H, nseg, seg_chunks, variant, has_beta;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Four floats to bf16 in two pairs (two v_cvt_pk_bf16_f32; converted one by one and then
+// packed, the compiler adds a byte permute per pair).
+__device__ __forceinline__ u32x2 pk4u(f32x4 x) {
+  const bf16x2 a = {(__bf16)x[0], (__bf16)x[1]}, b = {(__bf16)x[2], (__bf16)x[3]};
+  return u32x2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)};
+}
 
 // Operand with k along the ROWS (tokens) of a row-major [token][d] tile: lane (g, i)
 // receives column 16 nt + i at tokens 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3, the
@@ -193,10 +216,12 @@ __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Pass 0 (delta rule): for every chunk, TB = (I + L)^{-1} diag(beta), stored transposed
-// (row j of the stored tile is column j of TB) in bf16.  One wave per chunk, four
-// independent waves per workgroup (no barriers).  A partial last chunk has zero keys and
-// beta beyond its end, so its TB is zero there.
+// Pass 0 (delta rule): for the chunks the map pass reads (at d = 256 every chunk, which the
+// replay reads too), TB = (I + L)^{-1} diag(beta), stored transposed (row j of the stored
+// tile is column j of TB) in bf16.  One wave per chunk, four independent waves per workgroup
+// (no barriers); with tp_mode 2 (the chunks of the segments whose window alone does not give
+// the map) each wave takes every (grid width x 4)-th chunk of one segment in turn.  A
+// partial last chunk has zero keys and beta beyond its end, so its TB is zero there.
 //
 // Blocked solve on 16 x 16 blocks, in fp32: the four diagonal blocks D_b = (I + L_bb)^{-1}
 // by forward substitution (one lane per column of a block, the four blocks side by side,
@@ -215,22 +240,41 @@ struct TPrepLds {
   float d[4][SZD];
 };
 
+// The diagonal blocks D_b = (I + L_bb)^{-1}: lane (b, c) of a wave solves column c of
+// (I + L_bb) D_b = I by forward substitution, right-looking, reading L_bb^T (row k holds
+// column k of L_bb) from d (four blocks of row stride LDD, block stride SZD), and writes D_b
+// back row-major over L_bb^T.
+__device__ __forceinline__ void solve_diag_blocks(float *d, int b, int c) {
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.0f : 0.0f;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    const float xk = x[k];
+#pragma unroll
+    for (int q4 = (k + 1) / 4; q4 < 4; ++q4) {  // L_bb[r][k] for r > k: row k of L_bb^T
+      const f32x4 l = ld4(d + b * SZD + k * LDD + 4 * q4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * q4 + e > k) x[4 * q4 + e] -= l[e] * xk;
+    }
+  }
+  __asm__ volatile("" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) d[b * SZD + r * LDD + c] = x[r];
+}
+
 constexpr int TPW = 4;  // independent waves (chunks) per transform workgroup
 constexpr int MAP_WINDOW = 8;  // chunks the map pass tries first at the end of a segment
 // d = 256 holds twice the key fragments (128 registers), so two waves per SIMD
+// chunk ck of (b, h) = bh, by one wave with its LDS area L
 template <int DK>
-__global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(const Args a) {
-  __shared__ __attribute__((aligned(16))) TPrepLds sm[TPW];
-  // the wave index is uniform across the wave: saying so keeps every per-chunk address
-  // and buffer descriptor in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+__device__ __forceinline__ void tprep_chunk(const Args &a, int64_t bh, int64_t ck, TPrepLds &L, int lane) {
   const int l16 = lane & 15, grp = lane >> 4;
-  const int64_t cid = (int64_t)blockIdx.x * TPW + wave;
-  if (cid >= (int64_t)a.B * a.H * a.nch) return;
-  const int64_t bh = cid / a.nch, t0 = (cid % a.nch) * C;
+  const int64_t t0 = ck * C;
   const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
   const size_t base = (size_t)bh * a.T + t0;
-  TPrepLds &L = sm[wave];
+  __asm__ volatile("" ::: "memory");  // (a wave's chunks in turn: the previous one's LDS reads come first)
 
   // K rows as MFMA operands, straight from global memory: kf[rt][s] holds row 16 rt + l16,
   // columns 32 s + 8 grp .. +7 (the A and the B operand of K K^T have the same layout)
@@ -294,27 +338,7 @@ __global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(cons
   }
   __asm__ volatile("" ::: "memory");
 
-  {  // diagonal blocks: lane (b, c) solves column c of (I + L_bb) D_b = I, right-looking,
-     // then stores D_b row-major over L_bb^T
-    const int b = grp, c = l16;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.0f : 0.0f;
-#pragma unroll
-    for (int k = 0; k < 15; ++k) {
-      const float xk = x[k];
-#pragma unroll
-      for (int q4 = (k + 1) / 4; q4 < 4; ++q4) {  // L_bb[r][k] for r > k: row k of L_bb^T
-        const f32x4 l = ld4(L.d[b] + k * LDD + 4 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * q4 + e > k) x[4 * q4 + e] -= l[e] * xk;
-      }
-    }
-    __asm__ volatile("" ::: "memory");
-#pragma unroll
-    for (int r = 0; r < 16; ++r) L.d[b][r * LDD + c] = x[r];
-  }
+  solve_diag_blocks(&L.d[0][0], grp, l16);
   __asm__ volatile("" ::: "memory");
 
   // D_b as B operand (rows 4 grp + s of column l16) and as A operand (row l16, inner
@@ -361,7 +385,7 @@ __global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(cons
   // so that an operand fragment (columns 32 s + 4 q + 0..3 and 32 s + 16 + 4 q + 0..3 of
   // one row) is one 16-byte read.  Lane (grp, l16) of block (i, jb) holds row 16 i + l16,
   // columns 16 jb + 4 grp + 0..3 (eight bytes); blocks above the diagonal are zero.
-  bf16_t *dst = a.tb + (size_t)cid * T_CHUNK;
+  bf16_t *dst = a.tb + (size_t)(bh * a.nch + ck) * T_CHUNK;
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) {
     const f32x4 bj = ld4(L.beta + 16 * jb + 4 * grp);
@@ -372,10 +396,43 @@ __global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(cons
       if (i == jb) t = ld4(L.d[i] + l16 * LDD + 4 * grp);  // D_i row l16
       if (i > jb) t = ttT[i * (i - 1) / 2 + jb];
       t = t * bj;
-      const bf16x4 h = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-      gst8(dst + tb_offset(16 * i + l16) + 32 * (jb >> 1) + 8 * grp + 4 * (jb & 1), __builtin_bit_cast(u32x2, h));
+      gst8(dst + tb_offset(16 * i + l16) + 32 * (jb >> 1) + 8 * grp + 4 * (jb & 1), pk4u(t));
     }
   }
+}
+
+template <int DK>
+__global__ __launch_bounds__(TPW * 64, DK == 128 ? 3 : 2) void tprep_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) TPrepLds sm[TPW];
+  // the wave index is uniform across the wave: saying so keeps every per-chunk address
+  // and buffer descriptor in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  int64_t bh, ck;
+  int nloop = 1, stride = 0;
+  if (a.tp_mode == 2) {  // grid (x, mapped segment): the workgroup's waves stride over the chunks
+    const int nm = a.nseg - 1;
+    bh = blockIdx.y / nm;
+    const int seg = blockIdx.y % nm;
+    if (a.mzero[bh * a.nseg + seg]) return;  // its window's map stands
+    const int cwp = a.map_cw > 0 ? a.map_cw : a.seg_chunks, j0 = blockIdx.x * TPW + wave;
+    stride = gridDim.x * TPW;
+    nloop = j0 < cwp ? (cwp - j0 + stride - 1) / stride : 0;
+    ck = (int64_t)seg * a.seg_chunks + j0;
+  } else {
+    const int64_t cid = (int64_t)blockIdx.x * TPW + wave;
+    if (a.tp_mode == 1) {
+      const int64_t per = (int64_t)(a.nseg - 1) * MAP_WINDOW;
+      if (cid >= (int64_t)a.B * a.H * per) return;
+      bh = cid / per;
+      const int64_t r = cid % per;
+      ck = (r / MAP_WINDOW) * a.seg_chunks + a.map_cw + r % MAP_WINDOW;
+    } else {
+      if (cid >= (int64_t)a.B * a.H * a.tp_nch) return;
+      bh = cid / a.tp_nch;
+      ck = cid % a.tp_nch;
+    }
+  }
+  for (int i = 0; i < nloop; ++i, ck += stride) tprep_chunk<DK>(a, bh, ck, sm[wave], lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -388,7 +445,9 @@ __global__ __launch_bounds__(TPW * 64, DK == 128 ? 4 : 2) void tprep_kernel(cons
 // would cap the registers, the state waves share the loads); every state wave forms the
 // gate prefix sums itself, so one barrier per chunk suffices.  A segment is first tried on
 // its last 8 chunks, which suffice when their transition is exactly zero (the window, in
-// map_kernel).
+// map_kernel).  At d = 128 (map_mode 1, then 2) the window and the whole segment are two
+// launches, with the transforms of the segment's other chunks formed in between only where
+// the window does not suffice.
 // ---------------------------------------------------------------------------------------
 // Buffer descriptor as four words (base, size in bytes), for inline assembly.
 __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
@@ -553,10 +612,11 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   int seg, mb;
   split_block<NMB>((int)blockIdx.x, seg, mb);
   if (NMB > 1 && seg >= a.nseg - 1) return;  // (whole workgroup) past the last mapped segment
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  if (DELTA && a.map_mode == 2 && a.mzero[bh * a.nseg + seg]) return;  // the window's map stands
   bool m_kind = DELTA && wave >= HALF;  // transition (M) rows, started from the identity
   const int vcol0 = mb * VW;            // first B row / V column of the workgroup
   int row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;  // (unused by the loader)
-  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const int64_t T = a.T;
   const bool additive = a.variant == V_ADDITIVE;
   const bool use_beta = a.variant == V_GATED_DELTA || (a.variant == V_GATED && a.has_beta);
@@ -592,8 +652,12 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   // neither would see all of them: there every wave of both first carries transition rows
   // over the window (the workgroup's own half and the other's, so that both reach the same
   // verdict), and a zero transition is followed by the window's B rows alone.
-  const int cw = (!additive && nchunks > 2 * MAP_WINDOW) ? nchunks - MAP_WINDOW : 0;  // (no decay, no window)
+  const int cw = (!additive && nchunks > 2 * MAP_WINDOW && a.map_mode != 2) ? nchunks - MAP_WINDOW : 0;  // (no decay, no window)
   constexpr bool SPLIT = DELTA && NMB == 2;
+  if (DELTA && !SPLIT && a.map_mode == 1 && cw == 0) {  // no window: the whole segment in the next launch
+    if (tid == 0) a.mzero[bh * a.nseg + seg] = 0;
+    return;
+  }
   constexpr int NZF = SPLIT ? 8 : 4;  // verdict flags
 
   // chunk ci's tiles and raw gate values into one LDS copy, issued by the loader wave or
@@ -632,7 +696,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
       }
       if (cb == 0) break;
       __syncthreads();  // the window's verdict
-      if (sZero[0] & sZero[1] & sZero[2] & sZero[3]) break;
+      if ((sZero[0] & sZero[1] & sZero[2] & sZero[3]) || a.map_mode == 1) break;
       cb = 0;
     }
     return;
@@ -854,6 +918,10 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
       windowed = true;
       break;
     }
+    if (DELTA && !SPLIT && a.map_mode == 1) {  // the whole segment in the next launch
+      if (tid == 0) a.mzero[bh * a.nseg + seg] = 0;
+      return;
+    }
     if (SPLIT) {  // back to the workgroup's own rows
       m_kind = wave >= HALF;
       row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;
@@ -1010,6 +1078,10 @@ __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
 //   phase 1  K S^T, Y = V - diag(gamma) K S^T and U = TB Y (delta rule), or U = diag(beta) V
 //   phase 2  the decay-masked Q K^T tiles (dealt over the waves, into LDS) and S Q^T
 //   phase 3  O = diag(gamma) Q S^T + (P . Q K^T) U, stored; S <- gamma_C S + K^T diag(dec) U
+// At d = 128 (FORM) the delta rule's TB is not loaded: phase 1 also forms the blocks of the
+// chunk solve (ChunkSolve, between the K S^T products) into the tile TB would occupy, and
+// phase 2 finds U from Y by forward substitution (Subst, between the S Q^T products), then
+// forms the Q K^T tiles.
 // The tiles stream in with direct global-to-LDS loads while earlier work runs, in three
 // row buffers without extra copies: after phase 1 the V and TB tiles are no longer read, so
 // the next chunk's V and TB load during phases 2 and 3; after phase 2 the Q tile is free
@@ -1018,12 +1090,165 @@ __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
 // chunk (start: K, V, TB landed, previous chunk done; Q landed; A tiles written); they
 // order LDS only, so the output stores of a chunk stay in flight across them.
 // ---------------------------------------------------------------------------------------
+// 16x16x16 bf16 MFMA (one 16-token block of k): lane (g, i) holds A[i][4 g + e] and
+// B[4 g + e][i], the accumulator rows 4 g + e of column i, so an accumulator tile packed
+// to bf16 is directly a B operand.
+__device__ __forceinline__ f32x4 mfma_k16(v4i16 a, v4i16 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4i16 pk4(f32x4 x) {
+  return __builtin_bit_cast(v4i16, pk4u(x));
+}
+
+// The delta rule's chunk solve formed inside the replay (d = 128) instead of read as a stored
+// transform.  U = (I + L)^{-1} diag(beta) Y, L_tj = beta_t 2^{g_t - g_j} k_t.k_j for j < t,
+// is found by forward substitution over the chunk's four 16-token blocks.  With
+// L = diag(beta) L'' (L''_tj = 2^{g_t - g_j} k_t.k_j),
+//   U_i = D_i diag(beta_i) (Y_i - sum_{k<i} L''_ik U_k),   D_i = (I + L_ii)^{-1},
+// on bf16 MFMA with fp32 accumulation (each U_k enters the later blocks as the same bf16
+// values that the output and state products use).  Per chunk the workgroup writes -L''_ik
+// (i > k) and D_i diag(beta_i) in bf16 into the row-padded tile that holds a stored transform
+// otherwise, in the same MFMA k order (row t, column j = 32 s + 16 h + 4 q + e at position
+// 32 s + 8 q + 4 h + e).  Wave b inverts diagonal block b; the six blocks below the
+// diagonal are dealt over the waves.  L_bb = N is nilpotent (N^16 = 0), so
+//   D_b = (I - N)(I + N^2)(I + N^4)(I + N^8),
+// four levels of 16 x 16 products on 16x16x16 bf16 MFMA with fp32 accumulation.  D_b is
+// rounded to bf16 for the substitution in any case; the products' own rounding only
+// reaches the terms of second and higher order in N, and the error they add to U is below
+// that rounding's (seeded trials against fp64 with keys of norm up to 2, fast and slow
+// decay: the same U errors as with D_b solved exactly in fp64).  The transposed forms are carried
+// beside the powers, since an accumulator tile of X^T is X as an A operand:
+//   N^2 = N N, (N^2)^T = N^T N^T, N^4, (N^4)^T likewise, N^8 = N^4 N^4, and
+//   P^T <- P^T + (N^k)^T P^T from P^T = I - N^T, which ends as D_b^T: D_b as an A operand.
+// g (log2 decay prefix) is gw[0..63], beta gw[192..255].
+// c + X Y for 16 x 16 tiles held as accumulators: at = X^T, b = Y
+__device__ __forceinline__ f32x4 prod16(f32x4 at, f32x4 b, f32x4 c) { return mfma_k16(pk4(at), pk4(b), c); }
+// The pieces of the chunk solve, in steps that the replay spreads over its K S^T product (the
+// blocks of L and D) and its S Q^T product (the substitution), whose independent MFMAs fill
+// the latency between one dependent step and the next.
+template <int LDK> struct ChunkSolve {
+  f32x4 acc, n, nt, pt, n2, n2t, n4, n4t, n8;
+  // diagonal block b = wave: the Gram block (k_r . k_i, r = 16 b + 4 g + e, i = 16 b + l16)
+  __device__ __forceinline__ void gram(const bf16_t *sK, int b, int l16, int g) {
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sK + (16 * b + l16) * LDK + 32 * s + 8 * g);
+      acc = mfma_bf16(kf, kf, acc);
+    }
+  }
+  // N[r][i] (r > i) and N^T[r][i] = N[i][r] (i > r) in accumulator layout; P^T = I - N^T
+  __device__ __forceinline__ void scale(const float *gw, int b, int l16, int g) {
+    const float gi = gw[16 * b + l16], bi = gw[192 + 16 * b + l16];
+    const f32x4 gr = ld4(gw + 16 * b + 4 * g), br = ld4(gw + 192 + 16 * b + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // one decay per entry: 2^{g_r - g_i} below the diagonal, 2^{g_i - g_r} above
+      const int r = 4 * g + e;
+      const float d = gr[e] - gi, x = acc[e] * exp2_hw(r > l16 ? d : -d);
+      n[e] = r > l16 ? br[e] * x : 0.0f;
+      nt[e] = l16 > r ? bi * x : 0.0f;
+      pt[e] = (r == l16 ? 1.0f : 0.0f) - nt[e];
+    }
+  }
+  __device__ __forceinline__ void level(int l) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    if (l == 1) {
+      n2 = prod16(nt, n, z);
+      n2t = prod16(n, nt, z);
+    } else if (l == 2) {
+      pt = prod16(n2, pt, pt);
+      n4 = prod16(n2t, n2, z);
+      n4t = prod16(n2, n2t, z);
+    } else if (l == 3) {
+      pt = prod16(n4, pt, pt);
+      n8 = prod16(n4t, n4, z);
+    } else {
+      pt = prod16(n8, pt, pt);
+    }
+  }
+  // lane (g, l16) holds D_b[l16][4 g + e]: row 16 b + l16 of the tile, stored as D_b diag(beta_b)
+  __device__ __forceinline__ void store_d(bf16_t *sT, const float *gw, int b, int l16, int g) {
+    *reinterpret_cast<u32x2 *>(sT + (16 * b + l16) * LDT + 32 * (b >> 1) + 8 * g + 4 * (b & 1)) =
+        pk4u(pt * ld4(gw + 192 + 16 * b + 4 * g));
+  }
+  // block j of (i, k) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): -diag(beta_i)^{-1} L_ik into the tile
+  __device__ __forceinline__ void offdiag(const bf16_t *sK, bf16_t *sT, const float *gw, int j, int l16, int g) {
+    const int i = j >= 3 ? 3 : (j >= 1 ? 2 : 1), k = j - i * (i - 1) / 2;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sK + (16 * k + l16) * LDK + 32 * s + 8 * g);
+      const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * i + l16) * LDK + 32 * s + 8 * g);
+      a = mfma_bf16(fa, fb, a);
+    }
+    // a[e] = k_c . k_r for c = 16 k + 4 g + e, r = 16 i + l16 (r > c)
+    const int r = 16 * i + l16;
+    const float gr = gw[r];
+    const f32x4 gc = ld4(gw + 16 * k + 4 * g);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = -(exp2_hw(gr - gc[e]) * a[e]);
+    *reinterpret_cast<u32x2 *>(sT + r * LDT + 32 * (k >> 1) + 8 * g + 4 * (k & 1)) = pk4u(v);
+  }
+  // after iteration `it` of the wave's K S^T product (16 iterations of two MFMAs)
+  __device__ __forceinline__ void hook(int it, const bf16_t *sK, bf16_t *sT, const float *gw, int wave, int l16, int g) {
+    if (it == 0) gram(sK, wave, l16, g);
+    if (it == 2) scale(gw, wave, l16, g);
+    if (it == 3) level(1);
+    if (it == 5) level(2);
+    if (it == 7) offdiag(sK, sT, gw, wave, l16, g);
+    if (it == 8) level(3);
+    if (it == 11) level(4);
+    if (it == 12 && wave + 4 < 6) offdiag(sK, sT, gw, wave + 4, l16, g);
+    if (it == 14) store_d(sT, gw, wave, l16, g);
+  }
+};
+
+// The forward substitution, step k (0..6) after iteration 2 k + 1 of the S Q^T product; U
+// holds Y on entry and U on exit.
+struct Subst {
+  v4i16 dA0, dA1, dA2, dA3, nL10, nL32;
+  bf16x8 nL2, nL3;
+  __device__ __forceinline__ void load(const bf16_t *sT, int l16, int g) {
+    auto a4 = [&](int row, int pos) {
+      return __builtin_bit_cast(v4i16, *reinterpret_cast<const bf16x4 *>(sT + row * LDT + pos));
+    };
+    dA0 = a4(l16, 8 * g);
+    dA1 = a4(16 + l16, 8 * g + 4);
+    dA2 = a4(32 + l16, 32 + 8 * g);
+    dA3 = a4(48 + l16, 32 + 8 * g + 4);
+    nL10 = a4(16 + l16, 8 * g);
+    nL32 = a4(48 + l16, 32 + 8 * g);
+    nL2 = *reinterpret_cast<const bf16x8 *>(sT + (32 + l16) * LDT + 8 * g);
+    nL3 = *reinterpret_cast<const bf16x8 *>(sT + (48 + l16) * LDT + 8 * g);
+  }
+  template <int NCT> __device__ __forceinline__ void step(int k, f32x4 (&U)[4][NCT]) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      if (k == 0) U[0][c] = mfma_k16(dA0, pk4(U[0][c]), z);
+      if (k == 1) U[1][c] = mfma_k16(nL10, pk4(U[0][c]), U[1][c]);
+      if (k == 2) U[1][c] = mfma_k16(dA1, pk4(U[1][c]), z);
+      if (k == 3) {
+        const bf16x8 p01 = pack_pair(U[0][c], U[1][c]);
+        U[2][c] = mfma_bf16(nL2, p01, U[2][c]);
+        U[3][c] = mfma_bf16(nL3, p01, U[3][c]);
+      }
+      if (k == 4) U[2][c] = mfma_k16(dA2, pk4(U[2][c]), z);
+      if (k == 5) U[3][c] = mfma_k16(nL32, pk4(U[2][c]), U[3][c]);
+      if (k == 6) U[3][c] = mfma_k16(dA3, pk4(U[3][c]), z);
+    }
+  }
+};
+
 template <bool DELTA, int DK>
 __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args a) {
   constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NCT = Geo<DK>::NCT, RPW = 16 * NCT, LDK = DK + 16;
   constexpr int ROWS = NW * RPW, LDVR = ROWS + 16;  // state rows of a workgroup; its V tile's row stride
   constexpr int NRB = DV / ROWS;       // row blocks (workgroups) per segment
   constexpr int NIT = 4 * (DK / 32);   // (token tile, key step) pairs of a K S^T / Q S^T product
+  constexpr bool FORM = DELTA && DK == 128;  // the chunk solve formed here (form_solve_blocks)
+  static_assert(!FORM || NW == 4, "one diagonal block of the chunk solve per wave");
   __shared__ __attribute__((aligned(16))) bf16_t sR0[C * LDK], sR1[C * LDK], sV[C * LDVR];
   __shared__ __attribute__((aligned(16))) bf16_t sT[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];
@@ -1075,7 +1300,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     const size_t rb = bh * (size_t)T + t0;
     dma_tile<ROWS * 2, LDVR * 2, C, NW, false, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
                                                        (unsigned char *)sV, wave, ln);
-    if (DELTA)
+    if (DELTA && !FORM)
       dma_tb<NW, false>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
                  (unsigned char *)sT, wave, ln);
   };
@@ -1129,8 +1354,20 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     // ---- phase 1: U on this wave's rows, as operands with k = tokens (ufr), and with the
     // decay to the chunk end applied (dufr)
     bf16x8 ufr[NCT][2], dufr[NCT][2];
+    f32x4 U[4][NCT];  // (FORM: Y until the substitution after the barrier)
+    auto u_frags = [&]() {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f32x4 d0 = ld4(gw + 128 + 32 * s2 + 4 * g), d1 = ld4(gw + 128 + 32 * s2 + 16 + 4 * g);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          ufr[c][s2] = pack_pair(U[2 * s2][c], U[2 * s2 + 1][c]);
+          dufr[c][s2] = pack_pair(U[2 * s2][c] * d0, U[2 * s2 + 1][c] * d1);
+        }
+      }
+    };
+    ChunkSolve<LDK> cs;  // (FORM)
     {
-      f32x4 U[4][NCT];
       if (DELTA) {
         // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T (K fragments two steps ahead),
         // Y in registers (V read along tokens), then the lower-triangular product with TB
@@ -1152,9 +1389,10 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
 #pragma unroll
               for (int c = 0; c < NCT; ++c) sfr[c] = pack_pair(st[2 * s][c], st[2 * s + 1][c]);
             }
-            LA_FENCE();
+              LA_FENCE();
 #pragma unroll
             for (int c = 0; c < NCT; ++c) ks[mt][c] = mfma_bf16(kf[it % 3], sfr[c], ks[mt][c]);
+            if constexpr (FORM) cs.hook(it, sK, sT, gw, wave, l16, g);
           }
         }
 #undef LA_KF
@@ -1172,9 +1410,15 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
               y0[e] += (float)vf[e];
               y1[e] += (float)vf[4 + e];
             }
-            yfr[c][s] = pack_pair(y0, y1);
+            if constexpr (FORM) {
+              U[2 * s][c] = y0;
+              U[2 * s + 1][c] = y1;
+            } else {
+              yfr[c][s] = pack_pair(y0, y1);
+            }
           }
         }
+        if constexpr (!FORM) {
         // steps (mt, s), s = 1 only for mt >= 2 (T is lower triangular); the TB fragment of
         // the next step is read before this step's MFMAs
         bf16x8 tfb[2];
@@ -1193,6 +1437,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
           for (int c = 0; c < NCT; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
         }
 #undef LA_TF
+        }
       } else {  // U = diag(beta) V, read along tokens from the V tile
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -1209,20 +1454,11 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
         }
       }
       LA_FENCE();
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const f32x4 d0 = ld4(gw + 128 + 32 * s2 + 4 * g), d1 = ld4(gw + 128 + 32 * s2 + 16 + 4 * g);
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-          ufr[c][s2] = pack_pair(U[2 * s2][c], U[2 * s2 + 1][c]);
-          dufr[c][s2] = pack_pair(U[2 * s2][c] * d0, U[2 * s2 + 1][c] * d1);
-        }
-      }
+      if constexpr (!FORM) u_frags();
     }
     lds_dma_wait();
     lds_barrier();  // Q of chunk ci has landed; V and TB of chunk ci are no longer read
     if (more) issue_vt(ci + 1, lane_v);
-
     // ---- phase 2: decay-masked Q K^T tiles (ti, tj <= ti), dealt round robin over the
     // waves, each computed as its transpose K Q^T: lane (g, l16) holds A[t][j] for token
     // t = 16 ti + l16 and keys j = 16 tj + 4 g + 0..3, stored in row t at the positions of
@@ -1230,6 +1466,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     // (at d = 256 on the first four waves only: a cycle probe per phase showed the other
     // four, which share their SIMDs, finishing each phase last; 1% faster than over all eight)
     constexpr int NJW = NW == 8 ? 4 : NW;
+    auto qk_jobs = [&]() {
 #pragma unroll
     for (int m = 0; m < (10 + NJW - 1) / NJW; ++m) {
       const int job = wave + NJW * m;
@@ -1249,10 +1486,11 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (16 * tj + 4 * g + e <= t) ? exp2_hw(gt - gj[e]) * acc[e] : 0.0f;
-        *reinterpret_cast<bf16x4 *>(sA + t * LDA + 32 * (tj >> 1) + 8 * g + 4 * (tj & 1)) =
-            bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<u32x2 *>(sA + t * LDA + 32 * (tj >> 1) + 8 * g + 4 * (tj & 1)) = pk4u(v);
       }
     }
+    };
+    if constexpr (!FORM) qk_jobs();
     // O^T = S Q^T on this wave's rows: lane (g, l16) of tile (mt, c) holds
     // O[16 mt + l16][row0 + 8 g + 4 c + e] (Q fragments two steps ahead)
     f32x4 O[4][NCT];
@@ -1270,6 +1508,10 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     {
 #define LA_QF(it) *reinterpret_cast<const bf16x8 *>(sQ + (16 * ((it) % 4) + l16) * LDK + 32 * ((it) / 4) + 8 * g)
       bf16x8 qb[3], sfr[NCT];
+      // (FORM) U by forward substitution over the token blocks (Subst), one step after
+      // every other iteration
+      Subst sub;
+      if constexpr (FORM) sub.load(sT, l16, g);
       qb[0] = LA_QF(0);
       qb[1] = LA_QF(1);
 #pragma unroll
@@ -1283,8 +1525,15 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
         LA_FENCE();
 #pragma unroll
         for (int c = 0; c < NCT; ++c) O[mt][c] = mfma_bf16(sfr[c], qb[it % 3], O[mt][c]);
+        if constexpr (FORM) {
+          if (it % 2 == 1 && it / 2 < 7) sub.step(it / 2, U);
+        }
       }
 #undef LA_QF
+    }
+    if constexpr (FORM) {
+      u_frags();
+      qk_jobs();
     }
     lds_barrier();  // every wave's A tiles are written; Q of chunk ci is no longer read
     if (more) issue_kg(ci + 1, sQ, lane_v);
@@ -1315,8 +1564,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
                   __builtin_bit_cast(u32x4, pack_pair(O[mt][0], O[mt][1])));
           else  // outputs row0 + 4 g .. +3
             bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + row0 + 4 * g),
-                 __builtin_bit_cast(u32x2, bf16x4{(__bf16)O[mt][0][0], (__bf16)O[mt][0][1], (__bf16)O[mt][0][2],
-                                                  (__bf16)O[mt][0][3]}));
+                 pk4u(O[mt][0]));
         }
       }
 #undef LA_AF
@@ -1434,13 +1682,41 @@ template <int DK>
 void launch_passes(const Args &a, bool delta, int pass_mask, hipStream_t s) {
   constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NRB = DV / (NW * 16 * Geo<DK>::NCT);
   const int B = a.B, H = a.H;
+  // At d = 128 the replay forms its own chunk solve, and the stored transforms serve the map
+  // pass alone: pass 0 covers the windows of the mapped segments, and the map pass, in three
+  // launches, maps the windows, transforms the rest of the segments whose window transition
+  // is not zero, and maps those segments whole.
+  const bool windows_apart = delta && DK == 128 && a.nseg > 1;
+  const int cw = a.seg_chunks > 2 * MAP_WINDOW ? a.seg_chunks - MAP_WINDOW : 0;
   if (delta && (pass_mask & PASS_TRANSFORM)) {
-    const int64_t chunks = (int64_t)B * H * a.nch;
-    hipLaunchKernelGGL((tprep_kernel<DK>), dim3((unsigned)((chunks + TPW - 1) / TPW)), dim3(TPW * 64), 0, s, a);
+    Args t = a;
+    int64_t chunks = (int64_t)B * H * a.nch;
+    if (DK == 128) {
+      t.tp_mode = 1;
+      t.map_cw = cw;
+      chunks = windows_apart && cw > 0 ? (int64_t)B * H * (a.nseg - 1) * MAP_WINDOW : 0;
+    }
+    if (chunks > 0)
+      hipLaunchKernelGGL((tprep_kernel<DK>), dim3((unsigned)((chunks + TPW - 1) / TPW)), dim3(TPW * 64), 0, s, t);
   }
   if (a.nseg > 1 && (pass_mask & PASS_MAPS)) {
     // every segment but the last (whose end state only the replay needs)
-    if (delta) {
+    if (windows_apart) {
+      constexpr int NWT = map_waves<true, DK>(), NMB = (DV + DK) / (NWT * 16 * MapGeo<DK>::NCT);
+      static_assert(DK != 128 || NMB == 1, "one map workgroup per segment");
+      const dim3 grid(seg_grid(a.nseg - 1, NMB), H, B), block(map_threads<true, DK>());
+      Args m = a;
+      m.map_mode = 1;
+      hipLaunchKernelGGL((map_kernel<true, DK>), grid, block, 0, s, m);
+      Args t = a;
+      t.tp_mode = 2;
+      t.map_cw = cw;
+      const int cwp = cw > 0 ? cw : a.seg_chunks, gx = (cwp + TPW * 8 - 1) / (TPW * 8);
+      hipLaunchKernelGGL((tprep_kernel<DK>), dim3((unsigned)gx, (unsigned)(B * H * (a.nseg - 1))), dim3(TPW * 64), 0,
+                         s, t);
+      m.map_mode = 2;
+      hipLaunchKernelGGL((map_kernel<true, DK>), grid, block, 0, s, m);
+    } else if (delta) {
       constexpr int NWT = map_waves<true, DK>(), NMB = (DV + DK) / (NWT * 16 * MapGeo<DK>::NCT);
       hipLaunchKernelGGL((map_kernel<true, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3(map_threads<true, DK>()), 0,
                          s, a);
@@ -1505,6 +1781,10 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   a.tb = delta ? (bf16_t *)(ws + w.tb) : nullptr;
   a.T = T;
   a.nch = (T + C - 1) / C;
+  a.tp_nch = a.nch;
+  a.tp_mode = 0;
+  a.map_mode = 0;
+  a.map_cw = 0;
   a.B = B;
   a.H = H;
   a.nseg = p.nseg;

@@ -166,15 +166,18 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
  *                        la_prefill_pass(LA_PASS_SCAN, ...);
  *                        la_prefill_pass(LA_PASS_REPLAY, ...);
  *
- *   LA_PASS_TRANSFORM  gated delta rule on the chunked path: every chunk's UT transform
- *                      (I + L)^{-1} diag(beta), which depends on keys and gates only,
- *                      written to the workspace for the two passes that follow
+ *   LA_PASS_TRANSFORM  gated delta rule on the chunked path: the UT transforms
+ *                      (I + L)^{-1} diag(beta) of chunks, which depend on keys and gates
+ *                      only, written to the workspace for the passes that follow: at
+ *                      d_k = 256 every chunk's; at d_k = 128 those of each mapped segment's
+ *                      last 8 chunks (the replay forms its own from the keys it loads)
  *   LA_PASS_MAPS       per segment of chunks except the last, the affine map of its end
  *                      state on its start state (S_end = S_start M + B; M is d_k x d_k
  *                      for the gated delta rule, a scalar decay otherwise), written to
  *                      the workspace (when the decay over a segment's last 8 chunks takes
  *                      M to exactly zero in fp32, the map is formed from those chunks
- *                      alone: M = 0, B theirs)
+ *                      alone: M = 0, B theirs; at d_k = 128 the gated delta rule's other
+ *                      segments get the transforms of their remaining chunks here first)
  *   LA_PASS_SCAN       segment start states S_{i+1} = S_i M_i + B_i from S0
  *   LA_PASS_REPLAY     every segment from its start state: o, and S_T from the last one
  *
