@@ -524,6 +524,32 @@ __device__ __forceinline__ void dma_tile(u32x4 r, unsigned char *lds, int wave, 
   }
 }
 
+// dma_tile with the source offsets of this wave's wave-instructions (j = NWAVES m + wave)
+// computed once, for a kernel that loads the same tile shape every chunk: the offsets do
+// not depend on the chunk, and forming each (a division by the padded row length) costs
+// about ten VALU instructions per load.
+template <int ROWB, int LDB, int ROWS, int NWAVES, int SRCB = ROWB> struct TileOffsets {
+  static constexpr int NI = ROWS * LDB / 1024, NM = (NI + NWAVES - 1) / NWAVES;
+  static_assert(ROWS * LDB % 1024 == 0, "whole wave-instructions");
+  uint32_t off[NM];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int p = 1024 * (NWAVES * m + wave) + 16 * lane;
+      const int row = p / LDB, o = p - row * LDB;
+      off[m] = o < ROWB ? (uint32_t)(row * SRCB + o) : 0xFFFFFFF0u;
+    }
+  }
+  template <bool NT> __device__ __forceinline__ void issue(u32x4 r, unsigned char *lds, int wave) const {
+    const uint32_t base = lds_addr(lds);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int j = NWAVES * m + wave;
+      if (j < NI) lds_dma16<NT>(r, off[m], base + 1024u * (uint32_t)j);
+    }
+  }
+};
+
 // A stored transform (6 KB, tb_offset layout) into a row-padded LDS tile of row stride LDT:
 // 10 wave-instructions of 1 KB; LDS bytes that the stored layout omits (right of the
 // diagonal in rows 0..31) and the row padding are zero-filled.
@@ -1249,6 +1275,9 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   constexpr int NIT = 4 * (DK / 32);   // (token tile, key step) pairs of a K S^T / Q S^T product
   constexpr bool FORM = DELTA && DK == 128;  // the chunk solve formed here (form_solve_blocks)
   static_assert(!FORM || NW == 4, "one diagonal block of the chunk solve per wave");
+  // load offsets computed once (TileOffsets) where the registers allow: not at d = 256,
+  // whose 256 registers per lane would spill more
+  constexpr bool TOFF = DK == 128;
   __shared__ __attribute__((aligned(16))) bf16_t sR0[C * LDK], sR1[C * LDK], sV[C * LDVR];
   __shared__ __attribute__((aligned(16))) bf16_t sT[DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];
@@ -1293,13 +1322,21 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   int nchunks = a.seg_chunks;
   if (first + (int64_t)nchunks * C > T) nchunks = (int)((T - first + C - 1) / C);
 
+  // The K, Q and V tiles have one shape (rows of 2 d bytes padded to 2 LDK): one set of
+  // load offsets serves all three.
+  static_assert(ROWS == DK && LDVR == LDK && DV == DK, "K, Q and V tiles of one shape");
+  TileOffsets<DK * 2, LDK * 2, C, NW> toff;
+  if (TOFF) toff.init(wave, lane);
+  auto load_tile = [&](u32x4 r, bf16_t *lds, int ln) {
+    if constexpr (TOFF) toff.template issue<false>(r, (unsigned char *)lds, wave);
+    else dma_tile<DK * 2, LDK * 2, C, NW, false>(r, (unsigned char *)lds, wave, ln);
+  };
   // chunk ci's V and TB tiles (ln: the lane index, an opaque per-chunk copy in the loop)
   auto issue_vt = [&](int ci, int ln) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<ROWS * 2, LDVR * 2, C, NW, false, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
-                                                       (unsigned char *)sV, wave, ln);
+    load_tile(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2), sV, ln);
     if (DELTA && !FORM)
       dma_tb<NW, false>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2),
                  (unsigned char *)sT, wave, ln);
@@ -1309,15 +1346,14 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
     const size_t rb = bh * (size_t)T + t0;
-    dma_tile<DK * 2, LDK * 2, C, NW, false>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, wave, ln);
+    load_tile(rsrc_words(a.k + rb * DK, n * DK * 2), dK, ln);
     if (wave == 0 && !additive) lds_dma2<false>(rsrc_words(a.alpha + rb, n * 2), 2u * ln, lds_addr(sGraw[0]));
     if (wave == 1 && use_beta) lds_dma2<false>(rsrc_words(a.beta + rb, n * 2), 2u * ln, lds_addr(sGraw[1]));
   };
   auto issue_q = [&](int ci, bf16_t *dQ, int ln) {
     const int64_t t0 = first + (int64_t)ci * C;
     const uint32_t n = (uint32_t)((T - t0) < C ? (T - t0) : C);
-    dma_tile<DK * 2, LDK * 2, C, NW, false>(rsrc_words(a.q + (bh * (size_t)T + t0) * DK, n * DK * 2), (unsigned char *)dQ,
-                                     wave, ln);
+    load_tile(rsrc_words(a.q + (bh * (size_t)T + t0) * DK, n * DK * 2), dQ, ln);
   };
   // gates of chunk ci from the raw values (alpha = 1, beta = 0 past the sequence end)
   auto gates = [&](int ci) {
