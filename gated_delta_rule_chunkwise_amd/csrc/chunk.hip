@@ -1695,15 +1695,17 @@ WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d, const Plan &p) {
 // at once (two per CU at d = 128, one at d = 256, whose workgroups are twice as wide), but
 // only when the heads alone cannot fill half of it (a split costs one extra pass over the
 // keys and values).  More segments leave the replay's time unchanged and lengthen the scan, a
-// chain of one dependent step per segment.  Up to 2048 chunks per (b, h) at d = 128, half a
-// round (one replay workgroup per CU): the scan's chain and the map pass's second round then
-// cost more than the replay's lower occupancy (64K tokens x 16 heads: 0.533 against 0.551 ms;
-// equal at 256K, 7.74 against 7.55 ms at 1M).  Fewer when the workspace must stay within
-// `cap` bytes.
+// chain of one dependent step per segment.  At d = 128 the full round (two replay
+// workgroups per CU) is taken only when its segments keep at least 32 chunks each; shorter
+// segments lose the map pass's 8-chunk window (it needs more than 16) and lengthen the
+// scan, so half a round is taken instead (16 heads: 64K tokens 0.339 -> 0.323 ms with the
+// full round, 32K tokens 0.204 -> 0.314 ms; 4 heads x 64K tokens, 8 chunks per segment in a
+// full round, 0.270 -> 0.371 ms).  Fewer when the workspace must stay within `cap` bytes.
 Plan make_plan(bool delta, int B, int H, int64_t T, int dv, size_t cap) {
   const int64_t nch = (T + C - 1) / C;
   const int64_t units = (int64_t)B * H;  // a replay workgroup carries a whole state
-  const int64_t slots = (dv == 128 && nch > 2048) ? 512 : 256;
+  int64_t slots = 256;
+  if (dv == 128 && units < 128 && nch / ((512 + units - 1) / units) >= 32) slots = 512;
   Plan p = plan_of(nch, units < 128 ? (slots + units - 1) / units : 1);
   while (p.nseg > 1 && ws_layout(delta, B, H, T, dv, p).total > cap) p = plan_of(nch, p.nseg / 2);
   return p;
