@@ -300,11 +300,9 @@ def bench_gdn_prefill(torch, la, synth, dev, stream, B, H, T, D, steps, warmup, 
     pass_stats = {kk: stats(vv) for kk, vv in per_pass.items()}
     dom = max(pass_stats, key=lambda kk: pass_stats[kk]["mean"])
     wide = "" if D == 128 else f", {D}"
-    if D == 128:  # the replay forms each chunk's solve; stored transforms serve the map pass
+    if D == 128:  # the map and replay passes form each chunk's solve: no transform pass
         kernels = {"replay": "replay_kernel<true> (replay pass, forming each chunk's solve from its keys)",
-                   "maps": "map_kernel<true> (the segments' last 8 chunks), tprep_kernel and map_kernel<true> "
-                           "(the other chunks of segments whose transition over those 8 is not zero)",
-                   "transform": "tprep_kernel (UT transforms of the segments' last 8 chunks)",
+                   "maps": "map_kernel<true> (segment-map pass; helper waves form each chunk's solve blocks)",
                    "scan": "scan_delta_kernel (segment scan)"}
     else:
         kernels = {"replay": f"replay_kernel<true{wide}> (replay pass)",

@@ -136,8 +136,8 @@ def prefill_passes(variant, dtype, B, H, T, d_k, d_v):
     """The passes la_prefill runs for this problem, in order: calling la_prefill_pass with
     each in turn (same buffers, one workspace) is la_prefill."""
     nseg, _ = segments(variant, dtype, B, H, T, d_k, d_v)
-    ps = [PASS_TRANSFORM] if (_var(variant) == GATED_DELTA and dtype == BF16 and d_k == d_v
-                              and d_k in (128, 256)) else []
+    # the stored transforms exist at d = 256 only (at 128 the passes form each chunk's solve)
+    ps = [PASS_TRANSFORM] if (_var(variant) == GATED_DELTA and dtype == BF16 and d_k == d_v == 256) else []
     if nseg > 1:
         ps += [PASS_MAPS, PASS_SCAN]
     return ps + [PASS_REPLAY]

@@ -17,14 +17,14 @@
 //   S' = gamma_C S + U^T diag(e^{g_C - g}) K  =  S M_c + B_c
 //
 // T is the UT/WY transform of the chunk.  It depends on the keys and gates only.  At
-// d = 128 the replay forms what it needs of it per chunk from the K tile already in LDS (the
-// diagonal blocks (I + L_bb)^{-1} by doubling products, then U by forward substitution over
-// the chunk's 16-token blocks; ChunkSolve below), so no transform crosses HBM on the way to
-// the outputs.  The map pass reads stored transforms (pass 0 below: one wave per chunk forms
-// L from a K K^T Gram on bf16 MFMA, solves (I + L) T = I in fp32 by blocked forward
-// substitution (16 x 16 diagonal blocks on the VALU, the off-diagonal blocks on fp32 MFMA),
-// and stores T diag(beta) in bf16); at d = 128 only for the chunks it carries.  At d = 256
-// pass 0 covers every chunk and the replay reads the stored transforms too.  Every product
+// d = 128 the map and replay passes form what they need of it per chunk from the K tile
+// already in LDS (the diagonal blocks (I + L_bb)^{-1} by doubling products, then U by
+// forward substitution over the chunk's 16-token blocks; ChunkSolve, Subst below), so no
+// transform crosses HBM.  At d = 256 both read stored transforms, computed for every chunk
+// at once before any state is carried (pass 0 below: one wave per chunk forms L from a K K^T
+// Gram on bf16 MFMA, solves (I + L) T = I in fp32 by blocked forward substitution (16 x 16
+// diagonal blocks on the VALU, the off-diagonal blocks on fp32 MFMA), and stores T diag(beta)
+// in bf16).  Every product
 // with a 64- or 128-wide inner dimension runs on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with
 // fp32 accumulation; the state stays fp32.
 //
@@ -50,12 +50,8 @@
 //                          nothing to chain when every transition is zero)
 //   pass 3 (replay_kernel) every segment replayed from its start state, writing o; the
 //                          last segment also writes S_T
-// With one segment (enough heads to fill the chip) only pass 3 runs.  For the delta rule
-// pass 0 (tprep_kernel) precedes pass 1 (at d = 256 also pass 3 when there is one
-// segment).  At d = 128 pass 0 transforms the segments' last 8 chunks only, and pass 1 is
-// three launches: the maps of those 8 chunks (flagging each segment whose transition over
-// them is exactly zero, for which that map is the segment's), the transforms of the other
-// chunks of the segments not flagged, and the maps of those segments over all their chunks.
+// With one segment (enough heads to fill the chip) only pass 3 runs.  For the delta rule at
+// d = 256 pass 0 (tprep_kernel) precedes pass 1 (or pass 3 when there is one segment).
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -87,7 +83,10 @@ template <> struct Geo<256> { static constexpr int DK = 256, DV = 256, NW = 8, N
 template <int DK_> struct MapGeo { static constexpr int NCT = Geo<DK_>::NCT; };
 template <bool DELTA, int DK> constexpr int map_waves() { return (DELTA || DK == 256) ? 8 : 4; }
 template <int DK> constexpr bool map_loader() { return DK != 256; }
-template <bool DELTA, int DK> constexpr int map_threads() { return (map_waves<DELTA, DK>() + (map_loader<DK>() ? 1 : 0)) * 64; }
+// waves beside the state waves: at d = 128 one issues every load; for the delta rule there
+// it and three more form each chunk's solve blocks, one per SIMD
+template <bool DELTA, int DK> constexpr int map_helpers() { return map_loader<DK>() ? (DELTA ? 4 : 1) : 0; }
+template <bool DELTA, int DK> constexpr int map_threads() { return (map_waves<DELTA, DK>() + map_helpers<DELTA, DK>()) * 64; }
 
 // A stored transform, T diag(beta) in bf16, row-major in the MFMA k order: rows 0..31 keep
 // only their first 32 positions (the blocks right of the diagonal are zero), rows 32..63 all
@@ -107,13 +106,6 @@ struct Args {
   float *starts;     // [BH][nseg][DV][DK] segment start states
   bf16_t *tb;        // [BH][nch][C][C] per-chunk (T diag(beta))^T (delta rule)
   int64_t T, nch;
-  int64_t tp_nch;    // (tp_mode 0) chunks per (b, h), from the first, that pass 0 transforms
-  int tp_mode;       // pass 0: 0 the first tp_nch chunks; 1 the windows of the mapped segments;
-                     // 2 the chunks before the window of mapped segments not flagged in mzero
-  int map_mode;      // delta-rule map pass: 0 window, then the whole segment unless the window
-                     // suffices; 1 the window only (flags mzero, maps only where it suffices);
-                     // 2 whole segments where mzero is not set
-  int map_cw;        // first window chunk of a mapped segment (0: no window)
   int B, H, nseg, seg_chunks, variant, has_beta;
 };
 
@@ -216,12 +208,11 @@ __device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Pass 0 (delta rule): for the chunks the map pass reads (at d = 256 every chunk, which the
-// replay reads too), TB = (I + L)^{-1} diag(beta), stored transposed (row j of the stored
-// tile is column j of TB) in bf16.  One wave per chunk, four independent waves per workgroup
-// (no barriers); with tp_mode 2 (the chunks of the segments whose window alone does not give
-// the map) each wave takes every (grid width x 4)-th chunk of one segment in turn.  A
-// partial last chunk has zero keys and beta beyond its end, so its TB is zero there.
+// Pass 0 (delta rule, d = 256; at d = 128 the map and replay passes form their own chunk
+// solves): for every chunk, TB = (I + L)^{-1} diag(beta), stored transposed (row j of the
+// stored tile is column j of TB) in bf16.  One wave per chunk, four independent waves per
+// workgroup (no barriers).  A partial last chunk has zero keys and beta beyond its end, so
+// its TB is zero there.
 //
 // Blocked solve on 16 x 16 blocks, in fp32: the four diagonal blocks D_b = (I + L_bb)^{-1}
 // by forward substitution (one lane per column of a block, the four blocks side by side,
@@ -274,7 +265,6 @@ __device__ __forceinline__ void tprep_chunk(const Args &a, int64_t bh, int64_t c
   const int64_t t0 = ck * C;
   const int n = (int)((a.T - t0) < C ? (a.T - t0) : C);
   const size_t base = (size_t)bh * a.T + t0;
-  __asm__ volatile("" ::: "memory");  // (a wave's chunks in turn: the previous one's LDS reads come first)
 
   // K rows as MFMA operands, straight from global memory: kf[rt][s] holds row 16 rt + l16,
   // columns 32 s + 8 grp .. +7 (the A and the B operand of K K^T have the same layout)
@@ -402,38 +392,175 @@ __device__ __forceinline__ void tprep_chunk(const Args &a, int64_t bh, int64_t c
 }
 
 template <int DK>
-__global__ __launch_bounds__(TPW * 64, DK == 128 ? 3 : 2) void tprep_kernel(const Args a) {
+__global__ __launch_bounds__(TPW * 64, 2) void tprep_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) TPrepLds sm[TPW];
   // the wave index is uniform across the wave: saying so keeps every per-chunk address
   // and buffer descriptor in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  int64_t bh, ck;
-  int nloop = 1, stride = 0;
-  if (a.tp_mode == 2) {  // grid (x, mapped segment): the workgroup's waves stride over the chunks
-    const int nm = a.nseg - 1;
-    bh = blockIdx.y / nm;
-    const int seg = blockIdx.y % nm;
-    if (a.mzero[bh * a.nseg + seg]) return;  // its window's map stands
-    const int cwp = a.map_cw > 0 ? a.map_cw : a.seg_chunks, j0 = blockIdx.x * TPW + wave;
-    stride = gridDim.x * TPW;
-    nloop = j0 < cwp ? (cwp - j0 + stride - 1) / stride : 0;
-    ck = (int64_t)seg * a.seg_chunks + j0;
-  } else {
-    const int64_t cid = (int64_t)blockIdx.x * TPW + wave;
-    if (a.tp_mode == 1) {
-      const int64_t per = (int64_t)(a.nseg - 1) * MAP_WINDOW;
-      if (cid >= (int64_t)a.B * a.H * per) return;
-      bh = cid / per;
-      const int64_t r = cid % per;
-      ck = (r / MAP_WINDOW) * a.seg_chunks + a.map_cw + r % MAP_WINDOW;
-    } else {
-      if (cid >= (int64_t)a.B * a.H * a.tp_nch) return;
-      bh = cid / a.tp_nch;
-      ck = cid % a.tp_nch;
+  const int64_t cid = (int64_t)blockIdx.x * TPW + wave;
+  if (cid >= (int64_t)a.B * a.H * a.nch) return;
+  tprep_chunk<DK>(a, cid / a.nch, cid % a.nch, sm[wave], lane);
+}
+
+// 16x16x16 bf16 MFMA (one 16-token block of k): lane (g, i) holds A[i][4 g + e] and
+// B[4 g + e][i], the accumulator rows 4 g + e of column i, so an accumulator tile packed
+// to bf16 is directly a B operand.
+__device__ __forceinline__ f32x4 mfma_k16(v4i16 a, v4i16 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4i16 pk4(f32x4 x) {
+  return __builtin_bit_cast(v4i16, pk4u(x));
+}
+
+// The delta rule's chunk solve formed inside the replay (d = 128) instead of read as a stored
+// transform.  U = (I + L)^{-1} diag(beta) Y, L_tj = beta_t 2^{g_t - g_j} k_t.k_j for j < t,
+// is found by forward substitution over the chunk's four 16-token blocks.  With
+// L = diag(beta) L'' (L''_tj = 2^{g_t - g_j} k_t.k_j),
+//   U_i = D_i diag(beta_i) (Y_i - sum_{k<i} L''_ik U_k),   D_i = (I + L_ii)^{-1},
+// on bf16 MFMA with fp32 accumulation (each U_k enters the later blocks as the same bf16
+// values that the output and state products use).  Per chunk the workgroup writes -L''_ik
+// (i > k) and D_i diag(beta_i) in bf16 into the row-padded tile that holds a stored transform
+// otherwise, in the same MFMA k order (row t, column j = 32 s + 16 h + 4 q + e at position
+// 32 s + 8 q + 4 h + e).  Wave b inverts diagonal block b; the six blocks below the
+// diagonal are dealt over the waves.  L_bb = N is nilpotent (N^16 = 0), so
+//   D_b = (I - N)(I + N^2)(I + N^4)(I + N^8),
+// four levels of 16 x 16 products on 16x16x16 bf16 MFMA with fp32 accumulation.  D_b is
+// rounded to bf16 for the substitution in any case; the products' own rounding only
+// reaches the terms of second and higher order in N, and the error they add to U is below
+// that rounding's (seeded trials against fp64 with keys of norm up to 2, fast and slow
+// decay: the same U errors as with D_b solved exactly in fp64).  The transposed forms are carried
+// beside the powers, since an accumulator tile of X^T is X as an A operand:
+//   N^2 = N N, (N^2)^T = N^T N^T, N^4, (N^4)^T likewise, N^8 = N^4 N^4, and
+//   P^T <- P^T + (N^k)^T P^T from P^T = I - N^T, which ends as D_b^T: D_b as an A operand.
+// g (log2 decay prefix) is gw[0..63], beta gw[192..255].
+// c + X Y for 16 x 16 tiles held as accumulators: at = X^T, b = Y
+__device__ __forceinline__ f32x4 prod16(f32x4 at, f32x4 b, f32x4 c) { return mfma_k16(pk4(at), pk4(b), c); }
+// The pieces of the chunk solve, in steps that the replay spreads over its K S^T product (the
+// blocks of L and D) and its S Q^T product (the substitution), whose independent MFMAs fill
+// the latency between one dependent step and the next.
+template <int LDK, int DK, int NW> struct ChunkSolve {
+  static constexpr int NIT = 4 * (DK / 32), SP = NIT / 16;  // K S^T iterations; hook spacing
+  f32x4 acc, n, nt, pt, n2, n2t, n4, n4t, n8;
+  // diagonal block b = wave: the Gram block (k_r . k_i, r = 16 b + 4 g + e, i = 16 b + l16)
+  __device__ __forceinline__ void gram(const bf16_t *sK, int b, int l16, int g) {
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sK + (16 * b + l16) * LDK + 32 * s + 8 * g);
+      acc = mfma_bf16(kf, kf, acc);
     }
   }
-  for (int i = 0; i < nloop; ++i, ck += stride) tprep_chunk<DK>(a, bh, ck, sm[wave], lane);
-}
+  // N[r][i] (r > i) and N^T[r][i] = N[i][r] (i > r) in accumulator layout; P^T = I - N^T
+  __device__ __forceinline__ void scale(const float *gw, int b, int l16, int g) {
+    const float gi = gw[16 * b + l16], bi = gw[192 + 16 * b + l16];
+    const f32x4 gr = ld4(gw + 16 * b + 4 * g), br = ld4(gw + 192 + 16 * b + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // one decay per entry: 2^{g_r - g_i} below the diagonal, 2^{g_i - g_r} above
+      const int r = 4 * g + e;
+      const float d = gr[e] - gi, x = acc[e] * exp2_hw(r > l16 ? d : -d);
+      n[e] = r > l16 ? br[e] * x : 0.0f;
+      nt[e] = l16 > r ? bi * x : 0.0f;
+      pt[e] = (r == l16 ? 1.0f : 0.0f) - nt[e];
+    }
+  }
+  __device__ __forceinline__ void level(int l) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    if (l == 1) {
+      n2 = prod16(nt, n, z);
+      n2t = prod16(n, nt, z);
+    } else if (l == 2) {
+      pt = prod16(n2, pt, pt);
+      n4 = prod16(n2t, n2, z);
+      n4t = prod16(n2, n2t, z);
+    } else if (l == 3) {
+      pt = prod16(n4, pt, pt);
+      n8 = prod16(n4t, n4, z);
+    } else {
+      pt = prod16(n8, pt, pt);
+    }
+  }
+  // lane (g, l16) holds D_b[l16][4 g + e]: row 16 b + l16 of the tile, stored as D_b diag(beta_b)
+  __device__ __forceinline__ void store_d(bf16_t *sT, const float *gw, int b, int l16, int g) {
+    *reinterpret_cast<u32x2 *>(sT + (16 * b + l16) * LDT + 32 * (b >> 1) + 8 * g + 4 * (b & 1)) =
+        pk4u(pt * ld4(gw + 192 + 16 * b + 4 * g));
+  }
+  // block j of (i, k) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): -diag(beta_i)^{-1} L_ik into the tile
+  __device__ __forceinline__ void offdiag(const bf16_t *sK, bf16_t *sT, const float *gw, int j, int l16, int g) {
+    const int i = j >= 3 ? 3 : (j >= 1 ? 2 : 1), k = j - i * (i - 1) / 2;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sK + (16 * k + l16) * LDK + 32 * s + 8 * g);
+      const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * i + l16) * LDK + 32 * s + 8 * g);
+      a = mfma_bf16(fa, fb, a);
+    }
+    // a[e] = k_c . k_r for c = 16 k + 4 g + e, r = 16 i + l16 (r > c)
+    const int r = 16 * i + l16;
+    const float gr = gw[r];
+    const f32x4 gc = ld4(gw + 16 * k + 4 * g);
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = -(exp2_hw(gr - gc[e]) * a[e]);
+    *reinterpret_cast<u32x2 *>(sT + r * LDT + 32 * (k >> 1) + 8 * g + 4 * (k & 1)) = pk4u(v);
+  }
+  // after iteration `it` of the wave's K S^T product (NIT iterations of two MFMAs).  Four
+  // waves: each inverts diagonal block `wave` and forms blocks wave and wave + 4 below the
+  // diagonal; eight waves: waves 0-3 the diagonal blocks, waves 4-7 the blocks below.
+  __device__ __forceinline__ void hook(int it, const bf16_t *sK, bf16_t *sT, const float *gw, int wave, int l16, int g) {
+    const bool diag = NW == 4 || wave < 4;
+    const int jw = NW == 4 ? wave : wave - 4;  // first block below the diagonal (eight waves: waves 4-7)
+    if (diag) {
+      if (it == 0) gram(sK, wave, l16, g);
+      if (it == 2 * SP) scale(gw, wave, l16, g);
+      if (it == 3 * SP) level(1);
+      if (it == 5 * SP) level(2);
+      if (it == 8 * SP) level(3);
+      if (it == 11 * SP) level(4);
+      if (it == 14 * SP) store_d(sT, gw, wave, l16, g);
+    }
+    if (NW == 4 || wave >= 4) {
+      if (it == 7 * SP) offdiag(sK, sT, gw, jw, l16, g);
+      if (it == 12 * SP && jw + 4 < 6) offdiag(sK, sT, gw, jw + 4, l16, g);
+    }
+  }
+};
+
+// The forward substitution, step k (0..6) after iteration 2 k + 1 of the S Q^T product; U
+// holds Y on entry and U on exit.
+struct Subst {
+  v4i16 dA0, dA1, dA2, dA3, nL10, nL32;
+  bf16x8 nL2, nL3;
+  __device__ __forceinline__ void load(const bf16_t *sT, int l16, int g) {
+    auto a4 = [&](int row, int pos) {
+      return __builtin_bit_cast(v4i16, *reinterpret_cast<const bf16x4 *>(sT + row * LDT + pos));
+    };
+    dA0 = a4(l16, 8 * g);
+    dA1 = a4(16 + l16, 8 * g + 4);
+    dA2 = a4(32 + l16, 32 + 8 * g);
+    dA3 = a4(48 + l16, 32 + 8 * g + 4);
+    nL10 = a4(16 + l16, 8 * g);
+    nL32 = a4(48 + l16, 32 + 8 * g);
+    nL2 = *reinterpret_cast<const bf16x8 *>(sT + (32 + l16) * LDT + 8 * g);
+    nL3 = *reinterpret_cast<const bf16x8 *>(sT + (48 + l16) * LDT + 8 * g);
+  }
+  template <int NCT> __device__ __forceinline__ void step(int k, f32x4 (&U)[4][NCT]) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      if (k == 0) U[0][c] = mfma_k16(dA0, pk4(U[0][c]), z);
+      if (k == 1) U[1][c] = mfma_k16(nL10, pk4(U[0][c]), U[1][c]);
+      if (k == 2) U[1][c] = mfma_k16(dA1, pk4(U[1][c]), z);
+      if (k == 3) {
+        const bf16x8 p01 = pack_pair(U[0][c], U[1][c]);
+        U[2][c] = mfma_bf16(nL2, p01, U[2][c]);
+        U[3][c] = mfma_bf16(nL3, p01, U[3][c]);
+      }
+      if (k == 4) U[2][c] = mfma_k16(dA2, pk4(U[2][c]), z);
+      if (k == 5) U[3][c] = mfma_k16(nL32, pk4(U[2][c]), U[3][c]);
+      if (k == 6) U[3][c] = mfma_k16(dA3, pk4(U[3][c]), z);
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------------------
 // Pass 1 (segment maps), streamed through LDS with direct global-to-LDS loads: one
@@ -445,9 +572,10 @@ __global__ __launch_bounds__(TPW * 64, DK == 128 ? 3 : 2) void tprep_kernel(cons
 // would cap the registers, the state waves share the loads); every state wave forms the
 // gate prefix sums itself, so one barrier per chunk suffices.  A segment is first tried on
 // its last 8 chunks, which suffice when their transition is exactly zero (the window, in
-// map_kernel).  At d = 128 (map_mode 1, then 2) the window and the whole segment are two
-// launches, with the transforms of the segment's other chunks formed in between only where
-// the window does not suffice.
+// map_kernel).  At d = 128 the delta rule's map pass keeps three copies, and four helper
+// waves (one per SIMD, the loader among them) form each chunk's solve blocks one chunk ahead
+// of the state waves, which find U by forward substitution as the replay does: no stored
+// transform.
 // ---------------------------------------------------------------------------------------
 // Buffer descriptor as four words (base, size in bytes), for inline assembly.
 __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
@@ -627,10 +755,18 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   constexpr int LDVM = VW + 16;         // row stride of its V tile
   constexpr int NIT = 4 * (DK / 32);    // (token tile, key step) pairs of a K S^T product
   static_assert(MAPROWS % MWR == 0 && NMB * VW == DV, "every B (and M) row in one workgroup");
-  __shared__ __attribute__((aligned(16))) bf16_t sK0[C * LDK], sK1[C * LDK], sV0[C * LDVM], sV1[C * LDVM];
-  __shared__ __attribute__((aligned(16))) bf16_t sT0[DELTA ? C * LDT : 8], sT1[DELTA ? C * LDT : 8];
+  // d = 128, delta rule (FORMM): four helper waves (the loader the first of them) form each
+  // chunk's solve blocks into the tile a stored transform would occupy, one chunk ahead of
+  // the state waves, from three LDS copies of the tiles (the loads run two chunks ahead)
+  constexpr bool FORMM = DELTA && LOADER;
+  constexpr int NCP = FORMM ? 3 : 2;  // LDS copies of a chunk's tiles
+  __shared__ __attribute__((aligned(16))) bf16_t sKc[NCP][C * LDK], sVc[NCP][C * LDVM];
+  __shared__ __attribute__((aligned(16))) bf16_t sTc[DELTA ? NCP : 1][DELTA ? C * LDT : 8];
   __shared__ __attribute__((aligned(16))) float sGw[NWT][3 * C];
-  __shared__ __attribute__((aligned(16))) uint32_t sGraw[2][2][C];  // per copy: raw alpha, beta
+  __shared__ __attribute__((aligned(16))) float sGl[FORMM ? 4 : 1][FORMM ? 4 * C : 1];  // each helper's g (log2), beta
+  __shared__ __attribute__((aligned(16))) uint32_t sGraw[NCP][2][C];  // per copy: raw alpha, beta
+  bf16_t *const sK0 = sKc[0], *const sK1 = sKc[1], *const sV0 = sVc[0], *const sV1 = sVc[1];
+  bf16_t *const sT0 = sTc[0], *const sT1 = sTc[DELTA ? 1 : 0];
   __shared__ int sZero[8];  // the window's verdict (see below)
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -639,7 +775,6 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   split_block<NMB>((int)blockIdx.x, seg, mb);
   if (NMB > 1 && seg >= a.nseg - 1) return;  // (whole workgroup) past the last mapped segment
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
-  if (DELTA && a.map_mode == 2 && a.mzero[bh * a.nseg + seg]) return;  // the window's map stands
   bool m_kind = DELTA && wave >= HALF;  // transition (M) rows, started from the identity
   const int vcol0 = mb * VW;            // first B row / V column of the workgroup
   int row0 = vcol0 + (m_kind ? wave - HALF : wave) * RPW;  // (unused by the loader)
@@ -678,12 +813,8 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   // neither would see all of them: there every wave of both first carries transition rows
   // over the window (the workgroup's own half and the other's, so that both reach the same
   // verdict), and a zero transition is followed by the window's B rows alone.
-  const int cw = (!additive && nchunks > 2 * MAP_WINDOW && a.map_mode != 2) ? nchunks - MAP_WINDOW : 0;  // (no decay, no window)
+  const int cw = (!additive && nchunks > 2 * MAP_WINDOW) ? nchunks - MAP_WINDOW : 0;  // (no decay, no window)
   constexpr bool SPLIT = DELTA && NMB == 2;
-  if (DELTA && !SPLIT && a.map_mode == 1 && cw == 0) {  // no window: the whole segment in the next launch
-    if (tid == 0) a.mzero[bh * a.nseg + seg] = 0;
-    return;
-  }
   constexpr int NZF = SPLIT ? 8 : 4;  // verdict flags
 
   // chunk ci's tiles and raw gate values into one LDS copy, issued by the loader wave or
@@ -696,13 +827,73 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
     dma_tile<DK * 2, LDK * 2, C, NIW, true>(rsrc_words(a.k + rb * DK, n * DK * 2), (unsigned char *)dK, iw, ln);
     dma_tile<VW * 2, LDVM * 2, C, NIW, true, DV * 2>(rsrc_words(a.v + rb * DV + vcol0, n * DV * 2),
                                                      (unsigned char *)dV, iw, ln);
-    if (DELTA)
+    if (DELTA && !FORMM)
       dma_tb<NIW, true>(rsrc_words(a.tb + (bh * a.nch + (size_t)(t0 / C)) * T_CHUNK, T_CHUNK * 2), (unsigned char *)dT,
                         iw, ln);
     if (!additive && (LOADER || wave == 0)) lds_dma2<true>(rsrc_words(a.alpha + rb, n * 2), 2u * ln, lds_addr(dG));
     if (use_beta && (LOADER || wave == NIW - 1)) lds_dma2<true>(rsrc_words(a.beta + rb, n * 2), 2u * ln, lds_addr(dG + C));
   };
 
+  if constexpr (FORMM) if (wave >= NWT) {
+    // The helper waves (wave NWT, the first, also issues every load), over three copies:
+    // chunk c + 1's tiles land while the state waves work on chunk c - 1 (its loads are
+    // waited for before the barrier that starts chunk c); during chunk c the helpers form
+    // chunk c + 1's solve blocks, helper h the diagonal block h and the blocks h and h + 4
+    // below the diagonal, while chunk c + 2's tiles stream into the copy chunk c - 1 used.
+    // The window's chunks first, then (unless their transition is zero) the whole segment.
+    constexpr int LOADS = 2 * (C * LDK * 2 / 1024) + 2;  // loads per chunk: K, V, alpha, beta
+    static_assert(LDVM == LDK, "K and V tiles of one shape");
+    const int h = wave - NWT;
+    float *gl = sGl[h];
+    auto blocks = [&](int c, int u) {  // chunk c's blocks of this helper from copy u
+      const int64_t t0 = first + (int64_t)c * C;
+      const bool in = (int64_t)lane < T - t0;
+      const float al = in ? bf16_to_f32((bf16_t)sGraw[u][0][lane]) : 1.0f;
+      gl[lane] = wave_prefix_sum(log2f(al));
+      gl[192 + lane] = bf16_to_f32((bf16_t)sGraw[u][1][lane]);
+      __asm__ volatile("" ::: "memory");
+      ChunkSolve<LDK, DK, 4> cs;
+      cs.gram(sKc[u], h, l16, g);
+      cs.offdiag(sKc[u], sTc[u], gl, h, l16, g);
+      cs.scale(gl, h, l16, g);
+      if (h + 4 < 6) cs.offdiag(sKc[u], sTc[u], gl, h + 4, l16, g);
+#pragma unroll
+      for (int l = 1; l <= 4; ++l) cs.level(l);
+      cs.store_d(sTc[u], gl, h, l16, g);
+    };
+    for (int cb = cw; nchunks > 0;) {
+      if (h == 0) {
+        issue(cb, sKc[0], sVc[0], sTc[0], sGraw[0][0], lane);
+        if (cb + 1 < nchunks) {
+          issue(cb + 1, sKc[1], sVc[1], sTc[1], sGraw[1][0], lane);
+          vm_wait<LOADS>();
+        } else {
+          vm_wait<0>();
+        }
+      }
+      __syncthreads();  // chunk cb's tiles have landed
+      blocks(cb, 0);
+      if (h == 0 && cb + 1 < nchunks) vm_wait<0>();
+      for (int ci = cb; ci < nchunks; ci += 3) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const int c = ci + u;
+          if (c < nchunks) {
+            __syncthreads();  // chunk c's blocks formed; chunk c + 1's tiles landed
+            if (h == 0 && c + 2 < nchunks) issue(c + 2, sKc[(u + 2) % 3], sVc[(u + 2) % 3], sTc[(u + 2) % 3],
+                                                 sGraw[(u + 2) % 3][0], lane);
+            if (c + 1 < nchunks) blocks(c + 1, (u + 1) % 3);
+            if (h == 0 && c + 2 < nchunks) vm_wait<0>();
+          }
+        }
+      }
+      if (cb == 0) break;
+      __syncthreads();  // the window's verdict
+      if (sZero[0] & sZero[1] & sZero[2] & sZero[3]) break;
+      cb = 0;
+    }
+    return;
+  }
   if (LOADER && wave == NWT) {
     // The loader wave: chunk ci + 1 streams into one LDS copy while the state waves work
     // on chunk ci in the other; it waits for its loads before each barrier, so after the
@@ -722,7 +913,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
       }
       if (cb == 0) break;
       __syncthreads();  // the window's verdict
-      if ((sZero[0] & sZero[1] & sZero[2] & sZero[3]) || a.map_mode == 1) break;
+      if (sZero[0] & sZero[1] & sZero[2] & sZero[3]) break;
       cb = 0;
     }
     return;
@@ -745,7 +936,8 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
     gseg += gC;
     bf16x8 dufr[NCT][2];
     if (DELTA) {
-      // U = TB (V - diag(gamma) K S^T) (no V for the M rows), as in the replay
+      // U = TB (V - diag(gamma) K S^T) (no V for the M rows), as in the replay; at d = 128
+      // (FORMM) by forward substitution with the blocks the loader wave formed
       f32x4 ks[4][NCT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -772,6 +964,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
 #undef LA_KF
       LA_FENCE();
       bf16x8 yfr[NCT][2];
+      f32x4 U[4][NCT];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const f32x4 ga = ld4(gw + 32 * s + 4 * g), gb = ld4(gw + 32 * s + 16 + 4 * g);
@@ -786,10 +979,20 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
               y1[e] += (float)vf[4 + e];
             }
           }
-          yfr[c][s] = pack_pair(y0, y1);
+          if constexpr (FORMM) {
+            U[2 * s][c] = y0;
+            U[2 * s + 1][c] = y1;
+          } else {
+            yfr[c][s] = pack_pair(y0, y1);
+          }
         }
       }
-      f32x4 U[4][NCT];
+      if constexpr (FORMM) {  // U by forward substitution with the loader's blocks (Subst)
+        Subst sub;
+        sub.load(sT, l16, g);
+#pragma unroll
+        for (int k = 0; k < 7; ++k) sub.step(k, U);
+      } else {
 #define LA_TF(mt, s) *reinterpret_cast<const bf16x8 *>(sT + (16 * (mt) + l16) * LDT + 32 * (s) + 8 * g)
       bf16x8 tfb[2];
       tfb[0] = LA_TF(0, 0);
@@ -809,6 +1012,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
         for (int c = 0; c < NCT; ++c) U[mt][c] = mfma_bf16(tfb[it & 1], yfr[c][s], U[mt][c]);
       }
 #undef LA_TF
+      }
       LA_FENCE();
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -903,6 +1107,23 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
 #pragma unroll
         for (int c = 0; c < NCT; ++c) st[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if constexpr (FORMM) {  // three copies, chunk cj in copy (cj - cb) % 3
+      __syncthreads();  // (the helpers' first barrier: chunk cb's tiles have landed)
+      for (int ci = cb; ci < nchunks; ci += 3) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const int cj = ci + u;
+          if (cj < nchunks) {
+            __syncthreads();  // copy u holds chunk cj and its solve blocks; every wave is done with chunk cj - 1
+            if (m_kind && !m_dead && ((cj - cb) & 7) == 0 && cj > cb) m_dead = rows_zero();
+            if (!m_dead) {
+              const float gCj = gates(cj, sGraw[u][0]);
+              step(sKc[u], sVc[u], sTc[u], gCj);
+            }
+          }
+        }
+      }
+    } else {
     if (!LOADER) issue(cb, sK0, sV0, sT0, sGraw[0][0], lane);
     for (int ci = cb; ci < nchunks; ci += 2) {
       if (!LOADER) lds_dma_wait();
@@ -922,6 +1143,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
           step(sK1, sV1, sT1, gC1);
         }
       }
+    }
     }
     if (phase == 2) break;
     if (SPLIT && phase == 1) {
@@ -943,10 +1165,6 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
     if (zero && !SPLIT) {
       windowed = true;
       break;
-    }
-    if (DELTA && !SPLIT && a.map_mode == 1) {  // the whole segment in the next launch
-      if (tid == 0) a.mzero[bh * a.nseg + seg] = 0;
-      return;
     }
     if (SPLIT) {  // back to the workgroup's own rows
       m_kind = wave >= HALF;
@@ -1116,156 +1334,6 @@ __global__ __launch_bounds__(256) void scan_gated_kernel(const Args a) {
 // chunk (start: K, V, TB landed, previous chunk done; Q landed; A tiles written); they
 // order LDS only, so the output stores of a chunk stay in flight across them.
 // ---------------------------------------------------------------------------------------
-// 16x16x16 bf16 MFMA (one 16-token block of k): lane (g, i) holds A[i][4 g + e] and
-// B[4 g + e][i], the accumulator rows 4 g + e of column i, so an accumulator tile packed
-// to bf16 is directly a B operand.
-__device__ __forceinline__ f32x4 mfma_k16(v4i16 a, v4i16 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v4i16 pk4(f32x4 x) {
-  return __builtin_bit_cast(v4i16, pk4u(x));
-}
-
-// The delta rule's chunk solve formed inside the replay (d = 128) instead of read as a stored
-// transform.  U = (I + L)^{-1} diag(beta) Y, L_tj = beta_t 2^{g_t - g_j} k_t.k_j for j < t,
-// is found by forward substitution over the chunk's four 16-token blocks.  With
-// L = diag(beta) L'' (L''_tj = 2^{g_t - g_j} k_t.k_j),
-//   U_i = D_i diag(beta_i) (Y_i - sum_{k<i} L''_ik U_k),   D_i = (I + L_ii)^{-1},
-// on bf16 MFMA with fp32 accumulation (each U_k enters the later blocks as the same bf16
-// values that the output and state products use).  Per chunk the workgroup writes -L''_ik
-// (i > k) and D_i diag(beta_i) in bf16 into the row-padded tile that holds a stored transform
-// otherwise, in the same MFMA k order (row t, column j = 32 s + 16 h + 4 q + e at position
-// 32 s + 8 q + 4 h + e).  Wave b inverts diagonal block b; the six blocks below the
-// diagonal are dealt over the waves.  L_bb = N is nilpotent (N^16 = 0), so
-//   D_b = (I - N)(I + N^2)(I + N^4)(I + N^8),
-// four levels of 16 x 16 products on 16x16x16 bf16 MFMA with fp32 accumulation.  D_b is
-// rounded to bf16 for the substitution in any case; the products' own rounding only
-// reaches the terms of second and higher order in N, and the error they add to U is below
-// that rounding's (seeded trials against fp64 with keys of norm up to 2, fast and slow
-// decay: the same U errors as with D_b solved exactly in fp64).  The transposed forms are carried
-// beside the powers, since an accumulator tile of X^T is X as an A operand:
-//   N^2 = N N, (N^2)^T = N^T N^T, N^4, (N^4)^T likewise, N^8 = N^4 N^4, and
-//   P^T <- P^T + (N^k)^T P^T from P^T = I - N^T, which ends as D_b^T: D_b as an A operand.
-// g (log2 decay prefix) is gw[0..63], beta gw[192..255].
-// c + X Y for 16 x 16 tiles held as accumulators: at = X^T, b = Y
-__device__ __forceinline__ f32x4 prod16(f32x4 at, f32x4 b, f32x4 c) { return mfma_k16(pk4(at), pk4(b), c); }
-// The pieces of the chunk solve, in steps that the replay spreads over its K S^T product (the
-// blocks of L and D) and its S Q^T product (the substitution), whose independent MFMAs fill
-// the latency between one dependent step and the next.
-template <int LDK> struct ChunkSolve {
-  f32x4 acc, n, nt, pt, n2, n2t, n4, n4t, n8;
-  // diagonal block b = wave: the Gram block (k_r . k_i, r = 16 b + 4 g + e, i = 16 b + l16)
-  __device__ __forceinline__ void gram(const bf16_t *sK, int b, int l16, int g) {
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sK + (16 * b + l16) * LDK + 32 * s + 8 * g);
-      acc = mfma_bf16(kf, kf, acc);
-    }
-  }
-  // N[r][i] (r > i) and N^T[r][i] = N[i][r] (i > r) in accumulator layout; P^T = I - N^T
-  __device__ __forceinline__ void scale(const float *gw, int b, int l16, int g) {
-    const float gi = gw[16 * b + l16], bi = gw[192 + 16 * b + l16];
-    const f32x4 gr = ld4(gw + 16 * b + 4 * g), br = ld4(gw + 192 + 16 * b + 4 * g);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {  // one decay per entry: 2^{g_r - g_i} below the diagonal, 2^{g_i - g_r} above
-      const int r = 4 * g + e;
-      const float d = gr[e] - gi, x = acc[e] * exp2_hw(r > l16 ? d : -d);
-      n[e] = r > l16 ? br[e] * x : 0.0f;
-      nt[e] = l16 > r ? bi * x : 0.0f;
-      pt[e] = (r == l16 ? 1.0f : 0.0f) - nt[e];
-    }
-  }
-  __device__ __forceinline__ void level(int l) {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    if (l == 1) {
-      n2 = prod16(nt, n, z);
-      n2t = prod16(n, nt, z);
-    } else if (l == 2) {
-      pt = prod16(n2, pt, pt);
-      n4 = prod16(n2t, n2, z);
-      n4t = prod16(n2, n2t, z);
-    } else if (l == 3) {
-      pt = prod16(n4, pt, pt);
-      n8 = prod16(n4t, n4, z);
-    } else {
-      pt = prod16(n8, pt, pt);
-    }
-  }
-  // lane (g, l16) holds D_b[l16][4 g + e]: row 16 b + l16 of the tile, stored as D_b diag(beta_b)
-  __device__ __forceinline__ void store_d(bf16_t *sT, const float *gw, int b, int l16, int g) {
-    *reinterpret_cast<u32x2 *>(sT + (16 * b + l16) * LDT + 32 * (b >> 1) + 8 * g + 4 * (b & 1)) =
-        pk4u(pt * ld4(gw + 192 + 16 * b + 4 * g));
-  }
-  // block j of (i, k) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): -diag(beta_i)^{-1} L_ik into the tile
-  __device__ __forceinline__ void offdiag(const bf16_t *sK, bf16_t *sT, const float *gw, int j, int l16, int g) {
-    const int i = j >= 3 ? 3 : (j >= 1 ? 2 : 1), k = j - i * (i - 1) / 2;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sK + (16 * k + l16) * LDK + 32 * s + 8 * g);
-      const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(sK + (16 * i + l16) * LDK + 32 * s + 8 * g);
-      a = mfma_bf16(fa, fb, a);
-    }
-    // a[e] = k_c . k_r for c = 16 k + 4 g + e, r = 16 i + l16 (r > c)
-    const int r = 16 * i + l16;
-    const float gr = gw[r];
-    const f32x4 gc = ld4(gw + 16 * k + 4 * g);
-    f32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = -(exp2_hw(gr - gc[e]) * a[e]);
-    *reinterpret_cast<u32x2 *>(sT + r * LDT + 32 * (k >> 1) + 8 * g + 4 * (k & 1)) = pk4u(v);
-  }
-  // after iteration `it` of the wave's K S^T product (16 iterations of two MFMAs)
-  __device__ __forceinline__ void hook(int it, const bf16_t *sK, bf16_t *sT, const float *gw, int wave, int l16, int g) {
-    if (it == 0) gram(sK, wave, l16, g);
-    if (it == 2) scale(gw, wave, l16, g);
-    if (it == 3) level(1);
-    if (it == 5) level(2);
-    if (it == 7) offdiag(sK, sT, gw, wave, l16, g);
-    if (it == 8) level(3);
-    if (it == 11) level(4);
-    if (it == 12 && wave + 4 < 6) offdiag(sK, sT, gw, wave + 4, l16, g);
-    if (it == 14) store_d(sT, gw, wave, l16, g);
-  }
-};
-
-// The forward substitution, step k (0..6) after iteration 2 k + 1 of the S Q^T product; U
-// holds Y on entry and U on exit.
-struct Subst {
-  v4i16 dA0, dA1, dA2, dA3, nL10, nL32;
-  bf16x8 nL2, nL3;
-  __device__ __forceinline__ void load(const bf16_t *sT, int l16, int g) {
-    auto a4 = [&](int row, int pos) {
-      return __builtin_bit_cast(v4i16, *reinterpret_cast<const bf16x4 *>(sT + row * LDT + pos));
-    };
-    dA0 = a4(l16, 8 * g);
-    dA1 = a4(16 + l16, 8 * g + 4);
-    dA2 = a4(32 + l16, 32 + 8 * g);
-    dA3 = a4(48 + l16, 32 + 8 * g + 4);
-    nL10 = a4(16 + l16, 8 * g);
-    nL32 = a4(48 + l16, 32 + 8 * g);
-    nL2 = *reinterpret_cast<const bf16x8 *>(sT + (32 + l16) * LDT + 8 * g);
-    nL3 = *reinterpret_cast<const bf16x8 *>(sT + (48 + l16) * LDT + 8 * g);
-  }
-  template <int NCT> __device__ __forceinline__ void step(int k, f32x4 (&U)[4][NCT]) {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      if (k == 0) U[0][c] = mfma_k16(dA0, pk4(U[0][c]), z);
-      if (k == 1) U[1][c] = mfma_k16(nL10, pk4(U[0][c]), U[1][c]);
-      if (k == 2) U[1][c] = mfma_k16(dA1, pk4(U[1][c]), z);
-      if (k == 3) {
-        const bf16x8 p01 = pack_pair(U[0][c], U[1][c]);
-        U[2][c] = mfma_bf16(nL2, p01, U[2][c]);
-        U[3][c] = mfma_bf16(nL3, p01, U[3][c]);
-      }
-      if (k == 4) U[2][c] = mfma_k16(dA2, pk4(U[2][c]), z);
-      if (k == 5) U[3][c] = mfma_k16(nL32, pk4(U[2][c]), U[3][c]);
-      if (k == 6) U[3][c] = mfma_k16(dA3, pk4(U[3][c]), z);
-    }
-  }
-};
 
 template <bool DELTA, int DK>
 __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args a) {
@@ -1273,8 +1341,11 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   constexpr int ROWS = NW * RPW, LDVR = ROWS + 16;  // state rows of a workgroup; its V tile's row stride
   constexpr int NRB = DV / ROWS;       // row blocks (workgroups) per segment
   constexpr int NIT = 4 * (DK / 32);   // (token tile, key step) pairs of a K S^T / Q S^T product
-  constexpr bool FORM = DELTA && DK == 128;  // the chunk solve formed here (form_solve_blocks)
-  static_assert(!FORM || NW == 4, "one diagonal block of the chunk solve per wave");
+  // the chunk solve formed here (ChunkSolve, Subst) at d = 128.  At d = 256 it pushed the
+  // replay's spill from 28 to 80 bytes per lane and took 4.5 -> 5.5 ms, more than the
+  // transform pass it would save: there the replay reads stored transforms.
+  constexpr bool FORM = DELTA && DK == 128;
+  static_assert(!FORM || NW == 4 || NW == 8, "four or eight waves share the chunk solve");
   // load offsets computed once (TileOffsets) where the registers allow: not at d = 256,
   // whose 256 registers per lane would spill more
   constexpr bool TOFF = DK == 128;
@@ -1402,7 +1473,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
         }
       }
     };
-    ChunkSolve<LDK> cs;  // (FORM)
+    ChunkSolve<LDK, DK, NW> cs;  // (FORM)
     {
       if (DELTA) {
         // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T (K fragments two steps ahead),
@@ -1562,7 +1633,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
 #pragma unroll
         for (int c = 0; c < NCT; ++c) O[mt][c] = mfma_bf16(sfr[c], qb[it % 3], O[mt][c]);
         if constexpr (FORM) {
-          if (it % 2 == 1 && it / 2 < 7) sub.step(it / 2, U);
+          if (it % (NIT / 8) == 1 && it / (NIT / 8) < 7) sub.step(it / (NIT / 8), U);
         }
       }
 #undef LA_QF
@@ -1683,7 +1754,7 @@ WsLayout ws_layout(bool delta, int B, int H, int64_t T, int d, const Plan &p) {
     w.starts = off;
     off += up(bhs * (size_t)d * d * 4);
   }
-  if (delta) {
+  if (delta && d == 256) {  // (d = 128 forms its chunk solves where it uses them)
     w.tb = off;
     off += up(bh * nch * T_CHUNK * 2);
   }
@@ -1720,41 +1791,16 @@ template <int DK>
 void launch_passes(const Args &a, bool delta, int pass_mask, hipStream_t s) {
   constexpr int DV = Geo<DK>::DV, NW = Geo<DK>::NW, NRB = DV / (NW * 16 * Geo<DK>::NCT);
   const int B = a.B, H = a.H;
-  // At d = 128 the replay forms its own chunk solve, and the stored transforms serve the map
-  // pass alone: pass 0 covers the windows of the mapped segments, and the map pass, in three
-  // launches, maps the windows, transforms the rest of the segments whose window transition
-  // is not zero, and maps those segments whole.
-  const bool windows_apart = delta && DK == 128 && a.nseg > 1;
-  const int cw = a.seg_chunks > 2 * MAP_WINDOW ? a.seg_chunks - MAP_WINDOW : 0;
-  if (delta && (pass_mask & PASS_TRANSFORM)) {
-    Args t = a;
-    int64_t chunks = (int64_t)B * H * a.nch;
-    if (DK == 128) {
-      t.tp_mode = 1;
-      t.map_cw = cw;
-      chunks = windows_apart && cw > 0 ? (int64_t)B * H * (a.nseg - 1) * MAP_WINDOW : 0;
+  // at d = 128 the replay and the map pass form their own chunk solves (no stored transform)
+  if constexpr (DK == 256) {
+    if (delta && (pass_mask & PASS_TRANSFORM)) {
+      const int64_t chunks = (int64_t)B * H * a.nch;
+      hipLaunchKernelGGL((tprep_kernel<DK>), dim3((unsigned)((chunks + TPW - 1) / TPW)), dim3(TPW * 64), 0, s, a);
     }
-    if (chunks > 0)
-      hipLaunchKernelGGL((tprep_kernel<DK>), dim3((unsigned)((chunks + TPW - 1) / TPW)), dim3(TPW * 64), 0, s, t);
   }
   if (a.nseg > 1 && (pass_mask & PASS_MAPS)) {
     // every segment but the last (whose end state only the replay needs)
-    if (windows_apart) {
-      constexpr int NWT = map_waves<true, DK>(), NMB = (DV + DK) / (NWT * 16 * MapGeo<DK>::NCT);
-      static_assert(DK != 128 || NMB == 1, "one map workgroup per segment");
-      const dim3 grid(seg_grid(a.nseg - 1, NMB), H, B), block(map_threads<true, DK>());
-      Args m = a;
-      m.map_mode = 1;
-      hipLaunchKernelGGL((map_kernel<true, DK>), grid, block, 0, s, m);
-      Args t = a;
-      t.tp_mode = 2;
-      t.map_cw = cw;
-      const int cwp = cw > 0 ? cw : a.seg_chunks, gx = (cwp + TPW * 8 - 1) / (TPW * 8);
-      hipLaunchKernelGGL((tprep_kernel<DK>), dim3((unsigned)gx, (unsigned)(B * H * (a.nseg - 1))), dim3(TPW * 64), 0,
-                         s, t);
-      m.map_mode = 2;
-      hipLaunchKernelGGL((map_kernel<true, DK>), grid, block, 0, s, m);
-    } else if (delta) {
+    if (delta) {
       constexpr int NWT = map_waves<true, DK>(), NMB = (DV + DK) / (NWT * 16 * MapGeo<DK>::NCT);
       hipLaunchKernelGGL((map_kernel<true, DK>), dim3(seg_grid(a.nseg - 1, NMB), H, B), dim3(map_threads<true, DK>()), 0,
                          s, a);
@@ -1816,13 +1862,9 @@ hipError_t launch_chunk_prefill(int variant, int B, int H, int64_t T, int d_k, i
   a.gsum = p.nseg > 1 ? (float *)(ws + w.gsum) : nullptr;
   a.mzero = p.nseg > 1 ? (uint8_t *)(ws + w.gsum) : nullptr;
   a.starts = p.nseg > 1 ? (float *)(ws + w.starts) : nullptr;
-  a.tb = delta ? (bf16_t *)(ws + w.tb) : nullptr;
+  a.tb = delta && d_k == 256 ? (bf16_t *)(ws + w.tb) : nullptr;
   a.T = T;
   a.nch = (T + C - 1) / C;
-  a.tp_nch = a.nch;
-  a.tp_mode = 0;
-  a.map_mode = 0;
-  a.map_cw = 0;
   a.B = B;
   a.H = H;
   a.nseg = p.nseg;

@@ -100,11 +100,11 @@ const char *la_status_string(int status);
 
 /*
  * Workspace that la_prefill needs for this problem, in bytes (0 is possible).  The
- * workspace holds the chunked prefill's per-segment fp32 state maps and, for the gated
- * delta rule, one bf16 lower-triangular 64 x 64 transform per chunk of 64 tokens (6 KiB
- * per chunk and head: the zero blocks right of the diagonal in its first 32 rows are not
- * stored; see la_prefill_pass); for short fp32 ADDITIVE and GATED problems, the start state
- * and one fp32 d_v x d_k state sum per chunk.
+ * workspace holds the chunked prefill's per-segment fp32 state maps and start states and,
+ * for the gated delta rule at d_k = 256, one bf16 lower-triangular 64 x 64 transform per
+ * chunk of 64 tokens (6 KiB per chunk and head: the zero blocks right of the diagonal in
+ * its first 32 rows are not stored; see la_prefill_pass); for short fp32 ADDITIVE and GATED
+ * problems, the start state and one fp32 d_v x d_k state sum per chunk.
  * Returns LA_OK and writes *bytes, or the same validation error la_prefill would give.
  */
 int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int64_t seq_len,
@@ -129,7 +129,8 @@ int la_prefill_workspace_size(int variant, int dtype, int batch, int heads, int6
  *
  * Method: bf16 inputs take the chunkwise path -- chunks of 64 tokens, intra-chunk
  * products on MFMA with fp32 accumulation, the gated delta rule's WY/UT transform
- * solved per chunk in a pass of its own, and an fp32 state carried across chunks and
+ * solved per chunk (at d_k = 128 inside the passes that use it, at 256 in a pass of its
+ * own), and an fp32 state carried across chunks and
  * across segments of chunks (a three-pass segment scan: per-segment affine state maps,
  * a scan of the segment start states, then every segment replayed from its start
  * state).  fp32
@@ -166,18 +167,17 @@ int la_prefill(int variant, int dtype, int batch, int heads, int64_t seq_len, in
  *                        la_prefill_pass(LA_PASS_SCAN, ...);
  *                        la_prefill_pass(LA_PASS_REPLAY, ...);
  *
- *   LA_PASS_TRANSFORM  gated delta rule on the chunked path: the UT transforms
- *                      (I + L)^{-1} diag(beta) of chunks, which depend on keys and gates
- *                      only, written to the workspace for the passes that follow: at
- *                      d_k = 256 every chunk's; at d_k = 128 those of each mapped segment's
- *                      last 8 chunks (the replay forms its own from the keys it loads)
+ *   LA_PASS_TRANSFORM  gated delta rule on the chunked path at d_k = 256: every chunk's UT
+ *                      transform (I + L)^{-1} diag(beta), which depends on keys and gates
+ *                      only, written to the workspace for the passes that follow (at
+ *                      d_k = 128 nothing: the map and replay passes form each chunk's
+ *                      solve from the keys they load)
  *   LA_PASS_MAPS       per segment of chunks except the last, the affine map of its end
  *                      state on its start state (S_end = S_start M + B; M is d_k x d_k
  *                      for the gated delta rule, a scalar decay otherwise), written to
  *                      the workspace (when the decay over a segment's last 8 chunks takes
  *                      M to exactly zero in fp32, the map is formed from those chunks
- *                      alone: M = 0, B theirs; at d_k = 128 the gated delta rule's other
- *                      segments get the transforms of their remaining chunks here first)
+ *                      alone: M = 0, B theirs)
  *   LA_PASS_SCAN       segment start states S_{i+1} = S_i M_i + B_i from S0
  *   LA_PASS_REPLAY     every segment from its start state: o, and S_T from the last one
  *
@@ -207,8 +207,9 @@ int la_prefill_segments(int variant, int dtype, int batch, int heads, int64_t se
  * process ends.  The segment plan is chosen so that the workspace fits in it (fewer
  * segments than la_prefill may use, so results can differ from la_prefill's within the
  * rounding of the chunked path); a problem whose workspace exceeds it even with a single
- * segment returns LA_ERR_WORKSPACE before anything is launched (for the gated delta rule
- * with bf16 inputs, about B H T <= 1.4 million token-heads).  The stream must belong to
+ * segment returns LA_ERR_WORKSPACE before anything is launched (only the gated delta rule
+ * with bf16 inputs at d_k = 256 beyond about B H T = 1.4 million token-heads: at d_k = 128
+ * the workspace holds segment maps and start states only, at most about 96 MiB).  The stream must belong to
  * the current device.  Every call on a device shares that device's array and leaves its
  * contents behind: calls that overlap on one device (two streams, or two threads) race.
  * It calls no hipMalloc, hipFree or other allocating routine.

@@ -73,7 +73,7 @@ int main() {
                     need, nullptr) == LA_ERR_UNSUPPORTED);
   EXPECT(la_prefill_pass(7, LA_GATED_DELTA, LA_BF16, 1, 2, 1000, 128, 128, 0, q, k, v, al, be, S0, nullptr, o, S,
                          nullptr, ws, need, nullptr) == LA_ERR_INVALID);
-  EXPECT(la_prefill_noalloc(LA_GATED_DELTA, LA_BF16, 1, 16, (int64_t)1 << 20, 128, 128, 0, q, k, v, al, be, S0,
+  EXPECT(la_prefill_noalloc(LA_GATED_DELTA, LA_BF16, 1, 8, (int64_t)1 << 20, 256, 256, 0, q, k, v, al, be, S0,
                             nullptr, o, S, nullptr, nullptr) == LA_ERR_WORKSPACE);
 
   // decode

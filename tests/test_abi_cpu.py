@@ -127,18 +127,20 @@ def test_workspace_size_validates(lib):
 
 
 def test_workspace_holds_one_transform_per_chunk(lib):
-    """One segment per head (128 heads): the gated delta rule needs exactly one stored
-    transform per chunk and head (the lower-triangular 64 x 64 bf16 T diag(beta) without the
-    blocks right of the diagonal in its first 32 rows: 32 x 32 + 32 x 64 values); the gated
-    variant needs nothing."""
+    """One segment per head (128 heads): at d = 256 the gated delta rule needs exactly one
+    stored transform per chunk and head (the lower-triangular 64 x 64 bf16 T diag(beta)
+    without the blocks right of the diagonal in its first 32 rows: 32 x 32 + 32 x 64
+    values); at d = 128, where the passes form each chunk's solve from the keys they load,
+    and for the gated variant, nothing."""
     n = ctypes.c_size_t(0)
     T = 64 * 100 + 5  # 101 chunks, the last partial
-    assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 2, 64, T, 128, 128,
+    assert lib.la_prefill_workspace_size(la.GATED_DELTA, la.BF16, 2, 64, T, 256, 256,
                                          ctypes.byref(n)) == 0
     assert n.value == 2 * 64 * 101 * (32 * 32 + 32 * 64) * 2
-    assert lib.la_prefill_workspace_size(la.GATED, la.BF16, 2, 64, T, 128, 128,
-                                         ctypes.byref(n)) == 0
-    assert n.value == 0
+    for variant in (la.GATED_DELTA, la.GATED):
+        assert lib.la_prefill_workspace_size(variant, la.BF16, 2, 64, T, 128, 128,
+                                             ctypes.byref(n)) == 0
+        assert n.value == 0
 
 
 def test_width_256_plan_and_workspace(lib):
@@ -245,7 +247,7 @@ def test_noalloc_rejects_before_any_hip_call(lib):
     """la_prefill_noalloc validates the shape and checks that the workspace fits its static
     scratch (even with one segment) before it touches the device."""
     args = [P(A), P(2 * A), P(3 * A), P(4 * A), P(5 * A), None, None, P(6 * A), P(8 * A), None, None]
-    # 16 heads x 1M tokens of gated delta rule: the per-chunk transforms alone exceed it
-    assert lib.la_prefill_noalloc(la.GATED_DELTA, la.BF16, 1, 16, 1 << 20, 128, 128, 1e-6, *args) == -5
+    # 8 heads of 256 x 1M tokens of gated delta rule: the per-chunk transforms alone exceed it
+    assert lib.la_prefill_noalloc(la.GATED_DELTA, la.BF16, 1, 8, 1 << 20, 256, 256, 1e-6, *args) == -5
     assert lib.la_prefill_noalloc(9, la.BF16, 1, 2, 100, 128, 128, 1e-6, *args) == -2
     assert lib.la_prefill_noalloc(la.GATED_DELTA, la.BF16, 1, 2, 100, 96, 96, 1e-6, *args) == -3
