@@ -1075,8 +1075,8 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
   // the segment start has fallen below the smallest fp32 value) keeps them zero: with finite
   // inputs, K S^T, U and the update of such rows are exact zeros, so skipping its chunk work
   // leaves every result bit for bit as it was (the barriers and loads go on).  The wave
-  // checks every eight chunks, right after a barrier, when its last update has long
-  // completed.  Rows that merely become small (a decay per chunk above one half can hold the
+  // checks every eight chunks (at d = 128 every second chunk of the window), right after a
+  // barrier, when its last update has long completed.  Rows that merely become small (a decay per chunk above one half can hold the
   // smallest subnormal) are never skipped.
   auto rows_zero = [&]() -> bool {  // (whole wave) every state entry of the wave is 0
     bool nz = false;
@@ -1115,7 +1115,9 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
           const int cj = ci + u;
           if (cj < nchunks) {
             __syncthreads();  // copy u holds chunk cj and its solve blocks; every wave is done with chunk cj - 1
-            if (m_kind && !m_dead && ((cj - cb) & 7) == 0 && cj > cb) m_dead = rows_zero();
+            // (every eight chunks; inside the 8-chunk window every second one, where fast
+            // decay zeroes the transition rows within a chunk or two)
+            if (m_kind && !m_dead && ((cj - cb) & (phase == 1 ? 1 : 7)) == 0 && cj > cb) m_dead = rows_zero();
             if (!m_dead) {
               const float gCj = gates(cj, sGraw[u][0]);
               step(sKc[u], sVc[u], sTc[u], gCj);
