@@ -438,7 +438,7 @@ __device__ __forceinline__ f32x4 prod16(f32x4 at, f32x4 b, f32x4 c) { return mfm
 // The pieces of the chunk solve, in steps that the replay spreads over its K S^T product (the
 // blocks of L and D) and its S Q^T product (the substitution), whose independent MFMAs fill
 // the latency between one dependent step and the next.
-template <int LDK, int DK, int NW> struct ChunkSolve {
+template <int LDK, int DK> struct ChunkSolve {
   static constexpr int NIT = 4 * (DK / 32), SP = NIT / 16;  // K S^T iterations; hook spacing
   f32x4 acc, n, nt, pt, n2, n2t, n4, n4t, n8;
   // diagonal block b = wave: the Gram block (k_r . k_i, r = 16 b + 4 g + e, i = 16 b + l16)
@@ -503,25 +503,19 @@ template <int LDK, int DK, int NW> struct ChunkSolve {
     for (int e = 0; e < 4; ++e) v[e] = -(exp2_hw(gr - gc[e]) * a[e]);
     *reinterpret_cast<u32x2 *>(sT + r * LDT + 32 * (k >> 1) + 8 * g + 4 * (k & 1)) = pk4u(v);
   }
-  // after iteration `it` of the wave's K S^T product (NIT iterations of two MFMAs).  Four
-  // waves: each inverts diagonal block `wave` and forms blocks wave and wave + 4 below the
-  // diagonal; eight waves: waves 0-3 the diagonal blocks, waves 4-7 the blocks below.
+  // after iteration `it` of the wave's K S^T product (NIT iterations of two MFMAs), for
+  // four waves: each inverts diagonal block `wave` and forms blocks wave and wave + 4 below
+  // the diagonal
   __device__ __forceinline__ void hook(int it, const bf16_t *sK, bf16_t *sT, const float *gw, int wave, int l16, int g) {
-    const bool diag = NW == 4 || wave < 4;
-    const int jw = NW == 4 ? wave : wave - 4;  // first block below the diagonal (eight waves: waves 4-7)
-    if (diag) {
-      if (it == 0) gram(sK, wave, l16, g);
-      if (it == 2 * SP) scale(gw, wave, l16, g);
-      if (it == 3 * SP) level(1);
-      if (it == 5 * SP) level(2);
-      if (it == 8 * SP) level(3);
-      if (it == 11 * SP) level(4);
-      if (it == 14 * SP) store_d(sT, gw, wave, l16, g);
-    }
-    if (NW == 4 || wave >= 4) {
-      if (it == 7 * SP) offdiag(sK, sT, gw, jw, l16, g);
-      if (it == 12 * SP && jw + 4 < 6) offdiag(sK, sT, gw, jw + 4, l16, g);
-    }
+    if (it == 0) gram(sK, wave, l16, g);
+    if (it == 2 * SP) scale(gw, wave, l16, g);
+    if (it == 3 * SP) level(1);
+    if (it == 5 * SP) level(2);
+    if (it == 7 * SP) offdiag(sK, sT, gw, wave, l16, g);
+    if (it == 8 * SP) level(3);
+    if (it == 11 * SP) level(4);
+    if (it == 12 * SP && wave + 4 < 6) offdiag(sK, sT, gw, wave + 4, l16, g);
+    if (it == 14 * SP) store_d(sT, gw, wave, l16, g);
   }
 };
 
@@ -852,7 +846,7 @@ __global__ __launch_bounds__((map_threads<DELTA, DK>()), (map_loader<DK>() ? 3 :
       gl[lane] = wave_prefix_sum(log2f(al));
       gl[192 + lane] = bf16_to_f32((bf16_t)sGraw[u][1][lane]);
       __asm__ volatile("" ::: "memory");
-      ChunkSolve<LDK, DK, 4> cs;
+      ChunkSolve<LDK, DK> cs;
       cs.gram(sKc[u], h, l16, g);
       cs.offdiag(sKc[u], sTc[u], gl, h, l16, g);
       cs.scale(gl, h, l16, g);
@@ -1347,7 +1341,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
   // replay's spill from 28 to 80 bytes per lane and took 4.5 -> 5.5 ms, more than the
   // transform pass it would save: there the replay reads stored transforms.
   constexpr bool FORM = DELTA && DK == 128;
-  static_assert(!FORM || NW == 4 || NW == 8, "four or eight waves share the chunk solve");
+  static_assert(!FORM || NW == 4, "one diagonal block of the chunk solve per wave");
   // load offsets computed once (TileOffsets) where the registers allow: not at d = 256,
   // whose 256 registers per lane would spill more
   constexpr bool TOFF = DK == 128;
@@ -1475,7 +1469,7 @@ __global__ __launch_bounds__(Geo<DK>::NW * 64, 2) void replay_kernel(const Args 
         }
       }
     };
-    ChunkSolve<LDK, DK, NW> cs;  // (FORM)
+    ChunkSolve<LDK, DK> cs;  // (FORM)
     {
       if (DELTA) {
         // U = U~ - W S^T = TB (V - diag(gamma) K S^T): K S^T (K fragments two steps ahead),
