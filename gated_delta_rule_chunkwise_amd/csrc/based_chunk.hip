@@ -25,9 +25,11 @@
 // 160 internal features (10 tiles) instead of 273 (18 tiles with padding).  The ABI
 // layout [1, x, x (x) x] is restored when states are written: the antisymmetric part of
 // a start state never changes (every update is symmetric in (a, b)) and is added back.
-// Four waves each own one 16-column tile of s (10 x 4 fp32 accumulator tiles); the
-// normaliser z lives in LDS in fp32: its increment is a one-row MFMA operand, its product
-// with phi(q) is formed on the VALU from the fp32 features.  The state products are
+// In the replay, four waves each own one 16-column tile of s (10 x 4 fp32 accumulator
+// tiles); the normaliser z lives in LDS in fp32: its increment is a one-row MFMA operand,
+// its product with phi(q) is formed on the VALU from the fp32 features.  The map pass,
+// which has no numerator to form, deals the same 40 accumulator tiles out by feature
+// tile instead, so that no phi(k) fragment has to be shared between waves.  The state products are
 // v_mfma_f32_16x16x32_bf16 (q.k: 16x16x16) with fp32 accumulation; token-contraction
 // operands of k and v are read with ds_read_b64_tr_b16.
 //
@@ -58,8 +60,6 @@ constexpr int LDQ = DP + 8;  // bf16 [C][DP] row-major k tile (48-byte rows)
 constexpr int LDQ2 = 2 * DP + 8;  // bf16 [C][2 DP] q tile, each row holding q_t twice
 constexpr int LDV = DV + 8;  // bf16 [C][DV] row-major v tile
 constexpr int LDA = C + 8;   // bf16 [C][C] kernel matrix (transposed)
-
-enum { MODE_MAP = 0, MODE_OUT = 1 };
 
 struct Args {
   const bf16_t *q, *k, *v;
@@ -139,6 +139,12 @@ __device__ __forceinline__ bf16x8 pack_pair(f32x4 a, f32x4 b) {
   return pack8(a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
 }
 
+// Four floats to bf16 in two pairs (two v_cvt_pk_bf16_f32, no byte permutes)
+__device__ __forceinline__ u32x2 pk4u(f32x4 x) {
+  const bf16x2 a = {(__bf16)x[0], (__bf16)x[1]}, b = {(__bf16)x[2], (__bf16)x[3]};
+  return u32x2{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b)};
+}
+
 __device__ __forceinline__ f32x4 u16x4_to_f32(uint2 u) {
   f32x4 r;
   r[0] = __uint_as_float(u.x << 16);
@@ -179,16 +185,10 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-__device__ __forceinline__ void tri_index(int idx, int &ti, int &tj) {
-  ti = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
-  tj = idx - ti * (ti + 1) / 2;
-}
-
-// Three replay workgroups per CU (49 KB of LDS, at most 168 registers each), four for the
-// maps pass (32 KB).
-template <int MODE>
-__global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_kernel(const Args a) {
-  constexpr bool OUT = MODE == MODE_OUT;
+// Pass 3: every segment replayed from its start state, the outputs written; the last
+// segment writes the end state.  Three workgroups per CU (49 KB of LDS, at most 168
+// registers each).
+__global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) bf16_t sQ[C * LDQ2];
   __shared__ __attribute__((aligned(16))) bf16_t sK[C * LDQ];
   __shared__ __attribute__((aligned(16))) bf16_t sV[C * LDV];
@@ -198,13 +198,12 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
   __shared__ __attribute__((aligned(16))) float sDen[C];
   // phi(q) as MFMA B-operand fragments, [token tile][feature step][lane] (16 bytes each):
   // each wave builds its token tile's once per chunk, every wave reads all four
-  __shared__ __attribute__((aligned(16))) bf16x8 sPhi[MODE == MODE_OUT ? 4 * (NFT / 2) * 64 : 1];
+  __shared__ __attribute__((aligned(16))) bf16x8 sPhi[4 * (NFT / 2) * 64];
   // phi(k)^T of the 9 order-2 feature tiles as MFMA A-operand fragments, [tile][token
-  // step][lane], built once per chunk (four tiles per wave).  MODE_OUT keeps them in sPhi's
-  // space once the numerator is done with phi(q).
-  __shared__ __attribute__((aligned(16))) bf16x8 sPhiK[MODE == MODE_MAP ? ND * 2 * 64 : 1];
-  bf16x8 *const phik = OUT ? sPhi : sPhiK;
-  static_assert(!OUT || ND * 2 <= 4 * (NFT / 2), "phi(k) fragments must fit in sPhi");
+  // step][lane], built once per chunk (two or three tiles per wave), kept in sPhi's space
+  // once the numerator is done with phi(q)
+  bf16x8 *const phik = sPhi;
+  static_assert(ND * 2 <= 4 * (NFT / 2), "phi(k) fragments must fit in sPhi");
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int seg = blockIdx.x;
@@ -221,8 +220,8 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     // (segment 0's is S0 in internal order, so no replay workgroup reads S0 while the last
     // one writes S_T, which may be the same buffer); with one segment it starts from S0
     // (ABI layout); the map pass starts from zero
-    const float *src_i = (OUT && a.nseg > 1) ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
-    const float *src_a = (OUT && a.nseg == 1 && a.s0) ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
+    const float *src_i = a.nseg > 1 ? a.starts + (bh * a.nseg + seg) * (size_t)NF * (DV + 1) : nullptr;
+    const float *src_a = (a.nseg == 1 && a.s0) ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
 #pragma unroll
     for (int m = 0; m < NFT; ++m)
 #pragma unroll
@@ -232,7 +231,7 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
       }
     for (int fi = tid; fi < NF; fi += NTHR) {
       sZ[fi] = src_i ? src_i[(size_t)fi * (DV + 1) + DV]
-                     : abi_load(OUT && a.nseg == 1 && a.z0 ? a.z0 + bh * a.Dabi : nullptr, a.compact, fi, 1, 0);
+                     : abi_load(a.nseg == 1 && a.z0 ? a.z0 + bh * a.Dabi : nullptr, a.compact, fi, 1, 0);
     }
   }
 
@@ -252,9 +251,19 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     pv[0] = bld16(rv, 16u * (uint32_t)tid);                                                        \
     pv[1] = bld16(rv, 16u * (uint32_t)(tid + NTHR));                                               \
     if (tid < 2 * C) pkq = bld16(make_rsrc(a.k + rb * DP, ln * DP * 2), 16u * (uint32_t)tid);      \
-    else if (OUT) pkq = bld16(make_rsrc(a.q + rb * DP, ln * DP * 2), 16u * (uint32_t)(tid - 2 * C)); \
+    else pkq = bld16(make_rsrc(a.q + rb * DP, ln * DP * 2), 16u * (uint32_t)(tid - 2 * C)); \
   } while (0)
   if (nchunks > 0) LA_BLOAD(first);
+  // one-row operand (row 0): 1 at every token, for A 1 and sum_t k_t.  Past T (a partial
+  // last chunk) the loaded q, k, v are zero and A is causal, so an output row t < T never
+  // meets a token j > t, and the keys past T add nothing to the sums
+  const bf16x8 ones = (lane & 15) == 0 ? pack8(1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f)
+                                       : pack8(0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f);
+  if (tid < 128) {  // the above-diagonal tiles read by the A V products, A (0,1) and
+                           // (2,3): zero for every chunk (visible after the first barrier)
+    const int tile = tid >> 6, e = tid & 63;
+    *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
+  }
 
   for (int ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = first + (int64_t)ci * C;
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     if (tid < 2 * C) {
       const int r = tid >> 1, cv = tid & 1;
       *reinterpret_cast<u32x4 *>(sK + r * LDQ + cv * 8) = pkq;
-    } else if (OUT) {
+    } else {
       const int id = tid - 2 * C, r = id >> 1, cv = id & 1;
       *reinterpret_cast<u32x4 *>(sQ + r * LDQ2 + cv * 8) = pkq;
       *reinterpret_cast<u32x4 *>(sQ + r * LDQ2 + DP + cv * 8) = pkq;
@@ -281,37 +290,39 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     if (ci + 1 < nchunks) LA_BLOAD(t0 + C);
 
     // ---- phase B: kernel matrix A = 1 + QK^T + (QK^T)^2/2, causal, stored transposed
-    // (row j, column t) in bf16; tiles dealt round robin (a wave without a third tile
-    // recomputes tile 9 and stores the same values again).  q.k over d' = 16 is one
+    // (row j, column t) in bf16; the 10 lower tiles (ti >= tj) dealt round robin, 3, 3, 2
+    // and 2 a wave, with the wave index a constant in each branch so that tile addresses
+    // are immediates and only diagonal tiles are masked.  q.k over d' = 16 is one
     // v_mfma_f32_16x16x16_bf16 per tile: lane (g, i) supplies elements 4 g..4 g + 3 of row
-    // i; all six operand reads are issued before the first product.
-    float zq = 0.0f;  // MODE_OUT: z . phi(q_t) for token 16 wave + lane % 16
-    if (OUT) {
-      v4i16 fa[3], fb[3];
-      int tis[3], tjs[3];
+    // i; the operand reads are issued before the first product.
+    float zq = 0.0f;  // z . phi(q_t) for token 16 wave + lane % 16
+    {
+      static_for<NW>([&](auto wc) {
+        constexpr int W = decltype(wc)::value, NJ = W < 2 ? 3 : 2;
+        if (wave == W) {
+          v4i16 fa[NJ], fb[NJ];
+          static_for<NJ>([&](auto mc) {
+            constexpr int job = W + NW * decltype(mc)::value;
+            constexpr int ti = job >= 6 ? 3 : (job >= 3 ? 2 : (job >= 1 ? 1 : 0)), tj = job - ti * (ti + 1) / 2;
+            fa[decltype(mc)::value] = *reinterpret_cast<const v4i16 *>(sQ + (16 * ti + l16) * LDQ2 + 4 * g);
+            fb[decltype(mc)::value] = *reinterpret_cast<const v4i16 *>(sK + (16 * tj + l16) * LDQ + 4 * g);
+          });
+          static_for<NJ>([&](auto mc) {
+            constexpr int job = W + NW * decltype(mc)::value;
+            constexpr int ti = job >= 6 ? 3 : (job >= 3 ? 2 : (job >= 1 ? 1 : 0)), tj = job - ti * (ti + 1) / 2;
+            const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa[decltype(mc)::value], fb[decltype(mc)::value],
+                                                                      f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            f32x4 v;
 #pragma unroll
-      for (int mm = 0; mm < 3; ++mm) {
-        const int job = wave + NW * mm;
-        tri_index(job < 10 ? job : 9, tis[mm], tjs[mm]);
-        fa[mm] = *reinterpret_cast<const v4i16 *>(sQ + (16 * tis[mm] + l16) * LDQ2 + 4 * g);
-        fb[mm] = *reinterpret_cast<const v4i16 *>(sK + (16 * tjs[mm] + l16) * LDQ + 4 * g);
-      }
-#pragma unroll
-      for (int mm = 0; mm < 3; ++mm) {
-        const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa[mm], fb[mm], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const int ti = tis[mm], j = 16 * tjs[mm] + l16;
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = acc[e];
-          v[e] = (16 * ti + 4 * g + e >= j) ? 1.0f + x + 0.5f * x * x : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[e];
+              v[e] = __builtin_fmaf(x, __builtin_fmaf(0.5f, x, 1.0f), 1.0f);
+              if constexpr (ti == tj) v[e] = 4 * g + e >= l16 ? v[e] : 0.0f;
+            }
+            *reinterpret_cast<u32x2 *>(sA + (16 * tj + l16) * LDA + 16 * ti + 4 * g) = pk4u(v);
+          });
         }
-        *reinterpret_cast<bf16x4 *>(sA + j * LDA + 16 * ti + 4 * g) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-      }
-      if (tid < 128) {  // the above-diagonal tiles read by the A V products: A (0,1), (2,3)
-        const int tile = tid >> 6, e = tid & 63;
-        *reinterpret_cast<uint2 *>(sA + (32 * tile + 16 + (e >> 2)) * LDA + 32 * tile + 4 * (e & 3)) = make_uint2(0u, 0u);
-      }
+      });
       {  // phi(q_t) for this wave's token tile mt = wave, t = 16 mt + l16: the B operand of
          // feature step s holds rows 4 g + e of tiles 2 s and 2 s + 1.  With w[j] =
          // q_t[(4 g + j) mod 16] (three 8-byte reads of the doubled row), row r = 4 g + e of
@@ -360,20 +371,8 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     // ---- phase C: numerator and denominator on the entering state (transposed, so a
     // lane holds four consecutive outputs of one token), then the carry
     const bf16x8 vf0 = col_frag(sV, LDV, n_col, 0, lane_v), vf1 = col_frag(sV, LDV, n_col, 1, lane_v);
-    // one-row operand (row 0): valid-token indicator, for A 1 and Phi_K^T 1
-    bf16x8 ones[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      f32x4 a0, a1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a0[e] = (l16 == 0 && 32 * s2 + 4 * g + e < n) ? 1.0f : 0.0f;
-        a1[e] = (l16 == 0 && 32 * s2 + 16 + 4 * g + e < n) ? 1.0f : 0.0f;
-      }
-      ones[s2] = pack_pair(a0, a1);
-    }
     f32x4 num[4];
-    if (OUT) {
+    {
       // num^T[c][t] = sum_f s[f][c] phi_f(q_t) + sum_j v_j[c] A[t][j]: the state is the A
       // operand (rows = value columns, k = features), phi(q_t) (from LDS) the B operand;
       // the transposed product leaves four consecutive outputs of one token in each lane.
@@ -409,12 +408,12 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           if (s2 == 1 && mt < 2) continue;
-          dacc = mfma_bf16(ones[s2], col_frag(sA, LDA, mt, s2, lane_v), dacc);
+          dacc = mfma_bf16(ones, col_frag(sA, LDA, mt, s2, lane_v), dacc);
         }
         if (g == 0) sDen[16 * mt + l16] = dacc[0] + zq;
       }
     }
-    if (OUT) __syncthreads();  // every wave is done with phi(q) before sPhi is overwritten
+    __syncthreads();  // every wave is done with phi(q) before sPhi is overwritten
     {
       // phi(k)^T fragments of the order-2 tiles (A operand: rows = features, k = tokens),
       // tiles d = wave, wave + 4, ..., shared through LDS.  Row i of diagonal tile d is
@@ -469,12 +468,12 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
       // ready when the carry's are still in flight.
       const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
       f32x4 zg = {0.f, 0.f, 0.f, 0.f};
-      if (wave == 0) {
+      if (wave == 2) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(kj[s2], kj[s2], zg);
-      } else if (wave == 1) {
+      } else if (wave == 3) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(ones[s2], kj[s2], zg);  // row 0: sum_t k_t[l16]
+        for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(ones, kj[s2], zg);  // row 0: sum_t k_t[l16]
       }
       bf16x8 pkb[2][2];
       pkb[0][0] = phik[0 * 64 + lane_v];
@@ -493,14 +492,14 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) st[T_LIN] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[T_LIN]);
-      if (wave == 0) {
+      if (wave == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // G[a][b], a = 4 g + e, b = l16; unkept entries to a spare slot
           const int ra = 4 * g + e, d = (l16 - ra) & 15;
           const bool keep = d < ND - 1 || (d == ND - 1 && ra < DP / 2);
           sZinc[keep ? 16 * d + ra : NF + lane] = zg[e] * (d == 0 ? rs2 : 2.0f * rs2);
         }
-      } else if (wave == 1) {
+      } else if (wave == 3) {
         if (g == 0) {
           sZinc[16 * T_LIN + l16] = zg[0];
           // the constant feature counts the valid tokens
@@ -511,44 +510,191 @@ __global__ __launch_bounds__(NTHR, MODE == MODE_OUT ? 3 : 4) void based_chunk_ke
     __syncthreads();
 
     // ---- phase D: o = num / (den + eps) straight to HBM; z += this chunk's Phi_K^T 1
-    if (OUT) {
+    {
       const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const float r = __builtin_amdgcn_rcpf(sDen[16 * mt + l16] + a.eps);
         const f32x4 x = num[mt] * r;
-        const bf16x4 h = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-        bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + 16 * n_col + 4 * g), __builtin_bit_cast(u32x2, h));
+        bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + 16 * n_col + 4 * g), pk4u(x));
       }
     }
     for (int fi = tid; fi < NF; fi += NTHR) sZ[fi] += sZinc[fi];
   }
 #undef LA_BLOAD
 
-  if (OUT) {
-    if (seg == a.nseg - 1 && a.s_T) {  // the last segment's end state is S_T
-      __syncthreads();
-      const int l16 = lane & 15, g = lane >> 4;
-      const float *s0 = a.s0 ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
-      const float *z0 = a.z0 ? a.z0 + bh * a.Dabi : nullptr;
-#pragma unroll
-      for (int m = 0; m < NFT; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          abi_store(a.s_T + bh * (size_t)a.Dabi * DV, s0, a.compact, 16 * m + 4 * g + e, DV, 16 * n_col + l16,
-                    st[m][e]);
-      for (int fi = tid; fi < NF; fi += NTHR) abi_store(a.z_T + bh * a.Dabi, z0, a.compact, fi, 1, 0, sZ[fi]);
-    }
-  } else {
+  if (seg == a.nseg - 1 && a.s_T) {  // the last segment's end state is S_T
     __syncthreads();
     const int l16 = lane & 15, g = lane >> 4;
-    float *dst = a.dsum + (bh * a.nseg + seg) * (size_t)NF * (DV + 1);
+    const float *s0 = a.s0 ? a.s0 + bh * (size_t)a.Dabi * DV : nullptr;
+    const float *z0 = a.z0 ? a.z0 + bh * a.Dabi : nullptr;
 #pragma unroll
     for (int m = 0; m < NFT; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(size_t)(16 * m + 4 * g + e) * (DV + 1) + 16 * n_col + l16] = st[m][e];
-    for (int fi = tid; fi < NF; fi += NTHR) dst[(size_t)fi * (DV + 1) + DV] = sZ[fi];
+      for (int e = 0; e < 4; ++e)
+        abi_store(a.s_T + bh * (size_t)a.Dabi * DV, s0, a.compact, 16 * m + 4 * g + e, DV, 16 * n_col + l16,
+                  st[m][e]);
+    for (int fi = tid; fi < NF; fi += NTHR) abi_store(a.z_T + bh * a.Dabi, z0, a.compact, fi, 1, 0, sZ[fi]);
   }
+}
+
+// Pass 1: each segment's sums (delta s, delta z) from a zero state.  A segment with a
+// map never holds the sequence's last chunk (the plan gives the remainder to the last
+// segment), so its chunks are whole; loads past T would read zeros all the same, and the
+// constant feature's count is taken from T.  Here the waves own (feature tile,
+// value-column tile) pairs instead of column tiles: wave w keeps the order-2 tiles 2 w
+// and 2 w + 1 over all four column tiles and half of tile 8 + w / 2 (tile 8, or the
+// linear tile 9), ten accumulator tiles each, so every wave builds only the phi(k)
+// fragments it multiplies and none crosses LDS.  The normaliser's increment is kept as
+// the key Gram sum_t k_t k_t^T (wave 2) and sum_t k_t (wave 3), accumulated in registers
+// over the segment and scattered onto the diagonal tiles once at the end.  K and V are
+// staged through registers two chunks ahead into two LDS buffers: one barrier a chunk.
+__global__ __launch_bounds__(NTHR, 3) void based_map_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][C * LDQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][C * LDV];
+  __shared__ __attribute__((aligned(16))) float sZf[NF];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int seg = blockIdx.x;
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int64_t T = a.T;
+  const float rs2 = 0.70710678118654752f;
+  const int64_t first = (int64_t)seg * a.seg_chunks * C;
+  const int nchunks = a.seg_chunks;
+
+  f32x4 sf[2][4], sx[2], zg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    sx[i] = zg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sf[i][c] = zg;
+  }
+  // row 0 of a one-row operand: 1 at every token (A operand of sum_t k_t)
+  const bf16x8 ones = (lane & 15) == 0 ? pack8(1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f)
+                                       : pack8(0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f);
+
+  auto load = [&](u32x4(&pv)[2], u32x4 &pk, int64_t t0) {
+    const uint32_t ln = (uint32_t)((T - t0) < C ? (T - t0) : C);
+    const size_t rb = bh * (size_t)T + t0;
+    const rsrc_t rv = make_rsrc(a.v + rb * DV, ln * DV * 2);
+    pv[0] = bld16(rv, 16u * (uint32_t)tid);
+    pv[1] = bld16(rv, 16u * (uint32_t)(tid + NTHR));
+    if (tid < 2 * C) pk = bld16(make_rsrc(a.k + rb * DP, ln * DP * 2), 16u * (uint32_t)tid);
+  };
+  auto chunk = [&](int ci, u32x4(&pv)[2], u32x4 &pk, bf16_t *sKb, bf16_t *sVb) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int id = tid + NTHR * i;
+      *reinterpret_cast<u32x4 *>(sVb + (id >> 3) * LDV + (id & 7) * 8) = pv[i];
+    }
+    if (tid < 2 * C) *reinterpret_cast<u32x4 *>(sKb + (tid >> 1) * LDQ + (tid & 1) * 8) = pk;
+    // the buffer was last read two chunks ago, before every wave reached the previous
+    // chunk's barrier
+    __syncthreads();
+    if (ci + 2 < nchunks) load(pv, pk, first + (int64_t)(ci + 2) * C);
+    int lane_v = lane;  // opaque: keeps per-fragment LDS addresses inside the loop
+    asm volatile("" : "+v"(lane_v));
+    const int l16 = lane_v & 15;
+    const bf16x8 kj[2] = {col_frag(sKb, LDQ, 0, 0, lane_v), col_frag(sKb, LDQ, 0, 1, lane_v)};
+    bf16x8 vf[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) vf[c][s2] = col_frag(sVb, LDV, c, s2, lane_v);
+    f32x4 kf[2][2], kw[2][2];  // [s2][lo/hi]: k_t[i] and sqrt 2 k_t[i], i = lane % 16
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[s2][h][e] = (float)kj[s2][4 * h + e];
+          kw[s2][h][e] = kf[s2][h][e] * (2.0f * rs2);
+        }
+    // phi(k)^T fragments of diagonal tile d (rows = features, k = the lane's tokens)
+    auto phi = [&](auto dc, bf16x8(&p)[2]) {
+      constexpr int d = decltype(dc)::value;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        f32x4 f[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (d == 0) f[h][e] = kf[s2][h][e] * kf[s2][h][e] * rs2;
+            else f[h][e] = kw[s2][h][e] * row_ror<16 - d>(kf[s2][h][e]);
+            if constexpr (d == ND - 1)
+              if (l16 >= DP / 2) f[h][e] = l16 == DP / 2 ? 1.0f : 0.0f;
+          }
+        p[s2] = pack_pair(f[0], f[1]);
+      }
+    };
+    static_for<NW>([&](auto wc) {
+      constexpr int W = decltype(wc)::value;
+      if (wave == W) {
+        static_for<2>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          bf16x8 p[2];
+          phi(std::integral_constant<int, 2 * W + I>{}, p);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) sf[I][c] = mfma_bf16(p[s2], vf[c][s2], sf[I][c]);
+        });
+        constexpr int c0 = 2 * (W & 1);
+        bf16x8 p[2];
+        if constexpr (W < 2) phi(std::integral_constant<int, ND - 1>{}, p);
+        else {
+          p[0] = kj[0];
+          p[1] = kj[1];
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) sx[c] = mfma_bf16(p[s2], vf[c0 + c][s2], sx[c]);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if constexpr (W == 2) zg = mfma_bf16(kj[s2], kj[s2], zg);  // G[a][b], a = row, b = column
+          if constexpr (W == 3) zg = mfma_bf16(ones, kj[s2], zg);    // row 0: sum_t k_t[b]
+        }
+      }
+    });
+  };
+
+  u32x4 pva[2], pka, pvb[2], pkb;
+  if (nchunks > 0) load(pva, pka, first);
+  if (nchunks > 1) load(pvb, pkb, first + C);
+  for (int ci = 0; ci < nchunks; ci += 2) {
+    chunk(ci, pva, pka, sK[0], sV[0]);
+    if (ci + 1 < nchunks) chunk(ci + 1, pvb, pkb, sK[1], sV[1]);
+  }
+
+  // z: the Gram's kept entries (G[a][b] is pair (a, b) on diagonal (b - a) mod 16), the
+  // linear sums, the constant's count and tile 8's zero rows: every feature once
+  const int l16 = lane & 15, g = lane >> 4;
+  if (wave == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ra = 4 * g + e, d = (l16 - ra) & 15;
+      if (d < ND - 1 || (d == ND - 1 && ra < DP / 2)) sZf[16 * d + ra] = zg[e] * (d == 0 ? rs2 : 2.0f * rs2);
+    }
+  } else if (wave == 3 && g == 0) {
+    sZf[16 * T_LIN + l16] = zg[0];
+    const int64_t cnt = (T - first) < (int64_t)nchunks * C ? (T - first) : (int64_t)nchunks * C;
+    if (l16 >= DP / 2) sZf[16 * (ND - 1) + l16] = l16 == DP / 2 ? (float)cnt : 0.0f;
+  }
+  __syncthreads();
+  float *dst = a.dsum + (bh * a.nseg + seg) * (size_t)NF * (DV + 1);
+  const int c0 = 2 * (wave & 1), fx = ND - 1 + (wave >> 1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[(size_t)(16 * (2 * wave + i) + 4 * g + e) * (DV + 1) + 16 * c + l16] = sf[i][c][e];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) dst[(size_t)(16 * fx + 4 * g + e) * (DV + 1) + 16 * (c0 + c) + l16] = sx[c][e];
+  }
+  for (int fi = tid; fi < NF; fi += NTHR) dst[(size_t)fi * (DV + 1) + DV] = sZf[fi];
 }
 
 // Pass 2: the start states of all segments in internal order: segment 0's is the
@@ -646,11 +792,11 @@ hipError_t launch_based_chunk_prefill(bool compact, int B, int H, int64_t T, flo
   a.eps = eps;
   const dim3 grid(p.nseg, H, B);
   if (p.nseg > 1 && (pass_mask & PASS_MAPS))  // every segment but the last
-    hipLaunchKernelGGL(based_chunk_kernel<MODE_MAP>, dim3(p.nseg - 1, H, B), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL(based_map_kernel, dim3(p.nseg - 1, H, B), dim3(NTHR), 0, s, a);
   if (p.nseg > 1 && (pass_mask & PASS_SCAN))
     hipLaunchKernelGGL(based_scan_kernel, dim3((NF * (DV + 1) + 255) / 256, H, B), dim3(256), 0, s, a);
   if (pass_mask & PASS_REPLAY)
-    hipLaunchKernelGGL(based_chunk_kernel<MODE_OUT>, grid, dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL(based_replay_kernel, grid, dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 
