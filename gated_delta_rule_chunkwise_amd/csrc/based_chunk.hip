@@ -456,17 +456,11 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
           });
         }
       });
-      __syncthreads();
-    }
-    {
-      // carry.  Order-2 tile d (with the constant in tile 8): s += phi(K)_d^T V with the shared
-      // phi(K)_d^T fragments, read one tile ahead.  Linear tile: K^T V.  z's increment
-      // phi(K)^T 1: the order-2 part from the key Gram G = sum_t k_t k_t^T (wave 0; entry
-      // (a, b) lands in row a of diagonal tile (b - a) mod 16 when that is a kept row), the
-      // linear part sum_t k_t, the constant sum_t 1 and tile 8's zero rows (wave 1): every
-      // internal feature written once.  Its products go first so that their results are
-      // ready when the carry's are still in flight.
-      const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
+      // z's increment phi(K)^T 1, written before the barrier and off the carry's path: the
+      // order-2 part from the key Gram G = sum_t k_t k_t^T (wave 2, which builds two tiles;
+      // entry (a, b) lands in row a of diagonal tile (b - a) mod 16 when that is a kept row),
+      // the linear part sum_t k_t, the constant sum_t 1 and tile 8's zero rows (wave 3):
+      // every internal feature written once
       f32x4 zg = {0.f, 0.f, 0.f, 0.f};
       if (wave == 2) {
 #pragma unroll
@@ -475,6 +469,26 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(ones, kj[s2], zg);  // row 0: sum_t k_t[l16]
       }
+      if (wave == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // G[a][b], a = 4 g + e, b = l16; unkept entries to a spare slot
+          const int ra = 4 * g + e, d = (l16 - ra) & 15;
+          const bool keep = d < ND - 1 || (d == ND - 1 && ra < DP / 2);
+          sZinc[keep ? 16 * d + ra : NF + lane] = zg[e] * (d == 0 ? rs2 : 2.0f * rs2);
+        }
+      } else if (wave == 3) {
+        if (g == 0) {
+          sZinc[16 * T_LIN + l16] = zg[0];
+          // the constant feature counts the valid tokens
+          if (l16 >= DP / 2) sZinc[16 * (ND - 1) + l16] = l16 == DP / 2 ? (float)n : 0.0f;
+        }
+      }
+      __syncthreads();
+    }
+    {
+      // carry.  Order-2 tile d (with the constant in tile 8): s += phi(K)_d^T V with the shared
+      // phi(K)_d^T fragments, read one tile ahead.  Linear tile: K^T V.
+      const bf16x8 kj[2] = {col_frag(sK, LDQ, 0, 0, lane_v), col_frag(sK, LDQ, 0, 1, lane_v)};
       bf16x8 pkb[2][2];
       pkb[0][0] = phik[0 * 64 + lane_v];
       pkb[0][1] = phik[1 * 64 + lane_v];
@@ -492,20 +506,6 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) st[T_LIN] = mfma_bf16(kj[s2], s2 == 0 ? vf0 : vf1, st[T_LIN]);
-      if (wave == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {  // G[a][b], a = 4 g + e, b = l16; unkept entries to a spare slot
-          const int ra = 4 * g + e, d = (l16 - ra) & 15;
-          const bool keep = d < ND - 1 || (d == ND - 1 && ra < DP / 2);
-          sZinc[keep ? 16 * d + ra : NF + lane] = zg[e] * (d == 0 ? rs2 : 2.0f * rs2);
-        }
-      } else if (wave == 3) {
-        if (g == 0) {
-          sZinc[16 * T_LIN + l16] = zg[0];
-          // the constant feature counts the valid tokens
-          if (l16 >= DP / 2) sZinc[16 * (ND - 1) + l16] = l16 == DP / 2 ? (float)n : 0.0f;
-        }
-      }
     }
     __syncthreads();
 
