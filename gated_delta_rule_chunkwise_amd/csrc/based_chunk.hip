@@ -416,7 +416,7 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
     __syncthreads();  // every wave is done with phi(q) before sPhi is overwritten
     {
       // phi(k)^T fragments of the order-2 tiles (A operand: rows = features, k = tokens),
-      // tiles d = wave, wave + 4, ..., shared through LDS.  Row i of diagonal tile d is
+      // shared through LDS.  Row i of diagonal tile d is
       // k_t[i] k_t[(i + d) mod 16] times 1/sqrt 2 (d = 0) or sqrt 2 (both orders of the
       // pair); tile 8 keeps rows i < 8 and holds the constant 1 in row 8.  The K^T fragment
       // holds k_t[i] for i = lane % 16 at the lane's 8 tokens, so k_t[(i + d) mod 16] at the
@@ -433,52 +433,60 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
             kf[s2][h][e] = (float)kj[s2][4 * h + e];
             kw[s2][h][e] = kf[s2][h][e] * (2.0f * rs2);
           }
+      // the fragment of diagonal tile d for token step s2
+      auto build = [&](auto dc, int s2) {
+        constexpr int d = decltype(dc)::value;
+        f32x4 f[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (d == 0) f[h][e] = kf[s2][h][e] * kf[s2][h][e] * rs2;
+            else f[h][e] = kw[s2][h][e] * row_ror<16 - d>(kf[s2][h][e]);
+            if constexpr (d == ND - 1)
+              if (l16 >= DP / 2) f[h][e] = l16 == DP / 2 ? 1.0f : 0.0f;
+          }
+        phik[(d * 2 + s2) * 64 + lane] = pack_pair(f[0], f[1]);
+      };
+      // wave w: tiles w and w + 4, and waves 0 and 1 one token step each of tile 8
       static_for<NW>([&](auto wc) {
-        if (wave == decltype(wc)::value) {
-          static_for<(ND + NW - 1) / NW>([&](auto ic) {
-            constexpr int d = decltype(wc)::value + NW * decltype(ic)::value;
-            if constexpr (d < ND) {
+        constexpr int W = decltype(wc)::value;
+        if (wave == W) {
 #pragma unroll
-              for (int s2 = 0; s2 < 2; ++s2) {
-                f32x4 f[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) {
-                    if constexpr (d == 0) f[h][e] = kf[s2][h][e] * kf[s2][h][e] * rs2;
-                    else f[h][e] = kw[s2][h][e] * row_ror<16 - d>(kf[s2][h][e]);
-                    if constexpr (d == ND - 1)
-                      if (l16 >= DP / 2) f[h][e] = l16 == DP / 2 ? 1.0f : 0.0f;
-                  }
-                phik[(d * 2 + s2) * 64 + lane] = pack_pair(f[0], f[1]);
-              }
-            }
-          });
+          for (int s2 = 0; s2 < 2; ++s2) {
+            build(std::integral_constant<int, W>{}, s2);
+            build(std::integral_constant<int, W + NW>{}, s2);
+          }
+          if constexpr (W < 2) build(std::integral_constant<int, ND - 1>{}, W);
         }
       });
+      static_assert(ND - 1 == 2 * NW, "tiles 0..7 two a wave, tile 8 split between waves 0 and 1");
       // z's increment phi(K)^T 1, written before the barrier and off the carry's path: the
-      // order-2 part from the key Gram G = sum_t k_t k_t^T (wave 2, which builds two tiles;
-      // entry (a, b) lands in row a of diagonal tile (b - a) mod 16 when that is a kept row),
-      // the linear part sum_t k_t, the constant sum_t 1 and tile 8's zero rows (wave 3):
-      // every internal feature written once
-      f32x4 zg = {0.f, 0.f, 0.f, 0.f};
-      if (wave == 2) {
+      // order-2 part from the key Gram G = sum_t k_t k_t^T (waves 2 and 3, half its rows
+      // each; entry (a, b) lands in row a of diagonal tile (b - a) mod 16 when that is a kept
+      // row), the linear part sum_t k_t, the constant sum_t 1 and tile 8's zero rows (wave
+      // 3): every internal feature written once
+      if (wave >= 2) {  // both form G; wave 2 scatters its rows 4 g, 4 g + 1, wave 3 the other two
+        f32x4 zg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(kj[s2], kj[s2], zg);
-      } else if (wave == 3) {
+        auto scatter = [&](auto e0c) {  // G[a][b], a = 4 g + e, b = l16; unkept entries to a spare slot
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) zg = mfma_bf16(ones, kj[s2], zg);  // row 0: sum_t k_t[l16]
+          for (int e = decltype(e0c)::value; e < decltype(e0c)::value + 2; ++e) {
+            const int ra = 4 * g + e, d = (l16 - ra) & 15;
+            const bool keep = d < ND - 1 || (d == ND - 1 && ra < DP / 2);
+            sZinc[keep ? 16 * d + ra : NF + lane] = zg[e] * (d == 0 ? rs2 : 2.0f * rs2);
+          }
+        };
+        if (wave == 2) scatter(std::integral_constant<int, 0>{});
+        else scatter(std::integral_constant<int, 2>{});
       }
-      if (wave == 2) {
+      if (wave == 3) {
+        f32x4 zs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {  // G[a][b], a = 4 g + e, b = l16; unkept entries to a spare slot
-          const int ra = 4 * g + e, d = (l16 - ra) & 15;
-          const bool keep = d < ND - 1 || (d == ND - 1 && ra < DP / 2);
-          sZinc[keep ? 16 * d + ra : NF + lane] = zg[e] * (d == 0 ? rs2 : 2.0f * rs2);
-        }
-      } else if (wave == 3) {
+        for (int s2 = 0; s2 < 2; ++s2) zs = mfma_bf16(ones, kj[s2], zs);  // row 0: sum_t k_t[l16]
         if (g == 0) {
-          sZinc[16 * T_LIN + l16] = zg[0];
+          sZinc[16 * T_LIN + l16] = zs[0];
           // the constant feature counts the valid tokens
           if (l16 >= DP / 2) sZinc[16 * (ND - 1) + l16] = l16 == DP / 2 ? (float)n : 0.0f;
         }
