@@ -416,9 +416,9 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
     __syncthreads();  // every wave is done with phi(q) before sPhi is overwritten
     {
       // phi(k)^T fragments of the order-2 tiles (A operand: rows = features, k = tokens),
-      // shared through LDS.  Row i of diagonal tile d is
-      // k_t[i] k_t[(i + d) mod 16] times 1/sqrt 2 (d = 0) or sqrt 2 (both orders of the
-      // pair); tile 8 keeps rows i < 8 and holds the constant 1 in row 8.  The K^T fragment
+      // shared through LDS.  Row i of diagonal tile d is k_t[i] k_t[(i + d) mod 16] times
+      // 1/sqrt 2 (d = 0) or sqrt 2 (both orders of the pair); tile 8 keeps rows i < 8 and
+      // holds the constant 1 in row 8.  The K^T fragment
       // holds k_t[i] for i = lane % 16 at the lane's 8 tokens, so k_t[(i + d) mod 16] at the
       // same tokens is a DPP rotation of the 16-lane row, folded into the multiply (d must
       // be a constant, hence the uniform branch on the wave index).
