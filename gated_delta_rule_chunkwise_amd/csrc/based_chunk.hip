@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
   __shared__ __attribute__((aligned(16))) bf16_t sA[C * LDA];  // kernel matrix, transposed
   __shared__ __attribute__((aligned(16))) float sZ[NF];        // z, internal order
   __shared__ __attribute__((aligned(16))) float sZinc[NF + 64];  // this chunk's Phi_K^T 1 (+ spare slots)
-  __shared__ __attribute__((aligned(16))) float sDen[C];
+  __shared__ __attribute__((aligned(16))) float sDen[C];  // 1 / (den + eps) per token
   // phi(q) as MFMA B-operand fragments, [token tile][feature step][lane] (16 bytes each):
   // each wave builds its token tile's once per chunk, every wave reads all four
   __shared__ __attribute__((aligned(16))) bf16x8 sPhi[4 * (NFT / 2) * 64];
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
           if (s2 == 1 && mt < 2) continue;
           dacc = mfma_bf16(ones, col_frag(sA, LDA, mt, s2, lane_v), dacc);
         }
-        if (g == 0) sDen[16 * mt + l16] = dacc[0] + zq;
+        if (g == 0) sDen[16 * mt + l16] = __builtin_amdgcn_rcpf(dacc[0] + zq + a.eps);  // 1 / (den + eps)
       }
     }
     __syncthreads();  // every wave is done with phi(q) before sPhi is overwritten
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(NTHR, 3) void based_replay_kernel(const Args a) {
       const rsrc_t ro = make_rsrc(a.o + (bh * (size_t)T + t0) * DV, (uint32_t)n * DV * 2);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const float r = __builtin_amdgcn_rcpf(sDen[16 * mt + l16] + a.eps);
+        const float r = sDen[16 * mt + l16];
         const f32x4 x = num[mt] * r;
         bst8(ro, 2u * (uint32_t)((16 * mt + l16) * DV + 16 * n_col + 4 * g), pk4u(x));
       }
